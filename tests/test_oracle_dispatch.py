@@ -1,0 +1,62 @@
+"""Pins for the oracle's dispatch metadata (histogram, scan, stable placement).
+
+Checked against numpy.bincount / cumsum / stable argsort, against the
+per-expert boolean-mask gather of the lpnh.cn deep dive (section 3.2,
+redistribute_tokens), and against the bijection / inverse properties that the
+saved indices and locations of the DeepEP notes (section 7.5(2)) must have.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from moe_workloads import make_routing
+
+
+@pytest.mark.parametrize("T,E,k,skew", [(1, 1, 1, 0), (257, 8, 2, 0), (1000, 32, 8, 0),
+                                        (3000, 128, 4, 1.2), (500, 5, 5, 0), (0, 4, 2, 0)])
+def test_dispatch_against_library_routines(T, E, k, skew):
+    idx = make_routing(T, E, k, seed=T + E, skew=skew)
+    counts, offsets, dest, src = oracle.dispatch(idx, E)
+    assert np.array_equal(counts, np.bincount(idx.ravel(), minlength=E))
+    assert counts.sum() == T * k and offsets[E] == T * k
+    assert np.array_equal(offsets, np.concatenate([[0], np.cumsum(counts)]))
+    order = np.argsort(idx.ravel(), kind="stable")  # expert-major, (token, slot) order kept
+    assert np.array_equal(src, order // k)
+    flat_dest = dest.ravel()
+    assert np.array_equal(flat_dest[order], np.arange(T * k))
+    # bijection onto [0, T*k) and src_token inverts dest_row
+    assert np.array_equal(np.sort(flat_dest), np.arange(T * k))
+    if T:
+        assert np.array_equal(src[dest], np.repeat(np.arange(T), k).reshape(T, k))
+
+
+def test_dispatch_equals_per_expert_mask_gather():
+    T, E, k, d = 300, 12, 3, 5
+    idx = make_routing(T, E, k, seed=4, skew=0.8)
+    x = np.random.default_rng(0).standard_normal((T, d)).astype(np.float32)
+    counts, offsets, dest, src = oracle.dispatch(idx, E)
+    x_perm = x[src]
+    # lpnh.cn 3.2: tokens[expert_ids == i] for each expert i, concatenated
+    naive = np.concatenate([x[(idx == i).any(axis=1)] for i in range(E)])
+    assert np.array_equal(x_perm, naive)
+    # un-permute(permute(x)) == x, bit for bit
+    for j in range(k):
+        assert np.array_equal(x_perm[dest[:, j]], x)
+
+
+def test_dispatch_rejects_bad_routing():
+    with pytest.raises(ValueError):
+        oracle.dispatch(np.array([[0, 4]], dtype=np.int32), 4)   # id out of range
+    with pytest.raises(ValueError):
+        oracle.dispatch(np.array([[1, 1]], dtype=np.int32), 4)   # same expert twice
+    with pytest.raises(ValueError):
+        oracle.dispatch(np.array([[-1, 0]], dtype=np.int32), 4)
+
+
+def test_skewed_routing_leaves_empty_experts():
+    idx = make_routing(4000, 128, 4, seed=2, skew=2.5)
+    counts, offsets, _, _ = oracle.dispatch(idx, 128)
+    assert (counts == 0).sum() > 0
+    # empty experts have empty ranges
+    assert np.all(offsets[1:][counts == 0] == offsets[:-1][counts == 0])
