@@ -1,0 +1,190 @@
+"""Benchmark: one MoE layer forward (gate -> dispatch -> grouped SwiGLU FFN ->
+combine) on one MI355X, through the C ABI.
+
+    python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
+
+Prints ONE JSON line. `value` is routed tokens/s (T / time per layer forward)
+with every input already resident in HBM. Per-kernel durations come from HIP
+events that the library records on its stream between kernels
+(moe_forward_traced) during the timed steps themselves. The roofline entry is
+for the dominant kernel, the grouped up-projection (bf16 matrix cores).
+The cpu_baseline leg times the CPU oracle, single-threaded, on a bounded
+sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "routed tokens/s per MoE layer fwd (1 GPU); dispatch+combine HBM GB/s; FFN MFMA %"
+HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+F32_VEC_PEAK_TFLOPS = 157.3
+
+
+def algorithmic(cfg):
+    """Algorithmic bytes / FLOPs of each stage for one layer forward."""
+    T, d, E, k, S, h = cfg.T, cfg.d, cfg.E, cfg.k, cfg.S, cfg.h
+    b = 4 if cfg.act == "f32" else 2
+    bp = 1 if cfg.dispatch == "fp8" else b
+    rows = T * k + S * T
+    return {
+        "gate_bytes": T * d * b + E * d * b + 8 * T * k,
+        "gate_flops": 2 * T * d * E,
+        "dispatch_bytes": T * d * b + T * k * d * bp + 8 * T * k + 4 * T * k
+        + (8 * T * k if cfg.dispatch == "fp8" else 0),
+        "ffn_up_flops": 4 * rows * d * h,
+        "ffn_down_flops": 2 * rows * d * h,
+        "combine_bytes": T * k * d * b + (T * d * b if S else 0) + 8 * T * k + T * d * b,
+    }
+
+
+def cpu_baseline(cfg, n_tokens):
+    import oracle
+    from moe_workloads import make_inputs
+    inp = make_inputs(cfg)
+    toks = np.arange(min(n_tokens, cfg.T), dtype=np.int64)
+    t0 = time.perf_counter()
+    oracle.layer_tokens(inp, toks, nthreads=1)
+    dt = time.perf_counter() - t0
+    return {"value": round(len(toks) / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {len(toks)} tokens of the {cfg.name} batch, whole layer per token "
+                      f"(float32 gate chain, top-k, float64 SwiGLU experts, weighted sum), "
+                      f"1 thread, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="deepseekmoe_bf16")
+    ap.add_argument("--cpu-tokens", type=int, default=96)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share of the tokens on one GPU; "
+              "runs on more than one GPU are not part of this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mixture_experts_routing_gemm_amd as mm
+    from moe_workloads import CONFIGS, make_inputs
+
+    cfg = CONFIGS[args.config]
+    torch.cuda.set_device(0)
+    print(f"[bench] generating {cfg.name}", file=sys.stderr, flush=True)
+    inp = make_inputs(cfg)
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    x, wg, w1, w3, w2 = dev(inp.x), dev(inp.wg), dev(inp.w1), dev(inp.w3), dev(inp.w2)
+    bias = None if inp.bias is None else dev(inp.bias)
+    del inp
+    shape = mm.shape_of(cfg)
+    buf = mm.ForwardBuffers(shape)
+    nk = mm.moe_forward_kernel_count(shape)
+    names = [mm.moe_forward_kernel_name(shape, i) for i in range(nk)]
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        buf.run(x, wg, bias, w1, w3, w2)
+    torch.cuda.synchronize()
+
+    # one set of nk+1 events per timed step, created up front
+    evs = []
+    for _ in range(args.steps):
+        row = [torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)]
+        for e in row:
+            e.record(stream)
+        evs.append(row)
+    torch.cuda.synchronize()
+    handles = [[e.cuda_event for e in row] for row in evs]
+
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        buf.run(x, wg, bias, w1, w3, w2, events=handles[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert mm.moe_get_device_error(buf.ws) == mm.MOE_OK
+
+    per_kernel = np.array([[row[j].elapsed_time(row[j + 1]) for j in range(nk)] for row in evs])
+    step_ms = np.array([row[0].elapsed_time(row[nk]) for row in evs])
+    kmean = dict(zip(names, per_kernel.mean(axis=0).tolist()))
+    ms_per_step = wall * 1000.0 / args.steps
+
+    A = algorithmic(cfg)
+    t_gate = kmean["gate_topk"]
+    t_disp = sum(v for n, v in kmean.items() if n.startswith("dispatch"))
+    t_up, t_down = kmean["ffn_up"], kmean["ffn_down"]
+    t_ffn = t_up + t_down + kmean["ffn_plan"]
+    t_comb = kmean["combine"]
+    up_tflops = A["ffn_up_flops"] / (t_up * 1e-3) / 1e12
+    gemm_peak = BF16_PEAK_TFLOPS if cfg.act == "bf16" else F32_VEC_PEAK_TFLOPS
+    detail = {
+        "kernel_ms": {n: round(v, 5) for n, v in kmean.items()},
+        "step_ms_events_median": round(float(np.median(step_ms)), 5),
+        "gate_us": round(t_gate * 1e3, 2),
+        "gate_tflops": round(A["gate_flops"] / (t_gate * 1e-3) / 1e12, 3),
+        "dispatch_us": round(t_disp * 1e3, 2),
+        "dispatch_GBps": round(A["dispatch_bytes"] / (t_disp * 1e-3) / 1e9, 1),
+        "dispatch_hbm_frac": round(A["dispatch_bytes"] / (t_disp * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "ffn_us": round(t_ffn * 1e3, 2),
+        "ffn_mfma_frac": round((A["ffn_up_flops"] + A["ffn_down_flops"]) / (t_ffn * 1e-3) / 1e12
+                               / gemm_peak, 4),
+        "ffn_down_tflops": round(A["ffn_down_flops"] / (t_down * 1e-3) / 1e12, 1),
+        "combine_us": round(t_comb * 1e3, 2),
+        "combine_GBps": round(A["combine_bytes"] / (t_comb * 1e-3) / 1e9, 1),
+        "combine_hbm_frac": round(A["combine_bytes"] / (t_comb * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "routed_assignments_per_s": round(cfg.T * cfg.k / (ms_per_step * 1e-3), 1),
+    }
+    out = {
+        "metric": METRIC,
+        "value": round(cfg.T / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.act,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k,
+                   "S": cfg.S, "h": cfg.h, "dispatch": cfg.dispatch},
+        "roofline": {
+            "kernel": "ffn_up",
+            "bound": "mfma",
+            "achieved": round(up_tflops, 2),
+            "peak": gemm_peak,
+            "unit": "TFLOP/s",
+            "frac": round(up_tflops / gemm_peak, 4),
+            "traffic": None,
+        },
+        "detail": detail,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,205 @@
+/*
+ * moe.h -- C ABI of a single-GPU (MI355X, gfx950) Mixture-of-Experts layer
+ * forward pass: gate -> top-k -> dispatch -> grouped SwiGLU expert FFN ->
+ * combine, on one GPU's share of the tokens with every expert local.
+ *
+ * Sources for what each call computes (the pages the method comes from):
+ *  [wmrh]  "DeepSeek 中 MoE 的同步税" (wmrh.cn/news/47329), section 4.1: the
+ *          routing code (gate, softmax, top-k, renormalise by the selected
+ *          sum); section 4.3: gate/softmax/top-k fused into one kernel that
+ *          writes indices and weights; section 5.1: keep the router in
+ *          float32; section 2.1: fine-grained routed experts plus shared
+ *          experts every token passes through.
+ *  [lpnh]  the DeepSeek MoE routing deep dive (lpnh.cn/news/699721), section
+ *          2.2: per-token top-k gating kernel over an [N, E] score matrix.
+ *  [gsyq]  "Deepseek-MoE同步税本质与四层实战优化指南" (gsyq.cn), section 2.3:
+ *          each token's output is the gate-weighted sum of its experts'
+ *          outputs; section 3.1: per-token min/max affine FP8 quantiser at the
+ *          dispatch entry.
+ *  [deepep] "MoE数据特征、训练和推理的通信特点 ... DeepEP ... All-to-All"
+ *          (zzszmyf.github.io), section 7: dispatch reorders tokens by target
+ *          expert and packs them contiguously ([Local_Batch, Hidden] ->
+ *          [Num_Experts * Tokens_Per_Expert, Hidden]); the expert stage is a
+ *          local FFN; combine restores the original token order from the
+ *          metadata saved at dispatch (7.5(2): indices and locations), with no
+ *          padding (7.5(4)) and with sizes known before the payload moves.
+ *
+ * Conventions (all entry points):
+ *  - Every pointer argument except the moe_shape is a DEVICE pointer unless
+ *    stated; the caller allocates and owns every buffer, including the
+ *    workspace. The library never allocates, frees or synchronises inside a
+ *    compute call; all work is enqueued on `stream` (a hipStream_t; NULL is
+ *    the null stream) and the call returns before it runs.
+ *  - Arrays are dense row-major. Device pointers must be 16-byte aligned and
+ *    the workspace 256-byte aligned.
+ *  - Expert weight groups are ordered routed 0..E-1, then shared E..E+S-1.
+ *    W1, W3 are [E+S, h, d] and W2 is [E+S, d, h] (each row is one output
+ *    feature, nn.Linear layout). The gate weight is [E, d].
+ *  - Arguments are validated on the host before anything is enqueued; a bad
+ *    argument returns a negative moe_status and leaves the stream untouched.
+ *    T = 0 is valid, needs no buffers (they may be NULL) and enqueues nothing.
+ *    No C++ exception crosses the ABI.
+ *  - Expert ids in topk_idx outside [0, E), or an expert listed twice for one
+ *    token, are detected on the device: the offending slots are skipped
+ *    (dest_row = -1), no memory outside the buffers is touched, and a sticky
+ *    flag in the workspace is set; moe_get_device_error reports it.
+ *
+ * Shape limits: 1 <= E <= 256, 1 <= k <= min(E, 8), 0 <= S <= 8, T >= 0,
+ * T*k < 2^31 and T*S < 2^31. act = MOE_F32: d % 4 == 0. act = MOE_BF16:
+ * d % 128 == 0 and h % 64 == 0 (the expert GEMM tiles). dispatch must equal
+ * act, or be MOE_FP8_E4M3 with act = MOE_BF16.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1, /* null pointer, bad size, misaligned pointer */
+    MOE_ERR_UNSUPPORTED = -2, /* a shape or dtype combination outside the limits */
+    MOE_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+    MOE_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed */
+    MOE_ERR_BAD_INDEX = -5    /* (device flag) bad or repeated expert id seen */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
+
+/* which entry point a workspace is sized for */
+typedef enum {
+    MOE_STAGE_GATE = 0,
+    MOE_STAGE_DISPATCH = 1,
+    MOE_STAGE_FFN = 2,
+    MOE_STAGE_COMBINE = 3,
+    MOE_STAGE_FORWARD = 4
+} moe_stage;
+
+typedef struct {
+    int64_t T;        /* tokens on this GPU */
+    int32_t d;        /* model (hidden) width */
+    int32_t E;        /* routed experts */
+    int32_t k;        /* routed experts per token */
+    int32_t S;        /* shared experts (every token passes through them) */
+    int32_t h;        /* expert SwiGLU hidden width */
+    int32_t act;      /* moe_dtype of x, all weights, expert outputs and y */
+    int32_t dispatch; /* moe_dtype of the dispatched rows x_perm */
+} moe_shape;
+
+/* Host only. Bytes of workspace that `stage` needs for shape *s (0 when the
+ * stage needs none), or 0 for an invalid shape. */
+size_t moe_workspace_bytes(const moe_shape *s, int32_t stage);
+
+/* Clear the workspace header (the error flag and internal counters). Call once
+ * after allocating a workspace and before its first use; every call leaves the
+ * header in a valid state afterwards. Enqueued on stream. */
+int32_t moe_workspace_init(void *ws, size_t ws_bytes, void *stream);
+
+/* Host only. Static text for a moe_status value. */
+const char *moe_status_string(int32_t status);
+
+/*
+ * Gate + top-k + renormalised weights ([wmrh] 4.1 and 4.3, [lpnh] 2.2).
+ *  x [T,d] (act), w_gate [E,d] (act), bias [E] float32 or NULL.
+ *  logit[t,e] = sum_i x[t,i]*w_gate[e,i] (+ bias[e]) in float32, summed as one
+ *  fused multiply-add chain over i = 0..d-1 from +0.0 ([wmrh] 5.1: float32
+ *  router); topk_idx[t,:] (int32 [T,k]) = the k largest logits in descending
+ *  order, ties to the lower expert id; topk_w[t,j] (float32 [T,k]) =
+ *  softmax over all E renormalised over the selected k (= softmax of the k
+ *  selected logits). logits_dbg [T,E] float32 receives the logits if not NULL.
+ */
+int32_t moe_gate_topk(const moe_shape *s, const void *x, const void *w_gate,
+                      const float *bias, int32_t *topk_idx, float *topk_w,
+                      float *logits_dbg, void *stream);
+
+/*
+ * Dispatch ([deepep] 7 "Dispatch" and 7.5(2)/(4), [gsyq] 3.1 for FP8).
+ *  counts[e] (int32 [E]) = number of (t,j) with topk_idx[t,j] == e;
+ *  offsets (int32 [E+1]) = exclusive prefix sum, offsets[E] = T*k;
+ *  dest_row[t,j] (int32 [T,k]) = offsets[e] + number of tokens t' < t that
+ *  picked e (stable, expert-major, token order kept, no padding);
+ *  src_token[dest_row[t,j]] = t (int32 [T*k]);
+ *  x_perm[dest_row[t,j]] = x[t] (rows of act), or, with dispatch =
+ *  MOE_FP8_E4M3, the token's per-row affine e4m3 codes (uint8 [T*k, d]) with
+ *  qparams[dest_row[t,j]] = (scale, centre) (float32 [T*k, 2]): centre =
+ *  (max+min)/2, scale = (max-min)/2/448, code = e4m3 round-to-nearest-even of
+ *  clamp((x - centre) * (448 / ((max-min)/2)), +-448), all in float32; a
+ *  constant row gets codes 0 and scale 0. qparams may be NULL otherwise.
+ *  ws: MOE_STAGE_DISPATCH bytes.
+ */
+int32_t moe_dispatch(const moe_shape *s, const void *x, const int32_t *topk_idx,
+                     int32_t *counts, int32_t *offsets, int32_t *dest_row,
+                     int32_t *src_token, void *x_perm, float *qparams, void *ws,
+                     size_t ws_bytes, void *stream);
+
+/*
+ * Grouped SwiGLU expert FFN ([deepep] 7 "expert stage", [wmrh] 2.1).
+ *  For routed expert e, the rows offsets[e]..offsets[e+1]-1 of x_perm (fp8
+ *  rows are first dequantised to code*scale + centre): y_perm[r] =
+ *  W2_e (silu(W1_e v) * (W3_e v)), silu(a) = a / (1 + exp(-a)).
+ *  For the shared experts (S > 0), every token of x [T,d]:
+ *  y_shared[t] = sum_s W2_{E+s} (silu(W1_{E+s} x[t]) * (W3_{E+s} x[t])).
+ *  bf16: products in bf16 on the matrix cores with float32 accumulation; the
+ *  SwiGLU hidden vector is rounded to bf16 once, each output once.
+ *  y_perm [T*k, d] (act), y_shared [T,d] (act; NULL iff S == 0); x may be
+ *  NULL iff S == 0; qparams required iff dispatch is fp8.
+ *  ws: MOE_STAGE_FFN bytes.
+ */
+int32_t moe_grouped_ffn(const moe_shape *s, const void *x_perm, const float *qparams,
+                        const int32_t *offsets, const void *x, const void *w1,
+                        const void *w3, const void *w2, void *y_perm, void *y_shared,
+                        void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Combine ([gsyq] 2.3, [deepep] 7 "Combine"): un-permute and weighted sum,
+ *  y[t] = y_shared[t] + sum_j topk_w[t,j] * y_perm[dest_row[t,j]], accumulated
+ *  in float32 and rounded once to act. y_shared may be NULL (then 0); slots
+ *  with dest_row < 0 are skipped.
+ */
+int32_t moe_combine(const moe_shape *s, const void *y_perm, const void *y_shared,
+                    const int32_t *dest_row, const float *topk_w, void *y,
+                    void *stream);
+
+/*
+ * The whole layer: moe_gate_topk -> moe_dispatch -> moe_grouped_ffn ->
+ * moe_combine with intermediates in the workspace (MOE_STAGE_FORWARD bytes).
+ * y [T,d] (act) is the layer output; topk_idx, topk_w, counts, offsets,
+ * dest_row and src_token are written as by the stage calls.
+ */
+int32_t moe_forward(const moe_shape *s, const void *x, const void *w_gate,
+                    const float *bias, const void *w1, const void *w3, const void *w2,
+                    void *y, int32_t *topk_idx, float *topk_w, int32_t *counts,
+                    int32_t *offsets, int32_t *dest_row, int32_t *src_token, void *ws,
+                    size_t ws_bytes, void *stream);
+
+/*
+ * moe_forward that also records events[i] (hipEvent_t, created by the caller)
+ * on the stream before the first kernel and after each kernel, for per-kernel
+ * timing. n_events must be at least moe_forward_kernel_count(s) + 1; the
+ * kernel names are given by moe_forward_kernel_name.
+ */
+int32_t moe_forward_traced(const moe_shape *s, const void *x, const void *w_gate,
+                           const float *bias, const void *w1, const void *w3,
+                           const void *w2, void *y, int32_t *topk_idx, float *topk_w,
+                           int32_t *counts, int32_t *offsets, int32_t *dest_row,
+                           int32_t *src_token, void *ws, size_t ws_bytes, void *stream,
+                           void *const *events, int32_t n_events);
+
+/* Host only: number of kernels moe_forward launches for *s, and the name of
+ * the i-th ("gate_topk", "dispatch_rank", ...); NULL if out of range. */
+int32_t moe_forward_kernel_count(const moe_shape *s);
+const char *moe_forward_kernel_name(const moe_shape *s, int32_t i);
+
+/* Reads and clears the workspace's sticky device error flag. This call
+ * synchronises `stream`. Returns MOE_OK or MOE_ERR_BAD_INDEX (or an error). */
+int32_t moe_get_device_error(void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,18 @@
+"""MI355X-native forward pass of one Mixture-of-Experts layer.
+
+gate (float32 logits, top-k, renormalised weights) -> dispatch (histogram,
+scan, stable permutation, optional per-token affine FP8 rows) -> grouped
+SwiGLU expert FFN (bf16 matrix cores) -> combine (weighted un-permute).
+The work runs in the HIP kernels of libmoe_mi355x.so behind the C ABI in
+include/moe.h; this package is its ctypes binding. Build the library with
+``python -m mixture_experts_routing_gemm_amd.build``.
+"""
+
+from ._binding import (  # noqa: F401
+    EXPORTS, MOE_BF16, MOE_ERR_BAD_INDEX, MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED,
+    MOE_ERR_WORKSPACE, MOE_F32, MOE_FP8_E4M3, MOE_OK, STAGE_COMBINE, STAGE_DISPATCH, STAGE_FFN,
+    STAGE_FORWARD, STAGE_GATE, MoEError, alloc_workspace, make_shape, moe_combine, moe_dispatch,
+    moe_forward, moe_forward_kernel_count, moe_forward_kernel_name, moe_forward_traced,
+    moe_gate_topk, moe_get_device_error, moe_grouped_ffn, moe_shape, moe_workspace_bytes,
+    moe_workspace_init, shape_of, status_string)
+from .buffers import ForwardBuffers  # noqa: F401

@@ -1,0 +1,118 @@
+// Combine: un-permute and gate-weighted sum back to token order.
+//
+// Each token's output is the gate-weighted sum of its k experts' outputs
+// ("Deepseek-MoE同步税本质与四层实战优化指南", gsyq.cn, section 2.3), placed
+// back in the original token order from the metadata saved at dispatch (the
+// DeepEP notes, zzszmyf.github.io, section 7 "Combine" and 7.5(2)). The shared
+// experts' output, which every token receives with weight one ("DeepSeek 中
+// MoE 的同步税", wmrh.cn, section 2.1), is added in the same pass.
+//
+// One wave per token: the k source rows are gathered with 16-byte loads
+// (rows are contiguous), summed in float32 and rounded once.
+#include "moe_device.h"
+
+namespace moe {
+
+template <typename TAct>
+struct ActVec;
+
+template <>
+struct ActVec<float> {
+    static constexpr int N = 4;
+    __device__ static void unpack(u32x4 r, float* v) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = __uint_as_float(r[u]);
+    }
+    __device__ static u32x4 pack(const float* v) {
+        u32x4 r;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) r[u] = __float_as_uint(v[u]);
+        return r;
+    }
+};
+
+template <>
+struct ActVec<bf16_t> {
+    static constexpr int N = 8;
+    __device__ static void unpack(u32x4 r, float* v) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            v[2 * u] = bf16_lo(r[u]);
+            v[2 * u + 1] = bf16_hi(r[u]);
+        }
+    }
+    __device__ static u32x4 pack(const float* v) {
+        u32x4 r;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) r[u] = pack_bf16x2(v[2 * u], v[2 * u + 1]);
+        return r;
+    }
+};
+
+template <typename TAct>
+__global__ __launch_bounds__(256) void combine_kernel(
+    const TAct* __restrict__ y_perm, const TAct* __restrict__ y_sh,
+    const int32_t* __restrict__ dest_row, const float* __restrict__ topk_w, int64_t T, int d,
+    int k, int64_t rows, TAct* __restrict__ y) {
+    using V = ActVec<TAct>;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + w;
+    if (t >= T) return;
+    int p = -1;
+    float wt = 0.0f;
+    if (lane < k) {
+        p = dest_row[t * k + lane];
+        wt = topk_w[t * k + lane];
+        if (p < 0 || p >= rows) p = -1;
+    }
+    int pj[kMaxK];
+    float wj[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+        pj[j] = __shfl(p, j, kWave);
+        wj[j] = __shfl(wt, j, kWave);
+    }
+    const int nchunk = d / V::N;
+    for (int c = lane; c < nchunk; c += kWave) {
+        const int64_t col = static_cast<int64_t>(c) * V::N;
+        u32x4 src[kMaxK];
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j)
+            if (j < k && pj[j] >= 0) src[j] = load16(y_perm + static_cast<int64_t>(pj[j]) * d + col);
+        float acc[V::N];
+        if (y_sh != nullptr) {
+            V::unpack(load16(y_sh + t * d + col), acc);
+        } else {
+#pragma unroll
+            for (int u = 0; u < V::N; ++u) acc[u] = 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j) {
+            if (j < k && pj[j] >= 0) {
+                float v[V::N];
+                V::unpack(src[j], v);
+#pragma unroll
+                for (int u = 0; u < V::N; ++u) acc[u] = __builtin_fmaf(wj[j], v[u], acc[u]);
+            }
+        }
+        store16(y + t * d + col, V::pack(acc));
+    }
+}
+
+hipError_t launch_combine(const moe_shape& s, const void* y_perm, const void* y_sh,
+                          const int32_t* dest_row, const float* topk_w, void* y, hipStream_t st) {
+    const unsigned blocks = static_cast<unsigned>((s.T + 3) / 4);
+    const int64_t rows = s.T * s.k;
+    if (s.act == MOE_F32) {
+        combine_kernel<float><<<blocks, 256, 0, st>>>(
+            static_cast<const float*>(y_perm), static_cast<const float*>(y_sh), dest_row, topk_w,
+            s.T, s.d, s.k, rows, static_cast<float*>(y));
+    } else {
+        combine_kernel<bf16_t><<<blocks, 256, 0, st>>>(
+            static_cast<const bf16_t*>(y_perm), static_cast<const bf16_t*>(y_sh), dest_row, topk_w,
+            s.T, s.d, s.k, rows, static_cast<bf16_t*>(y));
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,299 @@
+// Host side of the C ABI declared in include/moe.h: argument validation,
+// workspace carving and the launch sequence. No call here allocates device
+// memory or synchronises, except moe_get_device_error (documented).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "moe.h"
+#include "moe_device.h"
+
+namespace moe {
+hipError_t launch_gate_topk(const moe_shape& s, const void* x, const void* wg, const float* bias,
+                            int32_t* idx, float* w, float* dbg, hipStream_t st);
+hipError_t launch_dispatch(const moe_shape& s, const void* x, const int32_t* topk_idx,
+                           int32_t* counts, int32_t* offsets, int32_t* dest_row,
+                           int32_t* src_token, void* x_perm, float* qparams, int32_t* rank,
+                           int32_t* blk, uint32_t* hdr, hipStream_t st, const Marks* mk);
+hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const float* qparams,
+                              const int32_t* offsets, const void* x, const void* w1,
+                              const void* w3, const void* w2, void* y_perm, void* y_shared,
+                              int32_t* plan, void* h_routed, void* h_shared, hipStream_t st,
+                              const Marks* mk);
+hipError_t launch_combine(const moe_shape& s, const void* y_perm, const void* y_sh,
+                          const int32_t* dest_row, const float* topk_w, void* y, hipStream_t st);
+
+__global__ void clear_header_kernel(uint32_t* hdr) { hdr[threadIdx.x] = 0u; }
+}  // namespace moe
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kHeaderBytes = 256;
+
+size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+size_t act_bytes(int32_t dt) { return dt == MOE_F32 ? 4 : (dt == MOE_BF16 ? 2 : 1); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Layout {
+    size_t rank = 0, blk = 0, plan = 0, x_perm = 0, qparams = 0, h_r = 0, h_s = 0, y_perm = 0,
+           y_sh = 0, total = 0;
+};
+
+Layout layout(const moe_shape& s, int stage) {
+    Layout L;
+    const size_t T = static_cast<size_t>(s.T), k = s.k, d = s.d, h = s.h, S = s.S, E = s.E;
+    const size_t es = act_bytes(s.act), esd = act_bytes(s.dispatch);
+    const size_t nblk = (T + kRankBlockTokens - 1) / kRankBlockTokens;
+    size_t off = kHeaderBytes;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = align256(off + bytes);
+        return at;
+    };
+    const bool disp = stage == MOE_STAGE_DISPATCH || stage == MOE_STAGE_FORWARD;
+    const bool ffn = stage == MOE_STAGE_FFN || stage == MOE_STAGE_FORWARD;
+    if (disp) {
+        L.rank = take(T * k * 4);
+        L.blk = take(nblk * E * 4);
+    }
+    if (ffn) {
+        L.plan = take((E + S + 2) * 4);
+        L.h_r = take(T * k * h * es);
+        L.h_s = take(T * S * h * es);
+    }
+    if (stage == MOE_STAGE_FORWARD) {
+        L.x_perm = take(T * k * d * esd);
+        L.qparams = take(s.dispatch == MOE_FP8_E4M3 ? T * k * 8 : 0);
+        L.y_perm = take(T * k * d * es);
+        L.y_sh = take(S > 0 ? T * d * es : 0);
+    }
+    L.total = (disp || ffn) ? off : 0;
+    return L;
+}
+
+// shape checks common to every entry point; `ffn` adds the GEMM tile limits
+int32_t check_shape(const moe_shape* s, bool ffn) {
+    if (s == nullptr) return MOE_ERR_INVALID_ARG;
+    if (s->T < 0 || s->d <= 0 || s->E <= 0 || s->k <= 0 || s->S < 0 || s->h <= 0 || s->k > s->E)
+        return MOE_ERR_INVALID_ARG;
+    if (s->E > kMaxE || s->k > kMaxK || s->S > kMaxS) return MOE_ERR_UNSUPPORTED;
+    if (s->act != MOE_F32 && s->act != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    const bool fp8 = s->dispatch == MOE_FP8_E4M3;
+    if (s->dispatch != s->act && !(fp8 && s->act == MOE_BF16)) return MOE_ERR_UNSUPPORTED;
+    if (s->act == MOE_F32 && s->d % 4 != 0) return MOE_ERR_UNSUPPORTED;
+    if (s->act == MOE_BF16 && s->d % (fp8 ? 16 : 8) != 0) return MOE_ERR_UNSUPPORTED;
+    if (ffn && s->act == MOE_BF16 && (s->d % 128 != 0 || s->h % 64 != 0))
+        return MOE_ERR_UNSUPPORTED;
+    if (s->T * s->k >= (int64_t(1) << 31) || s->T * (s->S + 1) >= (int64_t(1) << 31))
+        return MOE_ERR_UNSUPPORTED;
+    if (s->d > (1 << 20) || s->h > (1 << 20)) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+int32_t check_ptrs(std::initializer_list<const void*> required) {
+    for (const void* p : required)
+        if (p == nullptr || !aligned16(p)) return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+int32_t check_opt(std::initializer_list<const void*> optional) {
+    for (const void* p : optional)
+        if (p != nullptr && !aligned16(p)) return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+int32_t check_ws(const moe_shape& s, int stage, const void* ws, size_t ws_bytes) {
+    const size_t need = layout(s, stage).total;
+    if (need == 0) return MOE_OK;
+    if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return MOE_ERR_WORKSPACE;
+    if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+    return MOE_OK;
+}
+
+int32_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+template <typename T>
+T* at(void* ws, size_t off) {
+    return reinterpret_cast<T*>(static_cast<uint8_t*>(ws) + off);
+}
+
+#define MOE_TRY(expr)                       \
+    do {                                    \
+        const int32_t _rc = (expr);         \
+        if (_rc != MOE_OK) return _rc;      \
+    } while (0)
+
+int32_t forward_impl(const moe_shape* s, const void* x, const void* w_gate, const float* bias,
+                     const void* w1, const void* w3, const void* w2, void* y, int32_t* topk_idx,
+                     float* topk_w, int32_t* counts, int32_t* offsets, int32_t* dest_row,
+                     int32_t* src_token, void* ws, size_t ws_bytes, void* stream,
+                     const Marks* mk) {
+    MOE_TRY(check_shape(s, true));
+    if (s->T == 0) return MOE_OK;  // nothing to do; empty arrays may be null
+    MOE_TRY(check_ptrs({x, w_gate, w1, w3, w2, y, topk_idx, topk_w, counts, offsets, dest_row,
+                        src_token}));
+    MOE_TRY(check_opt({bias}));
+    MOE_TRY(check_ws(*s, MOE_STAGE_FORWARD, ws, ws_bytes));
+    const Layout L = layout(*s, MOE_STAGE_FORWARD);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    mark(mk);
+    MOE_TRY(hip_status(launch_gate_topk(*s, x, w_gate, bias, topk_idx, topk_w, nullptr, st)));
+    mark(mk);
+    const bool fp8 = s->dispatch == MOE_FP8_E4M3;
+    void* x_perm = at<void>(ws, L.x_perm);
+    float* qp = fp8 ? at<float>(ws, L.qparams) : nullptr;
+    MOE_TRY(hip_status(launch_dispatch(*s, x, topk_idx, counts, offsets, dest_row, src_token,
+                                       x_perm, qp, at<int32_t>(ws, L.rank),
+                                       at<int32_t>(ws, L.blk), at<uint32_t>(ws, 0), st, mk)));
+    void* y_perm = at<void>(ws, L.y_perm);
+    void* y_sh = s->S > 0 ? at<void>(ws, L.y_sh) : nullptr;
+    MOE_TRY(hip_status(launch_grouped_ffn(*s, x_perm, qp, offsets, x, w1, w3, w2, y_perm, y_sh,
+                                          at<int32_t>(ws, L.plan), at<void>(ws, L.h_r),
+                                          at<void>(ws, L.h_s), st, mk)));
+    MOE_TRY(hip_status(launch_combine(*s, y_perm, y_sh, dest_row, topk_w, y, st)));
+    mark(mk);
+    return MOE_OK;
+}
+
+const char* const kKernelNames[] = {"gate_topk",  "dispatch_rank", "dispatch_scan",
+                                    "dispatch_permute", "ffn_plan", "ffn_up",
+                                    "ffn_down",   "combine"};
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_bytes(const moe_shape* s, int32_t stage) {
+    if (stage < MOE_STAGE_GATE || stage > MOE_STAGE_FORWARD) return 0;
+    const bool ffn = stage == MOE_STAGE_FFN || stage == MOE_STAGE_FORWARD;
+    if (check_shape(s, ffn) != MOE_OK) return 0;
+    return layout(*s, stage).total;
+}
+
+int32_t moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+    if (ws == nullptr || ws_bytes < kHeaderBytes || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+        return MOE_ERR_WORKSPACE;
+    clear_header_kernel<<<1, kHeaderBytes / 4, 0, static_cast<hipStream_t>(stream)>>>(
+        static_cast<uint32_t*>(ws));
+    return hip_status(hipGetLastError());
+}
+
+const char* moe_status_string(int32_t status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument (null, misaligned or inconsistent)";
+        case MOE_ERR_UNSUPPORTED: return "unsupported shape or dtype combination";
+        case MOE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case MOE_ERR_HIP: return "HIP runtime error";
+        case MOE_ERR_BAD_INDEX: return "bad or repeated expert id in topk_idx";
+        default: return "unknown status";
+    }
+}
+
+int32_t moe_gate_topk(const moe_shape* s, const void* x, const void* w_gate, const float* bias,
+                      int32_t* topk_idx, float* topk_w, float* logits_dbg, void* stream) {
+    MOE_TRY(check_shape(s, false));
+    if (s->T == 0) return MOE_OK;
+    MOE_TRY(check_ptrs({x, w_gate, topk_idx, topk_w}));
+    MOE_TRY(check_opt({bias, logits_dbg}));
+    return hip_status(launch_gate_topk(*s, x, w_gate, bias, topk_idx, topk_w, logits_dbg,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_dispatch(const moe_shape* s, const void* x, const int32_t* topk_idx, int32_t* counts,
+                     int32_t* offsets, int32_t* dest_row, int32_t* src_token, void* x_perm,
+                     float* qparams, void* ws, size_t ws_bytes, void* stream) {
+    MOE_TRY(check_shape(s, false));
+    if (s->T == 0) return MOE_OK;
+    MOE_TRY(check_ptrs({x, topk_idx, counts, offsets, dest_row, src_token, x_perm}));
+    if (s->dispatch == MOE_FP8_E4M3) MOE_TRY(check_ptrs({qparams}));
+    MOE_TRY(check_opt({qparams}));
+    MOE_TRY(check_ws(*s, MOE_STAGE_DISPATCH, ws, ws_bytes));
+    const Layout L = layout(*s, MOE_STAGE_DISPATCH);
+    return hip_status(launch_dispatch(*s, x, topk_idx, counts, offsets, dest_row, src_token,
+                                      x_perm, qparams, at<int32_t>(ws, L.rank),
+                                      at<int32_t>(ws, L.blk), at<uint32_t>(ws, 0),
+                                      static_cast<hipStream_t>(stream), nullptr));
+}
+
+int32_t moe_grouped_ffn(const moe_shape* s, const void* x_perm, const float* qparams,
+                        const int32_t* offsets, const void* x, const void* w1, const void* w3,
+                        const void* w2, void* y_perm, void* y_shared, void* ws, size_t ws_bytes,
+                        void* stream) {
+    MOE_TRY(check_shape(s, true));
+    if (s->T == 0) return MOE_OK;
+    MOE_TRY(check_ptrs({x_perm, offsets, w1, w3, w2, y_perm}));
+    if (s->S > 0) MOE_TRY(check_ptrs({x, y_shared}));
+    else if (y_shared != nullptr) return MOE_ERR_INVALID_ARG;
+    if (s->dispatch == MOE_FP8_E4M3) MOE_TRY(check_ptrs({qparams}));
+    MOE_TRY(check_opt({x, qparams}));
+    MOE_TRY(check_ws(*s, MOE_STAGE_FFN, ws, ws_bytes));
+    const Layout L = layout(*s, MOE_STAGE_FFN);
+    return hip_status(launch_grouped_ffn(*s, x_perm, qparams, offsets, x, w1, w3, w2, y_perm,
+                                         y_shared, at<int32_t>(ws, L.plan), at<void>(ws, L.h_r),
+                                         at<void>(ws, L.h_s), static_cast<hipStream_t>(stream),
+                                         nullptr));
+}
+
+int32_t moe_combine(const moe_shape* s, const void* y_perm, const void* y_shared,
+                    const int32_t* dest_row, const float* topk_w, void* y, void* stream) {
+    MOE_TRY(check_shape(s, false));
+    if (s->T == 0) return MOE_OK;
+    MOE_TRY(check_ptrs({y_perm, dest_row, topk_w, y}));
+    MOE_TRY(check_opt({y_shared}));
+    return hip_status(launch_combine(*s, y_perm, y_shared, dest_row, topk_w, y,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_forward(const moe_shape* s, const void* x, const void* w_gate, const float* bias,
+                    const void* w1, const void* w3, const void* w2, void* y, int32_t* topk_idx,
+                    float* topk_w, int32_t* counts, int32_t* offsets, int32_t* dest_row,
+                    int32_t* src_token, void* ws, size_t ws_bytes, void* stream) {
+    return forward_impl(s, x, w_gate, bias, w1, w3, w2, y, topk_idx, topk_w, counts, offsets,
+                        dest_row, src_token, ws, ws_bytes, stream, nullptr);
+}
+
+int32_t moe_forward_traced(const moe_shape* s, const void* x, const void* w_gate,
+                           const float* bias, const void* w1, const void* w3, const void* w2,
+                           void* y, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                           int32_t* offsets, int32_t* dest_row, int32_t* src_token, void* ws,
+                           size_t ws_bytes, void* stream, void* const* events, int32_t n_events) {
+    if (events == nullptr || n_events < moe_forward_kernel_count(s) + 1) return MOE_ERR_INVALID_ARG;
+    for (int i = 0; i < n_events; ++i)
+        if (events[i] == nullptr) return MOE_ERR_INVALID_ARG;
+    Marks mk{reinterpret_cast<hipEvent_t const*>(events), n_events, 0,
+             static_cast<hipStream_t>(stream)};
+    return forward_impl(s, x, w_gate, bias, w1, w3, w2, y, topk_idx, topk_w, counts, offsets,
+                        dest_row, src_token, ws, ws_bytes, stream, &mk);
+}
+
+int32_t moe_forward_kernel_count(const moe_shape* s) {
+    (void)s;
+    return static_cast<int32_t>(sizeof(kKernelNames) / sizeof(kKernelNames[0]));
+}
+
+const char* moe_forward_kernel_name(const moe_shape* s, int32_t i) {
+    if (i < 0 || i >= moe_forward_kernel_count(s)) return nullptr;
+    if (i == 3 && s != nullptr && s->dispatch == MOE_FP8_E4M3) return "dispatch_permute_fp8";
+    return kKernelNames[i];
+}
+
+int32_t moe_get_device_error(void* ws, size_t ws_bytes, void* stream) {
+    if (ws == nullptr || ws_bytes < kHeaderBytes || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+        return MOE_ERR_WORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint32_t flag = 0;
+    if (hipMemcpyAsync(&flag, ws, sizeof flag, hipMemcpyDeviceToHost, st) != hipSuccess)
+        return MOE_ERR_HIP;
+    if (hipStreamSynchronize(st) != hipSuccess) return MOE_ERR_HIP;
+    clear_header_kernel<<<1, 1, 0, st>>>(static_cast<uint32_t*>(ws));
+    if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
+    return flag != 0 ? MOE_ERR_BAD_INDEX : MOE_OK;
+}
+
+}  // extern "C"

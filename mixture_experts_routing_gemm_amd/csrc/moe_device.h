@@ -1,0 +1,81 @@
+// Device-side helpers shared by the HIP kernels of the MoE layer (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+typedef uint16_t bf16_t;  // bf16 storage: the upper 16 bits of a float32
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kMaxK = 8;
+constexpr int kMaxE = 256;
+constexpr int kMaxS = 8;
+
+// tokens per dispatch ranking block (4 waves x 64 tokens)
+constexpr int kRankBlockTokens = 256;
+
+// workspace header words (the header is the first 256 bytes of a workspace)
+constexpr int kHdrErrorFlag = 0;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// round to nearest even (the gfx950 conversion instruction)
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+    return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ u32x4 load16(const void* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void store16(void* p, u32x4 v) {
+    *reinterpret_cast<u32x4*>(p) = v;
+}
+
+// wave-wide reductions over the 64 lanes
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+__device__ __forceinline__ void set_error(uint32_t* hdr, uint32_t bit) {
+    if (hdr) atomicOr(hdr + kHdrErrorFlag, bit);
+}
+
+// Host side: optional events recorded on the stream after each kernel, for
+// per-kernel timing of the whole-layer call.
+struct Marks {
+    hipEvent_t const* events;
+    int n;
+    mutable int next;
+    hipStream_t st;
+};
+inline void mark(const Marks* mk) {
+    if (mk != nullptr && mk->events != nullptr && mk->next < mk->n)
+        (void)hipEventRecord(mk->events[mk->next++], mk->st);
+}
+
+}  // namespace moe

@@ -1,0 +1,126 @@
+"""The C-ABI library loads, exports every declared symbol, and validates its
+arguments on the host (no GPU is touched by anything in this file)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+LIB = os.path.join(ROOT, "mixture_experts_routing_gemm_amd", "libmoe_mi355x.so")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def mm():
+    import mixture_experts_routing_gemm_amd as m
+    return m
+
+
+def test_library_exports_every_declared_symbol(mm):
+    names = declared_functions()
+    assert len(names) >= 12
+    lib = ctypes.CDLL(LIB)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(mm.EXPORTS)
+
+
+def test_status_strings(mm):
+    for st in (0, -1, -2, -3, -4, -5):
+        assert mm.status_string(st) and mm.status_string(st) != "unknown status"
+    assert mm.status_string(7) == "unknown status"
+
+
+def test_workspace_sizes(mm):
+    s = mm.make_shape(4096, 2048, 32, 8, 2, 1408, "bf16")
+    fwd = mm.moe_workspace_bytes(s, mm.STAGE_FORWARD)
+    # x_perm + y_perm + H (routed and shared) + y_sh at least
+    need = 4096 * 8 * 2048 * 2 * 2 + 4096 * (8 + 2) * 1408 * 2 + 4096 * 2048 * 2
+    assert need < fwd < need + (1 << 20)
+    assert mm.moe_workspace_bytes(s, mm.STAGE_GATE) == 0
+    assert mm.moe_workspace_bytes(s, mm.STAGE_COMBINE) == 0
+    assert 0 < mm.moe_workspace_bytes(s, mm.STAGE_DISPATCH) < (1 << 20)
+    bad = mm.make_shape(4096, 2048, 300, 8, 2, 1408, "bf16")
+    assert mm.moe_workspace_bytes(bad, mm.STAGE_FORWARD) == 0
+    assert mm.moe_workspace_bytes(s, 99) == 0
+
+
+def _raw(mm):
+    return mm._binding.lib
+
+
+FAKE = 0x100000  # an aligned, never-dereferenced address: every call below fails validation
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(E=300), -2), (dict(k=9, E=16), -2), (dict(k=5, E=4), -1), (dict(T=-1), -1),
+    (dict(S=9), -2), (dict(d=100), -2), (dict(h=100), -2), (dict(act=2), -2),
+    (dict(dispatch=2, act=0), -2), (dict(d=0), -1),
+])
+def test_forward_rejects_bad_shapes(mm, kw, status):
+    base = dict(T=64, d=256, E=8, k=2, S=1, h=128, act=1, dispatch=None)
+    base.update(kw)
+    s = mm.make_shape(base["T"], base["d"], base["E"], base["k"], base["S"], base["h"],
+                      base["act"], base["dispatch"])
+    p = ctypes.c_void_p(FAKE)
+    rc = _raw(mm).moe_forward(ctypes.byref(s), p, p, None, p, p, p, p, p, p, p, p, p, p, p,
+                              1 << 40, None)
+    assert rc == status
+
+
+def test_null_misaligned_and_workspace_errors(mm):
+    lib = _raw(mm)
+    s = mm.make_shape(64, 256, 8, 2, 0, 128, "bf16")
+    p = ctypes.c_void_p(FAKE)
+    odd = ctypes.c_void_p(FAKE + 8)
+    assert lib.moe_gate_topk(ctypes.byref(s), None, p, None, p, p, None, None) == -1
+    assert lib.moe_gate_topk(ctypes.byref(s), odd, p, None, p, p, None, None) == -1
+    assert lib.moe_gate_topk(None, p, p, None, p, p, None, None) == -1
+    # dispatch: workspace too small / missing / misaligned
+    assert lib.moe_dispatch(ctypes.byref(s), p, p, p, p, p, p, p, None, p, 16, None) == -3
+    assert lib.moe_dispatch(ctypes.byref(s), p, p, p, p, p, p, p, None, None, 1 << 30, None) == -3
+    assert lib.moe_dispatch(ctypes.byref(s), p, p, p, p, p, p, p, None,
+                            ctypes.c_void_p(FAKE + 16), 1 << 30, None) == -3
+    # fp8 dispatch needs qparams
+    s8 = mm.make_shape(64, 256, 8, 2, 0, 128, "bf16", "fp8")
+    assert lib.moe_dispatch(ctypes.byref(s8), p, p, p, p, p, p, p, None, p, 1 << 30, None) == -1
+    # shared experts need x and y_shared; no shared experts forbids y_shared
+    s1 = mm.make_shape(64, 256, 8, 2, 1, 128, "bf16")
+    assert lib.moe_grouped_ffn(ctypes.byref(s1), p, None, p, None, p, p, p, p, p, p, 1 << 30, None) == -1
+    assert lib.moe_grouped_ffn(ctypes.byref(s), p, None, p, None, p, p, p, p, p, p, 1 << 30, None) == -1
+    assert lib.moe_combine(ctypes.byref(s), p, None, None, p, p, None) == -1
+    assert lib.moe_workspace_init(None, 1024, None) == -3
+    assert lib.moe_get_device_error(None, 1024, None) == -3
+
+
+def test_zero_tokens_is_a_no_op(mm):
+    # T = 0 validates and returns OK without enqueuing anything
+    lib = _raw(mm)
+    s = mm.make_shape(0, 256, 8, 2, 1, 128, "bf16")
+    p = ctypes.c_void_p(FAKE)
+    assert lib.moe_gate_topk(ctypes.byref(s), p, p, None, p, p, None, None) == 0
+    assert lib.moe_combine(ctypes.byref(s), p, p, p, p, p, None) == 0
+    n = mm.moe_workspace_bytes(s, mm.STAGE_FORWARD)
+    assert lib.moe_forward(ctypes.byref(s), p, p, None, p, p, p, p, p, p, p, p, p, p, p, n, None) == 0
+
+
+def test_traced_forward_needs_enough_events(mm):
+    lib = _raw(mm)
+    s = mm.make_shape(64, 256, 8, 2, 1, 128, "bf16")
+    p = ctypes.c_void_p(FAKE)
+    n = mm.moe_forward_kernel_count(s)
+    ev = (ctypes.c_void_p * n)(*([FAKE] * n))
+    rc = lib.moe_forward_traced(ctypes.byref(s), p, p, None, p, p, p, p, p, p, p, p, p, p, p,
+                                1 << 40, None, ev, n)
+    assert rc == -1
+    assert mm.moe_forward_kernel_name(mm.make_shape(64, 256, 8, 2, 0, 128, "bf16", "fp8"), 3) == \
+        "dispatch_permute_fp8"
+    assert mm.moe_forward_kernel_name(s, n) is None

@@ -1,0 +1,139 @@
+"""GPU edge cases against the oracle at sizes it finishes in seconds: ragged
+token counts, a single token, one expert, k = E, the largest E and k, empty
+experts, constant rows on the fp8 path, float32 shapes off the tile grid, bad
+routing ids (turned into an error by the kernels' own checks), and T = 0."""
+
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import ORACLE_THREADS, act_torch, dev, host, rel_l2, requires_gpu, say
+from moe_workloads import CONFIGS, make_inputs, make_routing
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+
+def _mm():
+    import mixture_experts_routing_gemm_amd as mm
+    return mm
+
+
+def small_cfg(act="bf16", **kw):
+    base = CONFIGS["tiny_fp32" if act == "f32" else "deepseekmoe_bf16"]
+    kw.setdefault("sigma_w", 0.05)
+    return dataclasses.replace(base, name="edge", **kw)
+
+
+def forward_vs_oracle(inp):
+    mm, cfg = _mm(), inp.cfg
+    say(f"[edge] T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} S={cfg.S} h={cfg.h} act={cfg.act} "
+        f"dispatch={cfg.dispatch}")
+    shape = mm.shape_of(cfg)
+    buf = mm.ForwardBuffers(shape)
+    bias = None if inp.bias is None else dev(inp.bias)
+    buf.run(dev(inp.x), dev(inp.wg), bias, dev(inp.w1), dev(inp.w3), dev(inp.w2))
+    torch.cuda.synchronize()
+    assert mm.moe_get_device_error(buf.ws) == mm.MOE_OK
+    toks = np.arange(cfg.T)
+    oidx, ow, oy = oracle.layer_tokens(inp, toks, nthreads=ORACLE_THREADS)
+    counts, offsets, dest, src = oracle.dispatch(oidx, cfg.E)
+    assert np.array_equal(host(buf.topk_idx), oidx)
+    assert rel_l2(host(buf.topk_w), ow) <= 1e-5
+    assert np.array_equal(host(buf.counts), counts)
+    assert np.array_equal(host(buf.offsets), offsets)
+    assert np.array_equal(host(buf.dest_row), dest)
+    assert np.array_equal(host(buf.src_token)[: cfg.T * cfg.k], src)
+    err = rel_l2(host(buf.y), oy)
+    say(f"[edge] y rel-L2 {err:.3e}")
+    assert err <= cfg.tol_y
+    return buf, oidx
+
+
+@pytest.mark.parametrize("kw", [
+    dict(T=300, d=128, E=8, k=2, S=1, h=64),      # ragged T, partial tiles
+    dict(T=1, d=256, E=8, k=3, S=2, h=128),       # a single token
+    dict(T=257, d=128, E=1, k=1, S=0, h=64),      # one expert, one slot
+    dict(T=200, d=128, E=4, k=4, S=0, h=192),     # k = E
+    dict(T=700, d=128, E=256, k=8, S=2, h=64),    # largest E and k
+    dict(T=520, d=384, E=16, k=2, S=0, h=320),    # several n tiles, ragged experts
+], ids=["ragged", "one_token", "one_expert", "k_eq_E", "max_E_k", "wide"])
+def test_bf16_shapes(kw):
+    forward_vs_oracle(make_inputs(small_cfg(**kw), seed=1))
+
+
+@pytest.mark.parametrize("kw", [
+    dict(T=37, d=36, E=5, k=2, S=1, h=50),
+    dict(T=130, d=64, E=8, k=2, S=0, h=128),
+], ids=["odd_dims", "tiny_like"])
+def test_f32_shapes(kw):
+    forward_vs_oracle(make_inputs(small_cfg("f32", tol_y=1e-5, **kw), seed=2))
+
+
+def test_empty_experts_and_a_hot_expert():
+    cfg = small_cfg(T=1000, d=128, E=32, k=2, S=0, h=64)
+    inp = make_inputs(cfg, seed=3)
+    b = np.full(cfg.E, -50.0, dtype=np.float32)
+    b[[0, 5, 9]] = [40.0, 20.0, 20.0]
+    inp.bias = b
+    buf, oidx = forward_vs_oracle(inp)
+    counts = host(buf.counts)
+    assert counts[0] == cfg.T and (counts == 0).sum() >= 29
+
+
+def test_fp8_constant_rows_and_outliers():
+    cfg = small_cfg(T=260, d=256, E=8, k=3, S=1, h=128, dispatch="fp8", outlier_p=0.01,
+                    outlier_scale=50.0, tol_y=6e-2)
+    inp = make_inputs(cfg, seed=4)
+    inp.x[7] = inp.x[7, 0]      # constant row -> scale 0, codes 0
+    inp.x[100] = 0              # zero row
+    forward_vs_oracle(inp)
+
+
+def test_bad_routing_ids_raise_the_device_flag():
+    mm = _mm()
+    cfg = small_cfg(T=300, d=128, E=8, k=2, S=0, h=64)
+    inp = make_inputs(cfg, seed=5, gate_only=True)
+    idx = make_routing(cfg.T, cfg.E, cfg.k, seed=6)
+    bad = idx.copy()
+    bad[3, 1] = cfg.E          # out of range
+    bad[10, 0] = -1            # negative
+    bad[20, 1] = bad[20, 0]    # repeated expert
+    shape = mm.shape_of(cfg)
+    T, E, k = cfg.T, cfg.E, cfg.k
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    dest = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    src = torch.full((T * k,), -7, dtype=torch.int32, device="cuda")
+    x_perm = torch.zeros((T * k, cfg.d), dtype=torch.bfloat16, device="cuda")
+    ws = mm.alloc_workspace(shape, mm.STAGE_DISPATCH)
+    mm.moe_dispatch(shape, dev(inp.x), dev(bad), counts, offsets, dest, src, x_perm, None, ws)
+    assert mm.moe_get_device_error(ws) == mm.MOE_ERR_BAD_INDEX
+    assert mm.moe_get_device_error(ws) == mm.MOE_OK  # reading clears it
+    d = host(dest)
+    assert d[3, 1] == -1 and d[10, 0] == -1 and d[20, 1] == -1
+    valid = np.ones_like(bad, dtype=bool)
+    valid[3, 1] = valid[10, 0] = valid[20, 1] = False
+    exp_counts = np.bincount(bad[valid], minlength=E)
+    assert np.array_equal(host(counts), exp_counts)
+    assert host(offsets)[E] == valid.sum()
+    # every valid slot got a distinct row inside [0, valid.sum())
+    rows = d[valid]
+    assert np.array_equal(np.sort(rows), np.arange(valid.sum()))
+
+
+def test_zero_tokens():
+    mm = _mm()
+    cfg = small_cfg(T=0, d=128, E=8, k=2, S=1, h=64)
+    shape = mm.shape_of(cfg)
+    buf = mm.ForwardBuffers(shape)
+    x = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((9, 64, 128), dtype=torch.bfloat16, device="cuda")
+    w2 = torch.zeros((9, 128, 64), dtype=torch.bfloat16, device="cuda")
+    wg = torch.zeros((8, 128), dtype=torch.bfloat16, device="cuda")
+    buf.run(x, wg, None, w, w, w2)
+    torch.cuda.synchronize()

@@ -1,0 +1,245 @@
+"""GPU-vs-oracle parity on the five workloads, stage by stage and fused.
+
+Every call goes through the C ABI (the ctypes binding). Bars:
+  * bit-exact: gate logits, topk_idx, counts, offsets, dest_row, src_token,
+    the dispatched payload (a copy; fp8 codes and their (scale, centre));
+  * topk_w: relative L2 <= 1e-5 against the oracle's float64 weights;
+  * expert outputs and the layer output y: relative L2 <= the workload's
+    bound (1e-5 float32, 2e-2 bf16, 6e-2 fp8 dispatch) on sampled rows;
+  * combine alone: relative L2 <= 1e-6 (float32) or 2^-8 (bf16: one bf16
+    rounding of a float32 sum, relative error at most 2^-9 per element).
+Inputs of each stage come from the workload generator or from the oracle,
+never from the GPU path.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import ORACLE_THREADS, act_torch, as_f64, dev, host, rel_l2, requires_gpu, say
+from moe_workloads import CONFIG_ORDER, CONFIGS, make_inputs, make_rows
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+STAGES = ["gate", "dispatch", "ffn", "combine", "forward", "determinism"]
+
+_CACHE: dict = {}
+
+
+def _mm():
+    import mixture_experts_routing_gemm_amd as mm
+    return mm
+
+
+def get_case(name):
+    if name in _CACHE:
+        return _CACHE[name]
+    _CACHE.clear()
+    torch.cuda.empty_cache()
+    cfg = CONFIGS[name]
+    say(f"[case {name}] generating inputs T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} S={cfg.S} h={cfg.h}")
+    inp = make_inputs(cfg)
+    say(f"[case {name}] oracle gate + dispatch")
+    z = oracle.gate_logits(inp.x, inp.wg, inp.bias, nthreads=ORACLE_THREADS)
+    idx, w = oracle.select_topk(z, cfg.k)
+    counts, offsets, dest, src = oracle.dispatch(idx, cfg.E)
+    c = dict(cfg=cfg, inp=inp, z=z, idx=idx, w=w, counts=counts, offsets=offsets, dest=dest, src=src,
+             shape=_mm().shape_of(cfg), x=dev(inp.x), wg=dev(inp.wg),
+             bias=None if inp.bias is None else dev(inp.bias),
+             w1=dev(inp.w1), w3=dev(inp.w3), w2=dev(inp.w2))
+    _CACHE[name] = c
+    return c
+
+
+def sample_tokens(T, n=48, seed=0):
+    rng = np.random.default_rng(seed)
+    s = {0, 1, T // 2, T - 1} | set(rng.integers(0, T, n).tolist())
+    return np.array(sorted(t for t in s if 0 <= t < T), dtype=np.int64)
+
+
+def sample_rows(offsets, n=160, seed=0):
+    """First and last row of every non-empty expert block plus random rows."""
+    rng = np.random.default_rng(seed)
+    rows = set()
+    E = len(offsets) - 1
+    for e in range(E):
+        if offsets[e + 1] > offsets[e]:
+            rows.add(int(offsets[e]))
+            rows.add(int(offsets[e + 1] - 1))
+    rows |= set(rng.integers(0, offsets[E], n).tolist())
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def expert_of_rows(offsets, rows):
+    return (np.searchsorted(offsets, rows, side="right") - 1).astype(np.int32)
+
+
+def oracle_rows_input(c, tokens):
+    """float64 expert input rows for the given tokens (dequantised for fp8)."""
+    x = c["inp"].x[tokens]
+    if c["cfg"].dispatch == "fp8":
+        q, qp = oracle.fp8_quantize(x)
+        return oracle.fp8_dequantize(q, qp)
+    return oracle.rows_as_f64(x)
+
+
+# ------------------------------------------------------------------ stages --
+
+def run_gate(c):
+    mm, cfg = _mm(), c["cfg"]
+    T, E, k = cfg.T, cfg.E, cfg.k
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    z = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    mm.moe_gate_topk(c["shape"], c["x"], c["wg"], c["bias"], idx, w, z)
+    torch.cuda.synchronize()
+    zg = host(z)
+    nbad = int(np.sum(zg.view(np.uint32) != c["z"].view(np.uint32)))
+    assert nbad == 0, f"{nbad} logits differ from the oracle's float32 chain"
+    assert np.array_equal(host(idx), c["idx"])
+    assert rel_l2(host(w), c["w"]) <= 1e-5
+
+
+def run_dispatch(c):
+    mm, cfg = _mm(), c["cfg"]
+    T, E, k, d = cfg.T, cfg.E, cfg.k, cfg.d
+    fp8 = cfg.dispatch == "fp8"
+    idx = dev(c["idx"])
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    dest = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    src = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    if fp8:
+        x_perm = torch.empty((T * k, d), dtype=torch.uint8, device="cuda")
+        qp = torch.empty((T * k, 2), dtype=torch.float32, device="cuda")
+    else:
+        x_perm = torch.empty((T * k, d), dtype=act_torch(cfg.act), device="cuda")
+        qp = None
+    ws = mm.alloc_workspace(c["shape"], mm.STAGE_DISPATCH)
+    mm.moe_dispatch(c["shape"], c["x"], idx, counts, offsets, dest, src, x_perm, qp, ws)
+    assert mm.moe_get_device_error(ws) == mm.MOE_OK
+    assert np.array_equal(host(counts), c["counts"])
+    assert np.array_equal(host(offsets), c["offsets"])
+    assert np.array_equal(host(dest), c["dest"])
+    assert np.array_equal(host(src), c["src"])
+    src_dev = dev(c["src"].astype(np.int64))
+    if not fp8:
+        # the payload is a copy: x_perm == x[src_token], bit for bit
+        assert torch.equal(x_perm.view(torch.uint8), c["x"][src_dev].contiguous().view(torch.uint8))
+    else:
+        toks = sample_tokens(T, n=2000, seed=5)
+        q, qpo = oracle.fp8_quantize(c["inp"].x[toks], nthreads=ORACLE_THREADS)
+        rows = c["dest"][toks]  # [n, k]
+        xq = host(x_perm)
+        qpg = host(qp)
+        for j in range(k):
+            assert np.array_equal(xq[rows[:, j]], q), f"fp8 codes differ (slot {j})"
+            assert np.array_equal(qpg[rows[:, j]].view(np.uint32), qpo.view(np.uint32))
+
+
+def run_ffn(c):
+    mm, cfg = _mm(), c["cfg"]
+    T, k, d = cfg.T, cfg.k, cfg.d
+    fp8 = cfg.dispatch == "fp8"
+    src_dev = dev(c["src"].astype(np.int64))
+    if fp8:
+        say(f"[case {cfg.name}] oracle fp8 rows for the FFN input")
+        q, qpo = oracle.fp8_quantize(c["inp"].x, nthreads=ORACLE_THREADS)
+        x_perm = dev(q)[src_dev].contiguous()
+        qp = dev(qpo)[src_dev].contiguous()
+    else:
+        x_perm = c["x"][src_dev].contiguous()
+        qp = None
+    offsets = dev(c["offsets"])
+    y_perm = torch.empty((T * k, d), dtype=act_torch(cfg.act), device="cuda")
+    y_sh = torch.empty((T, d), dtype=act_torch(cfg.act), device="cuda") if cfg.S else None
+    ws = mm.alloc_workspace(c["shape"], mm.STAGE_FFN)
+    mm.moe_grouped_ffn(c["shape"], x_perm, qp, offsets, c["x"] if cfg.S else None,
+                       c["w1"], c["w3"], c["w2"], y_perm, y_sh, ws)
+    torch.cuda.synchronize()
+    rows = sample_rows(c["offsets"])
+    groups = expert_of_rows(c["offsets"], rows)
+    ref = oracle.expert_rows(oracle_rows_input(c, c["src"][rows]), groups, c["inp"].w1,
+                             c["inp"].w3, c["inp"].w2, nthreads=ORACLE_THREADS)
+    got = host(y_perm)[rows]
+    err = rel_l2(got, ref)
+    say(f"[case {cfg.name}] routed expert rows rel-L2 {err:.3e} over {len(rows)} rows")
+    assert err <= cfg.tol_y
+    if cfg.S:
+        toks = sample_tokens(T, n=24, seed=3)
+        xin = oracle.rows_as_f64(c["inp"].x[toks])
+        ref_sh = np.zeros((len(toks), d))
+        for s in range(cfg.S):
+            ref_sh += oracle.expert_rows(xin, np.full(len(toks), cfg.E + s, dtype=np.int32),
+                                         c["inp"].w1, c["inp"].w3, c["inp"].w2,
+                                         nthreads=ORACLE_THREADS)
+        err = rel_l2(host(y_sh)[toks], ref_sh)
+        say(f"[case {cfg.name}] shared experts rel-L2 {err:.3e}")
+        assert err <= cfg.tol_y
+
+
+def run_combine(c):
+    mm, cfg = _mm(), c["cfg"]
+    T, k, d = cfg.T, cfg.k, cfg.d
+    y_perm_np = make_rows(T * k, d, cfg.act, seed=11)
+    y_sh_np = make_rows(T, d, cfg.act, seed=12) if cfg.S else None
+    w32 = c["w"].astype(np.float32)
+    y = torch.empty((T, d), dtype=act_torch(cfg.act), device="cuda")
+    mm.moe_combine(c["shape"], dev(y_perm_np), None if y_sh_np is None else dev(y_sh_np),
+                   dev(c["dest"]), dev(w32), y)
+    torch.cuda.synchronize()
+    if T <= 4096:
+        toks = np.arange(T)
+        ref = oracle.combine(y_perm_np, y_sh_np, c["dest"], w32)
+    else:
+        toks = sample_tokens(T, n=4000, seed=2)
+        ref = oracle.combine(y_perm_np, None if y_sh_np is None else y_sh_np[toks],
+                             c["dest"][toks], w32[toks])
+    err = rel_l2(host(y)[toks], ref)
+    bound = 1e-6 if cfg.act == "f32" else 2.0 ** -8
+    say(f"[case {cfg.name}] combine rel-L2 {err:.3e} (bound {bound:.1e})")
+    assert err <= bound
+
+
+def run_forward(c, check_y=True):
+    mm, cfg = _mm(), c["cfg"]
+    buf = mm.ForwardBuffers(c["shape"])
+    buf.run(c["x"], c["wg"], c["bias"], c["w1"], c["w3"], c["w2"])
+    torch.cuda.synchronize()
+    assert mm.moe_get_device_error(buf.ws) == mm.MOE_OK
+    assert np.array_equal(host(buf.topk_idx), c["idx"])
+    assert rel_l2(host(buf.topk_w), c["w"]) <= 1e-5
+    assert np.array_equal(host(buf.counts), c["counts"])
+    assert np.array_equal(host(buf.offsets), c["offsets"])
+    assert np.array_equal(host(buf.dest_row), c["dest"])
+    assert np.array_equal(host(buf.src_token)[: cfg.T * cfg.k], c["src"])
+    if check_y:
+        toks = np.arange(cfg.T) if cfg.T <= 512 else sample_tokens(cfg.T, n=40, seed=9)
+        say(f"[case {cfg.name}] oracle layer on {len(toks)} tokens")
+        oidx, ow, oy = oracle.layer_tokens(c["inp"], toks, nthreads=ORACLE_THREADS)
+        assert np.array_equal(oidx, c["idx"][toks])
+        err = rel_l2(host(buf.y)[toks], oy)
+        say(f"[case {cfg.name}] layer output rel-L2 {err:.3e} (bound {cfg.tol_y:.0e})")
+        assert err <= cfg.tol_y
+    return buf
+
+
+def run_determinism(c):
+    a = run_forward(c, check_y=False)
+    ya = host(a.y).copy()
+    b = run_forward(c, check_y=False)
+    assert np.array_equal(host(b.y), ya)
+    assert np.array_equal(host(b.topk_w).view(np.uint32), host(a.topk_w).view(np.uint32))
+
+
+RUN = dict(gate=run_gate, dispatch=run_dispatch, ffn=run_ffn, combine=run_combine,
+           forward=run_forward, determinism=run_determinism)
+
+
+@pytest.mark.parametrize("name,stage", [(n, s) for n in CONFIG_ORDER for s in STAGES])
+def test_parity(name, stage):
+    say(f"[test] {name} {stage}")
+    RUN[stage](get_case(name))
