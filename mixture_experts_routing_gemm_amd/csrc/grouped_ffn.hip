@@ -19,6 +19,8 @@
 // the worst case and surplus work-groups exit at once. Work-group indices are
 // remapped so that each of the 8 XCDs walks a contiguous range of tiles, which
 // keeps an expert's weights and rows within one XCD's L2 as far as possible.
+#include <algorithm>
+
 #include "moe_device.h"
 
 namespace moe {
@@ -31,11 +33,14 @@ constexpr int kLdsStage = (kBM + kBN) * kBK * 2;  // bytes per pipeline stage
 constexpr int kF32BM = 64, kF32BN = 64, kF32BK = 16;
 
 // plan[g] = number of m-tiles of groups before g (g = 0..E+S); routed group g
-// has ceil(n_g / bm) m-tiles and each shared group ceil(T / bm).
+// has ceil(n_g / bm) m-tiles and each shared group ceil(T / bm). tile_group
+// (may be null) receives the group of every routed m-tile.
 __global__ __launch_bounds__(256) void ffn_plan_kernel(const int32_t* __restrict__ offsets,
                                                        int E, int S, int64_t T, int bm,
-                                                       int32_t* __restrict__ plan) {
+                                                       int32_t* __restrict__ plan,
+                                                       int32_t* __restrict__ tile_group) {
     __shared__ int mt[kMaxE + kMaxS];
+    __shared__ int pre[kMaxE + kMaxS + 1];
     const int G = E + S;
     for (int g = threadIdx.x; g < G; g += 256) {
         const int64_t n = g < E ? static_cast<int64_t>(offsets[g + 1] - offsets[g]) : T;
@@ -45,11 +50,17 @@ __global__ __launch_bounds__(256) void ffn_plan_kernel(const int32_t* __restrict
     if (threadIdx.x == 0) {
         int s = 0;
         for (int g = 0; g < G; ++g) {
+            pre[g] = s;
             plan[g] = s;
             s += mt[g];
         }
+        pre[G] = s;
         plan[G] = s;
     }
+    __syncthreads();
+    if (tile_group != nullptr)
+        for (int g = threadIdx.x; g < E; g += 256)
+            for (int m = 0; m < mt[g]; ++m) tile_group[pre[g] + m] = g;
 }
 
 struct GemmArgs {
@@ -58,6 +69,7 @@ struct GemmArgs {
     const uint8_t* a_shared;  // shared A rows: x [T, d] (up) or H_s [T, S*h] (down)
     const int32_t* offsets;   // [E+1]
     const int32_t* plan;      // [E+S+1]
+    const int32_t* tile_group;  // group of each routed m-tile (persistent kernel)
     const uint8_t* wa;        // up: W1 [G, h, d]; down: W2 [G, d, h]
     const uint8_t* wb;        // up: W3 [G, h, d]
     uint8_t* out_routed;      // up: H_r [T*k, h]; down: Y_perm [T*k, d]
@@ -99,11 +111,15 @@ __device__ __forceinline__ bool locate_tile(const GemmArgs& a, int mtg, int bm, 
     return true;
 }
 
-// byte offset of 16-byte chunk c of row r in a [rows][64] bf16 LDS tile,
-// XOR-swizzled so a wave's fragment reads spread over the banks
-__device__ __forceinline__ int lds_off(int r, int c) { return (r << 7) + ((c ^ (r & 7)) << 4); }
+// byte offset of 16-byte chunk c of row r in a [rows][64] bf16 LDS tile. The
+// XOR swizzle spreads the 16-byte reads of 8 (or 16) consecutive rows over
+// distinct banks for a 32-bank (or 64-bank) LDS.
+__device__ __forceinline__ int lds_off(int r, int c) {
+    return (r << 7) + ((c ^ ((r ^ (r >> 3)) & 7)) << 4);
+}
 
-__device__ __forceinline__ float silu(float v) { return v / (1.0f + __expf(-v)); }
+// silu(v) = v / (1 + e^-v), with the hardware reciprocal (about 1 ulp)
+__device__ __forceinline__ float silu(float v) { return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)); }
 
 // 8 e4m3 codes -> 8 bf16 values of code*scale + centre (one 16-byte chunk)
 __device__ __forceinline__ uint32_t dequant2(float lo, float hi, float scale, float centre) {
@@ -294,6 +310,368 @@ __global__ __launch_bounds__(kFfnThreads, 2) void ffn_gemm_kernel(GemmArgs a) {
     }
 }
 
+// ------------------------------------------------------ large-tile bf16 --
+// Persistent grouped GEMM: one 256-thread work-group per CU walks a list of
+// 256 x 256 output tiles (tokens x weight rows), K sliced by 32. Four waves
+// each own a 128 x 128 block, a 4 x 4 grid of 32x32x16 bf16 MFMAs.
+//  - Both operand slices go global -> LDS with the direct-to-LDS 16-byte loads
+//    into a 4-slot ring; each slice is requested three steps before it is
+//    read, and the waits count outstanding loads instead of draining them.
+//  - LDS fragments of the next 16-wide half-slice are read while the current
+//    one's MFMAs run.
+//  - The ring runs across tiles: the next tile's first slices are in flight
+//    while the current tile's epilogue runs, and no work-group is launched
+//    per tile.
+//  - Each XCD works through one contiguous range of tiles (tile order: m-tile
+//    major, n-tile minor), so concurrent work-groups on an XCD share an
+//    expert's weights and rows in that XCD's L2.
+// The weights are the MFMA's first operand: each lane's accumulator holds
+// four consecutive output features of one token, stored as one 8-byte word.
+// fp8 token rows stay as codes in LDS and are dequantised as fragments are
+// read.
+constexpr int kBigBM = 256, kBigBN = 256, kBigBK = 32, kBigSlots = 4;
+constexpr int kBigWM = 128, kBigWN = 128;
+constexpr int kBigMB = kBigWM / 32, kBigNB = kBigWN / 32;
+constexpr int kBigABytes = 2 * kBigBM * kBigBK;  // bf16 token rows (fp8 rows use half)
+constexpr int kBigBBytes = 2 * kBigBN * kBigBK;
+constexpr int kBigSlot = kBigABytes + kBigBBytes;
+// vector-memory instructions per wave per slice (fp8 slices are padded to it)
+constexpr int kBigLoads = kBigBM / 64 + kBigBN / 64;
+
+// byte offset of 16-byte chunk c (0..3) of row r in a [rows][32] bf16 tile;
+// conflict-free 16-byte reads of aligned runs of 8 rows (32 banks) or 16
+// rows (64 banks)
+__device__ __forceinline__ int lds_off32(int r, int c) {
+    return (r << 6) + ((c ^ (((r >> 1) & 3) ^ ((r >> 3) & 1))) << 4);
+}
+// byte offset of 8-code group g8 (0..3) of row r in a [rows][32] fp8 tile
+__device__ __forceinline__ int lds_off32_fp8(int r, int g8) {
+    return (r << 5) + (((g8 >> 1) ^ ((r >> 3) & 1)) << 4) + ((g8 & 1) << 3);
+}
+
+// Work-group barrier without the release/acquire fences of __syncthreads():
+// those would drain every outstanding load, including the prefetched slices.
+// The counted vmcnt wait before it orders the slice about to be read; the
+// empty asm keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void ring_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// s_waitcnt vmcnt(n) lgkmcnt(0) (gfx9 encoding): at most n vector-memory
+// instructions of this wave outstanding, and its LDS reads complete -- the
+// latter so that no ring slot can be refilled while a read of it is in flight
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);
+}
+
+// a wave-uniform pointer (lets the compiler keep it in SGPRs)
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+    return reinterpret_cast<const uint8_t*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+struct TileInfo {
+    int g, nt, m0, nrows, KT;
+    int64_t row_base;
+    bool shared;
+};
+
+// What one lane needs to fetch slices of one tile: wave-uniform bases and
+// 32-bit per-lane byte offsets (the launcher keeps every operand under 4 GiB
+// for this kernel). In the up-projection a wave's weight rows all come from
+// W1 (waves 0, 1) or all from W3 (waves 2, 3), so the weight base is uniform.
+struct TileSrc {
+    const uint8_t* abase;
+    const uint8_t* bbase;
+    uint32_t aoff[kBigBM / 64];  // token rows of this lane's DMA chunks
+    uint32_t boff[kBigBN / 64];  // weight rows of this lane's DMA chunks
+    float qs[kBigMB], qc[kBigMB];  // fp8 rows of this lane's fragments
+};
+
+template <int MODE>
+__device__ __forceinline__ TileInfo decode_tile(const GemmArgs& a, int L) {
+    TileInfo ti;
+    const int mtg = L / a.ntn;
+    ti.nt = L - mtg * a.ntn;
+    const int routed = a.plan[a.E];
+    if (mtg < routed) {
+        ti.g = a.tile_group[mtg];
+        ti.m0 = (mtg - a.plan[ti.g]) * kBigBM;
+        ti.row_base = a.offsets[ti.g];
+        ti.nrows = a.offsets[ti.g + 1] - a.offsets[ti.g];
+        ti.shared = false;
+    } else {
+        const int mtT = static_cast<int>((a.T + kBigBM - 1) / kBigBM);
+        const int q = mtg - routed;
+        ti.g = MODE == kModeDown ? a.E : a.E + q / mtT;
+        ti.m0 = (q % mtT) * kBigBM;
+        ti.row_base = 0;
+        ti.nrows = static_cast<int>(a.T);
+        ti.shared = true;
+    }
+    const int K = MODE == kModeDown ? (ti.shared ? a.S * a.h : a.h) : a.d;
+    ti.KT = K / kBigBK;
+    return ti;
+}
+
+template <int MODE>
+__device__ __forceinline__ void tile_sources(const GemmArgs& a, const TileInfo& ti, int wave,
+                                             int lane, TileSrc& src) {
+    const int wm = wave >> 1;
+    const int lr = lane & 31;
+    const bool fp8 = MODE == kModeUpFp8 && !ti.shared;
+    const int K = MODE == kModeDown ? (ti.shared ? a.S * a.h : a.h) : a.d;
+    const int last = ti.nrows - 1;
+    src.abase = ti.shared ? a.a_shared : a.a_routed;
+    // token DMA: a wave instruction fills 1 KB of LDS, lane i at byte 16*i:
+    // 16 bf16 rows of 64 B (row = i*64 + wave*16 + lane/4) or 32 fp8 rows of
+    // 32 B (row = i*128 + wave*32 + lane/2); each lane fetches the chunk the
+    // swizzle places at its position. Rows past the group's end re-read its
+    // last row; their outputs are never stored.
+#pragma unroll
+    for (int i = 0; i < kBigBM / 64; ++i) {
+        if (fp8) {
+            const int r = (i & 1) * 128 + wave * 32 + (lane >> 1);
+            const int c = (lane & 1) ^ ((r >> 3) & 1);
+            const int64_t row = ti.row_base + min(ti.m0 + r, last);
+            src.aoff[i] = static_cast<uint32_t>(row * K + c * 16);
+        } else {
+            const int r = i * 64 + wave * 16 + (lane >> 2);
+            const int c = (lane & 3) ^ (((r >> 1) & 3) ^ ((r >> 3) & 1));
+            const int64_t row = ti.row_base + min(ti.m0 + r, last);
+            src.aoff[i] = static_cast<uint32_t>(row * K * 2 + c * 16);
+        }
+    }
+#pragma unroll
+    for (int mb = 0; mb < kBigMB; ++mb) {
+        src.qs[mb] = 0.0f;
+        src.qc[mb] = 0.0f;
+        if (fp8) {
+            const int64_t row = ti.row_base + min(ti.m0 + wm * kBigWM + mb * 32 + lr, last);
+            src.qs[mb] = a.qparams[2 * row];
+            src.qc[mb] = a.qparams[2 * row + 1];
+        }
+    }
+    if (MODE == kModeDown) {
+        src.bbase = a.wa + static_cast<int64_t>(ti.shared ? a.E : ti.g) * a.d * a.h * 2;
+    } else {
+        src.bbase = ((wave >> 1) ? a.wb : a.wa) + static_cast<int64_t>(ti.g) * a.h * a.d * 2;
+    }
+#pragma unroll
+    for (int i = 0; i < kBigBN / 64; ++i) {
+        const int br = i * 64 + wave * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ (((br >> 1) & 3) ^ ((br >> 3) & 1));
+        if (MODE == kModeDown) {
+            const int n = ti.nt * kBigBN + br;
+            src.boff[i] = static_cast<uint32_t>(n) * a.h * 2 + c * 16;
+        } else {
+            // weight row br of the tile: 32-row blocks alternate W1 / W3
+            const int n = ti.nt * (kBigBN / 2) + ((br >> 5) >> 1) * 32 + (br & 31);
+            src.boff[i] = static_cast<uint32_t>(n) * a.d * 2 + c * 16;
+        }
+    }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void ffn_gemm_persistent_kernel(GemmArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    constexpr int MB = kBigMB, NB = kBigNB;
+    constexpr bool kFp8 = MODE == kModeUpFp8;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int wn = wave & 1, wm = wave >> 1;
+    const int lr = lane & 31, lg = lane >> 5;
+
+    // this work-group's tiles: XCD x takes the x-th eighth of the tile list,
+    // its work-groups interleave within it
+    const int routed = a.plan[a.E];
+    const int mtT = static_cast<int>((a.T + kBigBM - 1) / kBigBM);
+    const int nshared = MODE == kModeDown ? (a.S > 0 ? 1 : 0) : a.S;
+    const int total = (routed + nshared * mtT) * a.ntn;
+    const int xcd = blockIdx.x & 7, per_xcd = gridDim.x >> 3;
+    const int chunk = (total + 7) >> 3;
+    const int lo = xcd * chunk, hi = min(total, lo + chunk);
+    int L = lo + (blockIdx.x >> 3);
+    if (L >= hi) return;
+
+    TileInfo cur = decode_tile<MODE>(a, L);
+    TileSrc src;
+    tile_sources<MODE>(a, cur, wave, lane, src);
+    TileInfo nxt = cur;
+    TileSrc nsrc = src;
+    bool has_next = false;
+
+    // slice k of a tile into ring slot `slot`
+    auto issue = [&](const TileSrc& ts, bool shared, int k, int slot) {
+        const int k0 = k * kBigBK;
+        uint8_t* As = lds + slot * kBigSlot;
+        uint8_t* Bs = As + kBigABytes;
+        const uint8_t* bb = uniform_ptr(ts.bbase) + static_cast<int64_t>(k0) * 2;
+        if (MODE == kModeDown && shared) {
+            const int seg = k0 / a.h;
+            bb = uniform_ptr(ts.bbase) + static_cast<int64_t>(seg) * a.d * a.h * 2 +
+                 static_cast<int64_t>(k0 - seg * a.h) * 2;
+        }
+        const uint8_t* ab = uniform_ptr(ts.abase);
+        if (kFp8 && !shared) {
+#pragma unroll
+            for (int i = 0; i < kBigBM / 128; ++i)
+                __builtin_amdgcn_global_load_lds(ab + (ts.aoff[i] + k0), As + (i * 128 + wave * 32) * 32, 16, 0, 0);
+            // two more loads keep the per-slice count equal to the bf16 case;
+            // they rewrite weight rows with the same bytes
+#pragma unroll
+            for (int i = 0; i < kBigBM / 128; ++i)
+                __builtin_amdgcn_global_load_lds(bb + ts.boff[i], Bs + (i * 64 + wave * 16) * 64, 16, 0, 0);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kBigBM / 64; ++i)
+                __builtin_amdgcn_global_load_lds(ab + (ts.aoff[i] + k0 * 2), As + (i * 64 + wave * 16) * 64, 16, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < kBigBN / 64; ++i)
+            __builtin_amdgcn_global_load_lds(bb + ts.boff[i], Bs + (i * 64 + wave * 16) * 64, 16, 0, 0);
+    };
+    // LDS -> register fragments of 16-wide half-slice ks of a slot
+    auto load_frags = [&](int slot, int ks, bf16x8* fa, bf16x8* fb, const TileSrc& ts, bool shared) {
+        const uint8_t* As = lds + slot * kBigSlot;
+        const uint8_t* Bs = As + kBigABytes;
+        const int ch = ks * 2 + lg;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+            fb[nb] = *reinterpret_cast<const bf16x8*>(Bs + lds_off32(wn * kBigWN + nb * 32 + lr, ch));
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int r = wm * kBigWM + mb * 32 + lr;
+            if (kFp8 && !shared) {
+                const uint2 codes = *reinterpret_cast<const uint2*>(As + lds_off32_fp8(r, ch));
+                fa[mb] = __builtin_bit_cast(bf16x8, dequant8(codes, ts.qs[mb], ts.qc[mb]));
+            } else {
+                fa[mb] = *reinterpret_cast<const bf16x8*>(As + lds_off32(r, ch));
+            }
+        }
+    };
+
+    f32x16 acc[MB][NB];
+    auto mma = [&](const bf16x8* fa, const bf16x8* fb) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[nb], fa[mb], acc[mb][nb], 0, 0, 0);
+    };
+
+    // prologue: the first tile's slices 0..2
+    issue(src, cur.shared, 0, 0);
+    issue(src, cur.shared, 1, 1);
+    issue(src, cur.shared, 2, 2);
+
+    bf16x8 fa0[MB], fb0[NB], fa1[MB], fb1[NB];
+    while (true) {
+        // next tile of this work-group, decoded while this one computes
+        const int Ln = L + per_xcd;
+        has_next = Ln < hi;
+        if (has_next) {
+            nxt = decode_tile<MODE>(a, Ln);
+            tile_sources<MODE>(a, nxt, wave, lane, nsrc);
+        }
+        wait_vmcnt<2 * kBigLoads>();  // slice 0 of this tile has landed
+        ring_barrier();
+        load_frags(0, 0, fa0, fb0, src, cur.shared);
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+        const int KT = cur.KT;
+        // one step: compute slice k (slot j), request slice k+3 (of this
+        // tile or, near its end, of the next one)
+        auto step = [&](int k, int j) {
+            if (k + 3 < KT)
+                issue(src, cur.shared, k + 3, (j + 3) & 3);
+            else if (has_next)
+                issue(nsrc, nxt.shared, k + 3 - KT, (j + 3) & 3);
+            load_frags(j, 1, fa1, fb1, src, cur.shared);
+            mma(fa0, fb0);
+            if (k + 1 < KT) {
+                // slice k+1 must have landed; slices k+2, k+3 may still fly
+                const bool k3 = k + 3 < KT || has_next;
+                const bool k2 = k + 2 < KT || has_next;
+                if (k3)
+                    wait_vmcnt<2 * kBigLoads>();
+                else if (k2)
+                    wait_vmcnt<kBigLoads>();
+                else
+                    wait_vmcnt<0>();
+                ring_barrier();
+                load_frags((j + 1) & 3, 0, fa0, fb0, src, cur.shared);
+            }
+            mma(fa1, fb1);
+        };
+        for (int k = 0; k < KT; k += 4) {
+            step(k, 0);
+            step(k + 1, 1);
+            step(k + 2, 2);
+            step(k + 3, 3);
+        }
+
+        // epilogue: acc[mb][nb][v] is token (m0 + wm*128 + mb*32 + lr) and
+        // weight row (wn*128 + nb*32 + 8*(v/4) + 4*lg + v%4) of the tile
+        bf16_t* out = reinterpret_cast<bf16_t*>(cur.shared ? a.out_shared : a.out_routed);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int r = cur.m0 + wm * kBigWM + mb * 32 + lr;
+            if (r >= cur.nrows) continue;
+            const int64_t row = cur.row_base + r;
+            if (MODE == kModeDown) {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int col = cur.nt * kBigBN + wn * kBigWN + nb * 32 + 8 * q + 4 * lg;
+                        uint2 w;
+                        w.x = pack_bf16x2(acc[mb][nb][4 * q], acc[mb][nb][4 * q + 1]);
+                        w.y = pack_bf16x2(acc[mb][nb][4 * q + 2], acc[mb][nb][4 * q + 3]);
+                        *reinterpret_cast<uint2*>(out + row * a.d + col) = w;
+                    }
+            } else {
+                const int ldo = cur.shared ? a.S * a.h : a.h;
+                const int cbase = (cur.shared ? (cur.g - a.E) * a.h : 0) + cur.nt * (kBigBN / 2) +
+                                  wn * (kBigWN / 2);
+#pragma unroll
+                for (int pq = 0; pq < NB / 2; ++pq)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int col = cbase + pq * 32 + 8 * q + 4 * lg;
+                        float hv[4];
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+                            hv[u] = silu(acc[mb][2 * pq][4 * q + u]) * acc[mb][2 * pq + 1][4 * q + u];
+                        uint2 w;
+                        w.x = pack_bf16x2(hv[0], hv[1]);
+                        w.y = pack_bf16x2(hv[2], hv[3]);
+                        *reinterpret_cast<uint2*>(out + row * ldo + col) = w;
+                    }
+            }
+        }
+        if (!has_next) break;
+        // the epilogue's stores also count in vmcnt: drain before the next
+        // tile's counted waits
+        wait_vmcnt<0>();
+        L = Ln;
+        cur = nxt;
+        src = nsrc;
+    }
+}
+
 // ---------------------------------------------------------------- float32 --
 // Plain float32 FFN for act = MOE_F32 (vector FMA; the bf16 matrix cores
 // cannot reach float32 accuracy). 64x64 output tiles, 4x4 per thread.
@@ -400,7 +778,43 @@ int64_t max_mtiles(const moe_shape& s, int bm, bool down) {
 
 }  // namespace
 
-size_t ffn_lds_bytes() { return 2 * kLdsStage; }
+// the persistent kernels need 128 KB of LDS (the 4-slot ring)
+template <int MODE>
+hipError_t allow_big_lds() {
+    static hipError_t err = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&ffn_gemm_persistent_kernel<MODE>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, kBigSlots * kBigSlot);
+    return err;
+}
+
+int device_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+template <int MODE>
+hipError_t launch_gemm(const GemmArgs& a, int64_t mtiles, bool big, hipStream_t st) {
+    if (big) {
+        const hipError_t e = allow_big_lds<MODE>();
+        if (e != hipSuccess) return e;
+        int64_t blocks = std::min<int64_t>(device_cus(), mtiles * a.ntn);
+        blocks = (blocks + 7) & ~int64_t(7);
+        ffn_gemm_persistent_kernel<MODE><<<static_cast<unsigned>(blocks), 256, kBigSlots * kBigSlot, st>>>(a);
+    } else {
+        int64_t blocks = mtiles * a.ntn;
+        blocks = (blocks + 7) & ~int64_t(7);
+        ffn_gemm_kernel<MODE><<<static_cast<unsigned>(blocks), kFfnThreads, 2 * kLdsStage, st>>>(a);
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const float* qparams,
                               const int32_t* offsets, const void* x, const void* w1,
@@ -408,14 +822,24 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const floa
                               int32_t* plan, void* h_routed, void* h_shared, hipStream_t st,
                               const Marks* mk) {
     const bool f32 = s.act == MOE_F32;
-    const int bm = f32 ? kF32BM : kBM;
-    ffn_plan_kernel<<<1, 256, 0, st>>>(offsets, s.E, s.S, s.T, bm, plan);
+    // large tiles when both projections divide evenly into them (and K into
+    // whole groups of four slices)
+    const uint64_t rows = static_cast<uint64_t>(s.T) * (s.k + s.S);
+    const uint64_t wbytes = static_cast<uint64_t>(s.E + s.S) * s.d * s.h * 2;
+    const bool fits32 = rows * s.d * 2 < (uint64_t(1) << 32) && rows * s.h * 2 < (uint64_t(1) << 32) &&
+                        wbytes < (uint64_t(1) << 32);
+    const bool big = !f32 && fits32 && s.h % (kBigBN / 2) == 0 && s.d % kBigBN == 0 &&
+                     s.d % (4 * kBigBK) == 0 && s.h % (4 * kBigBK) == 0;
+    const int bm = f32 ? kF32BM : (big ? kBigBM : kBM);
+    int32_t* tile_group = plan + (s.E + s.S + 1);
+    ffn_plan_kernel<<<1, 256, 0, st>>>(offsets, s.E, s.S, s.T, bm, plan, big ? tile_group : nullptr);
     mark(mk);
 
     GemmArgs a;
     a.qparams = qparams;
     a.offsets = offsets;
     a.plan = plan;
+    a.tile_group = tile_group;
     a.T = s.T;
     a.E = s.E;
     a.S = s.S;
@@ -429,21 +853,19 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const floa
     a.wb = static_cast<const uint8_t*>(w3);
     a.out_routed = static_cast<uint8_t*>(h_routed);
     a.out_shared = static_cast<uint8_t*>(h_shared);
+    hipError_t err;
     if (f32) {
         a.ntn = (s.h + kF32BN - 1) / kF32BN;
         const int64_t mt = max_mtiles(s, kF32BM, false);
         ffn_gemm_f32_kernel<true><<<static_cast<unsigned>(mt * a.ntn), 256, 0, st>>>(a, 0);
+        err = hipGetLastError();
     } else {
-        a.ntn = s.h / (kBN / 2);
-        int64_t blocks = max_mtiles(s, kBM, false) * a.ntn;
-        blocks = (blocks + 7) & ~int64_t(7);
-        if (s.dispatch == MOE_FP8_E4M3)
-            ffn_gemm_kernel<kModeUpFp8><<<static_cast<unsigned>(blocks), kFfnThreads, 2 * kLdsStage, st>>>(a);
-        else
-            ffn_gemm_kernel<kModeUp><<<static_cast<unsigned>(blocks), kFfnThreads, 2 * kLdsStage, st>>>(a);
+        a.ntn = 2 * s.h / (big ? kBigBN : kBN);
+        const int64_t mt = max_mtiles(s, bm, false);
+        err = s.dispatch == MOE_FP8_E4M3 ? launch_gemm<kModeUpFp8>(a, mt, big, st)
+                                         : launch_gemm<kModeUp>(a, mt, big, st);
     }
     mark(mk);
-    hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
 
     // down-projection
@@ -457,14 +879,13 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const floa
         a.ntn = (s.d + kF32BN - 1) / kF32BN;
         const int64_t mt = max_mtiles(s, kF32BM, true);
         ffn_gemm_f32_kernel<false><<<static_cast<unsigned>(mt * a.ntn), 256, 0, st>>>(a, 0);
+        err = hipGetLastError();
     } else {
-        a.ntn = s.d / kBN;
-        int64_t blocks = max_mtiles(s, kBM, true) * a.ntn;
-        blocks = (blocks + 7) & ~int64_t(7);
-        ffn_gemm_kernel<kModeDown><<<static_cast<unsigned>(blocks), kFfnThreads, 2 * kLdsStage, st>>>(a);
+        a.ntn = s.d / (big ? kBigBN : kBN);
+        err = launch_gemm<kModeDown>(a, max_mtiles(s, bm, true), big, st);
     }
     mark(mk);
-    return hipGetLastError();
+    return err;
 }
 
 }  // namespace moe

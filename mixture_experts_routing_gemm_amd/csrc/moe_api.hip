@@ -62,7 +62,8 @@ Layout layout(const moe_shape& s, int stage) {
         L.blk = take(nblk * E * 4);
     }
     if (ffn) {
-        L.plan = take((E + S + 2) * 4);
+        // m-tile prefix [E+S+1] and the group of each routed m-tile
+        L.plan = take((E + S + 2 + T * k / 128 + E) * 4);
         L.h_r = take(T * k * h * es);
         L.h_s = take(T * S * h * es);
     }
