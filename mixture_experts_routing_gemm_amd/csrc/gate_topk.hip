@@ -17,7 +17,12 @@
 namespace moe {
 
 constexpr int kGateThreads = 256;
-constexpr int kGateKC = 32;  // K elements staged in LDS per step
+constexpr int kGateSub = 32;   // K steps unrolled at a time
+constexpr int kGateNReg = 6;   // staging registers (16 B each) per thread, bf16 input
+// float32 rows hold half as many elements per register; give them twice as many
+template <typename TIn>
+constexpr int gate_nreg() { return sizeof(TIn) == 4 ? 2 * kGateNReg : kGateNReg; }
+constexpr size_t kGateMaxLds = 160 * 1024;
 
 template <typename TIn>
 __device__ __forceinline__ void chunk_to_f32(u32x4 raw, float* v);
@@ -42,79 +47,127 @@ __device__ __forceinline__ bool ranks_before(float za, int ia, float zb, int ib)
     return za > zb || (za == zb && ia < ib);
 }
 
-// Thread layout: EGP = 2^egp_log2 groups of 4 experts across the threads'
+// Thread layout: EGP = 2^egp_log2 groups of ME experts across the threads'
 // low bits, TG = 256/EGP token groups of MT tokens each. A block handles
-// TT = TG*MT tokens and all E experts (padded to EP = 4*EGP).
-template <typename TIn, int MT>
+// TT = TG*MT tokens and all E experts (padded to EP = ME*EGP). K advances in
+// chunks of KC staged in LDS as K-contiguous float rows (double-buffered
+// through registers). One 16-byte LDS read gives an operand for 4 K steps;
+// the reads for 32 steps are issued before their FMAs, and each thread runs
+// MT*ME independent chains, each strictly in K order.
+template <typename TIn, int MT, int ME>
 __global__ __launch_bounds__(kGateThreads) void gate_topk_kernel(
     const TIn* __restrict__ x, const TIn* __restrict__ wg, const float* __restrict__ bias,
-    int64_t T, int d, int E, int k, int egp_log2, int32_t* __restrict__ topk_idx,
+    int64_t T, int d, int E, int k, int egp_log2, int KC, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, float* __restrict__ logits_dbg) {
     constexpr int VEC = 16 / sizeof(TIn);  // elements per 16-byte chunk
-    constexpr int CPR = kGateKC / VEC;     // chunks per staged row
+    const int CPR = KC / VEC;              // chunks per staged row (KC: multiple of 32)
+    const int LD = KC + 4;                 // padded LDS row (floats)
     const int EGP = 1 << egp_log2;
-    const int EP = EGP * 4;
+    const int EP = EGP * ME;
     const int TT = (kGateThreads >> egp_log2) * MT;
+    const int stage = LD * (TT + EP);  // floats per LDS buffer
 
     extern __shared__ float smem[];
-    float* xs = smem;                 // [KC][TT]
-    float* ws = smem + kGateKC * TT;  // [KC][EP]
 
     const int tid = threadIdx.x;
     const int eg = tid & (EGP - 1);
     const int tg = tid >> egp_log2;
     const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TT;
 
-    float acc[MT][4];
+    // staging: this thread's share of the (TT + EP) x CPR chunks of a K chunk
+    const int nchunks = (TT + EP) * CPR;
+    const int per_thread = (nchunks + kGateThreads - 1) / kGateThreads;  // <= NREG (launcher)
+    constexpr int NREG = gate_nreg<TIn>();
+    u32x4 reg[NREG];
+    auto fetch = [&](int i0) {
+        const int kc = min(KC, d - i0);
+#pragma unroll
+        for (int u = 0; u < NREG; ++u) {
+            const int q = tid + u * kGateThreads;
+            reg[u] = u32x4{0u, 0u, 0u, 0u};
+            if (u < per_thread && q < nchunks) {
+                const int r = q / CPR, c = q % CPR;
+                if (c * VEC < kc) {
+                    if (r < TT) {
+                        const int64_t t = t0 + r;
+                        if (t < T) reg[u] = load16(x + t * d + i0 + c * VEC);
+                    } else if (r - TT < E) {
+                        reg[u] = load16(wg + static_cast<int64_t>(r - TT) * d + i0 + c * VEC);
+                    }
+                }
+            }
+        }
+    };
+    // rows 0..TT-1 are tokens, TT..TT+EP-1 experts; row r, K offset j at r*LD + j
+    auto stash = [&](int buf) {
+        float* rows = smem + buf * stage;
+#pragma unroll
+        for (int u = 0; u < NREG; ++u) {
+            const int q = tid + u * kGateThreads;
+            if (u < per_thread && q < nchunks) {
+                const int r = q / CPR, c = q % CPR;
+                float v[VEC];
+                chunk_to_f32<TIn>(reg[u], v);
+                f32x4* dst = reinterpret_cast<f32x4*>(rows + r * LD + c * VEC);
+#pragma unroll
+                for (int w = 0; w < VEC / 4; ++w)
+                    dst[w] = f32x4{v[4 * w], v[4 * w + 1], v[4 * w + 2], v[4 * w + 3]};
+            }
+        }
+    };
+
+    float acc[MT][ME];
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[m][c] = 0.0f;
+        for (int c = 0; c < ME; ++c) acc[m][c] = 0.0f;
 
-    for (int i0 = 0; i0 < d; i0 += kGateKC) {
-        const int kc = min(kGateKC, d - i0);
-        const int cpr = kc / VEC;
-        for (int q = tid; q < TT * CPR; q += kGateThreads) {
-            const int r = q / CPR, c = q % CPR;
-            if (c < cpr) {
-                float v[VEC];
-                const int64_t t = t0 + r;
-                if (t < T) {
-                    chunk_to_f32<TIn>(load16(x + t * d + i0 + c * VEC), v);
-                } else {
+    // 32 K steps from kk: operands for all of them first, then the FMAs
+    auto fma32 = [&](const float* rows, int kk) {
+        f32x4 xq[8][MT], wq[8][ME];
 #pragma unroll
-                    for (int u = 0; u < VEC; ++u) v[u] = 0.0f;
-                }
-#pragma unroll
-                for (int u = 0; u < VEC; ++u) xs[(c * VEC + u) * TT + r] = v[u];
-            }
-        }
-        for (int q = tid; q < EP * CPR; q += kGateThreads) {
-            const int e = q / CPR, c = q % CPR;
-            if (c < cpr) {
-                float v[VEC];
-                if (e < E) {
-                    chunk_to_f32<TIn>(load16(wg + static_cast<int64_t>(e) * d + i0 + c * VEC), v);
-                } else {
-#pragma unroll
-                    for (int u = 0; u < VEC; ++u) v[u] = 0.0f;
-                }
-#pragma unroll
-                for (int u = 0; u < VEC; ++u) ws[(c * VEC + u) * EP + e] = v[u];
-            }
-        }
-        __syncthreads();
-        for (int kk = 0; kk < kc; ++kk) {
-            float xv[MT];
-#pragma unroll
-            for (int m = 0; m < MT; ++m) xv[m] = xs[kk * TT + tg * MT + m];
-            const f32x4 wv = *reinterpret_cast<const f32x4*>(ws + kk * EP + eg * 4);
+        for (int j = 0; j < 8; ++j) {
 #pragma unroll
             for (int m = 0; m < MT; ++m)
+                xq[j][m] = *reinterpret_cast<const f32x4*>(rows + (tg * MT + m) * LD + kk + 4 * j);
 #pragma unroll
-                for (int c = 0; c < 4; ++c) acc[m][c] = __builtin_fmaf(xv[m], wv[c], acc[m][c]);
+            for (int c = 0; c < ME; ++c)
+                wq[j][c] = *reinterpret_cast<const f32x4*>(rows + (TT + eg * ME + c) * LD + kk + 4 * j);
         }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+#pragma unroll
+                    for (int c = 0; c < ME; ++c)
+                        acc[m][c] = __builtin_fmaf(xq[j][m][q], wq[j][c][q], acc[m][c]);
+    };
+    auto fma1 = [&](const float* rows, int kk) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int c = 0; c < ME; ++c)
+                acc[m][c] = __builtin_fmaf(rows[(tg * MT + m) * LD + kk], rows[(TT + eg * ME + c) * LD + kk],
+                                           acc[m][c]);
+    };
+
+    fetch(0);
+    stash(0);
+    __syncthreads();
+    int buf = 0;
+    for (int i0 = 0; i0 < d; i0 += KC) {
+        const int kc = min(KC, d - i0);
+        const bool more = i0 + KC < d;
+        if (more) fetch(i0 + KC);  // global loads in flight during the FMAs
+        const float* rows = smem + buf * stage;
+        int kk = 0;
+        for (; kk + kGateSub <= kc; kk += kGateSub) fma32(rows, kk);
+        for (; kk < kc; ++kk) fma1(rows, kk);
+        if (more) stash(buf ^ 1);
         __syncthreads();
+        buf ^= 1;
     }
 
     // logits to LDS (reusing the staging space) and optionally to memory
@@ -125,8 +178,8 @@ __global__ __launch_bounds__(kGateThreads) void gate_topk_kernel(
         const int r = tg * MT + m;
         const int64_t t = t0 + r;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int e = eg * 4 + c;
+        for (int c = 0; c < ME; ++c) {
+            const int e = eg * ME + c;
             float z = acc[m][c];
             if (bias != nullptr && e < E) z = z + bias[e];
             zs[r * zld + e] = z;
@@ -183,51 +236,106 @@ __global__ __launch_bounds__(kGateThreads) void gate_topk_kernel(
 namespace {
 
 struct GateLaunch {
-    int egp_log2, mt, tt;
+    int egp_log2, mt, me, tt, kc;
     size_t smem;
 };
 
-GateLaunch gate_launch_shape(int E) {
-    int egp_log2 = 0;
-    while ((4 << egp_log2) < E) ++egp_log2;  // 4*EGP >= E, EGP <= 64
-    const int tg = kGateThreads >> egp_log2;
-    int mt = 1;
-    while (tg * mt < 32) mt *= 2;  // at least 32 tokens per block
-    GateLaunch g;
-    g.egp_log2 = egp_log2;
-    g.mt = mt;
-    g.tt = tg * mt;
-    const int ep = 4 << egp_log2;
-    const size_t stage = static_cast<size_t>(kGateKC) * (g.tt + ep);
-    const size_t zbuf = static_cast<size_t>(g.tt) * (ep + 1);
-    g.smem = sizeof(float) * (stage > zbuf ? stage : zbuf);
-    return g;
+// Tile shape for E experts and T tokens: the most independent chains per
+// thread (MT tokens x ME experts) that still gives at least 512 work-groups
+// (two per CU), falling back to the most work-groups when T is small; the
+// staging and logit buffers must fit the registers and the LDS. Every E in
+// 1..256 has a candidate (ME = 2, MT = 1 always fits). Each work-group walks
+// K in chunks of kc (longest that fits) so the next chunk's loads overlap
+// enough FMAs.
+GateLaunch gate_launch_shape(int E, int64_t T, int vec) {
+    GateLaunch best{};
+    int64_t best_blocks = -1;
+    int best_chains = -1;
+    for (int me : {4, 2}) {
+        int egp_log2 = 0;
+        while ((me << egp_log2) < E) ++egp_log2;
+        if (egp_log2 > 7) continue;
+        const int tg = kGateThreads >> egp_log2;
+        if (tg == 0) continue;
+        const int ep = me << egp_log2;
+        for (int mt : {8, 4, 2, 1}) {
+            const int tt = tg * mt;
+            if (tt > kGateThreads) continue;
+            // the longest K chunk (multiple of 32, at most 256) whose staging
+            // fits the registers and whose double buffer fits 128 KB of LDS
+            int kc = 0;
+            for (int c = 256; c >= kGateSub; c /= 2) {
+                const size_t stage = 2 * static_cast<size_t>(c + 4) * (tt + ep) * sizeof(float);
+                const int nreg = vec == 4 ? 2 * kGateNReg : kGateNReg;
+                if ((tt + ep) * (c / vec) <= nreg * kGateThreads && stage <= 128 * 1024) {
+                    kc = c;
+                    break;
+                }
+            }
+            if (kc == 0) continue;
+            const size_t stage = 2 * static_cast<size_t>(kc + 4) * (tt + ep);
+            const size_t zbuf = static_cast<size_t>(tt) * (ep + 1);
+            const size_t smem = sizeof(float) * (stage > zbuf ? stage : zbuf);
+            if (smem > kGateMaxLds) continue;
+            const int64_t blocks = (T + tt - 1) / tt;
+            const int chains = mt * me;
+            const bool ok = blocks >= 512;
+            const bool best_ok = best_blocks >= 512;
+            bool take;
+            if (best_blocks < 0) take = true;
+            else if (ok != best_ok) take = ok;
+            else if (ok) take = chains > best_chains;
+            else take = blocks > best_blocks || (blocks == best_blocks && chains > best_chains);
+            if (take) {
+                best.egp_log2 = egp_log2;
+                best.mt = mt;
+                best.me = me;
+                best.tt = tt;
+                best.kc = kc;
+                best.smem = smem;
+                best_blocks = blocks;
+                best_chains = chains;
+            }
+        }
+    }
+    return best;
+}
+
+template <typename TIn, int MT, int ME>
+void launch_shape(const GateLaunch& g, unsigned blocks, const moe_shape& s, const TIn* xp,
+                  const TIn* gp, const float* bias, int32_t* idx, float* w, float* dbg,
+                  hipStream_t st) {
+    if (g.smem > 64 * 1024 &&
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&gate_topk_kernel<TIn, MT, ME>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(g.smem)) != hipSuccess)
+        return;  // the launch error is reported by hipGetLastError
+    gate_topk_kernel<TIn, MT, ME><<<blocks, kGateThreads, g.smem, st>>>(
+        xp, gp, bias, s.T, s.d, s.E, s.k, g.egp_log2, g.kc, idx, w, dbg);
 }
 
 template <typename TIn>
 hipError_t launch_gate_t(const moe_shape& s, const void* x, const void* wg, const float* bias,
                          int32_t* idx, float* w, float* dbg, hipStream_t st) {
-    const GateLaunch g = gate_launch_shape(s.E);
+    const GateLaunch g = gate_launch_shape(s.E, s.T, 16 / static_cast<int>(sizeof(TIn)));
+    if (g.tt <= 0) return hipErrorInvalidConfiguration;
     const unsigned blocks = static_cast<unsigned>((s.T + g.tt - 1) / g.tt);
     const TIn* xp = static_cast<const TIn*>(x);
     const TIn* gp = static_cast<const TIn*>(wg);
-    switch (g.mt) {
-        case 1:
-            gate_topk_kernel<TIn, 1><<<blocks, kGateThreads, g.smem, st>>>(
-                xp, gp, bias, s.T, s.d, s.E, s.k, g.egp_log2, idx, w, dbg);
-            break;
-        case 2:
-            gate_topk_kernel<TIn, 2><<<blocks, kGateThreads, g.smem, st>>>(
-                xp, gp, bias, s.T, s.d, s.E, s.k, g.egp_log2, idx, w, dbg);
-            break;
-        case 4:
-            gate_topk_kernel<TIn, 4><<<blocks, kGateThreads, g.smem, st>>>(
-                xp, gp, bias, s.T, s.d, s.E, s.k, g.egp_log2, idx, w, dbg);
-            break;
-        default:
-            gate_topk_kernel<TIn, 8><<<blocks, kGateThreads, g.smem, st>>>(
-                xp, gp, bias, s.T, s.d, s.E, s.k, g.egp_log2, idx, w, dbg);
-            break;
+    if (g.me == 4) {
+        switch (g.mt) {
+            case 1: launch_shape<TIn, 1, 4>(g, blocks, s, xp, gp, bias, idx, w, dbg, st); break;
+            case 2: launch_shape<TIn, 2, 4>(g, blocks, s, xp, gp, bias, idx, w, dbg, st); break;
+            case 4: launch_shape<TIn, 4, 4>(g, blocks, s, xp, gp, bias, idx, w, dbg, st); break;
+            default: launch_shape<TIn, 8, 4>(g, blocks, s, xp, gp, bias, idx, w, dbg, st); break;
+        }
+    } else {
+        switch (g.mt) {
+            case 1: launch_shape<TIn, 1, 2>(g, blocks, s, xp, gp, bias, idx, w, dbg, st); break;
+            case 2: launch_shape<TIn, 2, 2>(g, blocks, s, xp, gp, bias, idx, w, dbg, st); break;
+            case 4: launch_shape<TIn, 4, 2>(g, blocks, s, xp, gp, bias, idx, w, dbg, st); break;
+            default: launch_shape<TIn, 8, 2>(g, blocks, s, xp, gp, bias, idx, w, dbg, st); break;
+        }
     }
     return hipGetLastError();
 }
