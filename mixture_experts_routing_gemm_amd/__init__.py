@@ -5,7 +5,7 @@ scan, stable permutation, optional per-token affine FP8 rows) -> grouped
 SwiGLU expert FFN (bf16 matrix cores) -> combine (weighted un-permute).
 The work runs in the HIP kernels of libmoe_mi355x.so behind the C ABI in
 include/moe.h; this package is its ctypes binding. Build the library with
-``python -m mixture_experts_routing_gemm_amd.build``.
+``python mixture_experts_routing_gemm_amd/build.py``.
 """
 
 from ._binding import (  # noqa: F401

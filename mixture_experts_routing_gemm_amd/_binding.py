@@ -65,7 +65,7 @@ def shape_of(cfg) -> moe_shape:
 def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(
-            f"{_LIB_PATH} is missing: build it with `python -m mixture_experts_routing_gemm_amd.build`")
+            f"{_LIB_PATH} is missing: build it with `python mixture_experts_routing_gemm_amd/build.py`")
     L = ctypes.CDLL(_LIB_PATH)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     sp = ctypes.POINTER(moe_shape)

@@ -1,6 +1,6 @@
 """Compile the HIP sources into the in-tree shared library libmoe_mi355x.so.
 
-    python -m mixture_experts_routing_gemm_amd.build
+    python mixture_experts_routing_gemm_amd/build.py
 
 Targets gfx950 only. Packed float32 instructions are disabled
 (-packed-fp32-ops) and floating-point contraction is off, so every fused
