@@ -2,6 +2,7 @@
 combine) on one MI355X, through the C ABI.
 
     python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
+    python bench.py --copy-probe-mib N    # counter calibration, see below
 
 Prints ONE JSON line. `value` is routed tokens/s (T / time per layer forward)
 with every input already resident in HBM. Per-kernel durations come from HIP
@@ -10,6 +11,13 @@ events that the library records on its stream between kernels
 for the dominant kernel, the grouped up-projection (bf16 matrix cores).
 The cpu_baseline leg times the CPU oracle, single-threaded, on a bounded
 sample of the same workload.
+
+roofline.traffic is the HBM byte count per launch of that kernel measured
+with the FETCH_SIZE and WRITE_SIZE counters (rocprofv3 --pmc, one run each),
+each scaled by what the same counter reads for a plain elementwise kernel of
+known size (--copy-probe-mib: reads N MiB, writes N MiB). The figures live in
+profiles/<kernel>_<workload>_traffic.txt together with the SHA-256 of the
+kernel's source file; when the source has changed since, traffic is null.
 """
 
 from __future__ import annotations
@@ -43,9 +51,48 @@ def algorithmic(cfg):
         "dispatch_bytes": T * d * b + T * k * d * bp + 8 * T * k + 4 * T * k
         + (8 * T * k if cfg.dispatch == "fp8" else 0),
         "ffn_up_flops": 4 * rows * d * h,
+        # token rows in, both weight matrices of every group, hidden rows out
+        "ffn_up_bytes": T * k * d * bp + S * T * d * b + (E + S) * 2 * h * d * b + rows * h * b
+        + (8 * T * k if cfg.dispatch == "fp8" else 0),
         "ffn_down_flops": 2 * rows * d * h,
         "combine_bytes": T * k * d * b + (T * d * b if S else 0) + 8 * T * k + T * d * b,
     }
+
+
+TRAFFIC_SOURCES = {"ffn_up": "mixture_experts_routing_gemm_amd/csrc/grouped_ffn.hip"}
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, or None if
+    there is none or the kernel's source changed after it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
+    src = TRAFFIC_SOURCES.get(kernel)
+    if src is None or not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            key, val = line.split(":", 1)
+            kv[key.strip()] = val.strip()
+    with open(os.path.join(ROOT, src), "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if kv.get("kernel_source_sha256") != sha or "traffic_bytes_per_launch" not in kv:
+        return None
+    return int(float(kv["traffic_bytes_per_launch"]))
+
+
+def copy_probe(mib):
+    """A plain elementwise kernel that reads and writes `mib` MiB, three times,
+    so that the HBM byte counters can be scaled against a known size."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4}))
 
 
 def cpu_baseline(cfg, n_tokens):
@@ -70,11 +117,15 @@ def main():
     ap.add_argument("--config", default="deepseekmoe_bf16")
     ap.add_argument("--cpu-tokens", type=int, default=96)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the tokens on one GPU; "
               "runs on more than one GPU are not part of this build", file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe_mib > 0:
+        copy_probe(args.copy_probe_mib)
+        return
 
     import torch
 
@@ -176,7 +227,8 @@ def main():
             "peak": gemm_peak,
             "unit": "TFLOP/s",
             "frac": round(up_tflops / gemm_peak, 4),
-            "traffic": None,
+            "traffic": measured_traffic("ffn_up", cfg.name),
+            "algorithmic_bytes": A["ffn_up_bytes"],
         },
         "detail": detail,
     }

@@ -311,18 +311,17 @@ __global__ __launch_bounds__(kFfnThreads, 2) void ffn_gemm_kernel(GemmArgs a) {
 }
 
 // ------------------------------------------------------ large-tile bf16 --
-// Persistent grouped GEMM. Work-groups of four waves walk a list of BM x BN
-// output tiles (tokens x weight rows), K sliced by 32; each wave owns a
-// (BM/2) x (BN/2) block of 32x32x16 bf16 MFMAs.
+// Persistent grouped GEMM: one 256-thread work-group per CU walks a list of
+// 256 x 256 output tiles (tokens x weight rows), K sliced by 32. Four waves
+// each own a 128 x 128 block, a 4 x 4 grid of 32x32x16 bf16 MFMAs.
 //  - Both operand slices go global -> LDS with the direct-to-LDS 16-byte loads
-//    into a ring of SLOTS slots; each slice is requested SLOTS-1 steps before
-//    it is read, and the waits count outstanding loads instead of draining.
+//    into a 4-slot ring; each slice is requested three steps before it is
+//    read, and the waits count outstanding loads instead of draining them.
 //  - LDS fragments of the next 16-wide half-slice are read while the current
 //    one's MFMAs run.
 //  - The ring runs across tiles: the next tile's first slices are in flight
 //    while the current tile's epilogue runs, and no work-group is launched
-//    per tile. With two work-groups per CU (the 128 x 256 shape) one's
-//    barriers, waits and epilogue overlap the other's MFMAs.
+//    per tile.
 //  - Each XCD works through one contiguous range of tiles (tile order: m-tile
 //    major, n-tile minor), so concurrent work-groups on an XCD share an
 //    expert's weights and rows in that XCD's L2.
@@ -330,24 +329,16 @@ __global__ __launch_bounds__(kFfnThreads, 2) void ffn_gemm_kernel(GemmArgs a) {
 // four consecutive output features of one token, stored as one 8-byte word.
 // fp8 token rows stay as codes in LDS and are dequantised as fragments are
 // read.
-template <int BM_, int BN_, int SLOTS_, int OCC_>
-struct BigCfg {
-    static constexpr int BM = BM_, BN = BN_, SLOTS = SLOTS_, OCC = OCC_;
-    static constexpr int BK = 32;
-    static constexpr int WM = BM / 2, WN = BN / 2;
-    static constexpr int MB = WM / 32, NB = WN / 32;
-    static constexpr int ABytes = 2 * BM * BK;  // bf16 token rows (fp8 rows use half)
-    static constexpr int BBytes = 2 * BN * BK;
-    static constexpr int Slot = ABytes + BBytes;
-    static constexpr int ALoads = BM / 64, ALoadsFp8 = BM / 128, BLoads = BN / 64;
-    // vector-memory instructions per wave per slice (fp8 slices are padded to it)
-    static constexpr int Loads = ALoads + BLoads;
-    static constexpr int Lds = SLOTS * Slot;
-    static_assert(BM % 128 == 0 && BN % 128 == 0, "tile");
-};
-// 256x256 tiles, four slots, one work-group per CU (a 128x256 tile with two
-// work-groups per CU measured slower on both projections)
-using BigWide = BigCfg<256, 256, 4, 1>;
+// (A 128 x 256 tile with three slots and two work-groups per CU measured
+// slower on both projections.)
+constexpr int kBigBM = 256, kBigBN = 256, kBigBK = 32, kBigSlots = 4;
+constexpr int kBigWM = 128, kBigWN = 128;
+constexpr int kBigMB = kBigWM / 32, kBigNB = kBigWN / 32;
+constexpr int kBigABytes = 2 * kBigBM * kBigBK;  // bf16 token rows (fp8 rows use half)
+constexpr int kBigBBytes = 2 * kBigBN * kBigBK;
+constexpr int kBigSlot = kBigABytes + kBigBBytes;
+// vector-memory instructions per wave per slice (fp8 slices are padded to it)
+constexpr int kBigLoads = kBigBM / 64 + kBigBN / 64;
 
 // byte offset of 16-byte chunk c (0..3) of row r in a [rows][32] bf16 tile;
 // conflict-free 16-byte reads of aligned runs of 8 rows (32 banks) or 16
@@ -379,17 +370,6 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);
 }
 
-// wait until at most `ahead` later slices' loads are outstanding
-template <int L, int MAXAHEAD>
-__device__ __forceinline__ void wait_slices(int ahead) {
-    if (MAXAHEAD >= 2 && ahead >= 2)
-        wait_vmcnt<(MAXAHEAD >= 2 ? 2 * L : 0)>();
-    else if (MAXAHEAD >= 1 && ahead >= 1)
-        wait_vmcnt<L>();
-    else
-        wait_vmcnt<0>();
-}
-
 // a wave-uniform pointer (lets the compiler keep it in SGPRs)
 __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
     const uint64_t v = reinterpret_cast<uint64_t>(p);
@@ -406,19 +386,17 @@ struct TileInfo {
 
 // What one lane needs to fetch slices of one tile: wave-uniform bases and
 // 32-bit per-lane byte offsets (the launcher keeps every operand under 4 GiB
-// for this kernel). In the up-projection a wave's weight DMA rows all come
-// from W1 (waves 0, 1) or all from W3 (waves 2, 3), so the weight base is
-// uniform.
-template <class C>
+// for this kernel). In the up-projection a wave's weight rows all come from
+// W1 (waves 0, 1) or all from W3 (waves 2, 3), so the weight base is uniform.
 struct TileSrc {
     const uint8_t* abase;
     const uint8_t* bbase;
-    uint32_t aoff[C::ALoads];      // token rows of this lane's DMA chunks
-    uint32_t boff[C::BLoads];      // weight rows of this lane's DMA chunks
-    float qs[C::MB], qc[C::MB];    // fp8 rows of this lane's fragments
+    uint32_t aoff[kBigBM / 64];  // token rows of this lane's DMA chunks
+    uint32_t boff[kBigBN / 64];  // weight rows of this lane's DMA chunks
+    float qs[kBigMB], qc[kBigMB];  // fp8 rows of this lane's fragments
 };
 
-template <int MODE, class C>
+template <int MODE>
 __device__ __forceinline__ TileInfo decode_tile(const GemmArgs& a, int L) {
     TileInfo ti;
     const int mtg = L / a.ntn;
@@ -426,27 +404,27 @@ __device__ __forceinline__ TileInfo decode_tile(const GemmArgs& a, int L) {
     const int routed = a.plan[a.E];
     if (mtg < routed) {
         ti.g = a.tile_group[mtg];
-        ti.m0 = (mtg - a.plan[ti.g]) * C::BM;
+        ti.m0 = (mtg - a.plan[ti.g]) * kBigBM;
         ti.row_base = a.offsets[ti.g];
         ti.nrows = a.offsets[ti.g + 1] - a.offsets[ti.g];
         ti.shared = false;
     } else {
-        const int mtT = static_cast<int>((a.T + C::BM - 1) / C::BM);
+        const int mtT = static_cast<int>((a.T + kBigBM - 1) / kBigBM);
         const int q = mtg - routed;
         ti.g = MODE == kModeDown ? a.E : a.E + q / mtT;
-        ti.m0 = (q % mtT) * C::BM;
+        ti.m0 = (q % mtT) * kBigBM;
         ti.row_base = 0;
         ti.nrows = static_cast<int>(a.T);
         ti.shared = true;
     }
     const int K = MODE == kModeDown ? (ti.shared ? a.S * a.h : a.h) : a.d;
-    ti.KT = K / C::BK;
+    ti.KT = K / kBigBK;
     return ti;
 }
 
-template <int MODE, class C>
+template <int MODE>
 __device__ __forceinline__ void tile_sources(const GemmArgs& a, const TileInfo& ti, int wave,
-                                             int lane, TileSrc<C>& src) {
+                                             int lane, TileSrc& src) {
     const int wm = wave >> 1;
     const int lr = lane & 31;
     const bool fp8 = MODE == kModeUpFp8 && !ti.shared;
@@ -459,9 +437,9 @@ __device__ __forceinline__ void tile_sources(const GemmArgs& a, const TileInfo& 
     // swizzle places at its position. Rows past the group's end re-read its
     // last row; their outputs are never stored.
 #pragma unroll
-    for (int i = 0; i < C::ALoads; ++i) {
+    for (int i = 0; i < kBigBM / 64; ++i) {
         if (fp8) {
-            const int r = (i % C::ALoadsFp8) * 128 + wave * 32 + (lane >> 1);
+            const int r = (i & 1) * 128 + wave * 32 + (lane >> 1);
             const int c = (lane & 1) ^ ((r >> 3) & 1);
             const int64_t row = ti.row_base + min(ti.m0 + r, last);
             src.aoff[i] = static_cast<uint32_t>(row * K + c * 16);
@@ -473,11 +451,11 @@ __device__ __forceinline__ void tile_sources(const GemmArgs& a, const TileInfo& 
         }
     }
 #pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb) {
+    for (int mb = 0; mb < kBigMB; ++mb) {
         src.qs[mb] = 0.0f;
         src.qc[mb] = 0.0f;
         if (fp8) {
-            const int64_t row = ti.row_base + min(ti.m0 + wm * C::WM + mb * 32 + lr, last);
+            const int64_t row = ti.row_base + min(ti.m0 + wm * kBigWM + mb * 32 + lr, last);
             src.qs[mb] = a.qparams[2 * row];
             src.qc[mb] = a.qparams[2 * row + 1];
         }
@@ -488,24 +466,25 @@ __device__ __forceinline__ void tile_sources(const GemmArgs& a, const TileInfo& 
         src.bbase = ((wave >> 1) ? a.wb : a.wa) + static_cast<int64_t>(ti.g) * a.h * a.d * 2;
     }
 #pragma unroll
-    for (int i = 0; i < C::BLoads; ++i) {
+    for (int i = 0; i < kBigBN / 64; ++i) {
         const int br = i * 64 + wave * 16 + (lane >> 2);
         const int c = (lane & 3) ^ (((br >> 1) & 3) ^ ((br >> 3) & 1));
         if (MODE == kModeDown) {
-            const int n = ti.nt * C::BN + br;
+            const int n = ti.nt * kBigBN + br;
             src.boff[i] = static_cast<uint32_t>(n) * a.h * 2 + c * 16;
         } else {
             // weight row br of the tile: 32-row blocks alternate W1 / W3
-            const int n = ti.nt * (C::BN / 2) + ((br >> 5) >> 1) * 32 + (br & 31);
+            const int n = ti.nt * (kBigBN / 2) + ((br >> 5) >> 1) * 32 + (br & 31);
             src.boff[i] = static_cast<uint32_t>(n) * a.d * 2 + c * 16;
         }
     }
 }
 
-template <int MODE, class C>
-__device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
+template <int MODE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void ffn_gemm_persistent_kernel(GemmArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    constexpr int MB = C::MB, NB = C::NB, S = C::SLOTS, D = S - 1;
+    constexpr int MB = kBigMB, NB = kBigNB;
     constexpr bool kFp8 = MODE == kModeUpFp8;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -515,7 +494,7 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
     // this work-group's tiles: XCD x takes the x-th eighth of the tile list,
     // its work-groups interleave within it
     const int routed = a.plan[a.E];
-    const int mtT = static_cast<int>((a.T + C::BM - 1) / C::BM);
+    const int mtT = static_cast<int>((a.T + kBigBM - 1) / kBigBM);
     const int nshared = MODE == kModeDown ? (a.S > 0 ? 1 : 0) : a.S;
     const int total = (routed + nshared * mtT) * a.ntn;
     const int xcd = blockIdx.x & 7, per_xcd = gridDim.x >> 3;
@@ -524,18 +503,18 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
     int L = lo + (blockIdx.x >> 3);
     if (L >= hi) return;
 
-    TileInfo cur = decode_tile<MODE, C>(a, L);
-    TileSrc<C> src;
-    tile_sources<MODE, C>(a, cur, wave, lane, src);
+    TileInfo cur = decode_tile<MODE>(a, L);
+    TileSrc src;
+    tile_sources<MODE>(a, cur, wave, lane, src);
     TileInfo nxt = cur;
-    TileSrc<C> nsrc = src;
+    TileSrc nsrc = src;
     bool has_next = false;
 
     // slice k of a tile into ring slot `slot`
-    auto issue = [&](const TileSrc<C>& ts, bool shared, int k, int slot) {
-        const int k0 = k * C::BK;
-        uint8_t* As = lds + slot * C::Slot;
-        uint8_t* Bs = As + C::ABytes;
+    auto issue = [&](const TileSrc& ts, bool shared, int k, int slot) {
+        const int k0 = k * kBigBK;
+        uint8_t* As = lds + slot * kBigSlot;
+        uint8_t* Bs = As + kBigABytes;
         const uint8_t* bb = uniform_ptr(ts.bbase) + static_cast<int64_t>(k0) * 2;
         if (MODE == kModeDown && shared) {
             const int seg = k0 / a.h;
@@ -545,34 +524,33 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
         const uint8_t* ab = uniform_ptr(ts.abase);
         if (kFp8 && !shared) {
 #pragma unroll
-            for (int i = 0; i < C::ALoadsFp8; ++i)
+            for (int i = 0; i < kBigBM / 128; ++i)
                 __builtin_amdgcn_global_load_lds(ab + (ts.aoff[i] + k0), As + (i * 128 + wave * 32) * 32, 16, 0, 0);
-            // more loads keep the per-slice count equal to the bf16 case;
+            // two more loads keep the per-slice count equal to the bf16 case;
             // they rewrite weight rows with the same bytes
 #pragma unroll
-            for (int i = 0; i < C::ALoads - C::ALoadsFp8; ++i)
-                __builtin_amdgcn_global_load_lds(bb + ts.boff[i % C::BLoads],
-                                                 Bs + ((i % C::BLoads) * 64 + wave * 16) * 64, 16, 0, 0);
+            for (int i = 0; i < kBigBM / 128; ++i)
+                __builtin_amdgcn_global_load_lds(bb + ts.boff[i], Bs + (i * 64 + wave * 16) * 64, 16, 0, 0);
         } else {
 #pragma unroll
-            for (int i = 0; i < C::ALoads; ++i)
+            for (int i = 0; i < kBigBM / 64; ++i)
                 __builtin_amdgcn_global_load_lds(ab + (ts.aoff[i] + k0 * 2), As + (i * 64 + wave * 16) * 64, 16, 0, 0);
         }
 #pragma unroll
-        for (int i = 0; i < C::BLoads; ++i)
+        for (int i = 0; i < kBigBN / 64; ++i)
             __builtin_amdgcn_global_load_lds(bb + ts.boff[i], Bs + (i * 64 + wave * 16) * 64, 16, 0, 0);
     };
     // LDS -> register fragments of 16-wide half-slice ks of a slot
-    auto load_frags = [&](int slot, int ks, bf16x8* fa, bf16x8* fb, const TileSrc<C>& ts, bool shared) {
-        const uint8_t* As = lds + slot * C::Slot;
-        const uint8_t* Bs = As + C::ABytes;
+    auto load_frags = [&](int slot, int ks, bf16x8* fa, bf16x8* fb, const TileSrc& ts, bool shared) {
+        const uint8_t* As = lds + slot * kBigSlot;
+        const uint8_t* Bs = As + kBigABytes;
         const int ch = ks * 2 + lg;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
-            fb[nb] = *reinterpret_cast<const bf16x8*>(Bs + lds_off32(wn * C::WN + nb * 32 + lr, ch));
+            fb[nb] = *reinterpret_cast<const bf16x8*>(Bs + lds_off32(wn * kBigWN + nb * 32 + lr, ch));
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-            const int r = wm * C::WM + mb * 32 + lr;
+            const int r = wm * kBigWM + mb * 32 + lr;
             if (kFp8 && !shared) {
                 const uint2 codes = *reinterpret_cast<const uint2*>(As + lds_off32_fp8(r, ch));
                 fa[mb] = __builtin_bit_cast(bf16x8, dequant8(codes, ts.qs[mb], ts.qc[mb]));
@@ -591,27 +569,23 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
                 acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[nb], fa[mb], acc[mb][nb], 0, 0, 0);
     };
 
-    // prologue: the first tile's slices 0..D-1
-#pragma unroll
-    for (int p = 0; p < D; ++p)
-        if (p < cur.KT) issue(src, cur.shared, p, p);
+    // prologue: the first tile's slices 0..2
+    issue(src, cur.shared, 0, 0);
+    issue(src, cur.shared, 1, 1);
+    issue(src, cur.shared, 2, 2);
 
     bf16x8 fa0[MB], fb0[NB], fa1[MB], fb1[NB];
-    int slot0 = 0;  // ring slot of the current tile's slice 0
     while (true) {
         // next tile of this work-group, decoded while this one computes
         const int Ln = L + per_xcd;
         has_next = Ln < hi;
         if (has_next) {
-            nxt = decode_tile<MODE, C>(a, Ln);
-            tile_sources<MODE, C>(a, nxt, wave, lane, nsrc);
+            nxt = decode_tile<MODE>(a, Ln);
+            tile_sources<MODE>(a, nxt, wave, lane, nsrc);
         }
-        const int KT = cur.KT;
-        // slice 0 landed; only this tile's slices 1..D-1 can still be in
-        // flight (the previous tile drained its stores and everything before)
-        wait_slices<C::Loads, D - 1>(min(D - 1, KT - 1));
+        wait_vmcnt<2 * kBigLoads>();  // slice 0 of this tile has landed
         ring_barrier();
-        load_frags(slot0, 0, fa0, fb0, src, cur.shared);
+        load_frags(0, 0, fa0, fb0, src, cur.shared);
 #pragma unroll
         for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -619,34 +593,44 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-        // one step: compute slice k (slot sk), request slice k+D (of this
+        const int KT = cur.KT;
+        // one step: compute slice k (slot j), request slice k+3 (of this
         // tile or, near its end, of the next one)
-        auto step = [&](int k) {
-            const int sk = (slot0 + k) % S;
-            const int sd = (slot0 + k + D) % S;
-            if (k + D < KT)
-                issue(src, cur.shared, k + D, sd);
+        auto step = [&](int k, int j) {
+            if (k + 3 < KT)
+                issue(src, cur.shared, k + 3, (j + 3) & 3);
             else if (has_next)
-                issue(nsrc, nxt.shared, k + D - KT, sd);
-            load_frags(sk, 1, fa1, fb1, src, cur.shared);
+                issue(nsrc, nxt.shared, k + 3 - KT, (j + 3) & 3);
+            load_frags(j, 1, fa1, fb1, src, cur.shared);
             mma(fa0, fb0);
             if (k + 1 < KT) {
-                // slice k+1 must have landed; later issued slices may fly
-                const int ahead = has_next ? D - 1 : min(D - 1, KT - 2 - k);
-                wait_slices<C::Loads, D - 1>(ahead);
+                // slice k+1 must have landed; slices k+2, k+3 may still fly
+                const bool k3 = k + 3 < KT || has_next;
+                const bool k2 = k + 2 < KT || has_next;
+                if (k3)
+                    wait_vmcnt<2 * kBigLoads>();
+                else if (k2)
+                    wait_vmcnt<kBigLoads>();
+                else
+                    wait_vmcnt<0>();
                 ring_barrier();
-                load_frags((sk + 1) % S, 0, fa0, fb0, src, cur.shared);
+                load_frags((j + 1) & 3, 0, fa0, fb0, src, cur.shared);
             }
             mma(fa1, fb1);
         };
-        for (int k = 0; k < KT; ++k) step(k);
+        for (int k = 0; k < KT; k += 4) {
+            step(k, 0);
+            step(k + 1, 1);
+            step(k + 2, 2);
+            step(k + 3, 3);
+        }
 
-        // epilogue: acc[mb][nb][v] is token (m0 + wm*WM + mb*32 + lr) and
-        // weight row (wn*WN + nb*32 + 8*(v/4) + 4*lg + v%4) of the tile
+        // epilogue: acc[mb][nb][v] is token (m0 + wm*128 + mb*32 + lr) and
+        // weight row (wn*128 + nb*32 + 8*(v/4) + 4*lg + v%4) of the tile
         bf16_t* out = reinterpret_cast<bf16_t*>(cur.shared ? a.out_shared : a.out_routed);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-            const int r = cur.m0 + wm * C::WM + mb * 32 + lr;
+            const int r = cur.m0 + wm * kBigWM + mb * 32 + lr;
             if (r >= cur.nrows) continue;
             const int64_t row = cur.row_base + r;
             if (MODE == kModeDown) {
@@ -654,7 +638,7 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
                 for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const int col = cur.nt * C::BN + wn * C::WN + nb * 32 + 8 * q + 4 * lg;
+                        const int col = cur.nt * kBigBN + wn * kBigWN + nb * 32 + 8 * q + 4 * lg;
                         uint2 w;
                         w.x = pack_bf16x2(acc[mb][nb][4 * q], acc[mb][nb][4 * q + 1]);
                         w.y = pack_bf16x2(acc[mb][nb][4 * q + 2], acc[mb][nb][4 * q + 3]);
@@ -662,8 +646,8 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
                     }
             } else {
                 const int ldo = cur.shared ? a.S * a.h : a.h;
-                const int cbase = (cur.shared ? (cur.g - a.E) * a.h : 0) + cur.nt * (C::BN / 2) +
-                                  wn * (C::WN / 2);
+                const int cbase = (cur.shared ? (cur.g - a.E) * a.h : 0) + cur.nt * (kBigBN / 2) +
+                                  wn * (kBigWN / 2);
 #pragma unroll
                 for (int pq = 0; pq < NB / 2; ++pq)
 #pragma unroll
@@ -684,18 +668,10 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
         // the epilogue's stores also count in vmcnt: drain before the next
         // tile's counted waits
         wait_vmcnt<0>();
-        slot0 = (slot0 + KT) % S;
         L = Ln;
         cur = nxt;
         src = nsrc;
     }
-}
-
-// one work-group (four waves, 512 registers each) per CU
-template <int MODE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void ffn_gemm_wide_kernel(GemmArgs a) {
-    persistent_gemm<MODE, BigWide>(a);
 }
 
 // ---------------------------------------------------------------- float32 --
@@ -804,9 +780,13 @@ int64_t max_mtiles(const moe_shape& s, int bm, bool down) {
 
 }  // namespace
 
-template <class C>
-hipError_t allow_big_lds(const void* kernel) {
-    return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, C::Lds);
+// the persistent kernels need 128 KB of LDS (the 4-slot ring)
+template <int MODE>
+hipError_t allow_big_lds() {
+    static hipError_t err = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&ffn_gemm_persistent_kernel<MODE>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, kBigSlots * kBigSlot);
+    return err;
 }
 
 int device_cus() {
@@ -823,23 +803,18 @@ int device_cus() {
 }
 
 template <int MODE>
-hipError_t launch_big(const GemmArgs& a, int64_t mtiles, hipStream_t st) {
-    using C = BigWide;
-    static const hipError_t e =
-        allow_big_lds<C>(reinterpret_cast<const void*>(&ffn_gemm_wide_kernel<MODE>));
-    if (e != hipSuccess) return e;
-    int64_t blocks = std::min<int64_t>(static_cast<int64_t>(device_cus()) * C::OCC, mtiles * a.ntn);
-    blocks = (blocks + 7) & ~int64_t(7);
-    ffn_gemm_wide_kernel<MODE><<<static_cast<unsigned>(blocks), 256, C::Lds, st>>>(a);
-    return hipGetLastError();
-}
-
-template <int MODE>
 hipError_t launch_gemm(const GemmArgs& a, int64_t mtiles, bool big, hipStream_t st) {
-    if (big) return launch_big<MODE>(a, mtiles, st);
-    int64_t blocks = mtiles * a.ntn;
-    blocks = (blocks + 7) & ~int64_t(7);
-    ffn_gemm_kernel<MODE><<<static_cast<unsigned>(blocks), kFfnThreads, 2 * kLdsStage, st>>>(a);
+    if (big) {
+        const hipError_t e = allow_big_lds<MODE>();
+        if (e != hipSuccess) return e;
+        int64_t blocks = std::min<int64_t>(device_cus(), mtiles * a.ntn);
+        blocks = (blocks + 7) & ~int64_t(7);
+        ffn_gemm_persistent_kernel<MODE><<<static_cast<unsigned>(blocks), 256, kBigSlots * kBigSlot, st>>>(a);
+    } else {
+        int64_t blocks = mtiles * a.ntn;
+        blocks = (blocks + 7) & ~int64_t(7);
+        ffn_gemm_kernel<MODE><<<static_cast<unsigned>(blocks), kFfnThreads, 2 * kLdsStage, st>>>(a);
+    }
     return hipGetLastError();
 }
 
@@ -855,10 +830,9 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const floa
     const uint64_t wbytes = static_cast<uint64_t>(s.E + s.S) * s.d * s.h * 2;
     const bool fits32 = rows * s.d * 2 < (uint64_t(1) << 32) && rows * s.h * 2 < (uint64_t(1) << 32) &&
                         wbytes < (uint64_t(1) << 32);
-    using C = BigWide;
-    const bool big = !f32 && fits32 && s.h % (C::BN / 2) == 0 && s.d % C::BN == 0 &&
-                     s.d % (2 * C::BK) == 0 && s.h % (2 * C::BK) == 0;
-    const int bm = f32 ? kF32BM : (big ? C::BM : kBM);
+    const bool big = !f32 && fits32 && s.h % (kBigBN / 2) == 0 && s.d % kBigBN == 0 &&
+                     s.d % (4 * kBigBK) == 0 && s.h % (4 * kBigBK) == 0;
+    const int bm = f32 ? kF32BM : (big ? kBigBM : kBM);
     int32_t* tile_group = plan + (s.E + s.S + 1);
     ffn_plan_kernel<<<1, 256, 0, st>>>(offsets, s.E, s.S, s.T, bm, plan, big ? tile_group : nullptr);
     mark(mk);
@@ -888,7 +862,7 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const floa
         ffn_gemm_f32_kernel<true><<<static_cast<unsigned>(mt * a.ntn), 256, 0, st>>>(a, 0);
         err = hipGetLastError();
     } else {
-        a.ntn = 2 * s.h / (big ? C::BN : kBN);
+        a.ntn = 2 * s.h / (big ? kBigBN : kBN);
         const int64_t mt = max_mtiles(s, bm, false);
         err = s.dispatch == MOE_FP8_E4M3 ? launch_gemm<kModeUpFp8>(a, mt, big, st)
                                          : launch_gemm<kModeUp>(a, mt, big, st);
@@ -909,7 +883,7 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const floa
         ffn_gemm_f32_kernel<false><<<static_cast<unsigned>(mt * a.ntn), 256, 0, st>>>(a, 0);
         err = hipGetLastError();
     } else {
-        a.ntn = s.d / (big ? C::BN : kBN);
+        a.ntn = s.d / (big ? kBigBN : kBN);
         err = launch_gemm<kModeDown>(a, max_mtiles(s, bm, true), big, st);
     }
     mark(mk);
