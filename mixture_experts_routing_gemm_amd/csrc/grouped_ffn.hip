@@ -20,6 +20,7 @@
 // remapped so that each of the 8 XCDs walks a contiguous range of tiles, which
 // keeps an expert's weights and rows within one XCD's L2 as far as possible.
 #include <algorithm>
+#include <type_traits>
 
 #include "moe_device.h"
 
@@ -33,12 +34,23 @@ constexpr int kLdsStage = (kBM + kBN) * kBK * 2;  // bytes per pipeline stage
 constexpr int kF32BM = 64, kF32BN = 64, kF32BK = 16;
 
 // plan[g] = number of m-tiles of groups before g (g = 0..E+S); routed group g
-// has ceil(n_g / bm) m-tiles and each shared group ceil(T / bm). tile_group
-// (may be null) receives the group of every routed m-tile.
+// has ceil(n_g / bm) m-tiles and each shared group ceil(T / bm).
+//
+// With `tiles` set (the persistent kernels) it also writes one descriptor per
+// m-tile for each projection and clears their tile counters:
+//   tiles[0 .. n_up)            up-projection: S*mtT shared m-tiles, then the
+//                               routed m-tiles group by group;
+//   tiles[n_up .. n_up+n_down)  down-projection: mtT shared m-tiles (one
+//                               group over the S concatenated hidden blocks,
+//                               if S > 0), then the routed m-tiles;
+// with n_up = S*mtT + R_max and n_down = mtT + R_max, R_max the bound on
+// routed m-tiles. A descriptor is {group, first row in the group, row of the
+// group's first row in the A operand, rows in the group}.
 __global__ __launch_bounds__(256) void ffn_plan_kernel(const int32_t* __restrict__ offsets,
                                                        int E, int S, int64_t T, int bm,
                                                        int32_t* __restrict__ plan,
-                                                       int32_t* __restrict__ tile_group) {
+                                                       int4* __restrict__ tiles, int n_up,
+                                                       int32_t* __restrict__ counters) {
     __shared__ int mt[kMaxE + kMaxS];
     __shared__ int pre[kMaxE + kMaxS + 1];
     const int G = E + S;
@@ -58,9 +70,25 @@ __global__ __launch_bounds__(256) void ffn_plan_kernel(const int32_t* __restrict
         plan[G] = s;
     }
     __syncthreads();
-    if (tile_group != nullptr)
-        for (int g = threadIdx.x; g < E; g += 256)
-            for (int m = 0; m < mt[g]; ++m) tile_group[pre[g] + m] = g;
+    if (tiles == nullptr) return;
+    if (threadIdx.x < 16) counters[threadIdx.x] = 0;
+    const int mtT = static_cast<int>((T + bm - 1) / bm);
+    const int nT = static_cast<int>(T);
+    int4* up = tiles;
+    int4* down = tiles + n_up;
+    for (int q = threadIdx.x; q < S * mtT; q += 256)
+        up[q] = make_int4(E + q / mtT, (q % mtT) * bm, 0, nT);
+    if (S > 0)
+        for (int q = threadIdx.x; q < mtT; q += 256) down[q] = make_int4(E, q * bm, 0, nT);
+    const int up0 = S * mtT, down0 = S > 0 ? mtT : 0;
+    for (int g = threadIdx.x; g < E; g += 256) {
+        const int rb = offsets[g], n = offsets[g + 1] - offsets[g];
+        for (int m = 0; m < mt[g]; ++m) {
+            const int4 t = make_int4(g, m * bm, rb, n);
+            up[up0 + pre[g] + m] = t;
+            down[down0 + pre[g] + m] = t;
+        }
+    }
 }
 
 struct GemmArgs {
@@ -69,7 +97,8 @@ struct GemmArgs {
     const uint8_t* a_shared;  // shared A rows: x [T, d] (up) or H_s [T, S*h] (down)
     const int32_t* offsets;   // [E+1]
     const int32_t* plan;      // [E+S+1]
-    const int32_t* tile_group;  // group of each routed m-tile (persistent kernel)
+    const int4* tiles;        // m-tile descriptors of this projection (persistent kernel)
+    int32_t* counters;        // 8 tile counters, one per XCD (persistent kernel)
     const uint8_t* wa;        // up: W1 [G, h, d]; down: W2 [G, d, h]
     const uint8_t* wb;        // up: W3 [G, h, d]
     uint8_t* out_routed;      // up: H_r [T*k, h]; down: Y_perm [T*k, d]
@@ -379,8 +408,7 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
 }
 
 struct TileInfo {
-    int g, nt, m0, nrows, KT;
-    int64_t row_base;
+    int g, nt, m0, row_base, nrows, KT;
     bool shared;
 };
 
@@ -396,27 +424,25 @@ struct TileSrc {
     float qs[kBigMB], qc[kBigMB];  // fp8 rows of this lane's fragments
 };
 
+// a 16-byte load from a wave-uniform address, through the scalar unit
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 load_uniform(const int4* p) {
+    return *(const __attribute__((address_space(4))) i32x4*)(p);
+}
+
+// Tile L of a projection's list: m-tile L / ntn (a descriptor written by the
+// plan kernel; the first nsh m-tiles are the shared experts'), n-tile L % ntn.
 template <int MODE>
-__device__ __forceinline__ TileInfo decode_tile(const GemmArgs& a, int L) {
+__device__ __forceinline__ TileInfo decode_tile(const GemmArgs& a, int L, int nsh) {
     TileInfo ti;
     const int mtg = L / a.ntn;
     ti.nt = L - mtg * a.ntn;
-    const int routed = a.plan[a.E];
-    if (mtg < routed) {
-        ti.g = a.tile_group[mtg];
-        ti.m0 = (mtg - a.plan[ti.g]) * kBigBM;
-        ti.row_base = a.offsets[ti.g];
-        ti.nrows = a.offsets[ti.g + 1] - a.offsets[ti.g];
-        ti.shared = false;
-    } else {
-        const int mtT = static_cast<int>((a.T + kBigBM - 1) / kBigBM);
-        const int q = mtg - routed;
-        ti.g = MODE == kModeDown ? a.E : a.E + q / mtT;
-        ti.m0 = (q % mtT) * kBigBM;
-        ti.row_base = 0;
-        ti.nrows = static_cast<int>(a.T);
-        ti.shared = true;
-    }
+    const i32x4 t = load_uniform(a.tiles + mtg);
+    ti.g = t[0];
+    ti.m0 = t[1];
+    ti.row_base = t[2];
+    ti.nrows = t[3];
+    ti.shared = mtg < nsh;
     const int K = MODE == kModeDown ? (ti.shared ? a.S * a.h : a.h) : a.d;
     ti.KT = K / kBigBK;
     return ti;
@@ -480,10 +506,13 @@ __device__ __forceinline__ void tile_sources(const GemmArgs& a, const TileInfo& 
     }
 }
 
+template <int N>
+using ic = std::integral_constant<int, N>;
+
 template <int MODE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void ffn_gemm_persistent_kernel(GemmArgs a) {
+__device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    int* lds_next = reinterpret_cast<int*>(lds + kBigSlots * kBigSlot);
     constexpr int MB = kBigMB, NB = kBigNB;
     constexpr bool kFp8 = MODE == kModeUpFp8;
     const int tid = threadIdx.x;
@@ -491,65 +520,101 @@ void ffn_gemm_persistent_kernel(GemmArgs a) {
     const int wn = wave & 1, wm = wave >> 1;
     const int lr = lane & 31, lg = lane >> 5;
 
-    // this work-group's tiles: XCD x takes the x-th eighth of the tile list,
-    // its work-groups interleave within it
+    // The tile list: the shared m-tiles first (in the down-projection each
+    // runs over S hidden blocks, S times the work of a routed tile), then the
+    // routed ones; n-tile minor. XCD x (work-groups b with b % 8 == x) owns
+    // the tiles whose work starts in the x-th eighth of the total, so the
+    // XCDs get equal work and each keeps its experts' weights in its own L2.
+    // Within an XCD the first round of tiles is static and later tiles are
+    // claimed from that XCD's counter.
     const int routed = a.plan[a.E];
     const int mtT = static_cast<int>((a.T + kBigBM - 1) / kBigBM);
-    const int nshared = MODE == kModeDown ? (a.S > 0 ? 1 : 0) : a.S;
-    const int total = (routed + nshared * mtT) * a.ntn;
+    const int nsh = MODE == kModeDown ? (a.S > 0 ? mtT : 0) : a.S * mtT;
+    const int64_t wsh = MODE == kModeDown ? max(a.S, 1) : 1;
+    const int n_sh = nsh * a.ntn;
+    const int total = n_sh + routed * a.ntn;
+    const int64_t sh_work = n_sh * wsh;
+    const int64_t work = sh_work + (total - n_sh);
+    auto tile_at = [&](int64_t w) -> int {  // first tile whose work starts at or after w
+        return w <= sh_work ? static_cast<int>((w + wsh - 1) / wsh)
+                            : n_sh + static_cast<int>(w - sh_work);
+    };
     const int xcd = blockIdx.x & 7, per_xcd = gridDim.x >> 3;
-    const int chunk = (total + 7) >> 3;
-    const int lo = xcd * chunk, hi = min(total, lo + chunk);
+    const int lo = tile_at(work * xcd / 8), hi = tile_at(work * (xcd + 1) / 8);
     int L = lo + (blockIdx.x >> 3);
     if (L >= hi) return;
+    int32_t* counter = a.counters + xcd;
+    if (tid == 0) lds_next[0] = lo + per_xcd + atomicAdd(counter, 1);
+    __syncthreads();
+    int Ln = lds_next[0];
 
-    TileInfo cur = decode_tile<MODE>(a, L);
+    TileInfo cur = decode_tile<MODE>(a, L, nsh);
     TileSrc src;
     tile_sources<MODE>(a, cur, wave, lane, src);
     TileInfo nxt = cur;
     TileSrc nsrc = src;
-    bool has_next = false;
 
-    // slice k of a tile into ring slot `slot`
-    auto issue = [&](const TileSrc& ts, bool shared, int k, int slot) {
-        const int k0 = k * kBigBK;
-        uint8_t* As = lds + slot * kBigSlot;
-        uint8_t* Bs = As + kBigABytes;
-        const uint8_t* bb = uniform_ptr(ts.bbase) + static_cast<int64_t>(k0) * 2;
-        if (MODE == kModeDown && shared) {
-            const int seg = k0 / a.h;
-            bb = uniform_ptr(ts.bbase) + static_cast<int64_t>(seg) * a.d * a.h * 2 +
-                 static_cast<int64_t>(k0 - seg * a.h) * 2;
-        }
-        const uint8_t* ab = uniform_ptr(ts.abase);
-        if (kFp8 && !shared) {
-#pragma unroll
-            for (int i = 0; i < kBigBM / 128; ++i)
-                __builtin_amdgcn_global_load_lds(ab + (ts.aoff[i] + k0), As + (i * 128 + wave * 32) * 32, 16, 0, 0);
-            // two more loads keep the per-slice count equal to the bf16 case;
-            // they rewrite weight rows with the same bytes
-#pragma unroll
-            for (int i = 0; i < kBigBM / 128; ++i)
-                __builtin_amdgcn_global_load_lds(bb + ts.boff[i], Bs + (i * 64 + wave * 16) * 64, 16, 0, 0);
-        } else {
-#pragma unroll
-            for (int i = 0; i < kBigBM / 64; ++i)
-                __builtin_amdgcn_global_load_lds(ab + (ts.aoff[i] + k0 * 2), As + (i * 64 + wave * 16) * 64, 16, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < kBigBN / 64; ++i)
-            __builtin_amdgcn_global_load_lds(bb + ts.boff[i], Bs + (i * 64 + wave * 16) * 64, 16, 0, 0);
+    // Requests of slice k of a tile into ring slot `slot`: kBigLoads
+    // direct-to-LDS instructions per wave, issued one at a time (i).
+    struct SliceReq {
+        const uint8_t* ab;
+        const uint8_t* bb;
+        uint8_t* As;
+        uint8_t* Bs;
+        int k0;
     };
-    // LDS -> register fragments of 16-wide half-slice ks of a slot
-    auto load_frags = [&](int slot, int ks, bf16x8* fa, bf16x8* fb, const TileSrc& ts, bool shared) {
+    auto slice_req = [&](const TileSrc& ts, int k, int slot) {
+        SliceReq q;
+        q.k0 = k * kBigBK;
+        q.As = lds + slot * kBigSlot;
+        q.Bs = q.As + kBigABytes;
+        int64_t kb = static_cast<int64_t>(q.k0) * 2;
+        if (MODE == kModeDown) {
+            // the shared group's K runs over the S hidden blocks in turn:
+            // slice k0 lies in block seg (always 0 for a routed group)
+            int seg = 0;
+#pragma unroll
+            for (int s = 1; s < kMaxS; ++s) seg += q.k0 >= s * a.h ? 1 : 0;
+            kb = static_cast<int64_t>(q.k0 - seg * a.h) * 2 + static_cast<int64_t>(seg) * a.d * a.h * 2;
+        }
+        q.bb = uniform_ptr(ts.bbase) + kb;
+        q.ab = uniform_ptr(ts.abase);
+        return q;
+    };
+    auto issue_one = [&](const TileSrc& ts, bool shared, const SliceReq& q, int i) {
+        if (kFp8 && !shared) {
+            // fp8 rows take half the loads; the others rewrite weight rows
+            // with the same bytes, so every slice counts kBigLoads loads
+            if (i < kBigBM / 128)
+                __builtin_amdgcn_global_load_lds(q.ab + (ts.aoff[i] + q.k0), q.As + (i * 128 + wave * 32) * 32,
+                                                 16, 0, 0);
+            else if (i < kBigBM / 64)
+                __builtin_amdgcn_global_load_lds(q.bb + ts.boff[i - kBigBM / 128],
+                                                 q.Bs + ((i - kBigBM / 128) * 64 + wave * 16) * 64, 16, 0, 0);
+        } else if (i < kBigBM / 64) {
+            __builtin_amdgcn_global_load_lds(q.ab + (ts.aoff[i] + q.k0 * 2), q.As + (i * 64 + wave * 16) * 64,
+                                             16, 0, 0);
+        }
+        if (i >= kBigBM / 64) {
+            const int b = i - kBigBM / 64;
+            __builtin_amdgcn_global_load_lds(q.bb + ts.boff[b], q.Bs + (b * 64 + wave * 16) * 64, 16, 0, 0);
+        }
+    };
+    auto issue = [&](const TileSrc& ts, bool shared, int k, int slot) {
+        const SliceReq q = slice_req(ts, k, slot);
+#pragma unroll
+        for (int i = 0; i < kBigLoads; ++i) issue_one(ts, shared, q, i);
+    };
+    // LDS -> register fragment i (B fragments 0..NB-1, then A fragments) of
+    // 16-wide half-slice ks of a slot
+    auto read_frag = [&](int slot, int ks, bf16x8* fa, bf16x8* fb, const TileSrc& ts, bool shared, int i) {
         const uint8_t* As = lds + slot * kBigSlot;
         const uint8_t* Bs = As + kBigABytes;
         const int ch = ks * 2 + lg;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-            fb[nb] = *reinterpret_cast<const bf16x8*>(Bs + lds_off32(wn * kBigWN + nb * 32 + lr, ch));
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
+        if (i < NB) {
+            fb[i] = *reinterpret_cast<const bf16x8*>(Bs + lds_off32(wn * kBigWN + i * 32 + lr, ch));
+        } else {
+            const int mb = i - NB;
             const int r = wm * kBigWM + mb * 32 + lr;
             if (kFp8 && !shared) {
                 const uint2 codes = *reinterpret_cast<const uint2*>(As + lds_off32_fp8(r, ch));
@@ -559,14 +624,15 @@ void ffn_gemm_persistent_kernel(GemmArgs a) {
             }
         }
     };
+    auto load_frags = [&](int slot, int ks, bf16x8* fa, bf16x8* fb, const TileSrc& ts, bool shared) {
+#pragma unroll
+        for (int i = 0; i < MB + NB; ++i) read_frag(slot, ks, fa, fb, ts, shared, i);
+    };
 
     f32x16 acc[MB][NB];
-    auto mma = [&](const bf16x8* fa, const bf16x8* fb) {
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-                acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[nb], fa[mb], acc[mb][nb], 0, 0, 0);
+    auto mma_one = [&](const bf16x8* fa, const bf16x8* fb, int i) {
+        const int mb = i / NB, nb = i % NB;
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[nb], fa[mb], acc[mb][nb], 0, 0, 0);
     };
 
     // prologue: the first tile's slices 0..2
@@ -576,15 +642,24 @@ void ffn_gemm_persistent_kernel(GemmArgs a) {
 
     bf16x8 fa0[MB], fb0[NB], fa1[MB], fb1[NB];
     while (true) {
-        // next tile of this work-group, decoded while this one computes
-        const int Ln = L + per_xcd;
-        has_next = Ln < hi;
-        if (has_next) {
-            nxt = decode_tile<MODE>(a, Ln);
-            tile_sources<MODE>(a, nxt, wave, lane, nsrc);
-        }
+        const bool has_next = Ln < hi;
+        // the next tile's descriptor (a scalar load) and a claim on the tile
+        // after it (published to the other waves before the last four
+        // slices). After the last tile the "next" tile is this one again: its
+        // first slices are re-read into free slots and never used, which
+        // keeps the last steps the same for every tile.
+        if (has_next) nxt = decode_tile<MODE>(a, Ln, nsh);
+        int claim = 0;
+        if (has_next && tid == 0) claim = atomicAdd(counter, 1);
+
         wait_vmcnt<2 * kBigLoads>();  // slice 0 of this tile has landed
         ring_barrier();
+        if (has_next) {
+            tile_sources<MODE>(a, nxt, wave, lane, nsrc);
+        } else {
+            nxt = cur;
+            nsrc = src;
+        }
         load_frags(0, 0, fa0, fb0, src, cur.shared);
 #pragma unroll
         for (int i = 0; i < MB; ++i)
@@ -594,36 +669,60 @@ void ffn_gemm_persistent_kernel(GemmArgs a) {
                 for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
         const int KT = cur.KT;
-        // one step: compute slice k (slot j), request slice k+3 (of this
-        // tile or, near its end, of the next one)
-        auto step = [&](int k, int j) {
-            if (k + 3 < KT)
-                issue(src, cur.shared, k + 3, (j + 3) & 3);
-            else if (has_next)
-                issue(nsrc, nxt.shared, k + 3 - KT, (j + 3) & 3);
-            load_frags(j, 1, fa1, fb1, src, cur.shared);
-            mma(fa0, fb0);
-            if (k + 1 < KT) {
-                // slice k+1 must have landed; slices k+2, k+3 may still fly
-                const bool k3 = k + 3 < KT || has_next;
-                const bool k2 = k + 2 < KT || has_next;
-                if (k3)
-                    wait_vmcnt<2 * kBigLoads>();
-                else if (k2)
-                    wait_vmcnt<kBigLoads>();
-                else
-                    wait_vmcnt<0>();
-                ring_barrier();
-                load_frags((j + 1) & 3, 0, fa0, fb0, src, cur.shared);
+        // One step computes slice k from ring slot J = k % 4 and requests
+        // slice k+3 into slot (J+3) % 4: from this tile (ISS 1) or, in the
+        // last three steps, from the next tile (ISS 2). Before its second
+        // half it waits until at most WN requested slices are still in
+        // flight (WN < 0: the tile's last step, nothing left to wait for).
+        auto step = [&](auto J, auto ISS, auto WN, int k) {
+            constexpr int j = decltype(J)::value, iss = decltype(ISS)::value;
+            constexpr int wn_ = decltype(WN)::value;
+            // first half: MFMAs on half-slice 0 (fa0, fb0), each followed by
+            // one request of slice k+3 and one fragment read of half-slice 1
+            const TileSrc& ts = iss == 2 ? nsrc : src;
+            const bool tsh = iss == 2 ? nxt.shared : cur.shared;
+            const SliceReq q = slice_req(ts, iss == 2 ? k + 3 - KT : k + 3, (j + 3) & 3);
+#pragma unroll
+            for (int i = 0; i < MB * NB; ++i) {
+                mma_one(fa0, fb0, i);
+                if (iss != 0 && i < kBigLoads) issue_one(ts, tsh, q, i);
+                if (i < MB + NB) read_frag(j, 1, fa1, fb1, src, cur.shared, i);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            mma(fa1, fb1);
+            if constexpr (wn_ >= 0) {
+                // second half: the next slice must have landed (at most WN
+                // requested slices still in flight) and be visible to all
+                // waves; its first fragments are read between the MFMAs on
+                // half-slice 1
+                wait_vmcnt<wn_ * kBigLoads>();
+                ring_barrier();
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < MB * NB; ++i) {
+                    mma_one(fa1, fb1, i);
+                    if (i < MB + NB) read_frag((j + 1) & 3, 0, fa0, fb0, src, cur.shared, i);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < MB * NB; ++i) mma_one(fa1, fb1, i);
+            }
         };
-        for (int k = 0; k < KT; k += 4) {
-            step(k, 0);
-            step(k + 1, 1);
-            step(k + 2, 2);
-            step(k + 3, 3);
+        int k = 0;
+        for (; k < KT - 4; k += 4) {
+            step(ic<0>(), ic<1>(), ic<2>(), k);
+            step(ic<1>(), ic<1>(), ic<2>(), k + 1);
+            step(ic<2>(), ic<1>(), ic<2>(), k + 2);
+            step(ic<3>(), ic<1>(), ic<2>(), k + 3);
         }
+        // the last four slices; the claimed tile index goes out through LDS
+        // with the first of these steps' barrier
+        if (tid == 0) lds_next[0] = has_next ? lo + per_xcd + claim : hi;
+        step(ic<0>(), ic<1>(), ic<2>(), k);
+        step(ic<1>(), ic<2>(), ic<2>(), k + 1);
+        step(ic<2>(), ic<2>(), ic<2>(), k + 2);
+        step(ic<3>(), ic<2>(), ic<-1>(), k + 3);
+        const int Ln2 = lds_next[0];
 
         // epilogue: acc[mb][nb][v] is token (m0 + wm*128 + mb*32 + lr) and
         // weight row (wn*128 + nb*32 + 8*(v/4) + 4*lg + v%4) of the tile
@@ -632,7 +731,7 @@ void ffn_gemm_persistent_kernel(GemmArgs a) {
         for (int mb = 0; mb < MB; ++mb) {
             const int r = cur.m0 + wm * kBigWM + mb * 32 + lr;
             if (r >= cur.nrows) continue;
-            const int64_t row = cur.row_base + r;
+            const int64_t row = static_cast<int64_t>(cur.row_base) + r;
             if (MODE == kModeDown) {
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
@@ -664,14 +763,23 @@ void ffn_gemm_persistent_kernel(GemmArgs a) {
                     }
             }
         }
-        if (!has_next) break;
         // the epilogue's stores also count in vmcnt: drain before the next
-        // tile's counted waits
+        // tile's counted waits (and, after the last tile, let the re-read
+        // slices land before the work-group's LDS is released)
         wait_vmcnt<0>();
+        if (!has_next) break;
         L = Ln;
+        Ln = Ln2;
         cur = nxt;
         src = nsrc;
     }
+}
+
+// one work-group of four waves per CU, 512 registers per lane
+template <int MODE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void ffn_gemm_persistent_kernel(GemmArgs a) {
+    persistent_gemm<MODE>(a);
 }
 
 // ---------------------------------------------------------------- float32 --
@@ -768,6 +876,28 @@ __global__ __launch_bounds__(256) void ffn_gemm_f32_kernel(GemmArgs a, int mt_ma
     }
 }
 
+// Plan area of the workspace: plan [E+S+1] ints, 16 tile counters (8 per
+// projection), then the up- and down-projection tile descriptors of the
+// persistent kernels (16 bytes each).
+struct PlanLayout {
+    size_t counters, tiles, bytes;
+    int n_up, n_down;
+};
+
+PlanLayout plan_layout(const moe_shape& s) {
+    PlanLayout p;
+    const int64_t mtT = (s.T + kBigBM - 1) / kBigBM;
+    const int64_t rmax = s.T * s.k / kBigBM + s.E;  // routed m-tiles, at most
+    p.n_up = static_cast<int>(s.S * mtT + rmax);
+    p.n_down = static_cast<int>(mtT + rmax);
+    p.counters = ((static_cast<size_t>(s.E + s.S + 1) * 4 + 63) / 64) * 64;
+    p.tiles = p.counters + 64;
+    p.bytes = p.tiles + static_cast<size_t>(p.n_up + p.n_down) * sizeof(int4);
+    return p;
+}
+
+size_t ffn_plan_bytes(const moe_shape& s) { return plan_layout(s).bytes; }
+
 namespace {
 
 // upper bound on the m-tiles of one launch
@@ -780,12 +910,14 @@ int64_t max_mtiles(const moe_shape& s, int bm, bool down) {
 
 }  // namespace
 
-// the persistent kernels need 128 KB of LDS (the 4-slot ring)
+// the persistent kernels need 128 KB of LDS (the 4-slot ring) and a word for
+// handing a claimed tile index to the work-group
+constexpr int kBigLds = kBigSlots * kBigSlot + 16;
 template <int MODE>
 hipError_t allow_big_lds() {
     static hipError_t err = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&ffn_gemm_persistent_kernel<MODE>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, kBigSlots * kBigSlot);
+        hipFuncAttributeMaxDynamicSharedMemorySize, kBigLds);
     return err;
 }
 
@@ -809,7 +941,7 @@ hipError_t launch_gemm(const GemmArgs& a, int64_t mtiles, bool big, hipStream_t 
         if (e != hipSuccess) return e;
         int64_t blocks = std::min<int64_t>(device_cus(), mtiles * a.ntn);
         blocks = (blocks + 7) & ~int64_t(7);
-        ffn_gemm_persistent_kernel<MODE><<<static_cast<unsigned>(blocks), 256, kBigSlots * kBigSlot, st>>>(a);
+        ffn_gemm_persistent_kernel<MODE><<<static_cast<unsigned>(blocks), 256, kBigLds, st>>>(a);
     } else {
         int64_t blocks = mtiles * a.ntn;
         blocks = (blocks + 7) & ~int64_t(7);
@@ -833,15 +965,19 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const floa
     const bool big = !f32 && fits32 && s.h % (kBigBN / 2) == 0 && s.d % kBigBN == 0 &&
                      s.d % (4 * kBigBK) == 0 && s.h % (4 * kBigBK) == 0;
     const int bm = f32 ? kF32BM : (big ? kBigBM : kBM);
-    int32_t* tile_group = plan + (s.E + s.S + 1);
-    ffn_plan_kernel<<<1, 256, 0, st>>>(offsets, s.E, s.S, s.T, bm, plan, big ? tile_group : nullptr);
+    const PlanLayout pl = plan_layout(s);
+    int32_t* counters = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(plan) + pl.counters);
+    int4* tiles = reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(plan) + pl.tiles);
+    ffn_plan_kernel<<<1, 256, 0, st>>>(offsets, s.E, s.S, s.T, bm, plan, big ? tiles : nullptr,
+                                       pl.n_up, counters);
     mark(mk);
 
     GemmArgs a;
     a.qparams = qparams;
     a.offsets = offsets;
     a.plan = plan;
-    a.tile_group = tile_group;
+    a.tiles = tiles;
+    a.counters = counters;
     a.T = s.T;
     a.E = s.E;
     a.S = s.S;
@@ -877,6 +1013,8 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const floa
     a.wb = nullptr;
     a.out_routed = static_cast<uint8_t*>(y_perm);
     a.out_shared = static_cast<uint8_t*>(y_shared);
+    a.tiles = tiles + pl.n_up;
+    a.counters = counters + 8;
     if (f32) {
         a.ntn = (s.d + kF32BN - 1) / kF32BN;
         const int64_t mt = max_mtiles(s, kF32BM, true);

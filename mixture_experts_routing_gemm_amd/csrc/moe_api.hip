@@ -21,6 +21,7 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const floa
                               const void* w3, const void* w2, void* y_perm, void* y_shared,
                               int32_t* plan, void* h_routed, void* h_shared, hipStream_t st,
                               const Marks* mk);
+size_t ffn_plan_bytes(const moe_shape& s);
 hipError_t launch_combine(const moe_shape& s, const void* y_perm, const void* y_sh,
                           const int32_t* dest_row, const float* topk_w, void* y, hipStream_t st);
 
@@ -62,8 +63,8 @@ Layout layout(const moe_shape& s, int stage) {
         L.blk = take(nblk * E * 4);
     }
     if (ffn) {
-        // m-tile prefix [E+S+1] and the group of each routed m-tile
-        L.plan = take((E + S + 2 + T * k / 128 + E) * 4);
+        // m-tile prefix, tile counters and tile descriptors
+        L.plan = take(ffn_plan_bytes(s));
         L.h_r = take(T * k * h * es);
         L.h_s = take(T * S * h * es);
     }
