@@ -369,15 +369,21 @@ constexpr int kBigSlot = kBigABytes + kBigBBytes;
 // vector-memory instructions per wave per slice (fp8 slices are padded to it)
 constexpr int kBigLoads = kBigBM / 64 + kBigBN / 64;
 
-// byte offset of 16-byte chunk c (0..3) of row r in a [rows][32] bf16 tile;
-// conflict-free 16-byte reads of aligned runs of 8 rows (32 banks) or 16
-// rows (64 banks)
+// A ring slot holds the token rows (A) and weight rows (B) of one K slice in
+// blocks of 64 rows: block q of A at byte 8192*q, block q of B at 8192*q +
+// 4096. Wave w fills block w of both, so its eight direct-to-LDS requests of a
+// slice share one LDS base (M0 = slot + 8192*w + 4096) and differ only in the
+// immediate offset (-4096 .. 3072).
+//
+// byte offset of 16-byte chunk c (0..3) of bf16 row r (32 values); the XOR
+// swizzle makes 16-byte reads of aligned runs of 8 rows (32 banks) or 16 rows
+// (64 banks) conflict-free
 __device__ __forceinline__ int lds_off32(int r, int c) {
-    return (r << 6) + ((c ^ (((r >> 1) & 3) ^ ((r >> 3) & 1))) << 4);
+    return ((r >> 6) << 13) + ((r & 63) << 6) + ((c ^ (((r >> 1) & 3) ^ ((r >> 3) & 1))) << 4);
 }
-// byte offset of 8-code group g8 (0..3) of row r in a [rows][32] fp8 tile
+// byte offset of 8-code group g8 (0..3) of fp8 row r (32 codes)
 __device__ __forceinline__ int lds_off32_fp8(int r, int g8) {
-    return (r << 5) + (((g8 >> 1) ^ ((r >> 3) & 1)) << 4) + ((g8 & 1) << 3);
+    return ((r >> 6) << 13) + ((r & 63) << 5) + (((g8 >> 1) ^ ((r >> 3) & 1)) << 4) + ((g8 & 1) << 3);
 }
 
 // Work-group barrier without the release/acquire fences of __syncthreads():
@@ -414,11 +420,12 @@ struct TileInfo {
 
 // What one lane needs to fetch slices of one tile: wave-uniform bases and
 // 32-bit per-lane byte offsets (the launcher keeps every operand under 4 GiB
-// for this kernel). In the up-projection a wave's weight rows all come from
-// W1 (waves 0, 1) or all from W3 (waves 2, 3), so the weight base is uniform.
+// for this kernel). In the up-projection the weight rows of a wave's DMA
+// requests 0, 1 come from W1 and those of requests 2, 3 from W3 (bbase3).
 struct TileSrc {
     const uint8_t* abase;
     const uint8_t* bbase;
+    const uint8_t* bbase3;
     uint32_t aoff[kBigBM / 64];  // token rows of this lane's DMA chunks
     uint32_t boff[kBigBN / 64];  // weight rows of this lane's DMA chunks
     float qs[kBigMB], qc[kBigMB];  // fp8 rows of this lane's fragments
@@ -458,19 +465,19 @@ __device__ __forceinline__ void tile_sources(const GemmArgs& a, const TileInfo& 
     const int last = ti.nrows - 1;
     src.abase = ti.shared ? a.a_shared : a.a_routed;
     // token DMA: a wave instruction fills 1 KB of LDS, lane i at byte 16*i:
-    // 16 bf16 rows of 64 B (row = i*64 + wave*16 + lane/4) or 32 fp8 rows of
-    // 32 B (row = i*128 + wave*32 + lane/2); each lane fetches the chunk the
+    // 16 bf16 rows of 64 B (row = wave*64 + i*16 + lane/4) or 32 fp8 rows of
+    // 32 B (row = wave*64 + i*32 + lane/2); each lane fetches the chunk the
     // swizzle places at its position. Rows past the group's end re-read its
     // last row; their outputs are never stored.
 #pragma unroll
     for (int i = 0; i < kBigBM / 64; ++i) {
         if (fp8) {
-            const int r = (i & 1) * 128 + wave * 32 + (lane >> 1);
+            const int r = wave * 64 + (i & 1) * 32 + (lane >> 1);
             const int c = (lane & 1) ^ ((r >> 3) & 1);
             const int64_t row = ti.row_base + min(ti.m0 + r, last);
             src.aoff[i] = static_cast<uint32_t>(row * K + c * 16);
         } else {
-            const int r = i * 64 + wave * 16 + (lane >> 2);
+            const int r = wave * 64 + i * 16 + (lane >> 2);
             const int c = (lane & 3) ^ (((r >> 1) & 3) ^ ((r >> 3) & 1));
             const int64_t row = ti.row_base + min(ti.m0 + r, last);
             src.aoff[i] = static_cast<uint32_t>(row * K * 2 + c * 16);
@@ -488,12 +495,14 @@ __device__ __forceinline__ void tile_sources(const GemmArgs& a, const TileInfo& 
     }
     if (MODE == kModeDown) {
         src.bbase = a.wa + static_cast<int64_t>(ti.shared ? a.E : ti.g) * a.d * a.h * 2;
+        src.bbase3 = src.bbase;
     } else {
-        src.bbase = ((wave >> 1) ? a.wb : a.wa) + static_cast<int64_t>(ti.g) * a.h * a.d * 2;
+        src.bbase = a.wa + static_cast<int64_t>(ti.g) * a.h * a.d * 2;
+        src.bbase3 = a.wb + static_cast<int64_t>(ti.g) * a.h * a.d * 2;
     }
 #pragma unroll
     for (int i = 0; i < kBigBN / 64; ++i) {
-        const int br = i * 64 + wave * 16 + (lane >> 2);
+        const int br = wave * 64 + i * 16 + (lane >> 2);
         const int c = (lane & 3) ^ (((br >> 1) & 3) ^ ((br >> 3) & 1));
         if (MODE == kModeDown) {
             const int n = ti.nt * kBigBN + br;
@@ -508,6 +517,16 @@ __device__ __forceinline__ void tile_sources(const GemmArgs& a, const TileInfo& 
 
 template <int N>
 using ic = std::integral_constant<int, N>;
+
+// f(ic<B>()), f(ic<B+1>()), ..., f(ic<E-1>()): a loop whose index is a
+// constant in every body
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(ic<B>());
+        static_for<B + 1, E>(f);
+    }
+}
 
 template <int MODE>
 __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
@@ -555,61 +574,78 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
     TileSrc nsrc = src;
 
     // Requests of slice k of a tile into ring slot `slot`: kBigLoads
-    // direct-to-LDS instructions per wave, issued one at a time (i).
+    // direct-to-LDS instructions per wave, issued one at a time (i), all from
+    // the LDS base of this wave's 8 KB block of the slot.
     struct SliceReq {
-        const uint8_t* ab;
-        const uint8_t* bb;
-        uint8_t* As;
-        uint8_t* Bs;
-        int k0;
+        const uint8_t* ab;   // token rows, wave-uniform
+        const uint8_t* bb;   // weight rows (W1 or W2), wave-uniform
+        const uint8_t* bb3;  // weight rows from W3 (up-projection)
+        uint32_t ka, kb;     // byte offsets of the slice within a row
+        uint8_t* base;
     };
-    auto slice_req = [&](const TileSrc& ts, int k, int slot) {
+    auto slice_req = [&](const TileSrc& ts, bool shared, int k, int slot) {
         SliceReq q;
-        q.k0 = k * kBigBK;
-        q.As = lds + slot * kBigSlot;
-        q.Bs = q.As + kBigABytes;
-        int64_t kb = static_cast<int64_t>(q.k0) * 2;
+        const int k0 = k * kBigBK;
+        q.base = lds + slot * kBigSlot + wave * 8192 + 4096;
+        q.ka = static_cast<uint32_t>(kFp8 && !shared ? k0 : k0 * 2);
+        q.kb = static_cast<uint32_t>(k0) * 2;
         if (MODE == kModeDown) {
             // the shared group's K runs over the S hidden blocks in turn:
             // slice k0 lies in block seg (always 0 for a routed group)
             int seg = 0;
 #pragma unroll
-            for (int s = 1; s < kMaxS; ++s) seg += q.k0 >= s * a.h ? 1 : 0;
-            kb = static_cast<int64_t>(q.k0 - seg * a.h) * 2 + static_cast<int64_t>(seg) * a.d * a.h * 2;
+            for (int s = 1; s < kMaxS; ++s) seg += k0 >= s * a.h ? 1 : 0;
+            q.kb = static_cast<uint32_t>(k0 - seg * a.h) * 2 + static_cast<uint32_t>(seg) * a.d * a.h * 2;
         }
-        q.bb = uniform_ptr(ts.bbase) + kb;
         q.ab = uniform_ptr(ts.abase);
+        q.bb = uniform_ptr(ts.bbase);
+        q.bb3 = uniform_ptr(ts.bbase3);
         return q;
     };
-    auto issue_one = [&](const TileSrc& ts, bool shared, const SliceReq& q, int i) {
-        if (kFp8 && !shared) {
-            // fp8 rows take half the loads; the others rewrite weight rows
-            // with the same bytes, so every slice counts kBigLoads loads
-            if (i < kBigBM / 128)
-                __builtin_amdgcn_global_load_lds(q.ab + (ts.aoff[i] + q.k0), q.As + (i * 128 + wave * 32) * 32,
-                                                 16, 0, 0);
-            else if (i < kBigBM / 64)
-                __builtin_amdgcn_global_load_lds(q.bb + ts.boff[i - kBigBM / 128],
-                                                 q.Bs + ((i - kBigBM / 128) * 64 + wave * 16) * 64, 16, 0, 0);
-        } else if (i < kBigBM / 64) {
-            __builtin_amdgcn_global_load_lds(q.ab + (ts.aoff[i] + q.k0 * 2), q.As + (i * 64 + wave * 16) * 64,
-                                             16, 0, 0);
-        }
-        if (i >= kBigBM / 64) {
-            const int b = i - kBigBM / 64;
-            __builtin_amdgcn_global_load_lds(q.bb + ts.boff[b], q.Bs + (b * 64 + wave * 16) * 64, 16, 0, 0);
+    // one 16-byte-per-lane request of sbase + voff; OFF is the immediate
+    // offset from the wave's LDS base, applied to the global address too, so
+    // the wave-uniform part of the address is moved back by it
+    auto dma = [&](const uint8_t* sbase, uint32_t voff, uint8_t* base, auto OFF) {
+        constexpr int off = decltype(OFF)::value;
+        const uint8_t* sb = uniform_ptr(sbase - off);
+        __builtin_amdgcn_global_load_lds(sb + voff, base, 16, off, 0);
+    };
+    auto issue_one = [&](const TileSrc& ts, bool shared, const SliceReq& q, auto I) {
+        constexpr int i = decltype(I)::value;
+        if constexpr (i < kBigBM / 64) {
+            if (kFp8 && !shared) {
+                // fp8 rows take two requests; the other two rewrite weight
+                // rows with the same bytes, so every slice counts kBigLoads
+                if constexpr (i < kBigBM / 128)
+                    dma(q.ab, ts.aoff[i] + q.ka, q.base, ic<-4096 + 1024 * i>());
+                else
+                    dma(q.bb, ts.boff[i - kBigBM / 128] + q.kb, q.base, ic<1024 * (i - kBigBM / 128)>());
+            } else {
+                dma(q.ab, ts.aoff[i] + q.ka, q.base, ic<-4096 + 1024 * i>());
+            }
+        } else {
+            // weight rows of request b: in the up-projection 32-row blocks
+            // alternate W1 / W3, so requests 0, 1 read W1 and 2, 3 read W3
+            constexpr int b = i - kBigBM / 64;
+            dma(MODE != kModeDown && b >= 2 ? q.bb3 : q.bb, ts.boff[b] + q.kb, q.base, ic<1024 * b>());
         }
     };
     auto issue = [&](const TileSrc& ts, bool shared, int k, int slot) {
-        const SliceReq q = slice_req(ts, k, slot);
-#pragma unroll
-        for (int i = 0; i < kBigLoads; ++i) issue_one(ts, shared, q, i);
+        const SliceReq q = slice_req(ts, shared, k, slot);
+        issue_one(ts, shared, q, ic<0>());
+        issue_one(ts, shared, q, ic<1>());
+        issue_one(ts, shared, q, ic<2>());
+        issue_one(ts, shared, q, ic<3>());
+        issue_one(ts, shared, q, ic<4>());
+        issue_one(ts, shared, q, ic<5>());
+        issue_one(ts, shared, q, ic<6>());
+        issue_one(ts, shared, q, ic<7>());
     };
     // LDS -> register fragment i (B fragments 0..NB-1, then A fragments) of
     // 16-wide half-slice ks of a slot
     auto read_frag = [&](int slot, int ks, bf16x8* fa, bf16x8* fb, const TileSrc& ts, bool shared, int i) {
         const uint8_t* As = lds + slot * kBigSlot;
-        const uint8_t* Bs = As + kBigABytes;
+        const uint8_t* Bs = As + 4096;
         const int ch = ks * 2 + lg;
         if (i < NB) {
             fb[i] = *reinterpret_cast<const bf16x8*>(Bs + lds_off32(wn * kBigWN + i * 32 + lr, ch));
@@ -681,14 +717,14 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
             // one request of slice k+3 and one fragment read of half-slice 1
             const TileSrc& ts = iss == 2 ? nsrc : src;
             const bool tsh = iss == 2 ? nxt.shared : cur.shared;
-            const SliceReq q = slice_req(ts, iss == 2 ? k + 3 - KT : k + 3, (j + 3) & 3);
-#pragma unroll
-            for (int i = 0; i < MB * NB; ++i) {
+            const SliceReq q = slice_req(ts, tsh, iss == 2 ? k + 3 - KT : k + 3, (j + 3) & 3);
+            static_for<0, MB * NB>([&](auto I) {
+                constexpr int i = decltype(I)::value;
                 mma_one(fa0, fb0, i);
-                if (iss != 0 && i < kBigLoads) issue_one(ts, tsh, q, i);
-                if (i < MB + NB) read_frag(j, 1, fa1, fb1, src, cur.shared, i);
+                if constexpr (iss != 0 && i < kBigLoads) issue_one(ts, tsh, q, I);
+                if constexpr (i < MB + NB) read_frag(j, 1, fa1, fb1, src, cur.shared, i);
                 __builtin_amdgcn_sched_barrier(0);
-            }
+            });
             if constexpr (wn_ >= 0) {
                 // second half: the next slice must have landed (at most WN
                 // requested slices still in flight) and be visible to all
