@@ -106,6 +106,9 @@ struct GemmArgs {
     int64_t T;
     int E, S, d, h;
     int ntn;  // n-tiles per group
+    // operand sizes in bytes (the persistent kernel reads through buffer
+    // resources of these sizes; each is below 4 GiB there)
+    uint32_t a_routed_bytes, a_shared_bytes, w_bytes;
 };
 
 // Finds the group and m-tile of m-tile index mtg. Down-projection: the S
@@ -368,12 +371,12 @@ constexpr int kBigBBytes = 2 * kBigBN * kBigBK;
 constexpr int kBigSlot = kBigABytes + kBigBBytes;
 // vector-memory instructions per wave per slice (fp8 slices are padded to it)
 constexpr int kBigLoads = kBigBM / 64 + kBigBN / 64;
+// fourth word of a raw buffer resource on gfx950 (untyped, no swizzle)
+constexpr int kBufferFlags = 0x00020000;
 
 // A ring slot holds the token rows (A) and weight rows (B) of one K slice in
 // blocks of 64 rows: block q of A at byte 8192*q, block q of B at 8192*q +
-// 4096. Wave w fills block w of both, so its eight direct-to-LDS requests of a
-// slice share one LDS base (M0 = slot + 8192*w + 4096) and differ only in the
-// immediate offset (-4096 .. 3072).
+// 4096. Wave w fills block w of both with four 1 KB requests each.
 //
 // byte offset of 16-byte chunk c (0..3) of bf16 row r (32 values); the XOR
 // swizzle makes 16-byte reads of aligned runs of 8 rows (32 banks) or 16 rows
@@ -418,14 +421,15 @@ struct TileInfo {
     bool shared;
 };
 
-// What one lane needs to fetch slices of one tile: wave-uniform bases and
-// 32-bit per-lane byte offsets (the launcher keeps every operand under 4 GiB
-// for this kernel). In the up-projection the weight rows of a wave's DMA
-// requests 0, 1 come from W1 and those of requests 2, 3 from W3 (bbase3).
+// What one lane needs to fetch slices of one tile: 32-bit byte offsets of
+// its token rows within the A operand and of its weight rows within the
+// tile's weight group (the launcher keeps every operand under 4 GiB for this
+// kernel), and the wave-uniform byte offset of that group within W1/W2 (and
+// W3). In the up-projection the weight rows of a wave's DMA requests 0, 1
+// come from W1 and those of requests 2, 3 from W3.
 struct TileSrc {
-    const uint8_t* abase;
-    const uint8_t* bbase;
-    const uint8_t* bbase3;
+    uint32_t gofs;
+    bool shared;
     uint32_t aoff[kBigBM / 64];  // token rows of this lane's DMA chunks
     uint32_t boff[kBigBN / 64];  // weight rows of this lane's DMA chunks
     float qs[kBigMB], qc[kBigMB];  // fp8 rows of this lane's fragments
@@ -463,7 +467,7 @@ __device__ __forceinline__ void tile_sources(const GemmArgs& a, const TileInfo& 
     const bool fp8 = MODE == kModeUpFp8 && !ti.shared;
     const int K = MODE == kModeDown ? (ti.shared ? a.S * a.h : a.h) : a.d;
     const int last = ti.nrows - 1;
-    src.abase = ti.shared ? a.a_shared : a.a_routed;
+    src.shared = ti.shared;
     // token DMA: a wave instruction fills 1 KB of LDS, lane i at byte 16*i:
     // 16 bf16 rows of 64 B (row = wave*64 + i*16 + lane/4) or 32 fp8 rows of
     // 32 B (row = wave*64 + i*32 + lane/2); each lane fetches the chunk the
@@ -493,13 +497,7 @@ __device__ __forceinline__ void tile_sources(const GemmArgs& a, const TileInfo& 
             src.qc[mb] = a.qparams[2 * row + 1];
         }
     }
-    if (MODE == kModeDown) {
-        src.bbase = a.wa + static_cast<int64_t>(ti.shared ? a.E : ti.g) * a.d * a.h * 2;
-        src.bbase3 = src.bbase;
-    } else {
-        src.bbase = a.wa + static_cast<int64_t>(ti.g) * a.h * a.d * 2;
-        src.bbase3 = a.wb + static_cast<int64_t>(ti.g) * a.h * a.d * 2;
-    }
+    src.gofs = static_cast<uint32_t>(MODE == kModeDown && ti.shared ? a.E : ti.g) * a.d * a.h * 2;
 #pragma unroll
     for (int i = 0; i < kBigBN / 64; ++i) {
         const int br = wave * 64 + i * 16 + (lane >> 2);
@@ -517,6 +515,20 @@ __device__ __forceinline__ void tile_sources(const GemmArgs& a, const TileInfo& 
 
 template <int N>
 using ic = std::integral_constant<int, N>;
+
+// One 16-byte-per-lane request through a raw buffer resource over
+// [base, base + bytes): lane i reads base + voff_i + soff (zero when past the
+// end) and writes it to LDS at lds + OFF + 16*i. (The instruction's immediate
+// offset would move the source address as well, so the LDS offset goes into
+// the LDS base instead.)
+template <int OFF>
+__device__ __forceinline__ void buffer_to_lds16(const uint8_t* base, uint32_t bytes, uint32_t voff,
+                                                uint32_t soff, uint8_t* lds) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, static_cast<int>(bytes), kBufferFlags);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds + OFF), 16, voff,
+                                             soff, 0, 0);
+}
 
 // f(ic<B>()), f(ic<B+1>()), ..., f(ic<E-1>()): a loop whose index is a
 // constant in every body
@@ -574,60 +586,56 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
     TileSrc nsrc = src;
 
     // Requests of slice k of a tile into ring slot `slot`: kBigLoads
-    // direct-to-LDS instructions per wave, issued one at a time (i), all from
-    // the LDS base of this wave's 8 KB block of the slot.
+    // buffer-to-LDS instructions per wave, issued one at a time (i). Wave w
+    // fills block w of A (LDS base `abase`) and of B (`bbase`); request i
+    // lands at its base + 1024*(i % 4).
     struct SliceReq {
-        const uint8_t* ab;   // token rows, wave-uniform
-        const uint8_t* bb;   // weight rows (W1 or W2), wave-uniform
-        const uint8_t* bb3;  // weight rows from W3 (up-projection)
-        uint32_t ka, kb;     // byte offsets of the slice within a row
-        uint8_t* base;
+        uint32_t ka;     // byte offset of the slice within a token row
+        uint32_t kb;     // byte offset of the slice's weight columns, group included
+        uint8_t* abase;
+        uint8_t* bbase;
     };
     auto slice_req = [&](const TileSrc& ts, bool shared, int k, int slot) {
         SliceReq q;
         const int k0 = k * kBigBK;
-        q.base = lds + slot * kBigSlot + wave * 8192 + 4096;
+        q.abase = lds + slot * kBigSlot + wave * 8192;
+        q.bbase = q.abase + 4096;
         q.ka = static_cast<uint32_t>(kFp8 && !shared ? k0 : k0 * 2);
-        q.kb = static_cast<uint32_t>(k0) * 2;
+        uint32_t kb = static_cast<uint32_t>(k0) * 2;
         if (MODE == kModeDown) {
             // the shared group's K runs over the S hidden blocks in turn:
             // slice k0 lies in block seg (always 0 for a routed group)
             int seg = 0;
 #pragma unroll
             for (int s = 1; s < kMaxS; ++s) seg += k0 >= s * a.h ? 1 : 0;
-            q.kb = static_cast<uint32_t>(k0 - seg * a.h) * 2 + static_cast<uint32_t>(seg) * a.d * a.h * 2;
+            kb = static_cast<uint32_t>(k0 - seg * a.h) * 2 + static_cast<uint32_t>(seg) * a.d * a.h * 2;
         }
-        q.ab = uniform_ptr(ts.abase);
-        q.bb = uniform_ptr(ts.bbase);
-        q.bb3 = uniform_ptr(ts.bbase3);
+        q.kb = __builtin_amdgcn_readfirstlane(ts.gofs + kb);
+        q.ka = __builtin_amdgcn_readfirstlane(q.ka);
         return q;
-    };
-    // one 16-byte-per-lane request of sbase + voff; OFF is the immediate
-    // offset from the wave's LDS base, applied to the global address too, so
-    // the wave-uniform part of the address is moved back by it
-    auto dma = [&](const uint8_t* sbase, uint32_t voff, uint8_t* base, auto OFF) {
-        constexpr int off = decltype(OFF)::value;
-        const uint8_t* sb = uniform_ptr(sbase - off);
-        __builtin_amdgcn_global_load_lds(sb + voff, base, 16, off, 0);
     };
     auto issue_one = [&](const TileSrc& ts, bool shared, const SliceReq& q, auto I) {
         constexpr int i = decltype(I)::value;
+        const uint8_t* abuf = shared ? a.a_shared : a.a_routed;
+        const uint32_t abytes = shared ? a.a_shared_bytes : a.a_routed_bytes;
         if constexpr (i < kBigBM / 64) {
             if (kFp8 && !shared) {
                 // fp8 rows take two requests; the other two rewrite weight
                 // rows with the same bytes, so every slice counts kBigLoads
                 if constexpr (i < kBigBM / 128)
-                    dma(q.ab, ts.aoff[i] + q.ka, q.base, ic<-4096 + 1024 * i>());
+                    buffer_to_lds16<1024 * i>(abuf, abytes, ts.aoff[i], q.ka, q.abase);
                 else
-                    dma(q.bb, ts.boff[i - kBigBM / 128] + q.kb, q.base, ic<1024 * (i - kBigBM / 128)>());
+                    buffer_to_lds16<1024 * (i - kBigBM / 128)>(a.wa, a.w_bytes, ts.boff[i - kBigBM / 128], q.kb,
+                                                              q.bbase);
             } else {
-                dma(q.ab, ts.aoff[i] + q.ka, q.base, ic<-4096 + 1024 * i>());
+                buffer_to_lds16<1024 * i>(abuf, abytes, ts.aoff[i], q.ka, q.abase);
             }
         } else {
             // weight rows of request b: in the up-projection 32-row blocks
             // alternate W1 / W3, so requests 0, 1 read W1 and 2, 3 read W3
             constexpr int b = i - kBigBM / 64;
-            dma(MODE != kModeDown && b >= 2 ? q.bb3 : q.bb, ts.boff[b] + q.kb, q.base, ic<1024 * b>());
+            buffer_to_lds16<1024 * b>(MODE != kModeDown && b >= 2 ? a.wb : a.wa, a.w_bytes, ts.boff[b], q.kb,
+                                      q.bbase);
         }
     };
     auto issue = [&](const TileSrc& ts, bool shared, int k, int slot) {
@@ -1020,9 +1028,16 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const floa
     a.d = s.d;
     a.h = s.h;
 
+    const uint64_t esd = s.dispatch == MOE_FP8_E4M3 ? 1 : 2;
+    const uint64_t Tk = static_cast<uint64_t>(s.T) * s.k, TS = static_cast<uint64_t>(s.T) * s.S;
+    const uint64_t wgroup = static_cast<uint64_t>(s.d) * s.h * 2;
+
     // up-projection + SwiGLU
     a.a_routed = static_cast<const uint8_t*>(x_perm);
     a.a_shared = static_cast<const uint8_t*>(x);
+    a.a_routed_bytes = static_cast<uint32_t>(Tk * s.d * esd);
+    a.a_shared_bytes = static_cast<uint32_t>(s.S > 0 ? static_cast<uint64_t>(s.T) * s.d * 2 : 0);
+    a.w_bytes = static_cast<uint32_t>((s.E + s.S) * wgroup);
     a.wa = static_cast<const uint8_t*>(w1);
     a.wb = static_cast<const uint8_t*>(w3);
     a.out_routed = static_cast<uint8_t*>(h_routed);
@@ -1045,6 +1060,8 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const floa
     // down-projection
     a.a_routed = static_cast<const uint8_t*>(h_routed);
     a.a_shared = static_cast<const uint8_t*>(h_shared);
+    a.a_routed_bytes = static_cast<uint32_t>(Tk * s.h * 2);
+    a.a_shared_bytes = static_cast<uint32_t>(TS * s.h * 2);
     a.wa = static_cast<const uint8_t*>(w2);
     a.wb = nullptr;
     a.out_routed = static_cast<uint8_t*>(y_perm);
