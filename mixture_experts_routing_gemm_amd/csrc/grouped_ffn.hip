@@ -343,9 +343,10 @@ __global__ __launch_bounds__(kFfnThreads, 2) void ffn_gemm_kernel(GemmArgs a) {
 }
 
 // ------------------------------------------------------ large-tile bf16 --
-// Persistent grouped GEMM: one 256-thread work-group per CU walks a list of
-// 256 x 256 output tiles (tokens x weight rows), K sliced by 32. Four waves
-// each own a 128 x 128 block, a 4 x 4 grid of 32x32x16 bf16 MFMAs.
+// Persistent grouped GEMM: one 512-thread work-group per CU walks a list of
+// 256 x 256 output tiles (tokens x weight rows), K sliced by 32. Eight waves
+// (two per SIMD, so one's memory requests overlap the other's MFMAs) each own
+// a 128 x 64 block, a 4 x 2 grid of 32x32x16 bf16 MFMAs.
 //  - Both operand slices go global -> LDS with the direct-to-LDS 16-byte loads
 //    into a 4-slot ring; each slice is requested three steps before it is
 //    read, and the waits count outstanding loads instead of draining them.
@@ -364,19 +365,19 @@ __global__ __launch_bounds__(kFfnThreads, 2) void ffn_gemm_kernel(GemmArgs a) {
 // (A 128 x 256 tile with three slots and two work-groups per CU measured
 // slower on both projections.)
 constexpr int kBigBM = 256, kBigBN = 256, kBigBK = 32, kBigSlots = 4;
-constexpr int kBigWM = 128, kBigWN = 128;
+constexpr int kBigWM = 128, kBigWN = 64;  // eight waves: 2 (M) x 4 (N)
 constexpr int kBigMB = kBigWM / 32, kBigNB = kBigWN / 32;
 constexpr int kBigABytes = 2 * kBigBM * kBigBK;  // bf16 token rows (fp8 rows use half)
 constexpr int kBigBBytes = 2 * kBigBN * kBigBK;
 constexpr int kBigSlot = kBigABytes + kBigBBytes;
 // vector-memory instructions per wave per slice (fp8 slices are padded to it)
-constexpr int kBigLoads = kBigBM / 64 + kBigBN / 64;
+constexpr int kBigLoads = 4;  // per wave per slice: 2 token-row and 2 weight-row requests
 // fourth word of a raw buffer resource on gfx950 (untyped, no swizzle)
 constexpr int kBufferFlags = 0x00020000;
 
 // A ring slot holds the token rows (A) and weight rows (B) of one K slice in
 // blocks of 64 rows: block q of A at byte 8192*q, block q of B at 8192*q +
-// 4096. Wave w fills block w of both with four 1 KB requests each.
+// 4096. Wave w fills half of block w/2 of both: two 1 KB requests each.
 //
 // byte offset of 16-byte chunk c (0..3) of bf16 row r (32 values); the XOR
 // swizzle makes 16-byte reads of aligned runs of 8 rows (32 banks) or 16 rows
@@ -425,13 +426,13 @@ struct TileInfo {
 // its token rows within the A operand and of its weight rows within the
 // tile's weight group (the launcher keeps every operand under 4 GiB for this
 // kernel), and the wave-uniform byte offset of that group within W1/W2 (and
-// W3). In the up-projection the weight rows of a wave's DMA requests 0, 1
-// come from W1 and those of requests 2, 3 from W3.
+// W3). In the up-projection the weight rows of a wave's DMA requests come
+// from W1 for even waves and from W3 for odd ones.
 struct TileSrc {
     uint32_t gofs;
     bool shared;
-    uint32_t aoff[kBigBM / 64];  // token rows of this lane's DMA chunks
-    uint32_t boff[kBigBN / 64];  // weight rows of this lane's DMA chunks
+    uint32_t aoff[2];  // token rows of this lane's DMA chunks
+    uint32_t boff[2];  // weight rows of this lane's DMA chunks
     float qs[kBigMB], qc[kBigMB];  // fp8 rows of this lane's fragments
 };
 
@@ -462,26 +463,26 @@ __device__ __forceinline__ TileInfo decode_tile(const GemmArgs& a, int L, int ns
 template <int MODE>
 __device__ __forceinline__ void tile_sources(const GemmArgs& a, const TileInfo& ti, int wave,
                                              int lane, TileSrc& src) {
-    const int wm = wave >> 1;
+    const int wm = wave >> 2;
     const int lr = lane & 31;
     const bool fp8 = MODE == kModeUpFp8 && !ti.shared;
     const int K = MODE == kModeDown ? (ti.shared ? a.S * a.h : a.h) : a.d;
     const int last = ti.nrows - 1;
     src.shared = ti.shared;
     // token DMA: a wave instruction fills 1 KB of LDS, lane i at byte 16*i:
-    // 16 bf16 rows of 64 B (row = wave*64 + i*16 + lane/4) or 32 fp8 rows of
-    // 32 B (row = wave*64 + i*32 + lane/2); each lane fetches the chunk the
-    // swizzle places at its position. Rows past the group's end re-read its
-    // last row; their outputs are never stored.
+    // 16 bf16 rows of 64 B (row = wave*32 + i*16 + lane/4) or 32 fp8 rows of
+    // 32 B (row = wave*32 + lane/2); each lane fetches the chunk the swizzle
+    // places at its position. Rows past the group's end re-read its last
+    // row; their outputs are never stored.
 #pragma unroll
-    for (int i = 0; i < kBigBM / 64; ++i) {
+    for (int i = 0; i < 2; ++i) {
         if (fp8) {
-            const int r = wave * 64 + (i & 1) * 32 + (lane >> 1);
+            const int r = wave * 32 + (lane >> 1);
             const int c = (lane & 1) ^ ((r >> 3) & 1);
             const int64_t row = ti.row_base + min(ti.m0 + r, last);
             src.aoff[i] = static_cast<uint32_t>(row * K + c * 16);
         } else {
-            const int r = wave * 64 + i * 16 + (lane >> 2);
+            const int r = wave * 32 + i * 16 + (lane >> 2);
             const int c = (lane & 3) ^ (((r >> 1) & 3) ^ ((r >> 3) & 1));
             const int64_t row = ti.row_base + min(ti.m0 + r, last);
             src.aoff[i] = static_cast<uint32_t>(row * K * 2 + c * 16);
@@ -499,8 +500,8 @@ __device__ __forceinline__ void tile_sources(const GemmArgs& a, const TileInfo& 
     }
     src.gofs = static_cast<uint32_t>(MODE == kModeDown && ti.shared ? a.E : ti.g) * a.d * a.h * 2;
 #pragma unroll
-    for (int i = 0; i < kBigBN / 64; ++i) {
-        const int br = wave * 64 + i * 16 + (lane >> 2);
+    for (int i = 0; i < 2; ++i) {
+        const int br = wave * 32 + i * 16 + (lane >> 2);
         const int c = (lane & 3) ^ (((br >> 1) & 3) ^ ((br >> 3) & 1));
         if (MODE == kModeDown) {
             const int n = ti.nt * kBigBN + br;
@@ -548,7 +549,7 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
     constexpr bool kFp8 = MODE == kModeUpFp8;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-    const int wn = wave & 1, wm = wave >> 1;
+    const int wn = wave & 3, wm = wave >> 2;
     const int lr = lane & 31, lg = lane >> 5;
 
     // The tile list: the shared m-tiles first (in the down-projection each
@@ -598,8 +599,8 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
     auto slice_req = [&](const TileSrc& ts, bool shared, int k, int slot) {
         SliceReq q;
         const int k0 = k * kBigBK;
-        q.abase = lds + slot * kBigSlot + wave * 8192;
-        q.bbase = q.abase + 4096;
+        q.abase = lds + slot * kBigSlot + (wave >> 1) * 8192 + (wave & 1) * (kFp8 && !shared ? 1024 : 2048);
+        q.bbase = lds + slot * kBigSlot + (wave >> 1) * 8192 + 4096 + (wave & 1) * 2048;
         q.ka = static_cast<uint32_t>(kFp8 && !shared ? k0 : k0 * 2);
         uint32_t kb = static_cast<uint32_t>(k0) * 2;
         if (MODE == kModeDown) {
@@ -618,24 +619,22 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
         constexpr int i = decltype(I)::value;
         const uint8_t* abuf = shared ? a.a_shared : a.a_routed;
         const uint32_t abytes = shared ? a.a_shared_bytes : a.a_routed_bytes;
-        if constexpr (i < kBigBM / 64) {
+        // up-projection: a wave's weight rows lie in one 32-row block, W1 for
+        // even waves and W3 for odd ones
+        const uint8_t* wbuf = MODE != kModeDown && (wave & 1) ? a.wb : a.wa;
+        if constexpr (i < 2) {
             if (kFp8 && !shared) {
-                // fp8 rows take two requests; the other two rewrite weight
-                // rows with the same bytes, so every slice counts kBigLoads
-                if constexpr (i < kBigBM / 128)
-                    buffer_to_lds16<1024 * i>(abuf, abytes, ts.aoff[i], q.ka, q.abase);
+                // fp8 rows take one request; the other rewrites weight rows
+                if constexpr (i == 0)
+                    buffer_to_lds16<0>(abuf, abytes, ts.aoff[0], q.ka, q.abase);
                 else
-                    buffer_to_lds16<1024 * (i - kBigBM / 128)>(a.wa, a.w_bytes, ts.boff[i - kBigBM / 128], q.kb,
-                                                              q.bbase);
+                    buffer_to_lds16<0>(wbuf, a.w_bytes, ts.boff[0], q.kb, q.bbase);
             } else {
                 buffer_to_lds16<1024 * i>(abuf, abytes, ts.aoff[i], q.ka, q.abase);
             }
         } else {
-            // weight rows of request b: in the up-projection 32-row blocks
-            // alternate W1 / W3, so requests 0, 1 read W1 and 2, 3 read W3
-            constexpr int b = i - kBigBM / 64;
-            buffer_to_lds16<1024 * b>(MODE != kModeDown && b >= 2 ? a.wb : a.wa, a.w_bytes, ts.boff[b], q.kb,
-                                      q.bbase);
+            constexpr int b = i - 2;
+            buffer_to_lds16<1024 * b>(wbuf, a.w_bytes, ts.boff[b], q.kb, q.bbase);
         }
     };
     auto issue = [&](const TileSrc& ts, bool shared, int k, int slot) {
@@ -644,10 +643,6 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
         issue_one(ts, shared, q, ic<1>());
         issue_one(ts, shared, q, ic<2>());
         issue_one(ts, shared, q, ic<3>());
-        issue_one(ts, shared, q, ic<4>());
-        issue_one(ts, shared, q, ic<5>());
-        issue_one(ts, shared, q, ic<6>());
-        issue_one(ts, shared, q, ic<7>());
     };
     // LDS -> register fragment i (B fragments 0..NB-1, then A fragments) of
     // 16-wide half-slice ks of a slot
@@ -769,7 +764,7 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
         const int Ln2 = lds_next[0];
 
         // epilogue: acc[mb][nb][v] is token (m0 + wm*128 + mb*32 + lr) and
-        // weight row (wn*128 + nb*32 + 8*(v/4) + 4*lg + v%4) of the tile
+        // weight row (wn*64 + nb*32 + 8*(v/4) + 4*lg + v%4) of the tile
         bf16_t* out = reinterpret_cast<bf16_t*>(cur.shared ? a.out_shared : a.out_routed);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
@@ -819,9 +814,9 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
     }
 }
 
-// one work-group of four waves per CU, 512 registers per lane
+// one work-group of eight waves per CU, 256 registers per lane
 template <int MODE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void ffn_gemm_persistent_kernel(GemmArgs a) {
     persistent_gemm<MODE>(a);
 }
@@ -985,7 +980,7 @@ hipError_t launch_gemm(const GemmArgs& a, int64_t mtiles, bool big, hipStream_t 
         if (e != hipSuccess) return e;
         int64_t blocks = std::min<int64_t>(device_cus(), mtiles * a.ntn);
         blocks = (blocks + 7) & ~int64_t(7);
-        ffn_gemm_persistent_kernel<MODE><<<static_cast<unsigned>(blocks), 256, kBigLds, st>>>(a);
+        ffn_gemm_persistent_kernel<MODE><<<static_cast<unsigned>(blocks), 512, kBigLds, st>>>(a);
     } else {
         int64_t blocks = mtiles * a.ntn;
         blocks = (blocks + 7) & ~int64_t(7);
