@@ -188,48 +188,33 @@ __global__ __launch_bounds__(kGateThreads) void gate_topk_kernel(
     }
     __syncthreads();
 
-    // top-k: one thread per token keeps a sorted list of the best k so far
-    for (int r = tid; r < TT; r += kGateThreads) {
+    // top-k by rank: expert e of token r is selected iff fewer than k experts
+    // rank before it (larger logit, or equal logit and lower id), and that
+    // count is its slot. Every (token, expert) pair is one independent count.
+    float* sz = zs + TT * zld;                               // [TT][kMaxK] selected logits
+    int* si = reinterpret_cast<int*>(sz + TT * kMaxK);       // [TT][kMaxK] selected ids
+    for (int q = tid; q < TT * E; q += kGateThreads) {
+        const int r = q / E, e = q - r * E;
+        const float z = zs[r * zld + e];
+        int rank = 0;
+        for (int e2 = 0; e2 < E; ++e2) rank += ranks_before(zs[r * zld + e2], e2, z, e) ? 1 : 0;
+        if (rank < k) {
+            sz[r * kMaxK + rank] = z;
+            si[r * kMaxK + rank] = e;
+        }
+    }
+    __syncthreads();
+    // weights: softmax over the k selected logits (slot 0 holds the largest),
+    // every slot summing the same k terms in slot order
+    for (int q = tid; q < TT * k; q += kGateThreads) {
+        const int r = q / k, p = q - r * k;
         const int64_t t = t0 + r;
         if (t >= T) continue;
-        float bv[kMaxK];
-        int bi[kMaxK];
-#pragma unroll
-        for (int p = 0; p < kMaxK; ++p) {
-            bv[p] = -__builtin_inff();
-            bi[p] = 0x7fffffff;
-        }
-        for (int e = 0; e < E; ++e) {
-            float cv = zs[r * zld + e];
-            int ci = e;
-#pragma unroll
-            for (int p = 0; p < kMaxK; ++p) {
-                if (p < k && ranks_before(cv, ci, bv[p], bi[p])) {
-                    const float tv = bv[p];
-                    const int ti = bi[p];
-                    bv[p] = cv;
-                    bi[p] = ci;
-                    cv = tv;
-                    ci = ti;
-                }
-            }
-        }
-        float ex[kMaxK];
+        const float zmax = sz[r * kMaxK];
         float sum = 0.0f;
-#pragma unroll
-        for (int p = 0; p < kMaxK; ++p) {
-            if (p < k) {
-                ex[p] = expf(bv[p] - bv[0]);
-                sum += ex[p];
-            }
-        }
-#pragma unroll
-        for (int p = 0; p < kMaxK; ++p) {
-            if (p < k) {
-                topk_idx[t * k + p] = bi[p];
-                topk_w[t * k + p] = ex[p] / sum;
-            }
-        }
+        for (int p2 = 0; p2 < k; ++p2) sum += expf(sz[r * kMaxK + p2] - zmax);
+        topk_idx[t * k + p] = si[r * kMaxK + p];
+        topk_w[t * k + p] = expf(sz[r * kMaxK + p] - zmax) / sum;
     }
 }
 
@@ -274,7 +259,7 @@ GateLaunch gate_launch_shape(int E, int64_t T, int vec) {
             }
             if (kc == 0) continue;
             const size_t stage = 2 * static_cast<size_t>(kc + 4) * (tt + ep);
-            const size_t zbuf = static_cast<size_t>(tt) * (ep + 1);
+            const size_t zbuf = static_cast<size_t>(tt) * (ep + 1 + 2 * kMaxK);
             const size_t smem = sizeof(float) * (stage > zbuf ? stage : zbuf);
             if (smem > kGateMaxLds) continue;
             const int64_t blocks = (T + tt - 1) / tt;
