@@ -514,9 +514,6 @@ __device__ __forceinline__ void tile_sources(const GemmArgs& a, const TileInfo& 
     }
 }
 
-template <int N>
-using ic = std::integral_constant<int, N>;
-
 // One 16-byte-per-lane request through a raw buffer resource over
 // [base, base + bytes): lane i reads base + voff_i + soff (zero when past the
 // end) and writes it to LDS at lds + OFF + 16*i. (The instruction's immediate
@@ -529,16 +526,6 @@ __device__ __forceinline__ void buffer_to_lds16(const uint8_t* base, uint32_t by
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, static_cast<int>(bytes), kBufferFlags);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds + OFF), 16, voff,
                                              soff, 0, 0);
-}
-
-// f(ic<B>()), f(ic<B+1>()), ..., f(ic<E-1>()): a loop whose index is a
-// constant in every body
-template <int B, int E, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-    if constexpr (B < E) {
-        f(ic<B>());
-        static_for<B + 1, E>(f);
-    }
 }
 
 template <int MODE>

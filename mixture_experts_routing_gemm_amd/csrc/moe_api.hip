@@ -11,7 +11,7 @@
 
 namespace moe {
 hipError_t launch_gate_topk(const moe_shape& s, const void* x, const void* wg, const float* bias,
-                            int32_t* idx, float* w, float* dbg, hipStream_t st);
+                            int32_t* idx, float* w, float* dbg, hipStream_t st, const Marks* mk);
 hipError_t launch_dispatch(const moe_shape& s, const void* x, const int32_t* topk_idx,
                            int32_t* counts, int32_t* offsets, int32_t* dest_row,
                            int32_t* src_token, void* x_perm, float* qparams, int32_t* rank,
@@ -144,7 +144,7 @@ int32_t forward_impl(const moe_shape* s, const void* x, const void* w_gate, cons
     const Layout L = layout(*s, MOE_STAGE_FORWARD);
     hipStream_t st = static_cast<hipStream_t>(stream);
     mark(mk);
-    MOE_TRY(hip_status(launch_gate_topk(*s, x, w_gate, bias, topk_idx, topk_w, nullptr, st)));
+    MOE_TRY(hip_status(launch_gate_topk(*s, x, w_gate, bias, topk_idx, topk_w, nullptr, st, mk)));
     mark(mk);
     const bool fp8 = s->dispatch == MOE_FP8_E4M3;
     void* x_perm = at<void>(ws, L.x_perm);
@@ -204,7 +204,7 @@ int32_t moe_gate_topk(const moe_shape* s, const void* x, const void* w_gate, con
     MOE_TRY(check_ptrs({x, w_gate, topk_idx, topk_w}));
     MOE_TRY(check_opt({bias, logits_dbg}));
     return hip_status(launch_gate_topk(*s, x, w_gate, bias, topk_idx, topk_w, logits_dbg,
-                                       static_cast<hipStream_t>(stream)));
+                                       static_cast<hipStream_t>(stream), nullptr));
 }
 
 int32_t moe_dispatch(const moe_shape* s, const void* x, const int32_t* topk_idx, int32_t* counts,

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "moe.h"
 
 namespace moe {
@@ -59,6 +61,19 @@ __device__ __forceinline__ float wave_min(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, kWave));
     return v;
+}
+
+template <int N>
+using ic = std::integral_constant<int, N>;
+
+// f(ic<B>()), f(ic<B+1>()), ..., f(ic<E-1>()): a loop whose index is a
+// constant in every body
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(ic<B>());
+        static_for<B + 1, E>(f);
+    }
 }
 
 __device__ __forceinline__ void set_error(uint32_t* hdr, uint32_t bit) {

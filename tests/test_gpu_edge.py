@@ -94,6 +94,45 @@ def test_fp8_constant_rows_and_outliers():
     forward_vs_oracle(inp)
 
 
+@pytest.mark.parametrize("act,T,d,E,k,bias", [
+    ("bf16", 150, 200, 24, 3, True),      # K tail past the last 64-wide block
+    ("bf16", 1000, 8, 3, 2, False),       # K shorter than one block
+    ("f32", 77, 100, 9, 4, True),         # float32 weights, K tail
+    ("bf16", 4100, 1096, 40, 5, False),   # partial last chunk, ragged token group
+    ("bf16", 16384, 192, 16, 2, True),    # 64 tokens x 4 experts per lane
+    ("bf16", 65536, 64, 64, 6, False),    # 32 tokens x 8 experts per lane
+    ("bf16", 3000, 512, 50, 4, True),     # 16 tokens x 4 experts per lane
+    ("f32", 500, 192, 100, 8, False),     # 16 tokens x 8 experts per lane, float32
+    ("bf16", 300, 256, 200, 8, True),     # more experts than a block covers
+], ids=["tail", "short_k", "f32", "partial_chunk", "tw64", "tw32", "tw16_me4", "f32_me8",
+        "e200"])
+def test_gate_both_paths(act, T, d, E, k, bias):
+    """moe_gate_topk with a logits buffer (logits kernel + top-k kernel) and
+    without (the fused kernel): bit-exact logits and ids, weights to 1e-5."""
+    mm = _mm()
+    cfg = small_cfg(act, T=T, d=d, E=E, k=k, S=0, h=64, tol_y=1e-5)
+    inp = make_inputs(cfg, seed=11, gate_only=True)
+    if bias:
+        inp.bias = np.random.default_rng(12).normal(0.0, 0.05, E).astype(np.float32)
+    say(f"[gate] act={act} T={T} d={d} E={E} k={k} bias={bias}")
+    z_ref = oracle.gate_logits(inp.x, inp.wg, inp.bias, nthreads=ORACLE_THREADS)
+    idx_ref, w_ref = oracle.select_topk(z_ref, k)
+    shape = mm.shape_of(cfg)
+    x, wg = dev(inp.x), dev(inp.wg)
+    b = None if inp.bias is None else dev(inp.bias)
+    for with_logits in (True, False):
+        idx = torch.full((T, k), -3, dtype=torch.int32, device="cuda")
+        w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+        z = torch.empty((T, E), dtype=torch.float32, device="cuda") if with_logits else None
+        mm.moe_gate_topk(shape, x, wg, b, idx, w, z)
+        torch.cuda.synchronize()
+        if with_logits:
+            nbad = int(np.sum(host(z).view(np.uint32) != z_ref.view(np.uint32)))
+            assert nbad == 0, f"{nbad} logits differ"
+        assert np.array_equal(host(idx), idx_ref), f"ids differ (logits buffer: {with_logits})"
+        assert rel_l2(host(w), w_ref) <= 1e-5
+
+
 def test_bad_routing_ids_raise_the_device_flag():
     mm = _mm()
     cfg = small_cfg(T=300, d=128, E=8, k=2, S=0, h=64)
