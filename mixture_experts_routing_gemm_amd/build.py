@@ -8,10 +8,12 @@ multiply-add in the kernels is one written explicitly.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import glob
 import os
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -22,30 +24,43 @@ LIB = os.path.join(PKG, "libmoe_mi355x.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Wall", "-Wno-unused-function",
 ]
+
+# the host pass does not know the packed-fp32 feature and says so; that is harmless
+_NOISE = "is not a recognized feature for this target"
 
 
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, *sources(), "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    # the host pass does not know the packed-fp32 feature and says so; that is harmless
-    noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+    err = "\n".join(l for l in res.stderr.splitlines() if _NOISE not in l)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if err.strip() and verbose:
         print(err, file=sys.stderr)
+
+
+def build(verbose: bool = False) -> str:
+    """Compiles every source to an object (in parallel), then links."""
+    with tempfile.TemporaryDirectory(prefix="moe_build_") as tmpdir:
+        objs = [os.path.join(tmpdir, os.path.basename(src) + ".o") for src in sources()]
+        cmds = [[HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
+                for src, obj in zip(sources(), objs)]
+        jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+        with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+            for f in [ex.submit(_run, c, verbose) for c in cmds]:
+                f.result()
+        tmp = LIB + ".tmp"
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 
