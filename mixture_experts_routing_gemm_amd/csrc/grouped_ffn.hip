@@ -46,6 +46,9 @@ constexpr int kF32BM = 64, kF32BN = 64, kF32BK = 16;
 // with n_up = S*mtT + R_max and n_down = mtT + R_max, R_max the bound on
 // routed m-tiles. A descriptor is {group, first row in the group, row of the
 // group's first row in the A operand, rows in the group}.
+// words after the 16 tile counters: routed half and full m-tile counts
+constexpr int kTileMetaHalf = 16, kTileMetaFull = 17;
+
 __global__ __launch_bounds__(256) void ffn_plan_kernel(const int32_t* __restrict__ offsets,
                                                        int E, int S, int64_t T, int bm,
                                                        int32_t* __restrict__ plan,
@@ -53,6 +56,7 @@ __global__ __launch_bounds__(256) void ffn_plan_kernel(const int32_t* __restrict
                                                        int32_t* __restrict__ counters) {
     __shared__ int mt[kMaxE + kMaxS];
     __shared__ int pre[kMaxE + kMaxS + 1];
+    __shared__ int fpre[kMaxE], hpre[kMaxE + 1];
     const int G = E + S;
     for (int g = threadIdx.x; g < G; g += 256) {
         const int64_t n = g < E ? static_cast<int64_t>(offsets[g + 1] - offsets[g]) : T;
@@ -68,6 +72,22 @@ __global__ __launch_bounds__(256) void ffn_plan_kernel(const int32_t* __restrict
         }
         pre[G] = s;
         plan[G] = s;
+        // a routed group's last m-tile holding at most bm/2 rows is a half
+        // tile; the persistent kernels schedule those after all full tiles
+        int f = 0, h = 0;
+        for (int g = 0; g < E; ++g) {
+            const int n = offsets[g + 1] - offsets[g];
+            const int half = mt[g] > 0 && n - (mt[g] - 1) * bm <= bm / 2 ? 1 : 0;
+            fpre[g] = f;
+            hpre[g] = h;
+            f += mt[g] - half;
+            h += half;
+        }
+        hpre[E] = h;
+        if (tiles != nullptr) {
+            counters[kTileMetaHalf] = h;
+            counters[kTileMetaFull] = f;
+        }
     }
     __syncthreads();
     if (tiles == nullptr) return;
@@ -81,12 +101,15 @@ __global__ __launch_bounds__(256) void ffn_plan_kernel(const int32_t* __restrict
     if (S > 0)
         for (int q = threadIdx.x; q < mtT; q += 256) down[q] = make_int4(E, q * bm, 0, nT);
     const int up0 = S * mtT, down0 = S > 0 ? mtT : 0;
+    const int nfull = pre[E] - hpre[E];
     for (int g = threadIdx.x; g < E; g += 256) {
         const int rb = offsets[g], n = offsets[g + 1] - offsets[g];
+        const int half = hpre[g + 1] - hpre[g];
         for (int m = 0; m < mt[g]; ++m) {
             const int4 t = make_int4(g, m * bm, rb, n);
-            up[up0 + pre[g] + m] = t;
-            down[down0 + pre[g] + m] = t;
+            const int at = m < mt[g] - half ? fpre[g] + m : nfull + hpre[g];
+            up[up0 + at] = t;
+            down[down0 + at] = t;
         }
     }
 }
@@ -99,6 +122,7 @@ struct GemmArgs {
     const int32_t* plan;      // [E+S+1]
     const int4* tiles;        // m-tile descriptors of this projection (persistent kernel)
     int32_t* counters;        // 8 tile counters, one per XCD (persistent kernel)
+    const int32_t* tile_meta; // [routed half m-tiles, routed full m-tiles] (persistent kernel)
     const uint8_t* wa;        // up: W1 [G, h, d]; down: W2 [G, d, h]
     const uint8_t* wb;        // up: W3 [G, h, d]
     uint8_t* out_routed;      // up: H_r [T*k, h]; down: Y_perm [T*k, d]
@@ -420,6 +444,7 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
 struct TileInfo {
     int g, nt, m0, row_base, nrows, KT;
     bool shared;
+    bool half;  // at most kBigBM/2 valid rows: the lower row of waves idles
 };
 
 // What one lane needs to fetch slices of one tile: 32-bit byte offsets of
@@ -455,6 +480,7 @@ __device__ __forceinline__ TileInfo decode_tile(const GemmArgs& a, int L, int ns
     ti.row_base = t[2];
     ti.nrows = t[3];
     ti.shared = mtg < nsh;
+    ti.half = ti.nrows - ti.m0 <= kBigBM / 2;
     const int K = MODE == kModeDown ? (ti.shared ? a.S * a.h : a.h) : a.d;
     ti.KT = K / kBigBK;
     return ti;
@@ -541,33 +567,40 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
 
     // The tile list: the shared m-tiles first (in the down-projection each
     // runs over S hidden blocks, S times the work of a routed tile), then the
-    // routed ones; n-tile minor. XCD x (work-groups b with b % 8 == x) owns
-    // the tiles whose work starts in the x-th eighth of the total, so the
-    // XCDs get equal work and each keeps its experts' weights in its own L2.
-    // Within an XCD the first round of tiles is static and later tiles are
-    // claimed from that XCD's counter.
+    // routed full m-tiles, then the routed half m-tiles; n-tile minor. XCD x
+    // (work-groups b with b % 8 == x) owns the full tiles whose work starts
+    // in the x-th eighth of the full part, then the x-th eighth of the half
+    // tiles, so the XCDs get equal work, each keeps its experts' weights in
+    // its own L2, and the short tiles come last. Within an XCD tiles are
+    // taken in claim order: the first round static, later ones from that
+    // XCD's counter.
     const int routed = a.plan[a.E];
+    const int n_half = a.tile_meta[0];
     const int mtT = static_cast<int>((a.T + kBigBM - 1) / kBigBM);
     const int nsh = MODE == kModeDown ? (a.S > 0 ? mtT : 0) : a.S * mtT;
     const int64_t wsh = MODE == kModeDown ? max(a.S, 1) : 1;
     const int n_sh = nsh * a.ntn;
-    const int total = n_sh + routed * a.ntn;
+    const int n_full = n_sh + (routed - n_half) * a.ntn;  // tiles before the half ones
+    const int n_halft = n_half * a.ntn;
     const int64_t sh_work = n_sh * wsh;
-    const int64_t work = sh_work + (total - n_sh);
+    const int64_t work = sh_work + (n_full - n_sh);
     auto tile_at = [&](int64_t w) -> int {  // first tile whose work starts at or after w
         return w <= sh_work ? static_cast<int>((w + wsh - 1) / wsh)
                             : n_sh + static_cast<int>(w - sh_work);
     };
     const int xcd = blockIdx.x & 7, per_xcd = gridDim.x >> 3;
-    const int lo = tile_at(work * xcd / 8), hi = tile_at(work * (xcd + 1) / 8);
-    int L = lo + (blockIdx.x >> 3);
-    if (L >= hi) return;
+    const int flo = tile_at(work * xcd / 8), fhi = tile_at(work * (xcd + 1) / 8);
+    const int hlo = n_full + n_halft * xcd / 8, hhi = n_full + n_halft * (xcd + 1) / 8;
+    const int nclaim = (fhi - flo) + (hhi - hlo);  // tiles of this XCD
+    auto tile_of = [&](int c) -> int { return c < fhi - flo ? flo + c : hlo + (c - (fhi - flo)); };
+    int C = blockIdx.x >> 3;  // claim index of the current tile
+    if (C >= nclaim) return;
     int32_t* counter = a.counters + xcd;
-    if (tid == 0) lds_next[0] = lo + per_xcd + atomicAdd(counter, 1);
+    if (tid == 0) lds_next[0] = per_xcd + atomicAdd(counter, 1);
     __syncthreads();
-    int Ln = lds_next[0];
+    int Cn = lds_next[0];
 
-    TileInfo cur = decode_tile<MODE>(a, L, nsh);
+    TileInfo cur = decode_tile<MODE>(a, tile_of(C), nsh);
     TileSrc src;
     tile_sources<MODE>(a, cur, wave, lane, src);
     TileInfo nxt = cur;
@@ -668,13 +701,13 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
 
     bf16x8 fa0[MB], fb0[NB], fa1[MB], fb1[NB];
     while (true) {
-        const bool has_next = Ln < hi;
+        const bool has_next = Cn < nclaim;
         // the next tile's descriptor (a scalar load) and a claim on the tile
         // after it (published to the other waves before the last four
         // slices). After the last tile the "next" tile is this one again: its
         // first slices are re-read into free slots and never used, which
         // keeps the last steps the same for every tile.
-        if (has_next) nxt = decode_tile<MODE>(a, Ln, nsh);
+        if (has_next) nxt = decode_tile<MODE>(a, tile_of(Cn), nsh);
         int claim = 0;
         if (has_next && tid == 0) claim = atomicAdd(counter, 1);
 
@@ -700,9 +733,12 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
         // last three steps, from the next tile (ISS 2). Before its second
         // half it waits until at most WN requested slices are still in
         // flight (WN < 0: the tile's last step, nothing left to wait for).
-        auto step = [&](auto J, auto ISS, auto WN, int k) {
+        // An IDLE wave (the lower row of waves on a half tile) keeps the
+        // requests, waits and barriers but does no MFMAs or fragment reads.
+        auto step = [&](auto J, auto ISS, auto WN, auto IDLE, int k) {
             constexpr int j = decltype(J)::value, iss = decltype(ISS)::value;
             constexpr int wn_ = decltype(WN)::value;
+            constexpr bool idle = decltype(IDLE)::value;
             // first half: MFMAs on half-slice 0 (fa0, fb0), each followed by
             // one request of slice k+3 and one fragment read of half-slice 1
             const TileSrc& ts = iss == 2 ? nsrc : src;
@@ -710,9 +746,9 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
             const SliceReq q = slice_req(ts, tsh, iss == 2 ? k + 3 - KT : k + 3, (j + 3) & 3);
             static_for<0, MB * NB>([&](auto I) {
                 constexpr int i = decltype(I)::value;
-                mma_one(fa0, fb0, i);
+                if constexpr (!idle) mma_one(fa0, fb0, i);
                 if constexpr (iss != 0 && i < kBigLoads) issue_one(ts, tsh, q, I);
-                if constexpr (i < MB + NB) read_frag(j, 1, fa1, fb1, src, cur.shared, i);
+                if constexpr (!idle && i < MB + NB) read_frag(j, 1, fa1, fb1, src, cur.shared, i);
                 __builtin_amdgcn_sched_barrier(0);
             });
             if constexpr (wn_ >= 0) {
@@ -723,32 +759,40 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
                 wait_vmcnt<wn_ * kBigLoads>();
                 ring_barrier();
                 __builtin_amdgcn_sched_barrier(0);
+                if constexpr (!idle) {
 #pragma unroll
-                for (int i = 0; i < MB * NB; ++i) {
-                    mma_one(fa1, fb1, i);
-                    if (i < MB + NB) read_frag((j + 1) & 3, 0, fa0, fb0, src, cur.shared, i);
-                    __builtin_amdgcn_sched_barrier(0);
+                    for (int i = 0; i < MB * NB; ++i) {
+                        mma_one(fa1, fb1, i);
+                        if (i < MB + NB) read_frag((j + 1) & 3, 0, fa0, fb0, src, cur.shared, i);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
                 }
-            } else {
+            } else if constexpr (!idle) {
 #pragma unroll
                 for (int i = 0; i < MB * NB; ++i) mma_one(fa1, fb1, i);
             }
         };
-        int k = 0;
-        for (; k < KT - 4; k += 4) {
-            step(ic<0>(), ic<1>(), ic<2>(), k);
-            step(ic<1>(), ic<1>(), ic<2>(), k + 1);
-            step(ic<2>(), ic<1>(), ic<2>(), k + 2);
-            step(ic<3>(), ic<1>(), ic<2>(), k + 3);
-        }
-        // the last four slices; the claimed tile index goes out through LDS
-        // with the first of these steps' barrier
-        if (tid == 0) lds_next[0] = has_next ? lo + per_xcd + claim : hi;
-        step(ic<0>(), ic<1>(), ic<2>(), k);
-        step(ic<1>(), ic<2>(), ic<2>(), k + 1);
-        step(ic<2>(), ic<2>(), ic<2>(), k + 2);
-        step(ic<3>(), ic<2>(), ic<-1>(), k + 3);
-        const int Ln2 = lds_next[0];
+        auto k_loop = [&](auto IDLE) {
+            int k = 0;
+            for (; k < KT - 4; k += 4) {
+                step(ic<0>(), ic<1>(), ic<2>(), IDLE, k);
+                step(ic<1>(), ic<1>(), ic<2>(), IDLE, k + 1);
+                step(ic<2>(), ic<1>(), ic<2>(), IDLE, k + 2);
+                step(ic<3>(), ic<1>(), ic<2>(), IDLE, k + 3);
+            }
+            // the last four slices; the claimed tile index goes out through
+            // LDS with the first of these steps' barrier
+            if (tid == 0) lds_next[0] = has_next ? per_xcd + claim : nclaim;
+            step(ic<0>(), ic<1>(), ic<2>(), IDLE, k);
+            step(ic<1>(), ic<2>(), ic<2>(), IDLE, k + 1);
+            step(ic<2>(), ic<2>(), ic<2>(), IDLE, k + 2);
+            step(ic<3>(), ic<2>(), ic<-1>(), IDLE, k + 3);
+        };
+        if (cur.half && wm == 1)
+            k_loop(std::true_type{});
+        else
+            k_loop(std::false_type{});
+        const int Cn2 = lds_next[0];
 
         // epilogue: acc[mb][nb][v] is token (m0 + wm*128 + mb*32 + lr) and
         // weight row (wn*64 + nb*32 + 8*(v/4) + 4*lg + v%4) of the tile
@@ -794,8 +838,7 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
         // slices land before the work-group's LDS is released)
         wait_vmcnt<0>();
         if (!has_next) break;
-        L = Ln;
-        Ln = Ln2;
+        Cn = Cn2;
         cur = nxt;
         src = nsrc;
     }
@@ -917,7 +960,7 @@ PlanLayout plan_layout(const moe_shape& s) {
     p.n_up = static_cast<int>(s.S * mtT + rmax);
     p.n_down = static_cast<int>(mtT + rmax);
     p.counters = ((static_cast<size_t>(s.E + s.S + 1) * 4 + 63) / 64) * 64;
-    p.tiles = p.counters + 64;
+    p.tiles = p.counters + 128;  // 16 counters, then the m-tile counts
     p.bytes = p.tiles + static_cast<size_t>(p.n_up + p.n_down) * sizeof(int4);
     return p;
 }
@@ -1004,6 +1047,7 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const floa
     a.plan = plan;
     a.tiles = tiles;
     a.counters = counters;
+    a.tile_meta = counters + kTileMetaHalf;
     a.T = s.T;
     a.E = s.E;
     a.S = s.S;
