@@ -37,22 +37,47 @@ constexpr int kF32BM = 64, kF32BN = 64, kF32BK = 16;
 // has ceil(n_g / bm) m-tiles and each shared group ceil(T / bm).
 //
 // With `tiles` set (the persistent kernels) it also writes one descriptor per
-// m-tile for each projection and clears their tile counters:
-//   tiles[0 .. n_up)            up-projection: S*mtT shared m-tiles, then the
-//                               routed m-tiles group by group;
-//   tiles[n_up .. n_up+n_down)  down-projection: mtT shared m-tiles (one
-//                               group over the S concatenated hidden blocks,
-//                               if S > 0), then the routed m-tiles;
-// with n_up = S*mtT + R_max and n_down = mtT + R_max, R_max the bound on
-// routed m-tiles. A descriptor is {group, first row in the group, row of the
-// group's first row in the A operand, rows in the group}.
+// tile (m-tile x n-tile) for each projection and clears their tile counters:
+//   tiles[0 .. n_up)            up-projection: the S shared groups' tiles,
+//                               then the routed full m-tiles' group by group,
+//                               then the routed half m-tiles';
+//   tiles[n_up .. n_up+n_down)  down-projection: the shared tiles (one group
+//                               over the S concatenated hidden blocks, if
+//                               S > 0), then the routed ones, in the same
+//                               order;
+// sized for the bound on routed m-tiles. Within a group the tiles go in
+// supertiles (write_group).
 // words after the 16 tile counters: routed half and full m-tile counts
 constexpr int kTileMetaHalf = 16, kTileMetaFull = 17;
+
+// Writes the tiles of M m-tiles (from m-tile m_first) by ntn n-tiles of
+// group g, all threads of the block together, in supertiles of
+// kSwzM x kSwzN: n-blocks of kSwzN n-tiles, within those m-blocks of kSwzM
+// m-tiles, within a supertile n-major. Tiles that follow each other in the
+// list then share operand panels (an m-tile's token rows, an n-tile's weight
+// rows), so work-groups that take them at about the same time find the
+// panels in L2. Tile i: {g | nt << 16, first row, row base, rows}.
+constexpr int kSwzM = 4, kSwzN = 4;
+__device__ void write_group(int4* out, int g, int m_first, int M, int bm, int rb, int n, int ntn) {
+    const int N = ntn;
+    for (int i = threadIdx.x; i < M * N; i += blockDim.x) {
+        const int nb = i / (kSwzN * M);
+        const int w = min(kSwzN, N - nb * kSwzN);
+        const int j = i - nb * kSwzN * M;
+        const int mb = j / (kSwzM * w);
+        const int hgt = min(kSwzM, M - mb * kSwzM);
+        const int jj = j - mb * kSwzM * w;
+        const int nt = nb * kSwzN + jj / hgt;
+        const int m = m_first + mb * kSwzM + jj % hgt;
+        out[i] = make_int4(g | (nt << 16), m * bm, rb, n);
+    }
+}
 
 __global__ __launch_bounds__(256) void ffn_plan_kernel(const int32_t* __restrict__ offsets,
                                                        int E, int S, int64_t T, int bm,
                                                        int32_t* __restrict__ plan,
                                                        int4* __restrict__ tiles, int n_up,
+                                                       int ntn_up, int ntn_down,
                                                        int32_t* __restrict__ counters) {
     __shared__ int mt[kMaxE + kMaxS];
     __shared__ int pre[kMaxE + kMaxS + 1];
@@ -94,24 +119,26 @@ __global__ __launch_bounds__(256) void ffn_plan_kernel(const int32_t* __restrict
     if (threadIdx.x < 16) counters[threadIdx.x] = 0;
     const int mtT = static_cast<int>((T + bm - 1) / bm);
     const int nT = static_cast<int>(T);
-    int4* up = tiles;
-    int4* down = tiles + n_up;
-    for (int q = threadIdx.x; q < S * mtT; q += 256)
-        up[q] = make_int4(E + q / mtT, (q % mtT) * bm, 0, nT);
-    if (S > 0)
-        for (int q = threadIdx.x; q < mtT; q += 256) down[q] = make_int4(E, q * bm, 0, nT);
-    const int up0 = S * mtT, down0 = S > 0 ? mtT : 0;
     const int nfull = pre[E] - hpre[E];
-    for (int g = threadIdx.x; g < E; g += 256) {
-        const int rb = offsets[g], n = offsets[g + 1] - offsets[g];
-        const int half = hpre[g + 1] - hpre[g];
-        for (int m = 0; m < mt[g]; ++m) {
-            const int4 t = make_int4(g, m * bm, rb, n);
-            const int at = m < mt[g] - half ? fpre[g] + m : nfull + hpre[g];
-            up[up0 + at] = t;
-            down[down0 + at] = t;
+    // one projection's list: the shared groups, the routed full m-tiles
+    // group by group, then the routed half m-tiles
+    auto write_list = [&](int4* list, int ntn, bool down) {
+        const int nsh_mt = down ? (S > 0 ? mtT : 0) : S * mtT;
+        const int nsg = down ? (S > 0 ? 1 : 0) : S;  // shared groups in this list
+        for (int q = 0; q < nsg; ++q)
+            write_group(list + static_cast<int64_t>(q) * mtT * ntn, E + q, 0, mtT, bm, 0, nT, ntn);
+        int4* routed = list + static_cast<int64_t>(nsh_mt) * ntn;
+        for (int g = 0; g < E; ++g) {
+            const int rb = offsets[g], n = offsets[g + 1] - offsets[g];
+            const int half = hpre[g + 1] - hpre[g];
+            write_group(routed + static_cast<int64_t>(fpre[g]) * ntn, g, 0, mt[g] - half, bm, rb, n, ntn);
+            if (half)
+                write_group(routed + static_cast<int64_t>(nfull + hpre[g]) * ntn, g, mt[g] - 1, 1, bm,
+                            rb, n, ntn);
         }
-    }
+    };
+    write_list(tiles, ntn_up, false);
+    write_list(tiles + n_up, ntn_down, true);
 }
 
 struct GemmArgs {
@@ -467,19 +494,18 @@ __device__ __forceinline__ i32x4 load_uniform(const int4* p) {
     return *(const __attribute__((address_space(4))) i32x4*)(p);
 }
 
-// Tile L of a projection's list: m-tile L / ntn (a descriptor written by the
-// plan kernel; the first nsh m-tiles are the shared experts'), n-tile L % ntn.
+// Tile L of a projection's list (a descriptor written by the plan kernel;
+// the first nsh * ntn tiles are the shared experts').
 template <int MODE>
 __device__ __forceinline__ TileInfo decode_tile(const GemmArgs& a, int L, int nsh) {
     TileInfo ti;
-    const int mtg = L / a.ntn;
-    ti.nt = L - mtg * a.ntn;
-    const i32x4 t = load_uniform(a.tiles + mtg);
-    ti.g = t[0];
+    const i32x4 t = load_uniform(a.tiles + L);
+    ti.g = t[0] & 0xffff;
+    ti.nt = t[0] >> 16;
     ti.m0 = t[1];
     ti.row_base = t[2];
     ti.nrows = t[3];
-    ti.shared = mtg < nsh;
+    ti.shared = L < nsh * a.ntn;
     ti.half = ti.nrows - ti.m0 <= kBigBM / 2;
     const int K = MODE == kModeDown ? (ti.shared ? a.S * a.h : a.h) : a.d;
     ti.KT = K / kBigBK;
@@ -795,42 +821,55 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
         const int Cn2 = lds_next[0];
 
         // epilogue: acc[mb][nb][v] is token (m0 + wm*128 + mb*32 + lr) and
-        // weight row (wn*64 + nb*32 + 8*(v/4) + 4*lg + v%4) of the tile
+        // weight row (wn*64 + nb*32 + 8*(v/4) + 4*lg + v%4) of the tile. A
+        // lane packs four bf16 per group q of 8 columns; lanes lr and lr+32
+        // hold the two halves of each group (lg). One half-wave swap per
+        // pair of groups gives lane lg=0 the 8 columns of group 2p and lane
+        // lg=1 those of group 2p+1, so each lane stores 16 contiguous bytes.
         bf16_t* out = reinterpret_cast<bf16_t*>(cur.shared ? a.out_shared : a.out_routed);
+        auto store_groups = [&](bf16_t* rowp, const uint32_t (&w)[4][2], bool ok) {
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const auto s0 = __builtin_amdgcn_permlane32_swap(w[2 * p][0], w[2 * p + 1][0], false, false);
+                const auto s1 = __builtin_amdgcn_permlane32_swap(w[2 * p][1], w[2 * p + 1][1], false, false);
+                if (ok) store16(rowp + 16 * p + 8 * lg, u32x4{s0[0], s1[0], s0[1], s1[1]});
+            }
+        };
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             const int r = cur.m0 + wm * kBigWM + mb * 32 + lr;
-            if (r >= cur.nrows) continue;
+            const bool ok = r < cur.nrows;  // the same for lanes lr and lr+32
             const int64_t row = static_cast<int64_t>(cur.row_base) + r;
             if (MODE == kModeDown) {
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
+                for (int nb = 0; nb < NB; ++nb) {
+                    uint32_t w[4][2];
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const int col = cur.nt * kBigBN + wn * kBigWN + nb * 32 + 8 * q + 4 * lg;
-                        uint2 w;
-                        w.x = pack_bf16x2(acc[mb][nb][4 * q], acc[mb][nb][4 * q + 1]);
-                        w.y = pack_bf16x2(acc[mb][nb][4 * q + 2], acc[mb][nb][4 * q + 3]);
-                        *reinterpret_cast<uint2*>(out + row * a.d + col) = w;
+                        w[q][0] = pack_bf16x2(acc[mb][nb][4 * q], acc[mb][nb][4 * q + 1]);
+                        w[q][1] = pack_bf16x2(acc[mb][nb][4 * q + 2], acc[mb][nb][4 * q + 3]);
                     }
+                    const int col = cur.nt * kBigBN + wn * kBigWN + nb * 32;
+                    store_groups(out + row * a.d + col, w, ok);
+                }
             } else {
                 const int ldo = cur.shared ? a.S * a.h : a.h;
                 const int cbase = (cur.shared ? (cur.g - a.E) * a.h : 0) + cur.nt * (kBigBN / 2) +
                                   wn * (kBigWN / 2);
 #pragma unroll
-                for (int pq = 0; pq < NB / 2; ++pq)
+                for (int pq = 0; pq < NB / 2; ++pq) {
+                    uint32_t w[4][2];
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const int col = cbase + pq * 32 + 8 * q + 4 * lg;
                         float hv[4];
 #pragma unroll
                         for (int u = 0; u < 4; ++u)
                             hv[u] = silu(acc[mb][2 * pq][4 * q + u]) * acc[mb][2 * pq + 1][4 * q + u];
-                        uint2 w;
-                        w.x = pack_bf16x2(hv[0], hv[1]);
-                        w.y = pack_bf16x2(hv[2], hv[3]);
-                        *reinterpret_cast<uint2*>(out + row * ldo + col) = w;
+                        w[q][0] = pack_bf16x2(hv[0], hv[1]);
+                        w[q][1] = pack_bf16x2(hv[2], hv[3]);
                     }
+                    store_groups(out + row * ldo + cbase + pq * 32, w, ok);
+                }
             }
         }
         // the epilogue's stores also count in vmcnt: drain before the next
@@ -950,15 +989,18 @@ __global__ __launch_bounds__(256) void ffn_gemm_f32_kernel(GemmArgs a, int mt_ma
 // persistent kernels (16 bytes each).
 struct PlanLayout {
     size_t counters, tiles, bytes;
-    int n_up, n_down;
+    int n_up, n_down;      // tile descriptors of each projection
+    int ntn_up, ntn_down;  // n-tiles per group
 };
 
 PlanLayout plan_layout(const moe_shape& s) {
     PlanLayout p;
     const int64_t mtT = (s.T + kBigBM - 1) / kBigBM;
     const int64_t rmax = s.T * s.k / kBigBM + s.E;  // routed m-tiles, at most
-    p.n_up = static_cast<int>(s.S * mtT + rmax);
-    p.n_down = static_cast<int>(mtT + rmax);
+    p.ntn_up = 2 * s.h / kBigBN;
+    p.ntn_down = s.d / kBigBN;
+    p.n_up = static_cast<int>((s.S * mtT + rmax) * p.ntn_up);
+    p.n_down = static_cast<int>((mtT + rmax) * p.ntn_down);
     p.counters = ((static_cast<size_t>(s.E + s.S + 1) * 4 + 63) / 64) * 64;
     p.tiles = p.counters + 128;  // 16 counters, then the m-tile counts
     p.bytes = p.tiles + static_cast<size_t>(p.n_up + p.n_down) * sizeof(int4);
@@ -1038,7 +1080,7 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const floa
     int32_t* counters = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(plan) + pl.counters);
     int4* tiles = reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(plan) + pl.tiles);
     ffn_plan_kernel<<<1, 256, 0, st>>>(offsets, s.E, s.S, s.T, bm, plan, big ? tiles : nullptr,
-                                       pl.n_up, counters);
+                                       pl.n_up, pl.ntn_up, pl.ntn_down, counters);
     mark(mk);
 
     GemmArgs a;
