@@ -46,31 +46,61 @@ constexpr int kF32BM = 64, kF32BN = 64, kF32BK = 16;
 //                               S > 0), then the routed ones, in the same
 //                               order;
 // sized for the bound on routed m-tiles. Within a group the tiles go in
-// supertiles (write_group).
-// words after the 16 tile counters: routed half and full m-tile counts
+// supertiles (swz_tile). Every block computes the prefix sums; block 0
+// writes plan[] and the counters, and the blocks share out the tiles.
+// Words after the 16 tile counters: routed half and full m-tile counts.
 constexpr int kTileMetaHalf = 16, kTileMetaFull = 17;
 
-// Writes the tiles of M m-tiles (from m-tile m_first) by ntn n-tiles of
-// group g, all threads of the block together, in supertiles of
-// kSwzM x kSwzN: n-blocks of kSwzN n-tiles, within those m-blocks of kSwzM
-// m-tiles, within a supertile n-major. Tiles that follow each other in the
-// list then share operand panels (an m-tile's token rows, an n-tile's weight
-// rows), so work-groups that take them at about the same time find the
-// panels in L2. Tile i: {g | nt << 16, first row, row base, rows}.
+// Tiles go in supertiles of kSwzM x kSwzN within a group: n-blocks of kSwzN
+// n-tiles, within those m-blocks of kSwzM m-tiles, within a supertile
+// n-major. Tiles that follow each other in the list then share operand
+// panels (an m-tile's token rows, an n-tile's weight rows), so work-groups
+// that take them at about the same time find the panels in L2.
 constexpr int kSwzM = 4, kSwzN = 4;
-__device__ void write_group(int4* out, int g, int m_first, int M, int bm, int rb, int n, int ntn) {
-    const int N = ntn;
-    for (int i = threadIdx.x; i < M * N; i += blockDim.x) {
-        const int nb = i / (kSwzN * M);
-        const int w = min(kSwzN, N - nb * kSwzN);
-        const int j = i - nb * kSwzN * M;
-        const int mb = j / (kSwzM * w);
-        const int hgt = min(kSwzM, M - mb * kSwzM);
-        const int jj = j - mb * kSwzM * w;
-        const int nt = nb * kSwzN + jj / hgt;
-        const int m = m_first + mb * kSwzM + jj % hgt;
-        out[i] = make_int4(g | (nt << 16), m * bm, rb, n);
+// tile j of an M x N grid in that order -> (m, nt)
+__device__ __forceinline__ void swz_tile(int M, int N, int j, int& m, int& nt) {
+    const int nb = j / (kSwzN * M);
+    const int w = min(kSwzN, N - nb * kSwzN);
+    const int r = j - nb * kSwzN * M;
+    const int mb = r / (kSwzM * w);
+    const int hgt = min(kSwzM, M - mb * kSwzM);
+    const int rr = r - mb * kSwzM * w;
+    nt = nb * kSwzN + rr / hgt;
+    m = mb * kSwzM + rr % hgt;
+}
+
+// out[0..n] = exclusive prefix sums of in[0..n) (out[n] = the total), by
+// one wave: each lane sums a run of consecutive entries, the runs' sums are
+// scanned across lanes. in and out may be the same LDS array.
+__device__ void wave_exclusive_scan(const int* in, int* out, int n) {
+    const int lane = threadIdx.x & 63;
+    const int per = (n + 63) / 64, b = min(n, lane * per), e = min(n, b + per);
+    int run = 0;
+    for (int i = b; i < e; ++i) run += in[i];
+    int incl = run;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t;
     }
+    int acc = incl - run;
+    for (int i = b; i < e; ++i) {
+        const int v = in[i];
+        out[i] = acc;
+        acc += v;
+    }
+    if (lane == 63) out[n] = incl;
+}
+
+// the last g in [0, n) with key[g] <= v (key non-decreasing, key[0] <= v)
+__device__ __forceinline__ int last_le(const int* key, int n, int v) {
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (key[mid] <= v) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
 }
 
 __global__ __launch_bounds__(256) void ffn_plan_kernel(const int32_t* __restrict__ offsets,
@@ -79,62 +109,71 @@ __global__ __launch_bounds__(256) void ffn_plan_kernel(const int32_t* __restrict
                                                        int4* __restrict__ tiles, int n_up,
                                                        int ntn_up, int ntn_down,
                                                        int32_t* __restrict__ counters) {
+    __shared__ int off_s[kMaxE + 1];
     __shared__ int mt[kMaxE + kMaxS];
     __shared__ int pre[kMaxE + kMaxS + 1];
-    __shared__ int fpre[kMaxE], hpre[kMaxE + 1];
+    __shared__ int fpre[kMaxE + 1], hpre[kMaxE + 1];
     const int G = E + S;
-    for (int g = threadIdx.x; g < G; g += 256) {
-        const int64_t n = g < E ? static_cast<int64_t>(offsets[g + 1] - offsets[g]) : T;
+    for (int g = threadIdx.x; g <= E; g += blockDim.x) off_s[g] = offsets[g];
+    __syncthreads();
+    for (int g = threadIdx.x; g < G; g += blockDim.x) {
+        const int64_t n = g < E ? static_cast<int64_t>(off_s[g + 1] - off_s[g]) : T;
         mt[g] = static_cast<int>((n + bm - 1) / bm);
     }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int s = 0;
-        for (int g = 0; g < G; ++g) {
-            pre[g] = s;
-            plan[g] = s;
-            s += mt[g];
-        }
-        pre[G] = s;
-        plan[G] = s;
-        // a routed group's last m-tile holding at most bm/2 rows is a half
-        // tile; the persistent kernels schedule those after all full tiles
-        int f = 0, h = 0;
-        for (int g = 0; g < E; ++g) {
-            const int n = offsets[g + 1] - offsets[g];
-            const int half = mt[g] > 0 && n - (mt[g] - 1) * bm <= bm / 2 ? 1 : 0;
-            fpre[g] = f;
-            hpre[g] = h;
-            f += mt[g] - half;
-            h += half;
-        }
-        hpre[E] = h;
-        if (tiles != nullptr) {
-            counters[kTileMetaHalf] = h;
-            counters[kTileMetaFull] = f;
-        }
+    // a routed group's last m-tile holding at most bm/2 rows is a half
+    // tile; the persistent kernels schedule those after all full tiles
+    for (int g = threadIdx.x; g < E; g += blockDim.x) {
+        const int n = off_s[g + 1] - off_s[g];
+        hpre[g] = mt[g] > 0 && n - (mt[g] - 1) * bm <= bm / 2 ? 1 : 0;
+        fpre[g] = mt[g] - hpre[g];
     }
     __syncthreads();
+    // exclusive prefix sums, one wave each
+    const int wave = threadIdx.x >> 6;
+    if (wave == 0) wave_exclusive_scan(mt, pre, G);
+    if (wave == 1) wave_exclusive_scan(fpre, fpre, E);
+    if (wave == 2) wave_exclusive_scan(hpre, hpre, E);
+    __syncthreads();
+    if (blockIdx.x == 0) {
+        for (int g = threadIdx.x; g <= G; g += blockDim.x) plan[g] = pre[g];
+        if (tiles != nullptr) {
+            if (threadIdx.x == 0) {
+                counters[kTileMetaHalf] = hpre[E];
+                counters[kTileMetaFull] = fpre[E];
+            }
+            if (threadIdx.x < 16) counters[threadIdx.x] = 0;
+        }
+    }
     if (tiles == nullptr) return;
-    if (threadIdx.x < 16) counters[threadIdx.x] = 0;
     const int mtT = static_cast<int>((T + bm - 1) / bm);
     const int nT = static_cast<int>(T);
-    const int nfull = pre[E] - hpre[E];
+    const int nfull = fpre[E], nhalf = hpre[E];
     // one projection's list: the shared groups, the routed full m-tiles
-    // group by group, then the routed half m-tiles
+    // group by group, then the routed half m-tiles; every thread takes
+    // tiles in turn and finds its group by binary search
     auto write_list = [&](int4* list, int ntn, bool down) {
-        const int nsh_mt = down ? (S > 0 ? mtT : 0) : S * mtT;
         const int nsg = down ? (S > 0 ? 1 : 0) : S;  // shared groups in this list
-        for (int q = 0; q < nsg; ++q)
-            write_group(list + static_cast<int64_t>(q) * mtT * ntn, E + q, 0, mtT, bm, 0, nT, ntn);
-        int4* routed = list + static_cast<int64_t>(nsh_mt) * ntn;
-        for (int g = 0; g < E; ++g) {
-            const int rb = offsets[g], n = offsets[g + 1] - offsets[g];
-            const int half = hpre[g + 1] - hpre[g];
-            write_group(routed + static_cast<int64_t>(fpre[g]) * ntn, g, 0, mt[g] - half, bm, rb, n, ntn);
-            if (half)
-                write_group(routed + static_cast<int64_t>(nfull + hpre[g]) * ntn, g, mt[g] - 1, 1, bm,
-                            rb, n, ntn);
+        const int nsh = nsg * mtT * ntn;
+        const int i0 = blockIdx.x * blockDim.x + threadIdx.x, stride = gridDim.x * blockDim.x;
+        for (int i = i0; i < nsh; i += stride) {
+            const int q = i / (mtT * ntn);
+            int m, nt;
+            swz_tile(mtT, ntn, i - q * mtT * ntn, m, nt);
+            list[i] = make_int4((E + q) | (nt << 16), m * bm, 0, nT);
+        }
+        int4* routed = list + nsh;
+        for (int i = i0; i < nfull * ntn; i += stride) {
+            const int g = last_le(fpre, E, i / ntn);
+            const int j = i - fpre[g] * ntn;
+            int m, nt;
+            swz_tile(fpre[g + 1] - fpre[g], ntn, j, m, nt);
+            routed[i] = make_int4(g | (nt << 16), m * bm, off_s[g], off_s[g + 1] - off_s[g]);
+        }
+        for (int i = i0; i < nhalf * ntn; i += stride) {
+            const int g = last_le(hpre, E, i / ntn);
+            const int nt = i - hpre[g] * ntn;
+            routed[nfull * ntn + i] =
+                make_int4(g | (nt << 16), (mt[g] - 1) * bm, off_s[g], off_s[g + 1] - off_s[g]);
         }
     };
     write_list(tiles, ntn_up, false);
@@ -1079,8 +1118,13 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const floa
     const PlanLayout pl = plan_layout(s);
     int32_t* counters = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(plan) + pl.counters);
     int4* tiles = reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(plan) + pl.tiles);
-    ffn_plan_kernel<<<1, 256, 0, st>>>(offsets, s.E, s.S, s.T, bm, plan, big ? tiles : nullptr,
-                                       pl.n_up, pl.ntn_up, pl.ntn_down, counters);
+    // every block redoes the prefix sums; the tile lists are shared out
+    const int plan_blocks = big ? static_cast<int>(std::min<int64_t>(
+                                      64, (std::max(pl.n_up, pl.n_down) + 255) / 256))
+                                : 1;
+    ffn_plan_kernel<<<std::max(plan_blocks, 1), 256, 0, st>>>(
+        offsets, s.E, s.S, s.T, bm, plan, big ? tiles : nullptr, pl.n_up, pl.ntn_up, pl.ntn_down,
+        counters);
     mark(mk);
 
     GemmArgs a;
