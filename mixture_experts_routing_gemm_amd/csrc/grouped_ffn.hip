@@ -249,14 +249,15 @@ __device__ __forceinline__ uint32_t dequant2(float lo, float hi, float scale, fl
 }
 __device__ __forceinline__ u32x4 dequant8(uint2 codes, float scale, float centre) {
     u32x4 out;
-    out[0] = dequant2(__builtin_amdgcn_cvt_f32_fp8(codes.x, 0), __builtin_amdgcn_cvt_f32_fp8(codes.x, 1),
-                      scale, centre);
-    out[1] = dequant2(__builtin_amdgcn_cvt_f32_fp8(codes.x, 2), __builtin_amdgcn_cvt_f32_fp8(codes.x, 3),
-                      scale, centre);
-    out[2] = dequant2(__builtin_amdgcn_cvt_f32_fp8(codes.y, 0), __builtin_amdgcn_cvt_f32_fp8(codes.y, 1),
-                      scale, centre);
-    out[3] = dequant2(__builtin_amdgcn_cvt_f32_fp8(codes.y, 2), __builtin_amdgcn_cvt_f32_fp8(codes.y, 3),
-                      scale, centre);
+    // v_cvt_pk_f32_fp8: codes 0,1 (false) or 2,3 (true) of a word
+    const auto p0 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(codes.x), false);
+    const auto p1 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(codes.x), true);
+    const auto p2 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(codes.y), false);
+    const auto p3 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(codes.y), true);
+    out[0] = dequant2(p0[0], p0[1], scale, centre);
+    out[1] = dequant2(p1[0], p1[1], scale, centre);
+    out[2] = dequant2(p2[0], p2[1], scale, centre);
+    out[3] = dequant2(p3[0], p3[1], scale, centre);
     return out;
 }
 
@@ -524,7 +525,6 @@ struct TileSrc {
     bool shared;
     uint32_t aoff[2];  // token rows of this lane's DMA chunks
     uint32_t boff[2];  // weight rows of this lane's DMA chunks
-    float qs[kBigMB], qc[kBigMB];  // fp8 rows of this lane's fragments
 };
 
 // a 16-byte load from a wave-uniform address, through the scalar unit
@@ -551,11 +551,32 @@ __device__ __forceinline__ TileInfo decode_tile(const GemmArgs& a, int L, int ns
     return ti;
 }
 
+// (scale, centre) of the fp8 token rows of this lane's A fragments: row
+// wm*128 + mb*32 + lr of the tile (zero for bf16 rows). Held for one tile
+// only; the next tile's are loaded during the epilogue, whose stores are
+// drained anyway, so that no second set stays live through the K loop.
+template <int MODE>
+__device__ __forceinline__ void tile_qparams(const GemmArgs& a, const TileInfo& ti, int wave,
+                                             int lane, float (&qs)[kBigMB], float (&qc)[kBigMB]) {
+    const bool fp8 = MODE == kModeUpFp8 && !ti.shared;
+    const int last = ti.nrows - 1;
+#pragma unroll
+    for (int mb = 0; mb < kBigMB; ++mb) {
+        qs[mb] = 0.0f;
+        qc[mb] = 0.0f;
+        if (fp8) {
+            const int64_t row =
+                ti.row_base + min(ti.m0 + (wave >> 2) * kBigWM + mb * 32 + (lane & 31), last);
+            const float2 q = *reinterpret_cast<const float2*>(a.qparams + 2 * row);
+            qs[mb] = q.x;
+            qc[mb] = q.y;
+        }
+    }
+}
+
 template <int MODE>
 __device__ __forceinline__ void tile_sources(const GemmArgs& a, const TileInfo& ti, int wave,
                                              int lane, TileSrc& src) {
-    const int wm = wave >> 2;
-    const int lr = lane & 31;
     const bool fp8 = MODE == kModeUpFp8 && !ti.shared;
     const int K = MODE == kModeDown ? (ti.shared ? a.S * a.h : a.h) : a.d;
     const int last = ti.nrows - 1;
@@ -577,16 +598,6 @@ __device__ __forceinline__ void tile_sources(const GemmArgs& a, const TileInfo& 
             const int c = (lane & 3) ^ (((r >> 1) & 3) ^ ((r >> 3) & 1));
             const int64_t row = ti.row_base + min(ti.m0 + r, last);
             src.aoff[i] = static_cast<uint32_t>(row * K * 2 + c * 16);
-        }
-    }
-#pragma unroll
-    for (int mb = 0; mb < kBigMB; ++mb) {
-        src.qs[mb] = 0.0f;
-        src.qc[mb] = 0.0f;
-        if (fp8) {
-            const int64_t row = ti.row_base + min(ti.m0 + wm * kBigWM + mb * 32 + lr, last);
-            src.qs[mb] = a.qparams[2 * row];
-            src.qc[mb] = a.qparams[2 * row + 1];
         }
     }
     src.gofs = static_cast<uint32_t>(MODE == kModeDown && ti.shared ? a.E : ti.g) * a.d * a.h * 2;
@@ -629,6 +640,19 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int wn = wave & 3, wm = wave >> 2;
     const int lr = lane & 31, lg = lane >> 5;
+    // operand bases and sizes as wave-uniform values, chosen by value below
+    // (a choice between two fields of the argument struct can otherwise
+    // become a load through a chosen address, from a private copy)
+    const uint8_t* const op_ar = uniform_ptr(a.a_routed);
+    const uint8_t* const op_as = uniform_ptr(a.a_shared);
+    const uint32_t by_ar = __builtin_amdgcn_readfirstlane(a.a_routed_bytes);
+    const uint32_t by_as = __builtin_amdgcn_readfirstlane(a.a_shared_bytes);
+    const uint32_t by_w = __builtin_amdgcn_readfirstlane(a.w_bytes);
+    // up-projection: a wave's weight rows lie in one 32-row block, W1 for
+    // even waves and W3 for odd ones
+    const uint8_t* const op_w = uniform_ptr(MODE != kModeDown && (wave & 1) ? a.wb : a.wa);
+    bf16_t* const out_r = reinterpret_cast<bf16_t*>(const_cast<uint8_t*>(uniform_ptr(a.out_routed)));
+    bf16_t* const out_s = reinterpret_cast<bf16_t*>(const_cast<uint8_t*>(uniform_ptr(a.out_shared)));
 
     // The tile list: the shared m-tiles first (in the down-projection each
     // runs over S hidden blocks, S times the work of a routed tile), then the
@@ -663,13 +687,19 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
     int32_t* counter = a.counters + xcd;
     if (tid == 0) lds_next[0] = per_xcd + atomicAdd(counter, 1);
     __syncthreads();
-    int Cn = lds_next[0];
+    int Cn = __builtin_amdgcn_readfirstlane(lds_next[0]);
 
     TileInfo cur = decode_tile<MODE>(a, tile_of(C), nsh);
     TileSrc src;
     tile_sources<MODE>(a, cur, wave, lane, src);
     TileInfo nxt = cur;
     TileSrc nsrc = src;
+    float qs[MB], qc[MB];
+    if constexpr (kFp8) tile_qparams<MODE>(a, cur, wave, lane, qs, qc);
+    // the claim on the tile after next; later ones are issued at the end of
+    // each epilogue, whose drain of the stores also waits for the claim
+    int claim = 0;
+    if (Cn < nclaim && tid == 0) claim = atomicAdd(counter, 1);
 
     // Requests of slice k of a tile into ring slot `slot`: kBigLoads
     // buffer-to-LDS instructions per wave, issued one at a time (i). Wave w
@@ -702,24 +732,25 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
     };
     auto issue_one = [&](const TileSrc& ts, bool shared, const SliceReq& q, auto I) {
         constexpr int i = decltype(I)::value;
-        const uint8_t* abuf = shared ? a.a_shared : a.a_routed;
-        const uint32_t abytes = shared ? a.a_shared_bytes : a.a_routed_bytes;
-        // up-projection: a wave's weight rows lie in one 32-row block, W1 for
-        // even waves and W3 for odd ones
-        const uint8_t* wbuf = MODE != kModeDown && (wave & 1) ? a.wb : a.wa;
+        // every operand of a buffer resource must be wave-uniform (the
+        // compiler cannot prove it for a tile read back from LDS, and would
+        // otherwise loop over lanes and drain the outstanding requests)
+        const uint8_t* abuf = uniform_ptr(shared ? op_as : op_ar);
+        const uint32_t abytes = __builtin_amdgcn_readfirstlane(shared ? by_as : by_ar);
+        const uint8_t* wbuf = op_w;
         if constexpr (i < 2) {
             if (kFp8 && !shared) {
                 // fp8 rows take one request; the other rewrites weight rows
                 if constexpr (i == 0)
                     buffer_to_lds16<0>(abuf, abytes, ts.aoff[0], q.ka, q.abase);
                 else
-                    buffer_to_lds16<0>(wbuf, a.w_bytes, ts.boff[0], q.kb, q.bbase);
+                    buffer_to_lds16<0>(wbuf, by_w, ts.boff[0], q.kb, q.bbase);
             } else {
                 buffer_to_lds16<1024 * i>(abuf, abytes, ts.aoff[i], q.ka, q.abase);
             }
         } else {
             constexpr int b = i - 2;
-            buffer_to_lds16<1024 * b>(wbuf, a.w_bytes, ts.boff[b], q.kb, q.bbase);
+            buffer_to_lds16<1024 * b>(wbuf, by_w, ts.boff[b], q.kb, q.bbase);
         }
     };
     auto issue = [&](const TileSrc& ts, bool shared, int k, int slot) {
@@ -741,8 +772,12 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
             const int mb = i - NB;
             const int r = wm * kBigWM + mb * 32 + lr;
             if (kFp8 && !shared) {
-                const uint2 codes = *reinterpret_cast<const uint2*>(As + lds_off32_fp8(r, ch));
-                fa[mb] = __builtin_bit_cast(bf16x8, dequant8(codes, ts.qs[mb], ts.qc[mb]));
+                // read as the same vector type as the bf16 fragments (a
+                // struct-typed read here made the compiler wait for every
+                // outstanding direct-to-LDS request first)
+                typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                const bf16x4 raw = *reinterpret_cast<const bf16x4*>(As + lds_off32_fp8(r, ch));
+                fa[mb] = __builtin_bit_cast(bf16x8, dequant8(__builtin_bit_cast(uint2, raw), qs[mb], qc[mb]));
             } else {
                 fa[mb] = *reinterpret_cast<const bf16x8*>(As + lds_off32(r, ch));
             }
@@ -767,14 +802,12 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
     bf16x8 fa0[MB], fb0[NB], fa1[MB], fb1[NB];
     while (true) {
         const bool has_next = Cn < nclaim;
-        // the next tile's descriptor (a scalar load) and a claim on the tile
-        // after it (published to the other waves before the last four
-        // slices). After the last tile the "next" tile is this one again: its
-        // first slices are re-read into free slots and never used, which
-        // keeps the last steps the same for every tile.
+        // the next tile's descriptor (a scalar load); the claim on the tile
+        // after it is already in `claim` and goes out to the other waves
+        // before the last four slices. After the last tile the "next" tile
+        // is this one again: its first slices are re-read into free slots and
+        // never used, which keeps the last steps the same for every tile.
         if (has_next) nxt = decode_tile<MODE>(a, tile_of(Cn), nsh);
-        int claim = 0;
-        if (has_next && tid == 0) claim = atomicAdd(counter, 1);
 
         wait_vmcnt<2 * kBigLoads>();  // slice 0 of this tile has landed
         ring_barrier();
@@ -857,7 +890,7 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
             k_loop(std::true_type{});
         else
             k_loop(std::false_type{});
-        const int Cn2 = lds_next[0];
+        const int Cn2 = __builtin_amdgcn_readfirstlane(lds_next[0]);
 
         // epilogue: acc[mb][nb][v] is token (m0 + wm*128 + mb*32 + lr) and
         // weight row (wn*64 + nb*32 + 8*(v/4) + 4*lg + v%4) of the tile. A
@@ -865,7 +898,7 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
         // hold the two halves of each group (lg). One half-wave swap per
         // pair of groups gives lane lg=0 the 8 columns of group 2p and lane
         // lg=1 those of group 2p+1, so each lane stores 16 contiguous bytes.
-        bf16_t* out = reinterpret_cast<bf16_t*>(cur.shared ? a.out_shared : a.out_routed);
+        bf16_t* out = cur.shared ? out_s : out_r;
         auto store_groups = [&](bf16_t* rowp, const uint32_t (&w)[4][2], bool ok) {
 #pragma unroll
             for (int p = 0; p < 2; ++p) {
@@ -911,6 +944,10 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
                 }
             }
         }
+        if constexpr (kFp8)
+            if (has_next) tile_qparams<MODE>(a, nxt, wave, lane, qs, qc);
+        // the next tile's claim on the one after it
+        if (has_next && Cn2 < nclaim && tid == 0) claim = atomicAdd(counter, 1);
         // the epilogue's stores also count in vmcnt: drain before the next
         // tile's counted waits (and, after the last tile, let the re-read
         // slices land before the work-group's LDS is released)
