@@ -476,9 +476,26 @@ constexpr int kBufferFlags = 0x00020000;
 __device__ __forceinline__ int lds_off32(int r, int c) {
     return ((r >> 6) << 13) + ((r & 63) << 6) + ((c ^ (((r >> 1) & 3) ^ ((r >> 3) & 1))) << 4);
 }
-// byte offset of 8-code group g8 (0..3) of fp8 row r (32 codes)
-__device__ __forceinline__ int lds_off32_fp8(int r, int g8) {
-    return ((r >> 6) << 13) + ((r & 63) << 5) + (((g8 >> 1) ^ ((r >> 3) & 1)) << 4) + ((g8 & 1) << 3);
+// fp8 token rows: wave w's request lands the codes of rows 32w..32w+31 (32 B
+// each, plain order) in the upper half of the 2 KB those rows take as bf16,
+// so that the wave can convert them in place.
+__device__ __forceinline__ int fp8_codes_off(int wave) {
+    return (wave >> 1) * 8192 + (wave & 1) * 2048 + 1024;
+}
+
+// Converts the 16 codes `w` this lane's request brought into `slot` (row
+// 32*wave + lane/2, K offsets 16*(lane&1)..+15, read from fp8_codes_off) to
+// bf16 code*scale + centre and writes them where the bf16 fragment reads
+// expect that row. The wave has read all its codes before it writes (a
+// wave's LDS accesses complete in order), so the in-place overwrite is safe;
+// no other wave touches these bytes until the next barrier.
+__device__ __forceinline__ void convert_codes(uint8_t* slot, int wave, int lane, u32x4 w,
+                                              float scale, float centre) {
+    const u32x4 lo = dequant8(uint2{w[0], w[1]}, scale, centre);
+    const u32x4 hi = dequant8(uint2{w[2], w[3]}, scale, centre);
+    const int r = wave * 32 + (lane >> 1), ch = 2 * (lane & 1);
+    *reinterpret_cast<bf16x8*>(slot + lds_off32(r, ch)) = __builtin_bit_cast(bf16x8, lo);
+    *reinterpret_cast<bf16x8*>(slot + lds_off32(r, ch + 1)) = __builtin_bit_cast(bf16x8, hi);
 }
 
 // Work-group barrier without the release/acquire fences of __syncthreads():
@@ -521,10 +538,13 @@ struct TileInfo {
 // W3). In the up-projection the weight rows of a wave's DMA requests come
 // from W1 for even waves and from W3 for odd ones.
 struct TileSrc {
+    const uint8_t* abuf;  // token operand of the tile (wave-uniform)
+    uint32_t abytes;      // its size in bytes
     uint32_t gofs;
     bool shared;
     uint32_t aoff[2];  // token rows of this lane's DMA chunks
     uint32_t boff[2];  // weight rows of this lane's DMA chunks
+    float cs, cc;      // fp8 rows: (scale, centre) of the row this lane converts
 };
 
 // a 16-byte load from a wave-uniform address, through the scalar unit
@@ -551,54 +571,45 @@ __device__ __forceinline__ TileInfo decode_tile(const GemmArgs& a, int L, int ns
     return ti;
 }
 
-// (scale, centre) of the fp8 token rows of this lane's A fragments: row
-// wm*128 + mb*32 + lr of the tile (zero for bf16 rows). Held for one tile
-// only; the next tile's are loaded during the epilogue, whose stores are
-// drained anyway, so that no second set stays live through the K loop.
-template <int MODE>
-__device__ __forceinline__ void tile_qparams(const GemmArgs& a, const TileInfo& ti, int wave,
-                                             int lane, float (&qs)[kBigMB], float (&qc)[kBigMB]) {
-    const bool fp8 = MODE == kModeUpFp8 && !ti.shared;
-    const int last = ti.nrows - 1;
-#pragma unroll
-    for (int mb = 0; mb < kBigMB; ++mb) {
-        qs[mb] = 0.0f;
-        qc[mb] = 0.0f;
-        if (fp8) {
-            const int64_t row =
-                ti.row_base + min(ti.m0 + (wave >> 2) * kBigWM + mb * 32 + (lane & 31), last);
-            const float2 q = *reinterpret_cast<const float2*>(a.qparams + 2 * row);
-            qs[mb] = q.x;
-            qc[mb] = q.y;
-        }
-    }
-}
-
 template <int MODE>
 __device__ __forceinline__ void tile_sources(const GemmArgs& a, const TileInfo& ti, int wave,
-                                             int lane, TileSrc& src) {
+                                             int lane, const uint8_t* op_ar, const uint8_t* op_as,
+                                             uint32_t by_ar, uint32_t by_as, TileSrc& src) {
+    // chosen here, by value, once per tile: a choice between two captured
+    // locals inside the request code became a load through a chosen
+    // address from a private copy
+    src.abuf = uniform_ptr(ti.shared ? op_as : op_ar);
+    src.abytes = __builtin_amdgcn_readfirstlane(ti.shared ? by_as : by_ar);
     const bool fp8 = MODE == kModeUpFp8 && !ti.shared;
     const int K = MODE == kModeDown ? (ti.shared ? a.S * a.h : a.h) : a.d;
     const int last = ti.nrows - 1;
     src.shared = ti.shared;
     // token DMA: a wave instruction fills 1 KB of LDS, lane i at byte 16*i:
-    // 16 bf16 rows of 64 B (row = wave*32 + i*16 + lane/4) or 32 fp8 rows of
-    // 32 B (row = wave*32 + lane/2); each lane fetches the chunk the swizzle
-    // places at its position. Rows past the group's end re-read its last
-    // row; their outputs are never stored.
+    // 16 bf16 rows of 64 B (row = wave*32 + i*16 + lane/4), each lane
+    // fetching the chunk the swizzle places at its position, or the codes of
+    // 32 fp8 rows of 32 B in plain order (row = wave*32 + lane/2, half
+    // lane&1), which the same lane converts to bf16 later. Rows past the
+    // group's end re-read its last row; their outputs are never stored.
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         if (fp8) {
             const int r = wave * 32 + (lane >> 1);
-            const int c = (lane & 1) ^ ((r >> 3) & 1);
             const int64_t row = ti.row_base + min(ti.m0 + r, last);
-            src.aoff[i] = static_cast<uint32_t>(row * K + c * 16);
+            src.aoff[i] = static_cast<uint32_t>(row * K + (lane & 1) * 16);
         } else {
             const int r = wave * 32 + i * 16 + (lane >> 2);
             const int c = (lane & 3) ^ (((r >> 1) & 3) ^ ((r >> 3) & 1));
             const int64_t row = ti.row_base + min(ti.m0 + r, last);
             src.aoff[i] = static_cast<uint32_t>(row * K * 2 + c * 16);
         }
+    }
+    src.cs = 0.0f;
+    src.cc = 0.0f;
+    if (fp8) {
+        const int64_t row = ti.row_base + min(ti.m0 + wave * 32 + (lane >> 1), last);
+        const float2 q = *reinterpret_cast<const float2*>(a.qparams + 2 * row);
+        src.cs = q.x;
+        src.cc = q.y;
     }
     src.gofs = static_cast<uint32_t>(MODE == kModeDown && ti.shared ? a.E : ti.g) * a.d * a.h * 2;
 #pragma unroll
@@ -691,11 +702,9 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
 
     TileInfo cur = decode_tile<MODE>(a, tile_of(C), nsh);
     TileSrc src;
-    tile_sources<MODE>(a, cur, wave, lane, src);
+    tile_sources<MODE>(a, cur, wave, lane, op_ar, op_as, by_ar, by_as, src);
     TileInfo nxt = cur;
     TileSrc nsrc = src;
-    float qs[MB], qc[MB];
-    if constexpr (kFp8) tile_qparams<MODE>(a, cur, wave, lane, qs, qc);
     // the claim on the tile after next; later ones are issued at the end of
     // each epilogue, whose drain of the stores also waits for the claim
     int claim = 0;
@@ -714,7 +723,8 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
     auto slice_req = [&](const TileSrc& ts, bool shared, int k, int slot) {
         SliceReq q;
         const int k0 = k * kBigBK;
-        q.abase = lds + slot * kBigSlot + (wave >> 1) * 8192 + (wave & 1) * (kFp8 && !shared ? 1024 : 2048);
+        q.abase = lds + slot * kBigSlot +
+                  (kFp8 && !shared ? fp8_codes_off(wave) : (wave >> 1) * 8192 + (wave & 1) * 2048);
         q.bbase = lds + slot * kBigSlot + (wave >> 1) * 8192 + 4096 + (wave & 1) * 2048;
         q.ka = static_cast<uint32_t>(kFp8 && !shared ? k0 : k0 * 2);
         uint32_t kb = static_cast<uint32_t>(k0) * 2;
@@ -735,8 +745,8 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
         // every operand of a buffer resource must be wave-uniform (the
         // compiler cannot prove it for a tile read back from LDS, and would
         // otherwise loop over lanes and drain the outstanding requests)
-        const uint8_t* abuf = uniform_ptr(shared ? op_as : op_ar);
-        const uint32_t abytes = __builtin_amdgcn_readfirstlane(shared ? by_as : by_ar);
+        const uint8_t* abuf = ts.abuf;
+        const uint32_t abytes = ts.abytes;
         const uint8_t* wbuf = op_w;
         if constexpr (i < 2) {
             if (kFp8 && !shared) {
@@ -771,16 +781,7 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
         } else {
             const int mb = i - NB;
             const int r = wm * kBigWM + mb * 32 + lr;
-            if (kFp8 && !shared) {
-                // read as the same vector type as the bf16 fragments (a
-                // struct-typed read here made the compiler wait for every
-                // outstanding direct-to-LDS request first)
-                typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-                const bf16x4 raw = *reinterpret_cast<const bf16x4*>(As + lds_off32_fp8(r, ch));
-                fa[mb] = __builtin_bit_cast(bf16x8, dequant8(__builtin_bit_cast(uint2, raw), qs[mb], qc[mb]));
-            } else {
-                fa[mb] = *reinterpret_cast<const bf16x8*>(As + lds_off32(r, ch));
-            }
+            fa[mb] = *reinterpret_cast<const bf16x8*>(As + lds_off32(r, ch));
         }
     };
     auto load_frags = [&](int slot, int ks, bf16x8* fa, bf16x8* fb, const TileSrc& ts, bool shared) {
@@ -794,10 +795,18 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
         acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[nb], fa[mb], acc[mb][nb], 0, 0, 0);
     };
 
-    // prologue: the first tile's slices 0..2
+    // prologue: the first tile's slices 0..2; fp8 rows of slice 0 are
+    // converted once this wave's request for them has landed (the barrier at
+    // the top of the tile loop publishes them)
     issue(src, cur.shared, 0, 0);
     issue(src, cur.shared, 1, 1);
     issue(src, cur.shared, 2, 2);
+    if (kFp8 && !cur.shared) {
+        wait_vmcnt<2 * kBigLoads>();
+        const u32x4 c0 = __builtin_bit_cast(
+            u32x4, *reinterpret_cast<const bf16x8*>(lds + fp8_codes_off(wave) + 16 * lane));
+        convert_codes(lds, wave, lane, c0, src.cs, src.cc);
+    }
 
     bf16x8 fa0[MB], fb0[NB], fa1[MB], fb1[NB];
     while (true) {
@@ -812,7 +821,7 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
         wait_vmcnt<2 * kBigLoads>();  // slice 0 of this tile has landed
         ring_barrier();
         if (has_next) {
-            tile_sources<MODE>(a, nxt, wave, lane, nsrc);
+            tile_sources<MODE>(a, nxt, wave, lane, op_ar, op_as, by_ar, by_as, nsrc);
         } else {
             nxt = cur;
             nsrc = src;
@@ -842,11 +851,29 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
             const TileSrc& ts = iss == 2 ? nsrc : src;
             const bool tsh = iss == 2 ? nxt.shared : cur.shared;
             const SliceReq q = slice_req(ts, tsh, iss == 2 ? k + 3 - KT : k + 3, (j + 3) & 3);
+            // fp8 rows: this wave converts its rows of slice k+1 (the next
+            // tile's slice 0 in a tile's last step), every wave alike, idle
+            // or not. Its codes request was the first of the eight issued
+            // in the last two steps, so at most seven may still be in flight.
+            const bool conv = kFp8 && !(wn_ < 0 ? nxt.shared : cur.shared);
+            const TileSrc& cts = wn_ < 0 ? nsrc : src;
+            uint8_t* const cslot = lds + ((j + 1) & 3) * kBigSlot;
+            u32x4 codes;
             static_for<0, MB * NB>([&](auto I) {
                 constexpr int i = decltype(I)::value;
+                if constexpr (kFp8 && i == 0) {
+                    if (conv) {
+                        wait_vmcnt<2 * kBigLoads - 1>();
+                        codes = __builtin_bit_cast(
+                            u32x4, *reinterpret_cast<const bf16x8*>(cslot + fp8_codes_off(wave) + 16 * lane));
+                    }
+                }
                 if constexpr (!idle) mma_one(fa0, fb0, i);
                 if constexpr (iss != 0 && i < kBigLoads) issue_one(ts, tsh, q, I);
                 if constexpr (!idle && i < MB + NB) read_frag(j, 1, fa1, fb1, src, cur.shared, i);
+                if constexpr (kFp8 && i == 2) {
+                    if (conv) convert_codes(cslot, wave, lane, codes, cts.cs, cts.cc);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             });
             if constexpr (wn_ >= 0) {
@@ -944,8 +971,6 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
                 }
             }
         }
-        if constexpr (kFp8)
-            if (has_next) tile_qparams<MODE>(a, nxt, wave, lane, qs, qc);
         // the next tile's claim on the one after it
         if (has_next && Cn2 < nclaim && tid == 0) claim = atomicAdd(counter, 1);
         // the epilogue's stores also count in vmcnt: drain before the next
