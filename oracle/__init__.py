@@ -51,13 +51,14 @@ def lib():
         L.oracle_gate_logits.argtypes = [i64, i32, i32, i32, vp, vp, vp, vp, i32]
         L.oracle_select_topk.argtypes = [i64, i32, i32, vp, vp, vp]
         L.oracle_dispatch.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp]
+        L.oracle_dispatch_capacity.argtypes = [i64, i32, i32, vp, i32, vp, vp, vp, vp]
         L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
         L.oracle_e4m3_decode.restype = ctypes.c_double
         L.oracle_e4m3_encode.argtypes = [ctypes.c_float]
         L.oracle_e4m3_encode.restype = ctypes.c_uint8
         L.oracle_fp8_quantize.argtypes = [i64, i32, i32, vp, vp, vp, i32]
         L.oracle_expert_rows.argtypes = [i32, i32, i32, i64, vp, vp, vp, vp, vp, vp, i32]
-        L.oracle_layer_tokens.argtypes = [i32, i32, i32, i32, i32, i32, i32, i64, vp,
+        L.oracle_layer_tokens.argtypes = [i32, i32, i32, i32, i32, i32, i32, i64, vp, vp,
                                           vp, vp, vp, vp, vp, vp, vp, vp, vp, i32]
         L.oracle_combine.argtypes = [i64, i32, i32, i32, vp, vp, vp, vp, i64, vp]
         L.oracle_bf16_to_float.argtypes = [ctypes.c_uint16]
@@ -117,16 +118,25 @@ def gate_topk(x, wg, k, bias=None, nthreads=1):
     return idx, w, z
 
 
-def dispatch(topk_idx, E):
-    """counts [E], offsets [E+1], dest_row [T,k], src_token [T*k] (int32)."""
+def dispatch(topk_idx, E, capacity=0):
+    """counts [E], offsets [E+1], dest_row [T,k], src_token [T*k] (int32).
+
+    capacity > 0: each expert keeps at most that many assignments, taken in
+    token order; the rest get dest_row -1 and no row, and src_token holds
+    offsets[E] meaningful entries (the rest are -1 here).
+    """
     idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
     T, k = idx.shape
     counts = np.empty(E, dtype=np.int32)
     offsets = np.empty(E + 1, dtype=np.int32)
     dest = np.empty((T, k), dtype=np.int32)
-    src = np.empty(T * k, dtype=np.int32)
-    _check(lib().oracle_dispatch(T, E, k, _p(idx), _p(counts), _p(offsets), _p(dest), _p(src)),
-           "dispatch")
+    src = np.full(T * k, -1, dtype=np.int32)
+    if capacity:
+        _check(lib().oracle_dispatch_capacity(T, E, k, _p(idx), int(capacity), _p(counts),
+                                              _p(offsets), _p(dest), _p(src)), "dispatch_capacity")
+    else:
+        _check(lib().oracle_dispatch(T, E, k, _p(idx), _p(counts), _p(offsets), _p(dest),
+                                     _p(src)), "dispatch")
     return counts, offsets, dest, src
 
 
@@ -169,8 +179,13 @@ def expert_rows(rows, group, w1, w3, w2, nthreads=1):
     return out
 
 
-def layer_tokens(inp, tokens, nthreads=1):
-    """Whole-layer output for the listed tokens: (topk_idx, topk_w, y float64)."""
+def layer_tokens(inp, tokens, nthreads=1, keep=None):
+    """Whole-layer output for the listed tokens: (topk_idx, topk_w, y float64).
+
+    keep [n, k] (bool, optional): the slots a capacity limit kept; a dropped
+    slot contributes nothing. Which slots are dropped depends on the whole
+    batch's routing, so the caller takes it from dispatch(..., capacity).
+    """
     cfg = inp.cfg
     tokens = np.ascontiguousarray(tokens, dtype=np.int64)
     n = tokens.shape[0]
@@ -179,7 +194,10 @@ def layer_tokens(inp, tokens, nthreads=1):
     y = np.empty((n, cfg.d), dtype=np.float64)
     b = None if inp.bias is None else np.ascontiguousarray(inp.bias, dtype=np.float32)
     _check(lib().oracle_layer_tokens(cfg.d, cfg.E, cfg.k, cfg.S, cfg.h, _dtype_code(inp.x),
-                                     1 if cfg.dispatch == "fp8" else 0, n, _p(tokens), _p(inp.x),
+                                     1 if cfg.dispatch == "fp8" else 0, n, _p(tokens),
+                                     _p(None if keep is None else
+                                        np.ascontiguousarray(keep, dtype=np.uint8).reshape(n, cfg.k)),
+                                     _p(inp.x),
                                      _p(inp.wg), _p(b), _p(inp.w1), _p(inp.w3), _p(inp.w2),
                                      _p(idx), _p(w), _p(y), _nthreads(nthreads)), "layer_tokens")
     return idx, w, y

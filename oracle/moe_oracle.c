@@ -27,6 +27,8 @@
  *              pair -- the reorder-and-pack step of the DeepEP notes
  *              (zzszmyf.github.io), section 7 "Dispatch", with the saved
  *              indices/locations of section 7.5(2) and no padding (7.5(4)).
+ *              With a per-expert cap, assignments beyond it in token order
+ *              are dropped (same notes, V3 load balancing part A).
  *   fp8        per-token min/max affine map onto OCP e4m3 -- gsyq.cn,
  *              section 3.1. Reading: centre c = (max+min)/2, half range
  *              r = (max-min)/2, v = (x - c) * (448 / r), clamp to +-448, round
@@ -185,6 +187,55 @@ int oracle_dispatch(int64_t T, int E, int k, const int32_t *topk_idx,
     return 0;
 }
 
+/*
+ * Capacity-limited dispatch: the hard per-expert token cap of the DeepEP notes
+ * (zzszmyf.github.io), "DeepSeek-V3 ... auxiliary-loss-free load balancing",
+ * part A (hard constraint and capacity): the router still picks its top-k,
+ * and once an expert holds its cap, later tokens that picked it are turned
+ * away -- here dropped, the option that page names beside reassignment.
+ * Assignments are taken in token order (ascending t); a token's k slots name
+ * distinct experts, so their order within the token does not matter. A kept
+ * assignment gets the next row of its expert; a dropped one gets
+ * dest_row = -1 and no row. counts[] are the kept counts and offsets[] their
+ * exclusive prefix sums. cap = 0 means no limit (the plain dispatch above).
+ */
+int oracle_dispatch_capacity(int64_t T, int E, int k, const int32_t *topk_idx,
+                             int32_t cap, int32_t *counts, int32_t *offsets,
+                             int32_t *dest_row, int32_t *src_token)
+{
+    if (T < 0 || E <= 0 || k <= 0 || cap < 0)
+        return -1;
+    for (int e = 0; e < E; ++e)
+        counts[e] = 0; /* rows held so far, then the kept counts */
+    for (int64_t t = 0; t < T; ++t)
+        for (int j = 0; j < k; ++j) {
+            int e = topk_idx[t * k + j];
+            if (e < 0 || e >= E)
+                return -2;
+            for (int jj = 0; jj < j; ++jj)
+                if (topk_idx[t * k + jj] == e)
+                    return -3;
+            if (cap == 0 || counts[e] < cap) {
+                dest_row[t * k + j] = counts[e]; /* rank within the expert for now */
+                counts[e] += 1;
+            } else {
+                dest_row[t * k + j] = -1;
+            }
+        }
+    offsets[0] = 0;
+    for (int e = 0; e < E; ++e)
+        offsets[e + 1] = offsets[e] + counts[e];
+    for (int64_t t = 0; t < T; ++t)
+        for (int j = 0; j < k; ++j) {
+            if (dest_row[t * k + j] < 0)
+                continue;
+            int32_t row = offsets[topk_idx[t * k + j]] + dest_row[t * k + j];
+            dest_row[t * k + j] = row;
+            src_token[row] = (int32_t)t;
+        }
+    return 0;
+}
+
 /* ----------------------------------------------------------------- fp8 ---- */
 
 /* OCP e4m3fn: 1 sign, 4 exponent bits (bias 7), 3 mantissa bits, no
@@ -340,10 +391,13 @@ int oracle_expert_rows(int d, int h, int wdt, int64_t n, const int32_t *group,
  * Full layer output for a list of tokens, each computed on its own:
  * gate -> top-k -> weights -> (fp8: quantise/dequantise the token's row for
  * the routed experts) -> y[t] = sum_s FFN_{E+s}(x[t]) + sum_j w_j FFN_{e_j}(xq).
+ * keep [n,k] (or NULL: every slot) marks the slots a capacity limit kept;
+ * a dropped slot contributes nothing (its weight is not given to the others).
  * Outputs per listed token: topk_idx [n,k], topk_w [n,k], y [n,d] float64.
  */
 int oracle_layer_tokens(int d, int E, int k, int S, int h, int dtype, int fp8,
-                        int64_t n, const int64_t *tokens, const void *x,
+                        int64_t n, const int64_t *tokens, const uint8_t *keep,
+                        const void *x,
                         const void *wg, const float *bias, const void *w1,
                         const void *w3, const void *w2, int32_t *topk_idx,
                         double *topk_w, double *y, int nthreads)
@@ -396,6 +450,8 @@ int oracle_layer_tokens(int d, int E, int k, int S, int h, int dtype, int fp8,
                     yr[i] += o[i];
             }
             for (int j = 0; j < k; ++j) {
+                if (keep && !keep[r * k + j])
+                    continue; /* dropped by a capacity limit */
                 int64_t g = topk_idx[r * k + j];
                 swiglu_ffn(d, h, dtype, vq, group_ptr(w1, dtype, g, (int64_t)h * d),
                            group_ptr(w3, dtype, g, (int64_t)h * d),

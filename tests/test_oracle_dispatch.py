@@ -60,3 +60,66 @@ def test_skewed_routing_leaves_empty_experts():
     assert (counts == 0).sum() > 0
     # empty experts have empty ranges
     assert np.all(offsets[1:][counts == 0] == offsets[:-1][counts == 0])
+
+
+# ------------------------------------------------------- capacity limit ----
+# The hard per-expert cap of the DeepEP notes (V3 load balancing, part A):
+# in token order, an expert that already holds `cap` rows turns later tokens
+# away (dropped here). Pinned by a per-expert rule written with numpy (the
+# first `cap` tokens, by token id, among those that picked the expert), by
+# the plain dispatch when the cap never binds, and by closed forms.
+
+def _kept_by_rule(idx, E, cap):
+    T, k = idx.shape
+    keep = np.zeros((T, k), dtype=bool)
+    for e in range(E):
+        t_hit, j_hit = np.nonzero(idx == e)          # row-major: ascending token id
+        keep[t_hit[:cap], j_hit[:cap]] = True
+    return keep
+
+
+@pytest.mark.parametrize("T,E,k,cap,skew", [(200, 8, 2, 30, 0), (1000, 32, 8, 200, 0.7),
+                                            (3000, 128, 4, 50, 2.5), (64, 4, 4, 1, 0),
+                                            (300, 6, 3, 7, 1.0)])
+def test_capacity_dispatch_against_per_expert_rule(T, E, k, cap, skew):
+    idx = make_routing(T, E, k, seed=T + cap, skew=skew)
+    counts, offsets, dest, src = oracle.dispatch(idx, E, capacity=cap)
+    keep = _kept_by_rule(idx, E, cap)
+    assert np.array_equal(dest >= 0, keep)
+    assert np.array_equal(counts, np.minimum(np.bincount(idx.ravel(), minlength=E), cap))
+    assert np.array_equal(offsets, np.concatenate([[0], np.cumsum(counts)]))
+    n = int(offsets[E])
+    assert n == keep.sum() and n <= E * cap
+    # kept slots: a bijection onto [0, n), expert-major and token-ascending
+    kd = dest[keep]
+    assert np.array_equal(np.sort(kd), np.arange(n))
+    order = np.argsort(np.where(keep, idx, E).ravel(), kind="stable")[:n]
+    assert np.array_equal(src[:n], order // k)
+    assert np.array_equal(src[dest[keep]], np.nonzero(keep)[0])
+    assert np.all(src[n:] == -1)
+
+
+def test_capacity_that_never_binds_is_the_plain_dispatch():
+    idx = make_routing(2000, 16, 4, seed=7, skew=1.5)
+    plain = oracle.dispatch(idx, 16)
+    capped = oracle.dispatch(idx, 16, capacity=int(plain[0].max()))
+    for a, b in zip(plain, capped):
+        assert np.array_equal(a, b)
+
+
+def test_capacity_one_keeps_each_experts_first_token():
+    idx = make_routing(500, 10, 3, seed=3)
+    counts, offsets, dest, src = oracle.dispatch(idx, 10, capacity=1)
+    for e in range(10):
+        first = np.nonzero((idx == e).any(axis=1))[0]
+        if len(first):
+            assert counts[e] == 1 and src[offsets[e]] == first[0]
+        else:
+            assert counts[e] == 0
+
+
+def test_capacity_rejects_bad_routing_and_negative_cap():
+    with pytest.raises(ValueError):
+        oracle.dispatch(np.array([[1, 1]], dtype=np.int32), 4, capacity=2)
+    with pytest.raises(ValueError):
+        oracle.dispatch(np.array([[0, 1]], dtype=np.int32), 4, capacity=-1)

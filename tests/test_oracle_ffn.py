@@ -120,3 +120,23 @@ def test_combine_k1_is_a_pure_unpermute():
     x = rng.standard_normal((T, d)).astype(np.float32)
     y = oracle.combine(x[src], None, dest, np.ones((T, 1), dtype=np.float32))
     assert np.array_equal(y, x.astype(np.float64))
+
+
+def test_layer_keep_mask():
+    # all slots kept: the plain layer; no slot kept and no shared experts:
+    # zero; with identical experts, dropping one slot of every token leaves
+    # (1 - w_dropped) of the dense FFN
+    inp = _small("f32", E=6, k=3, S=0)
+    toks = np.arange(inp.cfg.T)
+    idx, w, y = oracle.layer_tokens(inp, toks)
+    _, _, y_all = oracle.layer_tokens(inp, toks, keep=np.ones((len(toks), 3), dtype=bool))
+    assert np.array_equal(y_all, y)
+    _, _, y_none = oracle.layer_tokens(inp, toks, keep=np.zeros((len(toks), 3), dtype=bool))
+    assert np.all(y_none == 0)
+    for g in range(1, 6):
+        inp.w1[g], inp.w3[g], inp.w2[g] = inp.w1[0], inp.w3[0], inp.w2[0]
+    keep = np.ones((len(toks), 3), dtype=bool)
+    keep[:, 1] = False
+    _, w, y_drop = oracle.layer_tokens(inp, toks, keep=keep)
+    ref = dense_swiglu(_w64(inp.x), inp.w1[0], inp.w3[0], inp.w2[0]) * (1.0 - w[:, 1:2])
+    np.testing.assert_allclose(y_drop, ref, rtol=1e-10, atol=1e-12)
