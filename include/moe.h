@@ -23,6 +23,10 @@
  *          local FFN; combine restores the original token order from the
  *          metadata saved at dispatch (7.5(2): indices and locations), with no
  *          padding (7.5(4)) and with sizes known before the payload moves.
+ *          Its part on DeepSeek-V3's auxiliary-loss-free load balancing
+ *          ("A", hard constraint and capacity): a strict per-expert token
+ *          cap; once an expert is full, later tokens that picked it are
+ *          turned away (reassigned or dropped).
  *
  * Conventions (all entry points):
  *  - Every pointer argument except the moe_shape is a DEVICE pointer unless
@@ -88,6 +92,11 @@ typedef struct {
     int32_t h;        /* expert SwiGLU hidden width */
     int32_t act;      /* moe_dtype of x, all weights, expert outputs and y */
     int32_t dispatch; /* moe_dtype of the dispatched rows x_perm */
+    int32_t capacity; /* rows each routed expert may hold ([deepep] V3 "A"):
+                         0 = no limit (every assignment dispatched); C > 0 =
+                         assignments beyond an expert's first C, in token
+                         order, are dropped (see moe_dispatch). Negative is
+                         invalid. */
 } moe_shape;
 
 /* Host only. Bytes of workspace that `stage` needs for shape *s (0 when the
@@ -119,10 +128,17 @@ int32_t moe_gate_topk(const moe_shape *s, const void *x, const void *w_gate,
 /*
  * Dispatch ([deepep] 7 "Dispatch" and 7.5(2)/(4), [gsyq] 3.1 for FP8).
  *  counts[e] (int32 [E]) = number of (t,j) with topk_idx[t,j] == e;
- *  offsets (int32 [E+1]) = exclusive prefix sum, offsets[E] = T*k;
+ *  offsets (int32 [E+1]) = exclusive prefix sum (offsets[E] = T*k with no
+ *  capacity limit);
  *  dest_row[t,j] (int32 [T,k]) = offsets[e] + number of tokens t' < t that
  *  picked e (stable, expert-major, token order kept, no padding);
  *  src_token[dest_row[t,j]] = t (int32 [T*k]);
+ *  With s->capacity = C > 0 ([deepep] V3 "A", overflow dropped): an
+ *  assignment (t,j) to expert e is kept iff fewer than C tokens t' < t picked
+ *  e; counts[e] = min(C, number picking e); offsets and dest_row as above
+ *  over the kept assignments only; a dropped slot gets dest_row = -1 and no
+ *  row, and contributes nothing in moe_combine (its weight is not handed to
+ *  the other slots). Only src_token[0 .. offsets[E]) is written.
  *  x_perm[dest_row[t,j]] = x[t] (rows of act), or, with dispatch =
  *  MOE_FP8_E4M3, the token's per-row affine e4m3 codes (uint8 [T*k, d]) with
  *  qparams[dest_row[t,j]] = (scale, centre) (float32 [T*k, 2]): centre =

@@ -18,8 +18,12 @@
 //            lanes chose that expert, so a rank is a popcount -- stable and
 //            deterministic with no ordering of atomics.
 //   scan     one block: totals per expert, exclusive scan -> offsets, and
-//            each rank block's base row per expert.
-//   permute  one wave per token: 16-byte row loads once, k row stores.
+//            each rank block's base row per expert. With a per-expert
+//            capacity C (the notes' DeepSeek-V3 load balancing, part A: a
+//            strict token cap per expert) the counts are clamped to C first.
+//   permute  one wave per token: 16-byte row loads once, k row stores. A
+//            slot whose rank among its expert's assignments (token order)
+//            reaches C is dropped: dest_row = -1, no row.
 #include "moe_device.h"
 
 namespace moe {
@@ -87,7 +91,7 @@ __global__ __launch_bounds__(kRankThreads) void dispatch_rank_kernel(
 // blk[nblk][E] holds each rank block's per-expert counts on entry and, on
 // exit, the block's first destination row per expert.
 __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
-    int32_t* __restrict__ blk, int nblk, int E, int32_t* __restrict__ counts,
+    int32_t* __restrict__ blk, int nblk, int E, int cap, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets) {
     __shared__ int part[kScanThreads];  // [P][E] partial sums
     __shared__ int tot[kMaxE];
@@ -114,7 +118,7 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
             part[q * E + tid] = s;
             s += c;
         }
-        tot[tid] = s;
+        tot[tid] = cap > 0 ? min(s, cap) : s;  // rows the expert keeps
     }
     __syncthreads();
     if (tid == 0) {
@@ -139,10 +143,15 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
 
 // Destination rows of token t's k slots, computed by lanes 0..k-1 and
 // broadcast to the wave. Lanes 0..k-1 also write dest_row and src_token.
+// With cap > 0, a slot whose rank among all of its expert's assignments
+// (blk - offsets + r: earlier blocks' count plus the rank within the block)
+// is cap or more is dropped.
 __device__ __forceinline__ int token_dest(const int32_t* __restrict__ topk_idx,
                                           const int32_t* __restrict__ rank,
-                                          const int32_t* __restrict__ blk, int64_t t, int E,
-                                          int k, int lane, int32_t* __restrict__ dest_row,
+                                          const int32_t* __restrict__ blk,
+                                          const int32_t* __restrict__ offsets, int cap,
+                                          int64_t t, int E, int k, int lane,
+                                          int32_t* __restrict__ dest_row,
                                           int32_t* __restrict__ src_token) {
     int dst = -1;
     if (lane < k) {
@@ -150,7 +159,8 @@ __device__ __forceinline__ int token_dest(const int32_t* __restrict__ topk_idx,
         if (r >= 0) {
             const int e = topk_idx[t * k + lane];
             dst = blk[(t / kRankBlockTokens) * E + e] + r;
-            src_token[dst] = static_cast<int32_t>(t);
+            if (cap > 0 && dst - offsets[e] >= cap) dst = -1;
+            if (dst >= 0) src_token[dst] = static_cast<int32_t>(t);
         }
         dest_row[t * k + lane] = dst;
     }
@@ -159,13 +169,15 @@ __device__ __forceinline__ int token_dest(const int32_t* __restrict__ topk_idx,
 
 __global__ __launch_bounds__(256) void dispatch_permute_kernel(
     const uint8_t* __restrict__ x, const int32_t* __restrict__ topk_idx,
-    const int32_t* __restrict__ rank, const int32_t* __restrict__ blk, int64_t T, int E, int k,
-    int row_bytes, int32_t* __restrict__ dest_row, int32_t* __restrict__ src_token,
+    const int32_t* __restrict__ rank, const int32_t* __restrict__ blk,
+    const int32_t* __restrict__ offsets, int cap, int64_t T, int E, int k, int row_bytes,
+    int32_t* __restrict__ dest_row, int32_t* __restrict__ src_token,
     uint8_t* __restrict__ x_perm) {
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + w;
     if (t >= T) return;
-    const int dst = token_dest(topk_idx, rank, blk, t, E, k, lane, dest_row, src_token);
+    const int dst =
+        token_dest(topk_idx, rank, blk, offsets, cap, t, E, k, lane, dest_row, src_token);
     int dj[kMaxK];
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) dj[j] = __shfl(dst, j, kWave);
@@ -218,13 +230,15 @@ __device__ __forceinline__ u32x4 quant16(u32x4 a, u32x4 b, float c, float inv, b
 
 __global__ __launch_bounds__(256) void dispatch_permute_fp8_kernel(
     const bf16_t* __restrict__ x, const int32_t* __restrict__ topk_idx,
-    const int32_t* __restrict__ rank, const int32_t* __restrict__ blk, int64_t T, int E, int k,
-    int d, int32_t* __restrict__ dest_row, int32_t* __restrict__ src_token,
+    const int32_t* __restrict__ rank, const int32_t* __restrict__ blk,
+    const int32_t* __restrict__ offsets, int cap, int64_t T, int E, int k, int d,
+    int32_t* __restrict__ dest_row, int32_t* __restrict__ src_token,
     uint8_t* __restrict__ x_perm, float* __restrict__ qparams) {
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + w;
     if (t >= T) return;
-    const int dst = token_dest(topk_idx, rank, blk, t, E, k, lane, dest_row, src_token);
+    const int dst =
+        token_dest(topk_idx, rank, blk, offsets, cap, t, E, k, lane, dest_row, src_token);
     int dj[kMaxK];
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) dj[j] = __shfl(dst, j, kWave);
@@ -273,18 +287,18 @@ hipError_t launch_dispatch(const moe_shape& s, const void* x, const int32_t* top
     const int nblk = static_cast<int>((s.T + kRankBlockTokens - 1) / kRankBlockTokens);
     dispatch_rank_kernel<<<nblk, kRankThreads, 0, st>>>(topk_idx, s.T, s.E, s.k, rank, blk, hdr);
     mark(mk);
-    dispatch_scan_kernel<<<1, kScanThreads, 0, st>>>(blk, nblk, s.E, counts, offsets);
+    dispatch_scan_kernel<<<1, kScanThreads, 0, st>>>(blk, nblk, s.E, s.capacity, counts, offsets);
     mark(mk);
     const unsigned pblocks = static_cast<unsigned>((s.T + 3) / 4);
     if (s.dispatch == MOE_FP8_E4M3) {
         dispatch_permute_fp8_kernel<<<pblocks, 256, 0, st>>>(
-            static_cast<const bf16_t*>(x), topk_idx, rank, blk, s.T, s.E, s.k, s.d, dest_row,
-            src_token, static_cast<uint8_t*>(x_perm), qparams);
+            static_cast<const bf16_t*>(x), topk_idx, rank, blk, offsets, s.capacity, s.T, s.E,
+            s.k, s.d, dest_row, src_token, static_cast<uint8_t*>(x_perm), qparams);
     } else {
         const int row_bytes = s.d * (s.act == MOE_F32 ? 4 : 2);
         dispatch_permute_kernel<<<pblocks, 256, 0, st>>>(
-            static_cast<const uint8_t*>(x), topk_idx, rank, blk, s.T, s.E, s.k, row_bytes,
-            dest_row, src_token, static_cast<uint8_t*>(x_perm));
+            static_cast<const uint8_t*>(x), topk_idx, rank, blk, offsets, s.capacity, s.T, s.E,
+            s.k, row_bytes, dest_row, src_token, static_cast<uint8_t*>(x_perm));
     }
     mark(mk);
     return hipGetLastError();

@@ -81,7 +81,8 @@ Layout layout(const moe_shape& s, int stage) {
 // shape checks common to every entry point; `ffn` adds the GEMM tile limits
 int32_t check_shape(const moe_shape* s, bool ffn) {
     if (s == nullptr) return MOE_ERR_INVALID_ARG;
-    if (s->T < 0 || s->d <= 0 || s->E <= 0 || s->k <= 0 || s->S < 0 || s->h <= 0 || s->k > s->E)
+    if (s->T < 0 || s->d <= 0 || s->E <= 0 || s->k <= 0 || s->S < 0 || s->h <= 0 || s->k > s->E ||
+        s->capacity < 0)
         return MOE_ERR_INVALID_ARG;
     if (s->E > kMaxE || s->k > kMaxK || s->S > kMaxS) return MOE_ERR_UNSUPPORTED;
     if (s->act != MOE_F32 && s->act != MOE_BF16) return MOE_ERR_UNSUPPORTED;

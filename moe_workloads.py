@@ -57,6 +57,9 @@ class MoEConfig:
     zipf_bias: bool = False
     outlier_p: float = 0.0
     outlier_scale: float = 1.0
+    # rows each routed expert may hold (0: no limit); beyond it, assignments
+    # in token order are dropped
+    capacity: int = 0
     # relative-L2 bound on the layer output y
     tol_y: float = 2e-2
 
@@ -85,6 +88,15 @@ CONFIGS = {
         "fp8_dispatch", T=32768, d=4096, E=64, k=6, S=2, h=1024, act="bf16",
         dispatch="fp8", outlier_p=1e-3, outlier_scale=50.0, tol_y=6e-2),
 }
+
+# A capacity-limited variant of the skewed workload: capacity factor 1.25,
+# i.e. each expert holds at most 1.25 * T*k/E rows (the DeepEP notes, DeepSeek-V3
+# load balancing part A, put the factor near 1.0); under the skew most of the
+# hottest experts' assignments are dropped. Not one of the five configs: it is
+# a parity case for the capacity limit.
+CONFIGS["zipf_capacity_bf16"] = MoEConfig(
+    "zipf_capacity_bf16", T=16384, d=2048, E=128, k=4, S=0, h=512, act="bf16",
+    dispatch="act", zipf_bias=True, capacity=640, tol_y=2e-2)
 
 # the order the five configs are listed in the workload table
 CONFIG_ORDER = ["tiny_fp32", "deepseekmoe_bf16", "coarse_top2_bf16",
