@@ -51,7 +51,7 @@ def lib():
         L.oracle_gate_logits.argtypes = [i64, i32, i32, i32, vp, vp, vp, vp, i32]
         L.oracle_select_topk.argtypes = [i64, i32, i32, vp, vp, vp]
         L.oracle_dispatch.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp]
-        L.oracle_dispatch_capacity.argtypes = [i64, i32, i32, vp, i32, vp, vp, vp, vp]
+        L.oracle_dispatch_capacity.argtypes = [i64, i32, i32, vp, i32, i32, vp, vp, vp, vp, vp]
         L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
         L.oracle_e4m3_decode.restype = ctypes.c_double
         L.oracle_e4m3_encode.argtypes = [ctypes.c_float]
@@ -118,12 +118,15 @@ def gate_topk(x, wg, k, bias=None, nthreads=1):
     return idx, w, z
 
 
-def dispatch(topk_idx, E, capacity=0):
+def dispatch(topk_idx, E, capacity=0, reassign=False, return_route=False):
     """counts [E], offsets [E+1], dest_row [T,k], src_token [T*k] (int32).
 
-    capacity > 0: each expert keeps at most that many assignments, taken in
-    token order; the rest get dest_row -1 and no row, and src_token holds
-    offsets[E] meaningful entries (the rest are -1 here).
+    capacity > 0: each expert takes at most that many assignments in token
+    order; the overflow is dropped, or with reassign=True handed one at a
+    time to the least-loaded expert (ties to the lower id) while any is below
+    the cap. Dropped slots get dest_row -1 and no row; src_token holds
+    offsets[E] meaningful entries (the rest are -1 here). return_route adds
+    route [T,k]: the expert whose row each slot got, -1 if dropped.
     """
     idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
     T, k = idx.shape
@@ -131,12 +134,16 @@ def dispatch(topk_idx, E, capacity=0):
     offsets = np.empty(E + 1, dtype=np.int32)
     dest = np.empty((T, k), dtype=np.int32)
     src = np.full(T * k, -1, dtype=np.int32)
+    route = idx.copy()
     if capacity:
-        _check(lib().oracle_dispatch_capacity(T, E, k, _p(idx), int(capacity), _p(counts),
-                                              _p(offsets), _p(dest), _p(src)), "dispatch_capacity")
+        _check(lib().oracle_dispatch_capacity(T, E, k, _p(idx), int(capacity), int(bool(reassign)),
+                                              _p(counts), _p(offsets), _p(dest), _p(src),
+                                              _p(route)), "dispatch_capacity")
     else:
         _check(lib().oracle_dispatch(T, E, k, _p(idx), _p(counts), _p(offsets), _p(dest),
                                      _p(src)), "dispatch")
+    if return_route:
+        return counts, offsets, dest, src, route
     return counts, offsets, dest, src
 
 
@@ -179,12 +186,13 @@ def expert_rows(rows, group, w1, w3, w2, nthreads=1):
     return out
 
 
-def layer_tokens(inp, tokens, nthreads=1, keep=None):
+def layer_tokens(inp, tokens, nthreads=1, route=None):
     """Whole-layer output for the listed tokens: (topk_idx, topk_w, y float64).
 
-    keep [n, k] (bool, optional): the slots a capacity limit kept; a dropped
-    slot contributes nothing. Which slots are dropped depends on the whole
-    batch's routing, so the caller takes it from dispatch(..., capacity).
+    route [n, k] (int, optional): under a capacity limit, the expert whose
+    row each slot got (-1: dropped, contributes nothing; a reassigned slot
+    keeps its gate weight). It depends on the whole batch's routing, so the
+    caller takes it from dispatch(..., capacity, return_route=True).
     """
     cfg = inp.cfg
     tokens = np.ascontiguousarray(tokens, dtype=np.int64)
@@ -195,8 +203,8 @@ def layer_tokens(inp, tokens, nthreads=1, keep=None):
     b = None if inp.bias is None else np.ascontiguousarray(inp.bias, dtype=np.float32)
     _check(lib().oracle_layer_tokens(cfg.d, cfg.E, cfg.k, cfg.S, cfg.h, _dtype_code(inp.x),
                                      1 if cfg.dispatch == "fp8" else 0, n, _p(tokens),
-                                     _p(None if keep is None else
-                                        np.ascontiguousarray(keep, dtype=np.uint8).reshape(n, cfg.k)),
+                                     _p(None if route is None else
+                                        np.ascontiguousarray(route, dtype=np.int32).reshape(n, cfg.k)),
                                      _p(inp.x),
                                      _p(inp.wg), _p(b), _p(inp.w1), _p(inp.w3), _p(inp.w2),
                                      _p(idx), _p(w), _p(y), _nthreads(nthreads)), "layer_tokens")

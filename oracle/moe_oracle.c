@@ -192,19 +192,34 @@ int oracle_dispatch(int64_t T, int E, int k, const int32_t *topk_idx,
  * (zzszmyf.github.io), "DeepSeek-V3 ... auxiliary-loss-free load balancing",
  * part A (hard constraint and capacity): the router still picks its top-k,
  * and once an expert holds its cap, later tokens that picked it are turned
- * away -- here dropped, the option that page names beside reassignment.
- * Assignments are taken in token order (ascending t); a token's k slots name
- * distinct experts, so their order within the token does not matter. A kept
- * assignment gets the next row of its expert; a dropped one gets
- * dest_row = -1 and no row. counts[] are the kept counts and offsets[] their
- * exclusive prefix sums. cap = 0 means no limit (the plain dispatch above).
+ * away -- reassigned to the least-loaded expert of the batch, or dropped.
+ *
+ * First pass, in token order (ascending t; a token's k slots name distinct
+ * experts, so their order within the token does not matter): an assignment
+ * to an expert holding fewer than cap rows takes its next row; otherwise it
+ * overflows.
+ * reassign = 0: every overflowing assignment is dropped.
+ * reassign = 1: then, in the same order, each overflowing assignment goes to
+ * the expert with the fewest rows at that moment (ties to the lower id),
+ * taking its next row, as long as some expert holds fewer than cap rows;
+ * once every expert is full the rest are dropped. (Reading: "load" is the
+ * rows an expert holds; the reassignment follows the whole first pass.)
+ * An expert's rows are its first-pass rows in token order, then its
+ * reassigned rows in that order. A dropped assignment gets dest_row = -1
+ * and no row; route[t,j] (if not NULL) is the expert whose row it got, or -1.
+ * counts[] are the rows per expert and offsets[] their exclusive prefix
+ * sums. cap = 0 means no limit (the plain dispatch above).
  */
 int oracle_dispatch_capacity(int64_t T, int E, int k, const int32_t *topk_idx,
-                             int32_t cap, int32_t *counts, int32_t *offsets,
-                             int32_t *dest_row, int32_t *src_token)
+                             int32_t cap, int reassign, int32_t *counts,
+                             int32_t *offsets, int32_t *dest_row,
+                             int32_t *src_token, int32_t *route)
 {
     if (T < 0 || E <= 0 || k <= 0 || cap < 0)
         return -1;
+    int32_t *where = (int32_t *)malloc(sizeof(int32_t) * (size_t)(T * k + 1));
+    if (!where)
+        return -4;
     for (int e = 0; e < E; ++e)
         counts[e] = 0; /* rows held so far, then the kept counts */
     for (int64_t t = 0; t < T; ++t)
@@ -217,22 +232,43 @@ int oracle_dispatch_capacity(int64_t T, int E, int k, const int32_t *topk_idx,
                     return -3;
             if (cap == 0 || counts[e] < cap) {
                 dest_row[t * k + j] = counts[e]; /* rank within the expert for now */
+                where[t * k + j] = e;
                 counts[e] += 1;
             } else {
                 dest_row[t * k + j] = -1;
+                where[t * k + j] = -2; /* overflowed */
             }
         }
+    for (int64_t i = 0; i < T * k; ++i) {
+        if (where[i] != -2)
+            continue;
+        where[i] = -1;
+        if (!reassign)
+            continue;
+        int best = -1;
+        for (int e = 0; e < E; ++e)
+            if (counts[e] < cap && (best < 0 || counts[e] < counts[best]))
+                best = e;
+        if (best < 0)
+            continue; /* every expert is full */
+        dest_row[i] = counts[best];
+        where[i] = best;
+        counts[best] += 1;
+    }
     offsets[0] = 0;
     for (int e = 0; e < E; ++e)
         offsets[e + 1] = offsets[e] + counts[e];
     for (int64_t t = 0; t < T; ++t)
         for (int j = 0; j < k; ++j) {
-            if (dest_row[t * k + j] < 0)
+            if (route)
+                route[t * k + j] = where[t * k + j];
+            if (where[t * k + j] < 0)
                 continue;
-            int32_t row = offsets[topk_idx[t * k + j]] + dest_row[t * k + j];
+            int32_t row = offsets[where[t * k + j]] + dest_row[t * k + j];
             dest_row[t * k + j] = row;
             src_token[row] = (int32_t)t;
         }
+    free(where);
     return 0;
 }
 
@@ -391,12 +427,14 @@ int oracle_expert_rows(int d, int h, int wdt, int64_t n, const int32_t *group,
  * Full layer output for a list of tokens, each computed on its own:
  * gate -> top-k -> weights -> (fp8: quantise/dequantise the token's row for
  * the routed experts) -> y[t] = sum_s FFN_{E+s}(x[t]) + sum_j w_j FFN_{e_j}(xq).
- * keep [n,k] (or NULL: every slot) marks the slots a capacity limit kept;
- * a dropped slot contributes nothing (its weight is not given to the others).
+ * route [n,k] (or NULL: the top-k experts themselves) names the expert each
+ * slot's row went to under a capacity limit, -1 for a dropped slot, which
+ * contributes nothing (its weight is not given to the other slots); a
+ * reassigned slot keeps its gate weight.
  * Outputs per listed token: topk_idx [n,k], topk_w [n,k], y [n,d] float64.
  */
 int oracle_layer_tokens(int d, int E, int k, int S, int h, int dtype, int fp8,
-                        int64_t n, const int64_t *tokens, const uint8_t *keep,
+                        int64_t n, const int64_t *tokens, const int32_t *route,
                         const void *x,
                         const void *wg, const float *bias, const void *w1,
                         const void *w3, const void *w2, int32_t *topk_idx,
@@ -450,9 +488,9 @@ int oracle_layer_tokens(int d, int E, int k, int S, int h, int dtype, int fp8,
                     yr[i] += o[i];
             }
             for (int j = 0; j < k; ++j) {
-                if (keep && !keep[r * k + j])
+                if (route && route[r * k + j] < 0)
                     continue; /* dropped by a capacity limit */
-                int64_t g = topk_idx[r * k + j];
+                int64_t g = route ? route[r * k + j] : topk_idx[r * k + j];
                 swiglu_ffn(d, h, dtype, vq, group_ptr(w1, dtype, g, (int64_t)h * d),
                            group_ptr(w3, dtype, g, (int64_t)h * d),
                            group_ptr(w2, dtype, g, (int64_t)d * h), o, hbuf);

@@ -123,3 +123,76 @@ def test_capacity_rejects_bad_routing_and_negative_cap():
         oracle.dispatch(np.array([[1, 1]], dtype=np.int32), 4, capacity=2)
     with pytest.raises(ValueError):
         oracle.dispatch(np.array([[0, 1]], dtype=np.int32), 4, capacity=-1)
+
+
+# --------------------------------------------------- reassignment mode -----
+# Overflow handed one at a time, in token order, to the least-loaded expert
+# (ties to the lower id) while any expert is below the cap. Pinned by the
+# closed form of that water-filling rather than by replaying it: with
+# first-pass loads L_e = min(count_e, cap) and O overflowing assignments,
+# N(v) = sum_e max(0, v - L_e) assignments raise every expert to level v, so
+# the o-th overflow lands at the level v with N(v) <= o < N(v+1), on the
+# (o - N(v))-th expert in id order among those with L_e <= v, as that
+# expert's row v. The notes' claim that a cap at the average load makes the
+# per-expert counts "rectangular" (all equal) is checked as well.
+
+def _water_fill(L, O, cap):
+    """expert and rank of each overflow index 0..O-1 (-1, -1 once all full)."""
+    L = np.asarray(L, dtype=np.int64)
+    N = lambda v: int(np.maximum(0, v - L).sum())
+    out = []
+    for o in range(O):
+        if o >= N(cap):
+            out.append((-1, -1))
+            continue
+        v = int(L.min())
+        while N(v + 1) <= o:
+            v += 1
+        cand = np.nonzero(L <= v)[0]
+        out.append((int(cand[o - N(v)]), v))
+    return out
+
+
+@pytest.mark.parametrize("T,E,k,cap,skew", [(200, 8, 2, 60, 1.0), (1000, 16, 4, 200, 2.0),
+                                            (600, 32, 8, 130, 1.5), (300, 6, 3, 100, 0.3),
+                                            (400, 10, 2, 30, 2.5)])
+def test_reassignment_matches_water_filling(T, E, k, cap, skew):
+    idx = make_routing(T, E, k, seed=T + k, skew=skew)
+    counts, offsets, dest, src, route = oracle.dispatch(idx, E, capacity=cap, reassign=True,
+                                                        return_route=True)
+    first = _kept_by_rule(idx, E, cap)
+    L = np.minimum(np.bincount(idx.ravel(), minlength=E), cap)
+    over_t, over_j = np.nonzero(~first)                  # overflow in token order
+    fill = _water_fill(L, len(over_t), cap)
+    # first-pass slots keep their expert and rank
+    assert np.array_equal(route[first], idx[first])
+    exp_counts = L.copy()
+    for (t, j), (e, v) in zip(zip(over_t, over_j), fill):
+        assert route[t, j] == e
+        if e >= 0:
+            assert dest[t, j] == offsets[e] + v
+            exp_counts[e] += 1
+        else:
+            assert dest[t, j] == -1
+    assert np.array_equal(counts, exp_counts)
+    assert counts.max() <= cap and counts.sum() == min(T * k, E * cap)
+    n = int(offsets[E])
+    kept = dest >= 0
+    assert np.array_equal(np.sort(dest[kept]), np.arange(n))
+    assert np.array_equal(src[dest[kept]], np.nonzero(kept)[0])
+
+
+def test_cap_at_the_average_load_gives_equal_counts():
+    T, E, k = 512, 16, 4
+    cap = T * k // E
+    idx = make_routing(T, E, k, seed=1, skew=2.0)
+    counts, offsets, dest, _ = oracle.dispatch(idx, E, capacity=cap, reassign=True)
+    assert np.all(counts == cap) and np.all(dest >= 0)
+
+
+def test_reassignment_with_a_cap_that_never_binds_is_the_plain_dispatch():
+    idx = make_routing(800, 12, 3, seed=5, skew=1.0)
+    plain = oracle.dispatch(idx, 12)
+    re = oracle.dispatch(idx, 12, capacity=int(plain[0].max()), reassign=True)
+    for a, b in zip(plain, re):
+        assert np.array_equal(a, b)

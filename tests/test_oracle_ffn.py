@@ -122,21 +122,31 @@ def test_combine_k1_is_a_pure_unpermute():
     assert np.array_equal(y, x.astype(np.float64))
 
 
-def test_layer_keep_mask():
-    # all slots kept: the plain layer; no slot kept and no shared experts:
-    # zero; with identical experts, dropping one slot of every token leaves
-    # (1 - w_dropped) of the dense FFN
+def test_layer_route():
+    # the top-k as route: the plain layer; every slot dropped and no shared
+    # experts: zero; with identical experts, dropping one slot of every
+    # token leaves (1 - w_dropped) of the dense FFN, and moving a slot to
+    # another (identical) expert changes nothing
     inp = _small("f32", E=6, k=3, S=0)
     toks = np.arange(inp.cfg.T)
     idx, w, y = oracle.layer_tokens(inp, toks)
-    _, _, y_all = oracle.layer_tokens(inp, toks, keep=np.ones((len(toks), 3), dtype=bool))
-    assert np.array_equal(y_all, y)
-    _, _, y_none = oracle.layer_tokens(inp, toks, keep=np.zeros((len(toks), 3), dtype=bool))
+    _, _, y_same = oracle.layer_tokens(inp, toks, route=idx)
+    assert np.array_equal(y_same, y)
+    _, _, y_none = oracle.layer_tokens(inp, toks, route=np.full_like(idx, -1))
     assert np.all(y_none == 0)
+    # a route to a different expert computes that expert's FFN
+    moved = idx.copy()
+    moved[:, 0] = (idx[:, 0] + 1) % 6
+    _, _, y_moved = oracle.layer_tokens(inp, toks, route=moved)
+    v = _w64(inp.x)
+    ref = sum(w[:, j:j + 1] * np.stack([dense_swiglu(v[t:t + 1], inp.w1[g], inp.w3[g], inp.w2[g])[0]
+                                         for t, g in enumerate(moved[:, j])])
+              for j in range(3))
+    np.testing.assert_allclose(y_moved, ref, rtol=1e-10, atol=1e-12)
     for g in range(1, 6):
         inp.w1[g], inp.w3[g], inp.w2[g] = inp.w1[0], inp.w3[0], inp.w2[0]
-    keep = np.ones((len(toks), 3), dtype=bool)
-    keep[:, 1] = False
-    _, w, y_drop = oracle.layer_tokens(inp, toks, keep=keep)
-    ref = dense_swiglu(_w64(inp.x), inp.w1[0], inp.w3[0], inp.w2[0]) * (1.0 - w[:, 1:2])
+    drop = idx.copy()
+    drop[:, 1] = -1
+    _, w, y_drop = oracle.layer_tokens(inp, toks, route=drop)
+    ref = dense_swiglu(v, inp.w1[0], inp.w3[0], inp.w2[0]) * (1.0 - w[:, 1:2])
     np.testing.assert_allclose(y_drop, ref, rtol=1e-10, atol=1e-12)
