@@ -74,6 +74,9 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
 
+/* what happens to an assignment beyond an expert's capacity */
+typedef enum { MOE_OVERFLOW_DROP = 0, MOE_OVERFLOW_REASSIGN = 1 } moe_overflow;
+
 /* which entry point a workspace is sized for */
 typedef enum {
     MOE_STAGE_GATE = 0,
@@ -95,8 +98,10 @@ typedef struct {
     int32_t capacity; /* rows each routed expert may hold ([deepep] V3 "A"):
                          0 = no limit (every assignment dispatched); C > 0 =
                          assignments beyond an expert's first C, in token
-                         order, are dropped (see moe_dispatch). Negative is
+                         order, overflow (see moe_dispatch). Negative is
                          invalid. */
+    int32_t overflow; /* moe_overflow: overflowing assignments are dropped or
+                         reassigned to the least-loaded expert */
 } moe_shape;
 
 /* Host only. Bytes of workspace that `stage` needs for shape *s (0 when the
@@ -133,12 +138,21 @@ int32_t moe_gate_topk(const moe_shape *s, const void *x, const void *w_gate,
  *  dest_row[t,j] (int32 [T,k]) = offsets[e] + number of tokens t' < t that
  *  picked e (stable, expert-major, token order kept, no padding);
  *  src_token[dest_row[t,j]] = t (int32 [T*k]);
- *  With s->capacity = C > 0 ([deepep] V3 "A", overflow dropped): an
- *  assignment (t,j) to expert e is kept iff fewer than C tokens t' < t picked
- *  e; counts[e] = min(C, number picking e); offsets and dest_row as above
- *  over the kept assignments only; a dropped slot gets dest_row = -1 and no
- *  row, and contributes nothing in moe_combine (its weight is not handed to
- *  the other slots). Only src_token[0 .. offsets[E]) is written.
+ *  With s->capacity = C > 0 ([deepep] V3 "A"): an assignment (t,j) to
+ *  expert e keeps its expert iff fewer than C tokens t' < t picked e, and
+ *  otherwise overflows. MOE_OVERFLOW_DROP: an overflowing slot gets
+ *  dest_row = -1 and no row, and contributes nothing in moe_combine (its
+ *  weight is not handed to the other slots); counts[e] = min(C, number
+ *  picking e). MOE_OVERFLOW_REASSIGN: after that first pass the overflowing
+ *  slots, in token order (t, then j), go one at a time to the expert with
+ *  the fewest rows at that moment (ties to the lower id), as its next row,
+ *  while some expert holds fewer than C rows; the rest are dropped. A
+ *  reassigned slot keeps its gate weight and may land on an expert the
+ *  token already picked. An expert's rows are its first-pass rows in token
+ *  order, then its reassigned rows in that order; counts are the final rows
+ *  per expert. topk_idx is not changed: the expert of a slot's row is the e
+ *  with offsets[e] <= dest_row < offsets[e+1]. Only src_token[0 ..
+ *  offsets[E]) is written.
  *  x_perm[dest_row[t,j]] = x[t] (rows of act), or, with dispatch =
  *  MOE_FP8_E4M3, the token's per-row affine e4m3 codes (uint8 [T*k, d]) with
  *  qparams[dest_row[t,j]] = (scale, centre) (float32 [T*k, 2]): centre =

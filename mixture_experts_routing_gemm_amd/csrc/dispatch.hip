@@ -21,9 +21,14 @@
 //            each rank block's base row per expert. With a per-expert
 //            capacity C (the notes' DeepSeek-V3 load balancing, part A: a
 //            strict token cap per expert) the counts are clamped to C first.
+//   overflow (capacity with reassignment only) one block per rank block:
+//            the assignments that overflow their expert, in token order, go
+//            one at a time to the least-loaded expert (same notes, part A);
+//            see dispatch_overflow_kernel.
 //   permute  one wave per token: 16-byte row loads once, k row stores. A
 //            slot whose rank among its expert's assignments (token order)
-//            reaches C is dropped: dest_row = -1, no row.
+//            reaches C is dropped (dest_row = -1, no row) or takes the row
+//            the overflow kernel gave it.
 #include "moe_device.h"
 
 namespace moe {
@@ -88,12 +93,92 @@ __global__ __launch_bounds__(kRankThreads) void dispatch_rank_kernel(
     }
 }
 
+__device__ __forceinline__ int64_t wave_sum64(int64_t v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+// exclusive prefix sum of v over the lanes of a wave
+__device__ __forceinline__ int wave_excl_scan(int v) {
+    const int lane = threadIdx.x & 63;
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += u;
+    }
+    return incl - v;
+}
+
+// Final per-expert loads when the overflow is reassigned, by one wave.
+// load[e] holds the first-pass loads L_e = min(n_e, cap) on entry and the
+// final loads on exit; n[e] are the assignments per expert. The O
+// overflowing assignments go one at a time to the least-loaded expert (ties
+// to the lower id) while one is below cap, which fills level by level:
+// raising every expert to level v takes N(v) = sum_e max(0, v - L_e) of them.
+// With V the highest level N(V) <= O reaches (V < cap), every expert ends at
+// max(L_e, V), plus one for the first O - N(V) experts in id order with
+// L_e <= V; if N(cap) <= O every expert ends full.
+__device__ void water_fill_loads(const int* n, int* load, int E, int cap) {
+    const int lane = threadIdx.x & 63;
+    int L[4];
+    int64_t over = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int e = lane * 4 + q;
+        L[q] = e < E ? load[e] : 0;
+        over += e < E ? n[e] - load[e] : 0;
+    }
+    const int64_t O = wave_sum64(over);
+    auto N = [&](int v) {
+        int64_t acc = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (lane * 4 + q < E) acc += max(0, v - L[q]);
+        return wave_sum64(acc);
+    };
+    if (N(cap) <= O) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (lane * 4 + q < E) load[lane * 4 + q] = cap;
+        return;
+    }
+    int lo = 0, hi = cap - 1;  // N(0) = 0 <= O < N(cap)
+    while (lo < hi) {
+        const int mid = lo + (hi - lo + 1) / 2;
+        if (N(mid) <= O) lo = mid;
+        else hi = mid - 1;
+    }
+    const int V = lo;
+    const int64_t r = O - N(V);
+    int below = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) below += (lane * 4 + q < E && L[q] <= V) ? 1 : 0;
+    int rk = wave_excl_scan(below);  // id-order position among the experts at or below V
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int e = lane * 4 + q;
+        if (e >= E) continue;
+        int f = max(L[q], V);
+        if (L[q] <= V) {
+            if (rk < r) f += 1;
+            ++rk;
+        }
+        load[e] = f;
+    }
+}
+
 // blk[nblk][E] holds each rank block's per-expert counts on entry and, on
-// exit, the block's first destination row per expert.
+// exit, the number of the expert's assignments in earlier rank blocks.
+// With cap > 0, first_loads[e] receives min(n_e, cap); with reassign the
+// counts are the loads after reassignment.
 __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
-    int32_t* __restrict__ blk, int nblk, int E, int cap, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets) {
+    int32_t* __restrict__ blk, int nblk, int E, int cap, int reassign,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ first_loads) {
     __shared__ int part[kScanThreads];  // [P][E] partial sums
+    __shared__ int raw[kMaxE];
     __shared__ int tot[kMaxE];
     __shared__ int off[kMaxE + 1];
     const int tid = threadIdx.x;
@@ -118,9 +203,15 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
             part[q * E + tid] = s;
             s += c;
         }
-        tot[tid] = cap > 0 ? min(s, cap) : s;  // rows the expert keeps
+        raw[tid] = s;
+        tot[tid] = cap > 0 ? min(s, cap) : s;  // rows the expert keeps in the first pass
+        if (cap > 0) first_loads[tid] = tot[tid];
     }
     __syncthreads();
+    if (cap > 0 && reassign) {
+        if (tid < kWave) water_fill_loads(raw, tot, E, cap);
+        __syncthreads();
+    }
     if (tid == 0) {
         int s = 0;
         for (int q = 0; q < E; ++q) {
@@ -136,21 +227,130 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
     }
     if (tid == 0) offsets[E] = off[E];
     if (active) {
-        const int base = off[e] + part[p * E + e];
+        const int base = part[p * E + e];
         for (int b = b0; b < b1; ++b) blk[static_cast<int64_t>(b) * E + e] += base;
+    }
+}
+
+// Capacity with reassignment: one block per rank block of 256 tokens, one
+// thread per token. An assignment overflows iff its rank g among its
+// expert's assignments (token order) is cap or more. Its overflow index o
+// in token order is the block's base -- sum_e max(0, (expert e's assignments
+// in earlier blocks) - cap) -- plus the overflows of earlier tokens of the
+// block and of its own earlier slots. The o-th overflow lands, by the same
+// level filling as water_fill_loads, at level v with N(v) <= o < N(v+1) on
+// the (o - N(v))-th expert in id order among those with L_e <= v, as that
+// expert's row v; with o >= N(cap) it is dropped. With the first-pass loads
+// sorted ascending (s_i) and P_i their prefix sums, N(s_i) = i*s_i - P_i and
+// each level in [s_i, s_{i+1}) holds i+1 overflows.
+__global__ __launch_bounds__(kRankThreads) void dispatch_overflow_kernel(
+    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ rank,
+    const int32_t* __restrict__ blk, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ first_loads, int64_t T, int E, int k, int cap,
+    int32_t* __restrict__ dest_row, int32_t* __restrict__ src_token) {
+    __shared__ int Ls[kMaxE];
+    __shared__ int sl[kMaxE];
+    __shared__ long long Bk[kMaxE + 1];  // N at each sorted load; Bk[E] = N(cap)
+    __shared__ long long wred[4];
+    __shared__ int wtot[4];
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int b = blockIdx.x;
+    for (int e = tid; e < E; e += kRankThreads) Ls[e] = first_loads[e];
+    __syncthreads();
+    // sorted first-pass loads (ties by id) and this block's overflow base
+    long long ob = 0;
+    for (int e = tid; e < E; e += kRankThreads) {
+        int pos = 0;
+        for (int q = 0; q < E; ++q) pos += (Ls[q] < Ls[e] || (Ls[q] == Ls[e] && q < e)) ? 1 : 0;
+        sl[pos] = Ls[e];
+        ob += max(0, blk[static_cast<int64_t>(b) * E + e] - cap);
+    }
+    ob = wave_sum64(ob);
+    if (lane == 0) wred[w] = ob;
+    __syncthreads();
+    ob = wred[0] + wred[1] + wred[2] + wred[3];
+    if (w == 0) {
+        // prefix sums of the sorted loads, four entries per lane
+        int v4[4], sum = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int i = lane * 4 + q;
+            v4[q] = i < E ? sl[i] : 0;
+            sum += v4[q];
+        }
+        long long P = wave_excl_scan(sum);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int i = lane * 4 + q;
+            if (i < E) Bk[i] = static_cast<long long>(i) * v4[q] - P;
+            P += v4[q];
+        }
+        if (lane == 63) Bk[E] = static_cast<long long>(E) * cap - P;
+    }
+    // this token's overflowing slots
+    const int64_t t = static_cast<int64_t>(b) * kRankThreads + tid;
+    int mine = 0;
+    if (t < T) {
+        for (int j = 0; j < k; ++j) {
+            const int r = rank[t * k + j];
+            if (r < 0) continue;
+            const int e = topk_idx[t * k + j];
+            mine += blk[static_cast<int64_t>(b) * E + e] + r >= cap ? 1 : 0;
+        }
+    }
+    const int wex = wave_excl_scan(mine);
+    if (lane == 63) wtot[w] = wex + mine;
+    __syncthreads();
+    int before = wex;
+    for (int q = 0; q < w; ++q) before += wtot[q];
+    if (t >= T || mine == 0) return;
+    long long o = ob + before;
+    for (int j = 0; j < k; ++j) {
+        const int r = rank[t * k + j];
+        if (r < 0) continue;
+        const int e = topk_idx[t * k + j];
+        if (blk[static_cast<int64_t>(b) * E + e] + r < cap) continue;
+        int dst = -1;
+        if (o < Bk[E]) {
+            int lo = 0, hi = E - 1;  // the last i with Bk[i] <= o
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (Bk[mid] <= o) lo = mid;
+                else hi = mid - 1;
+            }
+            const long long within = o - Bk[lo];
+            const int v = sl[lo] + static_cast<int>(within / (lo + 1));
+            int pth = static_cast<int>(within % (lo + 1));
+            int ee = 0;
+            for (; ee < E; ++ee) {
+                if (Ls[ee] <= v) {
+                    if (pth == 0) break;
+                    --pth;
+                }
+            }
+            // the loads the scan kernel derived give expert ee more than v
+            // rows; checked so that no row outside its range is written
+            if (ee < E && v < offsets[ee + 1] - offsets[ee]) {
+                dst = offsets[ee] + v;
+                src_token[dst] = static_cast<int32_t>(t);
+            }
+        }
+        dest_row[t * k + j] = dst;
+        ++o;
     }
 }
 
 // Destination rows of token t's k slots, computed by lanes 0..k-1 and
 // broadcast to the wave. Lanes 0..k-1 also write dest_row and src_token.
-// With cap > 0, a slot whose rank among all of its expert's assignments
-// (blk - offsets + r: earlier blocks' count plus the rank within the block)
-// is cap or more is dropped.
+// A slot's rank g among all of its expert's assignments is the expert's
+// count in earlier rank blocks plus its rank within the block; its row is
+// offsets[e] + g. With cap > 0 a slot with g >= cap is dropped or, with
+// reassign, takes the row the overflow kernel wrote to dest_row.
 __device__ __forceinline__ int token_dest(const int32_t* __restrict__ topk_idx,
                                           const int32_t* __restrict__ rank,
                                           const int32_t* __restrict__ blk,
                                           const int32_t* __restrict__ offsets, int cap,
-                                          int64_t t, int E, int k, int lane,
+                                          int reassign, int64_t t, int E, int k, int lane,
                                           int32_t* __restrict__ dest_row,
                                           int32_t* __restrict__ src_token) {
     int dst = -1;
@@ -158,9 +358,13 @@ __device__ __forceinline__ int token_dest(const int32_t* __restrict__ topk_idx,
         const int r = rank[t * k + lane];
         if (r >= 0) {
             const int e = topk_idx[t * k + lane];
-            dst = blk[(t / kRankBlockTokens) * E + e] + r;
-            if (cap > 0 && dst - offsets[e] >= cap) dst = -1;
-            if (dst >= 0) src_token[dst] = static_cast<int32_t>(t);
+            const int g = blk[(t / kRankBlockTokens) * E + e] + r;
+            if (cap > 0 && g >= cap) {
+                dst = reassign ? dest_row[t * k + lane] : -1;
+            } else {
+                dst = offsets[e] + g;
+                src_token[dst] = static_cast<int32_t>(t);
+            }
         }
         dest_row[t * k + lane] = dst;
     }
@@ -170,14 +374,16 @@ __device__ __forceinline__ int token_dest(const int32_t* __restrict__ topk_idx,
 __global__ __launch_bounds__(256) void dispatch_permute_kernel(
     const uint8_t* __restrict__ x, const int32_t* __restrict__ topk_idx,
     const int32_t* __restrict__ rank, const int32_t* __restrict__ blk,
-    const int32_t* __restrict__ offsets, int cap, int64_t T, int E, int k, int row_bytes,
+    const int32_t* __restrict__ offsets, int cap, int reassign, int64_t T, int E, int k,
+    int row_bytes,
     int32_t* __restrict__ dest_row, int32_t* __restrict__ src_token,
     uint8_t* __restrict__ x_perm) {
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + w;
     if (t >= T) return;
     const int dst =
-        token_dest(topk_idx, rank, blk, offsets, cap, t, E, k, lane, dest_row, src_token);
+        token_dest(topk_idx, rank, blk, offsets, cap, reassign, t, E, k, lane, dest_row,
+                   src_token);
     int dj[kMaxK];
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) dj[j] = __shfl(dst, j, kWave);
@@ -231,14 +437,15 @@ __device__ __forceinline__ u32x4 quant16(u32x4 a, u32x4 b, float c, float inv, b
 __global__ __launch_bounds__(256) void dispatch_permute_fp8_kernel(
     const bf16_t* __restrict__ x, const int32_t* __restrict__ topk_idx,
     const int32_t* __restrict__ rank, const int32_t* __restrict__ blk,
-    const int32_t* __restrict__ offsets, int cap, int64_t T, int E, int k, int d,
+    const int32_t* __restrict__ offsets, int cap, int reassign, int64_t T, int E, int k, int d,
     int32_t* __restrict__ dest_row, int32_t* __restrict__ src_token,
     uint8_t* __restrict__ x_perm, float* __restrict__ qparams) {
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + w;
     if (t >= T) return;
     const int dst =
-        token_dest(topk_idx, rank, blk, offsets, cap, t, E, k, lane, dest_row, src_token);
+        token_dest(topk_idx, rank, blk, offsets, cap, reassign, t, E, k, lane, dest_row,
+                   src_token);
     int dj[kMaxK];
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) dj[j] = __shfl(dst, j, kWave);
@@ -283,22 +490,30 @@ __global__ __launch_bounds__(256) void dispatch_permute_fp8_kernel(
 hipError_t launch_dispatch(const moe_shape& s, const void* x, const int32_t* topk_idx,
                            int32_t* counts, int32_t* offsets, int32_t* dest_row,
                            int32_t* src_token, void* x_perm, float* qparams, int32_t* rank,
-                           int32_t* blk, uint32_t* hdr, hipStream_t st, const Marks* mk) {
+                           int32_t* blk, int32_t* first_loads, uint32_t* hdr, hipStream_t st,
+                           const Marks* mk) {
     const int nblk = static_cast<int>((s.T + kRankBlockTokens - 1) / kRankBlockTokens);
+    const int reassign = s.capacity > 0 && s.overflow == MOE_OVERFLOW_REASSIGN ? 1 : 0;
     dispatch_rank_kernel<<<nblk, kRankThreads, 0, st>>>(topk_idx, s.T, s.E, s.k, rank, blk, hdr);
     mark(mk);
-    dispatch_scan_kernel<<<1, kScanThreads, 0, st>>>(blk, nblk, s.E, s.capacity, counts, offsets);
+    dispatch_scan_kernel<<<1, kScanThreads, 0, st>>>(blk, nblk, s.E, s.capacity, reassign, counts,
+                                                     offsets, first_loads);
     mark(mk);
+    // (its time is counted with the permute's in a traced forward)
+    if (reassign)
+        dispatch_overflow_kernel<<<nblk, kRankThreads, 0, st>>>(topk_idx, rank, blk, offsets,
+                                                                first_loads, s.T, s.E, s.k,
+                                                                s.capacity, dest_row, src_token);
     const unsigned pblocks = static_cast<unsigned>((s.T + 3) / 4);
     if (s.dispatch == MOE_FP8_E4M3) {
         dispatch_permute_fp8_kernel<<<pblocks, 256, 0, st>>>(
-            static_cast<const bf16_t*>(x), topk_idx, rank, blk, offsets, s.capacity, s.T, s.E,
-            s.k, s.d, dest_row, src_token, static_cast<uint8_t*>(x_perm), qparams);
+            static_cast<const bf16_t*>(x), topk_idx, rank, blk, offsets, s.capacity, reassign, s.T,
+            s.E, s.k, s.d, dest_row, src_token, static_cast<uint8_t*>(x_perm), qparams);
     } else {
         const int row_bytes = s.d * (s.act == MOE_F32 ? 4 : 2);
         dispatch_permute_kernel<<<pblocks, 256, 0, st>>>(
-            static_cast<const uint8_t*>(x), topk_idx, rank, blk, offsets, s.capacity, s.T, s.E,
-            s.k, row_bytes, dest_row, src_token, static_cast<uint8_t*>(x_perm));
+            static_cast<const uint8_t*>(x), topk_idx, rank, blk, offsets, s.capacity, reassign, s.T,
+            s.E, s.k, row_bytes, dest_row, src_token, static_cast<uint8_t*>(x_perm));
     }
     mark(mk);
     return hipGetLastError();

@@ -58,8 +58,10 @@ class MoEConfig:
     outlier_p: float = 0.0
     outlier_scale: float = 1.0
     # rows each routed expert may hold (0: no limit); beyond it, assignments
-    # in token order are dropped
+    # in token order are dropped, or with reassign handed to the least-loaded
+    # expert
     capacity: int = 0
+    reassign: bool = False
     # relative-L2 bound on the layer output y
     tol_y: float = 2e-2
 
@@ -97,6 +99,13 @@ CONFIGS = {
 CONFIGS["zipf_capacity_bf16"] = MoEConfig(
     "zipf_capacity_bf16", T=16384, d=2048, E=128, k=4, S=0, h=512, act="bf16",
     dispatch="act", zipf_bias=True, capacity=640, tol_y=2e-2)
+
+# The same with the overflow reassigned to the least-loaded expert (the
+# option those notes say V3 mainly uses); capacity factor 1.0, so that every
+# expert ends with exactly T*k/E rows.
+CONFIGS["zipf_reassign_bf16"] = MoEConfig(
+    "zipf_reassign_bf16", T=16384, d=2048, E=128, k=4, S=0, h=512, act="bf16",
+    dispatch="act", zipf_bias=True, capacity=512, reassign=True, tol_y=2e-2)
 
 # the order the five configs are listed in the workload table
 CONFIG_ORDER = ["tiny_fp32", "deepseekmoe_bf16", "coarse_top2_bf16",

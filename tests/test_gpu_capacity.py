@@ -1,10 +1,11 @@
 """GPU parity of the capacity-limited dispatch (a strict per-expert row cap;
-assignments beyond it, in token order, are dropped) against the oracle.
+assignments beyond it, in token order, are dropped or reassigned to the
+least-loaded expert) against the oracle.
 
 Bars as in the other parity tests: routing and every dispatch array
 bit-exact, the dispatched rows a bit-exact copy, and the layer output within
-the workload's relative-L2 bound on sampled tokens, where the oracle's keep
-mask comes from its own capacity dispatch over the whole batch.
+the workload's relative-L2 bound on sampled tokens, where the oracle's
+per-slot route comes from its own capacity dispatch over the whole batch.
 """
 
 from __future__ import annotations
@@ -30,16 +31,17 @@ def _mm():
 def forward_vs_oracle(inp, toks=None):
     mm, cfg = _mm(), inp.cfg
     say(f"[capacity] T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} S={cfg.S} h={cfg.h} "
-        f"act={cfg.act} dispatch={cfg.dispatch} capacity={cfg.capacity}")
+        f"act={cfg.act} dispatch={cfg.dispatch} capacity={cfg.capacity} reassign={cfg.reassign}")
     shape = mm.shape_of(cfg)
-    assert shape.capacity == cfg.capacity
+    assert shape.capacity == cfg.capacity and shape.overflow == int(cfg.reassign)
     buf = mm.ForwardBuffers(shape)
     bias = None if inp.bias is None else dev(inp.bias)
     buf.run(dev(inp.x), dev(inp.wg), bias, dev(inp.w1), dev(inp.w3), dev(inp.w2))
     torch.cuda.synchronize()
     assert mm.moe_get_device_error(buf.ws) == mm.MOE_OK
     oidx, ow, _ = oracle.gate_topk(inp.x, inp.wg, cfg.k, inp.bias, nthreads=ORACLE_THREADS)
-    counts, offsets, dest, src = oracle.dispatch(oidx, cfg.E, capacity=cfg.capacity)
+    counts, offsets, dest, src, route = oracle.dispatch(oidx, cfg.E, capacity=cfg.capacity,
+                                                        reassign=cfg.reassign, return_route=True)
     n = int(offsets[cfg.E])
     say(f"[capacity] kept {n} of {cfg.T * cfg.k} assignments")
     assert np.array_equal(host(buf.topk_idx), oidx)
@@ -47,30 +49,33 @@ def forward_vs_oracle(inp, toks=None):
     assert np.array_equal(host(buf.offsets), offsets)
     assert np.array_equal(host(buf.dest_row), dest)
     assert np.array_equal(host(buf.src_token)[:n], src[:n])
-    keep = dest >= 0
     if toks is None:
         toks = np.arange(cfg.T)
-    _, _, oy = oracle.layer_tokens(inp, toks, nthreads=ORACLE_THREADS, keep=keep[toks])
+    _, _, oy = oracle.layer_tokens(inp, toks, nthreads=ORACLE_THREADS, route=route[toks])
     err = rel_l2(host(buf.y)[toks], oy)
     say(f"[capacity] y rel-L2 {err:.3e} on {len(toks)} tokens")
     assert err <= cfg.tol_y
-    return buf, keep
+    return buf, route
 
 
-def test_skewed_workload_with_capacity_factor_1_25():
-    cfg = CONFIGS["zipf_capacity_bf16"]
+@pytest.mark.parametrize("name", ["zipf_capacity_bf16", "zipf_reassign_bf16"])
+def test_skewed_workload_with_capacity(name):
+    cfg = CONFIGS[name]
     inp = make_inputs(cfg)
     rng = np.random.default_rng(0)
-    # the oracle's keep mask decides which sampled tokens lost a slot; take
-    # some of those, some that kept everything, and the ends
+    # the oracle's route decides which tokens lost or moved a slot; take some
+    # of those, some that kept their experts, and the ends
     oidx, _, _ = oracle.gate_topk(inp.x, inp.wg, cfg.k, inp.bias, nthreads=ORACLE_THREADS)
-    _, _, dest, _ = oracle.dispatch(oidx, cfg.E, capacity=cfg.capacity)
-    dropped = np.nonzero((dest < 0).any(axis=1))[0]
-    full = np.nonzero((dest >= 0).all(axis=1))[0]
-    assert len(dropped) > 0 and len(full) > 0
-    toks = np.unique(np.concatenate([rng.choice(dropped, 24), rng.choice(full, 16),
+    _, _, _, _, route = oracle.dispatch(oidx, cfg.E, capacity=cfg.capacity, reassign=cfg.reassign,
+                                        return_route=True)
+    moved = np.nonzero((route != oidx).any(axis=1))[0]
+    same = np.nonzero((route == oidx).all(axis=1))[0]
+    assert len(moved) > 0 and len(same) > 0
+    toks = np.unique(np.concatenate([rng.choice(moved, 24), rng.choice(same, 16),
                                      [0, cfg.T - 1]])).astype(np.int64)
-    forward_vs_oracle(inp, toks)
+    buf, _ = forward_vs_oracle(inp, toks)
+    if cfg.reassign and cfg.T * cfg.k == cfg.E * cfg.capacity:
+        assert np.all(host(buf.counts) == cfg.capacity)  # every expert equally loaded
 
 
 def test_capacity_dispatch_stage_payload():
@@ -111,17 +116,25 @@ def _small(act="bf16", **kw):
 
 @pytest.mark.parametrize("kw", [
     dict(T=300, d=128, E=8, k=2, S=1, h=64, capacity=1),        # one row per expert
+    dict(T=300, d=128, E=8, k=2, S=1, h=64, capacity=1, reassign=True),  # all but 8 dropped
+    dict(T=520, d=256, E=16, k=4, S=0, h=128, capacity=90, reassign=True),  # some overflow left
+    dict(T=512, d=128, E=16, k=2, S=0, h=64, capacity=64, reassign=True),   # exactly full
+    dict(T=700, d=128, E=256, k=8, S=2, h=64, capacity=30, reassign=True),  # largest E and k
     dict(T=520, d=256, E=16, k=4, S=0, h=128, capacity=90),     # binds on some experts
     dict(T=400, d=128, E=8, k=2, S=0, h=64, capacity=400),      # never binds
     dict(T=600, d=256, E=32, k=8, S=2, h=128, capacity=100, dispatch="fp8", tol_y=6e-2),
-], ids=["cap_1", "cap_binds", "cap_never_binds", "fp8_cap"])
+    dict(T=600, d=256, E=32, k=8, S=2, h=128, capacity=160, dispatch="fp8", tol_y=6e-2,
+         reassign=True),
+], ids=["cap_1", "re_cap_1", "re_overflow_left", "re_exact", "re_max_E_k", "cap_binds",
+        "cap_never_binds", "fp8_cap", "fp8_re"])
 def test_bf16_capacity_shapes(kw):
     forward_vs_oracle(make_inputs(_small(**kw), seed=6))
 
 
-def test_f32_capacity_odd_dims():
+@pytest.mark.parametrize("reassign", [False, True])
+def test_f32_capacity_odd_dims(reassign):
     forward_vs_oracle(make_inputs(_small("f32", T=97, d=36, E=5, k=2, S=1, h=50, capacity=20,
-                                         tol_y=1e-5), seed=7))
+                                         reassign=reassign, tol_y=1e-5), seed=7))
 
 
 def test_capacity_never_binding_equals_dropless():
@@ -129,9 +142,10 @@ def test_capacity_never_binding_equals_dropless():
     cfg = _small(T=500, d=128, E=8, k=2, S=1, h=64)
     inp = make_inputs(cfg, seed=8)
     outs = []
-    for cap in (0, cfg.T):
-        buf = mm.ForwardBuffers(mm.shape_of(dataclasses.replace(cfg, capacity=cap)))
+    for cap, re in ((0, False), (cfg.T, False), (cfg.T, True)):
+        buf = mm.ForwardBuffers(mm.shape_of(dataclasses.replace(cfg, capacity=cap, reassign=re)))
         buf.run(dev(inp.x), dev(inp.wg), None, dev(inp.w1), dev(inp.w3), dev(inp.w2))
         torch.cuda.synchronize()
         outs.append((host(buf.y).copy(), host(buf.dest_row).copy()))
-    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+    for y, dest in outs[1:]:
+        assert np.array_equal(outs[0][0], y) and np.array_equal(outs[0][1], dest)
