@@ -169,13 +169,14 @@ __device__ void water_fill_loads(const int* n, int* load, int E, int cap) {
     }
 }
 
-// blk[nblk][E] holds each rank block's per-expert counts on entry and, on
-// exit, the number of the expert's assignments in earlier rank blocks.
-// With cap > 0, first_loads[e] receives min(n_e, cap); with reassign the
-// counts are the loads after reassignment.
+// blk[nblk][E] holds each rank block's per-expert counts; pre[nblk][E]
+// receives the number of the expert's assignments in earlier rank blocks.
+// (Two arrays, so that the loads of a thread's run of blocks are not held
+// behind its stores.) With cap > 0, first_loads[e] receives min(n_e, cap);
+// with reassign the counts are the loads after reassignment.
 __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
-    int32_t* __restrict__ blk, int nblk, int E, int cap, int reassign,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ blk, int32_t* __restrict__ pre, int nblk, int E, int cap,
+    int reassign, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ first_loads) {
     __shared__ int part[kScanThreads];  // [P][E] partial sums
     __shared__ int raw[kMaxE];
@@ -188,12 +189,8 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
     const int per = (nblk + P - 1) / P;
     const int b0 = active ? min(nblk, p * per) : 0, b1 = active ? min(nblk, b0 + per) : 0;
     int run = 0;
-    for (int b = b0; b < b1; ++b) {
-        const int64_t i = static_cast<int64_t>(b) * E + e;
-        const int c = blk[i];
-        blk[i] = run;
-        run += c;
-    }
+#pragma unroll 8
+    for (int b = b0; b < b1; ++b) run += blk[static_cast<int64_t>(b) * E + e];
     if (active) part[p * E + e] = run;
     __syncthreads();
     if (tid < E) {
@@ -227,8 +224,13 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
     }
     if (tid == 0) offsets[E] = off[E];
     if (active) {
-        const int base = part[p * E + e];
-        for (int b = b0; b < b1; ++b) blk[static_cast<int64_t>(b) * E + e] += base;
+        int acc = part[p * E + e];
+#pragma unroll 8
+        for (int b = b0; b < b1; ++b) {
+            const int64_t i = static_cast<int64_t>(b) * E + e;
+            pre[i] = acc;
+            acc += blk[i];
+        }
     }
 }
 
@@ -245,7 +247,7 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
 // each level in [s_i, s_{i+1}) holds i+1 overflows.
 __global__ __launch_bounds__(kRankThreads) void dispatch_overflow_kernel(
     const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ rank,
-    const int32_t* __restrict__ blk, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ pre, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ first_loads, int64_t T, int E, int k, int cap,
     int32_t* __restrict__ dest_row, int32_t* __restrict__ src_token) {
     __shared__ int Ls[kMaxE];
@@ -263,7 +265,7 @@ __global__ __launch_bounds__(kRankThreads) void dispatch_overflow_kernel(
         int pos = 0;
         for (int q = 0; q < E; ++q) pos += (Ls[q] < Ls[e] || (Ls[q] == Ls[e] && q < e)) ? 1 : 0;
         sl[pos] = Ls[e];
-        ob += max(0, blk[static_cast<int64_t>(b) * E + e] - cap);
+        ob += max(0, pre[static_cast<int64_t>(b) * E + e] - cap);
     }
     ob = wave_sum64(ob);
     if (lane == 0) wred[w] = ob;
@@ -295,7 +297,7 @@ __global__ __launch_bounds__(kRankThreads) void dispatch_overflow_kernel(
             const int r = rank[t * k + j];
             if (r < 0) continue;
             const int e = topk_idx[t * k + j];
-            mine += blk[static_cast<int64_t>(b) * E + e] + r >= cap ? 1 : 0;
+            mine += pre[static_cast<int64_t>(b) * E + e] + r >= cap ? 1 : 0;
         }
     }
     const int wex = wave_excl_scan(mine);
@@ -309,7 +311,7 @@ __global__ __launch_bounds__(kRankThreads) void dispatch_overflow_kernel(
         const int r = rank[t * k + j];
         if (r < 0) continue;
         const int e = topk_idx[t * k + j];
-        if (blk[static_cast<int64_t>(b) * E + e] + r < cap) continue;
+        if (pre[static_cast<int64_t>(b) * E + e] + r < cap) continue;
         int dst = -1;
         if (o < Bk[E]) {
             int lo = 0, hi = E - 1;  // the last i with Bk[i] <= o
@@ -348,7 +350,7 @@ __global__ __launch_bounds__(kRankThreads) void dispatch_overflow_kernel(
 // reassign, takes the row the overflow kernel wrote to dest_row.
 __device__ __forceinline__ int token_dest(const int32_t* __restrict__ topk_idx,
                                           const int32_t* __restrict__ rank,
-                                          const int32_t* __restrict__ blk,
+                                          const int32_t* __restrict__ pre,
                                           const int32_t* __restrict__ offsets, int cap,
                                           int reassign, int64_t t, int E, int k, int lane,
                                           int32_t* __restrict__ dest_row,
@@ -358,7 +360,7 @@ __device__ __forceinline__ int token_dest(const int32_t* __restrict__ topk_idx,
         const int r = rank[t * k + lane];
         if (r >= 0) {
             const int e = topk_idx[t * k + lane];
-            const int g = blk[(t / kRankBlockTokens) * E + e] + r;
+            const int g = pre[(t / kRankBlockTokens) * E + e] + r;
             if (cap > 0 && g >= cap) {
                 dst = reassign ? dest_row[t * k + lane] : -1;
             } else {
@@ -373,7 +375,7 @@ __device__ __forceinline__ int token_dest(const int32_t* __restrict__ topk_idx,
 
 __global__ __launch_bounds__(256) void dispatch_permute_kernel(
     const uint8_t* __restrict__ x, const int32_t* __restrict__ topk_idx,
-    const int32_t* __restrict__ rank, const int32_t* __restrict__ blk,
+    const int32_t* __restrict__ rank, const int32_t* __restrict__ pre,
     const int32_t* __restrict__ offsets, int cap, int reassign, int64_t T, int E, int k,
     int row_bytes,
     int32_t* __restrict__ dest_row, int32_t* __restrict__ src_token,
@@ -382,7 +384,7 @@ __global__ __launch_bounds__(256) void dispatch_permute_kernel(
     const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + w;
     if (t >= T) return;
     const int dst =
-        token_dest(topk_idx, rank, blk, offsets, cap, reassign, t, E, k, lane, dest_row,
+        token_dest(topk_idx, rank, pre, offsets, cap, reassign, t, E, k, lane, dest_row,
                    src_token);
     int dj[kMaxK];
 #pragma unroll
@@ -436,7 +438,7 @@ __device__ __forceinline__ u32x4 quant16(u32x4 a, u32x4 b, float c, float inv, b
 
 __global__ __launch_bounds__(256) void dispatch_permute_fp8_kernel(
     const bf16_t* __restrict__ x, const int32_t* __restrict__ topk_idx,
-    const int32_t* __restrict__ rank, const int32_t* __restrict__ blk,
+    const int32_t* __restrict__ rank, const int32_t* __restrict__ pre,
     const int32_t* __restrict__ offsets, int cap, int reassign, int64_t T, int E, int k, int d,
     int32_t* __restrict__ dest_row, int32_t* __restrict__ src_token,
     uint8_t* __restrict__ x_perm, float* __restrict__ qparams) {
@@ -444,7 +446,7 @@ __global__ __launch_bounds__(256) void dispatch_permute_fp8_kernel(
     const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + w;
     if (t >= T) return;
     const int dst =
-        token_dest(topk_idx, rank, blk, offsets, cap, reassign, t, E, k, lane, dest_row,
+        token_dest(topk_idx, rank, pre, offsets, cap, reassign, t, E, k, lane, dest_row,
                    src_token);
     int dj[kMaxK];
 #pragma unroll
@@ -490,29 +492,29 @@ __global__ __launch_bounds__(256) void dispatch_permute_fp8_kernel(
 hipError_t launch_dispatch(const moe_shape& s, const void* x, const int32_t* topk_idx,
                            int32_t* counts, int32_t* offsets, int32_t* dest_row,
                            int32_t* src_token, void* x_perm, float* qparams, int32_t* rank,
-                           int32_t* blk, int32_t* first_loads, uint32_t* hdr, hipStream_t st,
-                           const Marks* mk) {
+                           int32_t* blk, int32_t* pre, int32_t* first_loads, uint32_t* hdr,
+                           hipStream_t st, const Marks* mk) {
     const int nblk = static_cast<int>((s.T + kRankBlockTokens - 1) / kRankBlockTokens);
     const int reassign = s.capacity > 0 && s.overflow == MOE_OVERFLOW_REASSIGN ? 1 : 0;
     dispatch_rank_kernel<<<nblk, kRankThreads, 0, st>>>(topk_idx, s.T, s.E, s.k, rank, blk, hdr);
     mark(mk);
-    dispatch_scan_kernel<<<1, kScanThreads, 0, st>>>(blk, nblk, s.E, s.capacity, reassign, counts,
-                                                     offsets, first_loads);
+    dispatch_scan_kernel<<<1, kScanThreads, 0, st>>>(blk, pre, nblk, s.E, s.capacity, reassign,
+                                                     counts, offsets, first_loads);
     mark(mk);
     // (its time is counted with the permute's in a traced forward)
     if (reassign)
-        dispatch_overflow_kernel<<<nblk, kRankThreads, 0, st>>>(topk_idx, rank, blk, offsets,
+        dispatch_overflow_kernel<<<nblk, kRankThreads, 0, st>>>(topk_idx, rank, pre, offsets,
                                                                 first_loads, s.T, s.E, s.k,
                                                                 s.capacity, dest_row, src_token);
     const unsigned pblocks = static_cast<unsigned>((s.T + 3) / 4);
     if (s.dispatch == MOE_FP8_E4M3) {
         dispatch_permute_fp8_kernel<<<pblocks, 256, 0, st>>>(
-            static_cast<const bf16_t*>(x), topk_idx, rank, blk, offsets, s.capacity, reassign, s.T,
+            static_cast<const bf16_t*>(x), topk_idx, rank, pre, offsets, s.capacity, reassign, s.T,
             s.E, s.k, s.d, dest_row, src_token, static_cast<uint8_t*>(x_perm), qparams);
     } else {
         const int row_bytes = s.d * (s.act == MOE_F32 ? 4 : 2);
         dispatch_permute_kernel<<<pblocks, 256, 0, st>>>(
-            static_cast<const uint8_t*>(x), topk_idx, rank, blk, offsets, s.capacity, reassign, s.T,
+            static_cast<const uint8_t*>(x), topk_idx, rank, pre, offsets, s.capacity, reassign, s.T,
             s.E, s.k, row_bytes, dest_row, src_token, static_cast<uint8_t*>(x_perm));
     }
     mark(mk);
