@@ -58,8 +58,9 @@ def lib():
         L.oracle_e4m3_encode.restype = ctypes.c_uint8
         L.oracle_fp8_quantize.argtypes = [i64, i32, i32, vp, vp, vp, i32]
         L.oracle_expert_rows.argtypes = [i32, i32, i32, i64, vp, vp, vp, vp, vp, vp, i32]
-        L.oracle_layer_tokens.argtypes = [i32, i32, i32, i32, i32, i32, i32, i64, vp, vp,
+        L.oracle_layer_tokens.argtypes = [i32, i32, i32, i32, i32, i32, i32, i64, vp, vp, vp,
                                           vp, vp, vp, vp, vp, vp, vp, vp, vp, i32]
+        L.oracle_fp8_quantize_ranges.argtypes = [i64, i32, i32, vp, vp, vp, vp]
         L.oracle_combine.argtypes = [i64, i32, i32, i32, vp, vp, vp, vp, i64, vp]
         L.oracle_bf16_to_float.argtypes = [ctypes.c_uint16]
         L.oracle_bf16_to_float.restype = ctypes.c_float
@@ -155,12 +156,22 @@ def e4m3_encode(v: float) -> int:
     return int(lib().oracle_e4m3_encode(float(v)))
 
 
-def fp8_quantize(x, nthreads=1):
-    """Per-row affine e4m3 codes [T,d] uint8 and qparams [T,2] float32 (s, c)."""
+def fp8_quantize(x, nthreads=1, ranges=None):
+    """Per-row affine e4m3 codes [T,d] uint8 and qparams [T,2] float32 (s, c).
+
+    ranges [T,2] (optional): the (min, max) each row is mapped from -- its
+    expert's or the batch's in the per-expert and global quantiser modes;
+    by default the row's own min/max.
+    """
     x = np.ascontiguousarray(x)
     T, d = x.shape
     q = np.empty((T, d), dtype=np.uint8)
     qp = np.empty((T, 2), dtype=np.float32)
+    if ranges is not None:
+        r = np.ascontiguousarray(ranges, dtype=np.float32).reshape(T, 2)
+        _check(lib().oracle_fp8_quantize_ranges(T, d, _dtype_code(x), _p(x), _p(r), _p(q), _p(qp)),
+               "fp8_quantize_ranges")
+        return q, qp
     _check(lib().oracle_fp8_quantize(T, d, _dtype_code(x), _p(x), _p(q), _p(qp),
                                      _nthreads(nthreads)), "fp8_quantize")
     return q, qp
@@ -186,13 +197,16 @@ def expert_rows(rows, group, w1, w3, w2, nthreads=1):
     return out
 
 
-def layer_tokens(inp, tokens, nthreads=1, route=None):
+def layer_tokens(inp, tokens, nthreads=1, route=None, qrange=None):
     """Whole-layer output for the listed tokens: (topk_idx, topk_w, y float64).
 
     route [n, k] (int, optional): under a capacity limit, the expert whose
     row each slot got (-1: dropped, contributes nothing; a reassigned slot
     keeps its gate weight). It depends on the whole batch's routing, so the
     caller takes it from dispatch(..., capacity, return_route=True).
+    qrange [n, k, 2] (optional, fp8 rows): the (min, max) range each slot's
+    row is quantised with -- its expert's or the batch's in the per-expert
+    and global quantiser modes; by default each token's own.
     """
     cfg = inp.cfg
     tokens = np.ascontiguousarray(tokens, dtype=np.int64)
@@ -205,6 +219,8 @@ def layer_tokens(inp, tokens, nthreads=1, route=None):
                                      1 if cfg.dispatch == "fp8" else 0, n, _p(tokens),
                                      _p(None if route is None else
                                         np.ascontiguousarray(route, dtype=np.int32).reshape(n, cfg.k)),
+                                     _p(None if qrange is None else
+                                        np.ascontiguousarray(qrange, dtype=np.float32).reshape(n, cfg.k, 2)),
                                      _p(inp.x),
                                      _p(inp.wg), _p(b), _p(inp.w1), _p(inp.w3), _p(inp.w2),
                                      _p(idx), _p(w), _p(y), _nthreads(nthreads)), "layer_tokens")

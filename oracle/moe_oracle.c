@@ -301,18 +301,17 @@ uint8_t oracle_e4m3_encode(float v)
     return (uint8_t)(best | (signbit(v) ? 0x80 : 0));
 }
 
-int oracle_fp8_quantize_row(int d, const float *xr, uint8_t *q, float *scale,
-                            float *centre)
+/*
+ * The affine map of the range [mn, mx] onto [-448, 448], applied to one row.
+ * Per-token mode takes the row's own min/max; the per-expert and global modes
+ * of gsyq.cn section 5.2 (the FP8 quantiser's three modes) take the min/max
+ * over the expert's rows or over the whole batch, which contain the row.
+ */
+int oracle_fp8_quantize_row_range(int d, const float *xr, float mn, float mx,
+                                  uint8_t *q, float *scale, float *centre)
 {
-    if (d <= 0)
+    if (d <= 0 || !(mn <= mx))
         return -1;
-    float mn = xr[0], mx = xr[0];
-    for (int i = 1; i < d; ++i) {
-        if (xr[i] < mn)
-            mn = xr[i];
-        if (xr[i] > mx)
-            mx = xr[i];
-    }
     float c = 0.5f * (mx + mn);
     float r = 0.5f * (mx - mn);
     *centre = c;
@@ -333,6 +332,41 @@ int oracle_fp8_quantize_row(int d, const float *xr, uint8_t *q, float *scale,
         q[i] = oracle_e4m3_encode(v);
     }
     return 0;
+}
+
+int oracle_fp8_quantize_row(int d, const float *xr, uint8_t *q, float *scale,
+                            float *centre)
+{
+    if (d <= 0)
+        return -1;
+    float mn = xr[0], mx = xr[0];
+    for (int i = 1; i < d; ++i) {
+        if (xr[i] < mn)
+            mn = xr[i];
+        if (xr[i] > mx)
+            mx = xr[i];
+    }
+    return oracle_fp8_quantize_row_range(d, xr, mn, mx, q, scale, centre);
+}
+
+/* rows [T,d] of x, each with its given range ranges[t] = (min, max) */
+int oracle_fp8_quantize_ranges(int64_t T, int d, int dtype, const void *x,
+                               const float *ranges, uint8_t *q, float *qp)
+{
+    if (T < 0 || d <= 0)
+        return -1;
+    float *row = (float *)malloc(sizeof(float) * (size_t)d);
+    if (!row)
+        return -4;
+    int rc = 0;
+    for (int64_t t = 0; t < T && rc == 0; ++t) {
+        for (int i = 0; i < d; ++i)
+            row[i] = elem(x, dtype, t * d + i);
+        rc = oracle_fp8_quantize_row_range(d, row, ranges[2 * t], ranges[2 * t + 1],
+                                           q + t * d, &qp[2 * t], &qp[2 * t + 1]);
+    }
+    free(row);
+    return rc;
 }
 
 /* quantise rows [T,d] of x (float32 or bf16): codes [T,d], qp [T,2] = (s, c) */
@@ -430,12 +464,14 @@ int oracle_expert_rows(int d, int h, int wdt, int64_t n, const int32_t *group,
  * route [n,k] (or NULL: the top-k experts themselves) names the expert each
  * slot's row went to under a capacity limit, -1 for a dropped slot, which
  * contributes nothing (its weight is not given to the other slots); a
- * reassigned slot keeps its gate weight.
+ * reassigned slot keeps its gate weight. qrange [n,k,2] (or NULL: each
+ * token's own min/max) gives the (min, max) range each slot's fp8 row is
+ * quantised with (the per-expert or global quantiser modes).
  * Outputs per listed token: topk_idx [n,k], topk_w [n,k], y [n,d] float64.
  */
 int oracle_layer_tokens(int d, int E, int k, int S, int h, int dtype, int fp8,
                         int64_t n, const int64_t *tokens, const int32_t *route,
-                        const void *x,
+                        const float *qrange, const void *x,
                         const void *wg, const float *bias, const void *w1,
                         const void *w3, const void *w2, int32_t *topk_idx,
                         double *topk_w, double *y, int nthreads)
@@ -491,6 +527,17 @@ int oracle_layer_tokens(int d, int E, int k, int S, int h, int dtype, int fp8,
                 if (route && route[r * k + j] < 0)
                     continue; /* dropped by a capacity limit */
                 int64_t g = route ? route[r * k + j] : topk_idx[r * k + j];
+                if (fp8 && qrange) {
+                    /* per-expert or global range for this slot */
+                    float s, c;
+                    if (oracle_fp8_quantize_row_range(d, xf, qrange[2 * (r * k + j)],
+                                                      qrange[2 * (r * k + j) + 1], q, &s, &c)) {
+                        rc = -5;
+                        continue;
+                    }
+                    for (int i = 0; i < d; ++i)
+                        vq[i] = oracle_e4m3_decode(q[i]) * (double)s + (double)c;
+                }
                 swiglu_ffn(d, h, dtype, vq, group_ptr(w1, dtype, g, (int64_t)h * d),
                            group_ptr(w3, dtype, g, (int64_t)h * d),
                            group_ptr(w2, dtype, g, (int64_t)d * h), o, hbuf);

@@ -150,3 +150,19 @@ def test_layer_route():
     _, w, y_drop = oracle.layer_tokens(inp, toks, route=drop)
     ref = dense_swiglu(v, inp.w1[0], inp.w3[0], inp.w2[0]) * (1.0 - w[:, 1:2])
     np.testing.assert_allclose(y_drop, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_layer_qrange_own_range_is_the_default():
+    inp = _small("bf16", E=6, k=2, S=1, fp8=True)
+    toks = np.arange(inp.cfg.T)
+    _, _, y = oracle.layer_tokens(inp, toks)
+    xf = bf16_bits_to_f32(inp.x)
+    own = np.stack([xf.min(1), xf.max(1)], 1).astype(np.float32)
+    qr = np.repeat(own[:, None, :], 2, axis=1)
+    _, _, y2 = oracle.layer_tokens(inp, toks, qrange=qr)
+    assert np.array_equal(y, y2)
+    # a wider range changes the routed experts' input only
+    wide = qr.copy()
+    wide[..., 0] -= 4.0
+    _, _, y3 = oracle.layer_tokens(inp, toks, qrange=wide)
+    assert not np.array_equal(y, y3)

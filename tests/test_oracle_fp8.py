@@ -85,3 +85,50 @@ def test_constant_row_is_exact():
     q, qp = oracle.fp8_quantize(x)
     assert np.all(q == 0) and np.all(qp[:, 0] == 0)
     assert np.array_equal(oracle.fp8_dequantize(q, qp), x.astype(np.float64))
+
+
+# ------------------------------------------- per-expert / global ranges ----
+# The quantiser's other modes (gsyq.cn section 5.2: per-token, per-expert,
+# global) map a row from a range wider than its own min/max: the expert's
+# rows' or the whole batch's. Pinned by the per-token map (a row's own range
+# must give the same codes) and by torch's e4m3 cast of the affine map
+# written out in float32.
+
+def _f32(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def test_own_range_equals_per_token_map():
+    rng = np.random.default_rng(3)
+    x = to_bf16_bits(rng.standard_normal((40, 96)).astype(np.float32) * 3)
+    q, qp = oracle.fp8_quantize(x)
+    xf = _f32(x)
+    q2, qp2 = oracle.fp8_quantize(x, ranges=np.stack([xf.min(1), xf.max(1)], 1))
+    assert np.array_equal(q, q2) and np.array_equal(qp.view(np.uint32), qp2.view(np.uint32))
+
+
+def test_wider_range_matches_torch_cast():
+    rng = np.random.default_rng(4)
+    x = to_bf16_bits(rng.standard_normal((64, 128)).astype(np.float32))
+    xf = _f32(x)
+    mn, mx = np.float32(xf.min() - 1.5), np.float32(xf.max() + 0.25)   # a group's wider range
+    ranges = np.tile(np.array([mn, mx], dtype=np.float32), (64, 1))
+    q, qp = oracle.fp8_quantize(x, ranges=ranges)
+    c = np.float32(0.5) * (mx + mn)
+    r = np.float32(0.5) * (mx - mn)
+    inv = np.float32(448.0) / r
+    v = np.clip((xf - c) * inv, -448.0, 448.0).astype(np.float32)
+    ref = torch.from_numpy(v).to(E4M3).view(torch.uint8).numpy()
+    assert np.array_equal(q, ref)
+    assert np.all(qp[:, 0] == r / np.float32(448.0)) and np.all(qp[:, 1] == c)
+    # the range's ends, where a row reaches them, land on the ends of e4m3
+    x2 = x.copy()
+    x2[0, 0], x2[0, 1] = to_bf16_bits(np.array([-3.0, 5.0], dtype=np.float32))
+    q2, _ = oracle.fp8_quantize(x2, ranges=np.tile(np.array([-3.0, 5.0], np.float32), (64, 1)))
+    assert oracle.e4m3_decode(int(q2[0, 0])) == -448.0 and oracle.e4m3_decode(int(q2[0, 1])) == 448.0
+
+
+def test_range_must_be_ordered():
+    x = to_bf16_bits(np.ones((1, 16), dtype=np.float32))
+    with pytest.raises(ValueError):
+        oracle.fp8_quantize(x, ranges=np.array([[1.0, 0.5]], dtype=np.float32))
