@@ -15,7 +15,8 @@
  *  [gsyq]  "Deepseek-MoE同步税本质与四层实战优化指南" (gsyq.cn), section 2.3:
  *          each token's output is the gate-weighted sum of its experts'
  *          outputs; section 3.1: per-token min/max affine FP8 quantiser at the
- *          dispatch entry.
+ *          dispatch entry; section 5.2: that quantiser's per-token,
+ *          per-expert and global modes.
  *  [deepep] "MoE数据特征、训练和推理的通信特点 ... DeepEP ... All-to-All"
  *          (zzszmyf.github.io), section 7: dispatch reorders tokens by target
  *          expert and packs them contiguously ([Local_Batch, Hidden] ->
@@ -77,6 +78,10 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
 /* what happens to an assignment beyond an expert's capacity */
 typedef enum { MOE_OVERFLOW_DROP = 0, MOE_OVERFLOW_REASSIGN = 1 } moe_overflow;
 
+/* the rows whose min/max range an fp8 row is mapped from ([gsyq] 5.2: the
+ * quantiser's per-token, per-expert and global modes) */
+typedef enum { MOE_QUANT_TOKEN = 0, MOE_QUANT_EXPERT = 1, MOE_QUANT_GLOBAL = 2 } moe_quant;
+
 /* which entry point a workspace is sized for */
 typedef enum {
     MOE_STAGE_GATE = 0,
@@ -102,6 +107,8 @@ typedef struct {
                          invalid. */
     int32_t overflow; /* moe_overflow: overflowing assignments are dropped or
                          reassigned to the least-loaded expert */
+    int32_t quant;    /* moe_quant, with dispatch = MOE_FP8_E4M3 only (else it
+                         must be MOE_QUANT_TOKEN) */
 } moe_shape;
 
 /* Host only. Bytes of workspace that `stage` needs for shape *s (0 when the
@@ -158,7 +165,12 @@ int32_t moe_gate_topk(const moe_shape *s, const void *x, const void *w_gate,
  *  qparams[dest_row[t,j]] = (scale, centre) (float32 [T*k, 2]): centre =
  *  (max+min)/2, scale = (max-min)/2/448, code = e4m3 round-to-nearest-even of
  *  clamp((x - centre) * (448 / ((max-min)/2)), +-448), all in float32; a
- *  constant row gets codes 0 and scale 0. qparams may be NULL otherwise.
+ *  constant row gets codes 0 and scale 0. With s->quant = MOE_QUANT_EXPERT
+ *  ([gsyq] 5.2) max and min are taken over every row dispatched to the
+ *  row's expert (its final rows, after any capacity limit), and with
+ *  MOE_QUANT_GLOBAL over all T rows of x; the map is otherwise the same, so
+ *  each dispatched row still carries its own (scale, centre).
+ *  qparams may be NULL otherwise.
  *  ws: MOE_STAGE_DISPATCH bytes.
  */
 int32_t moe_dispatch(const moe_shape *s, const void *x, const int32_t *topk_idx,

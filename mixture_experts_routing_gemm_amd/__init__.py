@@ -11,6 +11,7 @@ include/moe.h; this package is its ctypes binding. Build the library with
 from ._binding import (  # noqa: F401
     EXPORTS, MOE_BF16, MOE_ERR_BAD_INDEX, MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED,
     MOE_ERR_WORKSPACE, MOE_F32, MOE_FP8_E4M3, MOE_OK, MOE_OVERFLOW_DROP, MOE_OVERFLOW_REASSIGN,
+    MOE_QUANT_EXPERT, MOE_QUANT_GLOBAL, MOE_QUANT_TOKEN,
     STAGE_COMBINE, STAGE_DISPATCH, STAGE_FFN,
     STAGE_FORWARD, STAGE_GATE, MoEError, alloc_workspace, make_shape, moe_combine, moe_dispatch,
     moe_forward, moe_forward_kernel_count, moe_forward_kernel_name, moe_forward_traced,

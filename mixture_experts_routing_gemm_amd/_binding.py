@@ -41,34 +41,38 @@ class moe_shape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("S", ctypes.c_int32), ("h", ctypes.c_int32),
                 ("act", ctypes.c_int32), ("dispatch", ctypes.c_int32),
-                ("capacity", ctypes.c_int32), ("overflow", ctypes.c_int32)]
+                ("capacity", ctypes.c_int32), ("overflow", ctypes.c_int32),
+                ("quant", ctypes.c_int32)]
 
     def __repr__(self):
         return (f"moe_shape(T={self.T}, d={self.d}, E={self.E}, k={self.k}, S={self.S}, "
                 f"h={self.h}, act={self.act}, dispatch={self.dispatch}, capacity={self.capacity}, "
-                f"overflow={self.overflow})")
+                f"overflow={self.overflow}, quant={self.quant})")
 
 
 MOE_OVERFLOW_DROP, MOE_OVERFLOW_REASSIGN = 0, 1
+MOE_QUANT_TOKEN, MOE_QUANT_EXPERT, MOE_QUANT_GLOBAL = 0, 1, 2
+_QUANT = {"token": MOE_QUANT_TOKEN, "expert": MOE_QUANT_EXPERT, "global": MOE_QUANT_GLOBAL}
 
 
 def make_shape(T, d, E, k, S, h, act="bf16", dispatch=None, capacity=0,
-               reassign=False) -> moe_shape:
+               reassign=False, quant="token") -> moe_shape:
     a = _DTYPES[act] if isinstance(act, str) else int(act)
     if dispatch is None or dispatch == "act":
         dsp = a
     else:
         dsp = _DTYPES[dispatch] if isinstance(dispatch, str) else int(dispatch)
+    q = _QUANT[quant] if isinstance(quant, str) else int(quant)
     return moe_shape(int(T), int(d), int(E), int(k), int(S), int(h), a, dsp, int(capacity),
-                     MOE_OVERFLOW_REASSIGN if reassign else MOE_OVERFLOW_DROP)
+                     MOE_OVERFLOW_REASSIGN if reassign else MOE_OVERFLOW_DROP, q)
 
 
 def shape_of(cfg) -> moe_shape:
     """moe_shape from a workload config (fields T, d, E, k, S, h, act, dispatch,
-    and capacity / reassign if the config has them)."""
+    and capacity / reassign / quant if the config has them)."""
     return make_shape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.S, cfg.h, cfg.act,
                       "fp8" if cfg.dispatch == "fp8" else None, getattr(cfg, "capacity", 0),
-                      getattr(cfg, "reassign", False))
+                      getattr(cfg, "reassign", False), getattr(cfg, "quant", "token"))
 
 
 def _load():

@@ -177,12 +177,16 @@ __device__ void water_fill_loads(const int* n, int* load, int E, int cap) {
 __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
     const int32_t* __restrict__ blk, int32_t* __restrict__ pre, int nblk, int E, int cap,
     int reassign, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ first_loads) {
+    int32_t* __restrict__ first_loads, uint32_t* __restrict__ qstats) {
     __shared__ int part[kScanThreads];  // [P][E] partial sums
     __shared__ int raw[kMaxE];
     __shared__ int tot[kMaxE];
     __shared__ int off[kMaxE + 1];
     const int tid = threadIdx.x;
+    if (qstats != nullptr && tid <= E) {  // empty (min, max) ranges for the fp8 group modes
+        qstats[2 * tid] = 0xffffffffu;
+        qstats[2 * tid + 1] = 0u;
+    }
     const int P = kScanThreads / E;  // parts of the block range per expert
     const int e = tid % E, p = tid / E;
     const bool active = p < P;
@@ -489,17 +493,153 @@ __global__ __launch_bounds__(256) void dispatch_permute_fp8_kernel(
     }
 }
 
+// ------------------------------------------- fp8 per-expert / global ranges --
+// The quantiser's per-expert and global modes ("Deepseek-MoE同步税本质与四层实战
+// 优化指南", gsyq.cn, section 5.2, beside the per-token mode of section 3.1):
+// the same affine min/max map, with the range taken over all rows dispatched
+// to an expert (its final rows, after any capacity limit) or over the whole
+// batch. A float's order is kept by an unsigned key, so ranges merge with
+// integer atomics.
+__device__ __forceinline__ uint32_t order_key(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// expert whose row range holds `row` (offsets non-decreasing, row < offsets[E])
+__device__ __forceinline__ int expert_of_row(const int32_t* __restrict__ offsets, int E, int row) {
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (offsets[mid] <= row) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+constexpr int kStatsTokensPerWave = 16;
+
+// Places every slot (dest_row, src_token, as the permute does) and merges
+// each token's row min/max into its experts' ranges (qstats[2e], [2e+1]) or
+// into the batch's (qstats[2E], [2E+1]); a block reduces in LDS first and
+// then makes one pair of atomics per range it touched.
+__global__ __launch_bounds__(256) void dispatch_fp8_stats_kernel(
+    const bf16_t* __restrict__ x, const int32_t* __restrict__ topk_idx,
+    const int32_t* __restrict__ rank, const int32_t* __restrict__ pre,
+    const int32_t* __restrict__ offsets, int cap, int reassign, int global, int64_t T, int E,
+    int k, int d, int32_t* __restrict__ dest_row, int32_t* __restrict__ src_token,
+    uint32_t* __restrict__ qstats) {
+    __shared__ uint32_t smin[kMaxE + 1], smax[kMaxE + 1];
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    for (int g = tid; g <= E; g += 256) {
+        smin[g] = 0xffffffffu;
+        smax[g] = 0u;
+    }
+    __syncthreads();
+    const int64_t tbase = (static_cast<int64_t>(blockIdx.x) * 4 + w) * kStatsTokensPerWave;
+    for (int i = 0; i < kStatsTokensPerWave; ++i) {
+        const int64_t t = tbase + i;
+        if (t >= T) break;
+        const int dst = token_dest(topk_idx, rank, pre, offsets, cap, reassign, t, E, k, lane,
+                                   dest_row, src_token);
+        const uint8_t* src = reinterpret_cast<const uint8_t*>(x + t * d);
+        float mn = __builtin_inff(), mx = -__builtin_inff();
+        for (int c = lane; c < (d >> 3); c += kWave) {
+            const u32x4 a = load16(src + (static_cast<int64_t>(c) << 4));
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                mn = fminf(mn, fminf(bf16_lo(a[u]), bf16_hi(a[u])));
+                mx = fmaxf(mx, fmaxf(bf16_lo(a[u]), bf16_hi(a[u])));
+            }
+        }
+        mn = wave_min(mn);
+        mx = wave_max(mx);
+        if (global) {
+            if (lane == 0) {
+                atomicMin(&smin[E], order_key(mn));
+                atomicMax(&smax[E], order_key(mx));
+            }
+        } else if (lane < k && dst >= 0) {
+            const int g = expert_of_row(offsets, E, dst);
+            atomicMin(&smin[g], order_key(mn));
+            atomicMax(&smax[g], order_key(mx));
+        }
+    }
+    __syncthreads();
+    for (int g = tid; g <= E; g += 256) {
+        if (smin[g] != 0xffffffffu) {
+            atomicMin(&qstats[2 * g], smin[g]);
+            atomicMax(&qstats[2 * g + 1], smax[g]);
+        }
+    }
+}
+
+// Writes each dispatched copy of a row as e4m3 codes of its range's affine
+// map (the per-token kernel's arithmetic with the group's min/max), with
+// (scale, centre) per row. dest_row comes from the stats kernel.
+__global__ __launch_bounds__(256) void dispatch_permute_fp8_group_kernel(
+    const bf16_t* __restrict__ x, const int32_t* __restrict__ dest_row,
+    const int32_t* __restrict__ offsets, const uint32_t* __restrict__ qstats, int global,
+    int64_t T, int E, int k, int d, uint8_t* __restrict__ x_perm, float* __restrict__ qparams) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + w;
+    if (t >= T) return;
+    int dst = -1;
+    float centre = 0.0f, inv = 0.0f;
+    bool flat = true;
+    if (lane < k) {
+        dst = dest_row[t * k + lane];
+        if (dst >= 0) {
+            const int g = global ? E : expert_of_row(offsets, E, dst);
+            const float mn = key_value(qstats[2 * g]), mx = key_value(qstats[2 * g + 1]);
+            centre = 0.5f * (mx + mn);
+            const float half = 0.5f * (mx - mn);
+            flat = half == 0.0f;
+            inv = flat ? 0.0f : 448.0f / half;
+            qparams[2 * static_cast<int64_t>(dst)] = flat ? 0.0f : half / 448.0f;
+            qparams[2 * static_cast<int64_t>(dst) + 1] = centre;
+        }
+    }
+    int dj[kMaxK];
+    float cj[kMaxK], ij[kMaxK];
+    bool fj[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+        dj[j] = __shfl(dst, j, kWave);
+        cj[j] = __shfl(centre, j, kWave);
+        ij[j] = __shfl(inv, j, kWave);
+        fj[j] = __shfl(flat ? 1 : 0, j, kWave) != 0;
+    }
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(x + t * d);
+    const int ngroups = d >> 4;
+    for (int g = lane; g < ngroups; g += kWave) {
+        const u32x4 a = load16(src + (static_cast<int64_t>(g) << 5));
+        const u32x4 b = load16(src + (static_cast<int64_t>(g) << 5) + 16);
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j) {
+            if (j < k && dj[j] >= 0)
+                store16(x_perm + static_cast<int64_t>(dj[j]) * d + (static_cast<int64_t>(g) << 4),
+                        quant16(a, b, cj[j], ij[j], fj[j]));
+        }
+    }
+}
+
 hipError_t launch_dispatch(const moe_shape& s, const void* x, const int32_t* topk_idx,
                            int32_t* counts, int32_t* offsets, int32_t* dest_row,
                            int32_t* src_token, void* x_perm, float* qparams, int32_t* rank,
-                           int32_t* blk, int32_t* pre, int32_t* first_loads, uint32_t* hdr,
-                           hipStream_t st, const Marks* mk) {
+                           int32_t* blk, int32_t* pre, int32_t* first_loads, uint32_t* qstats,
+                           uint32_t* hdr, hipStream_t st, const Marks* mk) {
     const int nblk = static_cast<int>((s.T + kRankBlockTokens - 1) / kRankBlockTokens);
     const int reassign = s.capacity > 0 && s.overflow == MOE_OVERFLOW_REASSIGN ? 1 : 0;
     dispatch_rank_kernel<<<nblk, kRankThreads, 0, st>>>(topk_idx, s.T, s.E, s.k, rank, blk, hdr);
     mark(mk);
+    const bool fp8 = s.dispatch == MOE_FP8_E4M3;
+    const bool group = fp8 && s.quant != MOE_QUANT_TOKEN;
     dispatch_scan_kernel<<<1, kScanThreads, 0, st>>>(blk, pre, nblk, s.E, s.capacity, reassign,
-                                                     counts, offsets, first_loads);
+                                                     counts, offsets, first_loads,
+                                                     group ? qstats : nullptr);
     mark(mk);
     // (its time is counted with the permute's in a traced forward)
     if (reassign)
@@ -507,7 +647,18 @@ hipError_t launch_dispatch(const moe_shape& s, const void* x, const int32_t* top
                                                                 first_loads, s.T, s.E, s.k,
                                                                 s.capacity, dest_row, src_token);
     const unsigned pblocks = static_cast<unsigned>((s.T + 3) / 4);
-    if (s.dispatch == MOE_FP8_E4M3) {
+    if (group) {
+        // (the stats kernel's time is counted with the permute's in a traced forward)
+        const int global = s.quant == MOE_QUANT_GLOBAL ? 1 : 0;
+        const unsigned sblocks =
+            static_cast<unsigned>((s.T + 4 * kStatsTokensPerWave - 1) / (4 * kStatsTokensPerWave));
+        dispatch_fp8_stats_kernel<<<sblocks, 256, 0, st>>>(
+            static_cast<const bf16_t*>(x), topk_idx, rank, pre, offsets, s.capacity, reassign,
+            global, s.T, s.E, s.k, s.d, dest_row, src_token, qstats);
+        dispatch_permute_fp8_group_kernel<<<pblocks, 256, 0, st>>>(
+            static_cast<const bf16_t*>(x), dest_row, offsets, qstats, global, s.T, s.E, s.k, s.d,
+            static_cast<uint8_t*>(x_perm), qparams);
+    } else if (fp8) {
         dispatch_permute_fp8_kernel<<<pblocks, 256, 0, st>>>(
             static_cast<const bf16_t*>(x), topk_idx, rank, pre, offsets, s.capacity, reassign, s.T,
             s.E, s.k, s.d, dest_row, src_token, static_cast<uint8_t*>(x_perm), qparams);

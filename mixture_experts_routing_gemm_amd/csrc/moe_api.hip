@@ -15,8 +15,8 @@ hipError_t launch_gate_topk(const moe_shape& s, const void* x, const void* wg, c
 hipError_t launch_dispatch(const moe_shape& s, const void* x, const int32_t* topk_idx,
                            int32_t* counts, int32_t* offsets, int32_t* dest_row,
                            int32_t* src_token, void* x_perm, float* qparams, int32_t* rank,
-                           int32_t* blk, int32_t* pre, int32_t* first_loads, uint32_t* hdr,
-                           hipStream_t st, const Marks* mk);
+                           int32_t* blk, int32_t* pre, int32_t* first_loads, uint32_t* qstats,
+                           uint32_t* hdr, hipStream_t st, const Marks* mk);
 hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const float* qparams,
                               const int32_t* offsets, const void* x, const void* w1,
                               const void* w3, const void* w2, void* y_perm, void* y_shared,
@@ -42,7 +42,7 @@ size_t act_bytes(int32_t dt) { return dt == MOE_F32 ? 4 : (dt == MOE_BF16 ? 2 : 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct Layout {
-    size_t rank = 0, blk = 0, pre = 0, loads = 0, plan = 0, x_perm = 0, qparams = 0, h_r = 0, h_s = 0, y_perm = 0,
+    size_t rank = 0, blk = 0, pre = 0, loads = 0, qstats = 0, plan = 0, x_perm = 0, qparams = 0, h_r = 0, h_s = 0, y_perm = 0,
            y_sh = 0, total = 0;
 };
 
@@ -64,6 +64,7 @@ Layout layout(const moe_shape& s, int stage) {
         L.blk = take(nblk * E * 4);
         L.pre = take(nblk * E * 4);
         L.loads = take(E * 4);  // first-pass loads under a capacity limit
+        L.qstats = take((E + 1) * 8);  // fp8 (min, max) ranges of the group modes
     }
     if (ffn) {
         // m-tile prefix, tile counters and tile descriptors
@@ -85,7 +86,9 @@ Layout layout(const moe_shape& s, int stage) {
 int32_t check_shape(const moe_shape* s, bool ffn) {
     if (s == nullptr) return MOE_ERR_INVALID_ARG;
     if (s->T < 0 || s->d <= 0 || s->E <= 0 || s->k <= 0 || s->S < 0 || s->h <= 0 || s->k > s->E ||
-        s->capacity < 0 || (s->overflow != MOE_OVERFLOW_DROP && s->overflow != MOE_OVERFLOW_REASSIGN))
+        s->capacity < 0 || (s->overflow != MOE_OVERFLOW_DROP && s->overflow != MOE_OVERFLOW_REASSIGN) ||
+        s->quant < MOE_QUANT_TOKEN || s->quant > MOE_QUANT_GLOBAL ||
+        (s->quant != MOE_QUANT_TOKEN && s->dispatch != MOE_FP8_E4M3))
         return MOE_ERR_INVALID_ARG;
     if (s->E > kMaxE || s->k > kMaxK || s->S > kMaxS) return MOE_ERR_UNSUPPORTED;
     if (s->act != MOE_F32 && s->act != MOE_BF16) return MOE_ERR_UNSUPPORTED;
@@ -156,7 +159,7 @@ int32_t forward_impl(const moe_shape* s, const void* x, const void* w_gate, cons
     MOE_TRY(hip_status(launch_dispatch(*s, x, topk_idx, counts, offsets, dest_row, src_token,
                                        x_perm, qp, at<int32_t>(ws, L.rank),
                                        at<int32_t>(ws, L.blk), at<int32_t>(ws, L.pre),
-                                       at<int32_t>(ws, L.loads),
+                                       at<int32_t>(ws, L.loads), at<uint32_t>(ws, L.qstats),
                                        at<uint32_t>(ws, 0), st, mk)));
     void* y_perm = at<void>(ws, L.y_perm);
     void* y_sh = s->S > 0 ? at<void>(ws, L.y_sh) : nullptr;
@@ -226,7 +229,7 @@ int32_t moe_dispatch(const moe_shape* s, const void* x, const int32_t* topk_idx,
     return hip_status(launch_dispatch(*s, x, topk_idx, counts, offsets, dest_row, src_token,
                                       x_perm, qparams, at<int32_t>(ws, L.rank),
                                       at<int32_t>(ws, L.blk), at<int32_t>(ws, L.pre),
-                                      at<int32_t>(ws, L.loads),
+                                      at<int32_t>(ws, L.loads), at<uint32_t>(ws, L.qstats),
                                       at<uint32_t>(ws, 0), static_cast<hipStream_t>(stream),
                                       nullptr));
 }

@@ -62,6 +62,9 @@ class MoEConfig:
     # expert
     capacity: int = 0
     reassign: bool = False
+    # fp8 rows: the rows whose min/max range a row is mapped from ("token",
+    # "expert" or "global")
+    quant: str = "token"
     # relative-L2 bound on the layer output y
     tol_y: float = 2e-2
 

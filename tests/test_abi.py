@@ -64,14 +64,16 @@ FAKE = 0x100000  # an aligned, never-dereferenced address: every call below fail
     (dict(E=300), -2), (dict(k=9, E=16), -2), (dict(k=5, E=4), -1), (dict(T=-1), -1),
     (dict(S=9), -2), (dict(d=100), -2), (dict(h=100), -2), (dict(act=2), -2),
     (dict(dispatch=2, act=0), -2), (dict(d=0), -1), (dict(capacity=-1), -1),
-    (dict(capacity=4, overflow=2), -1),
+    (dict(capacity=4, overflow=2), -1), (dict(quant=1), -1), (dict(quant=3, dispatch=2), -1),
 ])
 def test_forward_rejects_bad_shapes(mm, kw, status):
-    base = dict(T=64, d=256, E=8, k=2, S=1, h=128, act=1, dispatch=None, capacity=0, overflow=0)
+    base = dict(T=64, d=256, E=8, k=2, S=1, h=128, act=1, dispatch=None, capacity=0, overflow=0,
+                quant=0)
     base.update(kw)
     s = mm.make_shape(base["T"], base["d"], base["E"], base["k"], base["S"], base["h"],
                       base["act"], base["dispatch"], base["capacity"])
     s.overflow = base["overflow"]
+    s.quant = base["quant"]
     p = ctypes.c_void_p(FAKE)
     rc = _raw(mm).moe_forward(ctypes.byref(s), p, p, None, p, p, p, p, p, p, p, p, p, p, p,
                               1 << 40, None)
