@@ -2,7 +2,13 @@
 combine) on one MI355X, through the C ABI.
 
     python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
+                    [--capacity-factor F [--reassign]] [--quant token|expert|global]
     python bench.py --copy-probe-mib N    # counter calibration, see below
+
+--capacity-factor F caps every routed expert at ceil(F * T*k / E) rows
+(overflow dropped, or with --reassign handed to the least-loaded expert);
+--quant picks the fp8 rows' range (fp8 workloads only). Both change the
+workload, and config names them.
 
 Prints ONE JSON line. `value` is routed tokens/s (T / time per layer forward)
 with every input already resident in HBM. Per-kernel durations come from HIP
@@ -39,23 +45,29 @@ BF16_PEAK_TFLOPS = 2500.0
 F32_VEC_PEAK_TFLOPS = 157.3
 
 
-def algorithmic(cfg):
-    """Algorithmic bytes / FLOPs of each stage for one layer forward."""
+def algorithmic(cfg, routed=None):
+    """Algorithmic bytes / FLOPs of each stage for one layer forward.
+
+    routed: the dispatched rows (T*k unless a capacity limit dropped some).
+    The fp8 per-expert and global modes read x once more for the ranges.
+    """
     T, d, E, k, S, h = cfg.T, cfg.d, cfg.E, cfg.k, cfg.S, cfg.h
+    R = T * k if routed is None else routed
     b = 4 if cfg.act == "f32" else 2
     bp = 1 if cfg.dispatch == "fp8" else b
-    rows = T * k + S * T
+    rows = R + S * T
+    xreads = 2 if getattr(cfg, "quant", "token") != "token" else 1
     return {
         "gate_bytes": T * d * b + E * d * b + 8 * T * k,
         "gate_flops": 2 * T * d * E,
-        "dispatch_bytes": T * d * b + T * k * d * bp + 8 * T * k + 4 * T * k
-        + (8 * T * k if cfg.dispatch == "fp8" else 0),
+        "dispatch_bytes": xreads * T * d * b + R * d * bp + 8 * T * k + 4 * T * k
+        + (8 * R if cfg.dispatch == "fp8" else 0),
         "ffn_up_flops": 4 * rows * d * h,
         # token rows in, both weight matrices of every group, hidden rows out
-        "ffn_up_bytes": T * k * d * bp + S * T * d * b + (E + S) * 2 * h * d * b + rows * h * b
-        + (8 * T * k if cfg.dispatch == "fp8" else 0),
+        "ffn_up_bytes": R * d * bp + S * T * d * b + (E + S) * 2 * h * d * b + rows * h * b
+        + (8 * R if cfg.dispatch == "fp8" else 0),
         "ffn_down_flops": 2 * rows * d * h,
-        "combine_bytes": T * k * d * b + (T * d * b if S else 0) + 8 * T * k + T * d * b,
+        "combine_bytes": R * d * b + (T * d * b if S else 0) + 8 * T * k + T * d * b,
     }
 
 
@@ -118,6 +130,9 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=96)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0)
+    ap.add_argument("--capacity-factor", type=float, default=0.0)
+    ap.add_argument("--reassign", action="store_true")
+    ap.add_argument("--quant", default="token", choices=["token", "expert", "global"])
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the tokens on one GPU; "
@@ -132,7 +147,16 @@ def main():
     import mixture_experts_routing_gemm_amd as mm
     from moe_workloads import CONFIGS, make_inputs
 
+    import dataclasses
+    import math
     cfg = CONFIGS[args.config]
+    if args.capacity_factor > 0:
+        cap = math.ceil(args.capacity_factor * cfg.T * cfg.k / cfg.E)
+        cfg = dataclasses.replace(cfg, capacity=cap, reassign=args.reassign)
+    if args.quant != "token":
+        if cfg.dispatch != "fp8":
+            sys.exit("--quant needs a workload with fp8 dispatch")
+        cfg = dataclasses.replace(cfg, quant=args.quant)
     torch.cuda.set_device(0)
     print(f"[bench] generating {cfg.name}", file=sys.stderr, flush=True)
     inp = make_inputs(cfg)
@@ -180,7 +204,8 @@ def main():
     kmean = dict(zip(names, per_kernel.mean(axis=0).tolist()))
     ms_per_step = wall * 1000.0 / args.steps
 
-    A = algorithmic(cfg)
+    routed = int(buf.offsets[-1].item())
+    A = algorithmic(cfg, routed)
     t_gate = kmean["gate_topk"]
     t_disp = sum(v for n, v in kmean.items() if n.startswith("dispatch"))
     t_up, t_down = kmean["ffn_up"], kmean["ffn_down"]
@@ -204,6 +229,7 @@ def main():
         "combine_GBps": round(A["combine_bytes"] / (t_comb * 1e-3) / 1e9, 1),
         "combine_hbm_frac": round(A["combine_bytes"] / (t_comb * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "routed_assignments_per_s": round(cfg.T * cfg.k / (ms_per_step * 1e-3), 1),
+        "dispatched_rows": routed,
     }
     out = {
         "metric": METRIC,
@@ -219,7 +245,10 @@ def main():
         "dtype": cfg.act,
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k,
-                   "S": cfg.S, "h": cfg.h, "dispatch": cfg.dispatch},
+                   "S": cfg.S, "h": cfg.h, "dispatch": cfg.dispatch,
+                   **({"capacity": cfg.capacity, "overflow": "reassign" if cfg.reassign else "drop"}
+                      if cfg.capacity else {}),
+                   **({"quant": cfg.quant} if cfg.quant != "token" else {})},
         "roofline": {
             "kernel": "ffn_up",
             "bound": "mfma",
@@ -227,7 +256,9 @@ def main():
             "peak": gemm_peak,
             "unit": "TFLOP/s",
             "frac": round(up_tflops / gemm_peak, 4),
-            "traffic": measured_traffic("ffn_up", cfg.name),
+            # counters were taken on the plain workload only
+            "traffic": (measured_traffic("ffn_up", cfg.name)
+                        if not cfg.capacity and cfg.quant == "token" else None),
             "algorithmic_bytes": A["ffn_up_bytes"],
         },
         "detail": detail,
