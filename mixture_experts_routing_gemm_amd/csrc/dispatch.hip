@@ -248,7 +248,9 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
 // the (o - N(v))-th expert in id order among those with L_e <= v, as that
 // expert's row v; with o >= N(cap) it is dropped. With the first-pass loads
 // sorted ascending (s_i) and P_i their prefix sums, N(s_i) = i*s_i - P_i and
-// each level in [s_i, s_{i+1}) holds i+1 overflows.
+// each level in [s_i, s_{i+1}) holds i+1 overflows, those of the experts at
+// sorted positions 0..i; a 256-bit mask of their ids per i turns "the p-th
+// in id order" into a select of the p-th set bit.
 __global__ __launch_bounds__(kRankThreads) void dispatch_overflow_kernel(
     const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ rank,
     const int32_t* __restrict__ pre, const int32_t* __restrict__ offsets,
@@ -256,6 +258,8 @@ __global__ __launch_bounds__(kRankThreads) void dispatch_overflow_kernel(
     int32_t* __restrict__ dest_row, int32_t* __restrict__ src_token) {
     __shared__ int Ls[kMaxE];
     __shared__ int sl[kMaxE];
+    __shared__ int sid[kMaxE];                 // expert id at each sorted position
+    __shared__ unsigned long long msk[kMaxE][kMaxE / 64];  // ids at sorted positions 0..i
     __shared__ long long Bk[kMaxE + 1];  // N at each sorted load; Bk[E] = N(cap)
     __shared__ long long wred[4];
     __shared__ int wtot[4];
@@ -269,12 +273,20 @@ __global__ __launch_bounds__(kRankThreads) void dispatch_overflow_kernel(
         int pos = 0;
         for (int q = 0; q < E; ++q) pos += (Ls[q] < Ls[e] || (Ls[q] == Ls[e] && q < e)) ? 1 : 0;
         sl[pos] = Ls[e];
+        sid[pos] = e;
         ob += max(0, pre[static_cast<int64_t>(b) * E + e] - cap);
     }
     ob = wave_sum64(ob);
     if (lane == 0) wred[w] = ob;
     __syncthreads();
     ob = wred[0] + wred[1] + wred[2] + wred[3];
+    if (w == 1 && lane < kMaxE / 64) {  // prefix ORs of the sorted ids, one word per lane
+        unsigned long long acc = 0ull;
+        for (int i = 0; i < E; ++i) {
+            if ((sid[i] >> 6) == lane) acc |= 1ull << (sid[i] & 63);
+            msk[i][lane] = acc;
+        }
+    }
     if (w == 0) {
         // prefix sums of the sorted loads, four entries per lane
         int v4[4], sum = 0;
@@ -327,12 +339,29 @@ __global__ __launch_bounds__(kRankThreads) void dispatch_overflow_kernel(
             const long long within = o - Bk[lo];
             const int v = sl[lo] + static_cast<int>(within / (lo + 1));
             int pth = static_cast<int>(within % (lo + 1));
-            int ee = 0;
-            for (; ee < E; ++ee) {
-                if (Ls[ee] <= v) {
-                    if (pth == 0) break;
-                    --pth;
+            // the pth set bit of the ids at sorted positions 0..lo
+            int ee = E;
+            for (int q = 0; q < kMaxE / 64; ++q) {
+                unsigned long long m = msk[lo][q];
+                const int c = __popcll(m);
+                if (pth >= c) {
+                    pth -= c;
+                    continue;
                 }
+                int base = 0;
+                for (int half = 32; half > 0; half >>= 1) {
+                    const unsigned long long low = m & ((1ull << half) - 1ull);
+                    const int cl = __popcll(low);
+                    if (pth >= cl) {
+                        pth -= cl;
+                        m >>= half;
+                        base += half;
+                    } else {
+                        m = low;
+                    }
+                }
+                ee = q * 64 + base;
+                break;
             }
             // the loads the scan kernel derived give expert ee more than v
             // rows; checked so that no row outside its range is written
@@ -519,7 +548,7 @@ __device__ __forceinline__ int expert_of_row(const int32_t* __restrict__ offsets
     return lo;
 }
 
-constexpr int kStatsTokensPerWave = 16;
+constexpr int kStatsTokensPerWave = 4;
 
 // Places every slot (dest_row, src_token, as the permute does) and merges
 // each token's row min/max into its experts' ranges (qstats[2e], [2e+1]) or
