@@ -29,6 +29,7 @@
 //            slot whose rank among its expert's assignments (token order)
 //            reaches C is dropped (dest_row = -1, no row) or takes the row
 //            the overflow kernel gave it.
+#include "ffn_plan.h"
 #include "moe_device.h"
 
 namespace moe {
@@ -238,6 +239,21 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
     }
 }
 
+// In a whole-layer forward the permute kernels' first fp.nblk work-groups
+// write the FFN's tile plan; returns the work-group's index among the
+// permute's own, or -1 for a plan work-group.
+__device__ __forceinline__ int permute_or_plan(const FfnPlanArgs& fp,
+                                               const int32_t* __restrict__ offsets, int E,
+                                               int64_t T) {
+    if (fp.plan == nullptr) return blockIdx.x;
+    if (static_cast<int>(blockIdx.x) < fp.nblk) {
+        ffn_plan_block(offsets, E, fp.S, T, fp.bm, fp.plan, fp.tiles, fp.n_up, fp.ntn_up,
+                       fp.ntn_down, fp.counters, blockIdx.x, fp.nblk);
+        return -1;
+    }
+    return blockIdx.x - fp.nblk;
+}
+
 // Capacity with reassignment: one block per rank block of 256 tokens, one
 // thread per token. An assignment overflows iff its rank g among its
 // expert's assignments (token order) is cap or more. Its overflow index o
@@ -412,9 +428,11 @@ __global__ __launch_bounds__(256) void dispatch_permute_kernel(
     const int32_t* __restrict__ offsets, int cap, int reassign, int64_t T, int E, int k,
     int row_bytes,
     int32_t* __restrict__ dest_row, int32_t* __restrict__ src_token,
-    uint8_t* __restrict__ x_perm) {
+    uint8_t* __restrict__ x_perm, FfnPlanArgs fp) {
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + w;
+    const int pb = permute_or_plan(fp, offsets, E, T);
+    if (pb < 0) return;
+    const int64_t t = static_cast<int64_t>(pb) * 4 + w;
     if (t >= T) return;
     const int dst =
         token_dest(topk_idx, rank, pre, offsets, cap, reassign, t, E, k, lane, dest_row,
@@ -474,9 +492,11 @@ __global__ __launch_bounds__(256) void dispatch_permute_fp8_kernel(
     const int32_t* __restrict__ rank, const int32_t* __restrict__ pre,
     const int32_t* __restrict__ offsets, int cap, int reassign, int64_t T, int E, int k, int d,
     int32_t* __restrict__ dest_row, int32_t* __restrict__ src_token,
-    uint8_t* __restrict__ x_perm, float* __restrict__ qparams) {
+    uint8_t* __restrict__ x_perm, float* __restrict__ qparams, FfnPlanArgs fp) {
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + w;
+    const int pb = permute_or_plan(fp, offsets, E, T);
+    if (pb < 0) return;
+    const int64_t t = static_cast<int64_t>(pb) * 4 + w;
     if (t >= T) return;
     const int dst =
         token_dest(topk_idx, rank, pre, offsets, cap, reassign, t, E, k, lane, dest_row,
@@ -611,9 +631,12 @@ __global__ __launch_bounds__(256) void dispatch_fp8_stats_kernel(
 __global__ __launch_bounds__(256) void dispatch_permute_fp8_group_kernel(
     const bf16_t* __restrict__ x, const int32_t* __restrict__ dest_row,
     const int32_t* __restrict__ offsets, const uint32_t* __restrict__ qstats, int global,
-    int64_t T, int E, int k, int d, uint8_t* __restrict__ x_perm, float* __restrict__ qparams) {
+    int64_t T, int E, int k, int d, uint8_t* __restrict__ x_perm, float* __restrict__ qparams,
+    FfnPlanArgs fp) {
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + w;
+    const int pb = permute_or_plan(fp, offsets, E, T);
+    if (pb < 0) return;
+    const int64_t t = static_cast<int64_t>(pb) * 4 + w;
     if (t >= T) return;
     int dst = -1;
     float centre = 0.0f, inv = 0.0f;
@@ -659,7 +682,8 @@ hipError_t launch_dispatch(const moe_shape& s, const void* x, const int32_t* top
                            int32_t* counts, int32_t* offsets, int32_t* dest_row,
                            int32_t* src_token, void* x_perm, float* qparams, int32_t* rank,
                            int32_t* blk, int32_t* pre, int32_t* first_loads, uint32_t* qstats,
-                           uint32_t* hdr, hipStream_t st, const Marks* mk) {
+                           uint32_t* hdr, const FfnPlanArgs& fp, hipStream_t st,
+                           const Marks* mk) {
     const int nblk = static_cast<int>((s.T + kRankBlockTokens - 1) / kRankBlockTokens);
     const int reassign = s.capacity > 0 && s.overflow == MOE_OVERFLOW_REASSIGN ? 1 : 0;
     dispatch_rank_kernel<<<nblk, kRankThreads, 0, st>>>(topk_idx, s.T, s.E, s.k, rank, blk, hdr);
@@ -675,7 +699,9 @@ hipError_t launch_dispatch(const moe_shape& s, const void* x, const int32_t* top
         dispatch_overflow_kernel<<<nblk, kRankThreads, 0, st>>>(topk_idx, rank, pre, offsets,
                                                                 first_loads, s.T, s.E, s.k,
                                                                 s.capacity, dest_row, src_token);
-    const unsigned pblocks = static_cast<unsigned>((s.T + 3) / 4);
+    // with a plan to write (whole-layer forward), its work-groups come first
+    const unsigned pblocks =
+        static_cast<unsigned>((s.T + 3) / 4) + (fp.plan != nullptr ? static_cast<unsigned>(fp.nblk) : 0u);
     if (group) {
         // (the stats kernel's time is counted with the permute's in a traced forward)
         const int global = s.quant == MOE_QUANT_GLOBAL ? 1 : 0;
@@ -686,16 +712,16 @@ hipError_t launch_dispatch(const moe_shape& s, const void* x, const int32_t* top
             global, s.T, s.E, s.k, s.d, dest_row, src_token, qstats);
         dispatch_permute_fp8_group_kernel<<<pblocks, 256, 0, st>>>(
             static_cast<const bf16_t*>(x), dest_row, offsets, qstats, global, s.T, s.E, s.k, s.d,
-            static_cast<uint8_t*>(x_perm), qparams);
+            static_cast<uint8_t*>(x_perm), qparams, fp);
     } else if (fp8) {
         dispatch_permute_fp8_kernel<<<pblocks, 256, 0, st>>>(
             static_cast<const bf16_t*>(x), topk_idx, rank, pre, offsets, s.capacity, reassign, s.T,
-            s.E, s.k, s.d, dest_row, src_token, static_cast<uint8_t*>(x_perm), qparams);
+            s.E, s.k, s.d, dest_row, src_token, static_cast<uint8_t*>(x_perm), qparams, fp);
     } else {
         const int row_bytes = s.d * (s.act == MOE_F32 ? 4 : 2);
         dispatch_permute_kernel<<<pblocks, 256, 0, st>>>(
             static_cast<const uint8_t*>(x), topk_idx, rank, pre, offsets, s.capacity, reassign, s.T,
-            s.E, s.k, row_bytes, dest_row, src_token, static_cast<uint8_t*>(x_perm));
+            s.E, s.k, row_bytes, dest_row, src_token, static_cast<uint8_t*>(x_perm), fp);
     }
     mark(mk);
     return hipGetLastError();

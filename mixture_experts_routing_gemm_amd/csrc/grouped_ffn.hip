@@ -22,6 +22,7 @@
 #include <algorithm>
 #include <type_traits>
 
+#include "ffn_plan.h"
 #include "moe_device.h"
 
 namespace moe {
@@ -33,151 +34,14 @@ constexpr int kFfnThreads = 256;
 constexpr int kLdsStage = (kBM + kBN) * kBK * 2;  // bytes per pipeline stage
 constexpr int kF32BM = 64, kF32BN = 64, kF32BK = 16;
 
-// plan[g] = number of m-tiles of groups before g (g = 0..E+S); routed group g
-// has ceil(n_g / bm) m-tiles and each shared group ceil(T / bm).
-//
-// With `tiles` set (the persistent kernels) it also writes one descriptor per
-// tile (m-tile x n-tile) for each projection and clears their tile counters:
-//   tiles[0 .. n_up)            up-projection: the S shared groups' tiles,
-//                               then the routed full m-tiles' group by group,
-//                               then the routed half m-tiles';
-//   tiles[n_up .. n_up+n_down)  down-projection: the shared tiles (one group
-//                               over the S concatenated hidden blocks, if
-//                               S > 0), then the routed ones, in the same
-//                               order;
-// sized for the bound on routed m-tiles. Within a group the tiles go in
-// supertiles (swz_tile). Every block computes the prefix sums; block 0
-// writes plan[] and the counters, and the blocks share out the tiles.
-// Words after the 16 tile counters: routed half and full m-tile counts.
-constexpr int kTileMetaHalf = 16, kTileMetaFull = 17;
-
-// Tiles go in supertiles of kSwzM x kSwzN within a group: n-blocks of kSwzN
-// n-tiles, within those m-blocks of kSwzM m-tiles, within a supertile
-// n-major. Tiles that follow each other in the list then share operand
-// panels (an m-tile's token rows, an n-tile's weight rows), so work-groups
-// that take them at about the same time find the panels in L2.
-constexpr int kSwzM = 4, kSwzN = 4;
-// tile j of an M x N grid in that order -> (m, nt)
-__device__ __forceinline__ void swz_tile(int M, int N, int j, int& m, int& nt) {
-    const int nb = j / (kSwzN * M);
-    const int w = min(kSwzN, N - nb * kSwzN);
-    const int r = j - nb * kSwzN * M;
-    const int mb = r / (kSwzM * w);
-    const int hgt = min(kSwzM, M - mb * kSwzM);
-    const int rr = r - mb * kSwzM * w;
-    nt = nb * kSwzN + rr / hgt;
-    m = mb * kSwzM + rr % hgt;
-}
-
-// out[0..n] = exclusive prefix sums of in[0..n) (out[n] = the total), by
-// one wave: each lane sums a run of consecutive entries, the runs' sums are
-// scanned across lanes. in and out may be the same LDS array.
-__device__ void wave_exclusive_scan(const int* in, int* out, int n) {
-    const int lane = threadIdx.x & 63;
-    const int per = (n + 63) / 64, b = min(n, lane * per), e = min(n, b + per);
-    int run = 0;
-    for (int i = b; i < e; ++i) run += in[i];
-    int incl = run;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += t;
-    }
-    int acc = incl - run;
-    for (int i = b; i < e; ++i) {
-        const int v = in[i];
-        out[i] = acc;
-        acc += v;
-    }
-    if (lane == 63) out[n] = incl;
-}
-
-// the last g in [0, n) with key[g] <= v (key non-decreasing, key[0] <= v)
-__device__ __forceinline__ int last_le(const int* key, int n, int v) {
-    int lo = 0, hi = n - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (key[mid] <= v) lo = mid;
-        else hi = mid - 1;
-    }
-    return lo;
-}
-
 __global__ __launch_bounds__(256) void ffn_plan_kernel(const int32_t* __restrict__ offsets,
                                                        int E, int S, int64_t T, int bm,
                                                        int32_t* __restrict__ plan,
                                                        int4* __restrict__ tiles, int n_up,
                                                        int ntn_up, int ntn_down,
                                                        int32_t* __restrict__ counters) {
-    __shared__ int off_s[kMaxE + 1];
-    __shared__ int mt[kMaxE + kMaxS];
-    __shared__ int pre[kMaxE + kMaxS + 1];
-    __shared__ int fpre[kMaxE + 1], hpre[kMaxE + 1];
-    const int G = E + S;
-    for (int g = threadIdx.x; g <= E; g += blockDim.x) off_s[g] = offsets[g];
-    __syncthreads();
-    for (int g = threadIdx.x; g < G; g += blockDim.x) {
-        const int64_t n = g < E ? static_cast<int64_t>(off_s[g + 1] - off_s[g]) : T;
-        mt[g] = static_cast<int>((n + bm - 1) / bm);
-    }
-    // a routed group's last m-tile holding at most bm/2 rows is a half
-    // tile; the persistent kernels schedule those after all full tiles
-    for (int g = threadIdx.x; g < E; g += blockDim.x) {
-        const int n = off_s[g + 1] - off_s[g];
-        hpre[g] = mt[g] > 0 && n - (mt[g] - 1) * bm <= bm / 2 ? 1 : 0;
-        fpre[g] = mt[g] - hpre[g];
-    }
-    __syncthreads();
-    // exclusive prefix sums, one wave each
-    const int wave = threadIdx.x >> 6;
-    if (wave == 0) wave_exclusive_scan(mt, pre, G);
-    if (wave == 1) wave_exclusive_scan(fpre, fpre, E);
-    if (wave == 2) wave_exclusive_scan(hpre, hpre, E);
-    __syncthreads();
-    if (blockIdx.x == 0) {
-        for (int g = threadIdx.x; g <= G; g += blockDim.x) plan[g] = pre[g];
-        if (tiles != nullptr) {
-            if (threadIdx.x == 0) {
-                counters[kTileMetaHalf] = hpre[E];
-                counters[kTileMetaFull] = fpre[E];
-            }
-            if (threadIdx.x < 16) counters[threadIdx.x] = 0;
-        }
-    }
-    if (tiles == nullptr) return;
-    const int mtT = static_cast<int>((T + bm - 1) / bm);
-    const int nT = static_cast<int>(T);
-    const int nfull = fpre[E], nhalf = hpre[E];
-    // one projection's list: the shared groups, the routed full m-tiles
-    // group by group, then the routed half m-tiles; every thread takes
-    // tiles in turn and finds its group by binary search
-    auto write_list = [&](int4* list, int ntn, bool down) {
-        const int nsg = down ? (S > 0 ? 1 : 0) : S;  // shared groups in this list
-        const int nsh = nsg * mtT * ntn;
-        const int i0 = blockIdx.x * blockDim.x + threadIdx.x, stride = gridDim.x * blockDim.x;
-        for (int i = i0; i < nsh; i += stride) {
-            const int q = i / (mtT * ntn);
-            int m, nt;
-            swz_tile(mtT, ntn, i - q * mtT * ntn, m, nt);
-            list[i] = make_int4((E + q) | (nt << 16), m * bm, 0, nT);
-        }
-        int4* routed = list + nsh;
-        for (int i = i0; i < nfull * ntn; i += stride) {
-            const int g = last_le(fpre, E, i / ntn);
-            const int j = i - fpre[g] * ntn;
-            int m, nt;
-            swz_tile(fpre[g + 1] - fpre[g], ntn, j, m, nt);
-            routed[i] = make_int4(g | (nt << 16), m * bm, off_s[g], off_s[g + 1] - off_s[g]);
-        }
-        for (int i = i0; i < nhalf * ntn; i += stride) {
-            const int g = last_le(hpre, E, i / ntn);
-            const int nt = i - hpre[g] * ntn;
-            routed[nfull * ntn + i] =
-                make_int4(g | (nt << 16), (mt[g] - 1) * bm, off_s[g], off_s[g + 1] - off_s[g]);
-        }
-    };
-    write_list(tiles, ntn_up, false);
-    write_list(tiles + n_up, ntn_down, true);
+    ffn_plan_block(offsets, E, S, T, bm, plan, tiles, n_up, ntn_up, ntn_down, counters,
+                   blockIdx.x, gridDim.x);
 }
 
 struct GemmArgs {
@@ -1162,31 +1026,58 @@ hipError_t launch_gemm(const GemmArgs& a, int64_t mtiles, bool big, hipStream_t 
     return hipGetLastError();
 }
 
-hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const float* qparams,
-                              const int32_t* offsets, const void* x, const void* w1,
-                              const void* w3, const void* w2, void* y_perm, void* y_shared,
-                              int32_t* plan, void* h_routed, void* h_shared, hipStream_t st,
-                              const Marks* mk) {
-    const bool f32 = s.act == MOE_F32;
-    // large tiles when both projections divide evenly into them (and K into
-    // whole groups of four slices)
+namespace {
+// work-groups of a plan of the persistent kernels: every one redoes the
+// prefix sums, the tile lists are shared out
+int plan_blocks(const PlanLayout& pl) {
+    return static_cast<int>(std::max<int64_t>(
+        1, std::min<int64_t>(64, (std::max(pl.n_up, pl.n_down) + 255) / 256)));
+}
+
+// large tiles when both projections divide evenly into them (and K into
+// whole groups of four slices)
+bool use_big_tiles(const moe_shape& s) {
     const uint64_t rows = static_cast<uint64_t>(s.T) * (s.k + s.S);
     const uint64_t wbytes = static_cast<uint64_t>(s.E + s.S) * s.d * s.h * 2;
     const bool fits32 = rows * s.d * 2 < (uint64_t(1) << 32) && rows * s.h * 2 < (uint64_t(1) << 32) &&
                         wbytes < (uint64_t(1) << 32);
-    const bool big = !f32 && fits32 && s.h % (kBigBN / 2) == 0 && s.d % kBigBN == 0 &&
-                     s.d % (4 * kBigBK) == 0 && s.h % (4 * kBigBK) == 0;
+    return s.act != MOE_F32 && fits32 && s.h % (kBigBN / 2) == 0 && s.d % kBigBN == 0 &&
+           s.d % (4 * kBigBK) == 0 && s.h % (4 * kBigBK) == 0;
+}
+}  // namespace
+
+bool ffn_fused_plan(const moe_shape& s, int32_t* plan, FfnPlanArgs* fp) {
+    fp->plan = nullptr;
+    if (!use_big_tiles(s)) return false;
+    const PlanLayout pl = plan_layout(s);
+    fp->plan = plan;
+    fp->counters = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(plan) + pl.counters);
+    fp->tiles = reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(plan) + pl.tiles);
+    fp->bm = kBigBM;
+    fp->n_up = pl.n_up;
+    fp->ntn_up = pl.ntn_up;
+    fp->ntn_down = pl.ntn_down;
+    fp->nblk = plan_blocks(pl);
+    fp->S = s.S;
+    return true;
+}
+
+hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const float* qparams,
+                              const int32_t* offsets, const void* x, const void* w1,
+                              const void* w3, const void* w2, void* y_perm, void* y_shared,
+                              int32_t* plan, void* h_routed, void* h_shared, bool plan_done,
+                              hipStream_t st, const Marks* mk) {
+    const bool f32 = s.act == MOE_F32;
+    const bool big = use_big_tiles(s);
     const int bm = f32 ? kF32BM : (big ? kBigBM : kBM);
     const PlanLayout pl = plan_layout(s);
     int32_t* counters = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(plan) + pl.counters);
     int4* tiles = reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(plan) + pl.tiles);
-    // every block redoes the prefix sums; the tile lists are shared out
-    const int plan_blocks = big ? static_cast<int>(std::min<int64_t>(
-                                      64, (std::max(pl.n_up, pl.n_down) + 255) / 256))
-                                : 1;
-    ffn_plan_kernel<<<std::max(plan_blocks, 1), 256, 0, st>>>(
-        offsets, s.E, s.S, s.T, bm, plan, big ? tiles : nullptr, pl.n_up, pl.ntn_up, pl.ntn_down,
-        counters);
+    // (plan_done: the dispatch permute of a whole-layer forward wrote it)
+    if (!plan_done)
+        ffn_plan_kernel<<<big ? plan_blocks(pl) : 1, 256, 0, st>>>(
+            offsets, s.E, s.S, s.T, bm, plan, big ? tiles : nullptr, pl.n_up, pl.ntn_up,
+            pl.ntn_down, counters);
     mark(mk);
 
     GemmArgs a;

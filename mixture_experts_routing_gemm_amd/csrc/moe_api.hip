@@ -6,6 +6,7 @@
 #include <cstdint>
 #include <cstring>
 
+#include "ffn_plan.h"
 #include "moe.h"
 #include "moe_device.h"
 
@@ -16,13 +17,15 @@ hipError_t launch_dispatch(const moe_shape& s, const void* x, const int32_t* top
                            int32_t* counts, int32_t* offsets, int32_t* dest_row,
                            int32_t* src_token, void* x_perm, float* qparams, int32_t* rank,
                            int32_t* blk, int32_t* pre, int32_t* first_loads, uint32_t* qstats,
-                           uint32_t* hdr, hipStream_t st, const Marks* mk);
+                           uint32_t* hdr, const FfnPlanArgs& fp, hipStream_t st,
+                           const Marks* mk);
 hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const float* qparams,
                               const int32_t* offsets, const void* x, const void* w1,
                               const void* w3, const void* w2, void* y_perm, void* y_shared,
-                              int32_t* plan, void* h_routed, void* h_shared, hipStream_t st,
-                              const Marks* mk);
+                              int32_t* plan, void* h_routed, void* h_shared, bool plan_done,
+                              hipStream_t st, const Marks* mk);
 size_t ffn_plan_bytes(const moe_shape& s);
+bool ffn_fused_plan(const moe_shape& s, int32_t* plan, FfnPlanArgs* fp);
 hipError_t launch_combine(const moe_shape& s, const void* y_perm, const void* y_sh,
                           const int32_t* dest_row, const float* topk_w, void* y, hipStream_t st);
 
@@ -156,16 +159,19 @@ int32_t forward_impl(const moe_shape* s, const void* x, const void* w_gate, cons
     const bool fp8 = s->dispatch == MOE_FP8_E4M3;
     void* x_perm = at<void>(ws, L.x_perm);
     float* qp = fp8 ? at<float>(ws, L.qparams) : nullptr;
+    // the FFN's tile plan is written by the dispatch permute's first work-groups
+    FfnPlanArgs fplan;
+    const bool plan_done = ffn_fused_plan(*s, at<int32_t>(ws, L.plan), &fplan);
     MOE_TRY(hip_status(launch_dispatch(*s, x, topk_idx, counts, offsets, dest_row, src_token,
                                        x_perm, qp, at<int32_t>(ws, L.rank),
                                        at<int32_t>(ws, L.blk), at<int32_t>(ws, L.pre),
                                        at<int32_t>(ws, L.loads), at<uint32_t>(ws, L.qstats),
-                                       at<uint32_t>(ws, 0), st, mk)));
+                                       at<uint32_t>(ws, 0), fplan, st, mk)));
     void* y_perm = at<void>(ws, L.y_perm);
     void* y_sh = s->S > 0 ? at<void>(ws, L.y_sh) : nullptr;
     MOE_TRY(hip_status(launch_grouped_ffn(*s, x_perm, qp, offsets, x, w1, w3, w2, y_perm, y_sh,
                                           at<int32_t>(ws, L.plan), at<void>(ws, L.h_r),
-                                          at<void>(ws, L.h_s), st, mk)));
+                                          at<void>(ws, L.h_s), plan_done, st, mk)));
     MOE_TRY(hip_status(launch_combine(*s, y_perm, y_sh, dest_row, topk_w, y, st)));
     mark(mk);
     return MOE_OK;
@@ -230,7 +236,8 @@ int32_t moe_dispatch(const moe_shape* s, const void* x, const int32_t* topk_idx,
                                       x_perm, qparams, at<int32_t>(ws, L.rank),
                                       at<int32_t>(ws, L.blk), at<int32_t>(ws, L.pre),
                                       at<int32_t>(ws, L.loads), at<uint32_t>(ws, L.qstats),
-                                      at<uint32_t>(ws, 0), static_cast<hipStream_t>(stream),
+                                      at<uint32_t>(ws, 0), FfnPlanArgs{nullptr, nullptr, nullptr, 0, 0, 0, 0, 0, 0},
+                                      static_cast<hipStream_t>(stream),
                                       nullptr));
 }
 
@@ -249,7 +256,7 @@ int32_t moe_grouped_ffn(const moe_shape* s, const void* x_perm, const float* qpa
     const Layout L = layout(*s, MOE_STAGE_FFN);
     return hip_status(launch_grouped_ffn(*s, x_perm, qparams, offsets, x, w1, w3, w2, y_perm,
                                          y_shared, at<int32_t>(ws, L.plan), at<void>(ws, L.h_r),
-                                         at<void>(ws, L.h_s), static_cast<hipStream_t>(stream),
+                                         at<void>(ws, L.h_s), false, static_cast<hipStream_t>(stream),
                                          nullptr));
 }
 
