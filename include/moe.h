@@ -222,7 +222,14 @@ int32_t moe_forward(const moe_shape *s, const void *x, const void *w_gate,
  * moe_forward that also records events[i] (hipEvent_t, created by the caller)
  * on the stream before the first kernel and after each kernel, for per-kernel
  * timing. n_events must be at least moe_forward_kernel_count(s) + 1; the
- * kernel names are given by moe_forward_kernel_name.
+ * kernel names are given by moe_forward_kernel_name. A NULL entry is not
+ * recorded (each recorded event adds a few microseconds to the pass, so a
+ * caller timing one kernel records only the two events around it). Some
+ * options run an extra kernel whose time falls in the next named interval:
+ * capacity reassignment (the overflow kernel, in the permute's) and the fp8
+ * per-expert / global modes (the range kernel, in the permute's); in a
+ * forward with the persistent GEMMs the FFN tile plan is written by the
+ * permute kernel, so the "ffn_plan" interval holds no kernel.
  */
 int32_t moe_forward_traced(const moe_shape *s, const void *x, const void *w_gate,
                            const float *bias, const void *w1, const void *w3,

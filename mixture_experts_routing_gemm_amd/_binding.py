@@ -205,9 +205,11 @@ def moe_forward(shape, x, w_gate, bias, w1, w3, w2, y, topk_idx, topk_w, counts,
 
 def moe_forward_traced(shape, x, w_gate, bias, w1, w3, w2, y, topk_idx, topk_w, counts, offsets,
                        dest_row, src_token, ws, events, stream=None):
-    """events: a sequence of raw hipEvent_t handles (ints)."""
+    """events: a sequence of raw hipEvent_t handles (ints), or None where no
+    event is to be recorded."""
     wp, wn = _ws(ws)
-    arr = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(int(e)) for e in events])
+    arr = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(None if e is None else int(e))
+                                            for e in events])
     _check(lib.moe_forward_traced(ctypes.byref(shape), _p(x), _p(w_gate), _p(bias), _p(w1),
                                   _p(w3), _p(w2), _p(y), _p(topk_idx), _p(topk_w), _p(counts),
                                   _p(offsets), _p(dest_row), _p(src_token), wp, wn, _s(stream),

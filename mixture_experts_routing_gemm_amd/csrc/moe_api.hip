@@ -284,8 +284,6 @@ int32_t moe_forward_traced(const moe_shape* s, const void* x, const void* w_gate
                            int32_t* offsets, int32_t* dest_row, int32_t* src_token, void* ws,
                            size_t ws_bytes, void* stream, void* const* events, int32_t n_events) {
     if (events == nullptr || n_events < moe_forward_kernel_count(s) + 1) return MOE_ERR_INVALID_ARG;
-    for (int i = 0; i < n_events; ++i)
-        if (events[i] == nullptr) return MOE_ERR_INVALID_ARG;
     Marks mk{reinterpret_cast<hipEvent_t const*>(events), n_events, 0,
              static_cast<hipStream_t>(stream)};
     return forward_impl(s, x, w_gate, bias, w1, w3, w2, y, topk_idx, topk_w, counts, offsets,

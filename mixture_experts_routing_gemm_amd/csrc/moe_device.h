@@ -81,7 +81,7 @@ __device__ __forceinline__ void set_error(uint32_t* hdr, uint32_t bit) {
 }
 
 // Host side: optional events recorded on the stream after each kernel, for
-// per-kernel timing of the whole-layer call.
+// per-kernel timing of the whole-layer call (a NULL entry is skipped).
 struct Marks {
     hipEvent_t const* events;
     int n;
@@ -89,8 +89,10 @@ struct Marks {
     hipStream_t st;
 };
 inline void mark(const Marks* mk) {
-    if (mk != nullptr && mk->events != nullptr && mk->next < mk->n)
-        (void)hipEventRecord(mk->events[mk->next++], mk->st);
+    if (mk != nullptr && mk->events != nullptr && mk->next < mk->n) {
+        hipEvent_t e = mk->events[mk->next++];
+        if (e != nullptr) (void)hipEventRecord(e, mk->st);
+    }
 }
 
 }  // namespace moe

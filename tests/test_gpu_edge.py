@@ -176,3 +176,28 @@ def test_zero_tokens():
     wg = torch.zeros((8, 128), dtype=torch.bfloat16, device="cuda")
     buf.run(x, wg, None, w, w, w2)
     torch.cuda.synchronize()
+
+
+def test_traced_forward_with_some_events_left_out():
+    # NULL entries are skipped; the output is the plain forward's
+    mm = _mm()
+    cfg = small_cfg(T=700, d=256, E=16, k=4, S=1, h=128)
+    inp = make_inputs(cfg, seed=9)
+    shape = mm.shape_of(cfg)
+    args = [dev(inp.x), dev(inp.wg), None, dev(inp.w1), dev(inp.w3), dev(inp.w2)]
+    plain = mm.ForwardBuffers(shape)
+    plain.run(*args)
+    nk = mm.moe_forward_kernel_count(shape)
+    names = [mm.moe_forward_kernel_name(shape, i) for i in range(nk)]
+    j = names.index("ffn_up")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)]
+    for e in ev:
+        e.record()  # torch creates the HIP event at its first record
+    torch.cuda.synchronize()
+    handles = [e.cuda_event if i in (j, j + 1) else None for i, e in enumerate(ev)]
+    assert all(h for h in handles if h is not None)
+    traced = mm.ForwardBuffers(shape)
+    traced.run(*args, events=handles)
+    torch.cuda.synchronize()
+    assert torch.equal(traced.y, plain.y) and torch.equal(traced.dest_row, plain.dest_row)
+    assert ev[j].elapsed_time(ev[j + 1]) > 0.0
