@@ -35,27 +35,74 @@ __device__ __forceinline__ bool ranks_before(float za, int ia, float zb, int ib)
     return za > zb || (za == zb && ia < ib);
 }
 
-// Top-k and weights of TT tokens whose logits sit in LDS (zs[r*zld + e]).
-// Expert e of token r is selected iff fewer than k experts rank before it
-// (larger logit, or equal logit and lower id), and that count is its slot;
-// every (token, expert) pair is one independent count. The weights are the
-// softmax over the k selected logits (slot 0 holds the largest), every slot
-// summing the same k terms in slot order. `sel` is LDS for TT*kMaxK logits
-// and TT*kMaxK ids. Called by all threads of the block.
+// Top-k and weights of TT tokens whose logits sit in LDS (zs[r*zld + e]),
+// under the order "larger logit first, then lower id" (ranks_before), which
+// is total, so the k experts that rank first, listed in that order, are
+// unique. Two ways to find them, by cost:
+//  - rank counting (small E): expert e of token r is selected iff fewer
+//    than k experts rank before it, and that count is its slot; every
+//    (token, expert) pair is one independent count, E*E*TT comparisons;
+//  - k argmax rounds (large E: E*E > 2560*k, where the counting's E*E
+//    reads outgrow about 40 dependent shuffle steps per round): one wave
+//    per token row, each lane keeps the best of its not yet taken experts
+//    (e = lane + 64*q), a butterfly of shuffles gives every lane the row's
+//    best, and its owner marks it taken; round p's winner is slot p.
+// The weights are the softmax over the k selected logits (slot 0 holds the
+// largest), every slot summing the same k terms in slot order. `sel` is LDS
+// for TT*kMaxK logits and TT*kMaxK ids. Called by all threads of the block.
 __device__ __forceinline__ void topk_rows(const float* zs, int zld, int TT, int E, int k,
                                           int64_t t0, int64_t T, float* sel,
                                           int32_t* __restrict__ topk_idx,
                                           float* __restrict__ topk_w) {
     float* sz = sel;                                        // [TT][kMaxK] selected logits
     int* si = reinterpret_cast<int*>(sz + TT * kMaxK);      // [TT][kMaxK] selected ids
-    for (int q = threadIdx.x; q < TT * E; q += blockDim.x) {
-        const int r = q / E, e = q - r * E;
-        const float z = zs[r * zld + e];
-        int rank = 0;
-        for (int e2 = 0; e2 < E; ++e2) rank += ranks_before(zs[r * zld + e2], e2, z, e) ? 1 : 0;
-        if (rank < k) {
-            sz[r * kMaxK + rank] = z;
-            si[r * kMaxK + rank] = e;
+    if (E * E <= 2560 * k) {
+        for (int q = threadIdx.x; q < TT * E; q += blockDim.x) {
+            const int r = q / E, e = q - r * E;
+            const float z = zs[r * zld + e];
+            int rank = 0;
+            for (int e2 = 0; e2 < E; ++e2) rank += ranks_before(zs[r * zld + e2], e2, z, e) ? 1 : 0;
+            if (rank < k) {
+                sz[r * kMaxK + rank] = z;
+                si[r * kMaxK + rank] = e;
+            }
+        }
+    }
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nwaves = blockDim.x >> 6;
+    constexpr int kPerLane = (kMaxE + 63) / 64;
+    for (int r = wave; r < TT && E * E > 2560 * k; r += nwaves) {
+        float z[kPerLane];
+#pragma unroll
+        for (int q = 0; q < kPerLane; ++q) {
+            const int e = lane + 64 * q;
+            z[q] = e < E ? zs[r * zld + e] : 0.0f;
+        }
+        unsigned taken = 0u;
+        for (int p = 0; p < k; ++p) {
+            float bz = -__builtin_inff();
+            int be = E;  // ranks after every real expert
+#pragma unroll
+            for (int q = 0; q < kPerLane; ++q) {
+                const int e = lane + 64 * q;
+                if (e < E && !((taken >> q) & 1u) && ranks_before(z[q], e, bz, be)) {
+                    bz = z[q];
+                    be = e;
+                }
+            }
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                const float oz = __shfl_xor(bz, o, 64);
+                const int oe = __shfl_xor(be, o, 64);
+                if (ranks_before(oz, oe, bz, be)) {
+                    bz = oz;
+                    be = oe;
+                }
+            }
+            if ((be & 63) == lane && be < E) taken |= 1u << (be >> 6);
+            if (lane == 0) {
+                sz[r * kMaxK + p] = bz;
+                si[r * kMaxK + p] = be;
+            }
         }
     }
     __syncthreads();

@@ -201,3 +201,23 @@ def test_traced_forward_with_some_events_left_out():
     torch.cuda.synchronize()
     assert torch.equal(traced.y, plain.y) and torch.equal(traced.dest_row, plain.dest_row)
     assert ev[j].elapsed_time(ev[j + 1]) > 0.0
+
+
+@pytest.mark.parametrize("E,k", [(16, 4), (128, 4), (200, 8)], ids=["E16", "E128", "E200"])
+def test_tied_logits_go_to_the_lower_id(E, k):
+    # gate rows duplicated in pairs: every logit appears twice, and the
+    # top-k must list the lower id of a tied pair first (bit-exact vs the
+    # oracle, whose tie rule is pinned on the CPU)
+    mm = _mm()
+    cfg = small_cfg(T=300, d=128, E=E, k=k, S=0, h=64)
+    inp = make_inputs(cfg, seed=11)
+    inp.wg[1::2] = inp.wg[0::2][: E // 2]
+    z = oracle.gate_logits(inp.x, inp.wg, None, nthreads=ORACLE_THREADS)
+    oidx, ow = oracle.select_topk(z, k)
+    assert np.any(z[:, 0] == z[:, 1])
+    idx = torch.empty((cfg.T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((cfg.T, k), dtype=torch.float32, device="cuda")
+    mm.moe_gate_topk(mm.shape_of(cfg), dev(inp.x), dev(inp.wg), None, idx, w, None)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(idx), oidx)
+    assert rel_l2(host(w), ow) <= 1e-5
