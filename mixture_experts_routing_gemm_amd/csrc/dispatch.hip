@@ -557,8 +557,9 @@ __device__ __forceinline__ float key_value(uint32_t k) {
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-// expert whose row range holds `row` (offsets non-decreasing, row < offsets[E])
-__device__ __forceinline__ int expert_of_row(const int32_t* __restrict__ offsets, int E, int row) {
+// expert whose row range holds `row` (offsets non-decreasing, row < offsets[E]);
+// `offsets` is the block's LDS copy
+__device__ __forceinline__ int expert_of_row(const int* offsets, int E, int row) {
     int lo = 0, hi = E - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -581,10 +582,12 @@ __global__ __launch_bounds__(256) void dispatch_fp8_stats_kernel(
     int k, int d, int32_t* __restrict__ dest_row, int32_t* __restrict__ src_token,
     uint32_t* __restrict__ qstats) {
     __shared__ uint32_t smin[kMaxE + 1], smax[kMaxE + 1];
+    __shared__ int off_s[kMaxE + 1];
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     for (int g = tid; g <= E; g += 256) {
         smin[g] = 0xffffffffu;
         smax[g] = 0u;
+        off_s[g] = offsets[g];
     }
     __syncthreads();
     const int64_t tbase = (static_cast<int64_t>(blockIdx.x) * 4 + w) * kStatsTokensPerWave;
@@ -611,7 +614,7 @@ __global__ __launch_bounds__(256) void dispatch_fp8_stats_kernel(
                 atomicMax(&smax[E], order_key(mx));
             }
         } else if (lane < k && dst >= 0) {
-            const int g = expert_of_row(offsets, E, dst);
+            const int g = expert_of_row(off_s, E, dst);
             atomicMin(&smin[g], order_key(mn));
             atomicMax(&smax[g], order_key(mx));
         }
@@ -636,6 +639,11 @@ __global__ __launch_bounds__(256) void dispatch_permute_fp8_group_kernel(
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int pb = permute_or_plan(fp, offsets, E, T);
     if (pb < 0) return;
+    __shared__ int off_s[kMaxE + 1];
+    if (!global) {
+        for (int g = threadIdx.x; g <= E; g += blockDim.x) off_s[g] = offsets[g];
+        __syncthreads();
+    }
     const int64_t t = static_cast<int64_t>(pb) * 4 + w;
     if (t >= T) return;
     int dst = -1;
@@ -644,7 +652,7 @@ __global__ __launch_bounds__(256) void dispatch_permute_fp8_group_kernel(
     if (lane < k) {
         dst = dest_row[t * k + lane];
         if (dst >= 0) {
-            const int g = global ? E : expert_of_row(offsets, E, dst);
+            const int g = global ? E : expert_of_row(off_s, E, dst);
             const float mn = key_value(qstats[2 * g]), mx = key_value(qstats[2 * g + 1]);
             centre = 0.5f * (mx + mn);
             const float half = 0.5f * (mx - mn);
