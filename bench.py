@@ -213,6 +213,9 @@ def main():
     wall = time.perf_counter() - t0
     assert mm.moe_get_device_error(buf.ws) == mm.MOE_OK
     up_ms_timed = float(np.mean([row[j_up].elapsed_time(row[j_up + 1]) for row in evs]))
+    # consecutive up-projection starts are one forward apart: the spread of
+    # the timed steps without further events
+    steps_ms = np.array([evs[i][j_up].elapsed_time(evs[i + 1][j_up]) for i in range(len(evs) - 1)])
 
     for i in range(n_tr):
         buf.run(x, wg, bias, w1, w3, w2, events=handles_tr[i])
@@ -236,6 +239,8 @@ def main():
         "kernel_ms_from": f"{n_tr} fully traced passes after the timed region (ffn_up: timed steps)",
         "ffn_up_ms_timed_steps": round(up_ms_timed, 5),
         "step_ms_events_median": round(float(np.median(step_ms)), 5),
+        "timed_step_ms_p10_median_p90": ([round(float(np.percentile(steps_ms, q)), 5) for q in (10, 50, 90)]
+                                         if len(steps_ms) else None),
         "gate_us": round(t_gate * 1e3, 2),
         "gate_tflops": round(A["gate_flops"] / (t_gate * 1e-3) / 1e12, 3),
         "dispatch_us": round(t_disp * 1e3, 2),
