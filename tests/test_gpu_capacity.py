@@ -149,3 +149,15 @@ def test_capacity_never_binding_equals_dropless():
         outs.append((host(buf.y).copy(), host(buf.dest_row).copy()))
     for y, dest in outs[1:]:
         assert np.array_equal(outs[0][0], y) and np.array_equal(outs[0][1], dest)
+
+
+def test_full_size_skewed_workload_reassigned_at_factor_1():
+    # zipf_stress_bf16 at its full size, as bench.py --capacity-factor 1.0
+    # --reassign times it: every dispatch array bit-exact, y on sampled tokens
+    base = CONFIGS["zipf_stress_bf16"]
+    cfg = dataclasses.replace(base, capacity=base.T * base.k // base.E, reassign=True)
+    inp = make_inputs(cfg)
+    rng = np.random.default_rng(1)
+    toks = np.unique(np.concatenate([rng.integers(0, cfg.T, 30), [0, cfg.T - 1]])).astype(np.int64)
+    buf, route = forward_vs_oracle(inp, toks)
+    assert np.all(host(buf.counts) == cfg.capacity)

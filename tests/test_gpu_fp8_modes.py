@@ -126,3 +126,52 @@ def test_fp8_expert_mode_at_larger_size():
 def test_token_mode_is_the_default_path():
     # quant = "token" must be the per-token kernel: same codes as before
     run_case(_cfg(quant="token", T=600))
+
+
+def test_full_size_fp8_workload_per_expert_ranges():
+    # fp8_dispatch at its full size with per-expert ranges, as bench.py
+    # --quant expert times it: the dispatch arrays bit-exact, the codes and
+    # (scale, centre) of sampled dispatched rows bit-exact, y on sampled tokens
+    mm = _mm()
+    cfg = dataclasses.replace(CONFIGS["fp8_dispatch"], quant="expert")
+    say(f"[fp8 modes] full size T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} quant=expert")
+    inp = make_inputs(cfg)
+    shape = mm.shape_of(cfg)
+    oidx, ow, _ = oracle.gate_topk(inp.x, inp.wg, cfg.k, None, nthreads=ORACLE_THREADS)
+    counts, offsets, dest, src = oracle.dispatch(oidx, cfg.E)
+    n = int(offsets[cfg.E])
+    xf = bf16_bits_to_f32(inp.x)
+    rr = group_ranges(xf, offsets, src, "expert")
+    T, E, k, d = cfg.T, cfg.E, cfg.k, cfg.d
+    g_counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    g_offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    g_dest = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    g_src = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    x_perm = torch.empty((T * k, d), dtype=torch.uint8, device="cuda")
+    qp = torch.empty((T * k, 2), dtype=torch.float32, device="cuda")
+    ws = mm.alloc_workspace(shape, mm.STAGE_DISPATCH)
+    xd = dev(inp.x)
+    mm.moe_dispatch(shape, xd, dev(oidx), g_counts, g_offsets, g_dest, g_src, x_perm, qp, ws)
+    assert mm.moe_get_device_error(ws) == mm.MOE_OK
+    assert np.array_equal(host(g_counts), counts)
+    assert np.array_equal(host(g_offsets), offsets)
+    assert np.array_equal(host(g_dest), dest)
+    assert np.array_equal(host(g_src)[:n], src[:n])
+    rng = np.random.default_rng(2)
+    rows = np.unique(np.concatenate([rng.integers(0, n, 3000), offsets[:-1][counts > 0],
+                                     offsets[1:][counts > 0] - 1]))
+    q_ref, qp_ref = oracle.fp8_quantize(inp.x[src[rows]], ranges=rr[rows])
+    assert np.array_equal(host(x_perm)[rows], q_ref)
+    assert np.array_equal(host(qp)[rows].view(np.uint32), qp_ref.view(np.uint32))
+    del x_perm, qp, ws
+    buf = mm.ForwardBuffers(shape)
+    buf.run(xd, dev(inp.wg), None, dev(inp.w1), dev(inp.w3), dev(inp.w2))
+    torch.cuda.synchronize()
+    assert mm.moe_get_device_error(buf.ws) == mm.MOE_OK
+    assert np.array_equal(host(buf.dest_row), dest)
+    toks = np.array([0, 1, 777, 16384, T - 1], dtype=np.int64)
+    qrange = np.stack([[rr[dest[t, j]] for j in range(k)] for t in toks]).astype(np.float32)
+    _, _, oy = oracle.layer_tokens(inp, toks, nthreads=ORACLE_THREADS, qrange=qrange)
+    err = rel_l2(host(buf.y)[toks], oy)
+    say(f"[fp8 modes] full size y rel-L2 {err:.3e}")
+    assert err <= cfg.tol_y
