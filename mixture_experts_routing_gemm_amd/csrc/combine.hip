@@ -72,30 +72,46 @@ __global__ __launch_bounds__(256) void combine_kernel(
         pj[j] = __shfl(p, j, kWave);
         wj[j] = __shfl(wt, j, kWave);
     }
+    // two chunks per lane per iteration: all of their loads are in flight
+    // before the first sum (the sums themselves are unchanged: per element,
+    // y_sh then w_j * row_j in slot order, rounded once)
     const int nchunk = d / V::N;
-    for (int c = lane; c < nchunk; c += kWave) {
-        const int64_t col = static_cast<int64_t>(c) * V::N;
-        u32x4 src[kMaxK];
+    for (int c0 = lane; c0 < nchunk; c0 += 2 * kWave) {
+        u32x4 src[2][kMaxK], sh[2];
 #pragma unroll
-        for (int j = 0; j < kMaxK; ++j)
-            if (j < k && pj[j] >= 0) src[j] = load16(y_perm + static_cast<int64_t>(pj[j]) * d + col);
-        float acc[V::N];
-        if (y_sh != nullptr) {
-            V::unpack(load16(y_sh + t * d + col), acc);
-        } else {
+        for (int h = 0; h < 2; ++h) {
+            const int c = c0 + h * kWave;
+            if (c >= nchunk) continue;
+            const int64_t col = static_cast<int64_t>(c) * V::N;
 #pragma unroll
-            for (int u = 0; u < V::N; ++u) acc[u] = 0.0f;
+            for (int j = 0; j < kMaxK; ++j)
+                if (j < k && pj[j] >= 0)
+                    src[h][j] = load16(y_perm + static_cast<int64_t>(pj[j]) * d + col);
+            if (y_sh != nullptr) sh[h] = load16(y_sh + t * d + col);
         }
 #pragma unroll
-        for (int j = 0; j < kMaxK; ++j) {
-            if (j < k && pj[j] >= 0) {
-                float v[V::N];
-                V::unpack(src[j], v);
+        for (int h = 0; h < 2; ++h) {
+            const int c = c0 + h * kWave;
+            if (c >= nchunk) continue;
+            const int64_t col = static_cast<int64_t>(c) * V::N;
+            float acc[V::N];
+            if (y_sh != nullptr) {
+                V::unpack(sh[h], acc);
+            } else {
 #pragma unroll
-                for (int u = 0; u < V::N; ++u) acc[u] = __builtin_fmaf(wj[j], v[u], acc[u]);
+                for (int u = 0; u < V::N; ++u) acc[u] = 0.0f;
             }
+#pragma unroll
+            for (int j = 0; j < kMaxK; ++j) {
+                if (j < k && pj[j] >= 0) {
+                    float v[V::N];
+                    V::unpack(src[h][j], v);
+#pragma unroll
+                    for (int u = 0; u < V::N; ++u) acc[u] = __builtin_fmaf(wj[j], v[u], acc[u]);
+                }
+            }
+            store16(y + t * d + col, V::pack(acc));
         }
-        store16(y + t * d + col, V::pack(acc));
     }
 }
 
