@@ -61,6 +61,8 @@ def lib():
         L.oracle_layer_tokens.argtypes = [i32, i32, i32, i32, i32, i32, i32, i64, vp, vp, vp,
                                           vp, vp, vp, vp, vp, vp, vp, vp, vp, i32]
         L.oracle_fp8_quantize_ranges.argtypes = [i64, i32, i32, vp, vp, vp, vp]
+        L.oracle_layer_backward.argtypes = [i32, i32, i32, i32, i32, i32, i32, i64, vp, vp, vp, vp,
+                                            vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.oracle_combine.argtypes = [i64, i32, i32, i32, vp, vp, vp, vp, i64, vp]
         L.oracle_bf16_to_float.argtypes = [ctypes.c_uint16]
         L.oracle_bf16_to_float.restype = ctypes.c_float
@@ -225,6 +227,29 @@ def layer_tokens(inp, tokens, nthreads=1, route=None, qrange=None):
                                      _p(inp.wg), _p(b), _p(inp.w1), _p(inp.w3), _p(inp.w2),
                                      _p(idx), _p(w), _p(y), _nthreads(nthreads)), "layer_tokens")
     return idx, w, y
+
+
+def layer_backward(inp, tokens, dy, route=None):
+    """Gradients of sum(dy * y) over the listed tokens (small sizes):
+    dict of dx [n,d], dtopk_w [n,k] and, summed over the tokens, dwg [E,d],
+    dw1 / dw3 [E+S,h,d], dw2 [E+S,d,h] -- all float64. The top-k choice is
+    held fixed, fp8 rows pass the gradient straight through, and route
+    (optional, -1 = dropped) gives each slot's expert as in layer_tokens."""
+    cfg = inp.cfg
+    tokens = np.ascontiguousarray(tokens, dtype=np.int64)
+    n, d, E, k, S, h = tokens.shape[0], cfg.d, cfg.E, cfg.k, cfg.S, cfg.h
+    dy = np.ascontiguousarray(dy, dtype=np.float64).reshape(n, d)
+    out = dict(dx=np.zeros((n, d)), dtopk_w=np.zeros((n, k)), dwg=np.zeros((E, d)),
+               dw1=np.zeros((E + S, h, d)), dw3=np.zeros((E + S, h, d)), dw2=np.zeros((E + S, d, h)))
+    b = None if inp.bias is None else np.ascontiguousarray(inp.bias, dtype=np.float32)
+    r = None if route is None else np.ascontiguousarray(route, dtype=np.int32).reshape(n, k)
+    _check(lib().oracle_layer_backward(d, E, k, S, h, _dtype_code(inp.x),
+                                       1 if cfg.dispatch == "fp8" else 0, n, _p(tokens), _p(r),
+                                       _p(inp.x), _p(inp.wg), _p(b), _p(inp.w1), _p(inp.w3),
+                                       _p(inp.w2), _p(dy), _p(out["dx"]), _p(out["dtopk_w"]),
+                                       _p(out["dwg"]), _p(out["dw1"]), _p(out["dw3"]),
+                                       _p(out["dw2"])), "layer_backward")
+    return out
 
 
 def combine(y_perm, y_shared, dest_row, topk_w):

@@ -575,3 +575,158 @@ int oracle_combine(int64_t T, int d, int k, int dtype, const void *y_perm,
     }
     return 0;
 }
+
+/* ------------------------------------------------------------ backward ---- */
+/*
+ * Backward of the layer over a list of tokens, for small sizes (every weight
+ * gradient is a dense float64 array). The pages describe the backward only
+ * as the forward's exchange run in reverse -- gradients return along the
+ * forward's routing path (gsyq.cn section 2.4; the DeepEP notes' backward
+ * pass section) -- so what it computes is the chain rule of the forward
+ * above, with these readings:
+ *   - the top-k choice is held fixed (it is not differentiable);
+ *   - fp8 rows pass the gradient straight through (d xq / d x = 1);
+ *   - a slot dropped by a capacity limit contributes no output, so its
+ *     d w is 0, but it stays in the token's softmax;
+ *   - the gate bias is a constant.
+ * For each listed token, with g = dy[t]:
+ *   shared s:  FFN_s backward with upstream g;
+ *   slot j:    o_j = FFN_e(xq), d w_j = <g, o_j>, FFN_e backward with w_j g;
+ *   weights:   d z_j = w_j (d w_j - sum_i w_i d w_i) for the selected experts;
+ *   gate:      dWg[e_j] += d z_j x, dx += d z_j Wg[e_j].
+ * FFN backward (v the input, a = W1 v, b = W3 v, s = 1/(1+e^-a),
+ * hv = a s b, upstream go): dW2 += go hv^T, dhv = W2^T go,
+ * da = dhv b (s + a s (1 - s)), db = dhv a s, dW1 += da v^T, dW3 += db v^T,
+ * dv = W1^T da + W3^T db.
+ * Outputs: dx [n,d], dtopk_w [n,k]; dwg [E,d], dw1/dw3 [E+S,h,d] and dw2
+ * [E+S,d,h] are accumulated (zero them first).
+ */
+static void swiglu_backward(int d, int h, int wdt, const double *v, const void *w1g,
+                            const void *w3g, const void *w2g, const double *go,
+                            double *dw1g, double *dw3g, double *dw2g, double *dv,
+                            double *a, double *b, double *hv, double *dhv)
+{
+    for (int j = 0; j < h; ++j) {
+        double aa = 0.0, bb = 0.0;
+        for (int i = 0; i < d; ++i) {
+            aa += (double)elem(w1g, wdt, (int64_t)j * d + i) * v[i];
+            bb += (double)elem(w3g, wdt, (int64_t)j * d + i) * v[i];
+        }
+        a[j] = aa;
+        b[j] = bb;
+        double sg = 1.0 / (1.0 + exp(-aa));
+        hv[j] = aa * sg * bb;
+    }
+    for (int i = 0; i < d; ++i)
+        for (int j = 0; j < h; ++j)
+            dw2g[(int64_t)i * h + j] += go[i] * hv[j];
+    for (int j = 0; j < h; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < d; ++i)
+            acc += (double)elem(w2g, wdt, (int64_t)i * h + j) * go[i];
+        dhv[j] = acc;
+    }
+    for (int i = 0; i < d; ++i)
+        dv[i] = 0.0;
+    for (int j = 0; j < h; ++j) {
+        double sg = 1.0 / (1.0 + exp(-a[j]));
+        double da = dhv[j] * b[j] * (sg + a[j] * sg * (1.0 - sg));
+        double db = dhv[j] * a[j] * sg;
+        for (int i = 0; i < d; ++i) {
+            dw1g[(int64_t)j * d + i] += da * v[i];
+            dw3g[(int64_t)j * d + i] += db * v[i];
+            dv[i] += (double)elem(w1g, wdt, (int64_t)j * d + i) * da +
+                     (double)elem(w3g, wdt, (int64_t)j * d + i) * db;
+        }
+    }
+}
+
+int oracle_layer_backward(int d, int E, int k, int S, int h, int dtype, int fp8,
+                          int64_t n, const int64_t *tokens, const int32_t *route,
+                          const void *x, const void *wg, const float *bias,
+                          const void *w1, const void *w3, const void *w2,
+                          const double *dy, double *dx, double *dtopk_w, double *dwg,
+                          double *dw1, double *dw3, double *dw2)
+{
+    if (d <= 0 || E <= 0 || E > 1024 || k <= 0 || k > E || k > 64 || S < 0 || h <= 0)
+        return -1;
+    float *z = (float *)malloc(sizeof(float) * (size_t)E);
+    float *xf = (float *)malloc(sizeof(float) * (size_t)d);
+    uint8_t *q = (uint8_t *)malloc((size_t)d);
+    double *v = (double *)malloc(sizeof(double) * (size_t)d);
+    double *vq = (double *)malloc(sizeof(double) * (size_t)d);
+    double *o = (double *)malloc(sizeof(double) * (size_t)d);
+    double *go = (double *)malloc(sizeof(double) * (size_t)d);
+    double *dv = (double *)malloc(sizeof(double) * (size_t)d);
+    double *tmp = (double *)malloc(sizeof(double) * (size_t)h * 5);
+    int32_t idx[64];
+    double w[64], dw[64];
+    int rc = 0;
+    if (!z || !xf || !q || !v || !vq || !o || !go || !dv || !tmp)
+        rc = -4;
+    const int64_t hd = (int64_t)h * d;
+    for (int64_t r = 0; r < n && rc == 0; ++r) {
+        int64_t t = tokens[r];
+        for (int e = 0; e < E; ++e)
+            z[e] = gate_logit(t, e, d, dtype, x, wg, bias);
+        select_one(E, k, z, idx, w);
+        for (int i = 0; i < d; ++i) {
+            xf[i] = elem(x, dtype, t * d + i);
+            v[i] = (double)xf[i];
+        }
+        if (fp8) {
+            float s, c;
+            oracle_fp8_quantize_row(d, xf, q, &s, &c);
+            for (int i = 0; i < d; ++i)
+                vq[i] = oracle_e4m3_decode(q[i]) * (double)s + (double)c;
+        } else {
+            memcpy(vq, v, sizeof(double) * (size_t)d);
+        }
+        const double *g = dy + r * d;
+        double *dxr = dx + r * d;
+        for (int i = 0; i < d; ++i)
+            dxr[i] = 0.0;
+        for (int s = 0; s < S; ++s) {
+            int64_t gi = E + s;
+            swiglu_backward(d, h, dtype, v, group_ptr(w1, dtype, gi, hd), group_ptr(w3, dtype, gi, hd),
+                            group_ptr(w2, dtype, gi, hd), g, dw1 + gi * hd, dw3 + gi * hd,
+                            dw2 + gi * hd, dv, tmp, tmp + h, tmp + 2 * h, tmp + 3 * h);
+            for (int i = 0; i < d; ++i)
+                dxr[i] += dv[i];
+        }
+        for (int j = 0; j < k; ++j) {
+            dw[j] = 0.0;
+            int64_t gi = route ? route[r * k + j] : idx[j];
+            if (gi < 0)
+                continue; /* dropped: no output, d w = 0 */
+            swiglu_ffn(d, h, dtype, vq, group_ptr(w1, dtype, gi, hd), group_ptr(w3, dtype, gi, hd),
+                       group_ptr(w2, dtype, gi, hd), o, tmp);
+            double acc = 0.0;
+            for (int i = 0; i < d; ++i) {
+                acc += g[i] * o[i];
+                go[i] = w[j] * g[i];
+            }
+            dw[j] = acc;
+            swiglu_backward(d, h, dtype, vq, group_ptr(w1, dtype, gi, hd), group_ptr(w3, dtype, gi, hd),
+                            group_ptr(w2, dtype, gi, hd), go, dw1 + gi * hd, dw3 + gi * hd,
+                            dw2 + gi * hd, dv, tmp, tmp + h, tmp + 2 * h, tmp + 3 * h);
+            for (int i = 0; i < d; ++i)
+                dxr[i] += dv[i]; /* straight through the fp8 rows */
+        }
+        double mean = 0.0;
+        for (int j = 0; j < k; ++j) {
+            dtopk_w[r * k + j] = dw[j];
+            mean += w[j] * dw[j];
+        }
+        for (int j = 0; j < k; ++j) {
+            double dz = w[j] * (dw[j] - mean);
+            int e = idx[j];
+            for (int i = 0; i < d; ++i) {
+                dwg[(int64_t)e * d + i] += dz * v[i];
+                dxr[i] += dz * (double)elem(wg, dtype, (int64_t)e * d + i);
+            }
+        }
+    }
+    free(z); free(xf); free(q); free(v); free(vq); free(o); free(go); free(dv); free(tmp);
+    return rc;
+}

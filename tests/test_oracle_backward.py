@@ -1,0 +1,144 @@
+"""Pins for the oracle's layer backward (gradients of sum(dy * y)).
+
+Checked against (1) autograd of a float64 torch re-implementation of the
+layer -- torch's autograd, a library routine, differentiates the forward
+written out with the same readings (top-k choice fixed, fp8 rows straight
+through, dropped slots kept in the softmax) -- and (2) central finite
+differences of the oracle's own forward (layer_tokens), which shares no code
+with the backward. The oracle's gate weights come from float32 logits, the
+re-implementation's from float64 ones, hence the 1e-6 tolerances.
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from moe_workloads import CONFIGS, bf16_bits_to_f32, make_inputs
+
+
+def _f64(a):
+    return torch.from_numpy(a.astype(np.float64) if a.dtype == np.float32
+                            else bf16_bits_to_f32(a).astype(np.float64))
+
+
+def _cfg(act="f32", **kw):
+    base = CONFIGS["tiny_fp32" if act == "f32" else "deepseekmoe_bf16"]
+    kw.setdefault("sigma_w", 0.3)
+    return dataclasses.replace(base, **kw)
+
+
+def torch_grads(inp, idx, dy, route=None):
+    """Autograd of sum(dy * y) for the layer written out in float64 torch."""
+    cfg = inp.cfg
+    X = _f64(inp.x).requires_grad_(True)
+    Wg = _f64(inp.wg).requires_grad_(True)
+    W1 = _f64(inp.w1).requires_grad_(True)
+    W3 = _f64(inp.w3).requires_grad_(True)
+    W2 = _f64(inp.w2).requires_grad_(True)
+    z = X @ Wg.T
+    if inp.bias is not None:
+        z = z + torch.from_numpy(inp.bias.astype(np.float64))
+    I = torch.from_numpy(idx.astype(np.int64))
+    w = torch.softmax(z.gather(1, I), dim=1)
+    w.retain_grad()
+    if cfg.dispatch == "fp8":
+        q, qp = oracle.fp8_quantize(inp.x)
+        Xq = X + (torch.from_numpy(oracle.fp8_dequantize(q, qp)) - X).detach()
+    else:
+        Xq = X
+
+    def ffn(v, g):
+        a = v @ W1[g].T
+        return (a * torch.sigmoid(a) * (v @ W3[g].T)) @ W2[g].T
+
+    y = torch.zeros_like(X)
+    for s in range(cfg.S):
+        y = y + ffn(X, cfg.E + s)
+    for t in range(cfg.T):
+        for j in range(cfg.k):
+            e = int(idx[t, j]) if route is None else int(route[t, j])
+            if e < 0:
+                continue
+            y[t] = y[t] + w[t, j] * ffn(Xq[t:t + 1], e)[0]
+    (torch.from_numpy(dy) * y).sum().backward()
+    return dict(dx=X.grad.numpy(), dwg=Wg.grad.numpy(), dw1=W1.grad.numpy(), dw3=W3.grad.numpy(),
+                dw2=W2.grad.numpy(), dtopk_w=w.grad.numpy())
+
+
+def _rel(a, b):
+    return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
+
+
+@pytest.mark.parametrize("act,kw", [
+    ("f32", dict(T=12, d=16, E=5, k=2, S=0, h=8)),
+    ("f32", dict(T=9, d=12, E=4, k=4, S=2, h=10)),      # k = E, shared experts
+    ("bf16", dict(T=10, d=16, E=6, k=3, S=1, h=8)),
+    ("bf16", dict(T=8, d=16, E=6, k=2, S=1, h=8, dispatch="fp8")),
+], ids=["f32", "k_eq_E_shared", "bf16", "fp8_rows"])
+def test_backward_matches_autograd(act, kw):
+    inp = make_inputs(_cfg(act, **kw), seed=3)
+    cfg = inp.cfg
+    toks = np.arange(cfg.T)
+    idx, _, _ = oracle.layer_tokens(inp, toks)
+    dy = np.random.default_rng(5).standard_normal((cfg.T, cfg.d))
+    got = oracle.layer_backward(inp, toks, dy)
+    ref = torch_grads(inp, idx, dy)
+    for key in ("dx", "dwg", "dw1", "dw3", "dw2", "dtopk_w"):
+        assert _rel(got[key], ref[key]) < 1e-6, (key, _rel(got[key], ref[key]))
+
+
+def test_dropped_slot_has_no_output_gradient():
+    inp = make_inputs(_cfg("f32", T=10, d=12, E=5, k=2, S=1, h=6), seed=4)
+    cfg = inp.cfg
+    toks = np.arange(cfg.T)
+    idx, _, _ = oracle.layer_tokens(inp, toks)
+    route = idx.copy()
+    route[::2, 1] = -1
+    dy = np.random.default_rng(6).standard_normal((cfg.T, cfg.d))
+    got = oracle.layer_backward(inp, toks, dy, route=route)
+    ref = torch_grads(inp, idx, dy, route=route)
+    for key in ("dx", "dwg", "dw1", "dw3", "dw2", "dtopk_w"):
+        assert _rel(got[key], ref[key]) < 1e-6, key
+    assert np.all(got["dtopk_w"][::2, 1] == 0.0)
+
+
+def test_backward_matches_finite_differences():
+    inp = make_inputs(_cfg("f32", T=6, d=10, E=4, k=2, S=1, h=7), seed=7)
+    cfg = inp.cfg
+    toks = np.arange(cfg.T)
+    dy = np.random.default_rng(8).standard_normal((cfg.T, cfg.d))
+    idx0, _, _ = oracle.layer_tokens(inp, toks)
+    g = oracle.layer_backward(inp, toks, dy)
+
+    def loss():
+        idx, _, y = oracle.layer_tokens(inp, toks)
+        return float(np.sum(dy * y)), np.array_equal(idx, idx0)
+
+    rng = np.random.default_rng(9)
+    checks = [("w1", "dw1"), ("w3", "dw3"), ("w2", "dw2"), ("x", "dx"), ("wg", "dwg")]
+    for arr_name, grad_name in checks:
+        arr = getattr(inp, arr_name)
+        done = 0
+        for _ in range(40):
+            if done == 4:
+                break
+            pos = tuple(rng.integers(0, s) for s in arr.shape)
+            old = arr[pos]
+            eps = np.float32(3e-3 if arr_name in ("x", "wg") else 1e-3)
+            arr[pos] = old + eps
+            hi_v, (lp, same_p) = arr[pos], loss()
+            arr[pos] = old - eps
+            lo_v, (lm, same_m) = arr[pos], loss()
+            arr[pos] = old
+            if not (same_p and same_m):
+                continue  # the step crossed a routing boundary: not differentiable there
+            fd = (lp - lm) / (float(hi_v) - float(lo_v))
+            an = g[grad_name][pos]
+            # the gate runs in float32, so its steps carry float32 noise
+            tol = 2e-3 * max(1.0, abs(an)) if arr_name in ("x", "wg") else 1e-5 * max(1.0, abs(an))
+            assert abs(fd - an) < tol, (arr_name, pos, fd, an)
+            done += 1
+        assert done == 4, arr_name
