@@ -138,7 +138,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the tokens on one GPU; "
-              "runs on more than one GPU are not part of this build", file=sys.stderr)
+              "multi-GPU runs are not implemented", file=sys.stderr)
         sys.exit(2)
     if args.copy_probe_mib > 0:
         copy_probe(args.copy_probe_mib)

@@ -11,7 +11,7 @@ import torch
 
 HAVE_GPU = torch.cuda.is_available()
 
-# oracle worker threads for full-size checks (the GPU machine gives 16 CPU threads)
+# oracle worker threads for full-size checks (at most 16 host threads)
 ORACLE_THREADS = min(16, os.cpu_count() or 1)
 
 
