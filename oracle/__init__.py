@@ -61,6 +61,8 @@ def lib():
         L.oracle_layer_tokens.argtypes = [i32, i32, i32, i32, i32, i32, i32, i64, vp, vp, vp,
                                           vp, vp, vp, vp, vp, vp, vp, vp, vp, i32]
         L.oracle_fp8_quantize_ranges.argtypes = [i64, i32, i32, vp, vp, vp, vp]
+        L.oracle_combine_backward.argtypes = [i64, i32, i32, i32, vp, vp, vp, vp, i64, vp, vp]
+        L.oracle_dispatch_backward.argtypes = [i64, i32, i32, i32, vp, vp, vp, i64, vp]
         L.oracle_layer_backward.argtypes = [i32, i32, i32, i32, i32, i32, i32, i64, vp, vp, vp, vp,
                                             vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.oracle_combine.argtypes = [i64, i32, i32, i32, vp, vp, vp, vp, i64, vp]
@@ -249,6 +251,36 @@ def layer_backward(inp, tokens, dy, route=None):
                                        _p(inp.w2), _p(dy), _p(out["dx"]), _p(out["dtopk_w"]),
                                        _p(out["dwg"]), _p(out["dw1"]), _p(out["dw3"]),
                                        _p(out["dw2"])), "layer_backward")
+    return out
+
+
+def combine_backward(dy, y_perm, dest_row, topk_w):
+    """(dy_perm [rows,d] float64, dtopk_w [T,k] float64): the transpose of
+    combine; rows no slot points at stay zero."""
+    dy = np.ascontiguousarray(dy)
+    y_perm = np.ascontiguousarray(y_perm)
+    assert dy.dtype == y_perm.dtype
+    dest = np.ascontiguousarray(dest_row, dtype=np.int32)
+    T, k = dest.shape
+    rows, d = y_perm.shape
+    w = np.ascontiguousarray(topk_w, dtype=np.float32)
+    dyp = np.zeros((rows, d))
+    dw = np.zeros((T, k))
+    _check(lib().oracle_combine_backward(T, d, k, _dtype_code(dy), _p(dy), _p(y_perm), _p(dest),
+                                         _p(w), rows, _p(dyp), _p(dw)), "combine_backward")
+    return dyp, dw
+
+
+def dispatch_backward(dx_perm, dx_shared, dest_row):
+    """dx [T,d] float64 = dx_shared + sum_j dx_perm[dest_row[t,j]]."""
+    dx_perm = np.ascontiguousarray(dx_perm)
+    dest = np.ascontiguousarray(dest_row, dtype=np.int32)
+    T, k = dest.shape
+    rows, d = dx_perm.shape
+    sh = None if dx_shared is None else np.ascontiguousarray(dx_shared)
+    out = np.empty((T, d))
+    _check(lib().oracle_dispatch_backward(T, d, k, _dtype_code(dx_perm), _p(dx_perm), _p(sh),
+                                          _p(dest), rows, _p(out)), "dispatch_backward")
     return out
 
 

@@ -730,3 +730,61 @@ int oracle_layer_backward(int d, int E, int k, int S, int h, int dtype, int fp8,
     free(z); free(xf); free(q); free(v); free(vq); free(o); free(go); free(dv); free(tmp);
     return rc;
 }
+
+/*
+ * The backward of combine and of dispatch on their own (the exchanges the
+ * pages run in reverse for the gradients: gsyq.cn section 2.4, the DeepEP
+ * notes' backward pass section), in float64 from rows stored as float32 or
+ * bf16:
+ *   combine backward   dy_perm[dest_row[t,j]] = w[t,j] dy[t] and
+ *                      dw[t,j] = <dy[t], y_perm[dest_row[t,j]]>;
+ *                      the shared experts' upstream gradient is dy itself;
+ *   dispatch backward  dx[t] = dx_sh[t] (if given) + sum_j dx_perm[dest_row[t,j]]
+ *                      (the transpose of copying row t to k places).
+ * Slots with dest_row < 0 (dropped) take and give nothing.
+ */
+int oracle_combine_backward(int64_t T, int d, int k, int dtype, const void *dy,
+                            const void *y_perm, const int32_t *dest_row,
+                            const float *topk_w, int64_t rows, double *dy_perm, double *dw)
+{
+    if (T < 0 || d <= 0 || k <= 0)
+        return -1;
+    for (int64_t t = 0; t < T; ++t)
+        for (int j = 0; j < k; ++j) {
+            int64_t p = dest_row[t * k + j];
+            if (p >= rows)
+                return -2;
+            double acc = 0.0;
+            if (p >= 0)
+                for (int i = 0; i < d; ++i) {
+                    double g = (double)elem(dy, dtype, t * d + i);
+                    dy_perm[p * d + i] = (double)topk_w[t * k + j] * g;
+                    acc += g * (double)elem(y_perm, dtype, p * d + i);
+                }
+            dw[t * k + j] = acc;
+        }
+    return 0;
+}
+
+int oracle_dispatch_backward(int64_t T, int d, int k, int dtype, const void *dx_perm,
+                             const void *dx_shared, const int32_t *dest_row, int64_t rows,
+                             double *dx)
+{
+    if (T < 0 || d <= 0 || k <= 0)
+        return -1;
+    for (int64_t t = 0; t < T; ++t) {
+        double *r = dx + t * d;
+        for (int i = 0; i < d; ++i)
+            r[i] = dx_shared ? (double)elem(dx_shared, dtype, t * d + i) : 0.0;
+        for (int j = 0; j < k; ++j) {
+            int64_t p = dest_row[t * k + j];
+            if (p >= rows)
+                return -2;
+            if (p < 0)
+                continue;
+            for (int i = 0; i < d; ++i)
+                r[i] += (double)elem(dx_perm, dtype, p * d + i);
+        }
+    }
+    return 0;
+}

@@ -142,3 +142,63 @@ def test_backward_matches_finite_differences():
             assert abs(fd - an) < tol, (arr_name, pos, fd, an)
             done += 1
         assert done == 4, arr_name
+
+
+# ------------------------------------------- combine / dispatch backward ---
+# Each is the transpose of a forward step the oracle already has, so the
+# adjoint identity <forward(a), b> = <a, backward(b)> pins it; dtopk_w is
+# also checked against the layer backward on the experts' real outputs.
+
+def _rows_f32(rng, n, d):
+    return rng.standard_normal((n, d)).astype(np.float32)
+
+
+@pytest.mark.parametrize("capacity", [0, 25])
+def test_combine_backward_is_the_transpose_of_combine(capacity):
+    from moe_workloads import make_routing
+    rng = np.random.default_rng(1)
+    T, E, k, d = 200, 8, 3, 24
+    idx = make_routing(T, E, k, seed=2, skew=1.0)
+    _, offsets, dest, _ = oracle.dispatch(idx, E, capacity=capacity)
+    w = rng.random((T, k)).astype(np.float32)
+    Y = _rows_f32(rng, T * k, d)
+    dy = _rows_f32(rng, T, d)
+    y = oracle.combine(Y, None, np.where(dest >= 0, dest, 0), w * (dest >= 0))
+    dyp, dw = oracle.combine_backward(dy, Y, dest, w)
+    lhs = float(np.sum(y * dy.astype(np.float64)))
+    rhs = float(np.sum(dyp * Y.astype(np.float64)))
+    assert abs(lhs - rhs) <= 1e-9 * max(1.0, abs(lhs))
+    # d w is the dot product of dy with the slot's row; dropped slots give 0
+    kept = dest >= 0
+    ref = np.einsum("td,tkd->tk", dy.astype(np.float64), Y[np.where(kept, dest, 0)].astype(np.float64))
+    np.testing.assert_allclose(dw[kept], ref[kept], rtol=1e-12, atol=1e-12)
+    assert np.all(dw[~kept] == 0.0)
+
+
+def test_dispatch_backward_is_the_transpose_of_the_permutation():
+    from moe_workloads import make_routing
+    rng = np.random.default_rng(3)
+    T, E, k, d = 150, 6, 2, 20
+    idx = make_routing(T, E, k, seed=4)
+    _, offsets, dest, src = oracle.dispatch(idx, E)
+    x = _rows_f32(rng, T, d)
+    g = _rows_f32(rng, T * k, d)
+    sh = _rows_f32(rng, T, d)
+    dx = oracle.dispatch_backward(g, sh, dest)
+    lhs = float(np.sum(x[src].astype(np.float64) * g)) + float(np.sum(x.astype(np.float64) * sh))
+    rhs = float(np.sum(x.astype(np.float64) * dx))
+    assert abs(lhs - rhs) <= 1e-9 * max(1.0, abs(lhs))
+
+
+def test_combine_backward_weights_match_the_layer_backward():
+    inp = make_inputs(_cfg("f32", T=10, d=12, E=5, k=2, S=0, h=8), seed=5)
+    cfg = inp.cfg
+    toks = np.arange(cfg.T)
+    idx, w, _ = oracle.layer_tokens(inp, toks)
+    _, offsets, dest, src = oracle.dispatch(idx, cfg.E)
+    groups = (np.searchsorted(offsets, np.arange(cfg.T * cfg.k), side="right") - 1).astype(np.int32)
+    Y = oracle.expert_rows(oracle.rows_as_f64(inp.x[src]), groups, inp.w1, inp.w3, inp.w2)
+    dy = np.random.default_rng(6).standard_normal((cfg.T, cfg.d)).astype(np.float32)
+    _, dw = oracle.combine_backward(dy, Y.astype(np.float32), dest, w.astype(np.float32))
+    ref = oracle.layer_backward(inp, toks, dy.astype(np.float64))["dtopk_w"]
+    assert _rel(dw, ref) < 1e-6
