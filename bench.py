@@ -70,6 +70,12 @@ def algorithmic(cfg, routed=None):
         + (8 * R if cfg.dispatch == "fp8" else 0),
         "ffn_down_flops": 2 * rows * d * h,
         "combine_bytes": R * d * b + (T * d * b if S else 0) + 8 * T * k + T * d * b,
+        # backward of combine: dy once, the forward rows in, their gradients out,
+        # routing metadata in and the weight gradients out
+        "combine_backward_bytes": T * d * b + 2 * R * d * b + 12 * T * k,
+        # backward of dispatch: the row gradients and the shared experts' in,
+        # the token gradients out
+        "dispatch_backward_bytes": R * d * b + (T * d * b if S else 0) + 4 * T * k + T * d * b,
     }
 
 
@@ -121,6 +127,45 @@ def cpu_baseline(cfg, n_tokens):
             "sample": f"first {len(toks)} tokens of the {cfg.name} batch, whole layer per token "
                       f"(float32 gate chain, top-k, float64 SwiGLU experts, weighted sum), "
                       f"1 thread, {dt:.1f} s"}
+
+
+def backward_leg(mm, torch, cfg, shape, buf, stream, A, reps=20):
+    """Time the two data-movement stages of the layer backward on this
+    forward's routing: synthetic gradients and expert rows, each launch
+    bracketed by its own pair of events (averaged over reps launches)."""
+    T, d, k = cfg.T, cfg.d, cfg.k
+    dt = torch.float32 if cfg.act == "f32" else torch.bfloat16
+    g = torch.Generator(device="cuda").manual_seed(7)
+    dy = torch.randn((T, d), device="cuda", generator=g).to(dt)
+    y_perm = torch.randn((T * k, d), device="cuda", generator=g).to(dt)
+    dy_perm = torch.empty((T * k, d), dtype=dt, device="cuda")
+    dw = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    dx_sh = torch.randn((T, d), device="cuda", generator=g).to(dt) if cfg.S else None
+    dx = torch.empty((T, d), dtype=dt, device="cuda")
+    calls = {
+        "combine_backward": lambda: mm.moe_combine_backward(
+            shape, dy, y_perm, buf.dest_row, buf.topk_w, dy_perm, dw, stream),
+        "dispatch_backward": lambda: mm.moe_dispatch_backward(
+            shape, dy_perm, dx_sh, buf.dest_row, dx, stream),
+    }
+    out = {}
+    for name, call in calls.items():
+        for _ in range(3):
+            call()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        torch.cuda.synchronize()
+        for a, b in ev:
+            a.record(stream)
+            call()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        gbps = A[name + "_bytes"] / (ms * 1e-3) / 1e9
+        out[name] = {"us": round(ms * 1e3, 2), "GBps": round(gbps, 1),
+                     "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "algorithmic_bytes": A[name + "_bytes"]}
+    return out
 
 
 def main():
@@ -227,6 +272,7 @@ def main():
 
     routed = int(buf.offsets[-1].item())
     A = algorithmic(cfg, routed)
+    bwd = backward_leg(mm, torch, cfg, shape, buf, stream, A)
     t_gate = kmean["gate_topk"]
     t_disp = sum(v for n, v in kmean.items() if n.startswith("dispatch"))
     t_up, t_down = up_ms_timed, kmean["ffn_down"]
@@ -255,6 +301,7 @@ def main():
         "combine_hbm_frac": round(A["combine_bytes"] / (t_comb * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "routed_assignments_per_s": round(cfg.T * cfg.k / (ms_per_step * 1e-3), 1),
         "dispatched_rows": routed,
+        "backward_stages": bwd,
     }
     out = {
         "metric": METRIC,

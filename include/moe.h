@@ -207,6 +207,39 @@ int32_t moe_combine(const moe_shape *s, const void *y_perm, const void *y_shared
                     void *stream);
 
 /*
+ * Backward of combine (the gradients returning along the routing path,
+ *  [gsyq] 2.4; [deepep] 7 "Combine", whose transpose this is): for every
+ *  slot (t,j) with p = dest_row[t,j] >= 0,
+ *    dy_perm[p]    = act(topk_w[t,j] * dy[t])          (rounded once)
+ *    dtopk_w[t,j]  = sum_c dy[t,c] * y_perm[p,c]       (float32 accumulation)
+ *  and dtopk_w[t,j] = 0 for a dropped slot (no row written).
+ *  dy [T,d] (act) is the gradient of the layer output, y_perm [>= max p + 1, d]
+ *  (act) the routed experts' forward output rows, dest_row [T,k] and topk_w
+ *  [T,k] as from the forward; dy_perm [T*k,d] (act) and dtopk_w [T,k] (f32)
+ *  are written. All device pointers, owned by the caller; rows of dy_perm no
+ *  slot maps to are left untouched. Errors: MOE_ERR_INVALID_ARG for a bad
+ *  shape or a NULL pointer (T = 0 is a no-op), MOE_ERR_HIP for a launch error.
+ *  dy_perm must not overlap dy or y_perm.
+ */
+int32_t moe_combine_backward(const moe_shape *s, const void *dy, const void *y_perm,
+                             const int32_t *dest_row, const float *topk_w, void *dy_perm,
+                             float *dtopk_w, void *stream);
+
+/*
+ * Backward of dispatch ([gsyq] 2.4; [deepep] 7 "Dispatch", whose transpose
+ *  this is): dispatch copies token t to its k rows, so its gradient sums them,
+ *    dx[t] = dx_shared[t] + sum_{j : dest_row[t,j] >= 0} dx_perm[dest_row[t,j]]
+ *  accumulated in float32 in slot order and rounded once to act. dx_perm
+ *  [rows,d] (act) holds the routed rows' input gradients, dx_shared [T,d] (act)
+ *  the shared experts' (NULL: zero), dest_row [T,k] as from the forward; dx
+ *  [T,d] (act) is written. Device pointers owned by the caller; errors as for
+ *  moe_combine_backward. The gradient with respect to the gate input is not
+ *  part of this call (it is a plain GEMM with the gate weights).
+ */
+int32_t moe_dispatch_backward(const moe_shape *s, const void *dx_perm, const void *dx_shared,
+                              const int32_t *dest_row, void *dx, void *stream);
+
+/*
  * The whole layer: moe_gate_topk -> moe_dispatch -> moe_grouped_ffn ->
  * moe_combine with intermediates in the workspace (MOE_STAGE_FORWARD bytes).
  * y [T,d] (act) is the layer output; topk_idx, topk_w, counts, offsets,

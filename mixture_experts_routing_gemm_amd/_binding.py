@@ -96,6 +96,10 @@ def _load():
     L.moe_grouped_ffn.restype = i32
     L.moe_combine.argtypes = [sp, vp, vp, vp, vp, vp, vp]
     L.moe_combine.restype = i32
+    L.moe_combine_backward.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp]
+    L.moe_combine_backward.restype = i32
+    L.moe_dispatch_backward.argtypes = [sp, vp, vp, vp, vp, vp]
+    L.moe_dispatch_backward.restype = i32
     L.moe_forward.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_forward.restype = i32
     L.moe_forward_traced.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -113,7 +117,8 @@ def _load():
 lib = _load()
 
 EXPORTS = ["moe_workspace_bytes", "moe_workspace_init", "moe_status_string", "moe_gate_topk",
-           "moe_dispatch", "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_forward_traced",
+           "moe_dispatch", "moe_grouped_ffn", "moe_combine", "moe_combine_backward",
+           "moe_dispatch_backward", "moe_forward", "moe_forward_traced",
            "moe_forward_kernel_count", "moe_forward_kernel_name", "moe_get_device_error"]
 
 
@@ -193,6 +198,17 @@ def moe_grouped_ffn(shape, x_perm, qparams, offsets, x, w1, w3, w2, y_perm, y_sh
 def moe_combine(shape, y_perm, y_shared, dest_row, topk_w, y, stream=None):
     _check(lib.moe_combine(ctypes.byref(shape), _p(y_perm), _p(y_shared), _p(dest_row),
                            _p(topk_w), _p(y), _s(stream)), "moe_combine")
+
+
+def moe_combine_backward(shape, dy, y_perm, dest_row, topk_w, dy_perm, dtopk_w, stream=None):
+    _check(lib.moe_combine_backward(ctypes.byref(shape), _p(dy), _p(y_perm), _p(dest_row),
+                                    _p(topk_w), _p(dy_perm), _p(dtopk_w), _s(stream)),
+           "moe_combine_backward")
+
+
+def moe_dispatch_backward(shape, dx_perm, dx_shared, dest_row, dx, stream=None):
+    _check(lib.moe_dispatch_backward(ctypes.byref(shape), _p(dx_perm), _p(dx_shared),
+                                     _p(dest_row), _p(dx), _s(stream)), "moe_dispatch_backward")
 
 
 def moe_forward(shape, x, w_gate, bias, w1, w3, w2, y, topk_idx, topk_w, counts, offsets,

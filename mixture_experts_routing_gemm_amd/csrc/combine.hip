@@ -8,7 +8,12 @@
 // MoE 的同步税", wmrh.cn, section 2.1), is added in the same pass.
 //
 // One wave per token: the k source rows are gathered with 16-byte loads
-// (rows are contiguous), summed in float32 and rounded once.
+// (rows are contiguous), summed in float32 and rounded once. With no weights
+// (topk_w == NULL) every slot has weight one: that is the backward of
+// dispatch, dx[t] = dx_sh[t] + sum_j dx_perm[dest_row[t,j]].
+//
+// The backward of combine (the gradients going back along the routing path,
+// gsyq.cn section 2.4) is its own kernel below.
 #include "moe_device.h"
 
 namespace moe {
@@ -62,7 +67,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
     float wt = 0.0f;
     if (lane < k) {
         p = dest_row[t * k + lane];
-        wt = topk_w[t * k + lane];
+        wt = topk_w != nullptr ? topk_w[t * k + lane] : 1.0f;
         if (p < 0 || p >= rows) p = -1;
     }
     int pj[kMaxK];
@@ -113,6 +118,85 @@ __global__ __launch_bounds__(256) void combine_kernel(
             store16(y + t * d + col, V::pack(acc));
         }
     }
+}
+
+// Backward of combine, one wave per token: dy_perm[dest_row[t,j]] =
+// bf16/f32(w_j * dy[t]) and dtopk_w[t,j] = <dy[t], y_perm[dest_row[t,j]]>,
+// accumulated in float32 per lane over its chunks and then across the wave;
+// a dropped slot (dest_row < 0) gets 0 and writes no row.
+template <typename TAct>
+__global__ __launch_bounds__(256) void combine_backward_kernel(
+    const TAct* __restrict__ dy, const TAct* __restrict__ y_perm,
+    const int32_t* __restrict__ dest_row, const float* __restrict__ topk_w, int64_t T, int d,
+    int k, int64_t rows, TAct* __restrict__ dy_perm, float* __restrict__ dtopk_w) {
+    using V = ActVec<TAct>;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + w;
+    if (t >= T) return;
+    int p = -1;
+    float wt = 0.0f;
+    if (lane < k) {
+        p = dest_row[t * k + lane];
+        wt = topk_w[t * k + lane];
+        if (p < 0 || p >= rows) p = -1;
+    }
+    int pj[kMaxK];
+    float wj[kMaxK], dot[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+        pj[j] = __shfl(p, j, kWave);
+        wj[j] = __shfl(wt, j, kWave);
+        dot[j] = 0.0f;
+    }
+    const int nchunk = d / V::N;
+    for (int c = lane; c < nchunk; c += kWave) {
+        const int64_t col = static_cast<int64_t>(c) * V::N;
+        float g[V::N];
+        V::unpack(load16(dy + t * d + col), g);
+        u32x4 src[kMaxK];
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j)
+            if (j < k && pj[j] >= 0) src[j] = load16(y_perm + static_cast<int64_t>(pj[j]) * d + col);
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j) {
+            if (j < k && pj[j] >= 0) {
+                float v[V::N], o[V::N];
+                V::unpack(src[j], v);
+#pragma unroll
+                for (int u = 0; u < V::N; ++u) {
+                    dot[j] = __builtin_fmaf(g[u], v[u], dot[j]);
+                    o[u] = wj[j] * g[u];
+                }
+                store16(dy_perm + static_cast<int64_t>(pj[j]) * d + col, V::pack(o));
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+        if (j < k) {
+            float sum = dot[j];
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, kWave);
+            if (lane == 0) dtopk_w[t * k + j] = pj[j] >= 0 ? sum : 0.0f;
+        }
+    }
+}
+
+hipError_t launch_combine_backward(const moe_shape& s, const void* dy, const void* y_perm,
+                                   const int32_t* dest_row, const float* topk_w, void* dy_perm,
+                                   float* dtopk_w, hipStream_t st) {
+    const unsigned blocks = static_cast<unsigned>((s.T + 3) / 4);
+    const int64_t rows = s.T * s.k;
+    if (s.act == MOE_F32) {
+        combine_backward_kernel<float><<<blocks, 256, 0, st>>>(
+            static_cast<const float*>(dy), static_cast<const float*>(y_perm), dest_row, topk_w, s.T,
+            s.d, s.k, rows, static_cast<float*>(dy_perm), dtopk_w);
+    } else {
+        combine_backward_kernel<bf16_t><<<blocks, 256, 0, st>>>(
+            static_cast<const bf16_t*>(dy), static_cast<const bf16_t*>(y_perm), dest_row, topk_w,
+            s.T, s.d, s.k, rows, static_cast<bf16_t*>(dy_perm), dtopk_w);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_combine(const moe_shape& s, const void* y_perm, const void* y_sh,

@@ -28,6 +28,9 @@ size_t ffn_plan_bytes(const moe_shape& s);
 bool ffn_fused_plan(const moe_shape& s, int32_t* plan, FfnPlanArgs* fp);
 hipError_t launch_combine(const moe_shape& s, const void* y_perm, const void* y_sh,
                           const int32_t* dest_row, const float* topk_w, void* y, hipStream_t st);
+hipError_t launch_combine_backward(const moe_shape& s, const void* dy, const void* y_perm,
+                                   const int32_t* dest_row, const float* topk_w, void* dy_perm,
+                                   float* dtopk_w, hipStream_t st);
 
 __global__ void clear_header_kernel(uint32_t* hdr) { hdr[threadIdx.x] = 0u; }
 }  // namespace moe
@@ -267,6 +270,27 @@ int32_t moe_combine(const moe_shape* s, const void* y_perm, const void* y_shared
     MOE_TRY(check_ptrs({y_perm, dest_row, topk_w, y}));
     MOE_TRY(check_opt({y_shared}));
     return hip_status(launch_combine(*s, y_perm, y_shared, dest_row, topk_w, y,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_combine_backward(const moe_shape* s, const void* dy, const void* y_perm,
+                             const int32_t* dest_row, const float* topk_w, void* dy_perm,
+                             float* dtopk_w, void* stream) {
+    MOE_TRY(check_shape(s, false));
+    if (s->T == 0) return MOE_OK;
+    MOE_TRY(check_ptrs({dy, y_perm, dest_row, topk_w, dy_perm, dtopk_w}));
+    return hip_status(launch_combine_backward(*s, dy, y_perm, dest_row, topk_w, dy_perm, dtopk_w,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_dispatch_backward(const moe_shape* s, const void* dx_perm, const void* dx_shared,
+                              const int32_t* dest_row, void* dx, void* stream) {
+    MOE_TRY(check_shape(s, false));
+    if (s->T == 0) return MOE_OK;
+    MOE_TRY(check_ptrs({dx_perm, dest_row, dx}));
+    MOE_TRY(check_opt({dx_shared}));
+    // the transpose of copying each row to its k places: combine with unit weights
+    return hip_status(launch_combine(*s, dx_perm, dx_shared, dest_row, nullptr, dx,
                                      static_cast<hipStream_t>(stream)));
 }
 

@@ -1,0 +1,203 @@
+"""GPU-vs-oracle parity of the two data-movement stages of the layer backward.
+
+The gradients return along the routing path (gsyq.cn, section 2.4; the
+DeepEP notes, section 7, dispatch and combine): the backward of combine sends
+w_j * dy[t] to each of token t's expert rows and takes the gate-weight
+gradient <dy[t], y_perm[row]>; the backward of dispatch sums each token's
+k row gradients (plus the shared experts') back into token order.
+
+Every call goes through the C ABI. Bars, element by element, derived from the
+arithmetic (u = 2^-24, the float32 unit roundoff; b = 2^-8, the bf16 one):
+  * dy_perm = round(w * dy): one float32 product, then one rounding to the
+    activation dtype: |err| <= (2u + b)|ref| for bf16, u|ref| for float32;
+  * dtopk_w: a float32 dot product of length d; a lane sums at most
+    n = ceil(d / (64 N)) N products in order (N = 8 bf16 or 4 float32 values
+    per 16-byte chunk), then a 6-level butterfly adds the lanes' sums:
+    |err| <= (n + 8) u sum_c |dy_c y_c|;
+  * dx: k + 1 float32 terms summed in slot order and rounded once:
+    |err| <= b|ref| + (k + 3) u sum |terms| for bf16 (b -> 0 for float32);
+  * rows of dy_perm that no slot maps to are never written (bit-exact).
+Inputs come from the seeded generators and the oracle's dispatch, never from
+the GPU path.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import act_torch, as_f64, dev, host, requires_gpu, say
+from moe_workloads import CONFIGS, make_routing, make_rows, make_weights
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+U = 2.0 ** -24
+SENTINEL = 0x7F7F  # bf16 / half of a float32 bit pattern never produced by a product here
+
+
+def _mm():
+    import mixture_experts_routing_gemm_amd as mm
+    return mm
+
+
+# (name, T, d, E, k, act, skew, capacity, reassign)
+CASES = [
+    ("f32_small", 777, 256, 8, 4, "f32", 0.0, 0, False),
+    ("bf16_ragged", 1001, 512, 16, 2, "bf16", 0.0, 0, False),
+    ("bf16_k8_wide", 513, 2056, 64, 8, "bf16", 0.0, 0, False),
+    ("bf16_drop", 2048, 1024, 32, 4, "bf16", 1.2, 200, False),
+    ("bf16_reassign", 2048, 1024, 32, 4, "bf16", 1.2, 260, True),
+    ("f32_drop_k1", 999, 64, 4, 1, "f32", 1.5, 100, False),
+    ("bf16_one_token", 1, 128, 8, 3, "bf16", 0.0, 0, False),
+]
+
+
+def _routing(T, E, k, skew, capacity, reassign, seed):
+    idx = make_routing(T, E, k, seed=seed, skew=skew)
+    _, offsets, dest, _ = oracle.dispatch(idx, E, capacity=capacity, reassign=reassign)
+    return dest, int(offsets[E])
+
+
+def _compact(dest, toks):
+    """Restrict to the sampled tokens: their slots' rows, renumbered 0.. in
+    slot order (dropped slots stay -1); returns (dest_s, source rows)."""
+    sub = dest[toks]
+    flat = sub.reshape(-1)
+    valid = flat >= 0
+    dest_s = np.full(flat.shape, -1, dtype=np.int32)
+    dest_s[valid] = np.arange(int(valid.sum()), dtype=np.int32)
+    return dest_s.reshape(sub.shape), flat[valid].astype(np.int64)
+
+
+def check_combine_backward(name, T, d, E, k, act, skew, capacity, reassign, toks=None, seed=5):
+    mm = _mm()
+    dest, nrows = _routing(T, E, k, skew, capacity, reassign, seed)
+    rows = T * k
+    dy = make_rows(T, d, act, seed=seed + 1)
+    y_perm = make_rows(rows, d, act, seed=seed + 2)
+    w = make_weights(T, k, seed=seed + 3)
+    shape = mm.make_shape(T, d, E, k, 0, 64, act, capacity=capacity, reassign=reassign)
+
+    dt = act_torch(act)
+    dyp = torch.empty((rows, d), dtype=dt, device="cuda")
+    if act == "bf16":
+        dyp.view(torch.int16).fill_(SENTINEL)
+    else:
+        dyp.view(torch.int32).fill_(SENTINEL << 16 | SENTINEL)
+    dw = torch.full((T, k), float("nan"), dtype=torch.float32, device="cuda")
+    say(f"[backward {name}] combine_backward T={T} d={d} E={E} k={k} {act} rows={nrows}")
+    mm.moe_combine_backward(shape, dev(dy), dev(y_perm), dev(dest), dev(w), dyp, dw)
+    torch.cuda.synchronize()
+    got_p, got_w = host(dyp), host(dw)
+
+    # rows no slot maps to keep the sentinel
+    mapped = np.zeros(rows, dtype=bool)
+    mapped[dest[dest >= 0]] = True
+    untouched = got_p[~mapped]
+    if untouched.size:
+        pat = untouched.view(np.uint16) if act == "f32" else untouched
+        assert np.all(pat == SENTINEL), "combine_backward wrote a row no slot maps to"
+
+    toks = np.arange(T) if toks is None else toks
+    dest_s, src_rows = _compact(dest, toks)
+    y_s = y_perm[src_rows]
+    ref_p, ref_w = oracle.combine_backward(dy[toks], y_s, dest_s, w[toks])
+
+    got_rows = as_f64(got_p[src_rows])
+    b = 2.0 ** -8 if act == "bf16" else 0.0
+    err = np.abs(got_rows - ref_p)
+    ok = err <= ((2 * U if b else U) + b) * np.abs(ref_p)
+    say(f"[backward {name}] dy_perm max rel {np.max(err / np.maximum(np.abs(ref_p), 1e-30)):.3e}")
+    assert ok.all(), f"dy_perm: {int((~ok).sum())} elements beyond one rounding"
+
+    # dtopk_w: slot by slot against the float64 dot product
+    gw = got_w[toks]
+    flat_dest = dest_s.reshape(-1)
+    scale = np.zeros(flat_dest.shape)
+    dyt = as_f64(dy[toks])
+    tok_of_slot = np.repeat(np.arange(len(toks)), k)
+    v = flat_dest >= 0
+    scale[v] = np.sum(np.abs(dyt[tok_of_slot[v]] * as_f64(y_s[flat_dest[v]])), axis=1)
+    per_chunk = 8 if act == "bf16" else 4
+    n_lane = -(-d // (64 * per_chunk)) * per_chunk
+    bound = (n_lane + 8) * U * scale.reshape(gw.shape)
+    werr = np.abs(gw - ref_w)
+    say(f"[backward {name}] dtopk_w max err/bound {np.max(werr / np.maximum(bound, 1e-300)):.3f}")
+    assert np.all(werr <= bound), "dtopk_w beyond the float32 dot-product bound"
+    assert np.all(gw[dest_s < 0] == 0.0), "a dropped slot's weight gradient is not zero"
+
+
+def check_dispatch_backward(name, T, d, E, k, act, skew, capacity, reassign, shared=True,
+                            toks=None, seed=9):
+    mm = _mm()
+    dest, nrows = _routing(T, E, k, skew, capacity, reassign, seed)
+    rows = max(nrows, 1)
+    dxp = make_rows(rows, d, act, seed=seed + 1)
+    dxs = make_rows(T, d, act, seed=seed + 2) if shared else None
+    shape = mm.make_shape(T, d, E, k, 0, 64, act, capacity=capacity, reassign=reassign)
+    dx = torch.empty((T, d), dtype=act_torch(act), device="cuda")
+    say(f"[backward {name}] dispatch_backward T={T} d={d} E={E} k={k} {act} shared={shared}")
+    mm.moe_dispatch_backward(shape, dev(dxp), None if dxs is None else dev(dxs), dev(dest), dx)
+    torch.cuda.synchronize()
+    got = as_f64(host(dx))
+
+    toks = np.arange(T) if toks is None else toks
+    dest_s, src_rows = _compact(dest, toks)
+    sh = None if dxs is None else dxs[toks]
+    ref = oracle.dispatch_backward(dxp[src_rows], sh, dest_s)
+    # sum of |terms| per element
+    absum = np.zeros_like(ref) if sh is None else np.abs(as_f64(sh))
+    rows64 = np.abs(as_f64(dxp[src_rows]))
+    for j in range(k):
+        r = dest_s[:, j]
+        m = r >= 0
+        absum[m] += rows64[r[m]]
+    b = 2.0 ** -8 if act == "bf16" else 0.0
+    bound = b * np.abs(ref) + (k + 3) * U * absum
+    err = np.abs(got[toks] - ref)
+    say(f"[backward {name}] dx max err/bound {np.max(err / np.maximum(bound, 1e-300)):.3f}")
+    assert np.all(err <= bound), "dx beyond one rounding of the float32 sum"
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_combine_backward(case):
+    check_combine_backward(*case)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("shared", [True, False])
+def test_dispatch_backward(case, shared):
+    check_dispatch_backward(*case, shared=shared)
+
+
+def test_backward_empty_batch():
+    """T = 0 is a no-op that touches nothing (NULL pointers are allowed)."""
+    mm = _mm()
+    shape = mm.make_shape(0, 128, 8, 2, 0, 64, "bf16")
+    mm.moe_combine_backward(shape, None, None, None, None, None, None)
+    mm.moe_dispatch_backward(shape, None, None, None, None)
+
+
+def test_backward_null_pointer_rejected():
+    mm = _mm()
+    shape = mm.make_shape(4, 128, 8, 2, 0, 64, "bf16")
+    t = torch.zeros((8, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(mm.MoEError):
+        mm.moe_combine_backward(shape, t, None, None, None, t, None)
+    with pytest.raises(mm.MoEError):
+        mm.moe_dispatch_backward(shape, None, None, None, t)
+
+
+@pytest.mark.parametrize("name", ["deepseekmoe_bf16", "coarse_top2_bf16"])
+def test_backward_full_size(name):
+    """At a workload's full size and routing shape (uniform routing of its
+    T, d, E, k), checked on sampled tokens."""
+    cfg = CONFIGS[name]
+    rng = np.random.default_rng(4)
+    toks = np.unique(np.concatenate([[0, 1, cfg.T // 2, cfg.T - 1],
+                                     rng.integers(0, cfg.T, 1500)])).astype(np.int64)
+    args = (name, cfg.T, cfg.d, cfg.E, cfg.k, cfg.act, 0.0, cfg.capacity, cfg.reassign)
+    check_combine_backward(*args, toks=toks)
+    check_dispatch_backward(*args, shared=True, toks=toks)
