@@ -63,6 +63,7 @@ def lib():
         L.oracle_fp8_quantize_ranges.argtypes = [i64, i32, i32, vp, vp, vp, vp]
         L.oracle_combine_backward.argtypes = [i64, i32, i32, i32, vp, vp, vp, vp, i64, vp, vp]
         L.oracle_dispatch_backward.argtypes = [i64, i32, i32, i32, vp, vp, vp, i64, vp]
+        L.oracle_gate_backward.argtypes = [i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
         L.oracle_layer_backward.argtypes = [i32, i32, i32, i32, i32, i32, i32, i64, vp, vp, vp, vp,
                                             vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.oracle_combine.argtypes = [i64, i32, i32, i32, vp, vp, vp, vp, i64, vp]
@@ -282,6 +283,26 @@ def dispatch_backward(dx_perm, dx_shared, dest_row):
     _check(lib().oracle_dispatch_backward(T, d, k, _dtype_code(dx_perm), _p(dx_perm), _p(sh),
                                           _p(dest), rows, _p(out)), "dispatch_backward")
     return out
+
+
+def gate_backward(x, wg, topk_idx, topk_w, dtopk_w):
+    """(dz [T,k], dx_gate [T,d], dwg [E,d]), all float64: the gate's backward
+    with the top-k choice held fixed; dz[t,j] is the gradient of the logit of
+    expert topk_idx[t,j] (every other logit's is zero)."""
+    x = np.ascontiguousarray(x)
+    wg = np.ascontiguousarray(wg)
+    assert x.dtype == wg.dtype
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    T, k = idx.shape
+    E, d = wg.shape
+    w = np.ascontiguousarray(topk_w, dtype=np.float64)
+    dw = np.ascontiguousarray(dtopk_w, dtype=np.float64)
+    dz = np.empty((T, k))
+    dxg = np.empty((T, d))
+    dwg = np.empty((E, d))
+    _check(lib().oracle_gate_backward(T, d, E, k, _dtype_code(x), _p(x), _p(wg), _p(idx), _p(w),
+                                      _p(dw), _p(dz), _p(dxg), _p(dwg)), "gate_backward")
+    return dz, dxg, dwg
 
 
 def combine(y_perm, y_shared, dest_row, topk_w):

@@ -788,3 +788,46 @@ int oracle_dispatch_backward(int64_t T, int d, int k, int dtype, const void *dx_
     }
     return 0;
 }
+
+/*
+ * Backward of the gate with the top-k choice held fixed (the layer backward
+ * above, its last step, on its own). The renormalised weights of a token
+ * are a softmax over its k chosen logits (the full softmax's normaliser
+ * cancels in p_i / sum_K p_l), so for slot j of token t
+ *   dz[t,j]      = w[t,j] * (dw[t,j] - sum_l w[t,l] dw[t,l])
+ * is the gradient of logit topk_idx[t,j]; every other logit gets zero.
+ * Through z = x Wg^T (+ a constant bias):
+ *   dx_gate[t]   = sum_j dz[t,j] Wg[topk_idx[t,j]]
+ *   dwg[e]      += sum over slots (t,j) with topk_idx[t,j] = e of dz[t,j] x[t]
+ * w and dw are float64; x and Wg float32 or bf16; all sums in float64.
+ * dwg [E,d] is overwritten.
+ */
+int oracle_gate_backward(int64_t T, int d, int E, int k, int dtype, const void *x,
+                         const void *wg, const int32_t *topk_idx, const double *w,
+                         const double *dw, double *dz, double *dx_gate, double *dwg)
+{
+    if (T < 0 || d <= 0 || E <= 0 || k <= 0 || k > E)
+        return -1;
+    for (int64_t i = 0; i < (int64_t)E * d; ++i)
+        dwg[i] = 0.0;
+    for (int64_t t = 0; t < T; ++t) {
+        double mean = 0.0;
+        for (int j = 0; j < k; ++j)
+            mean += w[t * k + j] * dw[t * k + j];
+        double *r = dx_gate + t * d;
+        for (int i = 0; i < d; ++i)
+            r[i] = 0.0;
+        for (int j = 0; j < k; ++j) {
+            int e = topk_idx[t * k + j];
+            if (e < 0 || e >= E)
+                return -2;
+            double g = w[t * k + j] * (dw[t * k + j] - mean);
+            dz[t * k + j] = g;
+            for (int i = 0; i < d; ++i) {
+                r[i] += g * (double)elem(wg, dtype, (int64_t)e * d + i);
+                dwg[(int64_t)e * d + i] += g * (double)elem(x, dtype, t * d + i);
+            }
+        }
+    }
+    return 0;
+}

@@ -202,3 +202,83 @@ def test_combine_backward_weights_match_the_layer_backward():
     _, dw = oracle.combine_backward(dy, Y.astype(np.float32), dest, w.astype(np.float32))
     ref = oracle.layer_backward(inp, toks, dy.astype(np.float64))["dtopk_w"]
     assert _rel(dw, ref) < 1e-6
+
+
+def test_gate_backward_weight_gradient_matches_the_layer_backward():
+    inp = make_inputs(_cfg("f32", T=10, d=12, E=5, k=2, S=0, h=8), seed=7)
+    cfg = inp.cfg
+    toks = np.arange(cfg.T)
+    idx, w, _ = oracle.layer_tokens(inp, toks)
+    dy = np.random.default_rng(8).standard_normal((cfg.T, cfg.d))
+    ref = oracle.layer_backward(inp, toks, dy)
+    _, _, dwg = oracle.gate_backward(inp.x, inp.wg, idx, w, ref["dtopk_w"])
+    assert _rel(dwg, ref["dwg"]) < 1e-12
+
+
+def _renormalised_topk(z, idx):
+    """The renormalised top-k weights from the full softmax (its definition)."""
+    p = np.exp(z - z.max())
+    p /= p.sum()
+    sel = p[idx]
+    return sel / sel.sum()
+
+
+def test_gate_logit_gradient_matches_finite_differences():
+    """dz against central differences of f(z) = sum_j dw_j w_j(z), where w(z)
+    is the full softmax restricted to the chosen experts and renormalised;
+    the logits of unchosen experts must get exactly zero gradient."""
+    rng = np.random.default_rng(9)
+    E, k, d = 7, 3, 4
+    z = rng.standard_normal(E)
+    idx = np.argsort(-z, kind="stable")[:k].astype(np.int32)
+    w = _renormalised_topk(z, idx)
+    dw = rng.standard_normal(k)
+    x = rng.standard_normal((1, d)).astype(np.float32)
+    wg = rng.standard_normal((E, d)).astype(np.float32)
+    dz, _, _ = oracle.gate_backward(x, wg, idx[None, :], w[None, :], dw[None, :])
+    eps = 1e-6
+    for e in range(E):
+        zp, zm = z.copy(), z.copy()
+        zp[e] += eps
+        zm[e] -= eps
+        fd = (dw @ _renormalised_topk(zp, idx) - dw @ _renormalised_topk(zm, idx)) / (2 * eps)
+        pos = np.nonzero(idx == e)[0]
+        got = dz[0, pos[0]] if pos.size else 0.0
+        assert abs(got - fd) < 1e-8, (e, got, fd)
+    assert abs(dz.sum()) < 1e-14
+
+
+def test_gate_backward_top1_has_no_logit_gradient():
+    """With k = 1 the weight is identically one."""
+    rng = np.random.default_rng(10)
+    x = rng.standard_normal((5, 8)).astype(np.float32)
+    wg = rng.standard_normal((4, 8)).astype(np.float32)
+    idx = rng.integers(0, 4, (5, 1)).astype(np.int32)
+    dz, dxg, dwg = oracle.gate_backward(x, wg, idx, np.ones((5, 1)), rng.standard_normal((5, 1)))
+    assert np.all(dz == 0.0) and np.all(dxg == 0.0) and np.all(dwg == 0.0)
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_gate_backward_is_the_gate_gemm_transposed(act):
+    """With dz scattered into a dense [T,E] matrix D: dx_gate = D Wg and
+    dwg = D^T x (the two products of z = x Wg^T, by a library matmul)."""
+    rng = np.random.default_rng(11)
+    T, d, E, k = 37, 24, 9, 3
+    x32 = rng.standard_normal((T, d)).astype(np.float32)
+    wg32 = rng.standard_normal((E, d)).astype(np.float32)
+    if act == "bf16":
+        from moe_workloads import to_bf16_bits
+        x, wg = to_bf16_bits(x32), to_bf16_bits(wg32)
+        xf, wgf = bf16_bits_to_f32(x).astype(np.float64), bf16_bits_to_f32(wg).astype(np.float64)
+    else:
+        x, wg, xf, wgf = x32, wg32, x32.astype(np.float64), wg32.astype(np.float64)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    w = rng.random((T, k)) + 0.1
+    w /= w.sum(axis=1, keepdims=True)
+    dw = rng.standard_normal((T, k))
+    dz, dxg, dwg = oracle.gate_backward(x, wg, idx, w, dw)
+    D = np.zeros((T, E))
+    for t in range(T):
+        D[t, idx[t]] = dz[t]
+    assert _rel(dxg, D @ wgf) < 1e-13
+    assert _rel(dwg, D.T @ xf) < 1e-13
