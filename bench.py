@@ -76,6 +76,10 @@ def algorithmic(cfg, routed=None):
         # backward of dispatch: the row gradients and the shared experts' in,
         # the token gradients out
         "dispatch_backward_bytes": R * d * b + (T * d * b if S else 0) + 4 * T * k + T * d * b,
+        # backward of the gate: dx read and written, x read once, W_gate read,
+        # dW_gate written (float32), w / dw / ids in and the logit gradients out
+        # (the per-range partials of dW_gate are not counted)
+        "gate_backward_bytes": 3 * T * d * b + E * d * b + 4 * E * d + 16 * T * k,
     }
 
 
@@ -129,7 +133,7 @@ def cpu_baseline(cfg, n_tokens):
                       f"1 thread, {dt:.1f} s"}
 
 
-def backward_leg(mm, torch, cfg, shape, buf, stream, A, reps=20):
+def backward_leg(mm, torch, cfg, shape, buf, stream, A, x, wg, reps=20):
     """Time the two data-movement stages of the layer backward on this
     forward's routing: synthetic gradients and expert rows, each launch
     bracketed by its own pair of events (averaged over reps launches)."""
@@ -142,11 +146,16 @@ def backward_leg(mm, torch, cfg, shape, buf, stream, A, reps=20):
     dw = torch.empty((T, k), dtype=torch.float32, device="cuda")
     dx_sh = torch.randn((T, d), device="cuda", generator=g).to(dt) if cfg.S else None
     dx = torch.empty((T, d), dtype=dt, device="cuda")
+    dz = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    dwg = torch.empty((cfg.E, d), dtype=torch.float32, device="cuda")
+    ws_gb = mm.alloc_workspace(shape, mm.STAGE_GATE_BACKWARD)
     calls = {
         "combine_backward": lambda: mm.moe_combine_backward(
             shape, dy, y_perm, buf.dest_row, buf.topk_w, dy_perm, dw, stream),
         "dispatch_backward": lambda: mm.moe_dispatch_backward(
             shape, dy_perm, dx_sh, buf.dest_row, dx, stream),
+        "gate_backward": lambda: mm.moe_gate_backward(
+            shape, x, wg, buf.topk_idx, buf.topk_w, dw, dz, dx, dwg, ws_gb, stream),
     }
     out = {}
     for name, call in calls.items():
@@ -272,7 +281,7 @@ def main():
 
     routed = int(buf.offsets[-1].item())
     A = algorithmic(cfg, routed)
-    bwd = backward_leg(mm, torch, cfg, shape, buf, stream, A)
+    bwd = backward_leg(mm, torch, cfg, shape, buf, stream, A, x, wg)
     t_gate = kmean["gate_topk"]
     t_disp = sum(v for n, v in kmean.items() if n.startswith("dispatch"))
     t_up, t_down = up_ms_timed, kmean["ffn_down"]

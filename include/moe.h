@@ -88,7 +88,8 @@ typedef enum {
     MOE_STAGE_DISPATCH = 1,
     MOE_STAGE_FFN = 2,
     MOE_STAGE_COMBINE = 3,
-    MOE_STAGE_FORWARD = 4
+    MOE_STAGE_FORWARD = 4,
+    MOE_STAGE_GATE_BACKWARD = 5
 } moe_stage;
 
 typedef struct {
@@ -238,6 +239,32 @@ int32_t moe_combine_backward(const moe_shape *s, const void *dy, const void *y_p
  */
 int32_t moe_dispatch_backward(const moe_shape *s, const void *dx_perm, const void *dx_shared,
                               const int32_t *dest_row, void *dx, void *stream);
+
+/*
+ * Backward of the gate ([wmrh] 4.1 and [gsyq] 2.1 gate, [gsyq] 2.4 backward)
+ *  with each token's top-k choice held fixed. The renormalised weights are a
+ *  softmax over the k chosen logits, so for slot j of token t
+ *    dlogits_topk[t,j] = w[t,j] (dw[t,j] - sum_l w[t,l] dw[t,l])   (float32)
+ *  is the gradient of the logit of expert topk_idx[t,j] (all other logits:
+ *  zero; a bias shifts logits by a constant and changes nothing here), with
+ *  w = topk_w, dw = dtopk_w (as from moe_combine_backward; 0 on dropped
+ *  slots). Through z = x w_gate^T:
+ *    dx[t]     = act(dx[t] + sum_j dlogits_topk[t,j] w_gate[topk_idx[t,j]])
+ *                (read, float32 sum in slot order, rounded once; NULL: skipped)
+ *    dw_gate[e] = sum over slots with topk_idx = e of dlogits_topk[t,j] x[t]
+ *                (float32 [E,d], overwritten: summed per range of tokens in
+ *                token order, then over the ranges in order; no atomics, so
+ *                every call gives the same bits).
+ *  ws: MOE_STAGE_GATE_BACKWARD bytes (the per-range partials).
+ *  x [T,d] and w_gate [E,d] (act), topk_idx/topk_w/dtopk_w/dlogits_topk
+ *  [T,k]; all device pointers owned by the caller, 16-byte aligned. Ids
+ *  outside [0,E) contribute nothing. T = 0 only clears dw_gate. Errors:
+ *  MOE_ERR_INVALID_ARG (bad shape, NULL or misaligned pointer), MOE_ERR_HIP.
+ */
+int32_t moe_gate_backward(const moe_shape *s, const void *x, const void *w_gate,
+                          const int32_t *topk_idx, const float *topk_w, const float *dtopk_w,
+                          float *dlogits_topk, void *dx, float *dw_gate, void *ws,
+                          size_t ws_bytes, void *stream);
 
 /*
  * The whole layer: moe_gate_topk -> moe_dispatch -> moe_grouped_ffn ->

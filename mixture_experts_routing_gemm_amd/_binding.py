@@ -27,6 +27,7 @@ MOE_ERR_BAD_INDEX = -5
 
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 STAGE_GATE, STAGE_DISPATCH, STAGE_FFN, STAGE_COMBINE, STAGE_FORWARD = 0, 1, 2, 3, 4
+STAGE_GATE_BACKWARD = 5
 
 _DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
 
@@ -100,6 +101,8 @@ def _load():
     L.moe_combine_backward.restype = i32
     L.moe_dispatch_backward.argtypes = [sp, vp, vp, vp, vp, vp]
     L.moe_dispatch_backward.restype = i32
+    L.moe_gate_backward.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_gate_backward.restype = i32
     L.moe_forward.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_forward.restype = i32
     L.moe_forward_traced.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -118,7 +121,7 @@ lib = _load()
 
 EXPORTS = ["moe_workspace_bytes", "moe_workspace_init", "moe_status_string", "moe_gate_topk",
            "moe_dispatch", "moe_grouped_ffn", "moe_combine", "moe_combine_backward",
-           "moe_dispatch_backward", "moe_forward", "moe_forward_traced",
+           "moe_dispatch_backward", "moe_gate_backward", "moe_forward", "moe_forward_traced",
            "moe_forward_kernel_count", "moe_forward_kernel_name", "moe_get_device_error"]
 
 
@@ -204,6 +207,15 @@ def moe_combine_backward(shape, dy, y_perm, dest_row, topk_w, dy_perm, dtopk_w, 
     _check(lib.moe_combine_backward(ctypes.byref(shape), _p(dy), _p(y_perm), _p(dest_row),
                                     _p(topk_w), _p(dy_perm), _p(dtopk_w), _s(stream)),
            "moe_combine_backward")
+
+
+def moe_gate_backward(shape, x, w_gate, topk_idx, topk_w, dtopk_w, dlogits_topk, dx, dw_gate, ws,
+                      stream=None):
+    wp, wn = _ws(ws)
+    _check(lib.moe_gate_backward(ctypes.byref(shape), _p(x), _p(w_gate), _p(topk_idx), _p(topk_w),
+                                 _p(dtopk_w), _p(dlogits_topk), _p(dx), _p(dw_gate), wp, wn,
+                                 _s(stream)),
+           "moe_gate_backward")
 
 
 def moe_dispatch_backward(shape, dx_perm, dx_shared, dest_row, dx, stream=None):

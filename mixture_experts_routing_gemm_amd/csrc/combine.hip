@@ -19,42 +19,6 @@
 namespace moe {
 
 template <typename TAct>
-struct ActVec;
-
-template <>
-struct ActVec<float> {
-    static constexpr int N = 4;
-    __device__ static void unpack(u32x4 r, float* v) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = __uint_as_float(r[u]);
-    }
-    __device__ static u32x4 pack(const float* v) {
-        u32x4 r;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) r[u] = __float_as_uint(v[u]);
-        return r;
-    }
-};
-
-template <>
-struct ActVec<bf16_t> {
-    static constexpr int N = 8;
-    __device__ static void unpack(u32x4 r, float* v) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            v[2 * u] = bf16_lo(r[u]);
-            v[2 * u + 1] = bf16_hi(r[u]);
-        }
-    }
-    __device__ static u32x4 pack(const float* v) {
-        u32x4 r;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) r[u] = pack_bf16x2(v[2 * u], v[2 * u + 1]);
-        return r;
-    }
-};
-
-template <typename TAct>
 __global__ __launch_bounds__(256) void combine_kernel(
     const TAct* __restrict__ y_perm, const TAct* __restrict__ y_sh,
     const int32_t* __restrict__ dest_row, const float* __restrict__ topk_w, int64_t T, int d,

@@ -1,0 +1,257 @@
+// Backward of the gate, with each token's top-k choice held fixed.
+//
+// The gradients return along the routing path ("Deepseek-MoE同步税本质与四层
+// 实战优化指南", gsyq.cn, section 2.4); the gate's part is the derivative of
+// the renormalised top-k weights (gate, softmax, top-k, renormalise by the
+// selected sum: "DeepSeek 中 MoE 的同步税", wmrh.cn, section 4.1; the top-k
+// gating step of gsyq.cn, section 2.1). Restricted to the
+// chosen experts the full softmax's normaliser cancels, so the weights are a
+// softmax over the k chosen logits and, for slot j of token t,
+//   dz[t,j] = w[t,j] (dw[t,j] - sum_l w[t,l] dw[t,l])
+// is the gradient of logit topk_idx[t,j]; every other logit's gradient is
+// zero. Through z = x Wg^T that sparse dz gives
+//   dx[t]  += sum_j dz[t,j] Wg[topk_idx[t,j]]   (k rows of Wg, L2-resident)
+//   dWg[e]  = sum over slots with topk_idx = e of dz[t,j] x[t].
+// Both are HBM-bound (x and dx are each streamed once), not GEMMs: dz has
+// only k non-zeros per token. dWg is summed per range of tokens in LDS (each
+// sum by one thread, in token order), stored as one float32 partial per
+// range, and the partials are then added in range order: no atomics, and
+// the result is the same on every call.
+#include "moe_device.h"
+
+namespace moe {
+
+// weight-gradient accumulators: E x W float32 in LDS, E * W at most 8192
+// (E <= 128) or 32768 (E <= 256)
+constexpr int kWgradSmall = 8192;
+constexpr int kWgradBig = 32768;
+// tokens whose (expert, dz) pairs are staged in LDS at a time
+constexpr int kWgradStage = 64;
+
+// One wave per token: dz, then dx[t] = act(dx[t] + sum_j dz_j Wg[e_j]) in
+// float32 (slot order, rounded once).
+template <typename TAct>
+__global__ __launch_bounds__(256) void gate_backward_token_kernel(
+    const TAct* __restrict__ wg, const int32_t* __restrict__ topk_idx,
+    const float* __restrict__ topk_w, const float* __restrict__ dtopk_w, int64_t T, int d, int E,
+    int k, float* __restrict__ dz, TAct* __restrict__ dx) {
+    using V = ActVec<TAct>;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + w;
+    if (t >= T) return;
+    int e = -1;
+    float wt = 0.0f, gw = 0.0f;
+    if (lane < k) {
+        e = topk_idx[t * k + lane];
+        wt = topk_w[t * k + lane];
+        gw = dtopk_w[t * k + lane];
+    }
+    float mean = wt * gw;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mean += __shfl_xor(mean, o, kWave);
+    const float g = wt * (gw - mean);
+    if (lane < k) dz[t * k + lane] = g;
+    if (dx == nullptr) return;
+    if (e < 0 || e >= E) e = -1;
+    int ej[kMaxK];
+    float gj[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+        ej[j] = __shfl(e, j, kWave);
+        gj[j] = __shfl(g, j, kWave);
+    }
+    const int nchunk = d / V::N;
+    for (int c = lane; c < nchunk; c += kWave) {
+        const int64_t col = static_cast<int64_t>(c) * V::N;
+        u32x4 src[kMaxK];
+        const u32x4 cur = load16(dx + t * d + col);
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j)
+            if (j < k && ej[j] >= 0) src[j] = load16(wg + static_cast<int64_t>(ej[j]) * d + col);
+        float acc[V::N];
+        V::unpack(cur, acc);
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j) {
+            if (j < k && ej[j] >= 0) {
+                float v[V::N];
+                V::unpack(src[j], v);
+#pragma unroll
+                for (int u = 0; u < V::N; ++u) acc[u] = __builtin_fmaf(gj[j], v[u], acc[u]);
+            }
+        }
+        store16(dx + t * d + col, V::pack(acc));
+    }
+}
+
+// CPL consecutive columns of row p widened to float32 (2 to 16 bytes)
+template <typename TAct, int CPL>
+__device__ __forceinline__ void load_cols(const TAct* p, float* v) {
+    if constexpr (CPL == 1) {
+        if constexpr (sizeof(TAct) == 4)
+            v[0] = *p;
+        else
+            v[0] = bf16_to_f32(*p);
+    } else if constexpr (sizeof(TAct) == 4) {
+        if constexpr (CPL == 4) {
+            const f32x4 r = *reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = r[u];
+        } else {
+            const float2 r = *reinterpret_cast<const float2*>(p);
+            v[0] = r.x;
+            v[1] = r.y;
+        }
+    } else {
+        if constexpr (CPL == 4) {
+            const uint2 r = *reinterpret_cast<const uint2*>(p);
+            v[0] = bf16_lo(r.x);
+            v[1] = bf16_hi(r.x);
+            v[2] = bf16_lo(r.y);
+            v[3] = bf16_hi(r.y);
+        } else {
+            const uint32_t r = *reinterpret_cast<const uint32_t*>(p);
+            v[0] = bf16_lo(r);
+            v[1] = bf16_hi(r);
+        }
+    }
+}
+
+// dWg over a tile of W = 64 * CPL columns and a range of tokens. Lane l of
+// every wave owns columns l*CPL .. l*CPL+CPL-1 of the tile; wave q owns the
+// experts e with e % 4 == q. Each wave walks every token of the range (the
+// rows come from HBM once, the other three waves hit the cache), and the
+// E x W float32 sums in LDS (at e * W + column) each have exactly one owner
+// thread, which adds its slots in token order: plain read-modify-writes, no
+// atomics, the same result on every call. A token's k (expert, dz) pairs
+// are staged at a stride of kMaxK and read with two 16-byte LDS loads each.
+// The tile then goes to this block's partial, part[blockIdx.y][e][column].
+template <typename TAct, int CPL, int ACC>
+__global__ __launch_bounds__(256) void gate_backward_wgrad_kernel(
+    const TAct* __restrict__ x, const int32_t* __restrict__ topk_idx,
+    const float* __restrict__ dz, int64_t T, int d, int E, int k, int64_t per_block,
+    float* __restrict__ part) {
+    constexpr int W = 64 * CPL;
+    constexpr int kAhead = 8;  // rows loaded before they are used
+    __shared__ float acc[ACC];
+    __shared__ __align__(16) int32_t s_e[kWgradStage * kMaxK];
+    __shared__ __align__(16) float s_g[kWgradStage * kMaxK];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int c0 = blockIdx.x * W;
+    const int col = c0 + lane * CPL;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.y) * per_block;
+    const int64_t t1 = t0 + per_block < T ? t0 + per_block : T;
+    for (int i = tid; i < E * W; i += 256) acc[i] = 0.0f;
+    for (int64_t s0 = t0; s0 < t1; s0 += kWgradStage) {
+        const int ns = static_cast<int>(t1 - s0 < kWgradStage ? t1 - s0 : kWgradStage);
+        __syncthreads();  // the accumulator is cleared / the last batch is consumed
+        for (int i = tid; i < ns * kMaxK; i += 256) {
+            const int tt = i / kMaxK, j = i % kMaxK;
+            int32_t e = -1;
+            float g = 0.0f;
+            if (j < k) {
+                e = topk_idx[(s0 + tt) * k + j];
+                g = dz[(s0 + tt) * k + j];
+            }
+            s_e[i] = (e >= 0 && e < E) ? e : -1;
+            s_g[i] = g;
+        }
+        __syncthreads();
+        if (col < d) {
+            for (int tb = 0; tb < ns; tb += kAhead) {
+                float xv[kAhead][CPL];
+#pragma unroll
+                for (int b = 0; b < kAhead; ++b)
+                    if (tb + b < ns) load_cols<TAct, CPL>(x + (s0 + tb + b) * d + col, xv[b]);
+#pragma unroll
+                for (int b = 0; b < kAhead; ++b) {
+                    if (tb + b >= ns) break;
+                    const int4* pe = reinterpret_cast<const int4*>(s_e + (tb + b) * kMaxK);
+                    const f32x4* pg = reinterpret_cast<const f32x4*>(s_g + (tb + b) * kMaxK);
+                    const int4 e0 = pe[0], e1 = pe[1];
+                    const f32x4 g0 = pg[0], g1 = pg[1];
+                    const int ev[kMaxK] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+                    const float gv[kMaxK] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+#pragma unroll
+                    for (int j = 0; j < kMaxK; ++j) {
+                        const int e = ev[j];
+                        if (e < 0 || (e & 3) != wave) continue;
+                        float* a = acc + e * W + lane * CPL;
+#pragma unroll
+                        for (int u = 0; u < CPL; ++u) a[u] = __builtin_fmaf(gv[j], xv[b][u], a[u]);
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+    float* out = part + static_cast<int64_t>(blockIdx.y) * E * d + c0;
+    for (int i = tid; i < E * W; i += 256) {
+        const int e = i / W, c = i % W;
+        if (c0 + c < d) out[static_cast<int64_t>(e) * d + c] = acc[i];
+    }
+}
+
+// dWg = sum of the nchunk partials, in block order (four columns a thread).
+__global__ __launch_bounds__(256) void gate_backward_reduce_kernel(
+    const f32x4* __restrict__ part, int64_t nchunk, int64_t n4, f32x4* __restrict__ dwg) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= n4) return;
+    f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+    int64_t c = 0;
+    for (; c + 8 <= nchunk; c += 8) {
+        f32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = part[(c + u) * n4 + i];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; c < nchunk; ++c) s += part[c * n4 + i];
+    dwg[i] = s;
+}
+
+template <typename TAct>
+void launch_wgrad(const GateWgradGrid& g, const TAct* x, const int32_t* topk_idx, const float* dz,
+                  const moe_shape& s, float* part, hipStream_t st) {
+    const dim3 grid(static_cast<unsigned>(g.nslice), static_cast<unsigned>(g.nchunk));
+    if (g.big)
+        gate_backward_wgrad_kernel<TAct, 2, kWgradBig><<<grid, 256, 0, st>>>(
+            x, topk_idx, dz, s.T, s.d, s.E, s.k, g.per_block, part);
+    else if (g.W == 256)
+        gate_backward_wgrad_kernel<TAct, 4, kWgradSmall><<<grid, 256, 0, st>>>(
+            x, topk_idx, dz, s.T, s.d, s.E, s.k, g.per_block, part);
+    else if (g.W == 128)
+        gate_backward_wgrad_kernel<TAct, 2, kWgradSmall><<<grid, 256, 0, st>>>(
+            x, topk_idx, dz, s.T, s.d, s.E, s.k, g.per_block, part);
+    else
+        gate_backward_wgrad_kernel<TAct, 1, kWgradSmall><<<grid, 256, 0, st>>>(
+            x, topk_idx, dz, s.T, s.d, s.E, s.k, g.per_block, part);
+}
+
+hipError_t launch_gate_backward(const moe_shape& s, const void* x, const void* wg,
+                                const int32_t* topk_idx, const float* topk_w,
+                                const float* dtopk_w, float* dz, void* dx, float* dwg,
+                                float* part, hipStream_t st) {
+    const int64_t T = s.T;
+    const GateWgradGrid g = gate_wgrad_grid(T, s.d, s.E, s.act == MOE_F32 ? 4 : 2);
+    const int64_t n4 = static_cast<int64_t>(s.E) * s.d / 4;
+    if (T > 0) {
+        const unsigned tblocks = static_cast<unsigned>((T + 3) / 4);
+        if (s.act == MOE_F32) {
+            gate_backward_token_kernel<float><<<tblocks, 256, 0, st>>>(
+                static_cast<const float*>(wg), topk_idx, topk_w, dtopk_w, T, s.d, s.E, s.k, dz,
+                static_cast<float*>(dx));
+            launch_wgrad<float>(g, static_cast<const float*>(x), topk_idx, dz, s, part, st);
+        } else {
+            gate_backward_token_kernel<bf16_t><<<tblocks, 256, 0, st>>>(
+                static_cast<const bf16_t*>(wg), topk_idx, topk_w, dtopk_w, T, s.d, s.E, s.k, dz,
+                static_cast<bf16_t*>(dx));
+            launch_wgrad<bf16_t>(g, static_cast<const bf16_t*>(x), topk_idx, dz, s, part, st);
+        }
+    }
+    gate_backward_reduce_kernel<<<static_cast<unsigned>((n4 + 255) / 256), 256, 0, st>>>(
+        reinterpret_cast<const f32x4*>(part), T > 0 ? g.nchunk : 0, n4,
+        reinterpret_cast<f32x4*>(dwg));
+    return hipGetLastError();
+}
+
+}  // namespace moe

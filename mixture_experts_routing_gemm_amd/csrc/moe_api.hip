@@ -28,6 +28,10 @@ size_t ffn_plan_bytes(const moe_shape& s);
 bool ffn_fused_plan(const moe_shape& s, int32_t* plan, FfnPlanArgs* fp);
 hipError_t launch_combine(const moe_shape& s, const void* y_perm, const void* y_sh,
                           const int32_t* dest_row, const float* topk_w, void* y, hipStream_t st);
+hipError_t launch_gate_backward(const moe_shape& s, const void* x, const void* wg,
+                                const int32_t* topk_idx, const float* topk_w,
+                                const float* dtopk_w, float* dz, void* dx, float* dwg,
+                                float* part, hipStream_t st);
 hipError_t launch_combine_backward(const moe_shape& s, const void* dy, const void* y_perm,
                                    const int32_t* dest_row, const float* topk_w, void* dy_perm,
                                    float* dtopk_w, hipStream_t st);
@@ -48,7 +52,7 @@ size_t act_bytes(int32_t dt) { return dt == MOE_F32 ? 4 : (dt == MOE_BF16 ? 2 : 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct Layout {
-    size_t rank = 0, blk = 0, pre = 0, loads = 0, qstats = 0, plan = 0, x_perm = 0, qparams = 0, h_r = 0, h_s = 0, y_perm = 0,
+    size_t part = 0, rank = 0, blk = 0, pre = 0, loads = 0, qstats = 0, plan = 0, x_perm = 0, qparams = 0, h_r = 0, h_s = 0, y_perm = 0,
            y_sh = 0, total = 0;
 };
 
@@ -84,7 +88,12 @@ Layout layout(const moe_shape& s, int stage) {
         L.y_perm = take(T * k * d * es);
         L.y_sh = take(S > 0 ? T * d * es : 0);
     }
-    L.total = (disp || ffn) ? off : 0;
+    if (stage == MOE_STAGE_GATE_BACKWARD) {
+        // one float32 [E, d] partial of the weight gradient per token range
+        const GateWgradGrid g = gate_wgrad_grid(s.T, s.d, s.E, static_cast<int>(es));
+        L.part = take(static_cast<size_t>(g.nchunk > 0 ? g.nchunk : 1) * E * s.d * 4);
+    }
+    L.total = (disp || ffn || stage == MOE_STAGE_GATE_BACKWARD) ? off : 0;
     return L;
 }
 
@@ -189,7 +198,7 @@ const char* const kKernelNames[] = {"gate_topk",  "dispatch_rank", "dispatch_sca
 extern "C" {
 
 size_t moe_workspace_bytes(const moe_shape* s, int32_t stage) {
-    if (stage < MOE_STAGE_GATE || stage > MOE_STAGE_FORWARD) return 0;
+    if (stage < MOE_STAGE_GATE || stage > MOE_STAGE_GATE_BACKWARD) return 0;
     const bool ffn = stage == MOE_STAGE_FFN || stage == MOE_STAGE_FORWARD;
     if (check_shape(s, ffn) != MOE_OK) return 0;
     return layout(*s, stage).total;
@@ -292,6 +301,23 @@ int32_t moe_dispatch_backward(const moe_shape* s, const void* dx_perm, const voi
     // the transpose of copying each row to its k places: combine with unit weights
     return hip_status(launch_combine(*s, dx_perm, dx_shared, dest_row, nullptr, dx,
                                      static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_gate_backward(const moe_shape* s, const void* x, const void* w_gate,
+                          const int32_t* topk_idx, const float* topk_w, const float* dtopk_w,
+                          float* dlogits_topk, void* dx, float* dw_gate, void* ws,
+                          size_t ws_bytes, void* stream) {
+    MOE_TRY(check_shape(s, false));
+    MOE_TRY(check_ptrs({dw_gate}));
+    MOE_TRY(check_ws(*s, MOE_STAGE_GATE_BACKWARD, ws, ws_bytes));
+    const Layout L = layout(*s, MOE_STAGE_GATE_BACKWARD);
+    if (s->T > 0) {
+        MOE_TRY(check_ptrs({x, w_gate, topk_idx, topk_w, dtopk_w, dlogits_topk}));
+        MOE_TRY(check_opt({dx}));
+    }
+    return hip_status(launch_gate_backward(*s, x, w_gate, topk_idx, topk_w, dtopk_w, dlogits_topk,
+                                           s->T > 0 ? dx : nullptr, dw_gate, at<float>(ws, L.part),
+                                           static_cast<hipStream_t>(stream)));
 }
 
 int32_t moe_forward(const moe_shape* s, const void* x, const void* w_gate, const float* bias,

@@ -63,6 +63,43 @@ __device__ __forceinline__ float wave_min(float v) {
     return v;
 }
 
+// Eight bf16 or four float32 values per 16-byte chunk, widened to float32
+template <typename TAct>
+struct ActVec;
+
+template <>
+struct ActVec<float> {
+    static constexpr int N = 4;
+    __device__ static void unpack(u32x4 r, float* v) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = __uint_as_float(r[u]);
+    }
+    __device__ static u32x4 pack(const float* v) {
+        u32x4 r;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) r[u] = __float_as_uint(v[u]);
+        return r;
+    }
+};
+
+template <>
+struct ActVec<bf16_t> {
+    static constexpr int N = 8;
+    __device__ static void unpack(u32x4 r, float* v) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            v[2 * u] = bf16_lo(r[u]);
+            v[2 * u + 1] = bf16_hi(r[u]);
+        }
+    }
+    __device__ static u32x4 pack(const float* v) {
+        u32x4 r;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) r[u] = pack_bf16x2(v[2 * u], v[2 * u + 1]);
+        return r;
+    }
+};
+
 template <int N>
 using ic = std::integral_constant<int, N>;
 
@@ -78,6 +115,38 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 __device__ __forceinline__ void set_error(uint32_t* hdr, uint32_t bit) {
     if (hdr) atomicOr(hdr + kHdrErrorFlag, bit);
+}
+
+// Grid of the gate-backward weight-gradient kernel (host and workspace
+// sizing): tiles of W columns times token ranges of per_block tokens. Up to
+// E = 128 the E x W float32 accumulator takes at most 32 KiB of LDS (four
+// blocks per compute unit); above, 128 KiB (one). Short ranges keep each
+// wave's walk over the tokens short, but every range stores an [E, d]
+// float32 partial: the partials may take as many bytes as x (at least
+// 32 MiB), and aim at about 2048 blocks, 256 tokens or fewer a range.
+struct GateWgradGrid {
+    int W, nslice;
+    bool big;
+    int64_t nchunk, per_block;
+};
+inline GateWgradGrid gate_wgrad_grid(int64_t T, int d, int E, int act_bytes) {
+    GateWgradGrid g;
+    g.big = E > 128;
+    g.W = g.big ? 128 : (E <= 32 ? 256 : (E <= 64 ? 128 : 64));
+    g.nslice = (d + g.W - 1) / g.W;
+    const int64_t x_bytes = T * d * act_bytes;
+    const int64_t budget = x_bytes > (int64_t(32) << 20) ? x_bytes : (int64_t(32) << 20);
+    const int64_t by_budget = budget / (int64_t(E) * d * 4);
+    const int64_t by_blocks = (2048 + g.nslice - 1) / g.nslice;
+    const int64_t by_length = (T + 255) / 256;
+    int64_t n = by_blocks > by_length ? by_blocks : by_length;
+    if (n > by_budget) n = by_budget;
+    const int64_t most = (T + 15) / 16;  // at least 16 tokens a range
+    if (n > most) n = most;
+    if (n < 1) n = 1;
+    g.per_block = (T + n - 1) / n;
+    g.nchunk = g.per_block > 0 ? (T + g.per_block - 1) / g.per_block : 0;
+    return g;
 }
 
 // Host side: optional events recorded on the stream after each kernel, for

@@ -47,6 +47,9 @@ def test_workspace_sizes(mm):
     assert need < fwd < need + (1 << 20)
     assert mm.moe_workspace_bytes(s, mm.STAGE_GATE) == 0
     assert mm.moe_workspace_bytes(s, mm.STAGE_COMBINE) == 0
+    # one float32 [E, d] partial per token range, at least one range
+    gb = mm.moe_workspace_bytes(s, mm.STAGE_GATE_BACKWARD)
+    assert gb >= 256 + s.E * s.d * 4 and gb % 256 == 0
     assert 0 < mm.moe_workspace_bytes(s, mm.STAGE_DISPATCH) < (1 << 20)
     bad = mm.make_shape(4096, 2048, 300, 8, 2, 1408, "bf16")
     assert mm.moe_workspace_bytes(bad, mm.STAGE_FORWARD) == 0

@@ -201,3 +201,110 @@ def test_backward_full_size(name):
     args = (name, cfg.T, cfg.d, cfg.E, cfg.k, cfg.act, 0.0, cfg.capacity, cfg.reassign)
     check_combine_backward(*args, toks=toks)
     check_dispatch_backward(*args, shared=True, toks=toks)
+
+
+# ---------------------------------------------------------------------------
+# Backward of the gate (top-k choice held fixed). Bars, element by element:
+#  * dz = w (dw - sum_l w_l dw_l): a float32 butterfly sum of k products and
+#    two more roundings: |err| <= bz = 10 u w (|dw| + sum_l |w_l dw_l|);
+#  * dx = act(dx0 + sum_j dz_j Wg[e_j]): b|ref| + (k + 3) u sum|terms|, plus
+#    sum_j bz_j |Wg[e_j]| for the error dz carries in;
+#  * dWg[e] = sum of dz x over e's slots in float32 (token order within a
+#    range of tokens, then the ranges' partials in order):
+#    (N_e + 2) u sum|dz x| + sum bz |x|, N_e = slots on expert e; two calls
+#    give the same bits;
+#  * every element of dWg is written (a NaN fill must not survive).
+
+# (name, T, d, E, k, act)
+GATE_CASES = [
+    ("bf16_small", 1000, 512, 16, 4, "bf16"),
+    ("f32_small", 333, 256, 8, 2, "f32"),
+    ("bf16_ragged_cols", 517, 2056, 64, 8, "bf16"),
+    ("bf16_E256", 300, 384, 256, 8, "bf16"),
+    ("bf16_E128", 600, 320, 128, 4, "bf16"),
+    ("f32_E100", 300, 96, 100, 3, "f32"),
+    ("bf16_top1", 200, 128, 8, 1, "bf16"),
+    ("bf16_one_token", 1, 64, 4, 2, "bf16"),
+]
+
+
+def _scatter(idx, vals, E):
+    T, k = idx.shape
+    D = np.zeros((T, E))
+    for j in range(k):
+        D[np.arange(T), idx[:, j]] += vals[:, j]
+    return D
+
+
+def check_gate_backward(name, T, d, E, k, act, with_dx=True, seed=21):
+    mm = _mm()
+    x = make_rows(T, d, act, seed=seed)
+    wg = make_rows(E, d, act, seed=seed + 1)
+    idx = make_routing(T, E, k, seed=seed + 2)
+    w = make_weights(T, k, seed=seed + 3)
+    rng = np.random.default_rng(seed + 4)
+    dw = rng.standard_normal((T, k)).astype(np.float32)
+    dw[rng.random((T, k)) < 0.05] = 0.0  # some slots dropped
+    dx0 = make_rows(T, d, act, seed=seed + 5)
+    shape = mm.make_shape(T, d, E, k, 0, 64, act)
+    dz = torch.full((T, k), float("nan"), dtype=torch.float32, device="cuda")
+    dx = dev(dx0) if with_dx else None
+    dwg = torch.full((E, d), float("nan"), dtype=torch.float32, device="cuda")
+    say(f"[gate-backward {name}] T={T} d={d} E={E} k={k} {act} dx={with_dx}")
+    ws = mm.alloc_workspace(shape, mm.STAGE_GATE_BACKWARD)
+    mm.moe_gate_backward(shape, dev(x), dev(wg), dev(idx), dev(w), dev(dw), dz, dx, dwg, ws)
+    torch.cuda.synchronize()
+
+    z_ref, dxg_ref, dwg_ref = oracle.gate_backward(x, wg, idx, w.astype(np.float64),
+                                                   dw.astype(np.float64))
+    w64, dw64 = w.astype(np.float64), dw.astype(np.float64)
+    bz = 10 * U * w64 * (np.abs(dw64) + np.sum(np.abs(w64 * dw64), axis=1, keepdims=True))
+    gz = host(dz).astype(np.float64)
+    assert np.all(np.abs(gz - z_ref) <= bz), "dz beyond its float32 bound"
+
+    xa, wga = np.abs(as_f64(x)), np.abs(as_f64(wg))
+    if with_dx:
+        ref = as_f64(dx0) + dxg_ref
+        terms = np.abs(as_f64(dx0)) + _scatter(idx, np.abs(z_ref), E) @ wga
+        b = 2.0 ** -8 if act == "bf16" else 0.0
+        bound = b * np.abs(ref) + (k + 3) * U * terms + _scatter(idx, bz, E) @ wga
+        err = np.abs(as_f64(host(dx)) - ref)
+        say(f"[gate-backward {name}] dx max err/bound {np.max(err / np.maximum(bound, 1e-300)):.3f}")
+        assert np.all(err <= bound), "dx beyond its bound"
+
+    got_wg = host(dwg).astype(np.float64)
+    again = torch.full_like(dwg, float("nan"))
+    mm.moe_gate_backward(shape, dev(x), dev(wg), dev(idx), dev(w), dev(dw), dz, None, again, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(again, dwg), "dw_gate differs between two calls"
+    assert np.all(np.isfinite(got_wg)), "dw_gate has unwritten elements"
+    n_e = np.bincount(idx.reshape(-1), minlength=E).astype(np.float64)[:, None]
+    bound = (n_e + 2) * U * (_scatter(idx, np.abs(z_ref), E).T @ xa) + _scatter(idx, bz, E).T @ xa
+    err = np.abs(got_wg - dwg_ref)
+    say(f"[gate-backward {name}] dw_gate max err/bound {np.max(err / np.maximum(bound, 1e-300)):.3f}")
+    assert np.all(err <= bound), "dw_gate beyond its float32 bound"
+
+
+@pytest.mark.parametrize("case", GATE_CASES, ids=[c[0] for c in GATE_CASES])
+def test_gate_backward(case):
+    check_gate_backward(*case)
+
+
+def test_gate_backward_without_dx():
+    check_gate_backward("no_dx", 700, 256, 32, 6, "bf16", with_dx=False)
+
+
+def test_gate_backward_empty_batch_clears_dw_gate():
+    mm = _mm()
+    shape = mm.make_shape(0, 256, 8, 2, 0, 64, "bf16")
+    dwg = torch.full((8, 256), float("nan"), dtype=torch.float32, device="cuda")
+    ws = mm.alloc_workspace(shape, mm.STAGE_GATE_BACKWARD)
+    mm.moe_gate_backward(shape, None, None, None, None, None, None, None, dwg, ws)
+    torch.cuda.synchronize()
+    assert torch.all(dwg == 0).item()
+
+
+@pytest.mark.parametrize("name", ["deepseekmoe_bf16", "coarse_top2_bf16"])
+def test_gate_backward_full_size(name):
+    cfg = CONFIGS[name]
+    check_gate_backward(name, cfg.T, cfg.d, cfg.E, cfg.k, cfg.act)
