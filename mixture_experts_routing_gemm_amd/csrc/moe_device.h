@@ -143,6 +143,7 @@ inline GateWgradGrid gate_wgrad_grid(int64_t T, int d, int E, int act_bytes) {
     if (n > by_budget) n = by_budget;
     const int64_t most = (T + 15) / 16;  // at least 16 tokens a range
     if (n > most) n = most;
+    if (n > 65535) n = 65535;  // the grid's y extent
     if (n < 1) n = 1;
     g.per_block = (T + n - 1) / n;
     g.nchunk = g.per_block > 0 ? (T + g.per_block - 1) / g.per_block : 0;
