@@ -158,10 +158,15 @@ __global__ __launch_bounds__(256) void gate_backward_wgrad_kernel(
         __syncthreads();
         if (col < d) {
             for (int tb = 0; tb < ns; tb += kAhead) {
+                // every load is issued before the first is used: a row past
+                // the batch reloads its last row (in bounds, never used), so
+                // no load sits behind a branch of its own
                 float xv[kAhead][CPL];
 #pragma unroll
-                for (int b = 0; b < kAhead; ++b)
-                    if (tb + b < ns) load_cols<TAct, CPL>(x + (s0 + tb + b) * d + col, xv[b]);
+                for (int b = 0; b < kAhead; ++b) {
+                    const int r = tb + b < ns ? tb + b : ns - 1;
+                    load_cols<TAct, CPL>(x + (s0 + r) * d + col, xv[b]);
+                }
 #pragma unroll
                 for (int b = 0; b < kAhead; ++b) {
                     if (tb + b >= ns) break;
