@@ -131,3 +131,35 @@ def test_traced_forward_needs_enough_events(mm):
     assert mm.moe_forward_kernel_name(mm.make_shape(64, 256, 8, 2, 0, 128, "bf16", "fp8"), 3) == \
         "dispatch_permute_fp8"
     assert mm.moe_forward_kernel_name(s, n) is None
+
+
+def test_backward_entry_points_validate_on_the_host(mm):
+    """The three backward stages reject NULL / misaligned pointers and a
+    missing or short workspace before anything is enqueued; T = 0 is a no-op
+    for the combine and dispatch transposes."""
+    lib = _raw(mm)
+    s = mm.make_shape(64, 256, 8, 2, 0, 128, "bf16")
+    p = ctypes.c_void_p(FAKE)
+    odd = ctypes.c_void_p(FAKE + 4)
+    sp = ctypes.byref(s)
+    # combine backward: every pointer is required
+    assert lib.moe_combine_backward(sp, p, p, p, p, p, None, None) == -1
+    assert lib.moe_combine_backward(sp, odd, p, p, p, p, p, None) == -1
+    assert lib.moe_combine_backward(None, p, p, p, p, p, p, None) == -1
+    # dispatch backward: dx_shared is optional, the rest required
+    assert lib.moe_dispatch_backward(sp, p, None, None, p, None) == -1
+    assert lib.moe_dispatch_backward(sp, p, odd, p, p, None) == -1
+    # gate backward: dw_gate and a workspace are always needed
+    n = mm.moe_workspace_bytes(s, mm.STAGE_GATE_BACKWARD)
+    assert n > 0
+    assert lib.moe_gate_backward(sp, p, p, p, p, p, p, None, None, p, n, None) == -1
+    assert lib.moe_gate_backward(sp, p, p, p, p, p, p, None, p, None, n, None) == -3
+    assert lib.moe_gate_backward(sp, p, p, p, p, p, p, None, p, p, n - 256, None) == -3
+    assert lib.moe_gate_backward(sp, p, p, p, p, p, None, None, p, p, n, None) == -1
+    assert lib.moe_gate_backward(sp, p, p, p, p, p, p, odd, p, p, n, None) == -1
+    # an unsupported shape is refused the same way as by the forward stages
+    bad = mm.make_shape(64, 256, 300, 2, 0, 128, "bf16")
+    assert lib.moe_combine_backward(ctypes.byref(bad), p, p, p, p, p, p, None) == -2
+    z = mm.make_shape(0, 256, 8, 2, 0, 128, "bf16")
+    assert lib.moe_combine_backward(ctypes.byref(z), None, None, None, None, None, None, None) == 0
+    assert lib.moe_dispatch_backward(ctypes.byref(z), None, None, None, None, None) == 0
