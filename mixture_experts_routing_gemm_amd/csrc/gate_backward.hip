@@ -123,9 +123,10 @@ __device__ __forceinline__ void load_cols(const TAct* p, float* v) {
 // E x W float32 sums in LDS (at e * W + column) each have exactly one owner
 // thread, which adds its slots in token order: plain read-modify-writes, no
 // atomics, the same result on every call. A token's k (expert, dz) pairs
-// are staged at a stride of kMaxK and read with two 16-byte LDS loads each.
-// The tile then goes to this block's partial, part[blockIdx.y][e][column].
-template <typename TAct, int CPL, int ACC>
+// are staged at a stride of kMaxK and read with 16-byte LDS loads, KS
+// slots (4 when k <= 4, else 8) a token. The tile then goes to this block's
+// partial, part[blockIdx.y][e][column].
+template <typename TAct, int CPL, int ACC, int KS>
 __global__ __launch_bounds__(256) void gate_backward_wgrad_kernel(
     const TAct* __restrict__ x, const int32_t* __restrict__ topk_idx,
     const float* __restrict__ dz, int64_t T, int d, int E, int k, int64_t per_block,
@@ -172,12 +173,21 @@ __global__ __launch_bounds__(256) void gate_backward_wgrad_kernel(
                     if (tb + b >= ns) break;
                     const int4* pe = reinterpret_cast<const int4*>(s_e + (tb + b) * kMaxK);
                     const f32x4* pg = reinterpret_cast<const f32x4*>(s_g + (tb + b) * kMaxK);
-                    const int4 e0 = pe[0], e1 = pe[1];
-                    const f32x4 g0 = pg[0], g1 = pg[1];
-                    const int ev[kMaxK] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
-                    const float gv[kMaxK] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+                    int ev[KS];
+                    float gv[KS];
 #pragma unroll
-                    for (int j = 0; j < kMaxK; ++j) {
+                    for (int q = 0; q < KS / 4; ++q) {
+                        const int4 eq = pe[q];
+                        const f32x4 gq = pg[q];
+                        ev[4 * q] = eq.x;
+                        ev[4 * q + 1] = eq.y;
+                        ev[4 * q + 2] = eq.z;
+                        ev[4 * q + 3] = eq.w;
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) gv[4 * q + u] = gq[u];
+                    }
+#pragma unroll
+                    for (int j = 0; j < KS; ++j) {
                         const int e = ev[j];
                         if (e < 0 || (e & 3) != wave) continue;
                         float* a = acc + e * W + lane * CPL;
@@ -214,22 +224,31 @@ __global__ __launch_bounds__(256) void gate_backward_reduce_kernel(
     dwg[i] = s;
 }
 
+template <typename TAct, int KS>
+void launch_wgrad_k(const GateWgradGrid& g, const TAct* x, const int32_t* topk_idx,
+                    const float* dz, const moe_shape& s, float* part, hipStream_t st) {
+    const dim3 grid(static_cast<unsigned>(g.nslice), static_cast<unsigned>(g.nchunk));
+    if (g.big)
+        gate_backward_wgrad_kernel<TAct, 2, kWgradBig, KS><<<grid, 256, 0, st>>>(
+            x, topk_idx, dz, s.T, s.d, s.E, s.k, g.per_block, part);
+    else if (g.W == 256)
+        gate_backward_wgrad_kernel<TAct, 4, kWgradSmall, KS><<<grid, 256, 0, st>>>(
+            x, topk_idx, dz, s.T, s.d, s.E, s.k, g.per_block, part);
+    else if (g.W == 128)
+        gate_backward_wgrad_kernel<TAct, 2, kWgradSmall, KS><<<grid, 256, 0, st>>>(
+            x, topk_idx, dz, s.T, s.d, s.E, s.k, g.per_block, part);
+    else
+        gate_backward_wgrad_kernel<TAct, 1, kWgradSmall, KS><<<grid, 256, 0, st>>>(
+            x, topk_idx, dz, s.T, s.d, s.E, s.k, g.per_block, part);
+}
+
 template <typename TAct>
 void launch_wgrad(const GateWgradGrid& g, const TAct* x, const int32_t* topk_idx, const float* dz,
                   const moe_shape& s, float* part, hipStream_t st) {
-    const dim3 grid(static_cast<unsigned>(g.nslice), static_cast<unsigned>(g.nchunk));
-    if (g.big)
-        gate_backward_wgrad_kernel<TAct, 2, kWgradBig><<<grid, 256, 0, st>>>(
-            x, topk_idx, dz, s.T, s.d, s.E, s.k, g.per_block, part);
-    else if (g.W == 256)
-        gate_backward_wgrad_kernel<TAct, 4, kWgradSmall><<<grid, 256, 0, st>>>(
-            x, topk_idx, dz, s.T, s.d, s.E, s.k, g.per_block, part);
-    else if (g.W == 128)
-        gate_backward_wgrad_kernel<TAct, 2, kWgradSmall><<<grid, 256, 0, st>>>(
-            x, topk_idx, dz, s.T, s.d, s.E, s.k, g.per_block, part);
+    if (s.k <= 4)
+        launch_wgrad_k<TAct, 4>(g, x, topk_idx, dz, s, part, st);
     else
-        gate_backward_wgrad_kernel<TAct, 1, kWgradSmall><<<grid, 256, 0, st>>>(
-            x, topk_idx, dz, s.T, s.d, s.E, s.k, g.per_block, part);
+        launch_wgrad_k<TAct, kMaxK>(g, x, topk_idx, dz, s, part, st);
 }
 
 hipError_t launch_gate_backward(const moe_shape& s, const void* x, const void* wg,
