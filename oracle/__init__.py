@@ -60,7 +60,7 @@ def lib():
         L.oracle_expert_rows.argtypes = [i32, i32, i32, i64, vp, vp, vp, vp, vp, vp, i32]
         L.oracle_layer_tokens.argtypes = [i32, i32, i32, i32, i32, i32, i32, i64, vp, vp, vp,
                                           vp, vp, vp, vp, vp, vp, vp, vp, vp, i32]
-        L.oracle_fp8_quantize_ranges.argtypes = [i64, i32, i32, vp, vp, vp, vp]
+        L.oracle_fp8_quantize_ranges.argtypes = [i64, i32, i32, vp, vp, vp, vp, i32]
         L.oracle_combine_backward.argtypes = [i64, i32, i32, i32, vp, vp, vp, vp, i64, vp, vp]
         L.oracle_dispatch_backward.argtypes = [i64, i32, i32, i32, vp, vp, vp, i64, vp]
         L.oracle_gate_backward.argtypes = [i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -174,8 +174,8 @@ def fp8_quantize(x, nthreads=1, ranges=None):
     qp = np.empty((T, 2), dtype=np.float32)
     if ranges is not None:
         r = np.ascontiguousarray(ranges, dtype=np.float32).reshape(T, 2)
-        _check(lib().oracle_fp8_quantize_ranges(T, d, _dtype_code(x), _p(x), _p(r), _p(q), _p(qp)),
-               "fp8_quantize_ranges")
+        _check(lib().oracle_fp8_quantize_ranges(T, d, _dtype_code(x), _p(x), _p(r), _p(q), _p(qp),
+                                                _nthreads(nthreads)), "fp8_quantize_ranges")
         return q, qp
     _check(lib().oracle_fp8_quantize(T, d, _dtype_code(x), _p(x), _p(q), _p(qp),
                                      _nthreads(nthreads)), "fp8_quantize")
@@ -330,3 +330,6 @@ def rows_as_f64(x):
     if x.dtype == np.float32:
         return x.astype(np.float64)
     return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+from .dense import layer_dense, routed_rows, shared_rows, swiglu_rows, token_inputs  # noqa: E402,F401

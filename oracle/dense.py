@@ -1,0 +1,186 @@
+"""Whole-batch form of the oracle's expert stage and layer output (test
+infrastructure only, like the rest of this package).
+
+The per-token oracle (``layer_tokens`` in moe_oracle.c) applies each expert
+FFN to one token row at a time with scalar float64 loops, which is too slow
+for every token of the large workloads. This module computes the same
+definition for all tokens at once, with one float64 matrix product per
+expert over the rows that chose it:
+
+    y[t] = sum_s FFN_{E+s}(x[t]) + sum_j w[t,j] FFN_{e_j}(xq[t]),
+    FFN_g(v) = W2_g (silu(W1_g v) * (W3_g v)),  silu(a) = a / (1 + e^-a)
+
+-- the gate-weighted sum of the chosen experts' outputs of
+"Deepseek-MoE同步税本质与四层实战优化指南" (gsyq.cn), section 2.3, with the
+always-on shared experts of "DeepSeek 中 MoE 的同步税" (wmrh.cn), section 2.1,
+and the FFN applied per expert as the DeepEP notes' expert stage
+(zzszmyf.github.io, section 7). The matrix product is a library step
+(numpy / BLAS in float64); nothing else is blocked or reordered. Gating,
+top-k, the fp8 map and the dispatch order are the C oracle's functions.
+
+Pinned against the per-token C oracle (``layer_tokens``, ``expert_rows``),
+an independent implementation of the same definition, on small cases of
+every workload kind (tests/test_oracle_dense.py).
+"""
+
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+
+def _f64(a):
+    """float32 or bf16-bit-pattern array -> float64 (exact)."""
+    if a.dtype == np.float32:
+        return a.astype(np.float64)
+    return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+class _Threads:
+    """Limits BLAS threads to n within the block (n falsy: leave as is)."""
+
+    def __init__(self, n):
+        self.n = n
+        self.ctx = None
+
+    def __enter__(self):
+        if self.n:
+            try:
+                from threadpoolctl import threadpool_limits
+                self.ctx = threadpool_limits(limits=int(self.n))
+            except ImportError:  # pragma: no cover
+                self.ctx = None
+        return self
+
+    def __exit__(self, *exc):
+        if self.ctx is not None:
+            self.ctx.restore_original_limits()
+        return False
+
+
+def swiglu_rows(v, w1g, w3g, w2g):
+    """FFN of one expert group applied to float64 rows v [n, d] -> [n, d]:
+    W2 (silu(W1 v) * (W3 v)), every product a float64 matrix product."""
+    a = v @ _f64(w1g).T
+    b = v @ _f64(w3g).T
+    with np.errstate(over="ignore"):
+        hmid = a / (1.0 + np.exp(-a)) * b
+    return hmid @ _f64(w2g).T
+
+
+def _dequant(codes, qp):
+    from . import fp8_dequantize
+    return fp8_dequantize(codes, qp)
+
+
+def token_inputs(inp, nthreads=None):
+    """float64 routed-expert input of every token [T, d]: the row itself, or
+    (fp8 dispatch) the row quantised with its own per-token affine map and
+    mapped back as code * scale + centre (gsyq.cn section 3.1)."""
+    from . import fp8_quantize
+    if inp.cfg.dispatch != "fp8":
+        return _f64(inp.x)
+    q, qp = fp8_quantize(inp.x, nthreads=nthreads or 1)
+    return _dequant(q, qp)
+
+
+def routed_input(inp, tokens, ranges=None, xq=None, nthreads=None):
+    """float64 input rows of the routed experts for the given tokens: the
+    rows themselves, or (fp8 dispatch) the rows quantised with the per-token
+    affine map -- or with the given (min, max) ranges [n, 2] -- and mapped
+    back as code * scale + centre (gsyq.cn section 3.1). xq: token_inputs(),
+    used when no ranges are given."""
+    from . import fp8_quantize
+    if ranges is None and xq is not None:
+        return xq[tokens]
+    x = inp.x[tokens]
+    if inp.cfg.dispatch != "fp8":
+        return _f64(x)
+    q, qp = fp8_quantize(x, ranges=ranges, nthreads=nthreads or 1)
+    return _dequant(q, qp)
+
+
+def routed_rows(inp, offsets, src_token, chunk=4096, nthreads=None, qranges=None, xq=None):
+    """The routed experts' output rows in dispatch order, one chunk at a time.
+
+    For expert e the rows offsets[e] .. offsets[e+1]-1 hold the tokens
+    src_token[...] (the dispatch order); each chunk is yielded as
+    (row0, row1, out [row1-row0, d] float64) with out[r] = FFN_e(xq[token]).
+    qranges [rows, 2] (optional, fp8): the (min, max) range each row is
+    quantised with (per-expert or global quantiser modes). xq: token_inputs().
+    """
+    E = len(offsets) - 1
+    with _Threads(nthreads):
+        for e in range(E):
+            lo, hi = int(offsets[e]), int(offsets[e + 1])
+            for r0 in range(lo, hi, chunk):
+                r1 = min(hi, r0 + chunk)
+                toks = np.asarray(src_token[r0:r1], dtype=np.int64)
+                rng = None if qranges is None else qranges[r0:r1]
+                v = routed_input(inp, toks, rng, xq, nthreads)
+                yield r0, r1, swiglu_rows(v, inp.w1[e], inp.w3[e], inp.w2[e])
+
+
+def shared_rows(inp, tokens, nthreads=None):
+    """sum_s FFN_{E+s}(x[t]) for the listed tokens, float64 [n, d]."""
+    cfg = inp.cfg
+    v = _f64(inp.x[tokens])
+    out = np.zeros((len(tokens), cfg.d))
+    with _Threads(nthreads):
+        for s in range(cfg.S):
+            g = cfg.E + s
+            out += swiglu_rows(v, inp.w1[g], inp.w3[g], inp.w2[g])
+    return out
+
+
+def layer_dense(inp, nthreads=None, route=None, qrange=None, chunk=4096, gate=None, xq=None,
+                tokens=None):
+    """Whole-layer output for every token: (topk_idx [T,k], topk_w [T,k]
+    float64, y [T,d] float64), the same quantities as layer_tokens over all
+    tokens.
+
+    route [T,k] (optional): the expert whose row each slot got under a
+    capacity limit, -1 = dropped (contributes nothing; a reassigned slot keeps
+    its gate weight). qrange [T,k,2] (optional, fp8): the (min, max) range of
+    each slot's row. gate (optional): (topk_idx, topk_w) already computed by
+    gate_logits / select_topk for these inputs. xq (optional):
+    token_inputs() for these inputs. tokens (optional): compute only these
+    tokens' outputs (gate, route, qrange and xq still cover the whole
+    batch); the results then have one row per listed token.
+    """
+    from . import gate_logits, select_topk
+    cfg = inp.cfg
+    if gate is None:
+        z = gate_logits(inp.x, inp.wg, inp.bias, nthreads=nthreads or 1)
+        idx, w = select_topk(z, cfg.k)
+    else:
+        idx, w = gate
+    if tokens is not None:
+        tokens = np.asarray(tokens, dtype=np.int64)
+        sub = dataclasses.replace(inp, cfg=cfg.with_tokens(len(tokens)), x=inp.x[tokens])
+        return layer_dense(sub, nthreads, None if route is None else np.asarray(route)[tokens],
+                           None if qrange is None else np.asarray(qrange)[tokens], chunk,
+                           (idx[tokens], w[tokens]), None if xq is None else xq[tokens])
+    T, d, E, k = cfg.T, cfg.d, cfg.E, cfg.k
+    exp_of = idx if route is None else np.asarray(route, dtype=np.int64).reshape(T, k)
+    if xq is None and qrange is None:
+        xq = token_inputs(inp, nthreads)
+    y = np.zeros((T, d))
+    with _Threads(nthreads):
+        for t0 in range(0, T, chunk):
+            t1 = min(T, t0 + chunk)
+            y[t0:t1] += shared_rows(inp, np.arange(t0, t1), nthreads=None)
+        for e in range(E):
+            tt, jj = np.nonzero(exp_of == e)  # token-ascending
+            for c0 in range(0, len(tt), chunk):
+                t_c, j_c = tt[c0:c0 + chunk], jj[c0:c0 + chunk]
+                rng = None if qrange is None else np.asarray(qrange)[t_c, j_c]
+                v = routed_input(inp, t_c, rng, xq, nthreads)
+                out = swiglu_rows(v, inp.w1[e], inp.w3[e], inp.w2[e])
+                contrib = w[t_c, j_c][:, None] * out
+                if np.all(np.diff(t_c) > 0):
+                    y[t_c] += contrib
+                else:  # a reassigned slot may land on an expert its token already has
+                    np.add.at(y, t_c, contrib)
+    return idx, w, y

@@ -349,23 +349,34 @@ int oracle_fp8_quantize_row(int d, const float *xr, uint8_t *q, float *scale,
     return oracle_fp8_quantize_row_range(d, xr, mn, mx, q, scale, centre);
 }
 
-/* rows [T,d] of x, each with its given range ranges[t] = (min, max) */
+/* rows [T,d] of x, each with its given range ranges[t] = (min, max); rows
+ * are independent, so threads change nothing in the result */
 int oracle_fp8_quantize_ranges(int64_t T, int d, int dtype, const void *x,
-                               const float *ranges, uint8_t *q, float *qp)
+                               const float *ranges, uint8_t *q, float *qp,
+                               int nthreads)
 {
     if (T < 0 || d <= 0)
         return -1;
-    float *row = (float *)malloc(sizeof(float) * (size_t)d);
-    if (!row)
-        return -4;
+    if (nthreads < 1)
+        nthreads = 1;
     int rc = 0;
-    for (int64_t t = 0; t < T && rc == 0; ++t) {
-        for (int i = 0; i < d; ++i)
-            row[i] = elem(x, dtype, t * d + i);
-        rc = oracle_fp8_quantize_row_range(d, row, ranges[2 * t], ranges[2 * t + 1],
-                                           q + t * d, &qp[2 * t], &qp[2 * t + 1]);
+#pragma omp parallel num_threads(nthreads)
+    {
+        float *row = (float *)malloc(sizeof(float) * (size_t)d);
+#pragma omp for schedule(dynamic, 64)
+        for (int64_t t = 0; t < T; ++t) {
+            if (!row) {
+                rc = -4;
+                continue;
+            }
+            for (int i = 0; i < d; ++i)
+                row[i] = elem(x, dtype, t * d + i);
+            if (oracle_fp8_quantize_row_range(d, row, ranges[2 * t], ranges[2 * t + 1],
+                                              q + t * d, &qp[2 * t], &qp[2 * t + 1]))
+                rc = -1;
+        }
+        free(row);
     }
-    free(row);
     return rc;
 }
 
