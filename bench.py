@@ -1,38 +1,56 @@
 """Benchmark: one MoE layer forward (gate -> dispatch -> grouped SwiGLU FFN ->
 combine) on one MI355X, through the C ABI.
 
-    python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
-                    [--capacity-factor F [--reassign]] [--quant token|expert|global]
+    python bench.py [--steps K] [--warmup W] [--config NAME] [--detail-configs all|none]
+                    [--no-cpu-baseline] [--capacity-factor F [--reassign]]
+                    [--quant token|expert|global]
     python bench.py --copy-probe-mib N    # counter calibration, see below
+
+Prints ONE JSON line for the headline workload (default: zipf_stress_bf16,
+T=65536, d=4096, E=128 top-4, h=512 -- the largest single-GPU workload by
+tokens and bytes). `value` is routed tokens/s, T / (median time of one layer
+forward), with every input already resident in HBM.
+
+Timing protocol, per step: write 1 GiB of scratch memory (outside the timed
+interval, so the 256 MB Infinity Cache cannot serve the step's inputs from
+the previous step), then run one forward whose first and last kernels are
+bracketed by HIP events recorded by the library on its stream
+(moe_forward_traced). ms_per_step is the median over the K steps, with p10
+and p90 beside it. Two more events in the same steps bracket the dominant
+kernel, the grouped up-projection, whose mean duration gives the roofline
+entry. The other per-kernel durations come from fully traced passes after
+the timed region (each recorded event adds a few microseconds to a pass),
+also with the flush before each.
+
+--detail-configs all (the default) also times the other large workloads
+(deepseekmoe_bf16, coarse_top2_bf16, fp8_dispatch) with the same protocol and
+puts their per-stage figures under detail.workloads.
 
 --capacity-factor F caps every routed expert at ceil(F * T*k / E) rows
 (overflow dropped, or with --reassign handed to the least-loaded expert);
 --quant picks the fp8 rows' range (fp8 workloads only). Both change the
 workload, and config names them.
 
-Prints ONE JSON line. `value` is routed tokens/s (T / time per layer forward)
-with every input already resident in HBM. The library records HIP events on
-its stream between kernels (moe_forward_traced): in the timed steps only the
-two around the dominant kernel, the grouped up-projection (bf16 matrix cores),
-whose mean duration gives the roofline entry; the other per-kernel durations
-come from fully traced passes right after the timed region (every recorded
-event adds a few microseconds to a pass).
 The cpu_baseline leg times the CPU oracle, single-threaded, on a bounded
-sample of the same workload.
+sample of the same batch (token prefixes until at least 10 s of CPU work).
 
-roofline.traffic is the HBM byte count per launch of that kernel measured
-with the FETCH_SIZE and WRITE_SIZE counters (rocprofv3 --pmc, one run each),
-each scaled by what the same counter reads for a plain elementwise kernel of
-known size (--copy-probe-mib: reads N MiB, writes N MiB). The figures live in
-profiles/<kernel>_<workload>_traffic.txt together with the SHA-256 of the
-kernel's source file; when the source has changed since, traffic is null.
+roofline.traffic is the HBM byte count per launch of the up-projection
+measured with the FETCH_SIZE and WRITE_SIZE counters (rocprofv3 --pmc, one
+run each), each scaled by what the same counter reads for a plain elementwise
+kernel of known size (--copy-probe-mib: reads N MiB, writes N MiB). The
+figures live in profiles/traffic_<workload>.txt together with the SHA-256 of
+each kernel's source file; a kernel whose source has changed since gets null.
 """
 
 from __future__ import annotations
 
 import argparse
+import dataclasses
+import hashlib
 import json
+import math
 import os
+import platform
 import sys
 import time
 
@@ -45,6 +63,24 @@ METRIC = "routed tokens/s per MoE layer fwd (1 GPU); dispatch+combine HBM GB/s; 
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 F32_VEC_PEAK_TFLOPS = 157.3
+# the gate's canonical fma chain runs on the non-packed float32 vector units
+F32_NONPACKED_PEAK_TFLOPS = 78.6
+HEADLINE = "zipf_stress_bf16"
+DETAIL_CONFIGS = ["deepseekmoe_bf16", "coarse_top2_bf16", "fp8_dispatch"]
+FLUSH_BYTES = 1 << 30
+
+CSRC = "mixture_experts_routing_gemm_amd/csrc/"
+# kernel name in the forward -> the source file whose hash a traffic figure is tied to
+KERNEL_SOURCES = {
+    "gate_topk": CSRC + "gate_common.h",
+    "dispatch_rank": CSRC + "dispatch.hip",
+    "dispatch_scan": CSRC + "dispatch.hip",
+    "dispatch_permute": CSRC + "dispatch.hip",
+    "dispatch_permute_fp8": CSRC + "dispatch.hip",
+    "ffn_up": CSRC + "grouped_ffn.hip",
+    "ffn_down": CSRC + "grouped_ffn.hip",
+    "combine": CSRC + "combine.hip",
+}
 
 
 def algorithmic(cfg, routed=None):
@@ -69,6 +105,8 @@ def algorithmic(cfg, routed=None):
         "ffn_up_bytes": R * d * bp + S * T * d * b + (E + S) * 2 * h * d * b + rows * h * b
         + (8 * R if cfg.dispatch == "fp8" else 0),
         "ffn_down_flops": 2 * rows * d * h,
+        # hidden rows in, W2 of every group, routed rows and shared sum out
+        "ffn_down_bytes": rows * h * b + (E + S) * d * h * b + R * d * b + (T * d * b if S else 0),
         "combine_bytes": R * d * b + (T * d * b if S else 0) + 8 * T * k + T * d * b,
         # backward of combine: dy once, the forward rows in, their gradients out,
         # routing metadata in and the weight gradients out
@@ -83,27 +121,30 @@ def algorithmic(cfg, routed=None):
     }
 
 
-TRAFFIC_SOURCES = {"ffn_up": "mixture_experts_routing_gemm_amd/csrc/grouped_ffn.hip"}
+def _sha(path):
+    with open(os.path.join(ROOT, path), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic(kernel, workload):
-    """HBM bytes per launch from the committed counter summary, or None if
-    there is none or the kernel's source changed after it was taken."""
-    import hashlib
-    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
-    src = TRAFFIC_SOURCES.get(kernel)
-    if src is None or not os.path.exists(path):
-        return None
-    kv = {}
+def measured_traffic(workload):
+    """{kernel: HBM bytes per launch} from the committed counter summary of
+    the workload, for the kernels whose source is unchanged since."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return {}
+    out = {}
     for line in open(path):
-        if ":" in line and not line.startswith("#"):
-            key, val = line.split(":", 1)
-            kv[key.strip()] = val.strip()
-    with open(os.path.join(ROOT, src), "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
-    if kv.get("kernel_source_sha256") != sha or "traffic_bytes_per_launch" not in kv:
-        return None
-    return int(float(kv["traffic_bytes_per_launch"]))
+        if line.startswith("#") or not line.strip():
+            continue
+        parts = line.split()
+        # kernel  fetch_kib  write_kib  traffic_bytes  source_sha256
+        if len(parts) != 5 or parts[0] == "kernel":
+            continue
+        name, _, _, traffic, sha = parts
+        src = KERNEL_SOURCES.get(name)
+        if src is not None and _sha(src) == sha:
+            out[name] = int(float(traffic))
+    return out
 
 
 def copy_probe(mib):
@@ -119,24 +160,50 @@ def copy_probe(mib):
     print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4}))
 
 
-def cpu_baseline(cfg, n_tokens):
+def host_cpu():
+    model = platform.processor() or "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count()
+    return model, os.cpu_count(), avail
+
+
+def cpu_baseline(inp, min_s=10.0, max_tokens=None):
+    """The oracle's whole layer, one thread, on growing token prefixes of the
+    same batch until at least min_s seconds of CPU work."""
     import oracle
-    from moe_workloads import make_inputs
-    inp = make_inputs(cfg)
-    toks = np.arange(min(n_tokens, cfg.T), dtype=np.int64)
+    cfg = inp.cfg
+    model, ncpu, avail = host_cpu()
+    n, dt = 0, 0.0
+    step = 16
+    cap = cfg.T if max_tokens is None else min(cfg.T, max_tokens)
     t0 = time.perf_counter()
-    oracle.layer_tokens(inp, toks, nthreads=1)
-    dt = time.perf_counter() - t0
-    return {"value": round(len(toks) / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {len(toks)} tokens of the {cfg.name} batch, whole layer per token "
+    while dt < min_s and n < cap:
+        toks = np.arange(n, min(cap, n + step), dtype=np.int64)
+        oracle.layer_tokens(inp, toks, nthreads=1)
+        n += len(toks)
+        dt = time.perf_counter() - t0
+        step = min(step * 2, 256)
+    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} tokens of the {cfg.name} batch, whole layer per token "
                       f"(float32 gate chain, top-k, float64 SwiGLU experts, weighted sum), "
-                      f"1 thread, {dt:.1f} s"}
+                      f"1 thread, {dt:.1f} s",
+            "host_cpu": model, "host_cpus": ncpu, "cpus_available": avail,
+            "cores_used": f"1 of {avail}"}
 
 
 def backward_leg(mm, torch, cfg, shape, buf, stream, A, x, wg, reps=20):
-    """Time the two data-movement stages of the layer backward on this
-    forward's routing: synthetic gradients and expert rows, each launch
-    bracketed by its own pair of events (averaged over reps launches)."""
+    """Time the data-movement stages of the layer backward on this forward's
+    routing: synthetic gradients and expert rows, each launch bracketed by
+    its own pair of events (averaged over reps launches)."""
     T, d, k = cfg.T, cfg.d, cfg.k
     dt = torch.float32 if cfg.act == "f32" else torch.bfloat16
     g = torch.Generator(device="cuda").manual_seed(7)
@@ -174,7 +241,129 @@ def backward_leg(mm, torch, cfg, shape, buf, stream, A, x, wg, reps=20):
         out[name] = {"us": round(ms * 1e3, 2), "GBps": round(gbps, 1),
                      "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
                      "algorithmic_bytes": A[name + "_bytes"]}
+    del dy, y_perm, dy_perm, dx_sh, dx, ws_gb
     return out
+
+
+def _pct(a, q):
+    return round(float(np.percentile(a, q)), 5) if len(a) else None
+
+
+def run_workload(cfg, steps, warmup, flush, with_backward=False, keep_host=False):
+    """Times one workload: K flushed steps with events around the forward and
+    the up-projection, then fully traced passes for the per-kernel split."""
+    import torch
+
+    import mixture_experts_routing_gemm_amd as mm
+    from moe_workloads import make_inputs
+
+    print(f"[bench] generating {cfg.name}", file=sys.stderr, flush=True)
+    inp = make_inputs(cfg)
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    x, wg, w1, w3, w2 = dev(inp.x), dev(inp.wg), dev(inp.w1), dev(inp.w3), dev(inp.w2)
+    bias = None if inp.bias is None else dev(inp.bias)
+    if not keep_host:
+        inp = None
+    shape = mm.shape_of(cfg)
+    buf = mm.ForwardBuffers(shape)
+    nk = mm.moe_forward_kernel_count(shape)
+    names = [mm.moe_forward_kernel_name(shape, i) for i in range(nk)]
+    stream = torch.cuda.current_stream()
+
+    def flush_cache(i):
+        flush.fill_(i & 0xFF)
+
+    for i in range(warmup):
+        flush_cache(i)
+        buf.run(x, wg, bias, w1, w3, w2)
+    torch.cuda.synchronize()
+
+    def make_events(n):
+        """n sets of nk+1 events, created (and recorded once) up front"""
+        out = []
+        for _ in range(n):
+            row = [torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)]
+            for e in row:
+                e.record(stream)
+            out.append(row)
+        torch.cuda.synchronize()
+        return out
+
+    j_up = names.index("ffn_up")
+    keep = (0, j_up, j_up + 1, nk)
+    evs = make_events(steps)
+    handles = [[e.cuda_event if j in keep else None for j, e in enumerate(row)] for row in evs]
+    n_tr = min(steps, 10)
+    evs_tr = make_events(n_tr)
+    handles_tr = [[e.cuda_event for e in row] for row in evs_tr]
+
+    print(f"[bench] {cfg.name}: timing {steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        flush_cache(i)
+        buf.run(x, wg, bias, w1, w3, w2, events=handles[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert mm.moe_get_device_error(buf.ws) == mm.MOE_OK
+    step_ms = np.array([row[0].elapsed_time(row[nk]) for row in evs])
+    up_ms = np.array([row[j_up].elapsed_time(row[j_up + 1]) for row in evs])
+
+    for i in range(n_tr):
+        flush_cache(i)
+        buf.run(x, wg, bias, w1, w3, w2, events=handles_tr[i])
+    torch.cuda.synchronize()
+    per_kernel = np.array([[row[j].elapsed_time(row[j + 1]) for j in range(nk)] for row in evs_tr])
+    kmean = dict(zip(names, per_kernel.mean(axis=0).tolist()))
+
+    routed = int(buf.offsets[-1].item())
+    A = algorithmic(cfg, routed)
+    ms_med = float(np.median(step_ms))
+    t_gate = kmean["gate_topk"]
+    t_disp = sum(v for n, v in kmean.items() if n.startswith("dispatch"))
+    t_up, t_down = float(np.mean(up_ms)), kmean["ffn_down"]
+    t_ffn = t_up + t_down + kmean["ffn_plan"]
+    t_comb = kmean["combine"]
+    gemm_peak = BF16_PEAK_TFLOPS if cfg.act == "bf16" else F32_VEC_PEAK_TFLOPS
+    res = {
+        "T": cfg.T,
+        "value": round(cfg.T / (ms_med * 1e-3), 1),
+        "ms_per_step": round(ms_med, 5),
+        "step_ms_p10_median_p90": [_pct(step_ms, 10), _pct(step_ms, 50), _pct(step_ms, 90)],
+        "wall_s_timed_loop_incl_flush": round(wall, 4),
+        "kernel_ms": {n: round(v, 5) for n, v in kmean.items()},
+        "ffn_up_ms_timed_steps": round(t_up, 5),
+        "gate_us": round(t_gate * 1e3, 2),
+        "gate_tflops": round(A["gate_flops"] / (t_gate * 1e-3) / 1e12, 3),
+        "gate_frac_of_f32_nonpacked_peak": round(A["gate_flops"] / (t_gate * 1e-3) / 1e12
+                                                 / F32_NONPACKED_PEAK_TFLOPS, 4),
+        "gate_GBps": round(A["gate_bytes"] / (t_gate * 1e-3) / 1e9, 1),
+        "dispatch_us": round(t_disp * 1e3, 2),
+        "dispatch_GBps": round(A["dispatch_bytes"] / (t_disp * 1e-3) / 1e9, 1),
+        "dispatch_hbm_frac": round(A["dispatch_bytes"] / (t_disp * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "ffn_us": round(t_ffn * 1e3, 2),
+        "ffn_mfma_frac": round((A["ffn_up_flops"] + A["ffn_down_flops"]) / (t_ffn * 1e-3) / 1e12
+                               / gemm_peak, 4),
+        "ffn_up_mfma_frac": round(A["ffn_up_flops"] / (t_up * 1e-3) / 1e12 / gemm_peak, 4),
+        "ffn_down_mfma_frac": round(A["ffn_down_flops"] / (t_down * 1e-3) / 1e12 / gemm_peak, 4),
+        "combine_us": round(t_comb * 1e3, 2),
+        "combine_GBps": round(A["combine_bytes"] / (t_comb * 1e-3) / 1e9, 1),
+        "combine_hbm_frac": round(A["combine_bytes"] / (t_comb * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "routed_assignments_per_s": round(cfg.T * cfg.k / (ms_med * 1e-3), 1),
+        "dispatched_rows": routed,
+    }
+    extra = {"A": A, "t_up": t_up, "gemm_peak": gemm_peak}
+    if with_backward:
+        res["backward_stages"] = backward_leg(mm, torch, cfg, shape, buf, stream, A, x, wg)
+    del x, wg, w1, w3, w2, bias, buf
+    torch.cuda.empty_cache()
+    return res, extra, inp
 
 
 def main():
@@ -182,9 +371,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="deepseekmoe_bf16")
-    ap.add_argument("--cpu-tokens", type=int, default=96)
+    ap.add_argument("--config", default=HEADLINE)
+    ap.add_argument("--detail-configs", default="all", choices=["all", "none"])
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0)
     ap.add_argument("--capacity-factor", type=float, default=0.0)
     ap.add_argument("--reassign", action="store_true")
@@ -200,11 +391,8 @@ def main():
 
     import torch
 
-    import mixture_experts_routing_gemm_amd as mm
-    from moe_workloads import CONFIGS, make_inputs
+    from moe_workloads import CONFIGS
 
-    import dataclasses
-    import math
     cfg = CONFIGS[args.config]
     if args.capacity_factor > 0:
         cap = math.ceil(args.capacity_factor * cfg.T * cfg.k / cfg.E)
@@ -214,112 +402,38 @@ def main():
             sys.exit("--quant needs a workload with fp8 dispatch")
         cfg = dataclasses.replace(cfg, quant=args.quant)
     torch.cuda.set_device(0)
-    print(f"[bench] generating {cfg.name}", file=sys.stderr, flush=True)
-    inp = make_inputs(cfg)
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
 
-    def dev(a):
-        a = np.ascontiguousarray(a)
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
-        return torch.from_numpy(a).cuda()
-
-    x, wg, w1, w3, w2 = dev(inp.x), dev(inp.wg), dev(inp.w1), dev(inp.w3), dev(inp.w2)
-    bias = None if inp.bias is None else dev(inp.bias)
-    del inp
-    shape = mm.shape_of(cfg)
-    buf = mm.ForwardBuffers(shape)
-    nk = mm.moe_forward_kernel_count(shape)
-    names = [mm.moe_forward_kernel_name(shape, i) for i in range(nk)]
-    stream = torch.cuda.current_stream()
-
-    for _ in range(args.warmup):
-        buf.run(x, wg, bias, w1, w3, w2)
-    torch.cuda.synchronize()
-
-    def make_events(n):
-        """n sets of nk+1 events, created (and recorded once) up front"""
-        out = []
-        for _ in range(n):
-            row = [torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)]
-            for e in row:
-                e.record(stream)
-            out.append(row)
-        torch.cuda.synchronize()
-        return out
-
-    # Timed steps record only the two events around the up-projection (each
-    # recorded event adds a few microseconds to a pass); the per-kernel
-    # breakdown comes from fully traced passes after the timed region.
-    j_up = names.index("ffn_up")
-    evs = make_events(args.steps)
-    handles = [[e.cuda_event if j in (j_up, j_up + 1) else None for j, e in enumerate(row)]
-               for row in evs]
-    n_tr = min(args.steps, 10)
-    evs_tr = make_events(n_tr)
-    handles_tr = [[e.cuda_event for e in row] for row in evs_tr]
-
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        buf.run(x, wg, bias, w1, w3, w2, events=handles[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    assert mm.moe_get_device_error(buf.ws) == mm.MOE_OK
-    up_ms_timed = float(np.mean([row[j_up].elapsed_time(row[j_up + 1]) for row in evs]))
-    # consecutive up-projection starts are one forward apart: the spread of
-    # the timed steps without further events
-    steps_ms = np.array([evs[i][j_up].elapsed_time(evs[i + 1][j_up]) for i in range(len(evs) - 1)])
-
-    for i in range(n_tr):
-        buf.run(x, wg, bias, w1, w3, w2, events=handles_tr[i])
-    torch.cuda.synchronize()
-    per_kernel = np.array([[row[j].elapsed_time(row[j + 1]) for j in range(nk)] for row in evs_tr])
-    step_ms = np.array([row[0].elapsed_time(row[nk]) for row in evs_tr])
-    kmean = dict(zip(names, per_kernel.mean(axis=0).tolist()))
-    ms_per_step = wall * 1000.0 / args.steps
-
-    routed = int(buf.offsets[-1].item())
-    A = algorithmic(cfg, routed)
-    bwd = backward_leg(mm, torch, cfg, shape, buf, stream, A, x, wg)
-    t_gate = kmean["gate_topk"]
-    t_disp = sum(v for n, v in kmean.items() if n.startswith("dispatch"))
-    t_up, t_down = up_ms_timed, kmean["ffn_down"]
-    t_ffn = t_up + t_down + kmean["ffn_plan"]
-    t_comb = kmean["combine"]
-    up_tflops = A["ffn_up_flops"] / (t_up * 1e-3) / 1e12
-    gemm_peak = BF16_PEAK_TFLOPS if cfg.act == "bf16" else F32_VEC_PEAK_TFLOPS
-    detail = {
-        "kernel_ms": {n: round(v, 5) for n, v in kmean.items()},
-        "kernel_ms_from": f"{n_tr} fully traced passes after the timed region (ffn_up: timed steps)",
-        "ffn_up_ms_timed_steps": round(up_ms_timed, 5),
-        "step_ms_events_median": round(float(np.median(step_ms)), 5),
-        "timed_step_ms_p10_median_p90": ([round(float(np.percentile(steps_ms, q)), 5) for q in (10, 50, 90)]
-                                         if len(steps_ms) else None),
-        "gate_us": round(t_gate * 1e3, 2),
-        "gate_tflops": round(A["gate_flops"] / (t_gate * 1e-3) / 1e12, 3),
-        "dispatch_us": round(t_disp * 1e3, 2),
-        "dispatch_GBps": round(A["dispatch_bytes"] / (t_disp * 1e-3) / 1e9, 1),
-        "dispatch_hbm_frac": round(A["dispatch_bytes"] / (t_disp * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-        "ffn_us": round(t_ffn * 1e3, 2),
-        "ffn_mfma_frac": round((A["ffn_up_flops"] + A["ffn_down_flops"]) / (t_ffn * 1e-3) / 1e12
-                               / gemm_peak, 4),
-        "ffn_down_tflops": round(A["ffn_down_flops"] / (t_down * 1e-3) / 1e12, 1),
-        "combine_us": round(t_comb * 1e3, 2),
-        "combine_GBps": round(A["combine_bytes"] / (t_comb * 1e-3) / 1e9, 1),
-        "combine_hbm_frac": round(A["combine_bytes"] / (t_comb * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-        "routed_assignments_per_s": round(cfg.T * cfg.k / (ms_per_step * 1e-3), 1),
-        "dispatched_rows": routed,
-        "backward_stages": bwd,
-    }
+    res, ex, inp = run_workload(cfg, args.steps, args.warmup, flush,
+                                with_backward=not args.no_backward,
+                                keep_host=not args.no_cpu_baseline)
+    A = ex["A"]
+    up_tflops = A["ffn_up_flops"] / (ex["t_up"] * 1e-3) / 1e12
+    plain = not cfg.capacity and cfg.quant == "token"
+    traffic = measured_traffic(cfg.name) if plain else {}
+    detail = dict(res)
+    for key in ("value", "ms_per_step", "T"):
+        detail.pop(key)
+    detail["timing"] = (f"per step: 1 GiB scratch write outside the timed interval, then one "
+                        f"forward between HIP events recorded on the library's stream; "
+                        f"ms_per_step = median of {args.steps} steps; kernel_ms from "
+                        f"{min(args.steps, 10)} fully traced passes (ffn_up: the timed steps)")
+    detail["traffic_bytes_per_launch"] = traffic or None
+    detail["algorithmic"] = {k: v for k, v in A.items() if not k.endswith("backward_bytes")}
+    if args.detail_configs == "all" and args.config == HEADLINE and plain:
+        detail["workloads"] = {}
+        for name in DETAIL_CONFIGS:
+            r, _, _ = run_workload(CONFIGS[name], max(5, args.steps // 2), max(2, args.warmup // 2),
+                                   flush)
+            detail["workloads"][name] = r
     out = {
         "metric": METRIC,
-        "value": round(cfg.T / (ms_per_step * 1e-3), 1),
+        "value": res["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": res["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -334,19 +448,17 @@ def main():
             "kernel": "ffn_up",
             "bound": "mfma",
             "achieved": round(up_tflops, 2),
-            "peak": gemm_peak,
+            "peak": ex["gemm_peak"],
             "unit": "TFLOP/s",
-            "frac": round(up_tflops / gemm_peak, 4),
-            # counters were taken on the plain workload only
-            "traffic": (measured_traffic("ffn_up", cfg.name)
-                        if not cfg.capacity and cfg.quant == "token" else None),
+            "frac": round(up_tflops / ex["gemm_peak"], 4),
+            "traffic": traffic.get("ffn_up"),
             "algorithmic_bytes": A["ffn_up_bytes"],
         },
         "detail": detail,
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_tokens)
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

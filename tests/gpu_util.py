@@ -49,6 +49,42 @@ def rel_l2(got, ref) -> float:
     return float(np.linalg.norm(got - ref) / (den if den > 0 else 1.0))
 
 
+class RowErrors:
+    """Relative L2 over a whole tensor, accumulated chunk by chunk, and the
+    worst single row's relative L2."""
+
+    def __init__(self):
+        self.num = 0.0
+        self.den = 0.0
+        self.worst = 0.0
+        self.worst_row = -1
+        self.rows = 0
+
+    def add(self, got, ref, row0=0):
+        g = as_f64(np.asarray(got))
+        r = np.asarray(ref, dtype=np.float64)
+        dn = np.sum((g - r) ** 2, axis=1)
+        rn = np.sum(r ** 2, axis=1)
+        self.num += float(dn.sum())
+        self.den += float(rn.sum())
+        per = np.sqrt(dn / np.where(rn > 0, rn, 1.0))
+        i = int(np.argmax(per))
+        if per[i] > self.worst:
+            self.worst, self.worst_row = float(per[i]), row0 + i
+        self.rows += len(r)
+
+    @property
+    def rel(self):
+        return float(np.sqrt(self.num / self.den)) if self.den > 0 else float(np.sqrt(self.num))
+
+    def check(self, what, tol):
+        say(f"{what}: rel-L2 {self.rel:.3e} over {self.rows} rows, worst row {self.worst_row} "
+            f"{self.worst:.3e} (bound {tol:.0e})")
+        assert self.rows > 0
+        assert self.rel <= tol, f"{what}: rel-L2 {self.rel:.3e} > {tol}"
+        assert self.worst <= tol, f"{what}: row {self.worst_row} rel-L2 {self.worst:.3e} > {tol}"
+
+
 def act_torch(act: str):
     return torch.float32 if act == "f32" else torch.bfloat16
 

@@ -17,7 +17,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import ORACLE_THREADS, dev, host, rel_l2, requires_gpu, say
+from gpu_util import ORACLE_THREADS, RowErrors, dev, host, rel_l2, requires_gpu, say
 from moe_workloads import CONFIGS, bf16_bits_to_f32, make_inputs
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
@@ -51,6 +51,15 @@ def group_ranges(xf, offsets, src, quant):
             rows = xf[src[a:b]]
             r[a:b] = (rows.min(), rows.max())
     return r
+
+
+def qrange_of(rr, dest):
+    """(min, max) range [T,k,2] of each slot's row (zeros for a dropped slot)"""
+    T, k = dest.shape
+    q = np.zeros((T, k, 2), dtype=np.float32)
+    kept = dest >= 0
+    q[kept] = rr[dest[kept]]
+    return q
 
 
 def run_case(cfg, toks=None):
@@ -96,16 +105,12 @@ def run_case(cfg, toks=None):
     assert np.array_equal(host(buf.dest_row), dest)
     if toks is None:
         toks = np.arange(T)
-    qrange = np.zeros((len(toks), k, 2), dtype=np.float32)
-    for i, t in enumerate(toks):
-        for j in range(k):
-            if dest[t, j] >= 0:
-                qrange[i, j] = rr[dest[t, j]]
-    _, _, oy = oracle.layer_tokens(inp, toks, nthreads=ORACLE_THREADS, route=route[toks],
-                                   qrange=qrange)
-    err = rel_l2(host(buf.y)[toks], oy)
-    say(f"[fp8 modes] y rel-L2 {err:.3e}")
-    assert err <= cfg.tol_y
+    qrange_all = qrange_of(rr, dest)
+    _, _, oy = oracle.layer_dense(inp, nthreads=ORACLE_THREADS, route=route, qrange=qrange_all,
+                                  tokens=toks)
+    acc = RowErrors()
+    acc.add(host(buf.y)[toks], oy)
+    acc.check(f"[fp8 modes] y on {len(toks)} tokens", cfg.tol_y)
 
 
 @pytest.mark.parametrize("quant", ["expert", "global"])
@@ -131,7 +136,7 @@ def test_token_mode_is_the_default_path():
 def test_full_size_fp8_workload_per_expert_ranges():
     # fp8_dispatch at its full size with per-expert ranges, as bench.py
     # --quant expert times it: the dispatch arrays bit-exact, the codes and
-    # (scale, centre) of sampled dispatched rows bit-exact, y on sampled tokens
+    # (scale, centre) of sampled dispatched rows bit-exact, y on 4096 tokens
     mm = _mm()
     cfg = dataclasses.replace(CONFIGS["fp8_dispatch"], quant="expert")
     say(f"[fp8 modes] full size T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} quant=expert")
@@ -169,9 +174,12 @@ def test_full_size_fp8_workload_per_expert_ranges():
     torch.cuda.synchronize()
     assert mm.moe_get_device_error(buf.ws) == mm.MOE_OK
     assert np.array_equal(host(buf.dest_row), dest)
-    toks = np.array([0, 1, 777, 16384, T - 1], dtype=np.int64)
-    qrange = np.stack([[rr[dest[t, j]] for j in range(k)] for t in toks]).astype(np.float32)
-    _, _, oy = oracle.layer_tokens(inp, toks, nthreads=ORACLE_THREADS, qrange=qrange)
-    err = rel_l2(host(buf.y)[toks], oy)
-    say(f"[fp8 modes] full size y rel-L2 {err:.3e}")
-    assert err <= cfg.tol_y
+    # y on 4096 tokens: a contiguous run, random ones and the ends
+    rng = np.random.default_rng(3)
+    toks = np.unique(np.concatenate([np.arange(1000, 3048), rng.integers(0, T, 2048),
+                                     [0, 1, T - 1]])).astype(np.int64)
+    _, _, oy = oracle.layer_dense(inp, nthreads=ORACLE_THREADS, qrange=qrange_of(rr, dest),
+                                  tokens=toks, gate=(oidx, ow))
+    acc = RowErrors()
+    acc.add(host(buf.y)[toks], oy)
+    acc.check(f"[fp8 modes] full size y on {len(toks)} tokens", cfg.tol_y)
