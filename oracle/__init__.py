@@ -332,4 +332,5 @@ def rows_as_f64(x):
     return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-from .dense import layer_dense, routed_rows, shared_rows, swiglu_rows, token_inputs  # noqa: E402,F401
+from .dense import (ffn_backward, layer_dense, routed_rows, shared_rows, swiglu_rows,  # noqa: E402,F401
+                    token_inputs)

@@ -31,7 +31,9 @@ import numpy as np
 
 
 def _f64(a):
-    """float32 or bf16-bit-pattern array -> float64 (exact)."""
+    """float64, float32 or bf16-bit-pattern array -> float64 (exact)."""
+    if a.dtype == np.float64:
+        return a
     if a.dtype == np.float32:
         return a.astype(np.float64)
     return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
@@ -184,3 +186,72 @@ def layer_dense(inp, nthreads=None, route=None, qrange=None, chunk=4096, gate=No
                 else:  # a reassigned slot may land on an expert its token already has
                     np.add.at(y, t_c, contrib)
     return idx, w, y
+
+
+def _swiglu_backward_rows(v, g, w1g, w3g, w2g):
+    """Backward of one expert group's FFN over float64 rows v [n, d] with
+    output gradients g [n, d]: (dv [n, d], dW1 [h, d], dW3 [h, d], dW2 [d, h]).
+
+    Forward: a = W1 v, b = W3 v, u = silu(a) = a sigma(a), hid = u b,
+    y = W2 hid. Backward by the chain rule: dhid = W2^T g, da = dhid b silu'(a)
+    with silu'(a) = sigma(a) (1 + a (1 - sigma(a))), db = dhid u,
+    dv = W1^T da + W3^T db; dW2 = g hid^T, dW1 = da v^T, dW3 = db v^T, summed
+    over the rows."""
+    W1, W3, W2 = _f64(w1g), _f64(w3g), _f64(w2g)
+    a = v @ W1.T
+    b = v @ W3.T
+    with np.errstate(over="ignore"):
+        sg = 1.0 / (1.0 + np.exp(-a))
+    u = a * sg
+    hid = u * b
+    dhid = g @ W2
+    da = dhid * b * (sg * (1.0 + a * (1.0 - sg)))
+    db = dhid * u
+    dv = da @ W1 + db @ W3
+    return dv, da.T @ v, db.T @ v, g.T @ hid
+
+
+def ffn_backward(inp, offsets, src_token, dy_perm, dy_shared=None, xq=None, nthreads=None,
+                 chunk=4096):
+    """Backward of the grouped expert FFN stage alone, every row at once.
+
+    The routed rows offsets[e] .. offsets[e+1]-1 hold the tokens
+    src_token[...] (dispatch order) with input xq[token] (token_inputs: the
+    fp8 rows dequantised; the quantiser passes the gradient straight through)
+    and output gradient dy_perm[row]; the shared experts see every token's x
+    with output gradient dy_shared[t] (the layer output's gradient, weight 1).
+    Returns float64 dict(dx_perm [R, d], dx_shared [T, d] or None (the sum
+    over the shared experts), dw1 / dw3 [E+S, h, d], dw2 [E+S, d, h]) --
+    the gradients returning through the expert stage ("Deepseek-MoE同步税本质与
+    四层实战优化指南", gsyq.cn, section 2.4: the backward pass runs the
+    exchanges in reverse, the expert computation between them)."""
+    cfg = inp.cfg
+    E, S, d, h, T = cfg.E, cfg.S, cfg.d, cfg.h, cfg.T
+    if xq is None:
+        xq = token_inputs(inp, nthreads)
+    R = int(offsets[E])
+    out = dict(dx_perm=np.zeros((R, d)), dx_shared=np.zeros((T, d)) if S else None,
+               dw1=np.zeros((E + S, h, d)), dw3=np.zeros((E + S, h, d)), dw2=np.zeros((E + S, d, h)))
+    with _Threads(nthreads):
+        for e in range(E):
+            for r0 in range(int(offsets[e]), int(offsets[e + 1]), chunk):
+                r1 = min(int(offsets[e + 1]), r0 + chunk)
+                v = xq[np.asarray(src_token[r0:r1], dtype=np.int64)]
+                g = _f64(np.ascontiguousarray(dy_perm[r0:r1]))
+                dv, d1, d3, d2 = _swiglu_backward_rows(v, g, inp.w1[e], inp.w3[e], inp.w2[e])
+                out["dx_perm"][r0:r1] = dv
+                out["dw1"][e] += d1
+                out["dw3"][e] += d3
+                out["dw2"][e] += d2
+        for s in range(S):
+            gi = E + s
+            for t0 in range(0, T, chunk):
+                t1 = min(T, t0 + chunk)
+                v = _f64(inp.x[t0:t1])
+                g = _f64(np.ascontiguousarray(dy_shared[t0:t1]))
+                dv, d1, d3, d2 = _swiglu_backward_rows(v, g, inp.w1[gi], inp.w3[gi], inp.w2[gi])
+                out["dx_shared"][t0:t1] += dv
+                out["dw1"][gi] += d1
+                out["dw3"][gi] += d3
+                out["dw2"][gi] += d2
+    return out

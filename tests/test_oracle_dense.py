@@ -129,3 +129,39 @@ def test_token_subset_equals_rows_of_the_whole_batch():
     i2, w2, y2 = oracle.layer_dense(inp, tokens=toks, gate=(idx, w))
     assert np.array_equal(i2, idx[toks]) and np.array_equal(w2, w[toks])
     assert _rel(y2, y[toks]) <= REL
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("deepseekmoe_bf16", dict(T=60, d=64, h=40, E=6, k=3, S=2)),
+    ("fp8_dispatch", dict(T=50, d=48, h=24, E=5, k=2, S=1)),
+    ("tiny_fp32", dict(T=40, d=16, h=12, E=4, k=2)),
+])
+def test_ffn_backward_matches_the_layer_backward(name, kw):
+    """The expert stage's backward, fed the gradient that combine's backward
+    hands it (w * dy for each kept slot's row, dy itself for the shared
+    experts), gives the layer backward's expert weight gradients; and its row
+    gradients, summed back per token (dispatch's backward) plus the gate's
+    term, give the layer backward's dx."""
+    cfg = dataclasses.replace(CONFIGS[name], sigma_w=0.2, **kw)
+    inp = make_inputs(cfg, seed=11)
+    T, k = cfg.T, cfg.k
+    dy = np.random.default_rng(3).standard_normal((T, cfg.d))
+    ref = oracle.layer_backward(inp, np.arange(T), dy)
+    z = oracle.gate_logits(inp.x, inp.wg, inp.bias)
+    idx, w = oracle.select_topk(z, k)
+    counts, offsets, dest, src = oracle.dispatch(idx, cfg.E)
+    dy_perm = np.zeros((int(offsets[-1]), cfg.d))
+    for t in range(T):
+        for j in range(k):
+            dy_perm[dest[t, j]] = w[t, j] * dy[t]
+    got = oracle.ffn_backward(inp, offsets, src, dy_perm, dy if cfg.S else None)
+    for key in ("dw1", "dw3", "dw2"):
+        assert _rel(got[key], ref[key]) <= 1e-11, key
+    dx = np.zeros((T, cfg.d))
+    for t in range(T):
+        for j in range(k):
+            dx[t] += got["dx_perm"][dest[t, j]]
+    if cfg.S:
+        dx += got["dx_shared"]
+    _, dxg, _ = oracle.gate_backward(inp.x, inp.wg, idx, w, ref["dtopk_w"])
+    assert _rel(dx + dxg, ref["dx"]) <= 1e-11
