@@ -50,9 +50,12 @@
  *    flag in the workspace is set; moe_get_device_error reports it.
  *
  * Shape limits: 1 <= E <= 256, 1 <= k <= min(E, 8), 0 <= S <= 8, T >= 0,
- * T*k < 2^31 and T*S < 2^31. act = MOE_F32: d % 4 == 0. act = MOE_BF16:
- * d % 128 == 0 and h % 64 == 0 (the expert GEMM tiles). dispatch must equal
- * act, or be MOE_FP8_E4M3 with act = MOE_BF16.
+ * T*k < 2^31 and T*S < 2^31, d and h at most 2^20. act = MOE_F32: d % 4 ==
+ * 0. act = MOE_BF16: d % 8 == 0 (d % 16 with fp8 rows), so that every row
+ * moves as 16-byte pieces; any h >= 1. dispatch must equal act, or be
+ * MOE_FP8_E4M3 with act = MOE_BF16. (Shapes with d % 256 == 0 and h % 128
+ * == 0 take the persistent large-tile expert GEMMs; the others a 128 x 128
+ * tile kernel.)
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -89,7 +92,8 @@ typedef enum {
     MOE_STAGE_FFN = 2,
     MOE_STAGE_COMBINE = 3,
     MOE_STAGE_FORWARD = 4,
-    MOE_STAGE_GATE_BACKWARD = 5
+    MOE_STAGE_GATE_BACKWARD = 5,
+    MOE_STAGE_FFN_BACKWARD = 6
 } moe_stage;
 
 typedef struct {
@@ -265,6 +269,38 @@ int32_t moe_gate_backward(const moe_shape *s, const void *x, const void *w_gate,
                           const int32_t *topk_idx, const float *topk_w, const float *dtopk_w,
                           float *dlogits_topk, void *dx, float *dw_gate, void *ws,
                           size_t ws_bytes, void *stream);
+
+/*
+ * Backward of the grouped SwiGLU expert FFN ([gsyq] 2.4: the gradients go
+ *  back along the forward's routing, through the experts' own computation
+ *  between the transposes of combine and dispatch). For routed expert e and
+ *  each row r of offsets[e]..offsets[e+1]-1 with input v = x_perm[r] (fp8
+ *  rows dequantised as in moe_grouped_ffn; the quantiser passes the gradient
+ *  straight through) and output gradient g = dy_perm[r] (as written by
+ *  moe_combine_backward):
+ *    a = W1_e v, b = W3_e v, u = silu(a), hid = u * b  (recomputed, bf16)
+ *    dhid = W2_e^T g;  da = dhid * b * s (1 + a (1 - s)), s = sigmoid(a);
+ *    db = dhid * u;  dx_perm[r] = W1_e^T da + W3_e^T db     (bf16 [T*k, d])
+ *    dW2_e = sum_r g hid^T, dW1_e = sum_r da v^T, dW3_e = sum_r db v^T
+ *  The shared experts (S > 0) do the same for every token t with input
+ *  x[t] and output gradient dy_shared[t] (the layer output's gradient);
+ *  dx_shared[t] (bf16 [T, d]) is the sum over the shared experts.
+ *  dw1, dw3 [E+S, h, d] and dw2 [E+S, d, h] are float32 and overwritten
+ *  (zero for an expert with no rows); each element is summed over the
+ *  group's rows in order by one work-group (no atomics: every call gives
+ *  the same bits). moe_dispatch_backward then sums dx_perm and dx_shared
+ *  back per token. act must be MOE_BF16 (MOE_ERR_UNSUPPORTED otherwise);
+ *  x, dy_shared and dx_shared are required iff S > 0 (else NULL); qparams
+ *  iff the rows are fp8. ws: MOE_STAGE_FFN_BACKWARD bytes (the recomputed
+ *  a, b, hid and the gradients da, db of every row). T = 0 only zeroes the
+ *  weight gradients. Errors as for moe_grouped_ffn.
+ */
+int32_t moe_grouped_ffn_backward(const moe_shape *s, const void *x_perm, const float *qparams,
+                                 const int32_t *offsets, const void *x, const void *w1,
+                                 const void *w3, const void *w2, const void *dy_perm,
+                                 const void *dy_shared, void *dx_perm, void *dx_shared,
+                                 float *dw1, float *dw3, float *dw2, void *ws, size_t ws_bytes,
+                                 void *stream);
 
 /*
  * The whole layer: moe_gate_topk -> moe_dispatch -> moe_grouped_ffn ->

@@ -28,6 +28,7 @@ MOE_ERR_BAD_INDEX = -5
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 STAGE_GATE, STAGE_DISPATCH, STAGE_FFN, STAGE_COMBINE, STAGE_FORWARD = 0, 1, 2, 3, 4
 STAGE_GATE_BACKWARD = 5
+STAGE_FFN_BACKWARD = 6
 
 _DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
 
@@ -102,6 +103,9 @@ def _load():
     L.moe_dispatch_backward.argtypes = [sp, vp, vp, vp, vp, vp]
     L.moe_dispatch_backward.restype = i32
     L.moe_gate_backward.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_grouped_ffn_backward.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                           vp, vp, sz, vp]
+    L.moe_grouped_ffn_backward.restype = i32
     L.moe_gate_backward.restype = i32
     L.moe_forward.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_forward.restype = i32
@@ -121,7 +125,7 @@ lib = _load()
 
 EXPORTS = ["moe_workspace_bytes", "moe_workspace_init", "moe_status_string", "moe_gate_topk",
            "moe_dispatch", "moe_grouped_ffn", "moe_combine", "moe_combine_backward",
-           "moe_dispatch_backward", "moe_gate_backward", "moe_forward", "moe_forward_traced",
+           "moe_dispatch_backward", "moe_gate_backward", "moe_grouped_ffn_backward", "moe_forward", "moe_forward_traced",
            "moe_forward_kernel_count", "moe_forward_kernel_name", "moe_get_device_error"]
 
 
@@ -216,6 +220,15 @@ def moe_gate_backward(shape, x, w_gate, topk_idx, topk_w, dtopk_w, dlogits_topk,
                                  _p(dtopk_w), _p(dlogits_topk), _p(dx), _p(dw_gate), wp, wn,
                                  _s(stream)),
            "moe_gate_backward")
+
+
+def moe_grouped_ffn_backward(shape, x_perm, qparams, offsets, x, w1, w3, w2, dy_perm, dy_shared,
+                             dx_perm, dx_shared, dw1, dw3, dw2, ws, stream=None):
+    wp, wn = _ws(ws)
+    _check(lib.moe_grouped_ffn_backward(ctypes.byref(shape), _p(x_perm), _p(qparams), _p(offsets),
+                                        _p(x), _p(w1), _p(w3), _p(w2), _p(dy_perm), _p(dy_shared),
+                                        _p(dx_perm), _p(dx_shared), _p(dw1), _p(dw3), _p(dw2), wp,
+                                        wn, _s(stream)), "moe_grouped_ffn_backward")
 
 
 def moe_dispatch_backward(shape, dx_perm, dx_shared, dest_row, dx, stream=None):

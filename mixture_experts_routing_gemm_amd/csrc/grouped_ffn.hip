@@ -57,8 +57,15 @@ struct GemmArgs {
     const uint8_t* wb;        // up: W3 [G, h, d]
     uint8_t* out_routed;      // up: H_r [T*k, h]; down: Y_perm [T*k, d]
     uint8_t* out_shared;      // up: H_s [T, S*h]; down: y_sh [T, d]
+    // up-projection that also keeps its pre-activations (the backward's
+    // recomputation): a = W1 v and b = W3 v in bf16, laid out as H
+    uint8_t* pre_a_routed;
+    uint8_t* pre_b_routed;
+    uint8_t* pre_a_shared;
+    uint8_t* pre_b_shared;
     int64_t T;
     int E, S, d, h;
+    int hs;   // row stride of one group's hidden block in H_r / H_s (h rounded up to 8)
     int ntn;  // n-tiles per group
     // operand sizes in bytes (the persistent kernel reads through buffer
     // resources of these sizes; each is below 4 GiB there)
@@ -125,7 +132,18 @@ __device__ __forceinline__ u32x4 dequant8(uint2 codes, float scale, float centre
     return out;
 }
 
-template <int MODE>
+// Register-staged 128 x 128 tile kernel for the shapes the persistent kernel
+// does not take: any d % 8 == 0 and any h. Operands move as 16-byte chunks of
+// 8 values. The hidden rows H are stored with their blocks padded to hs = h
+// rounded up to 8 (the padding columns hold zeros, written by the
+// up-projection from zero weight rows), so in the down-projection K runs
+// over whole chunks of hs; a chunk is either wholly inside K or wholly past
+// it. Chunks past K, and weight rows past N, are read as zeros, and outputs
+// past N are not stored. W2 rows have h values each: when h is not a
+// multiple of 8 their chunks are not 16-byte aligned and are read value by
+// value, up to h. In the shared down-projection K runs over the S hidden
+// blocks in turn, so each chunk finds its own block.
+template <int MODE, bool SAVE = false>
 __global__ __launch_bounds__(kFfnThreads, 2) void ffn_gemm_kernel(GemmArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int nwg = gridDim.x;
@@ -140,7 +158,8 @@ __global__ __launch_bounds__(kFfnThreads, 2) void ffn_gemm_kernel(GemmArgs a) {
     const bool shared = g >= a.E;
 
     // operand geometry
-    const int K = MODE == kModeDown ? (shared ? a.S * a.h : a.h) : a.d;
+    const int K = MODE == kModeDown ? (shared ? a.S * a.hs : a.hs) : a.d;
+    const int N = MODE == kModeDown ? a.d : a.h;  // output features of the group
     const int lda = K;  // elements (codes for fp8) per A row
     const int tid = threadIdx.x;
     const int c = tid & 7;     // 16-byte chunk within a 64-wide K slice
@@ -166,45 +185,70 @@ __global__ __launch_bounds__(kFfnThreads, 2) void ffn_gemm_kernel(GemmArgs a) {
             }
         }
     }
-    // B rows of this thread (weight rows = output features)
+    // B rows of this thread (weight rows = output features); NULL past N
     const uint8_t* brow[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int br = rr + 32 * i;  // 0..127 within the B tile
         if (MODE == kModeDown) {
             const int n = nt * kBN + br;
-            // shared: segment base chosen per K tile below
-            brow[i] = a.wa + (static_cast<int64_t>(shared ? a.E : g) * a.d + n) * a.h * 2;
+            // shared: the hidden block of each chunk is added in load_tile
+            brow[i] = n < N ? a.wa + (static_cast<int64_t>(shared ? a.E : g) * a.d + n) * a.h * 2
+                            : nullptr;
         } else {
             const int q = br >> 6, within = br & 63;
             const int n = nt * (kBN / 2) + q * 32 + (within & 31);
             const uint8_t* w = (within < 32) ? a.wa : a.wb;
-            brow[i] = w + (static_cast<int64_t>(g) * a.h + n) * a.d * 2;
+            brow[i] = n < N ? w + (static_cast<int64_t>(g) * a.h + n) * a.d * 2 : nullptr;
         }
     }
 
     const bool fp8_rows = MODE == kModeUpFp8 && !shared;
     u32x4 ra[4], rb[4];
     auto load_tile = [&](int k0) {
+        const int kk = k0 + c * 8;  // this thread's chunk
+        const bool kin = kk < K;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            if (arow[i] == nullptr) {
+            if (arow[i] == nullptr || !kin) {
                 ra[i] = u32x4{0u, 0u, 0u, 0u};
             } else if (fp8_rows) {
-                const uint2 codes = *reinterpret_cast<const uint2*>(arow[i] + k0 + c * 8);
+                const uint2 codes = *reinterpret_cast<const uint2*>(arow[i] + kk);
                 ra[i] = dequant8(codes, qs[i], qc[i]);
             } else {
-                ra[i] = load16(arow[i] + (static_cast<int64_t>(k0) + c * 8) * 2);
+                ra[i] = load16(arow[i] + static_cast<int64_t>(kk) * 2);
             }
         }
-        int64_t boff = (static_cast<int64_t>(k0) + c * 8) * 2;
-        if (MODE == kModeDown && shared) {
-            const int seg = k0 / a.h;  // shared expert whose hidden block holds k0
-            boff = static_cast<int64_t>(seg) * a.d * a.h * 2 +
-                   (static_cast<int64_t>(k0 - seg * a.h) + c * 8) * 2;
-        }
+        if (MODE == kModeDown) {
+            // the shared expert whose hidden block holds the chunk (0: routed)
+            const int seg = kk / a.hs;
+            const int local = kk - seg * a.hs;  // position within that block
+            const int64_t boff = static_cast<int64_t>(seg) * a.d * a.h * 2 + static_cast<int64_t>(local) * 2;
+            const int nval = a.h - local;  // values of the W2 row left from `local`
 #pragma unroll
-        for (int i = 0; i < 4; ++i) rb[i] = load16(brow[i] + boff);
+            for (int i = 0; i < 4; ++i) {
+                if (brow[i] == nullptr || !kin || nval <= 0) {
+                    rb[i] = u32x4{0u, 0u, 0u, 0u};
+                } else if ((a.h & 7) == 0) {
+                    rb[i] = load16(brow[i] + boff);
+                } else {
+                    const uint16_t* p = reinterpret_cast<const uint16_t*>(brow[i] + boff);
+                    uint32_t w[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint32_t lo = 2 * q < nval ? p[2 * q] : 0u;
+                        const uint32_t hi = 2 * q + 1 < nval ? p[2 * q + 1] : 0u;
+                        w[q] = lo | (hi << 16);
+                    }
+                    rb[i] = u32x4{w[0], w[1], w[2], w[3]};
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                rb[i] = (brow[i] == nullptr || !kin) ? u32x4{0u, 0u, 0u, 0u}
+                                                     : load16(brow[i] + static_cast<int64_t>(kk) * 2);
+        }
     };
     auto store_tile = [&](int buf) {
         uint8_t* As = lds + buf * kLdsStage;
@@ -229,7 +273,7 @@ __global__ __launch_bounds__(kFfnThreads, 2) void ffn_gemm_kernel(GemmArgs a) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    const int KT = K / kBK;
+    const int KT = (K + kBK - 1) / kBK;
     load_tile(0);
     store_tile(0);
     __syncthreads();
@@ -275,23 +319,31 @@ __global__ __launch_bounds__(kFfnThreads, 2) void ffn_gemm_kernel(GemmArgs a) {
 #pragma unroll
                     for (int nb = 0; nb < 2; ++nb) {
                         const int col = nt * kBN + wn * 64 + nb * 32 + lr;
-                        out[row * a.d + col] = f32_to_bf16(acc[mb][nb][v]);
+                        if (col < N) out[row * a.d + col] = f32_to_bf16(acc[mb][nb][v]);
                     }
                 }
             }
     } else {
         bf16_t* out = reinterpret_cast<bf16_t*>(shared ? a.out_shared : a.out_routed);
-        const int ldo = shared ? a.S * a.h : a.h;
-        const int col = (shared ? (g - a.E) * a.h : 0) + nt * (kBN / 2) + wn * 32 + lr;
+        bf16_t* pa = reinterpret_cast<bf16_t*>(shared ? a.pre_a_shared : a.pre_a_routed);
+        bf16_t* pb = reinterpret_cast<bf16_t*>(shared ? a.pre_b_shared : a.pre_b_routed);
+        const int ldo = shared ? a.S * a.hs : a.hs;
+        const int cloc = nt * (kBN / 2) + wn * 32 + lr;  // hidden feature within the group
+        const int col = (shared ? (g - a.E) * a.hs : 0) + cloc;
+        // columns h..hs-1 are padding: zero weight rows give silu(0) * 0 = 0
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int r = m0 + wm * 64 + mb * 32 + 8 * (v >> 2) + 4 * lg + (v & 3);
-                if (r < nrows) {
+                if (r < nrows && cloc < a.hs) {
                     const int64_t row = row_base + r;
                     const float hv = silu(acc[mb][0][v]) * acc[mb][1][v];
                     out[row * ldo + col] = f32_to_bf16(hv);
+                    if constexpr (SAVE) {
+                        pa[row * ldo + col] = f32_to_bf16(acc[mb][0][v]);
+                        pb[row * ldo + col] = f32_to_bf16(acc[mb][1][v]);
+                    }
                 }
             }
     }
@@ -974,6 +1026,10 @@ PlanLayout plan_layout(const moe_shape& s) {
 
 size_t ffn_plan_bytes(const moe_shape& s) { return plan_layout(s).bytes; }
 
+// values per group block of a hidden row: h, rounded up to 8 for bf16 so that
+// every hidden row and block starts on 16 bytes (float32 rows keep h)
+int ffn_hidden_stride(const moe_shape& s) { return s.act == MOE_F32 ? s.h : (s.h + 7) & ~7; }
+
 namespace {
 
 // upper bound on the m-tiles of one launch
@@ -1080,7 +1136,7 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const floa
             pl.ntn_down, counters);
     mark(mk);
 
-    GemmArgs a;
+    GemmArgs a{};
     a.qparams = qparams;
     a.offsets = offsets;
     a.plan = plan;
@@ -1092,6 +1148,7 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const floa
     a.S = s.S;
     a.d = s.d;
     a.h = s.h;
+    a.hs = ffn_hidden_stride(s);
 
     const uint64_t esd = s.dispatch == MOE_FP8_E4M3 ? 1 : 2;
     const uint64_t Tk = static_cast<uint64_t>(s.T) * s.k, TS = static_cast<uint64_t>(s.T) * s.S;
@@ -1114,7 +1171,7 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const floa
         ffn_gemm_f32_kernel<true><<<static_cast<unsigned>(mt * a.ntn), 256, 0, st>>>(a, 0);
         err = hipGetLastError();
     } else {
-        a.ntn = 2 * s.h / (big ? kBigBN : kBN);
+        a.ntn = big ? 2 * s.h / kBigBN : (s.h + kBN / 2 - 1) / (kBN / 2);
         const int64_t mt = max_mtiles(s, bm, false);
         err = s.dispatch == MOE_FP8_E4M3 ? launch_gemm<kModeUpFp8>(a, mt, big, st)
                                          : launch_gemm<kModeUp>(a, mt, big, st);
@@ -1125,8 +1182,8 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const floa
     // down-projection
     a.a_routed = static_cast<const uint8_t*>(h_routed);
     a.a_shared = static_cast<const uint8_t*>(h_shared);
-    a.a_routed_bytes = static_cast<uint32_t>(Tk * s.h * 2);
-    a.a_shared_bytes = static_cast<uint32_t>(TS * s.h * 2);
+    a.a_routed_bytes = static_cast<uint32_t>(Tk * a.hs * 2);
+    a.a_shared_bytes = static_cast<uint32_t>(TS * a.hs * 2);
     a.wa = static_cast<const uint8_t*>(w2);
     a.wb = nullptr;
     a.out_routed = static_cast<uint8_t*>(y_perm);
@@ -1139,11 +1196,57 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const floa
         ffn_gemm_f32_kernel<false><<<static_cast<unsigned>(mt * a.ntn), 256, 0, st>>>(a, 0);
         err = hipGetLastError();
     } else {
-        a.ntn = s.d / (big ? kBigBN : kBN);
+        a.ntn = big ? s.d / kBigBN : (s.d + kBN - 1) / kBN;
         err = launch_gemm<kModeDown>(a, max_mtiles(s, bm, true), big, st);
     }
     mark(mk);
     return err;
+}
+
+// The backward's recomputation of the up-projection (128 x 128 tile kernel):
+// a = W1 v, b = W3 v and H = silu(a) * b of every routed row and every
+// shared-expert block, in bf16, laid out as the forward's H (row stride hs,
+// shared blocks side by side). `plan` must hold the m-tile prefix for 128-row
+// tiles (ffn_plan_kernel with bm = 128).
+hipError_t launch_ffn_recompute(const moe_shape& s, const void* x_perm, const float* qparams,
+                                const int32_t* offsets, const void* x, const void* w1,
+                                const void* w3, const int32_t* plan, void* h_r, void* h_s,
+                                void* a_r, void* b_r, void* a_s, void* b_s, hipStream_t st) {
+    GemmArgs a{};
+    a.qparams = qparams;
+    a.offsets = offsets;
+    a.plan = plan;
+    a.T = s.T;
+    a.E = s.E;
+    a.S = s.S;
+    a.d = s.d;
+    a.h = s.h;
+    a.hs = ffn_hidden_stride(s);
+    a.a_routed = static_cast<const uint8_t*>(x_perm);
+    a.a_shared = static_cast<const uint8_t*>(x);
+    a.wa = static_cast<const uint8_t*>(w1);
+    a.wb = static_cast<const uint8_t*>(w3);
+    a.out_routed = static_cast<uint8_t*>(h_r);
+    a.out_shared = static_cast<uint8_t*>(h_s);
+    a.pre_a_routed = static_cast<uint8_t*>(a_r);
+    a.pre_b_routed = static_cast<uint8_t*>(b_r);
+    a.pre_a_shared = static_cast<uint8_t*>(a_s);
+    a.pre_b_shared = static_cast<uint8_t*>(b_s);
+    a.ntn = (s.h + kBN / 2 - 1) / (kBN / 2);
+    int64_t blocks = max_mtiles(s, kBM, false) * a.ntn;
+    blocks = (blocks + 7) & ~int64_t(7);
+    if (s.dispatch == MOE_FP8_E4M3)
+        ffn_gemm_kernel<kModeUpFp8, true><<<static_cast<unsigned>(blocks), kFfnThreads, 2 * kLdsStage, st>>>(a);
+    else
+        ffn_gemm_kernel<kModeUp, true><<<static_cast<unsigned>(blocks), kFfnThreads, 2 * kLdsStage, st>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_ffn_plan128(const moe_shape& s, const int32_t* offsets, int32_t* plan,
+                              hipStream_t st) {
+    ffn_plan_kernel<<<1, 256, 0, st>>>(offsets, s.E, s.S, s.T, kBM, plan, nullptr, 0, 0, 0,
+                                       nullptr);
+    return hipGetLastError();
 }
 
 }  // namespace moe

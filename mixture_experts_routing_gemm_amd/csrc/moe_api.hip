@@ -25,6 +25,7 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const floa
                               int32_t* plan, void* h_routed, void* h_shared, bool plan_done,
                               hipStream_t st, const Marks* mk);
 size_t ffn_plan_bytes(const moe_shape& s);
+int ffn_hidden_stride(const moe_shape& s);
 bool ffn_fused_plan(const moe_shape& s, int32_t* plan, FfnPlanArgs* fp);
 hipError_t launch_combine(const moe_shape& s, const void* y_perm, const void* y_sh,
                           const int32_t* dest_row, const float* topk_w, void* y, hipStream_t st);
@@ -36,7 +37,21 @@ hipError_t launch_combine_backward(const moe_shape& s, const void* dy, const voi
                                    const int32_t* dest_row, const float* topk_w, void* dy_perm,
                                    float* dtopk_w, hipStream_t st);
 
+size_t ffn_backward_ws_bytes(const moe_shape& s);
+hipError_t launch_ffn_backward(const moe_shape& s, const void* x_perm, const float* qparams,
+                               const int32_t* offsets, const void* x, const void* w1,
+                               const void* w3, const void* w2, const void* dy_perm,
+                               const void* dy_sh, void* dx_perm, void* dx_sh, float* dw1,
+                               float* dw3, float* dw2, void* ws, hipStream_t st,
+                               const Marks* mk);
+
 __global__ void clear_header_kernel(uint32_t* hdr) { hdr[threadIdx.x] = 0u; }
+
+__global__ void zero_f32_kernel(float* p, int64_t n) {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+        p[i] = 0.0f;
+}
 }  // namespace moe
 
 using namespace moe;
@@ -52,13 +67,13 @@ size_t act_bytes(int32_t dt) { return dt == MOE_F32 ? 4 : (dt == MOE_BF16 ? 2 : 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct Layout {
-    size_t part = 0, rank = 0, blk = 0, pre = 0, loads = 0, qstats = 0, plan = 0, x_perm = 0, qparams = 0, h_r = 0, h_s = 0, y_perm = 0,
+    size_t fbwd = 0, part = 0, rank = 0, blk = 0, pre = 0, loads = 0, qstats = 0, plan = 0, x_perm = 0, qparams = 0, h_r = 0, h_s = 0, y_perm = 0,
            y_sh = 0, total = 0;
 };
 
 Layout layout(const moe_shape& s, int stage) {
     Layout L;
-    const size_t T = static_cast<size_t>(s.T), k = s.k, d = s.d, h = s.h, S = s.S, E = s.E;
+    const size_t T = static_cast<size_t>(s.T), k = s.k, d = s.d, S = s.S, E = s.E;
     const size_t es = act_bytes(s.act), esd = act_bytes(s.dispatch);
     const size_t nblk = (T + kRankBlockTokens - 1) / kRankBlockTokens;
     size_t off = kHeaderBytes;
@@ -79,8 +94,9 @@ Layout layout(const moe_shape& s, int stage) {
     if (ffn) {
         // m-tile prefix, tile counters and tile descriptors
         L.plan = take(ffn_plan_bytes(s));
-        L.h_r = take(T * k * h * es);
-        L.h_s = take(T * S * h * es);
+        const size_t hs = static_cast<size_t>(ffn_hidden_stride(s));
+        L.h_r = take(T * k * hs * es);
+        L.h_s = take(T * S * hs * es);
     }
     if (stage == MOE_STAGE_FORWARD) {
         L.x_perm = take(T * k * d * esd);
@@ -93,12 +109,20 @@ Layout layout(const moe_shape& s, int stage) {
         const GateWgradGrid g = gate_wgrad_grid(s.T, s.d, s.E, static_cast<int>(es));
         L.part = take(static_cast<size_t>(g.nchunk > 0 ? g.nchunk : 1) * E * s.d * 4);
     }
-    L.total = (disp || ffn || stage == MOE_STAGE_GATE_BACKWARD) ? off : 0;
+    if (stage == MOE_STAGE_FFN_BACKWARD) {
+        // plan, recomputed a / b / hidden rows and their gradients
+        L.fbwd = take(ffn_backward_ws_bytes(s));
+    }
+    L.total = (disp || ffn || stage == MOE_STAGE_GATE_BACKWARD || stage == MOE_STAGE_FFN_BACKWARD)
+                  ? off
+                  : 0;
     return L;
 }
 
-// shape checks common to every entry point; `ffn` adds the GEMM tile limits
+// shape checks common to every entry point (`ffn`: the call runs the expert
+// GEMMs; they take any shape the other stages take)
 int32_t check_shape(const moe_shape* s, bool ffn) {
+    (void)ffn;
     if (s == nullptr) return MOE_ERR_INVALID_ARG;
     if (s->T < 0 || s->d <= 0 || s->E <= 0 || s->k <= 0 || s->S < 0 || s->h <= 0 || s->k > s->E ||
         s->capacity < 0 || (s->overflow != MOE_OVERFLOW_DROP && s->overflow != MOE_OVERFLOW_REASSIGN) ||
@@ -111,8 +135,6 @@ int32_t check_shape(const moe_shape* s, bool ffn) {
     if (s->dispatch != s->act && !(fp8 && s->act == MOE_BF16)) return MOE_ERR_UNSUPPORTED;
     if (s->act == MOE_F32 && s->d % 4 != 0) return MOE_ERR_UNSUPPORTED;
     if (s->act == MOE_BF16 && s->d % (fp8 ? 16 : 8) != 0) return MOE_ERR_UNSUPPORTED;
-    if (ffn && s->act == MOE_BF16 && (s->d % 128 != 0 || s->h % 64 != 0))
-        return MOE_ERR_UNSUPPORTED;
     if (s->T * s->k >= (int64_t(1) << 31) || s->T * (s->S + 1) >= (int64_t(1) << 31))
         return MOE_ERR_UNSUPPORTED;
     if (s->d > (1 << 20) || s->h > (1 << 20)) return MOE_ERR_UNSUPPORTED;
@@ -198,7 +220,7 @@ const char* const kKernelNames[] = {"gate_topk",  "dispatch_rank", "dispatch_sca
 extern "C" {
 
 size_t moe_workspace_bytes(const moe_shape* s, int32_t stage) {
-    if (stage < MOE_STAGE_GATE || stage > MOE_STAGE_GATE_BACKWARD) return 0;
+    if (stage < MOE_STAGE_GATE || stage > MOE_STAGE_FFN_BACKWARD) return 0;
     const bool ffn = stage == MOE_STAGE_FFN || stage == MOE_STAGE_FORWARD;
     if (check_shape(s, ffn) != MOE_OK) return 0;
     return layout(*s, stage).total;
@@ -318,6 +340,34 @@ int32_t moe_gate_backward(const moe_shape* s, const void* x, const void* w_gate,
     return hip_status(launch_gate_backward(*s, x, w_gate, topk_idx, topk_w, dtopk_w, dlogits_topk,
                                            s->T > 0 ? dx : nullptr, dw_gate, at<float>(ws, L.part),
                                            static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_grouped_ffn_backward(const moe_shape* s, const void* x_perm, const float* qparams,
+                                 const int32_t* offsets, const void* x, const void* w1,
+                                 const void* w3, const void* w2, const void* dy_perm,
+                                 const void* dy_shared, void* dx_perm, void* dx_shared, float* dw1,
+                                 float* dw3, float* dw2, void* ws, size_t ws_bytes,
+                                 void* stream) {
+    MOE_TRY(check_shape(s, true));
+    if (s->act != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    MOE_TRY(check_ptrs({w1, w3, w2, dw1, dw3, dw2}));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (s->T == 0) {
+        // no rows: every weight gradient is zero
+        const int64_t n13 = static_cast<int64_t>(s->E + s->S) * s->h * s->d;
+        for (float* p : {dw1, dw3, dw2}) zero_f32_kernel<<<1024, 256, 0, st>>>(p, n13);
+        return hip_status(hipGetLastError());
+    }
+    MOE_TRY(check_ptrs({x_perm, offsets, dy_perm, dx_perm}));
+    if (s->S > 0) MOE_TRY(check_ptrs({x, dy_shared, dx_shared}));
+    else if (dx_shared != nullptr || dy_shared != nullptr) return MOE_ERR_INVALID_ARG;
+    if (s->dispatch == MOE_FP8_E4M3) MOE_TRY(check_ptrs({qparams}));
+    MOE_TRY(check_opt({x, qparams}));
+    MOE_TRY(check_ws(*s, MOE_STAGE_FFN_BACKWARD, ws, ws_bytes));
+    const Layout L = layout(*s, MOE_STAGE_FFN_BACKWARD);
+    return hip_status(launch_ffn_backward(*s, x_perm, qparams, offsets, x, w1, w3, w2, dy_perm,
+                                          dy_shared, dx_perm, dx_shared, dw1, dw3, dw2,
+                                          at<void>(ws, L.fbwd), st, nullptr));
 }
 
 int32_t moe_forward(const moe_shape* s, const void* x, const void* w_gate, const float* bias,

@@ -65,7 +65,7 @@ FAKE = 0x100000  # an aligned, never-dereferenced address: every call below fail
 
 @pytest.mark.parametrize("kw,status", [
     (dict(E=300), -2), (dict(k=9, E=16), -2), (dict(k=5, E=4), -1), (dict(T=-1), -1),
-    (dict(S=9), -2), (dict(d=100), -2), (dict(h=100), -2), (dict(act=2), -2),
+    (dict(S=9), -2), (dict(d=100), -2), (dict(d=200, dispatch=2), -2), (dict(act=2), -2),
     (dict(dispatch=2, act=0), -2), (dict(d=0), -1), (dict(capacity=-1), -1),
     (dict(capacity=4, overflow=2), -1), (dict(quant=1), -1), (dict(quant=3, dispatch=2), -1),
 ])

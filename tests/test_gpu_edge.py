@@ -1,6 +1,7 @@
 """GPU edge cases against the oracle at sizes it finishes in seconds: ragged
 token counts, a single token, one expert, k = E, the largest E and k, empty
-experts, constant rows on the fp8 path, float32 shapes off the tile grid, bad
+experts, constant rows on the fp8 path, bf16 / fp8 / float32 shapes off the
+tile grid (any d % 8 == 0 -- 16 for fp8 rows -- and any h), bad
 routing ids (turned into an error by the kernels' own checks), and T = 0."""
 
 from __future__ import annotations
@@ -12,7 +13,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import ORACLE_THREADS, act_torch, dev, host, rel_l2, requires_gpu, say
+from gpu_util import ORACLE_THREADS, RowErrors, act_torch, dev, host, rel_l2, requires_gpu, say
 from moe_workloads import CONFIGS, make_inputs, make_routing
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
@@ -48,9 +49,9 @@ def forward_vs_oracle(inp):
     assert np.array_equal(host(buf.offsets), offsets)
     assert np.array_equal(host(buf.dest_row), dest)
     assert np.array_equal(host(buf.src_token)[: cfg.T * cfg.k], src)
-    err = rel_l2(host(buf.y), oy)
-    say(f"[edge] y rel-L2 {err:.3e}")
-    assert err <= cfg.tol_y
+    acc = RowErrors()
+    acc.add(host(buf.y), oy)
+    acc.check("[edge] y", cfg.tol_y)
     return buf, oidx
 
 
@@ -64,6 +65,44 @@ def forward_vs_oracle(inp):
 ], ids=["ragged", "one_token", "one_expert", "k_eq_E", "max_E_k", "wide"])
 def test_bf16_shapes(kw):
     forward_vs_oracle(make_inputs(small_cfg(**kw), seed=1))
+
+
+@pytest.mark.parametrize("kw", [
+    dict(T=333, d=200, E=6, k=2, S=1, h=100),     # d % 128 != 0, h % 8 != 0
+    dict(T=333, d=200, E=6, k=2, S=2, h=104),     # h % 64 != 0, shared blocks of 104
+    dict(T=100, d=8, E=4, k=2, S=2, h=37),        # the narrowest rows, odd h
+    dict(T=500, d=272, E=8, k=3, S=2, h=96, dispatch="fp8", tol_y=6e-2),   # fp8 rows, d % 256 != 0
+    dict(T=64, d=16, E=3, k=1, S=1, h=5, dispatch="fp8", tol_y=6e-2),      # fp8, tiny h
+], ids=["d200_h100", "d200_h104", "d8_h37", "fp8_d272_h96", "fp8_d16_h5"])
+def test_bf16_shapes_off_the_tile_grid(kw):
+    forward_vs_oracle(make_inputs(small_cfg(**kw), seed=5))
+
+
+def test_grouped_ffn_stage_off_the_tile_grid():
+    # moe_grouped_ffn alone on rows the oracle dispatched: every routed row
+    # and every shared-expert sum
+    mm = _mm()
+    cfg = small_cfg(T=400, d=136, E=5, k=2, S=2, h=60)
+    inp = make_inputs(cfg, seed=6)
+    oidx, _, _ = oracle.gate_topk(inp.x, inp.wg, cfg.k, None)
+    counts, offsets, dest, src = oracle.dispatch(oidx, cfg.E)
+    shape = mm.shape_of(cfg)
+    x = dev(inp.x)
+    x_perm = x[dev(src.astype(np.int64))].contiguous()
+    y_perm = torch.empty((cfg.T * cfg.k, cfg.d), dtype=torch.bfloat16, device="cuda")
+    y_sh = torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device="cuda")
+    ws = mm.alloc_workspace(shape, mm.STAGE_FFN)
+    mm.moe_grouped_ffn(shape, x_perm, None, dev(offsets), x, dev(inp.w1), dev(inp.w3),
+                       dev(inp.w2), y_perm, y_sh, ws)
+    torch.cuda.synchronize()
+    got = host(y_perm)
+    acc = RowErrors()
+    for r0, r1, ref in oracle.routed_rows(inp, offsets, src):
+        acc.add(got[r0:r1], ref, r0)
+    acc.check("[edge] routed rows d=136 h=60", cfg.tol_y)
+    acc = RowErrors()
+    acc.add(host(y_sh), oracle.shared_rows(inp, np.arange(cfg.T)))
+    acc.check("[edge] shared rows d=136 h=60", cfg.tol_y)
 
 
 @pytest.mark.parametrize("kw", [
