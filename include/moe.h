@@ -184,6 +184,26 @@ int32_t moe_dispatch(const moe_shape *s, const void *x, const int32_t *topk_idx,
                      size_t ws_bytes, void *stream);
 
 /*
+ * moe_dispatch without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments, kernels and results as
+ * moe_dispatch; the working arrays live in a 16 MiB device array owned by
+ * the library (one per GPU, held until the process ends). The call itself
+ * allocates nothing. Limit: the shape's MOE_STAGE_DISPATCH workspace
+ * (moe_workspace_bytes) must fit in 16 MiB -- about 4*T*k + 8*E*T/256 bytes,
+ * e.g. 2.3 MiB for T = 65536, k = 8, E = 256 -- else MOE_ERR_UNSUPPORTED
+ * before anything is enqueued. Every call on a GPU uses that GPU's one array: calls that
+ * overlap on one GPU (two streams, or host threads without ordering) race
+ * and give undefined results. The array is cleared where the kernels need
+ * it on every call; a bad or repeated expert id still gives dest_row = -1
+ * and no row, but no error flag is kept for moe_get_device_error. The
+ * current device must be the stream's.
+ */
+int32_t moe_dispatch_noalloc(const moe_shape *s, const void *x, const int32_t *topk_idx,
+                             int32_t *counts, int32_t *offsets, int32_t *dest_row,
+                             int32_t *src_token, void *x_perm, float *qparams, void *stream);
+
+/*
  * Grouped SwiGLU expert FFN ([deepep] 7 "expert stage", [wmrh] 2.1).
  *  For routed expert e, the rows offsets[e]..offsets[e+1]-1 of x_perm (fp8
  *  rows are first dequantised to code*scale + centre): y_perm[r] =

@@ -14,7 +14,7 @@ from ._binding import (  # noqa: F401
     MOE_QUANT_EXPERT, MOE_QUANT_GLOBAL, MOE_QUANT_TOKEN,
     STAGE_COMBINE, STAGE_DISPATCH, STAGE_FFN, STAGE_FFN_BACKWARD, STAGE_GATE_BACKWARD,
     STAGE_FORWARD, STAGE_GATE, MoEError, alloc_workspace, make_shape, moe_combine, moe_combine_backward,
-    moe_dispatch, moe_dispatch_backward, moe_gate_backward,
+    moe_dispatch, moe_dispatch_backward, moe_dispatch_noalloc, moe_gate_backward,
     moe_forward, moe_forward_kernel_count, moe_forward_kernel_name, moe_forward_traced,
     moe_gate_topk, moe_get_device_error, moe_grouped_ffn, moe_grouped_ffn_backward, moe_shape,
     moe_workspace_bytes,

@@ -94,6 +94,8 @@ def _load():
     L.moe_gate_topk.restype = i32
     L.moe_dispatch.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_dispatch.restype = i32
+    L.moe_dispatch_noalloc.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.moe_dispatch_noalloc.restype = i32
     L.moe_grouped_ffn.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_grouped_ffn.restype = i32
     L.moe_combine.argtypes = [sp, vp, vp, vp, vp, vp, vp]
@@ -124,7 +126,7 @@ def _load():
 lib = _load()
 
 EXPORTS = ["moe_workspace_bytes", "moe_workspace_init", "moe_status_string", "moe_gate_topk",
-           "moe_dispatch", "moe_grouped_ffn", "moe_combine", "moe_combine_backward",
+           "moe_dispatch", "moe_dispatch_noalloc", "moe_grouped_ffn", "moe_combine", "moe_combine_backward",
            "moe_dispatch_backward", "moe_gate_backward", "moe_grouped_ffn_backward", "moe_forward", "moe_forward_traced",
            "moe_forward_kernel_count", "moe_forward_kernel_name", "moe_get_device_error"]
 
@@ -192,6 +194,13 @@ def moe_dispatch(shape, x, topk_idx, counts, offsets, dest_row, src_token, x_per
     _check(lib.moe_dispatch(ctypes.byref(shape), _p(x), _p(topk_idx), _p(counts), _p(offsets),
                             _p(dest_row), _p(src_token), _p(x_perm), _p(qparams), wp, wn,
                             _s(stream)), "moe_dispatch")
+
+
+def moe_dispatch_noalloc(shape, x, topk_idx, counts, offsets, dest_row, src_token, x_perm,
+                         qparams, stream=None):
+    _check(lib.moe_dispatch_noalloc(ctypes.byref(shape), _p(x), _p(topk_idx), _p(counts),
+                                    _p(offsets), _p(dest_row), _p(src_token), _p(x_perm),
+                                    _p(qparams), _s(stream)), "moe_dispatch_noalloc")
 
 
 def moe_grouped_ffn(shape, x_perm, qparams, offsets, x, w1, w3, w2, y_perm, y_shared, ws,

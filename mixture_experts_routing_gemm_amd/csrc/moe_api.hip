@@ -5,6 +5,7 @@
 
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "ffn_plan.h"
 #include "moe.h"
@@ -55,6 +56,16 @@ __global__ void zero_f32_kernel(float* p, int64_t n) {
 }  // namespace moe
 
 using namespace moe;
+
+// ------------------------------------------------ allocation-free dispatch --
+// Device memory for moe_dispatch_noalloc's working arrays (the header with
+// the error flag, the per-slot ranks, the per-block counts and prefixes, the
+// first-pass loads and the fp8 ranges): one copy per GPU, held by the loaded
+// code object until the process ends. Host code never passes `scratch`
+// itself to a kernel -- in host code that name is only a stand-in -- but the
+// device address of the current GPU's copy, looked up once per device.
+static constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
 
 namespace {
 
@@ -211,6 +222,27 @@ int32_t forward_impl(const moe_shape* s, const void* x, const void* w_gate, cons
     return MOE_OK;
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (found with hipGetSymbolAddress on
+// the first call on that device, with the device current).
+int32_t scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return MOE_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
 const char* const kKernelNames[] = {"gate_topk",  "dispatch_rank", "dispatch_scan",
                                     "dispatch_permute", "ffn_plan", "ffn_up",
                                     "ffn_down",   "combine"};
@@ -272,6 +304,32 @@ int32_t moe_dispatch(const moe_shape* s, const void* x, const int32_t* topk_idx,
                                       at<int32_t>(ws, L.loads), at<uint32_t>(ws, L.qstats),
                                       at<uint32_t>(ws, 0), FfnPlanArgs{nullptr, nullptr, nullptr, 0, 0, 0, 0, 0, 0},
                                       static_cast<hipStream_t>(stream),
+                                      nullptr));
+}
+
+int32_t moe_dispatch_noalloc(const moe_shape* s, const void* x, const int32_t* topk_idx,
+                             int32_t* counts, int32_t* offsets, int32_t* dest_row,
+                             int32_t* src_token, void* x_perm, float* qparams, void* stream) {
+    MOE_TRY(check_shape(s, false));
+    if (s->T == 0) return MOE_OK;
+    MOE_TRY(check_ptrs({x, topk_idx, counts, offsets, dest_row, src_token, x_perm}));
+    if (s->dispatch == MOE_FP8_E4M3) MOE_TRY(check_ptrs({qparams}));
+    MOE_TRY(check_opt({qparams}));
+    if (layout(*s, MOE_STAGE_DISPATCH).total > kNoAllocScratchBytes) return MOE_ERR_UNSUPPORTED;
+    void* ws = nullptr;
+    MOE_TRY(scratch_address(&ws));
+    const Layout L = layout(*s, MOE_STAGE_DISPATCH);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    // the error flag left by an earlier call starts at zero again (a kernel,
+    // not a memset, so that the call can be captured in a graph)
+    clear_header_kernel<<<1, kHeaderBytes / 4, 0, st>>>(static_cast<uint32_t*>(ws));
+    MOE_TRY(hip_status(hipGetLastError()));
+    return hip_status(launch_dispatch(*s, x, topk_idx, counts, offsets, dest_row, src_token,
+                                      x_perm, qparams, at<int32_t>(ws, L.rank),
+                                      at<int32_t>(ws, L.blk), at<int32_t>(ws, L.pre),
+                                      at<int32_t>(ws, L.loads), at<uint32_t>(ws, L.qstats),
+                                      at<uint32_t>(ws, 0),
+                                      FfnPlanArgs{nullptr, nullptr, nullptr, 0, 0, 0, 0, 0, 0}, st,
                                       nullptr));
 }
 
