@@ -200,10 +200,11 @@ def cpu_baseline(inp, min_s=10.0, max_tokens=None):
             "cores_used": f"1 of {avail}"}
 
 
-def backward_leg(mm, torch, cfg, shape, buf, stream, A, x, wg, reps=20):
-    """Time the data-movement stages of the layer backward on this forward's
-    routing: synthetic gradients and expert rows, each launch bracketed by
-    its own pair of events (averaged over reps launches)."""
+def backward_leg(mm, torch, cfg, shape, buf, stream, A, x, wg, w1, w3, w2, reps=20):
+    """Time the stages of the layer backward on this forward's routing:
+    synthetic gradients and expert rows, each launch bracketed by its own
+    pair of events (averaged over reps launches); then the expert FFN's
+    backward (ffn_backward_leg)."""
     T, d, k = cfg.T, cfg.d, cfg.k
     dt = torch.float32 if cfg.act == "f32" else torch.bfloat16
     g = torch.Generator(device="cuda").manual_seed(7)
@@ -242,7 +243,63 @@ def backward_leg(mm, torch, cfg, shape, buf, stream, A, x, wg, reps=20):
                      "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
                      "algorithmic_bytes": A[name + "_bytes"]}
     del dy, y_perm, dy_perm, dx_sh, dx, ws_gb
+    out["ffn_backward"] = ffn_backward_leg(mm, torch, cfg, shape, buf, stream, x, w1, w3, w2,
+                                           reps=max(3, reps // 4))
     return out
+
+
+def ffn_backward_leg(mm, torch, cfg, shape, buf, stream, x, w1, w3, w2, reps=5):
+    """Time moe_grouped_ffn_backward on this forward's dispatch (its rows
+    from moe_dispatch, synthetic output gradients): the recomputation of
+    a, b and hid, dhid with the SwiGLU backward, dx, and the weight
+    gradients. MFMA share counts the 12 * rows * d * h FLOPs of the backward
+    proper (the recomputation's 4 * rows * d * h reported beside them)."""
+    T, d, E, k, S, h = cfg.T, cfg.d, cfg.E, cfg.k, cfg.S, cfg.h
+    fp8 = cfg.dispatch == "fp8"
+    R = T * k
+    x_perm = torch.empty((R, d), dtype=torch.uint8 if fp8 else torch.bfloat16, device="cuda")
+    qp = torch.empty((R, 2), dtype=torch.float32, device="cuda") if fp8 else None
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    dest = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    src = torch.empty(R, dtype=torch.int32, device="cuda")
+    ws_d = mm.alloc_workspace(shape, mm.STAGE_DISPATCH)
+    mm.moe_dispatch(shape, x, buf.topk_idx, counts, offsets, dest, src, x_perm, qp, ws_d, stream)
+    rows = int(offsets[-1].item()) + S * T
+    g = torch.Generator(device="cuda").manual_seed(9)
+    dy_perm = (0.05 * torch.randn((R, d), device="cuda", generator=g)).to(torch.bfloat16)
+    dy_sh = (0.05 * torch.randn((T, d), device="cuda", generator=g)).to(torch.bfloat16) if S else None
+    dx_perm = torch.empty((R, d), dtype=torch.bfloat16, device="cuda")
+    dx_sh = torch.empty((T, d), dtype=torch.bfloat16, device="cuda") if S else None
+    G = E + S
+    dw1 = torch.empty((G, h, d), dtype=torch.float32, device="cuda")
+    dw3 = torch.empty((G, h, d), dtype=torch.float32, device="cuda")
+    dw2 = torch.empty((G, d, h), dtype=torch.float32, device="cuda")
+    ws = mm.alloc_workspace(shape, mm.STAGE_FFN_BACKWARD)
+
+    def call():
+        mm.moe_grouped_ffn_backward(shape, x_perm, qp, offsets, x if S else None, w1, w3, w2,
+                                    dy_perm, dy_sh, dx_perm, dx_sh, dw1, dw3, dw2, ws, stream)
+    call()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a_, b_ in ev:
+        a_.record(stream)
+        call()
+        b_.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.median([a_.elapsed_time(b_) for a_, b_ in ev]))
+    flops = 12 * rows * d * h
+    peak = BF16_PEAK_TFLOPS
+    res = {"us": round(ms * 1e3, 2), "rows": rows, "backward_flops": flops,
+           "recompute_flops": 4 * rows * d * h,
+           "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+           "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / peak, 4),
+           "mfma_frac_incl_recompute": round(16 * rows * d * h / (ms * 1e-3) / 1e12 / peak, 4)}
+    del x_perm, qp, dy_perm, dy_sh, dx_perm, dx_sh, dw1, dw3, dw2, ws, ws_d
+    torch.cuda.empty_cache()
+    return res
 
 
 def _pct(a, q):
@@ -360,7 +417,8 @@ def run_workload(cfg, steps, warmup, flush, with_backward=False, keep_host=False
     }
     extra = {"A": A, "t_up": t_up, "gemm_peak": gemm_peak}
     if with_backward:
-        res["backward_stages"] = backward_leg(mm, torch, cfg, shape, buf, stream, A, x, wg)
+        res["backward_stages"] = backward_leg(mm, torch, cfg, shape, buf, stream, A, x, wg,
+                                              w1, w3, w2)
     del x, wg, w1, w3, w2, bias, buf
     torch.cuda.empty_cache()
     return res, extra, inp

@@ -1,0 +1,140 @@
+"""GPU parity of the grouped expert FFN's backward (moe_grouped_ffn_backward)
+against the oracle's whole-group backward (oracle.ffn_backward), through the
+C ABI.
+
+Inputs: the rows the oracle dispatched (bf16 copies, or its fp8 codes and
+(scale, centre)), random bf16 output gradients for every routed row and for
+the shared experts' sum. Bars, at the workload's relative-L2 bound (2e-2
+bf16, 6e-2 with fp8 rows): dx_perm and dx_shared over the whole tensor and
+on every row; dW1, dW3 and dW2 of every expert that has rows, each over its
+own tensor; exactly zero for an expert with no rows; and the same bits on a
+second call (every weight-gradient element has one owner and a fixed order).
+"""
+
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import ORACLE_THREADS, RowErrors, dev, host, rel_l2, requires_gpu, say
+from moe_workloads import CONFIGS, make_inputs, make_rows
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+
+def _mm():
+    import mixture_experts_routing_gemm_amd as mm
+    return mm
+
+
+def run_case(cfg, seed=1):
+    mm = _mm()
+    say(f"[ffn bwd] {cfg.name} T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} S={cfg.S} h={cfg.h} "
+        f"dispatch={cfg.dispatch}")
+    inp = make_inputs(cfg, seed=seed)
+    T, d, E, k, S, h = cfg.T, cfg.d, cfg.E, cfg.k, cfg.S, cfg.h
+    z = oracle.gate_logits(inp.x, inp.wg, inp.bias, nthreads=ORACLE_THREADS)
+    idx, _ = oracle.select_topk(z, k)
+    counts, offsets, dest, src = oracle.dispatch(idx, E)
+    R = int(offsets[-1])
+    fp8 = cfg.dispatch == "fp8"
+    src_d = dev(src[:R].astype(np.int64))
+    qp = None
+    if fp8:
+        q, qpo = oracle.fp8_quantize(inp.x, nthreads=ORACLE_THREADS)
+        x_perm = dev(q)[src_d].contiguous()
+        qp = dev(qpo)[src_d].contiguous()
+    else:
+        x_perm = dev(inp.x)[src_d].contiguous()
+    dy_perm = make_rows(R, d, "bf16", seed=21, sigma=0.05)
+    dy_sh = make_rows(T, d, "bf16", seed=22, sigma=0.05) if S else None
+    shape = mm.shape_of(cfg)
+    G = E + S
+    out = dict(dx_perm=torch.empty((R, d), dtype=torch.bfloat16, device="cuda"),
+               dx_sh=torch.empty((T, d), dtype=torch.bfloat16, device="cuda") if S else None,
+               dw1=torch.full((G, h, d), 7.0, dtype=torch.float32, device="cuda"),
+               dw3=torch.full((G, h, d), 7.0, dtype=torch.float32, device="cuda"),
+               dw2=torch.full((G, d, h), 7.0, dtype=torch.float32, device="cuda"))
+    ws = mm.alloc_workspace(shape, mm.STAGE_FFN_BACKWARD)
+    args = (shape, x_perm, qp, dev(offsets), dev(inp.x) if S else None, dev(inp.w1), dev(inp.w3),
+            dev(inp.w2), dev(dy_perm), None if dy_sh is None else dev(dy_sh))
+
+    def call():
+        mm.moe_grouped_ffn_backward(*args, out["dx_perm"], out["dx_sh"], out["dw1"], out["dw3"],
+                                    out["dw2"], ws)
+        torch.cuda.synchronize()
+
+    call()
+    got = {key: (None if v is None else host(v).copy()) for key, v in out.items()}
+    say("[ffn bwd] oracle backward")
+    ref = oracle.ffn_backward(inp, offsets, src, dy_perm, dy_sh, nthreads=ORACLE_THREADS)
+    acc = RowErrors()
+    acc.add(got["dx_perm"], ref["dx_perm"])
+    acc.check(f"[ffn bwd] {cfg.name} dx_perm", cfg.tol_y)
+    if S:
+        acc = RowErrors()
+        acc.add(got["dx_sh"], ref["dx_shared"])
+        acc.check(f"[ffn bwd] {cfg.name} dx_shared", cfg.tol_y)
+    rows = np.concatenate([np.diff(offsets), np.full(S, T)])
+    worst = {}
+    for key in ("dw1", "dw3", "dw2"):
+        for g in range(G):
+            if rows[g] == 0:
+                assert np.all(got[key][g] == 0.0), f"{key}[{g}]: an expert with no rows"
+                continue
+            err = rel_l2(got[key][g], ref[key][g])
+            worst[key] = max(worst.get(key, 0.0), err)
+            assert err <= cfg.tol_y, f"{key}[{g}] rel-L2 {err:.3e} (rows {rows[g]})"
+    say(f"[ffn bwd] {cfg.name} worst weight-gradient rel-L2 per expert: "
+        + ", ".join(f"{k_} {v:.3e}" for k_, v in worst.items())
+        + f"; experts with no rows: {int(np.sum(rows == 0))}")
+    # the same bits on a second call
+    call()
+    for key in ("dw1", "dw3", "dw2", "dx_perm"):
+        assert np.array_equal(host(out[key]), got[key]), f"{key} differs on a second call"
+
+
+def _cfg(base, **kw):
+    kw.setdefault("sigma_w", 0.05)
+    return dataclasses.replace(CONFIGS[base], name=f"{base}_bwd", **kw)
+
+
+@pytest.mark.parametrize("base,kw", [
+    ("deepseekmoe_bf16", dict(T=300, d=128, E=8, k=2, S=1, h=64)),
+    ("deepseekmoe_bf16", dict(T=333, d=200, E=6, k=2, S=2, h=100)),
+    ("deepseekmoe_bf16", dict(T=257, d=128, E=1, k=1, S=0, h=64)),
+    ("fp8_dispatch", dict(T=400, d=256, E=8, k=3, S=2, h=96)),
+    ("zipf_stress_bf16", dict(T=2048, d=256, E=128, k=4, h=128)),
+], ids=["small", "off_grid", "one_expert", "fp8_rows", "skewed_E128"])
+def test_ffn_backward_small(base, kw):
+    run_case(_cfg(base, **kw))
+
+
+@pytest.mark.parametrize("name", ["deepseekmoe_bf16", "coarse_top2_bf16"])
+def test_ffn_backward_full_size(name):
+    run_case(dataclasses.replace(CONFIGS[name], name=f"{name}_bwd"))
+
+
+def test_ffn_backward_skewed_workload_quarter_tokens():
+    # the E=128 skewed workload (zero-row experts and one expert with most
+    # rows) at a quarter of its tokens, its other dimensions in full
+    run_case(dataclasses.replace(CONFIGS["zipf_stress_bf16"], T=16384, name="zipf_bwd"))
+
+
+def test_ffn_backward_zero_tokens_zeroes_the_weight_gradients():
+    mm = _mm()
+    cfg = _cfg("deepseekmoe_bf16", T=0, d=64, E=4, k=2, S=1, h=32)
+    shape = mm.shape_of(cfg)
+    dw = [torch.full(s_, 3.0, dtype=torch.float32, device="cuda")
+          for s_ in ((5, 32, 64), (5, 32, 64), (5, 64, 32))]
+    w = torch.zeros((5, 32, 64), dtype=torch.bfloat16, device="cuda")
+    w2 = torch.zeros((5, 64, 32), dtype=torch.bfloat16, device="cuda")
+    mm.moe_grouped_ffn_backward(shape, None, None, None, None, w, w, w2, None, None, None, None,
+                                dw[0], dw[1], dw[2], None)
+    torch.cuda.synchronize()
+    for t in dw:
+        assert float(t.abs().max()) == 0.0
