@@ -332,5 +332,6 @@ def rows_as_f64(x):
     return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-from .dense import (ffn_backward, layer_dense, routed_rows, shared_rows, swiglu_rows,  # noqa: E402,F401
+from .dense import (ffn_backward, layer_dense, layer_dense_fp8w, quantize_expert_weights,  # noqa: E402,F401
+                    quantize_weight_rows, routed_rows, shared_rows, swiglu_rows, symmetric_ranges,
                     token_inputs)

@@ -79,11 +79,16 @@ def _dequant(codes, qp):
 def token_inputs(inp, nthreads=None):
     """float64 routed-expert input of every token [T, d]: the row itself, or
     (fp8 dispatch) the row quantised with its own per-token affine map and
-    mapped back as code * scale + centre (gsyq.cn section 3.1)."""
+    mapped back as code * scale + centre (gsyq.cn section 3.1) -- or, in the
+    per-token symmetric absmax mode ("token_absmax"), the same map over the
+    symmetric range [-max|x|, max|x|] (centre 0)."""
     from . import fp8_quantize
     if inp.cfg.dispatch != "fp8":
         return _f64(inp.x)
-    q, qp = fp8_quantize(inp.x, nthreads=nthreads or 1)
+    if getattr(inp.cfg, "quant", "token") == "token_absmax":
+        q, qp = fp8_quantize(inp.x, ranges=symmetric_ranges(_as_f32(inp.x)), nthreads=nthreads or 1)
+    else:
+        q, qp = fp8_quantize(inp.x, nthreads=nthreads or 1)
     return _dequant(q, qp)
 
 
@@ -255,3 +260,125 @@ def ffn_backward(inp, offsets, src_token, dy_perm, dy_shared=None, xq=None, nthr
                 out["dw3"][gi] += d3
                 out["dw2"][gi] += d2
     return out
+
+
+# ----------------------------------------------------------- fp8 weights ---
+# The pages name FP8 for the dispatched activations only ("Deepseek-MoE同步税本质
+# 与四层实战优化指南", gsyq.cn, sections 3.1 and 5.2: a per-token min/max map, and
+# per-token / per-expert / global modes); weight quantisation is not defined
+# there. The reading taken for the fp8-weight variant of the expert stage:
+#   * every weight row (one output feature of W1, W3 or W2) gets its own
+#     symmetric absmax scale: the same affine map as the activations, applied
+#     to the symmetric range [-max|w|, max|w|], so the centre is 0 and the
+#     scale is max|w| / 448;
+#   * the shared experts read the same per-token fp8 rows as the routed ones;
+#   * the hidden vector silu(a) * b is rounded to bf16 (float32 first) and
+#     quantised per row with a symmetric absmax scale over the row's h values
+#     (over the S * h values of the shared experts' concatenated blocks) before
+#     the down-projection.
+
+
+def symmetric_ranges(rows):
+    """(min, max) = (-max|v|, max|v|) per row of a float array [n, K]."""
+    amax = np.max(np.abs(rows), axis=1).astype(np.float32)
+    return np.stack([-amax, amax], axis=1)
+
+
+def _as_f32(a):
+    if a.dtype == np.float32:
+        return a
+    return (a.astype(np.uint32) << 16).view(np.float32)
+
+
+def quantize_weight_rows(w, nthreads=None):
+    """Symmetric absmax e4m3 codes of every row of w [..., K] (bf16 bits or
+    float32): (codes uint8 [..., K], scale float32 [...]); the row is
+    code * scale."""
+    from . import fp8_quantize
+    shp = w.shape
+    rows = np.ascontiguousarray(w.reshape(-1, shp[-1]))
+    q, qp = fp8_quantize(rows, ranges=symmetric_ranges(_as_f32(rows)), nthreads=nthreads or 1)
+    assert np.all(qp[:, 1] == 0.0)  # the symmetric range has centre 0
+    return q.reshape(shp), qp[:, 0].reshape(shp[:-1])
+
+
+def quantize_expert_weights(inp, nthreads=None):
+    """(q1, s1, q3, s3, q2, s2): every weight row of W1, W3 [G, h, d] and W2
+    [G, d, h] as symmetric absmax e4m3 codes with a float32 scale per row."""
+    q1, s1 = quantize_weight_rows(inp.w1, nthreads)
+    q3, s3 = quantize_weight_rows(inp.w3, nthreads)
+    q2, s2 = quantize_weight_rows(inp.w2, nthreads)
+    return q1, s1, q3, s3, q2, s2
+
+
+def _deq_rows(q, s):
+    from . import fp8_dequantize
+    shp = q.shape
+    qp = np.zeros((int(np.prod(shp[:-1])), 2), dtype=np.float32)
+    qp[:, 0] = s.reshape(-1)
+    return fp8_dequantize(q.reshape(-1, shp[-1]), qp).reshape(shp)
+
+
+def _bf16_round(v64):
+    """float64 -> float32 (nearest) -> bf16 (nearest even), as float64."""
+    u = v64.astype(np.float32).view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def _quant_hidden(hid):
+    """bf16 hidden rows [n, K] (float64 values) quantised per row with a
+    symmetric absmax e4m3 scale, back as float64 code * scale."""
+    from . import fp8_dequantize, fp8_quantize
+    h32 = hid.astype(np.float32)
+    q, qp = fp8_quantize(h32, ranges=symmetric_ranges(h32))
+    return fp8_dequantize(q, qp)
+
+
+def layer_dense_fp8w(inp, wq, nthreads=None, gate=None, xq=None):
+    """Whole-layer output with fp8 expert weights (the reading above):
+    (topk_idx, topk_w, y [T, d] float64). wq: quantize_expert_weights(inp).
+    Every expert FFN is W2q (Q(bf16(silu(W1q v) * (W3q v)))), Wq the
+    dequantised weights and Q the per-row symmetric absmax quantiser, v the
+    token's dequantised fp8 row (routed and shared experts alike)."""
+    from . import gate_logits, select_topk
+    cfg = inp.cfg
+    T, d, E, k, S, h = cfg.T, cfg.d, cfg.E, cfg.k, cfg.S, cfg.h
+    if gate is None:
+        z = gate_logits(inp.x, inp.wg, inp.bias, nthreads=nthreads or 1)
+        idx, w = select_topk(z, k)
+    else:
+        idx, w = gate
+    if xq is None:
+        xq = token_inputs(inp, nthreads)
+    q1, s1, q3, s3, q2, s2 = wq
+    y = np.zeros((T, d))
+
+    def up(v, g):
+        W1 = _deq_rows(q1[g], s1[g])
+        W3 = _deq_rows(q3[g], s3[g])
+        a = v @ W1.T
+        b = v @ W3.T
+        with np.errstate(over="ignore"):
+            return _bf16_round(a / (1.0 + np.exp(-a)) * b)
+
+    with _Threads(nthreads):
+        if S:
+            W2s = [_deq_rows(q2[E + s], s2[E + s]) for s in range(S)]
+            for t0 in range(0, T, 4096):
+                t1 = min(T, t0 + 4096)
+                v = xq[t0:t1]
+                hid = np.concatenate([up(v, E + s) for s in range(S)], axis=1)
+                hq = _quant_hidden(hid)
+                for s in range(S):
+                    y[t0:t1] += hq[:, s * h:(s + 1) * h] @ W2s[s].T
+        for e in range(E):
+            tt, jj = np.nonzero(idx == e)
+            if len(tt) == 0:
+                continue
+            W2 = _deq_rows(q2[e], s2[e])
+            for c0 in range(0, len(tt), 4096):
+                t_c, j_c = tt[c0:c0 + 4096], jj[c0:c0 + 4096]
+                hq = _quant_hidden(up(xq[t_c], e))
+                y[t_c] += w[t_c, j_c][:, None] * (hq @ W2.T)
+    return idx, w, y
