@@ -82,8 +82,15 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
 typedef enum { MOE_OVERFLOW_DROP = 0, MOE_OVERFLOW_REASSIGN = 1 } moe_overflow;
 
 /* the rows whose min/max range an fp8 row is mapped from ([gsyq] 5.2: the
- * quantiser's per-token, per-expert and global modes) */
-typedef enum { MOE_QUANT_TOKEN = 0, MOE_QUANT_EXPERT = 1, MOE_QUANT_GLOBAL = 2 } moe_quant;
+ * quantiser's per-token, per-expert and global modes), or the per-token
+ * symmetric absmax map: the same affine map over [-max|x|, max|x|], whose
+ * centre is 0 */
+typedef enum {
+    MOE_QUANT_TOKEN = 0,
+    MOE_QUANT_EXPERT = 1,
+    MOE_QUANT_GLOBAL = 2,
+    MOE_QUANT_TOKEN_ABSMAX = 3
+} moe_quant;
 
 /* which entry point a workspace is sized for */
 typedef enum {
@@ -93,7 +100,8 @@ typedef enum {
     MOE_STAGE_COMBINE = 3,
     MOE_STAGE_FORWARD = 4,
     MOE_STAGE_GATE_BACKWARD = 5,
-    MOE_STAGE_FFN_BACKWARD = 6
+    MOE_STAGE_FFN_BACKWARD = 6,
+    MOE_STAGE_FORWARD_FP8W = 7
 } moe_stage;
 
 typedef struct {
@@ -173,7 +181,8 @@ int32_t moe_gate_topk(const moe_shape *s, const void *x, const void *w_gate,
  *  constant row gets codes 0 and scale 0. With s->quant = MOE_QUANT_EXPERT
  *  ([gsyq] 5.2) max and min are taken over every row dispatched to the
  *  row's expert (its final rows, after any capacity limit), and with
- *  MOE_QUANT_GLOBAL over all T rows of x; the map is otherwise the same, so
+ *  MOE_QUANT_GLOBAL over all T rows of x, and with MOE_QUANT_TOKEN_ABSMAX
+ *  they are -max|x[t]| and max|x[t]| (centre 0); the map is otherwise the same, so
  *  each dispatched row still carries its own (scale, centre).
  *  qparams may be NULL otherwise.
  *  ws: MOE_STAGE_DISPATCH bytes.
@@ -333,6 +342,61 @@ int32_t moe_forward(const moe_shape *s, const void *x, const void *w_gate,
                     void *y, int32_t *topk_idx, float *topk_w, int32_t *counts,
                     int32_t *offsets, int32_t *dest_row, int32_t *src_token, void *ws,
                     size_t ws_bytes, void *stream);
+
+/*
+ * fp8 expert weights ([gsyq] 3.1 and 5.2 quantise the dispatched activations
+ * to FP8; the pages leave weight quantisation open). Reading: every weight
+ * row -- one output feature of W1, W3 or W2 -- is quantised to e4m3 with the
+ * activations' affine map over the symmetric range [-max|w|, max|w|]:
+ * centre 0, scale max|w| / 448, code = e4m3 round-to-nearest-even of
+ * clamp(w * (448 / max|w|), +-448) in float32 (codes 0 and scale 0 for a zero
+ * row). The shared experts' W2 rows are quantised jointly over their S
+ * concatenated hidden blocks (one scale per output feature, so that their
+ * down-projections still sum in one accumulator).
+ *
+ * Host only: the float32 count of the scale array wscale for shape *s:
+ *   s1 [E+S, h] | qsum1 [E+S, h] | s3 [E+S, h] | qsum3 [E+S, h] | s2 [E+S, d]
+ * (s: a row's scale; qsum: the sum of a W1 / W3 row's code values, for the
+ * activations' centre term; s2 of the shared experts repeated per expert).
+ * 0 for an invalid shape.
+ */
+size_t moe_fp8_weight_scale_floats(const moe_shape *s);
+
+/*
+ * Quantise bf16 expert weights w1, w3 [E+S, h, d] and w2 [E+S, d, h] (act =
+ * MOE_BF16, d % 8 == 0, h % 8 == 0) to e4m3 codes w1q, w3q, w2q (uint8, same
+ * shapes) and the scales wscale (moe_fp8_weight_scale_floats). Device
+ * pointers owned by the caller; errors as for the other calls.
+ */
+int32_t moe_quantize_weights(const moe_shape *s, const void *w1, const void *w3, const void *w2,
+                             uint8_t *w1q, uint8_t *w3q, uint8_t *w2q, float *wscale,
+                             void *stream);
+
+/*
+ * The whole layer with fp8 expert weights on the fp8 matrix cores: gate and
+ * dispatch as in moe_forward (s->dispatch must be MOE_FP8_E4M3, quant
+ * MOE_QUANT_TOKEN or MOE_QUANT_TOKEN_ABSMAX, act MOE_BF16); then every
+ * expert, routed and shared, computes on the token's fp8 row (so here the
+ * shared experts read the quantised rows too):
+ *   a = W1q v, b = W3q v (e4m3 x e4m3 products, float32 sums, row and
+ *   weight scales and the row's centre applied after the sum),
+ *   H = bf16(silu(a) * b), quantised per row with a symmetric absmax e4m3
+ *   scale (the shared experts' S blocks of a token together),
+ *   Y = W2q H (e4m3 x e4m3, scales after the sum), rounded to bf16,
+ * and combine as in moe_forward. w1q, w3q, w2q, wscale from
+ * moe_quantize_weights. Shapes: d % 256 == 0 and h % 256 == 0, else
+ * MOE_ERR_UNSUPPORTED. ws: MOE_STAGE_FORWARD_FP8W bytes. events (NULL: not
+ * traced) as for moe_forward_traced with at least 10 entries, recorded before
+ * the first kernel and after gate_topk, dispatch_rank, dispatch_scan,
+ * dispatch_permute_fp8, ffn_plan (no kernel when the permute writes the
+ * plan), ffn_up, ffn_hidden_quant, ffn_down and combine.
+ */
+int32_t moe_forward_fp8w(const moe_shape *s, const void *x, const void *w_gate,
+                         const float *bias, const uint8_t *w1q, const uint8_t *w3q,
+                         const uint8_t *w2q, const float *wscale, void *y, int32_t *topk_idx,
+                         float *topk_w, int32_t *counts, int32_t *offsets, int32_t *dest_row,
+                         int32_t *src_token, void *ws, size_t ws_bytes, void *stream,
+                         void *const *events, int32_t n_events);
 
 /*
  * moe_forward that also records events[i] (hipEvent_t, created by the caller)

@@ -29,6 +29,9 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 STAGE_GATE, STAGE_DISPATCH, STAGE_FFN, STAGE_COMBINE, STAGE_FORWARD = 0, 1, 2, 3, 4
 STAGE_GATE_BACKWARD = 5
 STAGE_FFN_BACKWARD = 6
+STAGE_FORWARD_FP8W = 7
+FP8W_KERNELS = ["gate_topk", "dispatch_rank", "dispatch_scan", "dispatch_permute_fp8", "ffn_plan",
+                "ffn_up", "ffn_hidden_quant", "ffn_down", "combine"]
 
 _DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
 
@@ -53,8 +56,9 @@ class moe_shape(ctypes.Structure):
 
 
 MOE_OVERFLOW_DROP, MOE_OVERFLOW_REASSIGN = 0, 1
-MOE_QUANT_TOKEN, MOE_QUANT_EXPERT, MOE_QUANT_GLOBAL = 0, 1, 2
-_QUANT = {"token": MOE_QUANT_TOKEN, "expert": MOE_QUANT_EXPERT, "global": MOE_QUANT_GLOBAL}
+MOE_QUANT_TOKEN, MOE_QUANT_EXPERT, MOE_QUANT_GLOBAL, MOE_QUANT_TOKEN_ABSMAX = 0, 1, 2, 3
+_QUANT = {"token": MOE_QUANT_TOKEN, "expert": MOE_QUANT_EXPERT, "global": MOE_QUANT_GLOBAL,
+          "token_absmax": MOE_QUANT_TOKEN_ABSMAX}
 
 
 def make_shape(T, d, E, k, S, h, act="bf16", dispatch=None, capacity=0,
@@ -114,6 +118,13 @@ def _load():
     L.moe_forward_traced.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                      sz, vp, ctypes.POINTER(vp), i32]
     L.moe_forward_traced.restype = i32
+    L.moe_fp8_weight_scale_floats.argtypes = [sp]
+    L.moe_fp8_weight_scale_floats.restype = sz
+    L.moe_quantize_weights.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.moe_quantize_weights.restype = i32
+    L.moe_forward_fp8w.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                   sz, vp, ctypes.POINTER(vp), i32]
+    L.moe_forward_fp8w.restype = i32
     L.moe_forward_kernel_count.argtypes = [sp]
     L.moe_forward_kernel_count.restype = i32
     L.moe_forward_kernel_name.argtypes = [sp, i32]
@@ -128,7 +139,8 @@ lib = _load()
 EXPORTS = ["moe_workspace_bytes", "moe_workspace_init", "moe_status_string", "moe_gate_topk",
            "moe_dispatch", "moe_dispatch_noalloc", "moe_grouped_ffn", "moe_combine", "moe_combine_backward",
            "moe_dispatch_backward", "moe_gate_backward", "moe_grouped_ffn_backward", "moe_forward", "moe_forward_traced",
-           "moe_forward_kernel_count", "moe_forward_kernel_name", "moe_get_device_error"]
+           "moe_forward_kernel_count", "moe_forward_kernel_name", "moe_get_device_error",
+           "moe_fp8_weight_scale_floats", "moe_quantize_weights", "moe_forward_fp8w"]
 
 
 def status_string(status: int) -> str:
@@ -264,6 +276,30 @@ def moe_forward_traced(shape, x, w_gate, bias, w1, w3, w2, y, topk_idx, topk_w, 
                                   _p(w3), _p(w2), _p(y), _p(topk_idx), _p(topk_w), _p(counts),
                                   _p(offsets), _p(dest_row), _p(src_token), wp, wn, _s(stream),
                                   arr, len(events)), "moe_forward_traced")
+
+
+def moe_fp8_weight_scale_floats(shape) -> int:
+    return int(lib.moe_fp8_weight_scale_floats(ctypes.byref(shape)))
+
+
+def moe_quantize_weights(shape, w1, w3, w2, w1q, w3q, w2q, wscale, stream=None):
+    _check(lib.moe_quantize_weights(ctypes.byref(shape), _p(w1), _p(w3), _p(w2), _p(w1q), _p(w3q),
+                                    _p(w2q), _p(wscale), _s(stream)), "moe_quantize_weights")
+
+
+def moe_forward_fp8w(shape, x, w_gate, bias, w1q, w3q, w2q, wscale, y, topk_idx, topk_w, counts,
+                     offsets, dest_row, src_token, ws, stream=None, events=None):
+    wp, wn = _ws(ws)
+    if events is None:
+        ev, n = None, 0
+    else:
+        ev = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(None if e is None else int(e))
+                                               for e in events])
+        n = len(events)
+    _check(lib.moe_forward_fp8w(ctypes.byref(shape), _p(x), _p(w_gate), _p(bias), _p(w1q), _p(w3q),
+                                _p(w2q), _p(wscale), _p(y), _p(topk_idx), _p(topk_w), _p(counts),
+                                _p(offsets), _p(dest_row), _p(src_token), wp, wn, _s(stream), ev, n),
+           "moe_forward_fp8w")
 
 
 def moe_forward_kernel_count(shape) -> int:

@@ -492,7 +492,8 @@ __global__ __launch_bounds__(256) void dispatch_permute_fp8_kernel(
     const int32_t* __restrict__ rank, const int32_t* __restrict__ pre,
     const int32_t* __restrict__ offsets, int cap, int reassign, int64_t T, int E, int k, int d,
     int32_t* __restrict__ dest_row, int32_t* __restrict__ src_token,
-    uint8_t* __restrict__ x_perm, float* __restrict__ qparams, FfnPlanArgs fp) {
+    uint8_t* __restrict__ x_perm, float* __restrict__ qparams, FfnPlanArgs fp, int sym,
+    uint8_t* __restrict__ x_self, float* __restrict__ q_self) {
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int pb = permute_or_plan(fp, offsets, E, T);
     if (pb < 0) return;
@@ -521,6 +522,11 @@ __global__ __launch_bounds__(256) void dispatch_permute_fp8_kernel(
     }
     mn = wave_min(mn);
     mx = wave_max(mx);
+    if (sym) {
+        // symmetric absmax: the same map over the range [-max|x|, max|x|]
+        mx = fmaxf(-mn, mx);
+        mn = -mx;
+    }
     const float centre = 0.5f * (mx + mn);
     const float half = 0.5f * (mx - mn);
     const bool flat = half == 0.0f;
@@ -529,6 +535,10 @@ __global__ __launch_bounds__(256) void dispatch_permute_fp8_kernel(
     if (lane < k && dst >= 0) {
         qparams[2 * static_cast<int64_t>(dst)] = scale;
         qparams[2 * static_cast<int64_t>(dst) + 1] = centre;
+    }
+    if (x_self != nullptr && lane == 0) {
+        q_self[2 * t] = scale;
+        q_self[2 * t + 1] = centre;
     }
     for (int g = lane; g < ngroups; g += kWave) {
         const u32x4 a = load16(src + (static_cast<int64_t>(g) << 5));
@@ -539,6 +549,8 @@ __global__ __launch_bounds__(256) void dispatch_permute_fp8_kernel(
             if (j < k && dj[j] >= 0)
                 store16(x_perm + static_cast<int64_t>(dj[j]) * d + (static_cast<int64_t>(g) << 4), q);
         }
+        // the token's own codes, for the shared experts of the fp8-weight path
+        if (x_self != nullptr) store16(x_self + t * d + (static_cast<int64_t>(g) << 4), q);
     }
 }
 
@@ -691,13 +703,13 @@ hipError_t launch_dispatch(const moe_shape& s, const void* x, const int32_t* top
                            int32_t* src_token, void* x_perm, float* qparams, int32_t* rank,
                            int32_t* blk, int32_t* pre, int32_t* first_loads, uint32_t* qstats,
                            uint32_t* hdr, const FfnPlanArgs& fp, hipStream_t st,
-                           const Marks* mk) {
+                           const Marks* mk, uint8_t* x_self, float* q_self) {
     const int nblk = static_cast<int>((s.T + kRankBlockTokens - 1) / kRankBlockTokens);
     const int reassign = s.capacity > 0 && s.overflow == MOE_OVERFLOW_REASSIGN ? 1 : 0;
     dispatch_rank_kernel<<<nblk, kRankThreads, 0, st>>>(topk_idx, s.T, s.E, s.k, rank, blk, hdr);
     mark(mk);
     const bool fp8 = s.dispatch == MOE_FP8_E4M3;
-    const bool group = fp8 && s.quant != MOE_QUANT_TOKEN;
+    const bool group = fp8 && (s.quant == MOE_QUANT_EXPERT || s.quant == MOE_QUANT_GLOBAL);
     dispatch_scan_kernel<<<1, kScanThreads, 0, st>>>(blk, pre, nblk, s.E, s.capacity, reassign,
                                                      counts, offsets, first_loads,
                                                      group ? qstats : nullptr);
@@ -724,7 +736,8 @@ hipError_t launch_dispatch(const moe_shape& s, const void* x, const int32_t* top
     } else if (fp8) {
         dispatch_permute_fp8_kernel<<<pblocks, 256, 0, st>>>(
             static_cast<const bf16_t*>(x), topk_idx, rank, pre, offsets, s.capacity, reassign, s.T,
-            s.E, s.k, s.d, dest_row, src_token, static_cast<uint8_t*>(x_perm), qparams, fp);
+            s.E, s.k, s.d, dest_row, src_token, static_cast<uint8_t*>(x_perm), qparams, fp,
+            s.quant == MOE_QUANT_TOKEN_ABSMAX ? 1 : 0, x_self, q_self);
     } else {
         const int row_bytes = s.d * (s.act == MOE_F32 ? 4 : 2);
         dispatch_permute_kernel<<<pblocks, 256, 0, st>>>(

@@ -27,7 +27,12 @@
 
 namespace moe {
 
-enum { kModeUp = 0, kModeUpFp8 = 1, kModeDown = 2 };
+// kModeUp / kModeDown: bf16 operands; kModeUpFp8: fp8 token rows converted to
+// bf16 in LDS; kModeUpF8W / kModeDownF8W: fp8 token (or hidden) rows and fp8
+// weights on the fp8 matrix cores, the scales applied in the epilogue.
+enum { kModeUp = 0, kModeUpFp8 = 1, kModeDown = 2, kModeUpF8W = 3, kModeDownF8W = 4 };
+constexpr bool is_down(int m) { return m == kModeDown || m == kModeDownF8W; }
+constexpr bool is_f8w(int m) { return m == kModeUpF8W || m == kModeDownF8W; }
 
 constexpr int kBM = 128, kBN = 128, kBK = 64;  // bf16 tile: rows x B rows x K
 constexpr int kFfnThreads = 256;
@@ -63,6 +68,13 @@ struct GemmArgs {
     uint8_t* pre_b_routed;
     uint8_t* pre_a_shared;
     uint8_t* pre_b_shared;
+    // fp8-weight modes: (scale, centre) of the shared experts' token rows
+    // [T, 2]; the weight scales s1 | qsum1 | s3 | qsum3 [G, h] | s2 [G, d];
+    // the hidden rows' scales, routed [rows] and shared [T]
+    const float* q_shared;
+    const float* wscale;
+    const float* hsc_r;
+    const float* hsc_s;
     int64_t T;
     int E, S, d, h;
     int hs;   // row stride of one group's hidden block in H_r / H_s (h rounded up to 8)
@@ -482,8 +494,8 @@ __device__ __forceinline__ TileInfo decode_tile(const GemmArgs& a, int L, int ns
     ti.nrows = t[3];
     ti.shared = L < nsh * a.ntn;
     ti.half = ti.nrows - ti.m0 <= kBigBM / 2;
-    const int K = MODE == kModeDown ? (ti.shared ? a.S * a.h : a.h) : a.d;
-    ti.KT = K / kBigBK;
+    const int K = is_down(MODE) ? (ti.shared ? a.S * a.h : a.h) : a.d;
+    ti.KT = K / (is_f8w(MODE) ? 2 * kBigBK : kBigBK);  // fp8: 64 values per 64-byte slice
     return ti;
 }
 
@@ -497,7 +509,8 @@ __device__ __forceinline__ void tile_sources(const GemmArgs& a, const TileInfo& 
     src.abuf = uniform_ptr(ti.shared ? op_as : op_ar);
     src.abytes = __builtin_amdgcn_readfirstlane(ti.shared ? by_as : by_ar);
     const bool fp8 = MODE == kModeUpFp8 && !ti.shared;
-    const int K = MODE == kModeDown ? (ti.shared ? a.S * a.h : a.h) : a.d;
+    const int K = is_down(MODE) ? (ti.shared ? a.S * a.h : a.h) : a.d;
+    const uint32_t eb = is_f8w(MODE) ? 1 : 2;  // bytes per operand value
     const int last = ti.nrows - 1;
     src.shared = ti.shared;
     // token DMA: a wave instruction fills 1 KB of LDS, lane i at byte 16*i:
@@ -516,7 +529,7 @@ __device__ __forceinline__ void tile_sources(const GemmArgs& a, const TileInfo& 
             const int r = wave * 32 + i * 16 + (lane >> 2);
             const int c = (lane & 3) ^ (((r >> 1) & 3) ^ ((r >> 3) & 1));
             const int64_t row = ti.row_base + min(ti.m0 + r, last);
-            src.aoff[i] = static_cast<uint32_t>(row * K * 2 + c * 16);
+            src.aoff[i] = static_cast<uint32_t>(row * K * eb + c * 16);
         }
     }
     src.cs = 0.0f;
@@ -527,18 +540,18 @@ __device__ __forceinline__ void tile_sources(const GemmArgs& a, const TileInfo& 
         src.cs = q.x;
         src.cc = q.y;
     }
-    src.gofs = static_cast<uint32_t>(MODE == kModeDown && ti.shared ? a.E : ti.g) * a.d * a.h * 2;
+    src.gofs = static_cast<uint32_t>(is_down(MODE) && ti.shared ? a.E : ti.g) * a.d * a.h * eb;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int br = wave * 32 + i * 16 + (lane >> 2);
         const int c = (lane & 3) ^ (((br >> 1) & 3) ^ ((br >> 3) & 1));
-        if (MODE == kModeDown) {
+        if (is_down(MODE)) {
             const int n = ti.nt * kBigBN + br;
-            src.boff[i] = static_cast<uint32_t>(n) * a.h * 2 + c * 16;
+            src.boff[i] = static_cast<uint32_t>(n) * a.h * eb + c * 16;
         } else {
             // weight row br of the tile: 32-row blocks alternate W1 / W3
             const int n = ti.nt * (kBigBN / 2) + ((br >> 5) >> 1) * 32 + (br & 31);
-            src.boff[i] = static_cast<uint32_t>(n) * a.d * 2 + c * 16;
+            src.boff[i] = static_cast<uint32_t>(n) * a.d * eb + c * 16;
         }
     }
 }
@@ -563,6 +576,10 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
     int* lds_next = reinterpret_cast<int*>(lds + kBigSlots * kBigSlot);
     constexpr int MB = kBigMB, NB = kBigNB;
     constexpr bool kFp8 = MODE == kModeUpFp8;
+    constexpr bool kF8W = is_f8w(MODE);
+    constexpr bool kDown = is_down(MODE);
+    constexpr int KS = kF8W ? 2 * kBigBK : kBigBK;  // operand values per slice
+    constexpr uint32_t EB = kF8W ? 1 : 2;          // bytes per operand value
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int wn = wave & 3, wm = wave >> 2;
@@ -577,7 +594,7 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
     const uint32_t by_w = __builtin_amdgcn_readfirstlane(a.w_bytes);
     // up-projection: a wave's weight rows lie in one 32-row block, W1 for
     // even waves and W3 for odd ones
-    const uint8_t* const op_w = uniform_ptr(MODE != kModeDown && (wave & 1) ? a.wb : a.wa);
+    const uint8_t* const op_w = uniform_ptr(!kDown && (wave & 1) ? a.wb : a.wa);
     bf16_t* const out_r = reinterpret_cast<bf16_t*>(const_cast<uint8_t*>(uniform_ptr(a.out_routed)));
     bf16_t* const out_s = reinterpret_cast<bf16_t*>(const_cast<uint8_t*>(uniform_ptr(a.out_shared)));
 
@@ -593,8 +610,8 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
     const int routed = a.plan[a.E];
     const int n_half = a.tile_meta[0];
     const int mtT = static_cast<int>((a.T + kBigBM - 1) / kBigBM);
-    const int nsh = MODE == kModeDown ? (a.S > 0 ? mtT : 0) : a.S * mtT;
-    const int64_t wsh = MODE == kModeDown ? max(a.S, 1) : 1;
+    const int nsh = kDown ? (a.S > 0 ? mtT : 0) : a.S * mtT;
+    const int64_t wsh = kDown ? max(a.S, 1) : 1;
     const int n_sh = nsh * a.ntn;
     const int n_full = n_sh + (routed - n_half) * a.ntn;  // tiles before the half ones
     const int n_halft = n_half * a.ntn;
@@ -638,19 +655,19 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
     };
     auto slice_req = [&](const TileSrc& ts, bool shared, int k, int slot) {
         SliceReq q;
-        const int k0 = k * kBigBK;
+        const int k0 = k * KS;
         q.abase = lds + slot * kBigSlot +
                   (kFp8 && !shared ? fp8_codes_off(wave) : (wave >> 1) * 8192 + (wave & 1) * 2048);
         q.bbase = lds + slot * kBigSlot + (wave >> 1) * 8192 + 4096 + (wave & 1) * 2048;
-        q.ka = static_cast<uint32_t>(kFp8 && !shared ? k0 : k0 * 2);
-        uint32_t kb = static_cast<uint32_t>(k0) * 2;
-        if (MODE == kModeDown) {
+        q.ka = static_cast<uint32_t>(kFp8 && !shared ? k0 : k0 * EB);
+        uint32_t kb = static_cast<uint32_t>(k0) * EB;
+        if (kDown) {
             // the shared group's K runs over the S hidden blocks in turn:
             // slice k0 lies in block seg (always 0 for a routed group)
             int seg = 0;
 #pragma unroll
             for (int s = 1; s < kMaxS; ++s) seg += k0 >= s * a.h ? 1 : 0;
-            kb = static_cast<uint32_t>(k0 - seg * a.h) * 2 + static_cast<uint32_t>(seg) * a.d * a.h * 2;
+            kb = static_cast<uint32_t>(k0 - seg * a.h) * EB + static_cast<uint32_t>(seg) * a.d * a.h * EB;
         }
         q.kb = __builtin_amdgcn_readfirstlane(ts.gofs + kb);
         q.ka = __builtin_amdgcn_readfirstlane(q.ka);
@@ -710,6 +727,28 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
         const int mb = i / NB, nb = i % NB;
         acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[nb], fa[mb], acc[mb][nb], 0, 0, 0);
     };
+    // fp8-weight modes: one 32x32x64 e4m3 MFMA per (mb, nb) and slice. A
+    // lane's 32-byte fragment of row r holds the slice's K values 16*lg ..
+    // 16*lg+15 and 32+16*lg .. 32+16*lg+15 (chunks lg and 2+lg), the same
+    // positions for the weight and the token operand, so every K value of
+    // the slice meets its partner once.
+    typedef int i32x8 __attribute__((ext_vector_type(8)));
+    i32x8 fa8[MB], fb8[NB];
+    auto read_frag8 = [&](int slot, bool isb, int r, i32x8& out) {
+        const uint8_t* base = lds + slot * kBigSlot + (isb ? 4096 : 0);
+        const u32x4 lo = __builtin_bit_cast(u32x4, *reinterpret_cast<const bf16x8*>(base + lds_off32(r, lg)));
+        const u32x4 hi = __builtin_bit_cast(u32x4, *reinterpret_cast<const bf16x8*>(base + lds_off32(r, 2 + lg)));
+        out = i32x8{static_cast<int>(lo[0]), static_cast<int>(lo[1]), static_cast<int>(lo[2]),
+                    static_cast<int>(lo[3]), static_cast<int>(hi[0]), static_cast<int>(hi[1]),
+                    static_cast<int>(hi[2]), static_cast<int>(hi[3])};
+    };
+    auto rfa8 = [&](int slot, int mb) { read_frag8(slot, false, wm * kBigWM + mb * 32 + lr, fa8[mb]); };
+    auto rfb8 = [&](int slot, int nb) { read_frag8(slot, true, wn * kBigWN + nb * 32 + lr, fb8[nb]); };
+    auto mma8 = [&](int mb, int nb) {
+        // operand formats 0 / 0: e4m3 for both; scales 127: 2^0
+        acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb8[nb], fa8[mb], acc[mb][nb], 0, 0,
+                                                                       0, 127, 0, 127);
+    };
 
     // prologue: the first tile's slices 0..2; fp8 rows of slice 0 are
     // converted once this wave's request for them has landed (the barrier at
@@ -742,7 +781,15 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
             nxt = cur;
             nsrc = src;
         }
-        load_frags(0, 0, fa0, fb0, src, cur.shared);
+        if constexpr (kF8W) {
+            // slice 0: both weight fragments and the first two token ones
+            rfb8(0, 0);
+            rfb8(0, 1);
+            rfa8(0, 0);
+            rfa8(0, 1);
+        } else {
+            load_frags(0, 0, fa0, fb0, src, cur.shared);
+        }
 #pragma unroll
         for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -767,6 +814,47 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
             const TileSrc& ts = iss == 2 ? nsrc : src;
             const bool tsh = iss == 2 ? nxt.shared : cur.shared;
             const SliceReq q = slice_req(ts, tsh, iss == 2 ? k + 3 - KT : k + 3, (j + 3) & 3);
+            if constexpr (kF8W) {
+                // first half: MFMAs of token blocks 0, 1 on slice k, each
+                // with one request of slice k+3; the fragments of token
+                // blocks 2, 3 of slice k are read meanwhile
+                static_for<0, 4>([&](auto I) {
+                    constexpr int i = decltype(I)::value;
+                    if constexpr (!idle) mma8(i & 1, i >> 1);
+                    if constexpr (iss != 0) issue_one(ts, tsh, q, I);
+                    if constexpr (!idle && i < 2) rfa8(j, 2 + i);
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+                if constexpr (wn_ >= 0) {
+                    // second half: slice k+1 must have landed; token blocks
+                    // 2, 3 on slice k, each MFMA followed by a read of the
+                    // next slice's fragment its predecessors no longer need
+                    wait_vmcnt<wn_ * kBigLoads>();
+                    ring_barrier();
+                    __builtin_amdgcn_sched_barrier(0);
+                    if constexpr (!idle) {
+                        constexpr int nj = (j + 1) & 3;
+                        mma8(2, 0);
+                        rfa8(nj, 0);
+                        __builtin_amdgcn_sched_barrier(0);
+                        mma8(3, 0);
+                        rfa8(nj, 1);
+                        __builtin_amdgcn_sched_barrier(0);
+                        mma8(2, 1);
+                        rfb8(nj, 0);
+                        __builtin_amdgcn_sched_barrier(0);
+                        mma8(3, 1);
+                        rfb8(nj, 1);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                } else if constexpr (!idle) {
+                    mma8(2, 0);
+                    mma8(3, 0);
+                    mma8(2, 1);
+                    mma8(3, 1);
+                }
+                return;
+            }
             // fp8 rows: this wave converts its rows of slice k+1 (the next
             // tile's slice 0 in a tile's last step), every wave alike, idle
             // or not. Its codes request was the first of the eight issued
@@ -850,19 +938,62 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
                 if (ok) store16(rowp + 16 * p + 8 * lg, u32x4{s0[0], s1[0], s0[1], s1[1]});
             }
         };
+        // fp8-weight modes: the weight rows' scales of this lane's 16 output
+        // features per 32-row block (4*lg + 8*q + u, u < 4): up-projection
+        // s1, qsum1, s3, qsum3 of hidden features fb + ...; down-projection
+        // s2 of output features (per block nb)
+        f32x4 wsc[4][4];
+        if constexpr (kF8W) {
+            const int64_t G = a.E + a.S, H = a.h;
+            if constexpr (kDown) {
+                const float* s2 = a.wscale + 4 * G * H + static_cast<int64_t>(cur.shared ? a.E : cur.g) * a.d +
+                                  cur.nt * kBigBN + wn * kBigWN + 4 * lg;
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        wsc[nb][q] = *reinterpret_cast<const f32x4*>(s2 + nb * 32 + 8 * q);
+            } else {
+                const float* sc = a.wscale + static_cast<int64_t>(cur.g) * H + cur.nt * (kBigBN / 2) +
+                                  wn * (kBigWN / 2) + 4 * lg;
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        wsc[t][q] = *reinterpret_cast<const f32x4*>(sc + t * G * H + 8 * q);
+            }
+        }
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             const int r = cur.m0 + wm * kBigWM + mb * 32 + lr;
             const bool ok = r < cur.nrows;  // the same for lanes lr and lr+32
             const int64_t row = static_cast<int64_t>(cur.row_base) + r;
-            if (MODE == kModeDown) {
+            // fp8-weight modes: this token row's scale (and centre)
+            float ts = 1.0f, tc = 0.0f;
+            if constexpr (kF8W) {
+                const int rc = min(r, cur.nrows - 1);
+                if constexpr (kDown) {
+                    ts = cur.shared ? a.hsc_s[rc] : a.hsc_r[cur.row_base + rc];
+                } else {
+                    const float2 q2 = cur.shared
+                                          ? *reinterpret_cast<const float2*>(a.q_shared + 2 * static_cast<int64_t>(rc))
+                                          : *reinterpret_cast<const float2*>(a.qparams + 2 * (static_cast<int64_t>(cur.row_base) + rc));
+                    ts = q2.x;
+                    tc = q2.y;
+                }
+            }
+            if (kDown) {
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
                     uint32_t w[4][2];
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        w[q][0] = pack_bf16x2(acc[mb][nb][4 * q], acc[mb][nb][4 * q + 1]);
-                        w[q][1] = pack_bf16x2(acc[mb][nb][4 * q + 2], acc[mb][nb][4 * q + 3]);
+                        float v[4];
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+                            v[u] = kF8W ? ts * (wsc[nb][q][u] * acc[mb][nb][4 * q + u]) : acc[mb][nb][4 * q + u];
+                        w[q][0] = pack_bf16x2(v[0], v[1]);
+                        w[q][1] = pack_bf16x2(v[2], v[3]);
                     }
                     const int col = cur.nt * kBigBN + wn * kBigWN + nb * 32;
                     store_groups(out + row * a.d + col, w, ok);
@@ -878,8 +1009,15 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
                     for (int q = 0; q < 4; ++q) {
                         float hv[4];
 #pragma unroll
-                        for (int u = 0; u < 4; ++u)
-                            hv[u] = silu(acc[mb][2 * pq][4 * q + u]) * acc[mb][2 * pq + 1][4 * q + u];
+                        for (int u = 0; u < 4; ++u) {
+                            float av = acc[mb][2 * pq][4 * q + u], bv = acc[mb][2 * pq + 1][4 * q + u];
+                            if constexpr (kF8W) {
+                                // sum_i (qx s + c) (qw sw) = sw (s sum qx qw + c sum qw)
+                                av = wsc[0][q][u] * __builtin_fmaf(ts, av, tc * wsc[1][q][u]);
+                                bv = wsc[2][q][u] * __builtin_fmaf(ts, bv, tc * wsc[3][q][u]);
+                            }
+                            hv[u] = silu(av) * bv;
+                        }
                         w[q][0] = pack_bf16x2(hv[0], hv[1]);
                         w[q][1] = pack_bf16x2(hv[2], hv[3]);
                     }
@@ -1247,6 +1385,90 @@ hipError_t launch_ffn_plan128(const moe_shape& s, const int32_t* offsets, int32_
     ffn_plan_kernel<<<1, 256, 0, st>>>(offsets, s.E, s.S, s.T, kBM, plan, nullptr, 0, 0, 0,
                                        nullptr);
     return hipGetLastError();
+}
+
+hipError_t launch_hidden_quant(const moe_shape& s, int hs, const void* h_r, const void* h_s,
+                               const int32_t* offsets, uint8_t* h8_r, uint8_t* h8_s,
+                               float* hsc_r, float* hsc_s, hipStream_t st);
+
+// The fp8-weight path of the expert stage takes the persistent kernels only:
+// d and h multiples of 256 (whole groups of four 64-value slices) and every
+// operand below 4 GiB.
+bool f8w_supported(const moe_shape& s) {
+    return use_big_tiles(s) && s.d % 256 == 0 && s.h % 256 == 0;
+}
+
+// The expert stage with fp8 weights: up-projection on the fp8 matrix cores
+// (routed rows x_perm and the shared experts' rows x8, both per-token fp8
+// codes), the hidden rows quantised per row, then the down-projection on the
+// fp8 matrix cores. Weight codes w1q, w3q [G, h, d], w2q [G, d, h] with the
+// scales of launch_quantize_weights.
+hipError_t launch_grouped_ffn_f8w(const moe_shape& s, const void* x_perm, const float* qparams,
+                                  const int32_t* offsets, const void* x8, const float* q8,
+                                  const uint8_t* w1q, const uint8_t* w3q, const uint8_t* w2q,
+                                  const float* wscale, void* y_perm, void* y_shared,
+                                  int32_t* plan, void* h_r, void* h_s, uint8_t* h8_r,
+                                  uint8_t* h8_s, float* hsc_r, float* hsc_s, bool plan_done,
+                                  hipStream_t st, const Marks* mk) {
+    const PlanLayout pl = plan_layout(s);
+    int32_t* counters = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(plan) + pl.counters);
+    int4* tiles = reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(plan) + pl.tiles);
+    if (!plan_done)
+        ffn_plan_kernel<<<plan_blocks(pl), 256, 0, st>>>(offsets, s.E, s.S, s.T, kBigBM, plan, tiles,
+                                                         pl.n_up, pl.ntn_up, pl.ntn_down, counters);
+    mark(mk);
+    const uint64_t Tk = static_cast<uint64_t>(s.T) * s.k, T = static_cast<uint64_t>(s.T);
+    const uint64_t G = static_cast<uint64_t>(s.E + s.S);
+    GemmArgs a{};
+    a.qparams = qparams;
+    a.offsets = offsets;
+    a.plan = plan;
+    a.tiles = tiles;
+    a.counters = counters;
+    a.tile_meta = counters + kTileMetaHalf;
+    a.q_shared = q8;
+    a.wscale = wscale;
+    a.hsc_r = hsc_r;
+    a.hsc_s = hsc_s;
+    a.T = s.T;
+    a.E = s.E;
+    a.S = s.S;
+    a.d = s.d;
+    a.h = s.h;
+    a.hs = s.h;
+    // up-projection + SwiGLU
+    a.a_routed = static_cast<const uint8_t*>(x_perm);
+    a.a_shared = static_cast<const uint8_t*>(x8);
+    a.a_routed_bytes = static_cast<uint32_t>(Tk * s.d);
+    a.a_shared_bytes = static_cast<uint32_t>(s.S > 0 ? T * s.d : 0);
+    a.w_bytes = static_cast<uint32_t>(G * s.h * s.d);
+    a.wa = w1q;
+    a.wb = w3q;
+    a.out_routed = static_cast<uint8_t*>(h_r);
+    a.out_shared = static_cast<uint8_t*>(h_s);
+    a.ntn = 2 * s.h / kBigBN;
+    hipError_t err = launch_gemm<kModeUpF8W>(a, max_mtiles(s, kBigBM, false), true, st);
+    mark(mk);
+    if (err != hipSuccess) return err;
+    // hidden rows -> per-row fp8 codes
+    err = launch_hidden_quant(s, s.h, h_r, h_s, offsets, h8_r, h8_s, hsc_r, hsc_s, st);
+    mark(mk);
+    if (err != hipSuccess) return err;
+    // down-projection
+    a.a_routed = h8_r;
+    a.a_shared = h8_s;
+    a.a_routed_bytes = static_cast<uint32_t>(Tk * s.h);
+    a.a_shared_bytes = static_cast<uint32_t>(T * s.S * s.h);
+    a.wa = w2q;
+    a.wb = nullptr;
+    a.out_routed = static_cast<uint8_t*>(y_perm);
+    a.out_shared = static_cast<uint8_t*>(y_shared);
+    a.tiles = tiles + pl.n_up;
+    a.counters = counters + 8;
+    a.ntn = s.d / kBigBN;
+    err = launch_gemm<kModeDownF8W>(a, max_mtiles(s, kBigBM, true), true, st);
+    mark(mk);
+    return err;
 }
 
 }  // namespace moe

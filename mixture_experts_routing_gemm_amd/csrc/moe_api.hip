@@ -19,7 +19,7 @@ hipError_t launch_dispatch(const moe_shape& s, const void* x, const int32_t* top
                            int32_t* src_token, void* x_perm, float* qparams, int32_t* rank,
                            int32_t* blk, int32_t* pre, int32_t* first_loads, uint32_t* qstats,
                            uint32_t* hdr, const FfnPlanArgs& fp, hipStream_t st,
-                           const Marks* mk);
+                           const Marks* mk, uint8_t* x_self = nullptr, float* q_self = nullptr);
 hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const float* qparams,
                               const int32_t* offsets, const void* x, const void* w1,
                               const void* w3, const void* w2, void* y_perm, void* y_shared,
@@ -39,6 +39,18 @@ hipError_t launch_combine_backward(const moe_shape& s, const void* dy, const voi
                                    float* dtopk_w, hipStream_t st);
 
 size_t ffn_backward_ws_bytes(const moe_shape& s);
+size_t fp8w_scale_floats(const moe_shape& s);
+bool f8w_supported(const moe_shape& s);
+hipError_t launch_quantize_weights(const moe_shape& s, const void* w1, const void* w3,
+                                   const void* w2, uint8_t* w1q, uint8_t* w3q, uint8_t* w2q,
+                                   float* wscale, hipStream_t st);
+hipError_t launch_grouped_ffn_f8w(const moe_shape& s, const void* x_perm, const float* qparams,
+                                  const int32_t* offsets, const void* x8, const float* q8,
+                                  const uint8_t* w1q, const uint8_t* w3q, const uint8_t* w2q,
+                                  const float* wscale, void* y_perm, void* y_shared,
+                                  int32_t* plan, void* h_r, void* h_s, uint8_t* h8_r,
+                                  uint8_t* h8_s, float* hsc_r, float* hsc_s, bool plan_done,
+                                  hipStream_t st, const Marks* mk);
 hipError_t launch_ffn_backward(const moe_shape& s, const void* x_perm, const float* qparams,
                                const int32_t* offsets, const void* x, const void* w1,
                                const void* w3, const void* w2, const void* dy_perm,
@@ -70,6 +82,10 @@ static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
 namespace {
 
 constexpr size_t kHeaderBytes = 256;
+// kernels of moe_forward_fp8w, in order: gate_topk, dispatch_rank,
+// dispatch_scan, dispatch_permute_fp8, ffn_plan, ffn_up, ffn_hidden_quant,
+// ffn_down, combine
+constexpr int kFp8wKernels = 9;
 
 size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
@@ -78,6 +94,7 @@ size_t act_bytes(int32_t dt) { return dt == MOE_F32 ? 4 : (dt == MOE_BF16 ? 2 : 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct Layout {
+    size_t x8 = 0, q8 = 0, h8_r = 0, h8_s = 0, hsc_r = 0, hsc_s = 0;  // fp8-weight forward
     size_t fbwd = 0, part = 0, rank = 0, blk = 0, pre = 0, loads = 0, qstats = 0, plan = 0, x_perm = 0, qparams = 0, h_r = 0, h_s = 0, y_perm = 0,
            y_sh = 0, total = 0;
 };
@@ -93,8 +110,9 @@ Layout layout(const moe_shape& s, int stage) {
         off = align256(off + bytes);
         return at;
     };
-    const bool disp = stage == MOE_STAGE_DISPATCH || stage == MOE_STAGE_FORWARD;
-    const bool ffn = stage == MOE_STAGE_FFN || stage == MOE_STAGE_FORWARD;
+    const bool fwd = stage == MOE_STAGE_FORWARD || stage == MOE_STAGE_FORWARD_FP8W;
+    const bool disp = stage == MOE_STAGE_DISPATCH || fwd;
+    const bool ffn = stage == MOE_STAGE_FFN || fwd;
     if (disp) {
         L.rank = take(T * k * 4);
         L.blk = take(nblk * E * 4);
@@ -109,11 +127,20 @@ Layout layout(const moe_shape& s, int stage) {
         L.h_r = take(T * k * hs * es);
         L.h_s = take(T * S * hs * es);
     }
-    if (stage == MOE_STAGE_FORWARD) {
+    if (fwd) {
         L.x_perm = take(T * k * d * esd);
         L.qparams = take(s.dispatch == MOE_FP8_E4M3 ? T * k * 8 : 0);
         L.y_perm = take(T * k * d * es);
         L.y_sh = take(S > 0 ? T * d * es : 0);
+    }
+    if (stage == MOE_STAGE_FORWARD_FP8W) {
+        // the shared experts' fp8 token rows, the hidden rows' codes and scales
+        L.x8 = take(S > 0 ? T * d : 0);
+        L.q8 = take(S > 0 ? T * 8 : 0);
+        L.h8_r = take(T * k * static_cast<size_t>(s.h));
+        L.h8_s = take(T * S * static_cast<size_t>(s.h));
+        L.hsc_r = take(T * k * 4);
+        L.hsc_s = take(S > 0 ? T * 4 : 0);
     }
     if (stage == MOE_STAGE_GATE_BACKWARD) {
         // one float32 [E, d] partial of the weight gradient per token range
@@ -137,7 +164,7 @@ int32_t check_shape(const moe_shape* s, bool ffn) {
     if (s == nullptr) return MOE_ERR_INVALID_ARG;
     if (s->T < 0 || s->d <= 0 || s->E <= 0 || s->k <= 0 || s->S < 0 || s->h <= 0 || s->k > s->E ||
         s->capacity < 0 || (s->overflow != MOE_OVERFLOW_DROP && s->overflow != MOE_OVERFLOW_REASSIGN) ||
-        s->quant < MOE_QUANT_TOKEN || s->quant > MOE_QUANT_GLOBAL ||
+        s->quant < MOE_QUANT_TOKEN || s->quant > MOE_QUANT_TOKEN_ABSMAX ||
         (s->quant != MOE_QUANT_TOKEN && s->dispatch != MOE_FP8_E4M3))
         return MOE_ERR_INVALID_ARG;
     if (s->E > kMaxE || s->k > kMaxK || s->S > kMaxS) return MOE_ERR_UNSUPPORTED;
@@ -150,6 +177,13 @@ int32_t check_shape(const moe_shape* s, bool ffn) {
         return MOE_ERR_UNSUPPORTED;
     if (s->d > (1 << 20) || s->h > (1 << 20)) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
+}
+
+// the fp8-weight path: bf16 activations with fp8 rows quantised per token
+// (affine or symmetric), on the persistent expert GEMMs
+bool f8w_shape_ok(const moe_shape& s) {
+    return s.act == MOE_BF16 && s.dispatch == MOE_FP8_E4M3 &&
+           (s.quant == MOE_QUANT_TOKEN || s.quant == MOE_QUANT_TOKEN_ABSMAX) && f8w_supported(s);
 }
 
 int32_t check_ptrs(std::initializer_list<const void*> required) {
@@ -243,6 +277,47 @@ int32_t scratch_address(void** out) {
     return MOE_OK;
 }
 
+int32_t forward_fp8w_impl(const moe_shape* s, const void* x, const void* w_gate,
+                          const float* bias, const uint8_t* w1q, const uint8_t* w3q,
+                          const uint8_t* w2q, const float* wscale, void* y, int32_t* topk_idx,
+                          float* topk_w, int32_t* counts, int32_t* offsets, int32_t* dest_row,
+                          int32_t* src_token, void* ws, size_t ws_bytes, void* stream,
+                          const Marks* mk) {
+    MOE_TRY(check_shape(s, true));
+    if (!f8w_shape_ok(*s)) return MOE_ERR_UNSUPPORTED;
+    if (s->T == 0) return MOE_OK;
+    MOE_TRY(check_ptrs({x, w_gate, w1q, w3q, w2q, wscale, y, topk_idx, topk_w, counts, offsets,
+                        dest_row, src_token}));
+    MOE_TRY(check_opt({bias}));
+    MOE_TRY(check_ws(*s, MOE_STAGE_FORWARD_FP8W, ws, ws_bytes));
+    const Layout L = layout(*s, MOE_STAGE_FORWARD_FP8W);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    mark(mk);
+    MOE_TRY(hip_status(launch_gate_topk(*s, x, w_gate, bias, topk_idx, topk_w, nullptr, st, mk)));
+    mark(mk);
+    void* x_perm = at<void>(ws, L.x_perm);
+    float* qp = at<float>(ws, L.qparams);
+    uint8_t* x8 = s->S > 0 ? at<uint8_t>(ws, L.x8) : nullptr;
+    float* q8 = s->S > 0 ? at<float>(ws, L.q8) : nullptr;
+    FfnPlanArgs fplan;
+    const bool plan_done = ffn_fused_plan(*s, at<int32_t>(ws, L.plan), &fplan);
+    MOE_TRY(hip_status(launch_dispatch(*s, x, topk_idx, counts, offsets, dest_row, src_token,
+                                       x_perm, qp, at<int32_t>(ws, L.rank), at<int32_t>(ws, L.blk),
+                                       at<int32_t>(ws, L.pre), at<int32_t>(ws, L.loads),
+                                       at<uint32_t>(ws, L.qstats), at<uint32_t>(ws, 0), fplan, st,
+                                       mk, x8, q8)));
+    void* y_perm = at<void>(ws, L.y_perm);
+    void* y_sh = s->S > 0 ? at<void>(ws, L.y_sh) : nullptr;
+    MOE_TRY(hip_status(launch_grouped_ffn_f8w(
+        *s, x_perm, qp, offsets, x8, q8, w1q, w3q, w2q, wscale, y_perm, y_sh,
+        at<int32_t>(ws, L.plan), at<void>(ws, L.h_r), at<void>(ws, L.h_s),
+        at<uint8_t>(ws, L.h8_r), at<uint8_t>(ws, L.h8_s), at<float>(ws, L.hsc_r),
+        s->S > 0 ? at<float>(ws, L.hsc_s) : nullptr, plan_done, st, mk)));
+    MOE_TRY(hip_status(launch_combine(*s, y_perm, y_sh, dest_row, topk_w, y, st)));
+    mark(mk);
+    return MOE_OK;
+}
+
 const char* const kKernelNames[] = {"gate_topk",  "dispatch_rank", "dispatch_scan",
                                     "dispatch_permute", "ffn_plan", "ffn_up",
                                     "ffn_down",   "combine"};
@@ -252,7 +327,9 @@ const char* const kKernelNames[] = {"gate_topk",  "dispatch_rank", "dispatch_sca
 extern "C" {
 
 size_t moe_workspace_bytes(const moe_shape* s, int32_t stage) {
-    if (stage < MOE_STAGE_GATE || stage > MOE_STAGE_FFN_BACKWARD) return 0;
+    if (stage < MOE_STAGE_GATE || stage > MOE_STAGE_FORWARD_FP8W) return 0;
+    if (stage == MOE_STAGE_FORWARD_FP8W && (check_shape(s, true) != MOE_OK || !f8w_shape_ok(*s)))
+        return 0;
     const bool ffn = stage == MOE_STAGE_FFN || stage == MOE_STAGE_FORWARD;
     if (check_shape(s, ffn) != MOE_OK) return 0;
     return layout(*s, stage).total;
@@ -426,6 +503,35 @@ int32_t moe_grouped_ffn_backward(const moe_shape* s, const void* x_perm, const f
     return hip_status(launch_ffn_backward(*s, x_perm, qparams, offsets, x, w1, w3, w2, dy_perm,
                                           dy_shared, dx_perm, dx_shared, dw1, dw3, dw2,
                                           at<void>(ws, L.fbwd), st, nullptr));
+}
+
+size_t moe_fp8_weight_scale_floats(const moe_shape* s) {
+    if (check_shape(s, true) != MOE_OK) return 0;
+    return fp8w_scale_floats(*s);
+}
+
+int32_t moe_quantize_weights(const moe_shape* s, const void* w1, const void* w3, const void* w2,
+                             uint8_t* w1q, uint8_t* w3q, uint8_t* w2q, float* wscale,
+                             void* stream) {
+    MOE_TRY(check_shape(s, true));
+    if (s->act != MOE_BF16 || s->d % 8 != 0 || s->h % 8 != 0) return MOE_ERR_UNSUPPORTED;
+    MOE_TRY(check_ptrs({w1, w3, w2, w1q, w3q, w2q, wscale}));
+    return hip_status(launch_quantize_weights(*s, w1, w3, w2, w1q, w3q, w2q, wscale,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_forward_fp8w(const moe_shape* s, const void* x, const void* w_gate, const float* bias,
+                         const uint8_t* w1q, const uint8_t* w3q, const uint8_t* w2q,
+                         const float* wscale, void* y, int32_t* topk_idx, float* topk_w,
+                         int32_t* counts, int32_t* offsets, int32_t* dest_row, int32_t* src_token,
+                         void* ws, size_t ws_bytes, void* stream, void* const* events,
+                         int32_t n_events) {
+    if (events != nullptr && n_events < kFp8wKernels + 1) return MOE_ERR_INVALID_ARG;
+    Marks mk{reinterpret_cast<hipEvent_t const*>(events), n_events, 0,
+             static_cast<hipStream_t>(stream)};
+    return forward_fp8w_impl(s, x, w_gate, bias, w1q, w3q, w2q, wscale, y, topk_idx, topk_w,
+                             counts, offsets, dest_row, src_token, ws, ws_bytes, stream,
+                             events != nullptr ? &mk : nullptr);
 }
 
 int32_t moe_forward(const moe_shape* s, const void* x, const void* w_gate, const float* bias,

@@ -270,7 +270,8 @@ def ffn_backward(inp, offsets, src_token, dy_perm, dy_shared=None, xq=None, nthr
 #   * every weight row (one output feature of W1, W3 or W2) gets its own
 #     symmetric absmax scale: the same affine map as the activations, applied
 #     to the symmetric range [-max|w|, max|w|], so the centre is 0 and the
-#     scale is max|w| / 448;
+#     scale is max|w| / 448 (the shared experts' W2 rows jointly over their
+#     concatenated blocks);
 #   * the shared experts read the same per-token fp8 rows as the routed ones;
 #   * the hidden vector silu(a) * b is rounded to bf16 (float32 first) and
 #     quantised per row with a symmetric absmax scale over the row's h values
@@ -304,10 +305,21 @@ def quantize_weight_rows(w, nthreads=None):
 
 def quantize_expert_weights(inp, nthreads=None):
     """(q1, s1, q3, s3, q2, s2): every weight row of W1, W3 [G, h, d] and W2
-    [G, d, h] as symmetric absmax e4m3 codes with a float32 scale per row."""
+    [G, d, h] as symmetric absmax e4m3 codes with a float32 scale per row.
+    The shared experts' W2 rows are quantised jointly: row n of the S
+    concatenated blocks [W2_E[n] | ... | W2_{E+S-1}[n]] has one scale (so
+    that their down-projections can share one accumulator)."""
+    cfg = inp.cfg
+    E, S, h = cfg.E, cfg.S, cfg.h
     q1, s1 = quantize_weight_rows(inp.w1, nthreads)
     q3, s3 = quantize_weight_rows(inp.w3, nthreads)
     q2, s2 = quantize_weight_rows(inp.w2, nthreads)
+    if S:
+        cat = np.concatenate([inp.w2[E + s] for s in range(S)], axis=1)  # [d, S*h]
+        qc, sc = quantize_weight_rows(cat, nthreads)
+        for s in range(S):
+            q2[E + s] = qc[:, s * h:(s + 1) * h]
+            s2[E + s] = sc
     return q1, s1, q3, s3, q2, s2
 
 

@@ -15,7 +15,7 @@ LIB = os.path.join(ROOT, "mixture_experts_routing_gemm_amd", "libmoe_mi355x.so")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -67,7 +67,7 @@ FAKE = 0x100000  # an aligned, never-dereferenced address: every call below fail
     (dict(E=300), -2), (dict(k=9, E=16), -2), (dict(k=5, E=4), -1), (dict(T=-1), -1),
     (dict(S=9), -2), (dict(d=100), -2), (dict(d=200, dispatch=2), -2), (dict(act=2), -2),
     (dict(dispatch=2, act=0), -2), (dict(d=0), -1), (dict(capacity=-1), -1),
-    (dict(capacity=4, overflow=2), -1), (dict(quant=1), -1), (dict(quant=3, dispatch=2), -1),
+    (dict(capacity=4, overflow=2), -1), (dict(quant=1), -1), (dict(quant=4, dispatch=2), -1),
 ])
 def test_forward_rejects_bad_shapes(mm, kw, status):
     base = dict(T=64, d=256, E=8, k=2, S=1, h=128, act=1, dispatch=None, capacity=0, overflow=0,

@@ -1,0 +1,175 @@
+"""GPU parity of the fp8-weight path and of the symmetric absmax mode.
+
+* moe_quantize_weights against the oracle's weight quantiser: every code
+  and every scale bit-exact (the shared experts' W2 rows jointly), and the
+  per-row code sums within float32 rounding of the oracle's float64 sums.
+* moe_forward_fp8w against oracle.layer_dense_fp8w: routing and dispatch
+  arrays bit-exact, the layer output within the fp8 bound (6e-2) over the
+  whole tensor and on every token.
+* MOE_QUANT_TOKEN_ABSMAX on the bf16-weight path: the dispatched codes and
+  (scale, centre = 0) bit-exact against the oracle's map over [-max|x|,
+  max|x|], and the layer output within 6e-2.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import ORACLE_THREADS, RowErrors, dev, host, requires_gpu, say
+from moe_workloads import CONFIGS, make_inputs
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+
+def _mm():
+    import mixture_experts_routing_gemm_amd as mm
+    return mm
+
+
+def _cfg(**kw):
+    base = dict(T=600, d=256, E=8, k=2, S=2, h=256, sigma_w=0.05)
+    base.update(kw)
+    return dataclasses.replace(CONFIGS["fp8_dispatch"], name="fp8w", **base)
+
+
+def quantize_on_gpu(mm, cfg, inp):
+    shape = mm.shape_of(cfg)
+    G, h, d = cfg.E + cfg.S, cfg.h, cfg.d
+    w1q = torch.empty((G, h, d), dtype=torch.uint8, device="cuda")
+    w3q = torch.empty((G, h, d), dtype=torch.uint8, device="cuda")
+    w2q = torch.empty((G, d, h), dtype=torch.uint8, device="cuda")
+    n = mm.moe_fp8_weight_scale_floats(shape)
+    assert n == 4 * G * h + G * d
+    wsc = torch.empty(n, dtype=torch.float32, device="cuda")
+    mm.moe_quantize_weights(shape, dev(inp.w1), dev(inp.w3), dev(inp.w2), w1q, w3q, w2q, wsc)
+    torch.cuda.synchronize()
+    return w1q, w3q, w2q, wsc
+
+
+def check_weights(cfg, inp, wq_gpu, wq_ref):
+    G, h, d = cfg.E + cfg.S, cfg.h, cfg.d
+    w1q, w3q, w2q, wsc = (host(t) for t in wq_gpu)
+    q1, s1, q3, s3, q2, s2 = wq_ref
+    assert np.array_equal(w1q, q1) and np.array_equal(w3q, q3) and np.array_equal(w2q, q2)
+    o = 0
+    for ref in (s1, None, s3, None):
+        got = wsc[o:o + G * h].reshape(G, h)
+        if ref is not None:
+            assert np.array_equal(got.view(np.uint32), ref.astype(np.float32).view(np.uint32))
+        o += G * h
+    assert np.array_equal(wsc[o:o + G * d].reshape(G, d).view(np.uint32),
+                          s2.astype(np.float32).view(np.uint32))
+    # the code sums of W1 / W3 rows (float32 sums against float64)
+    table = np.array([oracle.e4m3_decode(c) for c in range(256)])
+    for qs, q in ((wsc[G * h:2 * G * h], q1), (wsc[3 * G * h:4 * G * h], q3)):
+        ref = table[q].sum(axis=2).reshape(-1)
+        assert np.allclose(qs, ref, rtol=1e-6, atol=1e-3)
+
+
+def run_forward(cfg, seed=3, check_quant=True):
+    mm = _mm()
+    say(f"[fp8w] T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} S={cfg.S} h={cfg.h} quant={cfg.quant}")
+    inp = make_inputs(cfg, seed=seed)
+    shape = mm.shape_of(cfg)
+    wq_gpu = quantize_on_gpu(mm, cfg, inp)
+    wq_ref = oracle.quantize_expert_weights(inp, nthreads=ORACLE_THREADS)
+    if check_quant:
+        check_weights(cfg, inp, wq_gpu, wq_ref)
+    T, E, k, d = cfg.T, cfg.E, cfg.k, cfg.d
+    out = dict(y=torch.empty((T, d), dtype=torch.bfloat16, device="cuda"),
+               idx=torch.empty((T, k), dtype=torch.int32, device="cuda"),
+               w=torch.empty((T, k), dtype=torch.float32, device="cuda"),
+               counts=torch.empty(E, dtype=torch.int32, device="cuda"),
+               offsets=torch.empty(E + 1, dtype=torch.int32, device="cuda"),
+               dest=torch.empty((T, k), dtype=torch.int32, device="cuda"),
+               src=torch.empty(T * k, dtype=torch.int32, device="cuda"))
+    ws = mm.alloc_workspace(shape, mm.STAGE_FORWARD_FP8W)
+    bias = None if inp.bias is None else dev(inp.bias)
+    w1q, w3q, w2q, wsc = wq_gpu
+    mm.moe_forward_fp8w(shape, dev(inp.x), dev(inp.wg), bias, w1q, w3q, w2q, wsc, out["y"],
+                        out["idx"], out["w"], out["counts"], out["offsets"], out["dest"],
+                        out["src"], ws)
+    torch.cuda.synchronize()
+    assert mm.moe_get_device_error(ws) == mm.MOE_OK
+    z = oracle.gate_logits(inp.x, inp.wg, inp.bias, nthreads=ORACLE_THREADS)
+    idx, w = oracle.select_topk(z, k)
+    counts, offsets, dest, src = oracle.dispatch(idx, E)
+    assert np.array_equal(host(out["idx"]), idx)
+    assert np.array_equal(host(out["counts"]), counts)
+    assert np.array_equal(host(out["offsets"]), offsets)
+    assert np.array_equal(host(out["dest"]), dest)
+    assert np.array_equal(host(out["src"]), src)
+    say("[fp8w] oracle layer with fp8 weights")
+    _, _, oy = oracle.layer_dense_fp8w(inp, wq_ref, nthreads=ORACLE_THREADS, gate=(idx, w))
+    acc = RowErrors()
+    acc.add(host(out["y"]), oy)
+    acc.check(f"[fp8w] {cfg.name} y", cfg.tol_y)
+    # the same bits again
+    y0 = host(out["y"]).copy()
+    mm.moe_forward_fp8w(shape, dev(inp.x), dev(inp.wg), bias, w1q, w3q, w2q, wsc, out["y"],
+                        out["idx"], out["w"], out["counts"], out["offsets"], out["dest"],
+                        out["src"], ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out["y"]), y0)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(),
+    dict(S=0, E=16, k=4, T=1000),
+    dict(S=1, quant="token_absmax", T=333),
+    dict(T=2048, d=512, h=512, E=64, k=6, S=2),
+], ids=["small", "no_shared", "absmax_rows", "wider"])
+def test_fp8_weight_forward(kw):
+    run_forward(_cfg(**kw))
+
+
+def test_fp8_weight_forward_full_size():
+    # the fp8_dispatch workload at its full size with fp8 weights
+    run_forward(dataclasses.replace(CONFIGS["fp8_dispatch"], name="fp8_dispatch_fp8w"),
+                check_quant=True)
+
+
+def test_fp8_weight_shape_limits():
+    mm = _mm()
+    s = mm.make_shape(64, 384, 8, 2, 1, 256, "bf16", "fp8")  # d % 256 != 0
+    assert mm.moe_workspace_bytes(s, mm.STAGE_FORWARD_FP8W) == 0
+    s = mm.make_shape(64, 512, 8, 2, 1, 256, "bf16")  # bf16 rows: no fp8 path
+    assert mm.moe_workspace_bytes(s, mm.STAGE_FORWARD_FP8W) == 0
+
+
+def test_token_absmax_dispatch_and_layer():
+    mm = _mm()
+    cfg = dataclasses.replace(CONFIGS["fp8_dispatch"], T=900, d=512, E=16, k=4, S=1, h=256,
+                              sigma_w=0.05, quant="token_absmax", name="absmax")
+    inp = make_inputs(cfg, seed=4)
+    shape = mm.shape_of(cfg)
+    assert shape.quant == mm.MOE_QUANT_TOKEN_ABSMAX
+    buf = mm.ForwardBuffers(shape)
+    buf.run(dev(inp.x), dev(inp.wg), None, dev(inp.w1), dev(inp.w3), dev(inp.w2))
+    torch.cuda.synchronize()
+    idx, w, _ = oracle.gate_topk(inp.x, inp.wg, cfg.k, None, nthreads=ORACLE_THREADS)
+    counts, offsets, dest, src = oracle.dispatch(idx, cfg.E)
+    # the dispatch stage alone: codes and (scale, centre = 0) of every row
+    x_perm = torch.empty((cfg.T * cfg.k, cfg.d), dtype=torch.uint8, device="cuda")
+    qp = torch.empty((cfg.T * cfg.k, 2), dtype=torch.float32, device="cuda")
+    g = [torch.empty(n, dtype=torch.int32, device="cuda") for n in (cfg.E, cfg.E + 1)]
+    gd = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
+    gs = torch.empty(cfg.T * cfg.k, dtype=torch.int32, device="cuda")
+    ws = mm.alloc_workspace(shape, mm.STAGE_DISPATCH)
+    mm.moe_dispatch(shape, dev(inp.x), dev(idx), g[0], g[1], gd, gs, x_perm, qp, ws)
+    torch.cuda.synchronize()
+    x32 = (inp.x.astype(np.uint32) << 16).view(np.float32)
+    q_ref, qp_ref = oracle.fp8_quantize(inp.x, ranges=oracle.symmetric_ranges(x32))
+    assert np.all(qp_ref[:, 1] == 0.0)
+    s64 = src.astype(np.int64)
+    assert np.array_equal(host(x_perm), q_ref[s64])
+    assert np.array_equal(host(qp).view(np.uint32), qp_ref[s64].view(np.uint32))
+    _, _, oy = oracle.layer_dense(inp, nthreads=ORACLE_THREADS, gate=(idx, w))
+    acc = RowErrors()
+    acc.add(host(buf.y), oy)
+    acc.check("[absmax] y", cfg.tol_y)

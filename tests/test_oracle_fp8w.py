@@ -101,8 +101,9 @@ def torch_layer_fp8w(inp):
     y = torch.zeros((cfg.T, cfg.d), dtype=torch.float64)
     if S:
         hq = qh(torch.cat([hidden(v, E + s) for s in range(S)], dim=1))
-        for s in range(S):
-            y += hq[:, s * h:(s + 1) * h] @ deq(inp.w2[E + s]).T
+        # the shared W2 rows quantised jointly over the S blocks
+        w2s = deq(np.concatenate([inp.w2[E + s] for s in range(S)], axis=1))
+        y += hq @ w2s.T
     for t in range(cfg.T):
         for j in range(k):
             e = int(idx[t, j])
