@@ -62,11 +62,12 @@ sys.path.insert(0, ROOT)
 METRIC = "routed tokens/s per MoE layer fwd (1 GPU); dispatch+combine HBM GB/s; FFN MFMA %"
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0
 F32_VEC_PEAK_TFLOPS = 157.3
 # the gate's canonical fma chain runs on the non-packed float32 vector units
 F32_NONPACKED_PEAK_TFLOPS = 78.6
 HEADLINE = "zipf_stress_bf16"
-DETAIL_CONFIGS = ["deepseekmoe_bf16", "coarse_top2_bf16", "fp8_dispatch"]
+DETAIL_CONFIGS = ["deepseekmoe_bf16", "coarse_top2_bf16", "fp8_dispatch", "fp8_dispatch_fp8w"]
 FLUSH_BYTES = 1 << 30
 
 CSRC = "mixture_experts_routing_gemm_amd/csrc/"
@@ -79,6 +80,7 @@ KERNEL_SOURCES = {
     "dispatch_permute_fp8": CSRC + "dispatch.hip",
     "ffn_up": CSRC + "grouped_ffn.hip",
     "ffn_down": CSRC + "grouped_ffn.hip",
+    "ffn_hidden_quant": CSRC + "fp8_rows.hip",
     "combine": CSRC + "combine.hip",
 }
 
@@ -93,6 +95,7 @@ def algorithmic(cfg, routed=None):
     R = T * k if routed is None else routed
     b = 4 if cfg.act == "f32" else 2
     bp = 1 if cfg.dispatch == "fp8" else b
+    bw = 1 if getattr(cfg, "weights", "act") == "fp8" else b  # bytes per weight
     rows = R + S * T
     xreads = 2 if getattr(cfg, "quant", "token") != "token" else 1
     return {
@@ -102,11 +105,12 @@ def algorithmic(cfg, routed=None):
         + (8 * R if cfg.dispatch == "fp8" else 0),
         "ffn_up_flops": 4 * rows * d * h,
         # token rows in, both weight matrices of every group, hidden rows out
-        "ffn_up_bytes": R * d * bp + S * T * d * b + (E + S) * 2 * h * d * b + rows * h * b
-        + (8 * R if cfg.dispatch == "fp8" else 0),
+        "ffn_up_bytes": R * d * bp + S * T * d * (bw if bw == 1 else b) + (E + S) * 2 * h * d * bw
+        + rows * h * b + (8 * R if cfg.dispatch == "fp8" else 0),
         "ffn_down_flops": 2 * rows * d * h,
         # hidden rows in, W2 of every group, routed rows and shared sum out
-        "ffn_down_bytes": rows * h * b + (E + S) * d * h * b + R * d * b + (T * d * b if S else 0),
+        "ffn_down_bytes": rows * h * (1 if bw == 1 else b) + (E + S) * d * h * bw + R * d * b
+        + (T * d * b if S else 0),
         "combine_bytes": R * d * b + (T * d * b if S else 0) + 8 * T * k + T * d * b,
         # backward of combine: dy once, the forward rows in, their gradients out,
         # routing metadata in and the weight gradients out
@@ -329,16 +333,36 @@ def run_workload(cfg, steps, warmup, flush, with_backward=False, keep_host=False
         inp = None
     shape = mm.shape_of(cfg)
     buf = mm.ForwardBuffers(shape)
-    nk = mm.moe_forward_kernel_count(shape)
-    names = [mm.moe_forward_kernel_name(shape, i) for i in range(nk)]
     stream = torch.cuda.current_stream()
+    fp8w = getattr(cfg, "weights", "act") == "fp8"
+    if fp8w:
+        # fp8 expert weights: quantised once, before anything is timed
+        G = cfg.E + cfg.S
+        w1q = torch.empty((G, cfg.h, cfg.d), dtype=torch.uint8, device="cuda")
+        w3q = torch.empty_like(w1q)
+        w2q = torch.empty((G, cfg.d, cfg.h), dtype=torch.uint8, device="cuda")
+        wsc = torch.empty(mm.moe_fp8_weight_scale_floats(shape), dtype=torch.float32, device="cuda")
+        mm.moe_quantize_weights(shape, w1, w3, w2, w1q, w3q, w2q, wsc, stream)
+        ws8 = mm.alloc_workspace(shape, mm.STAGE_FORWARD_FP8W)
+        names = list(mm.FP8W_KERNELS)
+
+        def forward(events=None):
+            mm.moe_forward_fp8w(shape, x, wg, bias, w1q, w3q, w2q, wsc, buf.y, buf.topk_idx,
+                                buf.topk_w, buf.counts, buf.offsets, buf.dest_row, buf.src_token,
+                                ws8, stream, events)
+    else:
+        names = [mm.moe_forward_kernel_name(shape, i) for i in range(mm.moe_forward_kernel_count(shape))]
+
+        def forward(events=None):
+            buf.run(x, wg, bias, w1, w3, w2, events=events)
+    nk = len(names)
 
     def flush_cache(i):
         flush.fill_(i & 0xFF)
 
     for i in range(warmup):
         flush_cache(i)
-        buf.run(x, wg, bias, w1, w3, w2)
+        forward()
     torch.cuda.synchronize()
 
     def make_events(n):
@@ -365,16 +389,16 @@ def run_workload(cfg, steps, warmup, flush, with_backward=False, keep_host=False
     t0 = time.perf_counter()
     for i in range(steps):
         flush_cache(i)
-        buf.run(x, wg, bias, w1, w3, w2, events=handles[i])
+        forward(handles[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    assert mm.moe_get_device_error(buf.ws) == mm.MOE_OK
+    assert mm.moe_get_device_error(ws8 if fp8w else buf.ws) == mm.MOE_OK
     step_ms = np.array([row[0].elapsed_time(row[nk]) for row in evs])
     up_ms = np.array([row[j_up].elapsed_time(row[j_up + 1]) for row in evs])
 
     for i in range(n_tr):
         flush_cache(i)
-        buf.run(x, wg, bias, w1, w3, w2, events=handles_tr[i])
+        forward(handles_tr[i])
     torch.cuda.synchronize()
     per_kernel = np.array([[row[j].elapsed_time(row[j + 1]) for j in range(nk)] for row in evs_tr])
     kmean = dict(zip(names, per_kernel.mean(axis=0).tolist()))
@@ -385,9 +409,9 @@ def run_workload(cfg, steps, warmup, flush, with_backward=False, keep_host=False
     t_gate = kmean["gate_topk"]
     t_disp = sum(v for n, v in kmean.items() if n.startswith("dispatch"))
     t_up, t_down = float(np.mean(up_ms)), kmean["ffn_down"]
-    t_ffn = t_up + t_down + kmean["ffn_plan"]
+    t_ffn = t_up + t_down + kmean["ffn_plan"] + kmean.get("ffn_hidden_quant", 0.0)
     t_comb = kmean["combine"]
-    gemm_peak = BF16_PEAK_TFLOPS if cfg.act == "bf16" else F32_VEC_PEAK_TFLOPS
+    gemm_peak = (FP8_PEAK_TFLOPS if fp8w else BF16_PEAK_TFLOPS) if cfg.act == "bf16" else F32_VEC_PEAK_TFLOPS
     res = {
         "T": cfg.T,
         "value": round(cfg.T / (ms_med * 1e-3), 1),
@@ -415,13 +439,23 @@ def run_workload(cfg, steps, warmup, flush, with_backward=False, keep_host=False
         "routed_assignments_per_s": round(cfg.T * cfg.k / (ms_med * 1e-3), 1),
         "dispatched_rows": routed,
     }
+    res["gemm_peak_tflops"] = gemm_peak
     extra = {"A": A, "t_up": t_up, "gemm_peak": gemm_peak}
-    if with_backward:
+    if with_backward and not fp8w:
         res["backward_stages"] = backward_leg(mm, torch, cfg, shape, buf, stream, A, x, wg,
                                               w1, w3, w2)
     del x, wg, w1, w3, w2, bias, buf
+    if fp8w:
+        del w1q, w3q, w2q, wsc, ws8
     torch.cuda.empty_cache()
     return res, extra, inp
+
+
+def detail_config(configs, name):
+    """a workload by name; <name>_fp8w is <name> with fp8 expert weights"""
+    if name.endswith("_fp8w"):
+        return dataclasses.replace(configs[name[:-5]], weights="fp8", name=name)
+    return configs[name]
 
 
 def main():
@@ -437,7 +471,9 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0)
     ap.add_argument("--capacity-factor", type=float, default=0.0)
     ap.add_argument("--reassign", action="store_true")
-    ap.add_argument("--quant", default="token", choices=["token", "expert", "global"])
+    ap.add_argument("--quant", default="token", choices=["token", "expert", "global", "token_absmax"])
+    ap.add_argument("--fp8-weights", action="store_true",
+                    help="fp8 expert weights on the fp8 matrix cores (fp8-row workloads)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the tokens on one GPU; "
@@ -459,6 +495,10 @@ def main():
         if cfg.dispatch != "fp8":
             sys.exit("--quant needs a workload with fp8 dispatch")
         cfg = dataclasses.replace(cfg, quant=args.quant)
+    if args.fp8_weights:
+        if cfg.dispatch != "fp8":
+            sys.exit("--fp8-weights needs a workload with fp8 dispatch")
+        cfg = dataclasses.replace(cfg, weights="fp8", name=cfg.name + "_fp8w")
     torch.cuda.set_device(0)
     flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
 
@@ -467,7 +507,7 @@ def main():
                                 keep_host=not args.no_cpu_baseline)
     A = ex["A"]
     up_tflops = A["ffn_up_flops"] / (ex["t_up"] * 1e-3) / 1e12
-    plain = not cfg.capacity and cfg.quant == "token"
+    plain = not cfg.capacity and cfg.quant == "token" and cfg.weights == "act"
     traffic = measured_traffic(cfg.name) if plain else {}
     detail = dict(res)
     for key in ("value", "ms_per_step", "T"):
@@ -481,8 +521,8 @@ def main():
     if args.detail_configs == "all" and args.config == HEADLINE and plain:
         detail["workloads"] = {}
         for name in DETAIL_CONFIGS:
-            r, _, _ = run_workload(CONFIGS[name], max(5, args.steps // 2), max(2, args.warmup // 2),
-                                   flush)
+            r, _, _ = run_workload(detail_config(CONFIGS, name), max(5, args.steps // 2),
+                                   max(2, args.warmup // 2), flush)
             detail["workloads"][name] = r
     out = {
         "metric": METRIC,
@@ -495,13 +535,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": cfg.act,
+        "dtype": "fp8 weights, bf16 activations" if cfg.weights == "fp8" else cfg.act,
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k,
                    "S": cfg.S, "h": cfg.h, "dispatch": cfg.dispatch,
                    **({"capacity": cfg.capacity, "overflow": "reassign" if cfg.reassign else "drop"}
                       if cfg.capacity else {}),
-                   **({"quant": cfg.quant} if cfg.quant != "token" else {})},
+                   **({"quant": cfg.quant} if cfg.quant != "token" else {}),
+                   **({"weights": "fp8"} if cfg.weights == "fp8" else {})},
         "roofline": {
             "kernel": "ffn_up",
             "bound": "mfma",

@@ -63,8 +63,11 @@ class MoEConfig:
     capacity: int = 0
     reassign: bool = False
     # fp8 rows: the rows whose min/max range a row is mapped from ("token",
-    # "expert" or "global")
+    # "expert", "global"), or "token_absmax" (each row's symmetric range)
     quant: str = "token"
+    # expert weights: "act" (the activation dtype) or "fp8" (e4m3 codes with
+    # a scale per row, on the fp8 matrix cores; fp8 rows only)
+    weights: str = "act"
     # relative-L2 bound on the layer output y
     tol_y: float = 2e-2
 
