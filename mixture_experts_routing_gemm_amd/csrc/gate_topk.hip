@@ -289,10 +289,17 @@ bool launch_gate_rows_f32(const moe_shape& s, const void* x, const void* wg, con
 bool launch_gate_rows_bf16(const moe_shape& s, const void* x, const void* wg, const float* bias,
                            int32_t* idx, float* w, float* dbg, hipStream_t st);
 
+bool launch_gate_two_phase(const moe_shape& s, const void* x, const void* wg, const float* bias,
+                           int32_t* idx, float* w, hipStream_t st, hipError_t* err);
+
 hipError_t launch_gate_topk(const moe_shape& s, const void* x, const void* wg, const float* bias,
                             int32_t* idx, float* w, float* dbg, hipStream_t st, const Marks* mk) {
     (void)mk;
     if (s.T == 0) return hipSuccess;
+    // bf16 without the logits dump: approximate logits on the matrix cores,
+    // exact chains only for the experts that can still be selected
+    hipError_t err = hipSuccess;
+    if (dbg == nullptr && launch_gate_two_phase(s, x, wg, bias, idx, w, st, &err)) return err;
     const bool f32 = s.act == MOE_F32;
     if (f32 ? launch_gate_rows_f32(s, x, wg, bias, idx, w, dbg, st)
             : launch_gate_rows_bf16(s, x, wg, bias, idx, w, dbg, st))

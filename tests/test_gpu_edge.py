@@ -143,22 +143,30 @@ def test_fp8_constant_rows_and_outliers():
     ("bf16", 3000, 512, 50, 4, True),     # 16 tokens x 4 experts per lane
     ("f32", 500, 192, 100, 8, False),     # 16 tokens x 8 experts per lane, float32
     ("bf16", 300, 256, 200, 8, True),     # more experts than a block covers
+    ("bf16", 513, 320, 256, 8, False),    # the most experts, ragged token block
+    ("bf16", 129, 4096, 128, 1, True),    # k = 1, long chains
+    ("bf16", 32845, 136, 128, 4, True),   # the size the two-phase gate takes by itself
 ], ids=["tail", "short_k", "f32", "partial_chunk", "tw64", "tw32", "tw16_me4", "f32_me8",
-        "e200"])
-def test_gate_both_paths(act, T, d, E, k, bias):
-    """moe_gate_topk with a logits buffer (logits kernel + top-k kernel) and
-    without (the fused kernel): bit-exact logits and ids, weights to 1e-5."""
+        "e200", "e256", "k1", "large"])
+@pytest.mark.parametrize("path", ["auto", "two_phase", "one_phase"])
+def test_gate_both_paths(act, T, d, E, k, bias, path, monkeypatch):
+    """moe_gate_topk with a logits buffer (every logit's chain, then the
+    top-k) and without (bf16: approximate logits on the matrix cores and
+    exact chains for the candidates only): bit-exact logits and ids in both,
+    the same weight bits in both, weights to 1e-5 of the oracle's."""
     mm = _mm()
     cfg = small_cfg(act, T=T, d=d, E=E, k=k, S=0, h=64, tol_y=1e-5)
     inp = make_inputs(cfg, seed=11, gate_only=True)
     if bias:
         inp.bias = np.random.default_rng(12).normal(0.0, 0.05, E).astype(np.float32)
-    say(f"[gate] act={act} T={T} d={d} E={E} k={k} bias={bias}")
+    monkeypatch.setenv("MOE_GATE_PATH", path)
+    say(f"[gate] act={act} T={T} d={d} E={E} k={k} bias={bias} path={path}")
     z_ref = oracle.gate_logits(inp.x, inp.wg, inp.bias, nthreads=ORACLE_THREADS)
     idx_ref, w_ref = oracle.select_topk(z_ref, k)
     shape = mm.shape_of(cfg)
     x, wg = dev(inp.x), dev(inp.wg)
     b = None if inp.bias is None else dev(inp.bias)
+    ws_bits = []
     for with_logits in (True, False):
         idx = torch.full((T, k), -3, dtype=torch.int32, device="cuda")
         w = torch.empty((T, k), dtype=torch.float32, device="cuda")
@@ -170,6 +178,8 @@ def test_gate_both_paths(act, T, d, E, k, bias):
             assert nbad == 0, f"{nbad} logits differ"
         assert np.array_equal(host(idx), idx_ref), f"ids differ (logits buffer: {with_logits})"
         assert rel_l2(host(w), w_ref) <= 1e-5
+        ws_bits.append(host(w).view(np.uint32).copy())
+    assert np.array_equal(ws_bits[0], ws_bits[1]), "the two gate paths give different weight bits"
 
 
 def test_bad_routing_ids_raise_the_device_flag():
@@ -243,11 +253,13 @@ def test_traced_forward_with_some_events_left_out():
 
 
 @pytest.mark.parametrize("E,k", [(16, 4), (128, 4), (200, 8)], ids=["E16", "E128", "E200"])
-def test_tied_logits_go_to_the_lower_id(E, k):
+@pytest.mark.parametrize("path", ["two_phase", "one_phase"])
+def test_tied_logits_go_to_the_lower_id(E, k, path, monkeypatch):
     # gate rows duplicated in pairs: every logit appears twice, and the
     # top-k must list the lower id of a tied pair first (bit-exact vs the
     # oracle, whose tie rule is pinned on the CPU)
     mm = _mm()
+    monkeypatch.setenv("MOE_GATE_PATH", path)
     cfg = small_cfg(T=300, d=128, E=E, k=k, S=0, h=64)
     inp = make_inputs(cfg, seed=11)
     inp.wg[1::2] = inp.wg[0::2][: E // 2]
