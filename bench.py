@@ -74,6 +74,7 @@ CSRC = "mixture_experts_routing_gemm_amd/csrc/"
 # kernel name in the forward -> the source file whose hash a traffic figure is tied to
 KERNEL_SOURCES = {
     "gate_topk": CSRC + "gate_common.h",
+    "gate_two_phase": CSRC + "gate_two_phase.hip",
     "dispatch_rank": CSRC + "dispatch.hip",
     "dispatch_scan": CSRC + "dispatch.hip",
     "dispatch_permute": CSRC + "dispatch.hip",
@@ -344,7 +345,7 @@ def run_workload(cfg, steps, warmup, flush, with_backward=False, keep_host=False
         wsc = torch.empty(mm.moe_fp8_weight_scale_floats(shape), dtype=torch.float32, device="cuda")
         mm.moe_quantize_weights(shape, w1, w3, w2, w1q, w3q, w2q, wsc, stream)
         ws8 = mm.alloc_workspace(shape, mm.STAGE_FORWARD_FP8W)
-        names = list(mm.FP8W_KERNELS)
+        names = [mm.moe_forward_kernel_name(shape, 0)] + list(mm.FP8W_KERNELS[1:])
 
         def forward(events=None):
             mm.moe_forward_fp8w(shape, x, wg, bias, w1q, w3q, w2q, wsc, buf.y, buf.topk_idx,
@@ -406,7 +407,9 @@ def run_workload(cfg, steps, warmup, flush, with_backward=False, keep_host=False
     routed = int(buf.offsets[-1].item())
     A = algorithmic(cfg, routed)
     ms_med = float(np.median(step_ms))
-    t_gate = kmean["gate_topk"]
+    gate_name = names[0]
+    t_gate = kmean[gate_name]
+    gate_flop_rate = A["gate_flops"] / (t_gate * 1e-3) / 1e12
     t_disp = sum(v for n, v in kmean.items() if n.startswith("dispatch"))
     t_up, t_down = float(np.mean(up_ms)), kmean["ffn_down"]
     t_ffn = t_up + t_down + kmean["ffn_plan"] + kmean.get("ffn_hidden_quant", 0.0)
@@ -421,9 +424,8 @@ def run_workload(cfg, steps, warmup, flush, with_backward=False, keep_host=False
         "kernel_ms": {n: round(v, 5) for n, v in kmean.items()},
         "ffn_up_ms_timed_steps": round(t_up, 5),
         "gate_us": round(t_gate * 1e3, 2),
-        "gate_tflops": round(A["gate_flops"] / (t_gate * 1e-3) / 1e12, 3),
-        "gate_frac_of_f32_nonpacked_peak": round(A["gate_flops"] / (t_gate * 1e-3) / 1e12
-                                                 / F32_NONPACKED_PEAK_TFLOPS, 4),
+        "gate_kernel": gate_name,
+        "gate_tflops": round(gate_flop_rate, 3),
         "gate_GBps": round(A["gate_bytes"] / (t_gate * 1e-3) / 1e9, 1),
         "dispatch_us": round(t_disp * 1e3, 2),
         "dispatch_GBps": round(A["dispatch_bytes"] / (t_disp * 1e-3) / 1e9, 1),
@@ -439,6 +441,12 @@ def run_workload(cfg, steps, warmup, flush, with_backward=False, keep_host=False
         "routed_assignments_per_s": round(cfg.T * cfg.k / (ms_med * 1e-3), 1),
         "dispatched_rows": routed,
     }
+    if gate_name == "gate_two_phase":
+        # the logits' FLOPs run on the bf16 matrix cores (plus the candidates' chains)
+        res["gate_frac_of_bf16_peak"] = round(gate_flop_rate / BF16_PEAK_TFLOPS, 4)
+    else:
+        # every logit is a canonical fma chain on the non-packed float32 vector units
+        res["gate_frac_of_f32_nonpacked_peak"] = round(gate_flop_rate / F32_NONPACKED_PEAK_TFLOPS, 4)
     res["gemm_peak_tflops"] = gemm_peak
     extra = {"A": A, "t_up": t_up, "gemm_peak": gemm_peak}
     if with_backward and not fp8w:

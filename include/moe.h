@@ -419,7 +419,8 @@ int32_t moe_forward_traced(const moe_shape *s, const void *x, const void *w_gate
                            void *const *events, int32_t n_events);
 
 /* Host only: number of kernels moe_forward launches for *s, and the name of
- * the i-th ("gate_topk", "dispatch_rank", ...); NULL if out of range. */
+ * the i-th ("gate_topk", "dispatch_rank", ...); NULL if out of range. The
+ * gate's name is "gate_two_phase" when *s takes the two-phase gate. */
 int32_t moe_forward_kernel_count(const moe_shape *s);
 const char *moe_forward_kernel_name(const moe_shape *s, int32_t i);
 

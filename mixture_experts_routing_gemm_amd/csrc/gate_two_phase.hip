@@ -446,13 +446,17 @@ hipError_t launch_tp(const moe_shape& s, const void* x, const void* wg, const fl
 // The environment variable MOE_GATE_PATH = "two_phase" or "one_phase"
 // overrides the choice (both give the same results; tests use it to run
 // each path at any size).
-bool launch_gate_two_phase(const moe_shape& s, const void* x, const void* wg, const float* bias,
-                           int32_t* idx, float* w, hipStream_t st, hipError_t* err) {
+bool gate_two_phase_chosen(const moe_shape& s) {
     if (s.act != MOE_BF16 || s.E > 256) return false;
     const char* force = std::getenv("MOE_GATE_PATH");
     if (force != nullptr && std::strcmp(force, "one_phase") == 0) return false;
     const bool forced = force != nullptr && std::strcmp(force, "two_phase") == 0;
-    if (!forced && (s.E < 96 || s.T < 256 * kTpTok)) return false;
+    return forced || (s.E >= 96 && s.T >= 256 * kTpTok);
+}
+
+bool launch_gate_two_phase(const moe_shape& s, const void* x, const void* wg, const float* bias,
+                           int32_t* idx, float* w, hipStream_t st, hipError_t* err) {
+    if (!gate_two_phase_chosen(s)) return false;
     const int nb = (s.E + 31) / 32;
     if (nb <= 1) *err = launch_tp<1>(s, x, wg, bias, idx, w, st);
     else if (nb <= 2) *err = launch_tp<2>(s, x, wg, bias, idx, w, st);

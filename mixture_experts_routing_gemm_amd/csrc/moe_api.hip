@@ -12,6 +12,7 @@
 #include "moe_device.h"
 
 namespace moe {
+bool gate_two_phase_chosen(const moe_shape& s);
 hipError_t launch_gate_topk(const moe_shape& s, const void* x, const void* wg, const float* bias,
                             int32_t* idx, float* w, float* dbg, hipStream_t st, const Marks* mk);
 hipError_t launch_dispatch(const moe_shape& s, const void* x, const int32_t* topk_idx,
@@ -561,6 +562,7 @@ int32_t moe_forward_kernel_count(const moe_shape* s) {
 
 const char* moe_forward_kernel_name(const moe_shape* s, int32_t i) {
     if (i < 0 || i >= moe_forward_kernel_count(s)) return nullptr;
+    if (i == 0 && s != nullptr && s->T > 0 && gate_two_phase_chosen(*s)) return "gate_two_phase";
     if (i == 3 && s != nullptr && s->dispatch == MOE_FP8_E4M3) return "dispatch_permute_fp8";
     return kKernelNames[i];
 }

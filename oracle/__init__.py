@@ -2,9 +2,13 @@
 
 Only the tests, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
 leg import this package. The HIP library never loads it, and it never loads
-the HIP library. The arithmetic lives in ``moe_oracle.c`` (plain C, compiled
-with gcc -O2 -ffp-contract=off, FMA from the hardware instruction, no
-fast-math); this module only marshals numpy arrays into it.
+the HIP library. The per-token arithmetic lives in ``moe_oracle.c`` (plain C,
+compiled with gcc -O2 -ffp-contract=off, FMA from the hardware instruction,
+no fast-math); its loops over tokens or rows may be split over threads, and
+each result is computed the same way whichever thread runs it. ``dense.py``
+applies each expert to all of its rows with float64 matrix products (the
+whole-batch checks) and holds the fp8-weight variant. This module marshals
+numpy arrays into the C code.
 
 Parity status of each function (what pins it, besides itself) is listed in the
 ``test_oracle_*.py`` tests; every function here has at least one pin.
