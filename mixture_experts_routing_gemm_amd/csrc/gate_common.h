@@ -30,15 +30,21 @@ __device__ __forceinline__ void chunk_to_f32<bf16_t>(u32x4 raw, float* v) {
     }
 }
 
-// Is (za, ia) ranked before (zb, ib)? Larger logit first, then lower id.
+// Is (za, ia) ranked before (zb, ib)? Larger logit first, then lower id; a
+// NaN logit ranks after every number, NaNs among themselves by id.
 __device__ __forceinline__ bool ranks_before(float za, int ia, float zb, int ib) {
+    const bool na = za != za, nb = zb != zb;
+    if (na || nb) return na == nb ? ia < ib : nb;
     return za > zb || (za == zb && ia < ib);
 }
 
+// a selected logit as the softmax sees it: NaN counts as -inf (weight 0)
+__device__ __forceinline__ float softmax_logit(float z) { return z != z ? -__builtin_inff() : z; }
+
 // Top-k and weights of TT tokens whose logits sit in LDS (zs[r*zld + e]),
-// under the order "larger logit first, then lower id" (ranks_before), which
-// is total, so the k experts that rank first, listed in that order, are
-// unique. Two ways to find them, by cost:
+// under the order "larger logit first, then lower id, NaN last"
+// (ranks_before), which is total, so the k experts that rank first, listed
+// in that order, are unique. Two ways to find them, by cost:
 //  - rank counting (small E): expert e of token r is selected iff fewer
 //    than k experts rank before it, and that count is its slot; every
 //    (token, expert) pair is one independent count, E*E*TT comparisons;
@@ -79,8 +85,8 @@ __device__ __forceinline__ void topk_rows(const float* zs, int zld, int TT, int 
         }
         unsigned taken = 0u;
         for (int p = 0; p < k; ++p) {
-            float bz = -__builtin_inff();
-            int be = E;  // ranks after every real expert
+            float bz = __builtin_nanf("");
+            int be = E;  // ranks after every real expert, NaN ones included
 #pragma unroll
             for (int q = 0; q < kPerLane; ++q) {
                 const int e = lane + 64 * q;
@@ -110,11 +116,11 @@ __device__ __forceinline__ void topk_rows(const float* zs, int zld, int TT, int 
         const int r = q / k, p = q - r * k;
         const int64_t t = t0 + r;
         if (t >= T) continue;
-        const float zmax = sz[r * kMaxK];
+        const float zmax = softmax_logit(sz[r * kMaxK]);
         float sum = 0.0f;
-        for (int p2 = 0; p2 < k; ++p2) sum += expf(sz[r * kMaxK + p2] - zmax);
+        for (int p2 = 0; p2 < k; ++p2) sum += expf(softmax_logit(sz[r * kMaxK + p2]) - zmax);
         topk_idx[t * k + p] = si[r * kMaxK + p];
-        topk_w[t * k + p] = expf(sz[r * kMaxK + p] - zmax) / sum;
+        topk_w[t * k + p] = expf(softmax_logit(sz[r * kMaxK + p]) - zmax) / sum;
     }
 }
 

@@ -74,6 +74,25 @@ __device__ __forceinline__ void run_chains(const uint8_t* X, const uint8_t* W, c
     }
 }
 
+// Rank key of (logit z, expert e): a larger key ranks first, in the order
+// "larger logit, then lower id, NaN after every number" -- the logit's
+// order-preserving bits (-0 taken as +0; every NaN as 0) above ~e.
+__device__ __forceinline__ uint64_t rank_key(float z, int e) {
+    const uint32_t b = __float_as_uint(z + 0.0f);
+    uint32_t o = (b & 0x80000000u) != 0u ? ~b : (b | 0x80000000u);
+    if (z != z) o = 0u;
+    return (static_cast<uint64_t>(o) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(e));
+}
+__device__ __forceinline__ int key_id(uint64_t key) {
+    return static_cast<int>(~static_cast<uint32_t>(key));
+}
+// the logit of a key as the softmax takes it (NaN as -inf)
+__device__ __forceinline__ float key_softmax_logit(uint64_t key) {
+    const uint32_t o = static_cast<uint32_t>(key >> 32);
+    if (o == 0u) return -__builtin_inff();
+    return __uint_as_float((o & 0x80000000u) != 0u ? (o & 0x7fffffffu) : ~o);
+}
+
 template <int EB>
 __global__ __launch_bounds__(256, EB >= 8 ? 1 : 2) void gate_two_phase_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg, const float* __restrict__ bias,
@@ -200,7 +219,10 @@ __global__ __launch_bounds__(256, EB >= 8 ? 1 : 2) void gate_two_phase_kernel(
         float top[kMaxK];
 #pragma unroll
         for (int p = 0; p < kMaxK; ++p) top[p] = -__builtin_inff();
-        bool bad = false;  // a NaN anywhere: every expert is a candidate
+        // a NaN or infinity in any approximate logit or bound (NaN or
+        // infinite inputs, a NaN bias, sums near the float32 range): every
+        // expert of the token is a candidate, and the exact chains decide
+        bool bad = false;
 #pragma unroll
         for (int eb = 0; eb < EB; ++eb)
 #pragma unroll
@@ -212,7 +234,7 @@ __global__ __launch_bounds__(256, EB >= 8 ? 1 : 2) void gate_two_phase_kernel(
                                   8.0f * 0x1p-24f * __builtin_fabsf(zt) + 0x1p-126f;
                 const float L = zt - eps;
                 acc[eb][v] = zt;  // keep zt for the upper bounds
-                bad = bad || !(L == L) || !(eps == eps);
+                bad = bad || !(__builtin_fabsf(zt) < __builtin_inff()) || !(eps < __builtin_inff());
                 // insert L into the descending top-k list
                 float cur = L;
 #pragma unroll
@@ -375,42 +397,43 @@ __global__ __launch_bounds__(256, EB >= 8 ? 1 : 2) void gate_two_phase_kernel(
         // in the list's order), then the weights
         if (take) {
             const int64_t t = t0 + tw + lane;
-            float sz[kMaxK];
-            int si[kMaxK];
+            // the k largest rank keys, kept sorted by one max / min pass
+            // per candidate (0 is below every key)
+            uint64_t sk[kMaxK];
 #pragma unroll
-            for (int p = 0; p < kMaxK; ++p) {
-                sz[p] = -__builtin_inff();
-                si[p] = 0x7fffffff;
-            }
+            for (int p = 0; p < kMaxK; ++p) sk[p] = 0u;
             int q = pre;
             for (int eb = 0; eb < EB && cnt > 0; ++eb) {
                 uint32_t m = masks[(tw + lane) * EB + eb];
                 while (m != 0u) {
                     const int b = __ffs(m) - 1;
                     m &= m - 1u;
-                    float cz = pz[q++];
-                    int ci = eb * 32 + b;
+                    uint64_t ck = rank_key(pz[q++], eb * 32 + b);
 #pragma unroll
                     for (int p = 0; p < kMaxK; ++p) {
-                        if (p < k && (si[p] == 0x7fffffff || ranks_before(cz, ci, sz[p], si[p]))) {
-                            const float tz = sz[p];
-                            const int ti = si[p];
-                            sz[p] = cz;
-                            si[p] = ci;
-                            cz = tz;
-                            ci = ti;
-                            if (ti == 0x7fffffff) break;
+                        if (p < k) {
+                            const uint64_t hi = ck > sk[p] ? ck : sk[p];
+                            ck = ck > sk[p] ? sk[p] : ck;
+                            sk[p] = hi;
                         }
                     }
                 }
             }
             if (t < T) {
+                float sz[kMaxK];
+#pragma unroll
+                for (int p = 0; p < kMaxK; ++p) sz[p] = key_softmax_logit(sk[p]);
                 const float zmax = sz[0];
                 float sum = 0.0f;
-                for (int p2 = 0; p2 < k; ++p2) sum += expf(sz[p2] - zmax);
-                for (int p = 0; p < k; ++p) {
-                    topk_idx[t * k + p] = si[p];
-                    topk_w[t * k + p] = expf(sz[p] - zmax) / sum;
+#pragma unroll
+                for (int p = 0; p < kMaxK; ++p)
+                    if (p < k) sum += expf(sz[p] - zmax);
+#pragma unroll
+                for (int p = 0; p < kMaxK; ++p) {
+                    if (p < k) {
+                        topk_idx[t * k + p] = key_id(sk[p]);
+                        topk_w[t * k + p] = expf(sz[p] - zmax) / sum;
+                    }
                 }
             }
         }

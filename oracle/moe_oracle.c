@@ -99,9 +99,13 @@ int oracle_gate_logits(int64_t T, int d, int E, int dtype, const void *x,
     return 0;
 }
 
-/* is (za, ia) ranked before (zb, ib)?  larger logit first, then lower id */
+/* is (za, ia) ranked before (zb, ib)?  larger logit first, then lower id;
+ * a NaN logit ranks after every number, NaNs among themselves by id */
 static int ranks_before(float za, int ia, float zb, int ib)
 {
+    int na = isnan(za), nb = isnan(zb);
+    if (na || nb)
+        return na == nb ? ia < ib : nb;
     return za > zb || (za == zb && ia < ib);
 }
 
@@ -121,18 +125,21 @@ static void select_one(int E, int k, const float *z, int32_t *idx, double *w)
         taken[best] = 1;
         idx[j] = best;
     }
-    /* softmax over all E experts, then renormalise over the selected ones */
-    double zmax = (double)z[0];
-    for (int e = 1; e < E; ++e)
-        if ((double)z[e] > zmax)
+    /* softmax over all E experts, then renormalise over the selected ones;
+     * a NaN logit has probability 0 (it counts as -inf) */
+    double zmax = -INFINITY;
+    for (int e = 0; e < E; ++e)
+        if (!isnan(z[e]) && (double)z[e] > zmax)
             zmax = (double)z[e];
     double Z = 0.0;
     for (int e = 0; e < E; ++e)
-        Z += exp((double)z[e] - zmax);
+        if (!isnan(z[e]))
+            Z += exp((double)z[e] - zmax);
     double psel = 0.0;
     double p[64];
     for (int j = 0; j < k; ++j) {
-        p[j] = exp((double)z[idx[j]] - zmax) / Z;
+        float zj = z[idx[j]];
+        p[j] = isnan(zj) ? 0.0 / Z : exp((double)zj - zmax) / Z;
         psel += p[j];
     }
     for (int j = 0; j < k; ++j)

@@ -236,11 +236,11 @@ def _scatter(idx, vals, E):
     return D
 
 
-def check_gate_backward(name, T, d, E, k, act, with_dx=True, seed=21):
+def check_gate_backward(name, T, d, E, k, act, with_dx=True, seed=21, skew=0.0):
     mm = _mm()
     x = make_rows(T, d, act, seed=seed)
     wg = make_rows(E, d, act, seed=seed + 1)
-    idx = make_routing(T, E, k, seed=seed + 2)
+    idx = make_routing(T, E, k, seed=seed + 2, skew=skew)
     w = make_weights(T, k, seed=seed + 3)
     rng = np.random.default_rng(seed + 4)
     dw = rng.standard_normal((T, k)).astype(np.float32)
@@ -304,7 +304,12 @@ def test_gate_backward_empty_batch_clears_dw_gate():
     assert torch.all(dwg == 0).item()
 
 
-@pytest.mark.parametrize("name", ["deepseekmoe_bf16", "coarse_top2_bf16"])
+@pytest.mark.parametrize("name", ["deepseekmoe_bf16", "coarse_top2_bf16", "zipf_stress_bf16",
+                                  "fp8_dispatch"])
 def test_gate_backward_full_size(name):
+    # zipf_stress_bf16 with routing as skewed as its gate's (expert 0 in
+    # about 85 % of the tokens' top-1; most experts nearly empty);
+    # fp8_dispatch's gate backward is bf16 (k = 6)
     cfg = CONFIGS[name]
-    check_gate_backward(name, cfg.T, cfg.d, cfg.E, cfg.k, cfg.act)
+    skew = 3.0 if name == "zipf_stress_bf16" else 0.0
+    check_gate_backward(name, cfg.T, cfg.d, cfg.E, cfg.k, cfg.act, skew=skew)

@@ -182,6 +182,44 @@ def test_gate_both_paths(act, T, d, E, k, bias, path, monkeypatch):
     assert np.array_equal(ws_bits[0], ws_bits[1]), "the two gate paths give different weight bits"
 
 
+@pytest.mark.parametrize("E,k", [(16, 4), (128, 4), (200, 8)], ids=["E16", "E128", "E200"])
+@pytest.mark.parametrize("path", ["two_phase", "one_phase"])
+def test_nan_logits_rank_last(E, k, path, monkeypatch):
+    """NaN logits (from NaN or infinite inputs, or a NaN bias) rank after
+    every number, NaNs among themselves by id, and get weight 0; the ids
+    bit-exact against the oracle on both gate paths, NaN weights where the
+    oracle's are NaN, the rest to 1e-5."""
+    mm = _mm()
+    T, d = 600, 256
+    cfg = small_cfg("bf16", T=T, d=d, E=E, k=k, S=0, h=64, tol_y=1e-5)
+    inp = make_inputs(cfg, seed=21, gate_only=True)
+    rng = np.random.default_rng(22)
+    x = inp.x.copy()
+    x[rng.choice(T, 20, replace=False), rng.integers(0, d, 20)] = 0x7FC0  # NaN
+    x[rng.choice(T, 20, replace=False), rng.integers(0, d, 20)] = 0x7F80  # +inf
+    x[rng.choice(T, 20, replace=False), rng.integers(0, d, 20)] = 0xFF80  # -inf
+    inp.x = x
+    bias = rng.normal(0.0, 0.05, E).astype(np.float32)
+    bias[[1, E // 2]] = np.nan
+    inp.bias = bias
+    monkeypatch.setenv("MOE_GATE_PATH", path)
+    say(f"[gate nan] E={E} k={k} path={path}")
+    z_ref = oracle.gate_logits(inp.x, inp.wg, inp.bias, nthreads=ORACLE_THREADS)
+    idx_ref, w_ref = oracle.select_topk(z_ref, k)
+    assert np.isnan(z_ref).any(axis=1).all()  # every token has NaN logits
+    shape = mm.shape_of(cfg)
+    idx = torch.full((T, k), -3, dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    mm.moe_gate_topk(shape, dev(inp.x), dev(inp.wg), dev(inp.bias), idx, w, None)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(idx), idx_ref)
+    got = host(w).astype(np.float64)
+    assert np.array_equal(np.isnan(got), np.isnan(w_ref))
+    fin = ~np.isnan(w_ref)
+    assert np.all(got[fin & (w_ref == 0.0)] == 0.0)
+    assert rel_l2(got[fin], w_ref[fin]) <= 1e-5
+
+
 def test_bad_routing_ids_raise_the_device_flag():
     mm = _mm()
     cfg = small_cfg(T=300, d=128, E=8, k=2, S=0, h=64)

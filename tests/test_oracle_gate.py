@@ -95,6 +95,32 @@ def test_selection_brute_force_with_ties(seed):
         assert idx[0].tolist() == np.argsort(-z, kind="stable")[:k].tolist()
 
 
+@pytest.mark.parametrize("E,k", [(6, 2), (16, 4), (200, 8)])
+def test_nan_logits_rank_after_every_number(E, k):
+    # numpy's stable sort puts NaN after every number and keeps equal keys
+    # (NaNs included) in index order: the ranking the selection must follow
+    rng = np.random.default_rng(E)
+    z = (np.round(rng.standard_normal((300, E)) * 2) / 2).astype(np.float32)
+    z[rng.random((300, E)) < 0.2] = np.nan
+    z[5, :] = np.nan                 # every logit NaN
+    z[6, : E - k + 1] = np.nan       # fewer than k numbers
+    z[7, 1] = np.inf
+    z[8, :] = -np.inf
+    z[8, 3] = np.nan
+    idx, w = oracle.select_topk(z, k)
+    for t in range(len(z)):
+        assert idx[t].tolist() == np.argsort(-z[t], kind="stable")[:k].tolist(), t
+    # a NaN logit has probability 0; the numbers share the weight
+    sel = np.take_along_axis(z, idx, axis=1)
+    nan_sel = np.isnan(sel)
+    ok = ~np.all(nan_sel | (sel == -np.inf), axis=1) & ~np.any(sel == np.inf, axis=1)
+    assert np.all(w[ok][nan_sel[ok]] == 0.0)
+    ref = torch.softmax(torch.from_numpy(np.where(nan_sel, -np.inf, sel).astype(np.float64)), -1)
+    np.testing.assert_allclose(w[ok], ref.numpy()[ok], rtol=1e-12, atol=1e-300)
+    # no number to give the weight to: NaN weights
+    assert np.all(np.isnan(w[5])) and np.all(np.isnan(w[8]))
+
+
 def test_ties_go_to_lower_expert_id():
     rng = np.random.default_rng(3)
     d = 32
