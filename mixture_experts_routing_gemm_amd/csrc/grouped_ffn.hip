@@ -453,10 +453,13 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
     return reinterpret_cast<const uint8_t*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
+// (The flags are ints: a struct with bool members was copied through
+// scratch memory at every tile, and the wait for that scratch load drained
+// the prefetched slices.)
 struct TileInfo {
     int g, nt, m0, row_base, nrows, KT;
-    bool shared;
-    bool half;  // at most kBigBM/2 valid rows: the lower row of waves idles
+    int shared;
+    int half;  // at most kBigBM/2 valid rows: the lower row of waves idles
 };
 
 // What one lane needs to fetch slices of one tile: 32-bit byte offsets of
@@ -469,7 +472,7 @@ struct TileSrc {
     const uint8_t* abuf;  // token operand of the tile (wave-uniform)
     uint32_t abytes;      // its size in bytes
     uint32_t gofs;
-    bool shared;
+    int shared;
     uint32_t aoff[2];  // token rows of this lane's DMA chunks
     uint32_t boff[2];  // weight rows of this lane's DMA chunks
     float cs, cc;      // fp8 rows: (scale, centre) of the row this lane converts
@@ -764,14 +767,20 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
     }
 
     bf16x8 fa0[MB], fb0[NB], fa1[MB], fb1[NB];
+    // the next tile's descriptor: a scalar load, issued a tile ahead (for
+    // later tiles during the previous epilogue), so that its latency -- the
+    // descriptors were written by another kernel, often on another XCD --
+    // is not exposed by the wait at the top of the tile
+    TileInfo pre = cur;
+    if (Cn < nclaim) pre = decode_tile<MODE>(a, tile_of(Cn), nsh);
     while (true) {
         const bool has_next = Cn < nclaim;
-        // the next tile's descriptor (a scalar load); the claim on the tile
-        // after it is already in `claim` and goes out to the other waves
-        // before the last four slices. After the last tile the "next" tile
-        // is this one again: its first slices are re-read into free slots and
-        // never used, which keeps the last steps the same for every tile.
-        if (has_next) nxt = decode_tile<MODE>(a, tile_of(Cn), nsh);
+        // the claim on the tile after the next one is already in `claim` and
+        // goes out to the other waves before the last four slices. After the
+        // last tile the "next" tile is this one again: its first slices are
+        // re-read into free slots and never used, which keeps the last steps
+        // the same for every tile.
+        if (has_next) nxt = pre;
 
         wait_vmcnt<2 * kBigLoads>();  // slice 0 of this tile has landed
         ring_barrier();
@@ -922,6 +931,7 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
         else
             k_loop(std::false_type{});
         const int Cn2 = __builtin_amdgcn_readfirstlane(lds_next[0]);
+        if (has_next && Cn2 < nclaim) pre = decode_tile<MODE>(a, tile_of(Cn2), nsh);
 
         // epilogue: acc[mb][nb][v] is token (m0 + wm*128 + mb*32 + lr) and
         // weight row (wn*64 + nb*32 + 8*(v/4) + 4*lg + v%4) of the tile. A
