@@ -77,6 +77,9 @@ struct BwdArgs {
     float* dw2;              // [G, d, h]
     int ntn;                 // n-tiles per group (dh, dx)
     int tpg;                 // output tiles per group and gradient (wgrad)
+    // layout of the da / db rows the weight gradients read: row stride of a
+    // routed row and of a shared row, and the step between shared groups
+    int dd_ld, dd_lds, dd_gs;
 };
 
 // byte offset of 16-byte chunk c (0..7) of row r of a [128][64] bf16 tile
@@ -404,7 +407,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void ffn_bwd_wgrad_kernel(BwdArgs a
     // A (m, k = row): q = 0: dy[row][m]; else da / db [row][m]
     const uint8_t* A = q == 0 ? (shared ? a.dy_sh : a.dy_perm) : (q == 1 ? (shared ? a.da_s : a.da_r)
                                                                          : (shared ? a.db_s : a.db_r));
-    const int lda = q == 0 ? a.d : ldh, aoff = q == 0 ? 0 : hoff, acount = q == 0 ? a.d : a.hs;
+    const int lda = q == 0 ? a.d : (shared ? a.dd_lds : a.dd_ld);
+    const int aoff = q == 0 ? 0 : s * a.dd_gs, acount = q == 0 ? a.d : a.hs;
     // B (n, k = row): q = 0: hid[row][n]; else the input row v[row][n]
     const uint8_t* B = q == 0 ? (shared ? a.h_s : a.h_r) : (shared ? a.x : a.x_perm);
     const int ldb = q == 0 ? ldh : a.d, boff = q == 0 ? hoff : 0, bcount = q == 0 ? a.hs : a.d;
@@ -457,7 +461,58 @@ __global__ __launch_bounds__(kBwdThreads, 2) void ffn_bwd_wgrad_kernel(BwdArgs a
         }
 }
 
+// dst[b][c][dcol0 + r] = src[b][r][c] for a batch of [rows, cols] bf16
+// matrices (rows and cols multiples of 64; dst rows hold ldd values). One
+// work-group per 64 x 64 block through LDS: 16-byte reads along the source
+// rows, 16-byte writes along the destination rows.
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16_t* __restrict__ src, int rows,
+                                                             int cols, int64_t sstride,
+                                                             bf16_t* __restrict__ dst, int ldd,
+                                                             int dcol0, int64_t dstride) {
+    __shared__ uint16_t t[64][66];
+    const int tid = threadIdx.x, c8 = tid & 7, rr = tid >> 3;
+    const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+    const bf16_t* sb = src + blockIdx.z * sstride;
+    bf16_t* db = dst + blockIdx.z * dstride;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int r = rr + 32 * i;
+        const u32x4 v = load16(reinterpret_cast<const uint8_t*>(sb + static_cast<int64_t>(r0 + r) * cols + c0 + 8 * c8));
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            t[r][8 * c8 + 2 * u] = static_cast<uint16_t>(v[u] & 0xffffu);
+            t[r][8 * c8 + 2 * u + 1] = static_cast<uint16_t>(v[u] >> 16);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int c = rr + 32 * i;  // a destination row
+        u32x4 v;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            v[u] = static_cast<uint32_t>(t[8 * c8 + 2 * u][c]) | (static_cast<uint32_t>(t[8 * c8 + 2 * u + 1][c]) << 16);
+        *reinterpret_cast<u32x4*>(db + static_cast<int64_t>(c0 + c) * ldd + dcol0 + r0 + 8 * c8) = v;
+    }
+}
+
 int ffn_hidden_stride(const moe_shape& s);
+bool ffn_backward_big(const moe_shape& s);
+size_t ffn_plan_bytes(const moe_shape& s);
+size_t ffn_plan_bytes_dh(const moe_shape& s);
+hipError_t launch_ffn_bwd_gemms(const moe_shape& s, const void* x_perm, const float* qparams,
+                                const int32_t* offsets, const void* x, const void* w1,
+                                const void* w3, const void* w2t, const void* w13t,
+                                const void* dy_perm, const void* dy_sh, void* dx_perm, void* dx_sh,
+                                int32_t* plan_f, int32_t* plan_dh, void* h_r, void* h_s, void* a_r,
+                                void* b_r, void* a_s, void* b_s, void* dd_r, void* dd_s,
+                                hipStream_t st, const Marks* mk);
+bool wgrad_supported(const moe_shape& s);
+size_t wgrad_ws_bytes(const moe_shape& s);
+hipError_t launch_ffn_wgrad(const moe_shape& s, const int32_t* offsets, const void* dd_r,
+                            const void* dd_s, const void* v_r, const void* v_s, const void* dy_r,
+                            const void* dy_s, const void* hid_r, const void* hid_s, float* dw1,
+                            float* dw3, float* dw2, void* ws, hipStream_t st);
 hipError_t launch_ffn_plan128(const moe_shape& s, const int32_t* offsets, int32_t* plan,
                               hipStream_t st);
 hipError_t launch_ffn_recompute(const moe_shape& s, const void* x_perm, const float* qparams,
@@ -468,29 +523,53 @@ hipError_t launch_ffn_recompute(const moe_shape& s, const void* x_perm, const fl
 // Workspace of the backward: the 128-row plan, then a, b, hid, da, db of the
 // routed rows ([R, hs] bf16 each) and of the shared experts ([T, S*hs]).
 struct BwdLayout {
-    size_t plan, a_r, b_r, h_r, da_r, db_r, a_s, b_s, h_s, da_s, db_s, bytes;
+    bool big;  // the persistent-kernel path
+    bool wg;   // the weight gradients on the persistent kernel too
+    size_t plan, plan_dh, a_r, b_r, h_r, da_r, db_r, a_s, b_s, h_s, da_s, db_s, w2t, w13t, wgq, bytes;
 };
+// Workspace: the 128-row plan (or the two persistent plans), the recomputed
+// a, b, H and the gradients da, db of every row; on the persistent path da
+// and db share rows ([da | db], 2h values per group) and the transposed
+// weights W2T [G, h, d] and W13T [G, d, 2h] follow.
 BwdLayout bwd_layout(const moe_shape& s) {
-    BwdLayout L;
+    BwdLayout L{};
+    L.big = ffn_backward_big(s);
     const size_t hs = static_cast<size_t>(ffn_hidden_stride(s));
     const size_t R = static_cast<size_t>(s.T) * s.k, TS = static_cast<size_t>(s.T) * s.S;
+    const size_t G = static_cast<size_t>(s.E + s.S), dh = static_cast<size_t>(s.d) * s.h;
     size_t off = 0;
     auto take = [&](size_t n) {
         const size_t at = off;
         off = (off + n + 255) & ~static_cast<size_t>(255);
         return at;
     };
-    L.plan = take(static_cast<size_t>(s.E + s.S + 1) * 4);
+    if (L.big) {
+        L.plan = take(ffn_plan_bytes(s));
+        L.plan_dh = take(ffn_plan_bytes_dh(s));
+    } else {
+        L.plan = take(static_cast<size_t>(s.E + s.S + 1) * 4);
+    }
     L.a_r = take(R * hs * 2);
     L.b_r = take(R * hs * 2);
     L.h_r = take(R * hs * 2);
-    L.da_r = take(R * hs * 2);
-    L.db_r = take(R * hs * 2);
     L.a_s = take(TS * hs * 2);
     L.b_s = take(TS * hs * 2);
     L.h_s = take(TS * hs * 2);
-    L.da_s = take(TS * hs * 2);
-    L.db_s = take(TS * hs * 2);
+    if (L.big) {
+        L.da_r = take(R * 2 * hs * 2);
+        L.db_r = L.da_r + hs * 2;
+        L.da_s = take(TS * 2 * hs * 2);
+        L.db_s = L.da_s + hs * 2;
+        L.w2t = take(G * dh * 2);
+        L.w13t = take(G * dh * 2 * 2);
+        L.wg = wgrad_supported(s);
+        if (L.wg) L.wgq = take(wgrad_ws_bytes(s));
+    } else {
+        L.da_r = take(R * hs * 2);
+        L.db_r = take(R * hs * 2);
+        L.da_s = take(TS * hs * 2);
+        L.db_s = take(TS * hs * 2);
+    }
     L.bytes = off;
     return L;
 }
@@ -507,7 +586,6 @@ hipError_t launch_ffn_backward(const moe_shape& s, const void* x_perm, const flo
     uint8_t* w = static_cast<uint8_t*>(ws);
     BwdArgs a{};
     a.offsets = offsets;
-    a.plan = reinterpret_cast<const int32_t*>(w + L.plan);
     a.T = s.T;
     a.E = s.E;
     a.S = s.S;
@@ -538,26 +616,63 @@ hipError_t launch_ffn_backward(const moe_shape& s, const void* x_perm, const flo
     a.dw1 = dw1;
     a.dw3 = dw3;
     a.dw2 = dw2;
-
+    hipError_t e;
     mark(mk);
-    hipError_t e = launch_ffn_plan128(s, offsets, reinterpret_cast<int32_t*>(w + L.plan), st);
-    if (e != hipSuccess) return e;
-    e = launch_ffn_recompute(s, x_perm, qparams, offsets, x, w1, w3,
-                             reinterpret_cast<const int32_t*>(w + L.plan), w + L.h_r, w + L.h_s,
-                             w + L.a_r, w + L.b_r, w + L.a_s, w + L.b_s, st);
-    if (e != hipSuccess) return e;
-    mark(mk);
-    const int64_t mtT = (s.T + kTB - 1) / kTB;
-    const int64_t routed = static_cast<int64_t>(s.T) * s.k / kTB + s.E;  // routed m-tiles, at most
-    auto grid = [](int64_t n) { return static_cast<unsigned>((n + 7) & ~int64_t(7)); };
-    a.ntn = (a.hs + kTB - 1) / kTB;
-    ffn_bwd_dh_kernel<<<grid((routed + s.S * mtT) * a.ntn), kBwdThreads, kBwdLds, st>>>(a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    mark(mk);
-    a.ntn = (s.d + kTB - 1) / kTB;
-    ffn_bwd_dx_kernel<<<grid((routed + (s.S > 0 ? mtT : 0)) * a.ntn), kBwdThreads, kBwdLds, st>>>(a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    mark(mk);
+    if (L.big) {
+        // W2T [G, h, d] and W13T [G, d, 2h] = [W1 | W3] transposed per group
+        const int G = s.E + s.S;
+        const int64_t dh = static_cast<int64_t>(s.d) * s.h;
+        bf16_t* w2t = reinterpret_cast<bf16_t*>(w + L.w2t);
+        bf16_t* w13t = reinterpret_cast<bf16_t*>(w + L.w13t);
+        transpose_bf16_kernel<<<dim3(s.h / 64, s.d / 64, G), 256, 0, st>>>(
+            static_cast<const bf16_t*>(w2), s.d, s.h, dh, w2t, s.d, 0, dh);
+        transpose_bf16_kernel<<<dim3(s.d / 64, s.h / 64, G), 256, 0, st>>>(
+            static_cast<const bf16_t*>(w1), s.h, s.d, dh, w13t, 2 * s.h, 0, 2 * dh);
+        transpose_bf16_kernel<<<dim3(s.d / 64, s.h / 64, G), 256, 0, st>>>(
+            static_cast<const bf16_t*>(w3), s.h, s.d, dh, w13t, 2 * s.h, s.h, 2 * dh);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        e = launch_ffn_bwd_gemms(s, x_perm, qparams, offsets, x, w1, w3, w2t, w13t, dy_perm, dy_sh,
+                                 dx_perm, dx_sh, reinterpret_cast<int32_t*>(w + L.plan),
+                                 reinterpret_cast<int32_t*>(w + L.plan_dh), w + L.h_r, w + L.h_s,
+                                 w + L.a_r, w + L.b_r, w + L.a_s, w + L.b_s, w + L.da_r, w + L.da_s,
+                                 st, mk);
+        if (e != hipSuccess) return e;
+        // the weight gradients read [da | db] rows and the routed m-tile
+        // prefix of 128-row tiles is not needed by them
+        a.dd_ld = 2 * s.h;
+        a.dd_lds = 2 * s.S * s.h;
+        a.dd_gs = 2 * s.h;
+    } else {
+        a.plan = reinterpret_cast<const int32_t*>(w + L.plan);
+        a.dd_ld = a.hs;
+        a.dd_lds = s.S * a.hs;
+        a.dd_gs = a.hs;
+        e = launch_ffn_plan128(s, offsets, reinterpret_cast<int32_t*>(w + L.plan), st);
+        if (e != hipSuccess) return e;
+        e = launch_ffn_recompute(s, x_perm, qparams, offsets, x, w1, w3,
+                                 reinterpret_cast<const int32_t*>(w + L.plan), w + L.h_r, w + L.h_s,
+                                 w + L.a_r, w + L.b_r, w + L.a_s, w + L.b_s, st);
+        if (e != hipSuccess) return e;
+        mark(mk);
+        const int64_t mtT = (s.T + kTB - 1) / kTB;
+        const int64_t routed = static_cast<int64_t>(s.T) * s.k / kTB + s.E;  // routed m-tiles, at most
+        auto grid = [](int64_t n) { return static_cast<unsigned>((n + 7) & ~int64_t(7)); };
+        a.ntn = (a.hs + kTB - 1) / kTB;
+        ffn_bwd_dh_kernel<<<grid((routed + s.S * mtT) * a.ntn), kBwdThreads, kBwdLds, st>>>(a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        mark(mk);
+        a.ntn = (s.d + kTB - 1) / kTB;
+        ffn_bwd_dx_kernel<<<grid((routed + (s.S > 0 ? mtT : 0)) * a.ntn), kBwdThreads, kBwdLds, st>>>(a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        mark(mk);
+    }
+    if (L.big && L.wg) {
+        e = launch_ffn_wgrad(s, offsets, w + L.da_r, w + L.da_s, x_perm, x, dy_perm, dy_sh, w + L.h_r,
+                             w + L.h_s, dw1, dw3, dw2, w + L.wgq, st);
+        if (e != hipSuccess) return e;
+        mark(mk);
+        return hipSuccess;
+    }
     a.tpg = ((s.d + kTB - 1) / kTB) * ((s.h + kTB - 1) / kTB);
     const int64_t nblk = 3 * static_cast<int64_t>(s.E + s.S) * a.tpg;
     ffn_bwd_wgrad_kernel<<<static_cast<unsigned>(nblk), kBwdThreads, kBwdLds, st>>>(a);

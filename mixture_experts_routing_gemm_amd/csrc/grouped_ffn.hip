@@ -23,6 +23,7 @@
 #include <type_traits>
 
 #include "ffn_plan.h"
+#include "lds_ring.h"
 #include "moe_device.h"
 
 namespace moe {
@@ -30,8 +31,17 @@ namespace moe {
 // kModeUp / kModeDown: bf16 operands; kModeUpFp8: fp8 token rows converted to
 // bf16 in LDS; kModeUpF8W / kModeDownF8W: fp8 token (or hidden) rows and fp8
 // weights on the fp8 matrix cores, the scales applied in the epilogue.
-enum { kModeUp = 0, kModeUpFp8 = 1, kModeDown = 2, kModeUpF8W = 3, kModeDownF8W = 4 };
+// For the backward (persistent kernel only): kModeUpSave / kModeUpFp8Save are
+// kModeUp / kModeUpFp8 that also store the pre-activations a and b;
+// kModeDh computes dhid = dy W2 (K = d, from the transposed W2, one weight
+// row per output column) with the SwiGLU backward in its epilogue.
+enum {
+    kModeUp = 0, kModeUpFp8 = 1, kModeDown = 2, kModeUpF8W = 3, kModeDownF8W = 4,
+    kModeUpSave = 5, kModeUpFp8Save = 6, kModeDh = 7
+};
 constexpr bool is_down(int m) { return m == kModeDown || m == kModeDownF8W; }
+constexpr bool is_fp8rows(int m) { return m == kModeUpFp8 || m == kModeUpFp8Save; }
+constexpr bool is_save(int m) { return m == kModeUpSave || m == kModeUpFp8Save; }
 constexpr bool is_f8w(int m) { return m == kModeUpF8W || m == kModeDownF8W; }
 
 constexpr int kBM = 128, kBN = 128, kBK = 64;  // bf16 tile: rows x B rows x K
@@ -391,8 +401,6 @@ constexpr int kBigBBytes = 2 * kBigBN * kBigBK;
 constexpr int kBigSlot = kBigABytes + kBigBBytes;
 // vector-memory instructions per wave per slice (fp8 slices are padded to it)
 constexpr int kBigLoads = 4;  // per wave per slice: 2 token-row and 2 weight-row requests
-// fourth word of a raw buffer resource on gfx950 (untyped, no swizzle)
-constexpr int kBufferFlags = 0x00020000;
 
 // A ring slot holds the token rows (A) and weight rows (B) of one K slice in
 // blocks of 64 rows: block q of A at byte 8192*q, block q of B at 8192*q +
@@ -424,33 +432,6 @@ __device__ __forceinline__ void convert_codes(uint8_t* slot, int wave, int lane,
     const int r = wave * 32 + (lane >> 1), ch = 2 * (lane & 1);
     *reinterpret_cast<bf16x8*>(slot + lds_off32(r, ch)) = __builtin_bit_cast(bf16x8, lo);
     *reinterpret_cast<bf16x8*>(slot + lds_off32(r, ch + 1)) = __builtin_bit_cast(bf16x8, hi);
-}
-
-// Work-group barrier without the release/acquire fences of __syncthreads():
-// those would drain every outstanding load, including the prefetched slices.
-// The counted vmcnt wait before it orders the slice about to be read; the
-// empty asm keeps the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void ring_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// s_waitcnt vmcnt(n) lgkmcnt(0) (gfx9 encoding): at most n vector-memory
-// instructions of this wave outstanding, and its LDS reads complete -- the
-// latter so that no ring slot can be refilled while a read of it is in flight
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);
-}
-
-// a wave-uniform pointer (lets the compiler keep it in SGPRs)
-__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
-    const uint64_t v = reinterpret_cast<uint64_t>(p);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
-    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
-    return reinterpret_cast<const uint8_t*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
 // (The flags are ints: a struct with bool members was copied through
@@ -511,7 +492,7 @@ __device__ __forceinline__ void tile_sources(const GemmArgs& a, const TileInfo& 
     // address from a private copy
     src.abuf = uniform_ptr(ti.shared ? op_as : op_ar);
     src.abytes = __builtin_amdgcn_readfirstlane(ti.shared ? by_as : by_ar);
-    const bool fp8 = MODE == kModeUpFp8 && !ti.shared;
+    const bool fp8 = is_fp8rows(MODE) && !ti.shared;
     const int K = is_down(MODE) ? (ti.shared ? a.S * a.h : a.h) : a.d;
     const uint32_t eb = is_f8w(MODE) ? 1 : 2;  // bytes per operand value
     const int last = ti.nrows - 1;
@@ -551,6 +532,11 @@ __device__ __forceinline__ void tile_sources(const GemmArgs& a, const TileInfo& 
         if (is_down(MODE)) {
             const int n = ti.nt * kBigBN + br;
             src.boff[i] = static_cast<uint32_t>(n) * a.h * eb + c * 16;
+        } else if (MODE == kModeDh) {
+            // the transposed W2 [G, h, d]: weight row n is hidden feature n
+            // (rows past h, in a last partial n-tile, are read and unused)
+            const int n = ti.nt * kBigBN + br;
+            src.boff[i] = static_cast<uint32_t>(n) * a.d * eb + c * 16;
         } else {
             // weight row br of the tile: 32-row blocks alternate W1 / W3
             const int n = ti.nt * (kBigBN / 2) + ((br >> 5) >> 1) * 32 + (br & 31);
@@ -559,26 +545,12 @@ __device__ __forceinline__ void tile_sources(const GemmArgs& a, const TileInfo& 
     }
 }
 
-// One 16-byte-per-lane request through a raw buffer resource over
-// [base, base + bytes): lane i reads base + voff_i + soff (zero when past the
-// end) and writes it to LDS at lds + OFF + 16*i. (The instruction's immediate
-// offset would move the source address as well, so the LDS offset goes into
-// the LDS base instead.)
-template <int OFF>
-__device__ __forceinline__ void buffer_to_lds16(const uint8_t* base, uint32_t bytes, uint32_t voff,
-                                                uint32_t soff, uint8_t* lds) {
-    const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, static_cast<int>(bytes), kBufferFlags);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds + OFF), 16, voff,
-                                             soff, 0, 0);
-}
-
 template <int MODE>
 __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     int* lds_next = reinterpret_cast<int*>(lds + kBigSlots * kBigSlot);
     constexpr int MB = kBigMB, NB = kBigNB;
-    constexpr bool kFp8 = MODE == kModeUpFp8;
+    constexpr bool kFp8 = is_fp8rows(MODE);
     constexpr bool kF8W = is_f8w(MODE);
     constexpr bool kDown = is_down(MODE);
     constexpr int KS = kF8W ? 2 * kBigBK : kBigBK;  // operand values per slice
@@ -992,7 +964,7 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
                     tc = q2.y;
                 }
             }
-            if (kDown) {
+            if constexpr (kDown) {
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
                     uint32_t w[4][2];
@@ -1007,6 +979,47 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
                     }
                     const int col = cur.nt * kBigBN + wn * kBigWN + nb * 32;
                     store_groups(out + row * a.d + col, w, ok);
+                }
+            } else if constexpr (MODE == kModeDh) {
+                // dhid -> da = dhid b s (1 + a (1 - s)), db = dhid silu(a)
+                // (s = sigmoid(a)) from the recomputed a, b; da and db of a
+                // group's row side by side: [da | db], 2h values per group
+                const int sg = cur.shared ? cur.g - a.E : 0;
+                const int lpre = cur.shared ? a.S * a.h : a.h;
+                const int lout = 2 * lpre;
+                const int64_t prow = static_cast<int64_t>(cur.row_base) + min(r, cur.nrows - 1);
+                const bf16_t* pa = reinterpret_cast<const bf16_t*>(cur.shared ? a.pre_a_shared : a.pre_a_routed) +
+                                   prow * lpre + sg * a.h;
+                const bf16_t* pb = reinterpret_cast<const bf16_t*>(cur.shared ? a.pre_b_shared : a.pre_b_routed) +
+                                   prow * lpre + sg * a.h;
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const int col = cur.nt * kBigBN + wn * kBigWN + nb * 32;
+                    if (col >= a.h) continue;  // a last partial n-tile (h % 256 == 128)
+                    uint32_t wa_[4][2], wb_[4][2];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int f = col + 8 * q + 4 * lg;
+                        const uint2 av4 = *reinterpret_cast<const uint2*>(pa + f);
+                        const uint2 bv4 = *reinterpret_cast<const uint2*>(pb + f);
+                        const float av[4] = {bf16_lo(av4.x), bf16_hi(av4.x), bf16_lo(av4.y), bf16_hi(av4.y)};
+                        const float bv[4] = {bf16_lo(bv4.x), bf16_hi(bv4.x), bf16_lo(bv4.y), bf16_hi(bv4.y)};
+                        float da[4], db[4];
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const float dh = acc[mb][nb][4 * q + u];
+                            const float sgm = __builtin_amdgcn_rcpf(1.0f + __expf(-av[u]));
+                            da[u] = dh * bv[u] * (sgm * (1.0f + av[u] * (1.0f - sgm)));
+                            db[u] = dh * (av[u] * sgm);
+                        }
+                        wa_[q][0] = pack_bf16x2(da[0], da[1]);
+                        wa_[q][1] = pack_bf16x2(da[2], da[3]);
+                        wb_[q][0] = pack_bf16x2(db[0], db[1]);
+                        wb_[q][1] = pack_bf16x2(db[2], db[3]);
+                    }
+                    bf16_t* orow = out + row * lout + sg * 2 * a.h + col;
+                    store_groups(orow, wa_, ok);
+                    store_groups(orow + a.h, wb_, ok);
                 }
             } else {
                 const int ldo = cur.shared ? a.S * a.h : a.h;
@@ -1032,6 +1045,20 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
                         w[q][1] = pack_bf16x2(hv[2], hv[3]);
                     }
                     store_groups(out + row * ldo + cbase + pq * 32, w, ok);
+                    if constexpr (is_save(MODE)) {
+                        // the pre-activations a, b (bf16), laid out as H
+                        uint32_t wa_[4][2], wb_[4][2];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            wa_[q][0] = pack_bf16x2(acc[mb][2 * pq][4 * q], acc[mb][2 * pq][4 * q + 1]);
+                            wa_[q][1] = pack_bf16x2(acc[mb][2 * pq][4 * q + 2], acc[mb][2 * pq][4 * q + 3]);
+                            wb_[q][0] = pack_bf16x2(acc[mb][2 * pq + 1][4 * q], acc[mb][2 * pq + 1][4 * q + 1]);
+                            wb_[q][1] = pack_bf16x2(acc[mb][2 * pq + 1][4 * q + 2], acc[mb][2 * pq + 1][4 * q + 3]);
+                        }
+                        const int64_t at = row * ldo + cbase + pq * 32;
+                        store_groups(reinterpret_cast<bf16_t*>(cur.shared ? a.pre_a_shared : a.pre_a_routed) + at, wa_, ok);
+                        store_groups(reinterpret_cast<bf16_t*>(cur.shared ? a.pre_b_shared : a.pre_b_routed) + at, wb_, ok);
+                    }
                 }
             }
         }
@@ -1158,12 +1185,14 @@ struct PlanLayout {
     int ntn_up, ntn_down;  // n-tiles per group
 };
 
-PlanLayout plan_layout(const moe_shape& s) {
+// (ntn_up, ntn_down: n-tiles per group of the two tile lists; the forward's
+// are 2h/256 and d/256)
+PlanLayout plan_layout(const moe_shape& s, int ntn_up, int ntn_down) {
     PlanLayout p;
     const int64_t mtT = (s.T + kBigBM - 1) / kBigBM;
     const int64_t rmax = s.T * s.k / kBigBM + s.E;  // routed m-tiles, at most
-    p.ntn_up = 2 * s.h / kBigBN;
-    p.ntn_down = s.d / kBigBN;
+    p.ntn_up = ntn_up;
+    p.ntn_down = ntn_down;
     p.n_up = static_cast<int>((s.S * mtT + rmax) * p.ntn_up);
     p.n_down = static_cast<int>((mtT + rmax) * p.ntn_down);
     p.counters = ((static_cast<size_t>(s.E + s.S + 1) * 4 + 63) / 64) * 64;
@@ -1171,6 +1200,7 @@ PlanLayout plan_layout(const moe_shape& s) {
     p.bytes = p.tiles + static_cast<size_t>(p.n_up + p.n_down) * sizeof(int4);
     return p;
 }
+PlanLayout plan_layout(const moe_shape& s) { return plan_layout(s, 2 * s.h / kBigBN, s.d / kBigBN); }
 
 size_t ffn_plan_bytes(const moe_shape& s) { return plan_layout(s).bytes; }
 
@@ -1214,14 +1244,21 @@ int device_cus() {
     return cus[dev];
 }
 
+// one work-group per CU (at most one per tile), a multiple of 8 (XCDs)
+template <int MODE>
+hipError_t launch_persistent(const GemmArgs& a, int64_t mtiles, hipStream_t st) {
+    const hipError_t e = allow_big_lds<MODE>();
+    if (e != hipSuccess) return e;
+    int64_t blocks = std::min<int64_t>(device_cus(), mtiles * a.ntn);
+    blocks = (blocks + 7) & ~int64_t(7);
+    ffn_gemm_persistent_kernel<MODE><<<static_cast<unsigned>(blocks), 512, kBigLds, st>>>(a);
+    return hipGetLastError();
+}
+
 template <int MODE>
 hipError_t launch_gemm(const GemmArgs& a, int64_t mtiles, bool big, hipStream_t st) {
     if (big) {
-        const hipError_t e = allow_big_lds<MODE>();
-        if (e != hipSuccess) return e;
-        int64_t blocks = std::min<int64_t>(device_cus(), mtiles * a.ntn);
-        blocks = (blocks + 7) & ~int64_t(7);
-        ffn_gemm_persistent_kernel<MODE><<<static_cast<unsigned>(blocks), 512, kBigLds, st>>>(a);
+        return launch_persistent<MODE>(a, mtiles, st);
     } else {
         int64_t blocks = mtiles * a.ntn;
         blocks = (blocks + 7) & ~int64_t(7);
@@ -1477,6 +1514,122 @@ hipError_t launch_grouped_ffn_f8w(const moe_shape& s, const void* x_perm, const 
     a.counters = counters + 8;
     a.ntn = s.d / kBigBN;
     err = launch_gemm<kModeDownF8W>(a, max_mtiles(s, kBigBM, true), true, st);
+    mark(mk);
+    return err;
+}
+
+// ------------------------------------------------- backward on big tiles --
+// The expert FFN backward's GEMMs on the persistent kernel, for the shapes it
+// takes (use_big_tiles) with [da | db] rows (2h values) within 32-bit offsets:
+//   recompute  a = W1 v, b = W3 v and H of every row (kModeUpSave);
+//   dh         dhid = dy W2 with the SwiGLU backward (kModeDh), from W2T
+//              [G, h, d] = W2 transposed per group, writing [da | db] rows;
+//   dx         dv = [da | db] W13T^T (kModeDown with K = 2h), W13T [G, d, 2h]
+//              = [W1 | W3] transposed per group (the shared experts' K
+//              blocks concatenated, so their dx is summed in the accumulator).
+// Two tile plans: the forward's (up list: recompute, down list: dx) and one
+// with h/256 n-tiles per group for dh.
+bool ffn_backward_big(const moe_shape& s) {
+    const uint64_t rows = static_cast<uint64_t>(s.T) * (s.k + s.S);
+    const uint64_t wbytes = static_cast<uint64_t>(s.E + s.S) * s.d * s.h * 2;
+    return use_big_tiles(s) && rows * 2 * s.h * 2 < (uint64_t(1) << 32) &&
+           2 * wbytes < (uint64_t(1) << 32);
+}
+
+size_t ffn_plan_bytes_dh(const moe_shape& s) {
+    return plan_layout(s, (s.h + kBigBN - 1) / kBigBN, s.d / kBigBN).bytes;
+}
+
+hipError_t launch_ffn_bwd_gemms(const moe_shape& s, const void* x_perm, const float* qparams,
+                                const int32_t* offsets, const void* x, const void* w1,
+                                const void* w3, const void* w2t, const void* w13t,
+                                const void* dy_perm, const void* dy_sh, void* dx_perm, void* dx_sh,
+                                int32_t* plan_f, int32_t* plan_dh, void* h_r, void* h_s, void* a_r,
+                                void* b_r, void* a_s, void* b_s, void* dd_r, void* dd_s,
+                                hipStream_t st, const Marks* mk) {
+    const PlanLayout pf = plan_layout(s);
+    const PlanLayout pd = plan_layout(s, (s.h + kBigBN - 1) / kBigBN, s.d / kBigBN);
+    int32_t* cf = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(plan_f) + pf.counters);
+    int4* tf = reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(plan_f) + pf.tiles);
+    int32_t* cd = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(plan_dh) + pd.counters);
+    int4* td = reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(plan_dh) + pd.tiles);
+    ffn_plan_kernel<<<plan_blocks(pf), 256, 0, st>>>(offsets, s.E, s.S, s.T, kBigBM, plan_f, tf, pf.n_up,
+                                                     pf.ntn_up, pf.ntn_down, cf);
+    ffn_plan_kernel<<<plan_blocks(pd), 256, 0, st>>>(offsets, s.E, s.S, s.T, kBigBM, plan_dh, td, pd.n_up,
+                                                     pd.ntn_up, pd.ntn_down, cd);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const uint64_t R = static_cast<uint64_t>(s.T) * s.k, T = static_cast<uint64_t>(s.T);
+    const uint64_t G = static_cast<uint64_t>(s.E + s.S);
+    const uint64_t esd = s.dispatch == MOE_FP8_E4M3 ? 1 : 2;
+    GemmArgs a{};
+    a.qparams = qparams;
+    a.offsets = offsets;
+    a.T = s.T;
+    a.E = s.E;
+    a.S = s.S;
+    a.d = s.d;
+    a.h = s.h;
+    a.hs = s.h;
+    // recompute: a, b and H
+    a.plan = plan_f;
+    a.tiles = tf;
+    a.counters = cf;
+    a.tile_meta = cf + kTileMetaHalf;
+    a.a_routed = static_cast<const uint8_t*>(x_perm);
+    a.a_shared = static_cast<const uint8_t*>(x);
+    a.a_routed_bytes = static_cast<uint32_t>(R * s.d * esd);
+    a.a_shared_bytes = static_cast<uint32_t>(s.S > 0 ? T * s.d * 2 : 0);
+    a.w_bytes = static_cast<uint32_t>(G * s.d * s.h * 2);
+    a.wa = static_cast<const uint8_t*>(w1);
+    a.wb = static_cast<const uint8_t*>(w3);
+    a.out_routed = static_cast<uint8_t*>(h_r);
+    a.out_shared = static_cast<uint8_t*>(h_s);
+    a.pre_a_routed = static_cast<uint8_t*>(a_r);
+    a.pre_b_routed = static_cast<uint8_t*>(b_r);
+    a.pre_a_shared = static_cast<uint8_t*>(a_s);
+    a.pre_b_shared = static_cast<uint8_t*>(b_s);
+    a.ntn = pf.ntn_up;
+    err = s.dispatch == MOE_FP8_E4M3 ? launch_persistent<kModeUpFp8Save>(a, max_mtiles(s, kBigBM, false), st)
+                                     : launch_persistent<kModeUpSave>(a, max_mtiles(s, kBigBM, false), st);
+    mark(mk);
+    if (err != hipSuccess) return err;
+    // dh: [da | db] rows
+    a.plan = plan_dh;
+    a.tiles = td;
+    a.counters = cd;
+    a.tile_meta = cd + kTileMetaHalf;
+    a.a_routed = static_cast<const uint8_t*>(dy_perm);
+    a.a_shared = static_cast<const uint8_t*>(dy_sh);
+    a.a_routed_bytes = static_cast<uint32_t>(R * s.d * 2);
+    a.a_shared_bytes = static_cast<uint32_t>(s.S > 0 ? T * s.d * 2 : 0);
+    a.wa = static_cast<const uint8_t*>(w2t);
+    a.wb = static_cast<const uint8_t*>(w2t);
+    a.out_routed = static_cast<uint8_t*>(dd_r);
+    a.out_shared = static_cast<uint8_t*>(dd_s);
+    a.ntn = pd.ntn_up;
+    err = launch_persistent<kModeDh>(a, max_mtiles(s, kBigBM, false), st);
+    mark(mk);
+    if (err != hipSuccess) return err;
+    // dx = [da | db] W13T^T: the down-projection with 2h hidden values
+    a.plan = plan_f;
+    a.tiles = tf + pf.n_up;
+    a.counters = cf + 8;
+    a.tile_meta = cf + kTileMetaHalf;
+    a.h = 2 * s.h;
+    a.hs = 2 * s.h;
+    a.a_routed = static_cast<const uint8_t*>(dd_r);
+    a.a_shared = static_cast<const uint8_t*>(dd_s);
+    a.a_routed_bytes = static_cast<uint32_t>(R * 2 * s.h * 2);
+    a.a_shared_bytes = static_cast<uint32_t>(T * s.S * 2 * s.h * 2);
+    a.w_bytes = static_cast<uint32_t>(G * s.d * 2 * s.h * 2);
+    a.wa = static_cast<const uint8_t*>(w13t);
+    a.wb = nullptr;
+    a.pre_a_routed = a.pre_b_routed = a.pre_a_shared = a.pre_b_shared = nullptr;
+    a.out_routed = static_cast<uint8_t*>(dx_perm);
+    a.out_shared = static_cast<uint8_t*>(dx_sh);
+    a.ntn = pf.ntn_down;
+    err = launch_persistent<kModeDown>(a, max_mtiles(s, kBigBM, true), st);
     mark(mk);
     return err;
 }

@@ -109,7 +109,8 @@ def _cfg(base, **kw):
     ("deepseekmoe_bf16", dict(T=257, d=128, E=1, k=1, S=0, h=64)),
     ("fp8_dispatch", dict(T=400, d=256, E=8, k=3, S=2, h=96)),
     ("zipf_stress_bf16", dict(T=2048, d=256, E=128, k=4, h=128)),
-], ids=["small", "off_grid", "one_expert", "fp8_rows", "skewed_E128"])
+    ("fp8_dispatch", dict(T=700, d=512, E=8, k=3, S=2, h=384)),
+], ids=["small", "off_grid", "one_expert", "fp8_rows", "skewed_E128", "fp8_rows_big_tiles"])
 def test_ffn_backward_small(base, kw):
     run_case(_cfg(base, **kw))
 
