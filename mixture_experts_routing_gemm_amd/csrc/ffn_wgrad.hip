@@ -38,7 +38,7 @@ constexpr int kWgLds = kWgSlots * kWgSlot;
 struct WgradArgs {
     const int32_t* offsets;  // [E+1] routed row offsets
     const int32_t* order;    // [E+S] groups by rows, descending (written by the plan)
-    int32_t* counter;        // the tile queue
+    int32_t* counters;       // [8] tile queues, one per XCD
     int64_t T;
     int E, S, d, h;
     // [da | db] rows: routed [R, 2h], shared [T, S*2h]
@@ -62,11 +62,11 @@ struct WgradArgs {
     int t13;
 };
 
-// Plan: the groups ordered by rows, descending (ties by index), and the queue
-// cleared. One work-group.
+// Plan: the groups ordered by rows, descending (ties by index), and the
+// queues cleared. One work-group.
 __global__ __launch_bounds__(256) void wgrad_plan_kernel(const int32_t* __restrict__ offsets, int E,
                                                          int S, int64_t T, int32_t* __restrict__ order,
-                                                         int32_t* __restrict__ counter) {
+                                                         int32_t* __restrict__ counters) {
     __shared__ int rows[kMaxE + kMaxS];
     const int G = E + S;
     for (int g = threadIdx.x; g < G; g += blockDim.x)
@@ -77,7 +77,17 @@ __global__ __launch_bounds__(256) void wgrad_plan_kernel(const int32_t* __restri
         for (int q = 0; q < G; ++q) rank += (rows[q] > rows[g] || (rows[q] == rows[g] && q < g)) ? 1 : 0;
         order[rank] = g;
     }
-    if (threadIdx.x == 0) *counter = 0;
+    if (threadIdx.x < 8) counters[threadIdx.x] = 0;
+}
+
+// The tile list (groups longest first, then their tiles) is dealt to the 8
+// XCDs in chunks of kWgChunk consecutive tiles, chunk j to XCD j % 8: every
+// XCD gets about an eighth of every group's work (balance), and the tiles of
+// a chunk, which share one row panel, run under one L2. Position c of XCD
+// x's list is tile (c / kWgChunk * 8 + x) * kWgChunk + c % kWgChunk.
+constexpr int kWgChunk = 4;
+__device__ __forceinline__ int wg_tile_of(int x, int c) {
+    return ((c / kWgChunk) * 8 + x) * kWgChunk + c % kWgChunk;
 }
 
 // swizzle of the 16-byte chunks of slice row k: chunk c is stored at c ^ sw(k),
@@ -89,18 +99,54 @@ __device__ __forceinline__ int wg_off(int k, int m) {
 }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
-// the fragment of 32 features (f0 + lane % 32) x 16 rows (k0 + 8 (lane / 32) + e)
-// of an operand slice in LDS
-__device__ __forceinline__ bf16x8 wg_frag(const uint8_t* op, int f0, int k0, int lane) {
+// This lane's byte offset, within an operand slice, of the 8 bytes it points
+// the transposing read at for the fragment of features f0 .. f0+31 and rows
+// 0 .. 15: row k = 8 (lane / 32) + (lane % 16) / 4, features f = f0 + 16
+// ((lane / 16) % 2) + 4 (lane % 4) .. +3. Rows 4 and 16 further are a
+// constant offset (k % 4 and so the swizzle stay the same).
+__device__ __forceinline__ uint32_t wg_frag_off(int f0, int lane) {
     const int g = lane >> 4, s = lane & 15;
-    const int k = k0 + 8 * (g >> 1) + (s >> 2);
+    const int k = 8 * (g >> 1) + (s >> 2);
     const int f = f0 + 16 * (g & 1) + 4 * (s & 3);
-    typedef __attribute__((address_space(3))) v4i16 lds_v4;
-    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(op + wg_off(k, f)));
-    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(op + wg_off(k + 4, f)));
-    const v4i16 v = {lo[0], lo[1], lo[2], lo[3]};
-    const v4i16 w = {hi[0], hi[1], hi[2], hi[3]};
+    return static_cast<uint32_t>(wg_off(k, f));
+}
+// the LDS byte address of a pointer into the work-group's LDS
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint8_t*)p));
+}
+
+__device__ __forceinline__ bf16x8 wg_join(uint64_t lo, uint64_t hi) {
+    const v4i16 v = __builtin_bit_cast(v4i16, lo), w = __builtin_bit_cast(v4i16, hi);
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v, w, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Three fragments of half-slice KS (rows 16 KS .. 16 KS + 15) of a slice:
+// out[j] from the operand at a[j] (the slot address of A or B plus this
+// lane's offset), OFF[j] = 0 for A, 16384 for B. Each fragment is two
+// transposing reads, rows +0 and +4 (2048 bytes apart; the next half-slice
+// 8192 further). Written as an asm block that waits for its own reads before
+// it ends: the builtin form of the read makes the compiler wait for every
+// outstanding buffer-to-LDS request first, which would drain the prefetched
+// slices at every step.
+template <int KS, int O0, int O1, int O2>
+__device__ __forceinline__ void wg_read3(uint32_t a0, uint32_t a1, uint32_t a2, bf16x8& f0, bf16x8& f1,
+                                         bf16x8& f2) {
+    constexpr int k = KS * 8192;
+    uint64_t r[6];
+    asm volatile("ds_read_b64_tr_b16 %0, %6 offset:%c9\n"
+                 "ds_read_b64_tr_b16 %1, %6 offset:%c10\n"
+                 "ds_read_b64_tr_b16 %2, %7 offset:%c11\n"
+                 "ds_read_b64_tr_b16 %3, %7 offset:%c12\n"
+                 "ds_read_b64_tr_b16 %4, %8 offset:%c13\n"
+                 "ds_read_b64_tr_b16 %5, %8 offset:%c14\n"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5])
+                 : "v"(a0), "v"(a1), "v"(a2), "i"(O0 + k), "i"(O0 + k + 2048), "i"(O1 + k),
+                   "i"(O1 + k + 2048), "i"(O2 + k), "i"(O2 + k + 2048)
+                 : "memory");
+    f0 = wg_join(r[0], r[1]);
+    f1 = wg_join(r[2], r[3]);
+    f2 = wg_join(r[4], r[5]);
 }
 
 struct WgTile {
@@ -140,16 +186,23 @@ void ffn_wgrad_kernel(WgradArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int wn = wave & 3, wm = wave >> 2;
     const int lr = lane & 31, lg = lane >> 5;
-    const int G = a.E + a.S;
-    const int total = G * a.ntiles;
-
-    int L = blockIdx.x;  // the first tile is static, later ones come from the queue
-    for (int it = 0; L < total; ++it) {
-        const WgTile t = wg_decode(a, L);
+    // this lane's offsets of the six fragments of a half-slice: the two B
+    // blocks (features wn*64 + 32 i), then the four A blocks (wm*128 + 32 i)
+    uint32_t fo[6];
+#pragma unroll
+    for (int i = 0; i < 6; ++i)
+        fo[i] = wg_frag_off(i < 2 ? wn * 64 + i * 32 : wm * 128 + (i - 2) * 32, lane);
+    // XCD x (work-groups b with b % 8 == x) takes the tiles of its list: the
+    // first one static, later ones from its queue
+    const int xcd = blockIdx.x & 7, per_xcd = static_cast<int>(gridDim.x >> 3);
+    const int total = (a.E + a.S) * a.ntiles;
+    int c = static_cast<int>(blockIdx.x >> 3);
+    for (int it = 0; wg_tile_of(xcd, c) < total; ++it) {
+        const WgTile t = wg_decode(a, wg_tile_of(xcd, c));
         // the claim on the next tile, published through LDS at the end (two
         // words by tile parity: a word is rewritten only after every wave
         // has passed the barrier that follows its read)
-        if (tid == 0) lds_next[it & 1] = static_cast<int>(gridDim.x) + atomicAdd(a.counter, 1);
+        if (tid == 0) lds_next[it & 1] = per_xcd + atomicAdd(a.counters + xcd, 1);
 
         // operands of this tile: A rows hold its M features, B rows its N
         const uint8_t* abuf;
@@ -215,32 +268,53 @@ void ffn_wgrad_kernel(WgradArgs a) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-        if (KT > 0) issue(0);
-        if (KT > 1) issue(1);
-        if (KT > 2) issue(2);
-        for (int k = 0; k < KT; ++k) {
-            // slice k has landed once at most the later slices' requests
+        // One step per slice k. First half: slice k+3 is requested (into the
+        // slot of slice k-1), the MFMAs of slice k's first 16 rows (fa0, fb0,
+        // read before) are issued, and the fragments of its last 16 rows are
+        // read while those MFMAs run; then, once slice k+1 has landed and
+        // every wave has passed the barrier, the MFMAs of the last 16 rows are
+        // issued and slice k+1's first fragments read meanwhile.
+        bf16x8 fa0[4], fb0[2], fa1[4], fb1[2];
+        auto read_half = [&](const uint8_t* A, auto KS, bf16x8 (&fa)[4], bf16x8 (&fb)[2]) {
+            constexpr int ks = decltype(KS)::value;
+            const uint32_t base = lds_addr(A);
+            wg_read3<ks, kWgOp, kWgOp, 0>(base + fo[0], base + fo[1], base + fo[2], fb[0], fb[1], fa[0]);
+            wg_read3<ks, 0, 0, 0>(base + fo[3], base + fo[4], base + fo[5], fa[1], fa[2], fa[3]);
+        };
+        auto mma = [&](const bf16x8* fa, const bf16x8* fb) {
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mb], fb[nb], acc[mb][nb], 0, 0, 0);
+        };
+        if (KT > 0) {
+            issue(0);
+            if (KT > 1) issue(1);
+            if (KT > 2) issue(2);
+            // slice 0 has landed once at most the later slices' requests
             // (four per slice) are outstanding
-            if (k + 2 < KT) wait_vmcnt<8>();
-            else if (k + 1 < KT) wait_vmcnt<4>();
+            if (KT > 2) wait_vmcnt<8>();
+            else if (KT > 1) wait_vmcnt<4>();
             else wait_vmcnt<0>();
             ring_barrier();
-            if (k + 3 < KT) issue(k + 3);  // into the slot of slice k - 1, read by now
+            read_half(lds, ic<0>(), fa0, fb0);
+        }
+        for (int k = 0; k < KT; ++k) {
             const uint8_t* A = lds + (k & 3) * kWgSlot;
-            const uint8_t* B = A + kWgOp;
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                bf16x8 fa[4], fb[2];
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb) fb[nb] = wg_frag(B, wn * 64 + nb * 32, ks * 16, lane);
-#pragma unroll
-                for (int mb = 0; mb < 4; ++mb) fa[mb] = wg_frag(A, wm * 128 + mb * 32, ks * 16, lane);
-#pragma unroll
-                for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-                    for (int nb = 0; nb < 2; ++nb)
-                        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mb], fb[nb], acc[mb][nb], 0, 0, 0);
+            if (k + 3 < KT) issue(k + 3);
+            mma(fa0, fb0);
+            read_half(A, ic<1>(), fa1, fb1);
+            const bool next = k + 1 < KT;
+            if (next) {
+                // slices issued after k+1: k+2 and k+3, as far as they exist
+                if (k + 3 < KT) wait_vmcnt<8>();
+                else if (k + 2 < KT) wait_vmcnt<4>();
+                else wait_vmcnt<0>();
+                ring_barrier();
             }
+            mma(fa1, fb1);
+            if (next) read_half(lds + ((k + 1) & 3) * kWgSlot, ic<0>(), fa0, fb0);
         }
 
         // epilogue: acc[mb][nb][v] is output row m = wm*128 + mb*32 + 8 (v/4)
@@ -274,7 +348,7 @@ void ffn_wgrad_kernel(WgradArgs a) {
         // is visible, and every wave is done with the ring
         wait_vmcnt<0>();
         __syncthreads();
-        L = lds_next[it & 1];
+        c = lds_next[it & 1];
     }
 }
 
@@ -287,7 +361,7 @@ bool wgrad_supported(const moe_shape& s) {
            R * s.d * 2 < lim && T * s.d * 2 < lim && R * 2 * s.h * 2 < lim && T * s.S * 2 * s.h * 2 < lim;
 }
 
-size_t wgrad_ws_bytes(const moe_shape& s) { return static_cast<size_t>(s.E + s.S + 16) * 4; }
+size_t wgrad_ws_bytes(const moe_shape& s) { return static_cast<size_t>(s.E + s.S + 32) * 4; }
 
 int device_cus();
 
@@ -303,12 +377,14 @@ hipError_t launch_ffn_wgrad(const moe_shape& s, const int32_t* offsets, const vo
     if (attr != hipSuccess) return attr;
     const int G = s.E + s.S;
     int32_t* order = static_cast<int32_t*>(ws);
-    int32_t* counter = order + G;
-    wgrad_plan_kernel<<<1, 256, 0, st>>>(offsets, s.E, s.S, s.T, order, counter);
+    int32_t* counters = order + G + 16;
+    const int t13 = (2 * s.h / kWgT) * (s.d / kWgT);
+    const int ntiles = t13 + (s.d / kWgT) * ((s.h + kWgT - 1) / kWgT);
+    wgrad_plan_kernel<<<1, 256, 0, st>>>(offsets, s.E, s.S, s.T, order, counters);
     WgradArgs a{};
     a.offsets = offsets;
     a.order = order;
-    a.counter = counter;
+    a.counters = counters;
     a.T = s.T;
     a.E = s.E;
     a.S = s.S;
@@ -334,10 +410,10 @@ hipError_t launch_ffn_wgrad(const moe_shape& s, const int32_t* offsets, const vo
     a.dw1 = dw1;
     a.dw3 = dw3;
     a.dw2 = dw2;
-    a.t13 = (2 * s.h / kWgT) * (s.d / kWgT);
-    a.ntiles = a.t13 + (s.d / kWgT) * ((s.h + kWgT - 1) / kWgT);
-    const int64_t total = static_cast<int64_t>(G) * a.ntiles;
-    const unsigned blocks = static_cast<unsigned>(std::min<int64_t>(device_cus(), total));
+    a.t13 = t13;
+    a.ntiles = ntiles;
+    // a multiple of 8 work-groups (one per CU): the same count on every XCD
+    const unsigned blocks = static_cast<unsigned>(std::max(8, device_cus() & ~7));
     ffn_wgrad_kernel<<<blocks, 512, kWgLds + 16, st>>>(a);
     return hipGetLastError();
 }
