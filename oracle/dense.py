@@ -338,12 +338,12 @@ def _bf16_round(v64):
     return u.astype(np.uint32).view(np.float32).astype(np.float64)
 
 
-def _quant_hidden(hid):
+def _quant_hidden(hid, nthreads=None):
     """bf16 hidden rows [n, K] (float64 values) quantised per row with a
     symmetric absmax e4m3 scale, back as float64 code * scale."""
     from . import fp8_dequantize, fp8_quantize
     h32 = hid.astype(np.float32)
-    q, qp = fp8_quantize(h32, ranges=symmetric_ranges(h32))
+    q, qp = fp8_quantize(h32, ranges=symmetric_ranges(h32), nthreads=nthreads or 1)
     return fp8_dequantize(q, qp)
 
 
@@ -381,7 +381,7 @@ def layer_dense_fp8w(inp, wq, nthreads=None, gate=None, xq=None):
                 t1 = min(T, t0 + 4096)
                 v = xq[t0:t1]
                 hid = np.concatenate([up(v, E + s) for s in range(S)], axis=1)
-                hq = _quant_hidden(hid)
+                hq = _quant_hidden(hid, nthreads)
                 for s in range(S):
                     y[t0:t1] += hq[:, s * h:(s + 1) * h] @ W2s[s].T
         for e in range(E):
@@ -391,6 +391,6 @@ def layer_dense_fp8w(inp, wq, nthreads=None, gate=None, xq=None):
             W2 = _deq_rows(q2[e], s2[e])
             for c0 in range(0, len(tt), 4096):
                 t_c, j_c = tt[c0:c0 + 4096], jj[c0:c0 + 4096]
-                hq = _quant_hidden(up(xq[t_c], e))
+                hq = _quant_hidden(up(xq[t_c], e), nthreads)
                 y[t_c] += w[t_c, j_c][:, None] * (hq @ W2.T)
     return idx, w, y

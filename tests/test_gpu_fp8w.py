@@ -77,6 +77,7 @@ def run_forward(cfg, seed=3, check_quant=True):
     inp = make_inputs(cfg, seed=seed)
     shape = mm.shape_of(cfg)
     wq_gpu = quantize_on_gpu(mm, cfg, inp)
+    say("[fp8w] oracle weight codes")
     wq_ref = oracle.quantize_expert_weights(inp, nthreads=ORACLE_THREADS)
     if check_quant:
         check_weights(cfg, inp, wq_gpu, wq_ref)
@@ -96,6 +97,7 @@ def run_forward(cfg, seed=3, check_quant=True):
                         out["src"], ws)
     torch.cuda.synchronize()
     assert mm.moe_get_device_error(ws) == mm.MOE_OK
+    say("[fp8w] oracle routing")
     z = oracle.gate_logits(inp.x, inp.wg, inp.bias, nthreads=ORACLE_THREADS)
     idx, w = oracle.select_topk(z, k)
     counts, offsets, dest, src = oracle.dispatch(idx, E)
