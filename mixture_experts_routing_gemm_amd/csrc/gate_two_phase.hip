@@ -26,28 +26,69 @@
 // among the candidates by (z, id) and the softmax over the selected logits,
 // exactly as the one-phase kernel computes them.
 //
-// One work-group of four waves takes 128 tokens: phase 1 stages 64-wide K
-// slices of x and of the gate weight through LDS (as 16-byte chunks, the
-// next slice's loads in flight during the current MFMAs); each wave holds
-// 32 tokens x all experts (EB blocks of 32) in accumulators, one 32x32x16
-// MFMA per block and 16 K values. A lane then holds half of one token's
+// One work-group per CU takes 256 tokens (eight waves; 128 tokens and four
+// waves with more than 128 experts, whose accumulators need the registers of
+// two waves). Both phases that read x stream 32-wide K slices of x and of the
+// gate weight through a ring of six LDS slots filled by direct buffer-to-LDS
+// loads, five slices in flight: the reads of x bound the gate, and with about
+// 4 us of loaded HBM latency it takes some 80 KB of x in flight per CU to
+// approach the bandwidth (one slice in flight per work-group of 128 tokens,
+// as staged through registers before, read x at about 2 TB/s). In phase 1 each
+// wave holds 32 tokens x all experts (EB blocks of 32) in accumulators, one
+// 32x32x16 MFMA per block and 16 K values, and sums the squares of the
+// fragments it reads for the norms. A lane then holds half of one token's
 // approximate logits, its partner lane (lane ^ 32) the other half; they
 // find tau and the candidate mask together. Phase 3 streams x and the
-// weights through LDS once more and runs the chains of the wave's candidate
-// (token, expert) pairs, up to eight per lane; each token's lane then picks
-// its top-k.
+// weights once more and runs the chains of the wave's candidate (token,
+// expert) pairs, up to eight per lane; each token's lane then picks its
+// top-k.
 #include <cstdlib>
 #include <cstring>
 
 #include "gate_common.h"
+#include "lds_ring.h"
 
 namespace moe {
 
-constexpr int kTpTok = 128;         // tokens per work-group
-constexpr int kTpK = 64;            // K values per step
+constexpr int kTpK = 32;            // K values per ring slot (64 bytes of a row)
 constexpr int kTpPairCap = 512;     // candidate pairs per wave per pass (LDS)
 
-__device__ __forceinline__ int tp_off(int r, int c) { return (r << 7) + ((c ^ ((r ^ (r >> 3)) & 7)) << 4); }
+// byte offset of 16-byte chunk c (0..3) of row r in a slot's area of 64-byte
+// rows; the XOR swizzle keeps 16-byte reads of aligned runs of 8 rows (32
+// banks) or 16 rows (64 banks) conflict-free
+__device__ __forceinline__ int tp_off(int r, int c) {
+    return (r << 6) + ((c ^ (((r >> 1) & 3) ^ ((r >> 3) & 1))) << 4);
+}
+
+// Work-group and ring geometry for EB blocks of 32 experts. A slot holds
+// the work-group's x rows and the weight rows of one K slice; the weight
+// rows are padded to 16 per wave so that every wave issues the same number
+// of 1 KB requests per slot.
+template <int EB>
+struct TpRing {
+    static constexpr int kTok = EB <= 4 ? 256 : 128;  // tokens per work-group
+    static constexpr int kWaves = kTok / 32;
+    static constexpr int kThreads = kWaves * kWave;
+    static constexpr int kWRows = EB * 32 > 16 * kWaves ? EB * 32 : 16 * kWaves;
+    static constexpr int kXBytes = kTok * 64;
+    static constexpr int kSlot = kXBytes + kWRows * 64;
+    static constexpr int kSlots = 6;
+    static constexpr int kReq = 2 + kWRows / (16 * kWaves);  // per wave per slot: 2 of x, the rest weights
+    static constexpr int kLds = kSlots * kSlot + (kTok + 2 * EB * 32) * 4 + kTok * EB * 4 + 4 * kWaves;
+};
+
+// waits until at most `ahead` slots' requests (R per slot) are in flight
+template <int R, int A>
+__device__ __forceinline__ void tp_wait_slots(int ahead) {
+    if constexpr (A == 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (ahead >= A)
+            wait_vmcnt<A * R>();
+        else
+            tp_wait_slots<R, A - 1>(ahead);
+    }
+}
 
 // NC chains of one lane over a 64-value K slice in LDS, in the canonical
 // order (i ascending within each chain); pc[j] = (token row << 16) | expert.
@@ -62,7 +103,7 @@ __device__ __forceinline__ void run_chains(const uint8_t* X, const uint8_t* W, c
         for (int j = 0; j < NC; ++j) {
             const int xrow = pc[j] >> 16, e = pc[j] & 0xffff;
             xv[j] = *reinterpret_cast<const u32x4*>(X + tp_off(xrow, g));
-            wv[j] = *reinterpret_cast<const u32x4*>(W + (e >> 7) * (128 * 128) + tp_off(e & 127, g));
+            wv[j] = *reinterpret_cast<const u32x4*>(W + tp_off(e, g));
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -94,40 +135,88 @@ __device__ __forceinline__ float key_softmax_logit(uint64_t key) {
 }
 
 template <int EB>
-__global__ __launch_bounds__(256, EB >= 8 ? 1 : 2) void gate_two_phase_kernel(
+__global__ __launch_bounds__(TpRing<EB>::kThreads, 1) void gate_two_phase_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg, const float* __restrict__ bias,
     int64_t T, int d, int E, int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
-    constexpr int XB = kTpTok * kTpK * 2;        // bytes of an x slice
-    constexpr int WB = EB * 32 * kTpK * 2;       // bytes of a weight slice
-    constexpr int STAGE = XB + WB;
+    using RG = TpRing<EB>;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    float* nx = reinterpret_cast<float*>(lds + 2 * STAGE);      // [128] |x|^2
-    float* nw = nx + kTpTok;                                    // [EB*32] |w|^2
-    uint32_t* masks = reinterpret_cast<uint32_t*>(nw + EB * 32);  // [128][EB] candidates
+    float* nx = reinterpret_cast<float*>(lds + RG::kSlots * RG::kSlot);  // [kTok] |x|
+    float* nw = nx + RG::kTok;                                            // [EB*32] |w|
+    uint32_t* masks = reinterpret_cast<uint32_t*>(nw + EB * 32);           // [kTok][EB] candidates
+    float* nb = reinterpret_cast<float*>(masks + RG::kTok * EB);           // [EB*32] the bias
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int lr = lane & 31, lg = lane >> 5;
-    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTpTok;
-    const int c = tid & 7, rr = tid >> 3;  // staging: chunk c of rows rr + 32 i
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * RG::kTok;
+    // the bias, read once (phases 2 and 3 take every expert's from LDS; the
+    // barrier after phase 1 publishes it)
+    if (bias != nullptr)
+        for (int e = tid; e < EB * 32; e += RG::kThreads) nb[e] = e < E ? bias[e] : 0.0f;
+
+    // The ring. Request i (< kReq) of a slot, issued by every wave, is block
+    // j = wave + kWaves i of 16 rows: x rows 16 j.. for i < 2, weight rows
+    // 16 (j - 2 kWaves).. after. Lane l brings the logical chunk (l % 4) ^ swizzle
+    // of row l / 4 of its block, which the direct load writes at byte 16 l:
+    // where tp_off puts it. Rows past the token count or the experts, and
+    // chunks past d, read as zeros (offsets beyond the buffer's size).
+    const int64_t nrows = T - t0 < RG::kTok ? T - t0 : RG::kTok;
+    const uint8_t* xbuf = uniform_ptr(reinterpret_cast<const uint8_t*>(x + t0 * d));
+    const uint32_t xbytes = static_cast<uint32_t>(nrows * d * 2);
+    const uint8_t* wbuf = uniform_ptr(reinterpret_cast<const uint8_t*>(wg));
+    const uint32_t wbytes = static_cast<uint32_t>(static_cast<int64_t>(E) * d * 2);
+    uint32_t voff[RG::kReq];
+    int kch[RG::kReq];  // K offset of the lane's chunk within a slice
+#pragma unroll
+    for (int i = 0; i < RG::kReq; ++i) {
+        const int j = wave + RG::kWaves * i;
+        const int row = (i < 2 ? j : j - 2 * RG::kWaves) * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ (((row >> 1) & 3) ^ ((row >> 3) & 1));
+        voff[i] = static_cast<uint32_t>(row) * static_cast<uint32_t>(d) * 2u + static_cast<uint32_t>(c) * 16u;
+        kch[i] = c * 8;
+    }
+    const int KT = (d + kTpK - 1) / kTpK;
+    // slice kt of a walk that starts at slice rot (and wraps) goes to slot kt % kSlots
+    auto issue = [&](int kt, int rot) {
+        uint8_t* S = lds + (kt % RG::kSlots) * RG::kSlot;
+        const int kr = kt + rot < KT ? kt + rot : kt + rot - KT;
+        const int k0 = kr * kTpK;
+        const uint32_t soff = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(k0 * 2));
+#pragma unroll
+        for (int i = 0; i < RG::kReq; ++i) {
+            const int j = wave + RG::kWaves * i;
+            const uint32_t v = k0 + kch[i] < d ? voff[i] : 0x80000000u;
+            if (i < 2)
+                buffer_to_lds16<0>(xbuf, xbytes, v, soff, S + j * 1024);
+            else
+                buffer_to_lds16<0>(wbuf, wbytes, v, soff, S + RG::kXBytes + (j - 2 * RG::kWaves) * 1024);
+        }
+    };
+    // Runs body(slot) on the KT slices, starting at slice rot and wrapping
+    // around, each once it has landed and every wave may read it. The slice
+    // kSlots - 1 ahead is requested right after the barrier into the slot
+    // read one step earlier, which every wave has finished by then. Ends
+    // with nothing in flight; the caller synchronises before the ring's
+    // bytes are used otherwise.
+    auto stream = [&](int rot, auto body) {
+        for (int s = 0; s < RG::kSlots - 1 && s < KT; ++s) issue(s, rot);
+        for (int kt = 0; kt < KT; ++kt) {
+            const int ahead = min(RG::kSlots - 2, KT - 1 - kt);
+            tp_wait_slots<RG::kReq, RG::kSlots - 2>(ahead);
+            ring_barrier();
+            if (kt + RG::kSlots - 1 < KT) issue(kt + RG::kSlots - 1, rot);
+            body(lds + (kt % RG::kSlots) * RG::kSlot);
+        }
+    };
 
     // ---- phase 1: approximate logits on the matrix cores, and the norms
-    const bf16_t* xr[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t t = t0 + rr + 32 * i;
-        xr[i] = t < T ? x + t * d : nullptr;
-    }
-    const bf16_t* wr[EB];
-#pragma unroll
-    for (int i = 0; i < EB; ++i) {
-        const int e = rr + 32 * i;
-        wr[i] = e < E ? wg + static_cast<int64_t>(e) * d : nullptr;
-    }
-    float sx[4] = {0.0f, 0.0f, 0.0f, 0.0f}, sw[EB];
-#pragma unroll
-    for (int i = 0; i < EB; ++i) sw[i] = 0.0f;
-    u32x4 rx[4], rw[EB];
+    // from the fragments read for them: a lane sums the squares of its
+    // token's chunks; wave w those of weight blocks w, w + kWaves. Neither
+    // depends on the order of the slices (the bound covers any order of
+    // the sums), so each work-group starts at its own slice: when every
+    // work-group reads the same columns of rows d*2 bytes apart at once,
+    // the reads share their low address bits and go at about 3 TB/s; the
+    // staggered walk measured 3.7.
     auto sumsq = [](u32x4 v) {
         float s = 0.0f;
 #pragma unroll
@@ -138,75 +227,58 @@ __global__ __launch_bounds__(256, EB >= 8 ? 1 : 2) void gate_two_phase_kernel(
         }
         return s;
     };
-    // the staging loads of one K step (with the norms' sums in phase 1)
-    auto load = [&](int k0, bool sums) {
-        const int kk = k0 + c * 8;
-        const bool kin = kk < d;
+    constexpr int kNwq = (EB + RG::kWaves - 1) / RG::kWaves;
+    float sx = 0.0f, sw[kNwq];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            rx[i] = (xr[i] != nullptr && kin) ? load16(xr[i] + kk) : u32x4{0u, 0u, 0u, 0u};
-            if (sums) sx[i] += sumsq(rx[i]);
-        }
-#pragma unroll
-        for (int i = 0; i < EB; ++i) {
-            rw[i] = (wr[i] != nullptr && kin) ? load16(wr[i] + kk) : u32x4{0u, 0u, 0u, 0u};
-            if (sums) sw[i] += sumsq(rw[i]);
-        }
-    };
-    auto put = [&](int buf) {
-        uint8_t* X = lds + buf * STAGE;
-        uint8_t* W = X + XB;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(X + tp_off(rr + 32 * i, c)) = rx[i];
-#pragma unroll
-        for (int i = 0; i < EB; ++i) {
-            const int e = rr + 32 * i;  // weight block e / 128 at its own 16 KB
-            *reinterpret_cast<u32x4*>(W + (e >> 7) * (128 * 128) + tp_off(e & 127, c)) = rw[i];
-        }
-    };
+    for (int q = 0; q < kNwq; ++q) sw[q] = 0.0f;
     f32x16 acc[EB];
 #pragma unroll
     for (int i = 0; i < EB; ++i)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][v] = 0.0f;
-    const int KT = (d + kTpK - 1) / kTpK;
-    load(0, true);
-    put(0);
-    __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-        if (kt + 1 < KT) load((kt + 1) * kTpK, true);
-        const uint8_t* X = lds + (kt & 1) * STAGE;
-        const uint8_t* W = X + XB;
+    stream(static_cast<int>(blockIdx.x % static_cast<unsigned>(KT)), [&](const uint8_t* S) {
+        const uint8_t* X = S;
+        const uint8_t* W = S + RG::kXBytes;
+        // every fragment of the slice first, then the MFMAs, then the
+        // squares (a branch among the reads would expose each one's latency)
+        bf16x8 xf[kTpK / 16], wf[kTpK / 16][EB];
 #pragma unroll
         for (int ks = 0; ks < kTpK / 16; ++ks) {
             const int ch = ks * 2 + lg;
-            const bf16x8 xf = *reinterpret_cast<const bf16x8*>(X + tp_off(wave * 32 + lr, ch));
+            xf[ks] = *reinterpret_cast<const bf16x8*>(X + tp_off(wave * 32 + lr, ch));
 #pragma unroll
-            for (int eb = 0; eb < EB; ++eb) {
-                const int e = eb * 32 + lr;
-                const bf16x8 wf = *reinterpret_cast<const bf16x8*>(W + (e >> 7) * (128 * 128) + tp_off(e & 127, ch));
-                acc[eb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, xf, acc[eb], 0, 0, 0);
+            for (int eb = 0; eb < EB; ++eb)
+                wf[ks][eb] = *reinterpret_cast<const bf16x8*>(W + tp_off(eb * 32 + lr, ch));
+        }
+#pragma unroll
+        for (int ks = 0; ks < kTpK / 16; ++ks)
+#pragma unroll
+            for (int eb = 0; eb < EB; ++eb)
+                acc[eb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ks][eb], xf[ks], acc[eb], 0, 0, 0);
+#pragma unroll
+        for (int ks = 0; ks < kTpK / 16; ++ks) sx += sumsq(__builtin_bit_cast(u32x4, xf[ks]));
+#pragma unroll
+        for (int q = 0; q < kNwq; ++q) {
+            const int eb = wave + RG::kWaves * q;
+            if (eb < EB) {
+#pragma unroll
+                for (int ks = 0; ks < kTpK / 16; ++ks)
+                    sw[q] += sumsq(*reinterpret_cast<const u32x4*>(W + tp_off(eb * 32 + lr, ks * 2 + lg)));
             }
         }
-        if (kt + 1 < KT) put((kt + 1) & 1);
-        __syncthreads();
-    }
-    // norms: the 8 lanes of a row group (c = 0..7) hold one row's partial sums
+    });
+    // norms: lanes lr and lr + 32 hold the two halves of a row's sum
+    {
+        const float v = sx + __shfl_xor(sx, 32, kWave);
+        if (lg == 0) nx[wave * 32 + lr] = __builtin_sqrtf(v);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float v = sx[i];
-        v += __shfl_xor(v, 1, kWave);
-        v += __shfl_xor(v, 2, kWave);
-        v += __shfl_xor(v, 4, kWave);
-        if (c == 0) nx[rr + 32 * i] = v;
-    }
-#pragma unroll
-    for (int i = 0; i < EB; ++i) {
-        float v = sw[i];
-        v += __shfl_xor(v, 1, kWave);
-        v += __shfl_xor(v, 2, kWave);
-        v += __shfl_xor(v, 4, kWave);
-        if (c == 0) nw[rr + 32 * i] = v;
+        for (int q = 0; q < kNwq; ++q) {
+            const int eb = wave + RG::kWaves * q;
+            if (eb < EB) {
+                const float u = sw[q] + __shfl_xor(sw[q], 32, kWave);
+                if (lg == 0) nw[eb * 32 + lr] = __builtin_sqrtf(u);
+            }
+        }
     }
     __syncthreads();
 
@@ -214,8 +286,8 @@ __global__ __launch_bounds__(256, EB >= 8 ? 1 : 2) void gate_two_phase_kernel(
     // eb*32 + 8*(v/4) + 4*lg + v%4.
     {
         const int tl = wave * 32 + lr;
-        const float sxn = __builtin_sqrtf(nx[tl]);
         const float du = static_cast<float>(d) * 0x1p-24f;
+        const float c1 = 8.0f * du * nx[tl];  // eps = c1 |w| + 8 * 2^-24 |zt| + 2^-126
         float top[kMaxK];
 #pragma unroll
         for (int p = 0; p < kMaxK; ++p) top[p] = -__builtin_inff();
@@ -229,9 +301,8 @@ __global__ __launch_bounds__(256, EB >= 8 ? 1 : 2) void gate_two_phase_kernel(
             for (int v = 0; v < 16; ++v) {
                 const int e = eb * 32 + 8 * (v >> 2) + 4 * lg + (v & 3);
                 if (e >= E) continue;
-                const float zt = acc[eb][v] + (bias != nullptr ? bias[e] : 0.0f);
-                const float eps = 8.0f * du * sxn * __builtin_sqrtf(nw[e]) +
-                                  8.0f * 0x1p-24f * __builtin_fabsf(zt) + 0x1p-126f;
+                const float zt = acc[eb][v] + (bias != nullptr ? nb[e] : 0.0f);
+                const float eps = c1 * nw[e] + 8.0f * 0x1p-24f * __builtin_fabsf(zt) + 0x1p-126f;
                 const float L = zt - eps;
                 acc[eb][v] = zt;  // keep zt for the upper bounds
                 bad = bad || !(__builtin_fabsf(zt) < __builtin_inff()) || !(eps < __builtin_inff());
@@ -278,8 +349,7 @@ __global__ __launch_bounds__(256, EB >= 8 ? 1 : 2) void gate_two_phase_kernel(
                 const int e = eb * 32 + b;
                 if (e >= E) continue;
                 const float zt = acc[eb][v];
-                const float eps = 8.0f * du * sxn * __builtin_sqrtf(nw[e]) +
-                                  8.0f * 0x1p-24f * __builtin_fabsf(zt) + 0x1p-126f;
+                const float eps = c1 * nw[e] + 8.0f * 0x1p-24f * __builtin_fabsf(zt) + 0x1p-126f;
                 if (bad || zt + eps >= tau) word |= 1u << b;
             }
             word |= __shfl_xor(word, 32, kWave);
@@ -292,14 +362,14 @@ __global__ __launch_bounds__(256, EB >= 8 ? 1 : 2) void gate_two_phase_kernel(
     // Each wave lists its tokens' candidate (token, expert) pairs, as many
     // tokens as fit (kTpPairCap pairs; one token always does) per pass; all
     // waves run as many passes as the wave that needs most. A pass streams
-    // x and the gate weight through LDS again, 64 K values at a time, and
-    // lane l advances the chains of pairs l + 64 j, j < nc (nc = the list's
-    // length over 64, rounded up to 1, 2, 4 or 8; lanes past the end repeat
-    // pair 0 and discard it) in the canonical order. The pair list and the
-    // logits live in the wave's part of the staging area while it is idle.
+    // x and the gate weight through the ring again, and lane l advances the
+    // chains of pairs l + 64 j, j < nc (nc = the list's length over 64,
+    // rounded up; lanes past the end repeat pair 0 and discard it) in the
+    // canonical order. The pair list and the logits live in the wave's part
+    // of the ring while it is idle.
     int* pair = reinterpret_cast<int*>(lds) + wave * 2 * kTpPairCap;
     float* pz = reinterpret_cast<float*>(pair + kTpPairCap);
-    int* npass = reinterpret_cast<int*>(masks + kTpTok * EB);  // [4] passes per wave
+    int* npass = reinterpret_cast<int*>(nb + EB * 32);  // [kWaves] passes per wave
     const int tw = wave * 32;  // the wave's first token within the block
     int cnt = 0;  // candidates of lane lr's token (lanes < 32; none past T)
     if (lane < 32 && t0 + tw + lane < T) {
@@ -332,7 +402,9 @@ __global__ __launch_bounds__(256, EB >= 8 ? 1 : 2) void gate_two_phase_kernel(
         if (lane == 0) npass[wave] = np;
     }
     __syncthreads();
-    const int passes = max(max(npass[0], npass[1]), max(npass[2], npass[3]));
+    int passes = 0;
+#pragma unroll
+    for (int w = 0; w < RG::kWaves; ++w) passes = max(passes, npass[w]);
     int next = 0;
     for (int pass = 0; pass < passes; ++pass) {
         int pre = 0, total = 0;
@@ -356,7 +428,7 @@ __global__ __launch_bounds__(256, EB >= 8 ? 1 : 2) void gate_two_phase_kernel(
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the list is written
         __builtin_amdgcn_wave_barrier();
         constexpr int kCh = kTpPairCap / kWave;
-        const int nc = total <= kWave ? 1 : (total <= 2 * kWave ? 2 : (total <= 4 * kWave ? 4 : 8));
+        const int nc = total <= kWave ? 1 : (total + kWave - 1) / kWave;
         int pc[kCh];
         float z[kCh];
 #pragma unroll
@@ -365,30 +437,31 @@ __global__ __launch_bounds__(256, EB >= 8 ? 1 : 2) void gate_two_phase_kernel(
             pc[j] = (total > 0 && r < total) ? pair[r] : (total > 0 ? pair[0] : 0);
             z[j] = 0.0f;
         }
-        __syncthreads();  // every list is read before the staging area refills
-        load(0, false);
-        put(0);
-        __syncthreads();
-        for (int kt = 0; kt < KT; ++kt) {
-            if (kt + 1 < KT) load((kt + 1) * kTpK, false);
-            const uint8_t* X = lds + (kt & 1) * STAGE;
-            const uint8_t* W = X + XB;
+        __syncthreads();  // every list is read before the ring refills
+        stream(0, [&](const uint8_t* S) {  // the chains' order: from slice 0
+            const uint8_t* X = S;
+            const uint8_t* W = S + RG::kXBytes;
             if (total > 0) {
-                if (nc == 1) run_chains<1>(X, W, pc, z);
-                else if (nc == 2) run_chains<2>(X, W, pc, z);
-                else if (nc == 4) run_chains<4>(X, W, pc, z);
-                else run_chains<8>(X, W, pc, z);
+                switch (nc) {
+                    case 1: run_chains<1>(X, W, pc, z); break;
+                    case 2: run_chains<2>(X, W, pc, z); break;
+                    case 3: run_chains<3>(X, W, pc, z); break;
+                    case 4: run_chains<4>(X, W, pc, z); break;
+                    case 5: run_chains<5>(X, W, pc, z); break;
+                    case 6: run_chains<6>(X, W, pc, z); break;
+                    case 7: run_chains<7>(X, W, pc, z); break;
+                    default: run_chains<8>(X, W, pc, z); break;
+                }
             }
-            if (kt + 1 < KT) put((kt + 1) & 1);
-            __syncthreads();
-        }
+        });
+        __syncthreads();  // every wave is done with the last slice before the lists' bytes are rewritten
         // the exact logits of the listed pairs, in the wave's own part
 #pragma unroll
         for (int j = 0; j < kCh; ++j) {
             const int r = j * kWave + lane;
             if (r < total) {
                 const int e = pc[j] & 0xffff;
-                pz[r] = bias != nullptr ? z[j] + bias[e] : z[j];
+                pz[r] = bias != nullptr ? z[j] + nb[e] : z[j];
             }
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);
@@ -446,14 +519,15 @@ namespace {
 template <int EB>
 hipError_t launch_tp(const moe_shape& s, const void* x, const void* wg, const float* bias,
                      int32_t* idx, float* w, hipStream_t st) {
-    constexpr int lds = 2 * (kTpTok * kTpK * 2 + EB * 32 * kTpK * 2) + (kTpTok + EB * 32) * 4 +
-                        kTpTok * EB * 4 + 16;
-    static_assert(2 * (kTpTok * kTpK * 2) >= 4 * 2 * kTpPairCap * 4, "pair lists fit in the staging area");
+    using RG = TpRing<EB>;
+    constexpr int lds = RG::kLds;
+    static_assert(RG::kSlots * RG::kSlot >= RG::kWaves * 2 * kTpPairCap * 4, "pair lists fit in the ring");
+    static_assert(lds <= 160 * 1024, "LDS of one work-group");
     static hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gate_two_phase_kernel<EB>),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (attr != hipSuccess) return attr;
-    const unsigned blocks = static_cast<unsigned>((s.T + kTpTok - 1) / kTpTok);
-    gate_two_phase_kernel<EB><<<blocks, 256, lds, st>>>(static_cast<const bf16_t*>(x),
+    const unsigned blocks = static_cast<unsigned>((s.T + RG::kTok - 1) / RG::kTok);
+    gate_two_phase_kernel<EB><<<blocks, RG::kThreads, lds, st>>>(static_cast<const bf16_t*>(x),
                                                          static_cast<const bf16_t*>(wg), bias, s.T,
                                                          s.d, s.E, s.k, idx, w);
     return hipGetLastError();
@@ -470,11 +544,13 @@ hipError_t launch_tp(const moe_shape& s, const void* x, const void* wg, const fl
 // overrides the choice (both give the same results; tests use it to run
 // each path at any size).
 bool gate_two_phase_chosen(const moe_shape& s) {
-    if (s.act != MOE_BF16 || s.E > 256) return false;
+    // (d below 2^21: the ring's offsets, and the out-of-range offset it
+    // uses for chunks past d, stay within 32 bits)
+    if (s.act != MOE_BF16 || s.E > 256 || s.d >= (1 << 21)) return false;
     const char* force = std::getenv("MOE_GATE_PATH");
     if (force != nullptr && std::strcmp(force, "one_phase") == 0) return false;
     const bool forced = force != nullptr && std::strcmp(force, "two_phase") == 0;
-    return forced || (s.E >= 96 && s.T >= 256 * kTpTok);
+    return forced || (s.E >= 96 && s.T >= 32768);
 }
 
 bool launch_gate_two_phase(const moe_shape& s, const void* x, const void* wg, const float* bias,
