@@ -26,9 +26,9 @@
 // among the candidates by (z, id) and the softmax over the selected logits,
 // exactly as the one-phase kernel computes them.
 //
-// One work-group per CU takes 256 tokens (eight waves; 128 tokens and four
-// waves with more than 128 experts, whose accumulators need the registers of
-// two waves). Both phases that read x stream 32-wide K slices of x and of the
+// A work-group takes 256 tokens (eight waves) with 65 to 128 experts, else
+// 128 (four waves: with more than 128 experts the accumulators need the
+// registers of two waves; with 64 or fewer, two work-groups fit on a CU). Both phases that read x stream 32-wide K slices of x and of the
 // gate weight through a ring of six LDS slots filled by direct buffer-to-LDS
 // loads, five slices in flight: the reads of x bound the gate, and with about
 // 4 us of loaded HBM latency it takes some 80 KB of x in flight per CU to
@@ -66,7 +66,7 @@ __device__ __forceinline__ int tp_off(int r, int c) {
 // of 1 KB requests per slot.
 template <int EB>
 struct TpRing {
-    static constexpr int kTok = EB <= 4 ? 256 : 128;  // tokens per work-group
+    static constexpr int kTok = EB == 4 ? 256 : 128;  // tokens per work-group
     static constexpr int kWaves = kTok / 32;
     static constexpr int kThreads = kWaves * kWave;
     static constexpr int kWRows = EB * 32 > 16 * kWaves ? EB * 32 : 16 * kWaves;
@@ -536,9 +536,10 @@ hipError_t launch_tp(const moe_shape& s, const void* x, const void* wg, const fl
 
 // The two-phase gate for bf16 inputs where it is the faster one: its cost
 // follows the reads of x (twice) and the candidates' chains, the one-phase
-// kernel's the T*E chains, so it wins with many experts -- measured: E = 128,
-// T = 65536, d = 4096 in 0.51 ms against 1.37 ms; E = 64, T = 32768 in 0.47
-// against 0.36 -- and needs enough 128-token work-groups to fill the chip.
+// kernel's the T*E chains, so it wins with many experts -- measured at
+// d = 4096: E = 128, T = 65536, k = 4 in 0.36-0.41 ms against 1.37 ms;
+// E = 64, T = 32768, k = 6 in 0.35 against 0.39; E = 32, T = 4096 in 0.14
+// against 0.03 -- and needs enough work-groups to fill the chip.
 // Returns false (nothing launched) otherwise.
 // The environment variable MOE_GATE_PATH = "two_phase" or "one_phase"
 // overrides the choice (both give the same results; tests use it to run
@@ -550,7 +551,7 @@ bool gate_two_phase_chosen(const moe_shape& s) {
     const char* force = std::getenv("MOE_GATE_PATH");
     if (force != nullptr && std::strcmp(force, "one_phase") == 0) return false;
     const bool forced = force != nullptr && std::strcmp(force, "two_phase") == 0;
-    return forced || (s.E >= 96 && s.T >= 32768);
+    return forced || (s.E >= 64 && s.T >= 32768);
 }
 
 bool launch_gate_two_phase(const moe_shape& s, const void* x, const void* wg, const float* bias,
