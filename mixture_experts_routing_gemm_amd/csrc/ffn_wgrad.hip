@@ -418,4 +418,42 @@ hipError_t launch_ffn_wgrad(const moe_shape& s, const int32_t* offsets, const vo
     return hipGetLastError();
 }
 
+// The gate backward's weight gradient (see GateMfmaPlan): for the C chunks
+// of token rows at `offsets` (C + 1 entries, in the workspace), the [dW1;
+// dW3] tiles of the kernel with the chunks as groups, Zp [T, F] as the
+// [da | db] rows (h = F / 2) and x [T, d] as the input rows: chunk c's
+// features f < F / 2 go to p1 [C, F / 2, d], the others to p3. No dW2 tiles.
+// ws: C + 32 ints (the chunk order and the queues).
+hipError_t launch_wgrad_planes(const int32_t* offsets, int C, int64_t T, int d, int F,
+                               const void* zp, const void* x, float* p1, float* p3, void* ws,
+                               hipStream_t st) {
+    static hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_wgrad_kernel),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, kWgLds + 16);
+    if (attr != hipSuccess) return attr;
+    if (C < 1 || C > kMaxE || F % kWgT != 0 || d % kWgT != 0) return hipErrorInvalidValue;
+    int32_t* order = static_cast<int32_t*>(ws);
+    int32_t* counters = order + C + 16;
+    wgrad_plan_kernel<<<1, 256, 0, st>>>(offsets, C, 0, T, order, counters);
+    WgradArgs a{};
+    a.offsets = offsets;
+    a.order = order;
+    a.counters = counters;
+    a.T = T;
+    a.E = C;
+    a.S = 0;
+    a.d = d;
+    a.h = F / 2;
+    a.dd_r = static_cast<const uint8_t*>(zp);
+    a.v_r = static_cast<const uint8_t*>(x);
+    a.bytes_dd_r = static_cast<uint32_t>(static_cast<uint64_t>(T) * F * 2);
+    a.bytes_v_r = static_cast<uint32_t>(static_cast<uint64_t>(T) * d * 2);
+    a.dw1 = p1;
+    a.dw3 = p3;
+    a.t13 = (F / kWgT) * (d / kWgT);
+    a.ntiles = a.t13;
+    const unsigned blocks = static_cast<unsigned>(std::max(8, device_cus() & ~7));
+    ffn_wgrad_kernel<<<blocks, 512, kWgLds + 16, st>>>(a);
+    return hipGetLastError();
+}
+
 }  // namespace moe

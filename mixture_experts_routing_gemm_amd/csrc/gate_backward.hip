@@ -12,11 +12,16 @@
 // zero. Through z = x Wg^T that sparse dz gives
 //   dx[t]  += sum_j dz[t,j] Wg[topk_idx[t,j]]   (k rows of Wg, L2-resident)
 //   dWg[e]  = sum over slots with topk_idx = e of dz[t,j] x[t].
-// Both are HBM-bound (x and dx are each streamed once), not GEMMs: dz has
-// only k non-zeros per token. dWg is summed per range of tokens in LDS (each
-// sum by one thread, in token order), stored as one float32 partial per
-// range, and the partials are then added in range order: no atomics, and
-// the result is the same on every call.
+// dx is HBM-bound (x and dx are each streamed once). dWg, for bf16 x with d
+// a multiple of 256, is dense on the matrix cores: dz spread over [T, E] and
+// split exactly into three bf16 planes (GateMfmaPlan), so that dWg = Zp^T x
+// has exact products; the token kernel writes the plane rows, the expert
+// FFN's weight-gradient kernel sums them against x per chunk of tokens, and
+// the chunks and planes are added in a fixed order. Otherwise dWg is summed
+// per range of tokens in LDS (each sum by one thread, in token order),
+// stored as one float32 partial per range, and the partials are then added
+// in range order. No atomics either way: the result is the same on every
+// call.
 #include "moe_device.h"
 
 namespace moe {
@@ -28,14 +33,21 @@ constexpr int kWgradBig = 32768;
 // tokens whose (expert, dz) pairs are staged in LDS at a time
 constexpr int kWgradStage = 64;
 
+// the most plane features of a token row (E <= 256)
+constexpr int kMaxPlaneF = 768;
+
 // One wave per token: dz, then dx[t] = act(dx[t] + sum_j dz_j Wg[e_j]) in
-// float32 (slot order, rounded once).
+// float32 (slot order, rounded once). With zp, also the token's plane row
+// (GateMfmaPlan; F features): slots with the same expert are summed first
+// (in slot order, into the first of them), and the row is built in LDS and
+// stored whole.
 template <typename TAct>
 __global__ __launch_bounds__(256) void gate_backward_token_kernel(
     const TAct* __restrict__ wg, const int32_t* __restrict__ topk_idx,
     const float* __restrict__ topk_w, const float* __restrict__ dtopk_w, int64_t T, int d, int E,
-    int k, float* __restrict__ dz, TAct* __restrict__ dx) {
+    int k, float* __restrict__ dz, TAct* __restrict__ dx, bf16_t* __restrict__ zp, int F) {
     using V = ActVec<TAct>;
+    __shared__ __attribute__((aligned(16))) uint16_t zrow[4][kMaxPlaneF];
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + w;
     if (t >= T) return;
@@ -51,7 +63,6 @@ __global__ __launch_bounds__(256) void gate_backward_token_kernel(
     for (int o = 32; o > 0; o >>= 1) mean += __shfl_xor(mean, o, kWave);
     const float g = wt * (gw - mean);
     if (lane < k) dz[t * k + lane] = g;
-    if (dx == nullptr) return;
     if (e < 0 || e >= E) e = -1;
     int ej[kMaxK];
     float gj[kMaxK];
@@ -60,6 +71,37 @@ __global__ __launch_bounds__(256) void gate_backward_token_kernel(
         ej[j] = __shfl(e, j, kWave);
         gj[j] = __shfl(g, j, kWave);
     }
+    if (zp != nullptr) {
+        uint16_t* row = zrow[w];
+        for (int c = lane; c < F / 8; c += kWave) *reinterpret_cast<u32x4*>(row + 8 * c) = u32x4{0u, 0u, 0u, 0u};
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the zeros are written
+        __builtin_amdgcn_wave_barrier();
+        if (lane < k && e >= 0) {
+            float gs = 0.0f;
+            bool first = true;
+#pragma unroll
+            for (int j = 0; j < kMaxK; ++j) {
+                if (j < k && ej[j] == e) {
+                    gs += gj[j];
+                    if (j < lane) first = false;
+                }
+            }
+            if (first) {
+                const bf16_t hi = f32_to_bf16(gs);
+                const float r1 = gs - bf16_to_f32(hi);
+                const bf16_t mid = f32_to_bf16(r1);
+                const bf16_t lo = f32_to_bf16(r1 - bf16_to_f32(mid));
+                row[e] = hi;
+                row[E + e] = mid;
+                row[2 * E + e] = lo;
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+        for (int c = lane; c < F / 8; c += kWave)
+            store16(zp + t * F + 8 * c, *reinterpret_cast<const u32x4*>(row + 8 * c));
+    }
+    if (dx == nullptr) return;
     const int nchunk = d / V::N;
     for (int c = lane; c < nchunk; c += kWave) {
         const int64_t col = static_cast<int64_t>(c) * V::N;
@@ -206,6 +248,42 @@ __global__ __launch_bounds__(256) void gate_backward_wgrad_kernel(
     }
 }
 
+// The chunk boundaries of the matrix-core weight gradient: offsets[c] =
+// min(T, c * chunk), c = 0..C.
+__global__ __launch_bounds__(256) void gate_chunk_offsets_kernel(int64_t T, int64_t chunk, int C,
+                                                                 int32_t* __restrict__ offsets) {
+    for (int c = threadIdx.x; c <= C; c += 256) {
+        const int64_t o = static_cast<int64_t>(c) * chunk;
+        offsets[c] = static_cast<int32_t>(o < T ? o : T);
+    }
+}
+
+// dWg[e] = sum over the chunks, in order, of (hi + (mid + lo)) of the plane
+// partials: plane p of expert e is feature f = p E + e, in p1 [C, F/2, d]
+// when f < F/2, else in p3 (four columns a thread).
+__global__ __launch_bounds__(256) void gate_plane_reduce_kernel(const float* __restrict__ p1,
+                                                                const float* __restrict__ p3, int C,
+                                                                int E, int d, int F,
+                                                                f32x4* __restrict__ dwg) {
+    const int64_t n4 = static_cast<int64_t>(E) * d / 4;
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= n4) return;
+    const int e = static_cast<int>(i / (d / 4));
+    const int col = static_cast<int>(i - static_cast<int64_t>(e) * (d / 4)) * 4;
+    const int hh = F / 2;
+    auto plane = [&](int c, int f) {
+        const float* src = f < hh ? p1 + (static_cast<int64_t>(c) * hh + f) * d
+                                  : p3 + (static_cast<int64_t>(c) * hh + (f - hh)) * d;
+        return *reinterpret_cast<const f32x4*>(src + col);
+    };
+    f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int c = 0; c < C; ++c) {
+        const f32x4 hi = plane(c, e), mid = plane(c, E + e), lo = plane(c, 2 * E + e);
+        s += hi + (mid + lo);
+    }
+    dwg[i] = s;
+}
+
 // dWg = sum of the nchunk partials, in block order (four columns a thread).
 __global__ __launch_bounds__(256) void gate_backward_reduce_kernel(
     const f32x4* __restrict__ part, int64_t nchunk, int64_t n4, f32x4* __restrict__ dwg) {
@@ -251,24 +329,80 @@ void launch_wgrad(const GateWgradGrid& g, const TAct* x, const int32_t* topk_idx
         launch_wgrad_k<TAct, kMaxK>(g, x, topk_idx, dz, s, part, st);
 }
 
+hipError_t launch_wgrad_planes(const int32_t* offsets, int C, int64_t T, int d, int F,
+                               const void* zp, const void* x, float* p1, float* p3, void* ws,
+                               hipStream_t st);
+
+namespace {
+// the parts of the matrix-core path's workspace: plane partials [C, F, d]
+// float32 (p1 then p3), plane rows [T, F] bf16, chunk offsets and the
+// weight-gradient kernel's order and queues
+struct GateMfmaWs {
+    size_t p1, p3, zp, offsets, meta, total;
+};
+GateMfmaWs gate_mfma_ws(const GateMfmaPlan& p, int64_t T, int d) {
+    GateMfmaWs w{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = (off + bytes + 255) / 256 * 256;
+        return at;
+    };
+    const size_t half = static_cast<size_t>(p.C) * (p.F / 2) * d * 4;
+    w.p1 = take(half);
+    w.p3 = take(half);
+    w.zp = take(static_cast<size_t>(T) * p.F * 2);
+    w.offsets = take(static_cast<size_t>(p.C + 1) * 4);
+    w.meta = take(static_cast<size_t>(p.C + 32) * 4);
+    w.total = off;
+    return w;
+}
+}  // namespace
+
+size_t gate_backward_ws_bytes(const moe_shape& s) {
+    const GateMfmaPlan p = gate_mfma_plan(s.T, s.d, s.E, s.act == MOE_BF16);
+    if (p.use) return gate_mfma_ws(p, s.T, s.d).total;
+    const GateWgradGrid g = gate_wgrad_grid(s.T, s.d, s.E, s.act == MOE_F32 ? 4 : 2);
+    return static_cast<size_t>(g.nchunk > 0 ? g.nchunk : 1) * s.E * s.d * 4;
+}
+
 hipError_t launch_gate_backward(const moe_shape& s, const void* x, const void* wg,
                                 const int32_t* topk_idx, const float* topk_w,
                                 const float* dtopk_w, float* dz, void* dx, float* dwg,
                                 float* part, hipStream_t st) {
     const int64_t T = s.T;
     const GateWgradGrid g = gate_wgrad_grid(T, s.d, s.E, s.act == MOE_F32 ? 4 : 2);
+    const GateMfmaPlan mp = gate_mfma_plan(T, s.d, s.E, s.act == MOE_BF16);
     const int64_t n4 = static_cast<int64_t>(s.E) * s.d / 4;
+    const unsigned tblocks = static_cast<unsigned>((T + 3) / 4);
+    if (mp.use) {
+        uint8_t* base = reinterpret_cast<uint8_t*>(part);
+        const GateMfmaWs w = gate_mfma_ws(mp, T, s.d);
+        float* p1 = reinterpret_cast<float*>(base + w.p1);
+        float* p3 = reinterpret_cast<float*>(base + w.p3);
+        bf16_t* zp = reinterpret_cast<bf16_t*>(base + w.zp);
+        int32_t* offsets = reinterpret_cast<int32_t*>(base + w.offsets);
+        gate_backward_token_kernel<bf16_t><<<tblocks, 256, 0, st>>>(
+            static_cast<const bf16_t*>(wg), topk_idx, topk_w, dtopk_w, T, s.d, s.E, s.k, dz,
+            static_cast<bf16_t*>(dx), zp, mp.F);
+        gate_chunk_offsets_kernel<<<1, 256, 0, st>>>(T, mp.chunk, mp.C, offsets);
+        const hipError_t err =
+            launch_wgrad_planes(offsets, mp.C, T, s.d, mp.F, zp, x, p1, p3, base + w.meta, st);
+        if (err != hipSuccess) return err;
+        gate_plane_reduce_kernel<<<static_cast<unsigned>((n4 + 255) / 256), 256, 0, st>>>(
+            p1, p3, mp.C, s.E, s.d, mp.F, reinterpret_cast<f32x4*>(dwg));
+        return hipGetLastError();
+    }
     if (T > 0) {
-        const unsigned tblocks = static_cast<unsigned>((T + 3) / 4);
         if (s.act == MOE_F32) {
             gate_backward_token_kernel<float><<<tblocks, 256, 0, st>>>(
                 static_cast<const float*>(wg), topk_idx, topk_w, dtopk_w, T, s.d, s.E, s.k, dz,
-                static_cast<float*>(dx));
+                static_cast<float*>(dx), nullptr, 0);
             launch_wgrad<float>(g, static_cast<const float*>(x), topk_idx, dz, s, part, st);
         } else {
             gate_backward_token_kernel<bf16_t><<<tblocks, 256, 0, st>>>(
                 static_cast<const bf16_t*>(wg), topk_idx, topk_w, dtopk_w, T, s.d, s.E, s.k, dz,
-                static_cast<bf16_t*>(dx));
+                static_cast<bf16_t*>(dx), nullptr, 0);
             launch_wgrad<bf16_t>(g, static_cast<const bf16_t*>(x), topk_idx, dz, s, part, st);
         }
     }

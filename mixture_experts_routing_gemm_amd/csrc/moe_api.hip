@@ -31,6 +31,7 @@ int ffn_hidden_stride(const moe_shape& s);
 bool ffn_fused_plan(const moe_shape& s, int32_t* plan, FfnPlanArgs* fp);
 hipError_t launch_combine(const moe_shape& s, const void* y_perm, const void* y_sh,
                           const int32_t* dest_row, const float* topk_w, void* y, hipStream_t st);
+size_t gate_backward_ws_bytes(const moe_shape& s);
 hipError_t launch_gate_backward(const moe_shape& s, const void* x, const void* wg,
                                 const int32_t* topk_idx, const float* topk_w,
                                 const float* dtopk_w, float* dz, void* dx, float* dwg,
@@ -144,9 +145,9 @@ Layout layout(const moe_shape& s, int stage) {
         L.hsc_s = take(S > 0 ? T * 4 : 0);
     }
     if (stage == MOE_STAGE_GATE_BACKWARD) {
-        // one float32 [E, d] partial of the weight gradient per token range
-        const GateWgradGrid g = gate_wgrad_grid(s.T, s.d, s.E, static_cast<int>(es));
-        L.part = take(static_cast<size_t>(g.nchunk > 0 ? g.nchunk : 1) * E * s.d * 4);
+        // the weight gradient's partials (and, on the matrix-core path, the
+        // plane rows and the chunk queue)
+        L.part = take(gate_backward_ws_bytes(s));
     }
     if (stage == MOE_STAGE_FFN_BACKWARD) {
         // plan, recomputed a / b / hidden rows and their gradients

@@ -150,6 +150,37 @@ inline GateWgradGrid gate_wgrad_grid(int64_t T, int d, int E, int act_bytes) {
     return g;
 }
 
+// The gate backward's weight gradient on the matrix cores, for bf16 x with d
+// a multiple of 256. dz is split exactly into three bf16 planes (hi = bf16(dz),
+// mid = bf16(dz - hi), lo = dz - hi - mid: 8 + 8 + 8 significant bits), laid
+// out as [T, F] rows [hi | mid | lo | zeros] (plane p of expert e at feature
+// p E + e; F = 3E rounded up to 256), and Zp^T x is summed per chunk of
+// tokens by the expert FFN's weight-gradient kernel: every product of a
+// plane value and an x value is exact in float32, so only the order of the
+// float32 sums differs from a per-token sum. About two 256 x 256 tiles per
+// CU, chunks of at least 256 tokens.
+struct GateMfmaPlan {
+    bool use;
+    int F, C;       // plane features; token chunks
+    int64_t chunk;  // tokens per chunk (the last one may be shorter)
+};
+inline GateMfmaPlan gate_mfma_plan(int64_t T, int d, int E, bool bf16) {
+    GateMfmaPlan p{};
+    p.F = ((3 * E + 255) / 256) * 256;
+    const int64_t lim = int64_t(1) << 32;
+    p.use = bf16 && T > 0 && d % 256 == 0 && T * d * 2 < lim && T * p.F * 2 < lim;
+    if (!p.use) return p;
+    const int64_t tiles = static_cast<int64_t>(p.F / 256) * (d / 256);  // per chunk
+    int64_t C = (512 + tiles - 1) / tiles;
+    const int64_t most = (T + 255) / 256;
+    if (C > most) C = most;
+    if (C > 256) C = 256;
+    if (C < 1) C = 1;
+    p.chunk = (T + C - 1) / C;
+    p.C = static_cast<int>((T + p.chunk - 1) / p.chunk);
+    return p;
+}
+
 // Host side: optional events recorded on the stream after each kernel, for
 // per-kernel timing of the whole-layer call (a NULL entry is skipped).
 struct Marks {

@@ -225,6 +225,10 @@ GATE_CASES = [
     ("f32_E100", 300, 96, 100, 3, "f32"),
     ("bf16_top1", 200, 128, 8, 1, "bf16"),
     ("bf16_one_token", 1, 64, 4, 2, "bf16"),
+    # the matrix-core weight gradient (bf16, d % 256 == 0): plane rows of
+    # 768 features (E = 256), padded planes (E = 100), ragged chunks
+    ("bf16_mfma_E256", 700, 512, 256, 8, "bf16"),
+    ("bf16_mfma_E100", 1500, 768, 100, 3, "bf16"),
 ]
 
 
@@ -236,11 +240,14 @@ def _scatter(idx, vals, E):
     return D
 
 
-def check_gate_backward(name, T, d, E, k, act, with_dx=True, seed=21, skew=0.0):
+def check_gate_backward(name, T, d, E, k, act, with_dx=True, seed=21, skew=0.0, repeat=False):
     mm = _mm()
     x = make_rows(T, d, act, seed=seed)
     wg = make_rows(E, d, act, seed=seed + 1)
     idx = make_routing(T, E, k, seed=seed + 2, skew=skew)
+    if repeat:
+        # one expert in two slots of every third token: both slots' terms count
+        idx[::3, 1] = idx[::3, 0]
     w = make_weights(T, k, seed=seed + 3)
     rng = np.random.default_rng(seed + 4)
     dw = rng.standard_normal((T, k)).astype(np.float32)
@@ -292,6 +299,13 @@ def test_gate_backward(case):
 
 def test_gate_backward_without_dx():
     check_gate_backward("no_dx", 700, 256, 32, 6, "bf16", with_dx=False)
+
+
+@pytest.mark.parametrize("d", [256, 200], ids=["mfma", "lds"])
+def test_gate_backward_repeated_expert(d):
+    # both weight-gradient paths sum every slot of an expert, also when a
+    # token lists it twice
+    check_gate_backward(f"repeat_d{d}", 900, d, 16, 4, "bf16", repeat=True)
 
 
 def test_gate_backward_empty_batch_clears_dw_gate():
