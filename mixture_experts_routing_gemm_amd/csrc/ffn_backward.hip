@@ -464,12 +464,16 @@ __global__ __launch_bounds__(kBwdThreads, 2) void ffn_bwd_wgrad_kernel(BwdArgs a
 // dst[b][c][dcol0 + r] = src[b][r][c] for a batch of [rows, cols] bf16
 // matrices (rows and cols multiples of 64; dst rows hold ldd values). One
 // work-group per 64 x 64 block through LDS: 16-byte reads along the source
-// rows, 16-byte writes along the destination rows.
+// rows, 16-byte writes along the destination rows. Routed groups b < E with
+// no rows (offsets[b + 1] == offsets[b]) are skipped: no tile of the
+// backward's GEMMs reads their transposed weights.
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16_t* __restrict__ src, int rows,
                                                              int cols, int64_t sstride,
                                                              bf16_t* __restrict__ dst, int ldd,
-                                                             int dcol0, int64_t dstride) {
+                                                             int dcol0, int64_t dstride,
+                                                             const int32_t* __restrict__ offsets, int E) {
     __shared__ uint16_t t[64][66];
+    if (static_cast<int>(blockIdx.z) < E && offsets[blockIdx.z + 1] == offsets[blockIdx.z]) return;
     const int tid = threadIdx.x, c8 = tid & 7, rr = tid >> 3;
     const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
     const bf16_t* sb = src + blockIdx.z * sstride;
@@ -625,11 +629,11 @@ hipError_t launch_ffn_backward(const moe_shape& s, const void* x_perm, const flo
         bf16_t* w2t = reinterpret_cast<bf16_t*>(w + L.w2t);
         bf16_t* w13t = reinterpret_cast<bf16_t*>(w + L.w13t);
         transpose_bf16_kernel<<<dim3(s.h / 64, s.d / 64, G), 256, 0, st>>>(
-            static_cast<const bf16_t*>(w2), s.d, s.h, dh, w2t, s.d, 0, dh);
+            static_cast<const bf16_t*>(w2), s.d, s.h, dh, w2t, s.d, 0, dh, offsets, s.E);
         transpose_bf16_kernel<<<dim3(s.d / 64, s.h / 64, G), 256, 0, st>>>(
-            static_cast<const bf16_t*>(w1), s.h, s.d, dh, w13t, 2 * s.h, 0, 2 * dh);
+            static_cast<const bf16_t*>(w1), s.h, s.d, dh, w13t, 2 * s.h, 0, 2 * dh, offsets, s.E);
         transpose_bf16_kernel<<<dim3(s.d / 64, s.h / 64, G), 256, 0, st>>>(
-            static_cast<const bf16_t*>(w3), s.h, s.d, dh, w13t, 2 * s.h, s.h, 2 * dh);
+            static_cast<const bf16_t*>(w3), s.h, s.d, dh, w13t, 2 * s.h, s.h, 2 * dh, offsets, s.E);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         e = launch_ffn_bwd_gemms(s, x_perm, qparams, offsets, x, w1, w3, w2t, w13t, dy_perm, dy_sh,
                                  dx_perm, dx_sh, reinterpret_cast<int32_t*>(w + L.plan),

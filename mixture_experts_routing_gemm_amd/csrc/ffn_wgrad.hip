@@ -204,6 +204,28 @@ void ffn_wgrad_kernel(WgradArgs a) {
         // has passed the barrier that follows its read)
         if (tid == 0) lds_next[it & 1] = per_xcd + atomicAdd(a.counters + xcd, 1);
 
+        if (t.nrows == 0) {
+            // a group without rows (common under skewed routing): its
+            // gradient tile is zero, stored a row of 16-byte chunks per
+            // 64 lanes instead of through the accumulator layout
+            const int M0 = t.mt * kWgT, N0 = t.nt * kWgT;
+            const int ncols = t.type == 0 ? kWgT : min(kWgT, a.h - N0);
+            const int q = ncols / 4;  // 16-byte chunks a row
+            for (int i = tid; i < kWgT * q; i += 512) {
+                const int m = M0 + i / q, col = N0 + 4 * (i % q);
+                float* out;
+                if (t.type == 0)
+                    out = m < a.h ? a.dw1 + (static_cast<int64_t>(t.g) * a.h + m) * a.d + col
+                                  : a.dw3 + (static_cast<int64_t>(t.g) * a.h + (m - a.h)) * a.d + col;
+                else
+                    out = a.dw2 + (static_cast<int64_t>(t.g) * a.d + m) * a.h + col;
+                *reinterpret_cast<f32x4*>(out) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+            wait_vmcnt<0>();
+            __syncthreads();
+            c = lds_next[it & 1];
+            continue;
+        }
         // operands of this tile: A rows hold its M features, B rows its N
         const uint8_t* abuf;
         const uint8_t* bbuf;
