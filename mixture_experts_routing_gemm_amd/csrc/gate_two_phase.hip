@@ -304,7 +304,7 @@ __global__ __launch_bounds__(TpRing<EB>::kThreads, 1) void gate_two_phase_kernel
                 const float zt = acc[eb][v] + (bias != nullptr ? nb[e] : 0.0f);
                 const float eps = c1 * nw[e] + 8.0f * 0x1p-24f * __builtin_fabsf(zt) + 0x1p-126f;
                 const float L = zt - eps;
-                acc[eb][v] = zt;  // keep zt for the upper bounds
+                acc[eb][v] = zt + eps;  // keep the upper bound U for the mask
                 bad = bad || !(__builtin_fabsf(zt) < __builtin_inff()) || !(eps < __builtin_inff());
                 // insert L into the descending top-k list
                 float cur = L;
@@ -348,9 +348,7 @@ __global__ __launch_bounds__(TpRing<EB>::kThreads, 1) void gate_two_phase_kernel
                 const int b = 8 * (v >> 2) + 4 * lg + (v & 3);
                 const int e = eb * 32 + b;
                 if (e >= E) continue;
-                const float zt = acc[eb][v];
-                const float eps = c1 * nw[e] + 8.0f * 0x1p-24f * __builtin_fabsf(zt) + 0x1p-126f;
-                if (bad || zt + eps >= tau) word |= 1u << b;
+                if (bad || acc[eb][v] >= tau) word |= 1u << b;
             }
             word |= __shfl_xor(word, 32, kWave);
             if (lg == 0) masks[tl * EB + eb] = word;
