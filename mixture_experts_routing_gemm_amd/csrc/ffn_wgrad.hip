@@ -15,7 +15,8 @@
 // slots, three slices ahead), and the matrix-core fragments, which need 8
 // consecutive rows of one feature per lane, come out of LDS through the
 // transposing read (ds_read_b64_tr_b16: within each 16 lanes, lane i gets
-// element r of the 4 values that lane (i >> 2) + 4 r points at, value i & 3).
+// element r of the 4 values that lane (i >> 2) + 4 r points at, value i & 3),
+// interleaved one fragment per MFMA.
 //
 // One work-group of eight waves per CU takes 256 x 256 output tiles from a
 // list ordered by the group's rows, longest first; each output element has
@@ -115,38 +116,39 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint8_t*)p));
 }
 
-__device__ __forceinline__ bf16x8 wg_join(uint64_t lo, uint64_t hi) {
-    const v4i16 v = __builtin_bit_cast(v4i16, lo), w = __builtin_bit_cast(v4i16, hi);
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v, w, 0, 1, 2, 3, 4, 5, 6, 7));
+// The slices' buffer -> LDS requests are inline asm, with the LDS address
+// bound to M0 as an input so that the compiler sets M0 itself (the asm has no
+// register results: the request writes LDS only, and the kernel's counted
+// waits and barriers order it). Issued through the builtin instead, each
+// request counts as an LDS write to the compiler, which then waits for every
+// outstanding request before each transposing read it cannot tell apart from
+// them, draining the prefetched slices at every step. The reads themselves
+// are builtins, so the compiler schedules them among the MFMAs with partial
+// waits. (s_nop 0: one wait state between an M0 write and an LDS DMA.)
+typedef int i32x4w __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void wg_dma16(i32x4w rsrc, uint32_t voff, uint32_t ldsaddr) {
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "{m0}"(ldsaddr));
 }
-
-// Three fragments of half-slice KS (rows 16 KS .. 16 KS + 15) of a slice:
-// out[j] from the operand at a[j] (the slot address of A or B plus this
-// lane's offset), OFF[j] = 0 for A, 16384 for B. Each fragment is two
-// transposing reads, rows +0 and +4 (2048 bytes apart; the next half-slice
-// 8192 further). Written as an asm block that waits for its own reads before
-// it ends: the builtin form of the read makes the compiler wait for every
-// outstanding buffer-to-LDS request first, which would drain the prefetched
-// slices at every step.
-template <int KS, int O0, int O1, int O2>
-__device__ __forceinline__ void wg_read3(uint32_t a0, uint32_t a1, uint32_t a2, bf16x8& f0, bf16x8& f1,
-                                         bf16x8& f2) {
-    constexpr int k = KS * 8192;
-    uint64_t r[6];
-    asm volatile("ds_read_b64_tr_b16 %0, %6 offset:%c9\n"
-                 "ds_read_b64_tr_b16 %1, %6 offset:%c10\n"
-                 "ds_read_b64_tr_b16 %2, %7 offset:%c11\n"
-                 "ds_read_b64_tr_b16 %3, %7 offset:%c12\n"
-                 "ds_read_b64_tr_b16 %4, %8 offset:%c13\n"
-                 "ds_read_b64_tr_b16 %5, %8 offset:%c14\n"
-                 "s_waitcnt lgkmcnt(0)"
-                 : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5])
-                 : "v"(a0), "v"(a1), "v"(a2), "i"(O0 + k), "i"(O0 + k + 2048), "i"(O1 + k),
-                   "i"(O1 + k + 2048), "i"(O2 + k), "i"(O2 + k + 2048)
-                 : "memory");
-    f0 = wg_join(r[0], r[1]);
-    f1 = wg_join(r[2], r[3]);
-    f2 = wg_join(r[4], r[5]);
+// a raw buffer resource over [base, base + bytes), wave-uniform
+__device__ __forceinline__ i32x4w wg_rsrc(const uint8_t* base, uint32_t bytes) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    i32x4w r;
+    r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b)));
+    r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b >> 32) & 0xffffu));
+    r[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+    r[3] = kBufferFlags;
+    return r;
+}
+// One fragment: the transposing reads of rows +0 and +4 (2048 bytes apart) at
+// byte offset a of the work-group's LDS (lds_base).
+__device__ __forceinline__ bf16x8 wg_frag(const uint8_t* lds_base, uint32_t a) {
+    typedef __attribute__((address_space(3))) v4i16 lv4;
+    const __attribute__((address_space(3))) uint8_t* p = (const __attribute__((address_space(3))) uint8_t*)lds_base;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lv4*)(p + a));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lv4*)(p + a + 2048));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 struct WgTile {
@@ -253,6 +255,7 @@ void ffn_wgrad_kernel(WgradArgs a) {
         bbuf = uniform_ptr(bbuf);
         abytes = __builtin_amdgcn_readfirstlane(abytes);
         bbytes = __builtin_amdgcn_readfirstlane(bbytes);
+        const i32x4w ars = wg_rsrc(abuf, abytes), brs = wg_rsrc(bbuf, bbytes);
         // this lane's two chunks per operand and slice: request q (0, 1) of
         // the wave fills LDS bytes 1024 (2 wave + q) + 16 lane of the
         // operand's slice, i.e. slice row k = 4 wave + 2 q + lane / 32 and
@@ -277,8 +280,8 @@ void ffn_wgrad_kernel(WgradArgs a) {
                 const bool in = k < t.nrows;
                 const uint32_t ao = in ? arow[q] + static_cast<uint32_t>(k) * lda : 0xfffffff0u;
                 const uint32_t bo = in ? brow[q] + static_cast<uint32_t>(k) * ldb : 0xfffffff0u;
-                buffer_to_lds16<0>(abuf, abytes, ao, 0, slot + 1024 * (2 * wave + q));
-                buffer_to_lds16<0>(bbuf, bbytes, bo, 0, slot + kWgOp + 1024 * (2 * wave + q));
+                wg_dma16(ars, ao, __builtin_amdgcn_readfirstlane(lds_addr(slot + 1024 * (2 * wave + q))));
+                wg_dma16(brs, bo, __builtin_amdgcn_readfirstlane(lds_addr(slot + kWgOp + 1024 * (2 * wave + q))));
             }
         };
 
@@ -291,24 +294,26 @@ void ffn_wgrad_kernel(WgradArgs a) {
                 for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
         // One step per slice k. First half: slice k+3 is requested (into the
-        // slot of slice k-1), the MFMAs of slice k's first 16 rows (fa0, fb0,
-        // read before) are issued, and the fragments of its last 16 rows are
-        // read while those MFMAs run; then, once slice k+1 has landed and
-        // every wave has passed the barrier, the MFMAs of the last 16 rows are
-        // issued and slice k+1's first fragments read meanwhile.
+        // slot of slice k-1), and the MFMAs of slice k's first 16 rows (fa0,
+        // fb0, read before) are issued, each followed by the read of one
+        // fragment of its last 16 rows; then, once slice k+1 has landed and
+        // every wave has passed the barrier, the MFMAs of the last 16 rows,
+        // each followed by the read of one of slice k+1's first fragments.
+        // (After the last slice those reads take a settled slot and are not
+        // used: one MFMA chain per half, with no branch around it.)
         bf16x8 fa0[4], fb0[2], fa1[4], fb1[2];
-        auto read_half = [&](const uint8_t* A, auto KS, bf16x8 (&fa)[4], bf16x8 (&fb)[2]) {
+        // fragment i of half-slice KS of slot R: the two B blocks, then the
+        // four A blocks
+        auto frag_of = [&](const uint8_t* R, auto KS, int i) {
             constexpr int ks = decltype(KS)::value;
-            const uint32_t base = lds_addr(A);
-            wg_read3<ks, kWgOp, kWgOp, 0>(base + fo[0], base + fo[1], base + fo[2], fb[0], fb[1], fa[0]);
-            wg_read3<ks, 0, 0, 0>(base + fo[3], base + fo[4], base + fo[5], fa[1], fa[2], fa[3]);
+            const uint32_t base = static_cast<uint32_t>(R - lds) + ks * 8192;
+            return wg_frag(lds, base + (i < 2 ? kWgOp : 0) + fo[i]);
         };
-        auto mma = [&](const bf16x8* fa, const bf16x8* fb) {
+        auto read_half = [&](const uint8_t* R, auto KS, bf16x8 (&fa)[4], bf16x8 (&fb)[2]) {
+            fb[0] = frag_of(R, KS, 0);
+            fb[1] = frag_of(R, KS, 1);
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
-                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mb], fb[nb], acc[mb][nb], 0, 0, 0);
+            for (int i = 0; i < 4; ++i) fa[i] = frag_of(R, KS, 2 + i);
         };
         if (KT > 0) {
             issue(0);
@@ -322,11 +327,25 @@ void ffn_wgrad_kernel(WgradArgs a) {
             ring_barrier();
             read_half(lds, ic<0>(), fa0, fb0);
         }
+        // the MFMAs of one half-slice (fa, fb), each followed by the read of
+        // one fragment of half-slice KS of slot R (into na, nb)
+        auto mma_read = [&](const bf16x8* fa, const bf16x8* fb, const uint8_t* R, auto KS, bf16x8 (&na)[4],
+                            bf16x8 (&nb)[2]) {
+            static_for<0, 8>([&](auto I) {
+                constexpr int i = decltype(I)::value;
+                acc[i / 2][i % 2] =
+                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i / 2], fb[i % 2], acc[i / 2][i % 2], 0, 0, 0);
+                if constexpr (i < 2)
+                    nb[i] = frag_of(R, KS, i);
+                else if constexpr (i < 6)
+                    na[i - 2] = frag_of(R, KS, i);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        };
         for (int k = 0; k < KT; ++k) {
             const uint8_t* A = lds + (k & 3) * kWgSlot;
             if (k + 3 < KT) issue(k + 3);
-            mma(fa0, fb0);
-            read_half(A, ic<1>(), fa1, fb1);
+            mma_read(fa0, fb0, A, ic<1>(), fa1, fb1);
             const bool next = k + 1 < KT;
             if (next) {
                 // slices issued after k+1: k+2 and k+3, as far as they exist
@@ -335,8 +354,7 @@ void ffn_wgrad_kernel(WgradArgs a) {
                 else wait_vmcnt<0>();
                 ring_barrier();
             }
-            mma(fa1, fb1);
-            if (next) read_half(lds + ((k + 1) & 3) * kWgSlot, ic<0>(), fa0, fb0);
+            mma_read(fa1, fb1, lds + ((k + 1) & 3) * kWgSlot, ic<0>(), fa0, fb0);
         }
 
         // epilogue: acc[mb][nb][v] is output row m = wm*128 + mb*32 + 8 (v/4)
