@@ -79,6 +79,7 @@ KERNEL_SOURCES = {
     "dispatch_scan": CSRC + "dispatch.hip",
     "dispatch_permute": CSRC + "dispatch.hip",
     "dispatch_permute_fp8": CSRC + "dispatch.hip",
+    "dispatch_map": CSRC + "dispatch.hip",
     "ffn_up": CSRC + "grouped_ffn.hip",
     "ffn_down": CSRC + "grouped_ffn.hip",
     "ffn_hidden_quant": CSRC + "fp8_rows.hip",
@@ -86,11 +87,14 @@ KERNEL_SOURCES = {
 }
 
 
-def algorithmic(cfg, routed=None):
+def algorithmic(cfg, routed=None, gathered=False):
     """Algorithmic bytes / FLOPs of each stage for one layer forward.
 
     routed: the dispatched rows (T*k unless a capacity limit dropped some).
     The fp8 per-expert and global modes read x once more for the ranges.
+    gathered: the forward's up-projection reads its routed rows from x
+    through src_token, so its dispatch stage moves only the routing maps;
+    "dispatch_rows_bytes" is what the permutation into x_perm moves.
     """
     T, d, E, k, S, h = cfg.T, cfg.d, cfg.E, cfg.k, cfg.S, cfg.h
     R = T * k if routed is None else routed
@@ -99,11 +103,15 @@ def algorithmic(cfg, routed=None):
     bw = 1 if getattr(cfg, "weights", "act") == "fp8" else b  # bytes per weight
     rows = R + S * T
     xreads = 2 if getattr(cfg, "quant", "token") != "token" else 1
+    rows_bytes = (xreads * T * d * b + R * d * bp + 8 * T * k + 4 * T * k
+                  + (8 * R if cfg.dispatch == "fp8" else 0))
     return {
         "gate_bytes": T * d * b + E * d * b + 8 * T * k,
         "gate_flops": 2 * T * d * E,
-        "dispatch_bytes": xreads * T * d * b + R * d * bp + 8 * T * k + 4 * T * k
-        + (8 * R if cfg.dispatch == "fp8" else 0),
+        # ids in, dest_row and src_token out (and, unless gathered, x in and
+        # the permuted rows out)
+        "dispatch_bytes": 8 * T * k + 4 * R if gathered else rows_bytes,
+        "dispatch_rows_bytes": rows_bytes,
         "ffn_up_flops": 4 * rows * d * h,
         # token rows in, both weight matrices of every group, hidden rows out
         "ffn_up_bytes": R * d * bp + S * T * d * (bw if bw == 1 else b) + (E + S) * 2 * h * d * bw
@@ -251,6 +259,44 @@ def backward_leg(mm, torch, cfg, shape, buf, stream, A, x, wg, w1, w3, w2, reps=
     out["ffn_backward"] = ffn_backward_leg(mm, torch, cfg, shape, buf, stream, x, w1, w3, w2,
                                            reps=max(3, reps // 4))
     return out
+
+
+def dispatch_leg(mm, torch, cfg, shape, buf, stream, x, flush_cache, nbytes, reps=10):
+    """Time moe_dispatch with its permuted rows written out (x_perm), on this
+    forward's routing, each call after the cache flush, one event pair
+    around each call: the permutation's HBM rate, which the whole-layer
+    forward does not pay when its up-projection gathers the rows."""
+    T, d, E, k = cfg.T, cfg.d, cfg.E, cfg.k
+    R = T * k
+    x_perm = torch.empty((R, d), dtype=torch.bfloat16, device="cuda")
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    dest = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    src = torch.empty(R, dtype=torch.int32, device="cuda")
+    ws_d = mm.alloc_workspace(shape, mm.STAGE_DISPATCH)
+
+    def call():
+        mm.moe_dispatch(shape, x, buf.topk_idx, counts, offsets, dest, src, x_perm, None, ws_d,
+                        stream)
+    call()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    torch.cuda.synchronize()
+    for i, (a_, b_) in enumerate(ev):
+        flush_cache(i)
+        a_.record(stream)
+        call()
+        b_.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.median([a_.elapsed_time(b_) for a_, b_ in ev]))
+    n = int(offsets[-1].item())
+    same = bool(torch.equal(src[:n], buf.src_token[:n]) and torch.equal(dest, buf.dest_row)
+                and torch.equal(offsets, buf.offsets))
+    del x_perm, counts, offsets, dest, src, ws_d
+    torch.cuda.empty_cache()
+    return {"us": round(ms * 1e3, 2), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "algorithmic_bytes": nbytes, "maps_equal_forward": same}
 
 
 def ffn_backward_leg(mm, torch, cfg, shape, buf, stream, x, w1, w3, w2, reps=5):
@@ -405,7 +451,8 @@ def run_workload(cfg, steps, warmup, flush, with_backward=False, keep_host=False
     kmean = dict(zip(names, per_kernel.mean(axis=0).tolist()))
 
     routed = int(buf.offsets[-1].item())
-    A = algorithmic(cfg, routed)
+    gathered = "dispatch_map" in names
+    A = algorithmic(cfg, routed, gathered)
     ms_med = float(np.median(step_ms))
     gate_name = names[0]
     t_gate = kmean[gate_name]
@@ -448,6 +495,10 @@ def run_workload(cfg, steps, warmup, flush, with_backward=False, keep_host=False
         # every logit is a canonical fma chain on the non-packed float32 vector units
         res["gate_frac_of_f32_nonpacked_peak"] = round(gate_flop_rate / F32_NONPACKED_PEAK_TFLOPS, 4)
     res["gemm_peak_tflops"] = gemm_peak
+    if gathered:
+        res["rows_gathered_in_ffn_up"] = True
+        res["dispatch_materialized"] = dispatch_leg(mm, torch, cfg, shape, buf, stream, x,
+                                                    flush_cache, A["dispatch_rows_bytes"])
     extra = {"A": A, "t_up": t_up, "gemm_peak": gemm_peak}
     if with_backward and not fp8w:
         res["backward_stages"] = backward_leg(mm, torch, cfg, shape, buf, stream, A, x, wg,

@@ -422,6 +422,9 @@ __device__ __forceinline__ int token_dest(const int32_t* __restrict__ topk_idx,
     return dst;
 }
 
+// ROWS = false: the maps only, for a forward whose up-projection gathers
+// the rows from x itself
+template <bool ROWS>
 __global__ __launch_bounds__(256) void dispatch_permute_kernel(
     const uint8_t* __restrict__ x, const int32_t* __restrict__ topk_idx,
     const int32_t* __restrict__ rank, const int32_t* __restrict__ pre,
@@ -437,6 +440,7 @@ __global__ __launch_bounds__(256) void dispatch_permute_kernel(
     const int dst =
         token_dest(topk_idx, rank, pre, offsets, cap, reassign, t, E, k, lane, dest_row,
                    src_token);
+    if (!ROWS) return;
     int dj[kMaxK];
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) dj[j] = __shfl(dst, j, kWave);
@@ -740,7 +744,9 @@ hipError_t launch_dispatch(const moe_shape& s, const void* x, const int32_t* top
             s.quant == MOE_QUANT_TOKEN_ABSMAX ? 1 : 0, x_self, q_self);
     } else {
         const int row_bytes = s.d * (s.act == MOE_F32 ? 4 : 2);
-        dispatch_permute_kernel<<<pblocks, 256, 0, st>>>(
+        // no x_perm: the maps only (the rows are gathered where they are used)
+        auto kern = x_perm == nullptr ? dispatch_permute_kernel<false> : dispatch_permute_kernel<true>;
+        kern<<<pblocks, 256, 0, st>>>(
             static_cast<const uint8_t*>(x), topk_idx, rank, pre, offsets, s.capacity, reassign, s.T,
             s.E, s.k, row_bytes, dest_row, src_token, static_cast<uint8_t*>(x_perm), fp);
     }

@@ -68,6 +68,10 @@ __global__ __launch_bounds__(256) void ffn_plan_kernel(const int32_t* __restrict
 
 struct GemmArgs {
     const uint8_t* a_routed;  // routed A rows: x_perm (bf16 or fp8 codes) or H_r
+    // bf16 up-projection of the persistent kernel: when set, routed row r is
+    // token a_gather[r] of a_shared (x) and a_routed is not read, so the
+    // permuted rows never have to be written out
+    const int32_t* a_gather;
     const float* qparams;     // fp8 rows: [rows, 2] = (scale, centre)
     const uint8_t* a_shared;  // shared A rows: x [T, d] (up) or H_s [T, S*h] (down)
     const int32_t* offsets;   // [E+1]
@@ -492,15 +496,37 @@ __device__ __forceinline__ TileInfo decode_tile(const GemmArgs& a, int L, int ns
     return ti;
 }
 
+// the bf16 up-projection may read its routed rows straight from x
+template <int MODE>
+constexpr bool can_gather() { return MODE == kModeUp; }
+
+// Tokens of the rows that this lane's requests (q = 0, 1) and its partner's
+// (q = 2, 3) fetch for a routed tile, numbered as tile_sources numbers them,
+// when the rows are gathered from x.
+template <int MODE>
+__device__ __forceinline__ void gather_tokens(const GemmArgs& a, const TileInfo& ti, int wave,
+                                              int lane, int (&tok)[4]) {
+    const int last = ti.nrows - 1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int wv = q < 2 ? wave : (wave & 3) + 4;
+        const int r = wv * 32 + (q & 1) * 16 + (lane >> 2);
+        tok[q] = a.a_gather[ti.row_base + min(ti.m0 + r, last)];
+    }
+}
+
 template <int MODE>
 __device__ __forceinline__ void tile_sources(const GemmArgs& a, const TileInfo& ti, int wave,
                                              int lane, const uint8_t* op_ar, const uint8_t* op_as,
-                                             uint32_t by_ar, uint32_t by_as, TileSrc& src) {
+                                             uint32_t by_ar, uint32_t by_as, bool gather,
+                                             const int (&tok)[4], TileSrc& src) {
+    // routed rows gathered from x by token
+    const bool gat = can_gather<MODE>() && gather && !ti.shared;
     // chosen here, by value, once per tile: a choice between two captured
     // locals inside the request code became a load through a chosen
     // address from a private copy
-    src.abuf = uniform_ptr(ti.shared ? op_as : op_ar);
-    src.abytes = __builtin_amdgcn_readfirstlane(ti.shared ? by_as : by_ar);
+    src.abuf = uniform_ptr(ti.shared || gat ? op_as : op_ar);
+    src.abytes = __builtin_amdgcn_readfirstlane(ti.shared || gat ? by_as : by_ar);
     const bool fp8 = is_fp8rows(MODE) && !ti.shared;
     const int K = is_down(MODE) ? (ti.shared ? a.S * a.h : a.h) : a.d;
     const uint32_t eb = is_f8w(MODE) ? 1 : 2;  // bytes per operand value
@@ -512,10 +538,14 @@ __device__ __forceinline__ void tile_sources(const GemmArgs& a, const TileInfo& 
     // 32 fp8 rows of 32 B in plain order (row = wave*32 + lane/2, half
     // lane&1), which the same lane converts to bf16 later. Rows past the
     // group's end re-read its last row; their outputs are never stored.
-    auto token_rows = [&](int wv, uint32_t* out) {
+    auto token_rows = [&](int wv, uint32_t* out, int q0) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            if (fp8) {
+            if (gat) {
+                const int r = wv * 32 + i * 16 + (lane >> 2);
+                const int c = (lane & 3) ^ (((r >> 1) & 3) ^ ((r >> 3) & 1));
+                out[i] = static_cast<uint32_t>(tok[q0 + i]) * static_cast<uint32_t>(K) * eb + c * 16;
+            } else if (fp8) {
                 const int r = wv * 32 + (lane >> 1);
                 const int64_t row = ti.row_base + min(ti.m0 + r, last);
                 out[i] = static_cast<uint32_t>(row * K + (lane & 1) * 16);
@@ -527,12 +557,12 @@ __device__ __forceinline__ void tile_sources(const GemmArgs& a, const TileInfo& 
             }
         }
     };
-    token_rows(wave, src.aoff);
+    token_rows(wave, src.aoff, 0);
     // (written in every mode: fields left unwritten made the copy of the
     // sources at a tile boundary go through scratch memory, and its wait
     // drained the prefetched slices)
     src.paoff[0] = src.paoff[1] = src.pboff[0] = src.pboff[1] = 0u;
-    if constexpr (pairs_issue(MODE)) token_rows((wave & 3) + 4, src.paoff);
+    if constexpr (pairs_issue(MODE)) token_rows((wave & 3) + 4, src.paoff, 2);
     src.cs = 0.0f;
     src.cc = 0.0f;
     if (fp8) {
@@ -630,8 +660,23 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
     int Cn = __builtin_amdgcn_readfirstlane(lds_next[0]);
 
     TileInfo cur = decode_tile<MODE>(a, tile_of(C), nsh);
+    // the next tile's descriptor: a scalar load, issued a tile ahead (for
+    // later tiles during the previous epilogue), so that its latency -- the
+    // descriptors were written by another kernel, often on another XCD --
+    // is not exposed by the wait at the top of the tile
+    TileInfo pre = cur;
+    if (Cn < nclaim) pre = decode_tile<MODE>(a, tile_of(Cn), nsh);
+    // Rows gathered from x: the tokens of this tile's rows and of the next
+    // one's. Later tiles' tokens are loaded at the end of the epilogue two
+    // tiles ahead, so the drain there covers them and no wait on them falls
+    // inside the K loop or at the top of a tile.
+    const bool gather = can_gather<MODE>() && a.a_gather != nullptr;
+    int tok[4] = {0, 0, 0, 0}, ptok[4] = {0, 0, 0, 0};
+    if (gather && !cur.shared) gather_tokens<MODE>(a, cur, wave, lane, tok);
+    if (gather && Cn < nclaim && !pre.shared) gather_tokens<MODE>(a, pre, wave, lane, ptok);
     TileSrc src;
-    tile_sources<MODE>(a, cur, wave, lane, op_ar, op_as, by_ar, by_as, src);
+    tile_sources<MODE>(a, cur, wave, lane, op_ar, op_as, by_ar, by_as, gather, tok, src);
+    if (gather) wait_vmcnt<0>();
     TileInfo nxt = cur;
     TileSrc nsrc = src;
     // the claim on the tile after next; later ones are issued at the end of
@@ -779,12 +824,6 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
     }
 
     bf16x8 fa0[MB], fb0[NB], fa1[MB], fb1[NB];
-    // the next tile's descriptor: a scalar load, issued a tile ahead (for
-    // later tiles during the previous epilogue), so that its latency -- the
-    // descriptors were written by another kernel, often on another XCD --
-    // is not exposed by the wait at the top of the tile
-    TileInfo pre = cur;
-    if (Cn < nclaim) pre = decode_tile<MODE>(a, tile_of(Cn), nsh);
     while (true) {
         const bool has_next = Cn < nclaim;
         // the claim on the tile after the next one is already in `claim` and
@@ -797,7 +836,7 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
         wait_vmcnt<2 * kReqs>();  // slice 0 of this tile has landed
         ring_barrier();
         if (has_next) {
-            tile_sources<MODE>(a, nxt, wave, lane, op_ar, op_as, by_ar, by_as, nsrc);
+            tile_sources<MODE>(a, nxt, wave, lane, op_ar, op_as, by_ar, by_as, gather, ptok, nsrc);
         } else {
             nxt = cur;
             nsrc = src;
@@ -1143,6 +1182,8 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
                 }
             }
         }
+        // the tokens of the tile after next (used at the top of the next tile)
+        if (gather && has_next && Cn2 < nclaim && !pre.shared) gather_tokens<MODE>(a, pre, wave, lane, ptok);
         // the next tile's claim on the one after it
         if (has_next && Cn2 < nclaim && tid == 0) claim = atomicAdd(counter, 1);
         // the epilogue's stores also count in vmcnt: drain before the next
@@ -1368,6 +1409,10 @@ bool use_big_tiles(const moe_shape& s) {
 }
 }  // namespace
 
+bool ffn_gathers_rows(const moe_shape& s) {
+    return use_big_tiles(s) && s.act == MOE_BF16 && s.dispatch == MOE_BF16;
+}
+
 bool ffn_fused_plan(const moe_shape& s, int32_t* plan, FfnPlanArgs* fp) {
     fp->plan = nullptr;
     if (!use_big_tiles(s)) return false;
@@ -1388,8 +1433,9 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const floa
                               const int32_t* offsets, const void* x, const void* w1,
                               const void* w3, const void* w2, void* y_perm, void* y_shared,
                               int32_t* plan, void* h_routed, void* h_shared, bool plan_done,
-                              hipStream_t st, const Marks* mk) {
+                              hipStream_t st, const Marks* mk, const int32_t* gather) {
     const bool f32 = s.act == MOE_F32;
+    if (gather != nullptr && !ffn_gathers_rows(s)) return hipErrorInvalidValue;
     const bool big = use_big_tiles(s);
     const int bm = f32 ? kF32BM : (big ? kBigBM : kBM);
     const PlanLayout pl = plan_layout(s);
@@ -1422,9 +1468,11 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const floa
 
     // up-projection + SwiGLU
     a.a_routed = static_cast<const uint8_t*>(x_perm);
+    a.a_gather = gather;
     a.a_shared = static_cast<const uint8_t*>(x);
     a.a_routed_bytes = static_cast<uint32_t>(Tk * s.d * esd);
-    a.a_shared_bytes = static_cast<uint32_t>(s.S > 0 ? static_cast<uint64_t>(s.T) * s.d * 2 : 0);
+    a.a_shared_bytes =
+        static_cast<uint32_t>(s.S > 0 || gather != nullptr ? static_cast<uint64_t>(s.T) * s.d * 2 : 0);
     a.w_bytes = static_cast<uint32_t>((s.E + s.S) * wgroup);
     a.wa = static_cast<const uint8_t*>(w1);
     a.wb = static_cast<const uint8_t*>(w3);
@@ -1446,6 +1494,7 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const floa
     if (err != hipSuccess) return err;
 
     // down-projection
+    a.a_gather = nullptr;
     a.a_routed = static_cast<const uint8_t*>(h_routed);
     a.a_shared = static_cast<const uint8_t*>(h_shared);
     a.a_routed_bytes = static_cast<uint32_t>(Tk * a.hs * 2);

@@ -25,7 +25,10 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const floa
                               const int32_t* offsets, const void* x, const void* w1,
                               const void* w3, const void* w2, void* y_perm, void* y_shared,
                               int32_t* plan, void* h_routed, void* h_shared, bool plan_done,
-                              hipStream_t st, const Marks* mk);
+                              hipStream_t st, const Marks* mk, const int32_t* gather = nullptr);
+// whether the whole-layer forward's up-projection reads its routed rows from
+// x through src_token (bf16 rows, persistent tiles) instead of from x_perm
+bool ffn_gathers_rows(const moe_shape& s);
 size_t ffn_plan_bytes(const moe_shape& s);
 int ffn_hidden_stride(const moe_shape& s);
 bool ffn_fused_plan(const moe_shape& s, int32_t* plan, FfnPlanArgs* fp);
@@ -130,7 +133,9 @@ Layout layout(const moe_shape& s, int stage) {
         L.h_s = take(T * S * hs * es);
     }
     if (fwd) {
-        L.x_perm = take(T * k * d * esd);
+        // (no permuted rows when the up-projection gathers them from x)
+        const bool gather = stage == MOE_STAGE_FORWARD && ffn_gathers_rows(s);
+        L.x_perm = take(gather ? 0 : T * k * d * esd);
         L.qparams = take(s.dispatch == MOE_FP8_E4M3 ? T * k * 8 : 0);
         L.y_perm = take(T * k * d * es);
         L.y_sh = take(S > 0 ? T * d * es : 0);
@@ -238,7 +243,11 @@ int32_t forward_impl(const moe_shape* s, const void* x, const void* w_gate, cons
     MOE_TRY(hip_status(launch_gate_topk(*s, x, w_gate, bias, topk_idx, topk_w, nullptr, st, mk)));
     mark(mk);
     const bool fp8 = s->dispatch == MOE_FP8_E4M3;
-    void* x_perm = at<void>(ws, L.x_perm);
+    // With bf16 rows on the persistent tiles the permutation is applied where
+    // the rows are consumed: dispatch writes only dest_row and src_token, and
+    // the up-projection fetches routed row r from x[src_token[r]].
+    const bool gather = ffn_gathers_rows(*s);
+    void* x_perm = gather ? nullptr : at<void>(ws, L.x_perm);
     float* qp = fp8 ? at<float>(ws, L.qparams) : nullptr;
     // the FFN's tile plan is written by the dispatch permute's first work-groups
     FfnPlanArgs fplan;
@@ -252,7 +261,8 @@ int32_t forward_impl(const moe_shape* s, const void* x, const void* w_gate, cons
     void* y_sh = s->S > 0 ? at<void>(ws, L.y_sh) : nullptr;
     MOE_TRY(hip_status(launch_grouped_ffn(*s, x_perm, qp, offsets, x, w1, w3, w2, y_perm, y_sh,
                                           at<int32_t>(ws, L.plan), at<void>(ws, L.h_r),
-                                          at<void>(ws, L.h_s), plan_done, st, mk)));
+                                          at<void>(ws, L.h_s), plan_done, st, mk,
+                                          gather ? src_token : nullptr)));
     MOE_TRY(hip_status(launch_combine(*s, y_perm, y_sh, dest_row, topk_w, y, st)));
     mark(mk);
     return MOE_OK;
@@ -565,6 +575,7 @@ const char* moe_forward_kernel_name(const moe_shape* s, int32_t i) {
     if (i < 0 || i >= moe_forward_kernel_count(s)) return nullptr;
     if (i == 0 && s != nullptr && s->T > 0 && gate_two_phase_chosen(*s)) return "gate_two_phase";
     if (i == 3 && s != nullptr && s->dispatch == MOE_FP8_E4M3) return "dispatch_permute_fp8";
+    if (i == 3 && s != nullptr && s->T > 0 && ffn_gathers_rows(*s)) return "dispatch_map";
     return kKernelNames[i];
 }
 

@@ -42,9 +42,20 @@ def test_status_strings(mm):
 def test_workspace_sizes(mm):
     s = mm.make_shape(4096, 2048, 32, 8, 2, 1408, "bf16")
     fwd = mm.moe_workspace_bytes(s, mm.STAGE_FORWARD)
-    # x_perm + y_perm + H (routed and shared) + y_sh at least
-    need = 4096 * 8 * 2048 * 2 * 2 + 4096 * (8 + 2) * 1408 * 2 + 4096 * 2048 * 2
+    # y_perm + H (routed and shared) + y_sh at least: with bf16 rows on the
+    # 256 x 256 tiles the up-projection gathers its rows from x, so the whole
+    # layer's forward holds no x_perm
+    need = 4096 * 8 * 2048 * 2 + 4096 * (8 + 2) * 1408 * 2 + 4096 * 2048 * 2
     assert need < fwd < need + (1 << 20)
+    # fp8 rows are written out by dispatch: x_perm (1 byte a value) and its
+    # (scale, centre) pairs as well
+    s8 = mm.make_shape(4096, 2048, 32, 8, 2, 1408, "bf16", dispatch="fp8")
+    need8 = need + 4096 * 8 * 2048 + 4096 * 8 * 8
+    assert need8 < mm.moe_workspace_bytes(s8, mm.STAGE_FORWARD) < need8 + (1 << 20)
+    # shapes off the 256 x 256 tiles (h % 128 != 0) keep x_perm
+    so = mm.make_shape(4096, 2048, 32, 8, 2, 1400, "bf16")
+    needo = 4096 * 8 * 2048 * 2 * 2 + 4096 * (8 + 2) * 1400 * 2 + 4096 * 2048 * 2
+    assert needo < mm.moe_workspace_bytes(so, mm.STAGE_FORWARD) < needo + (1 << 20)
     assert mm.moe_workspace_bytes(s, mm.STAGE_GATE) == 0
     assert mm.moe_workspace_bytes(s, mm.STAGE_COMBINE) == 0
     # one float32 [E, d] partial per token range, at least one range
