@@ -335,7 +335,10 @@ int32_t moe_grouped_ffn_backward(const moe_shape *s, const void *x_perm, const f
  * The whole layer: moe_gate_topk -> moe_dispatch -> moe_grouped_ffn ->
  * moe_combine with intermediates in the workspace (MOE_STAGE_FORWARD bytes).
  * y [T,d] (act) is the layer output; topk_idx, topk_w, counts, offsets,
- * dest_row and src_token are written as by the stage calls.
+ * dest_row and src_token are written as by the stage calls. With bf16 rows
+ * on the 256 x 256 tiles (d % 256 == 0, h % 128 == 0) the permuted rows are
+ * not written: the up-projection reads routed row r from x[src_token[r]]
+ * (same results), and the workspace holds no x_perm.
  */
 int32_t moe_forward(const moe_shape *s, const void *x, const void *w_gate,
                     const float *bias, const void *w1, const void *w3, const void *w2,
