@@ -26,7 +26,7 @@ from moe_workloads import CONFIG_ORDER, CONFIGS, make_inputs, make_rows
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
 
-STAGES = ["gate", "dispatch", "ffn", "combine", "forward", "determinism"]
+STAGES = ["gate", "dispatch", "ffn", "combine", "forward", "determinism", "chain"]
 
 _CACHE: dict = {}
 
@@ -211,8 +211,45 @@ def run_determinism(c):
     assert np.array_equal(host(b.topk_w).view(np.uint32), host(a.topk_w).view(np.uint32))
 
 
+def run_chain(c):
+    """moe_forward against the stage calls chained on its routing: dispatch
+    with the permuted rows written out, the grouped FFN on them, combine.
+    Where the forward's up-projection gathers its rows from x instead, every
+    row still meets the same operand values in the same order, so y must be
+    the same bits (all tokens)."""
+    mm, cfg = _mm(), c["cfg"]
+    T, k, d, E = cfg.T, cfg.k, cfg.d, cfg.E
+    shape = c["shape"]
+    buf = run_forward(c, check_y=False)
+    gathered = mm.moe_forward_kernel_name(shape, 3) == "dispatch_map"
+    say(f"[case {cfg.name}] forward {'gathers its rows' if gathered else 'reads x_perm'}; stage chain")
+    fp8 = cfg.dispatch == "fp8"
+    x_perm = torch.empty((T * k, d), dtype=torch.uint8 if fp8 else act_torch(cfg.act), device="cuda")
+    qp = torch.empty((T * k, 2), dtype=torch.float32, device="cuda") if fp8 else None
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    dest = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    src = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    mm.moe_dispatch(shape, c["x"], buf.topk_idx, counts, offsets, dest, src, x_perm, qp,
+                    mm.alloc_workspace(shape, mm.STAGE_DISPATCH))
+    y_perm = torch.empty((T * k, d), dtype=act_torch(cfg.act), device="cuda")
+    y_sh = torch.empty((T, d), dtype=act_torch(cfg.act), device="cuda") if cfg.S else None
+    mm.moe_grouped_ffn(shape, x_perm, qp, offsets, c["x"] if cfg.S else None, c["w1"], c["w3"],
+                       c["w2"], y_perm, y_sh, mm.alloc_workspace(shape, mm.STAGE_FFN))
+    y = torch.empty((T, d), dtype=act_torch(cfg.act), device="cuda")
+    mm.moe_combine(shape, y_perm, y_sh, dest, buf.topk_w, y)
+    torch.cuda.synchronize()
+    assert torch.equal(dest, buf.dest_row) and torch.equal(offsets, buf.offsets)
+    n = int(offsets[-1].item())  # rows kept (a capacity limit may drop some)
+    assert torch.equal(src[:n], buf.src_token[:n])
+    bits = torch.int32 if cfg.act == "f32" else torch.int16
+    differ = int((y.view(bits) != buf.y.view(bits)).any(dim=1).sum().item())
+    say(f"[case {cfg.name}] tokens whose y differs from the stage chain: {differ} of {T}")
+    assert differ == 0
+
+
 RUN = dict(gate=run_gate, dispatch=run_dispatch, ffn=run_ffn, combine=run_combine,
-           forward=run_forward, determinism=run_determinism)
+           forward=run_forward, determinism=run_determinism, chain=run_chain)
 
 
 @pytest.mark.parametrize("name,stage", [(n, s) for n in CONFIG_ORDER for s in STAGES])
