@@ -445,6 +445,12 @@ __device__ __forceinline__ void convert_codes(uint8_t* slot, int wave, int lane,
     *reinterpret_cast<bf16x8*>(slot + lds_off32(r, ch + 1)) = __builtin_bit_cast(bf16x8, hi);
 }
 
+// a 16-byte store to global memory (the operands of the kernels are global:
+// a generic pointer would make it a flat store, which also counts in lgkmcnt)
+__device__ __forceinline__ void store16g(void* p, u32x4 v) {
+    *(__attribute__((address_space(1))) u32x4*)(p) = v;
+}
+
 // (The flags are ints: a struct with bool members was copied through
 // scratch memory at every tile, and the wait for that scratch load drained
 // the prefetched slices.)
@@ -996,7 +1002,7 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
             for (int p = 0; p < 2; ++p) {
                 const auto s0 = __builtin_amdgcn_permlane32_swap(w[2 * p][0], w[2 * p + 1][0], false, false);
                 const auto s1 = __builtin_amdgcn_permlane32_swap(w[2 * p][1], w[2 * p + 1][1], false, false);
-                if (ok) store16(rowp + 16 * p + 8 * lg, u32x4{s0[0], s1[0], s0[1], s1[1]});
+                if (ok) store16g(rowp + 16 * p + 8 * lg, u32x4{s0[0], s1[0], s0[1], s1[1]});
             }
         };
         // fp8-weight modes: the weight rows' scales of this lane's 16 output
@@ -1036,6 +1042,18 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
         // the weight scales as well and has no registers to spare.)
         constexpr bool kStage = MODE == kModeDown;
         uint8_t* stage = nullptr;
+        // staged stores go through a buffer resource over the group's rows,
+        // so rows past the group fall outside it and are dropped by the
+        // range check (no branch per store); lane L stores 16 bytes of row
+        // L / 8 of each 8-row group, chunk L % 8 of the wave's 128 bytes
+        const uint32_t orow = static_cast<uint32_t>(a.d) * 2;
+        // (wave-uniform by construction; said so, or the compiler loops over
+        // lanes around every store)
+        const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t*>(uniform_ptr(reinterpret_cast<const uint8_t*>(out + static_cast<int64_t>(cur.row_base) * a.d))), 0,
+            static_cast<int>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(cur.nrows) * orow)), kBufferFlags);
+        const uint32_t obase = static_cast<uint32_t>(cur.m0 + wm * kBigWM + (lane >> 3)) * orow +
+                               static_cast<uint32_t>(cur.nt * kBigBN + wn * kBigWN + (lane & 7) * 8) * 2;
         if constexpr (kStage) {
             ring_barrier();
             stage = lds + 3 * kBigSlot + wave * 4096;
@@ -1090,15 +1108,17 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
                 }
                 // four stores of 8 rows x 128 bytes: lane L takes row 8 i + L/8,
                 // chunk L % 8
+                if constexpr (kStage) {
+                    u32x4 v[4];
 #pragma unroll
-                for (int i = 0; i < 4 && kStage; ++i) {
-                    const int rr = 8 * i + (lane >> 3), cc = lane & 7;
-                    const u32x4 v = *reinterpret_cast<const u32x4*>(stage + rr * 128 + ((cc ^ ((rr >> 1) & 7)) << 4));
-                    const int r2 = cur.m0 + wm * kBigWM + mb * 32 + rr;
-                    if (r2 < cur.nrows)
-                        store16(out + (static_cast<int64_t>(cur.row_base) + r2) * a.d + cur.nt * kBigBN + wn * kBigWN +
-                                    cc * 8,
-                                v);
+                    for (int i = 0; i < 4; ++i) {
+                        const int rr = 8 * i + (lane >> 3), cc = lane & 7;
+                        v[i] = *reinterpret_cast<const u32x4*>(stage + rr * 128 + ((cc ^ ((rr >> 1) & 7)) << 4));
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            v[i], orsrc, obase + static_cast<uint32_t>(mb * 32 + 8 * i) * orow, 0, 0);
                 }
             } else if constexpr (MODE == kModeDh) {
                 // dhid -> da = dhid b s (1 + a (1 - s)), db = dhid silu(a)
