@@ -1045,7 +1045,9 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
         // staged stores go through a buffer resource over the group's rows,
         // so rows past the group fall outside it and are dropped by the
         // range check (no branch per store); lane L stores 16 bytes of row
-        // L / 8 of each 8-row group, chunk L % 8 of the wave's 128 bytes
+        // L / 8 of each 8-row group, chunk L % 8 of the wave's 128 bytes.
+        // The rows are written once and read once, by combine: the stores
+        // are non-temporal (aux 2), so they do not evict operand panels.
         const uint32_t orow = static_cast<uint32_t>(a.d) * 2;
         // (wave-uniform by construction; said so, or the compiler loops over
         // lanes around every store)
@@ -1118,7 +1120,7 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         __builtin_amdgcn_raw_buffer_store_b128(
-                            v[i], orsrc, obase + static_cast<uint32_t>(mb * 32 + 8 * i) * orow, 0, 0);
+                            v[i], orsrc, obase + static_cast<uint32_t>(mb * 32 + 8 * i) * orow, 0, 2);
                 }
             } else if constexpr (MODE == kModeDh) {
                 // dhid -> da = dhid b s (1 + a (1 - s)), db = dhid silu(a)
