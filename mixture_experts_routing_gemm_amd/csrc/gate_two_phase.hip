@@ -177,7 +177,7 @@ __global__ __launch_bounds__(TpRing<EB>::kThreads, 1) void gate_two_phase_kernel
     }
     const int KT = (d + kTpK - 1) / kTpK;
     // slice kt of a walk that starts at slice rot (and wraps) goes to slot kt % kSlots
-    auto issue = [&](int kt, int rot) {
+    auto issue = [&](int kt, int rot, auto AX) {
         uint8_t* S = lds + (kt % RG::kSlots) * RG::kSlot;
         const int kr = kt + rot < KT ? kt + rot : kt + rot - KT;
         const int k0 = kr * kTpK;
@@ -187,7 +187,7 @@ __global__ __launch_bounds__(TpRing<EB>::kThreads, 1) void gate_two_phase_kernel
             const int j = wave + RG::kWaves * i;
             const uint32_t v = k0 + kch[i] < d ? voff[i] : 0x80000000u;
             if (i < 2)
-                buffer_to_lds16<0>(xbuf, xbytes, v, soff, S + j * 1024);
+                buffer_to_lds16<0, decltype(AX)::value>(xbuf, xbytes, v, soff, S + j * 1024);
             else
                 buffer_to_lds16<0>(wbuf, wbytes, v, soff, S + RG::kXBytes + (j - 2 * RG::kWaves) * 1024);
         }
@@ -198,13 +198,13 @@ __global__ __launch_bounds__(TpRing<EB>::kThreads, 1) void gate_two_phase_kernel
     // read one step earlier, which every wave has finished by then. Ends
     // with nothing in flight; the caller synchronises before the ring's
     // bytes are used otherwise.
-    auto stream = [&](int rot, auto body) {
-        for (int s = 0; s < RG::kSlots - 1 && s < KT; ++s) issue(s, rot);
+    auto stream = [&](int rot, auto body, auto AX) {
+        for (int s = 0; s < RG::kSlots - 1 && s < KT; ++s) issue(s, rot, AX);
         for (int kt = 0; kt < KT; ++kt) {
             const int ahead = min(RG::kSlots - 2, KT - 1 - kt);
             tp_wait_slots<RG::kReq, RG::kSlots - 2>(ahead);
             ring_barrier();
-            if (kt + RG::kSlots - 1 < KT) issue(kt + RG::kSlots - 1, rot);
+            if (kt + RG::kSlots - 1 < KT) issue(kt + RG::kSlots - 1, rot, AX);
             body(lds + (kt % RG::kSlots) * RG::kSlot);
         }
     };
@@ -266,7 +266,9 @@ __global__ __launch_bounds__(TpRing<EB>::kThreads, 1) void gate_two_phase_kernel
                     sw[q] += sumsq(*reinterpret_cast<const u32x4*>(W + tp_off(eb * 32 + lr, ks * 2 + lg)));
             }
         }
-    });
+    }, std::integral_constant<int, 2>{});  // x requests non-temporal (aux 2): with x about the
+                                             // Infinity Cache's size, the chains' pass then hits it
+                                             // more often (-8 % on 32768 x 4096 tokens)
     // norms: lanes lr and lr + 32 hold the two halves of a row's sum
     {
         const float v = sx + __shfl_xor(sx, 32, kWave);
@@ -451,7 +453,7 @@ __global__ __launch_bounds__(TpRing<EB>::kThreads, 1) void gate_two_phase_kernel
                     default: run_chains<8>(X, W, pc, z); break;
                 }
             }
-        });
+        }, std::integral_constant<int, 0>{});
         __syncthreads();  // every wave is done with the last slice before the lists' bytes are rewritten
         // the exact logits of the listed pairs, in the wave's own part
 #pragma unroll

@@ -41,14 +41,14 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
 // [base, base + bytes): lane i reads base + voff_i + soff (zero when past the
 // end) and writes it to LDS at lds + OFF + 16*i. (The instruction's immediate
 // offset would move the source address as well, so the LDS offset goes into
-// the LDS base instead.)
-template <int OFF>
+// the LDS base instead.) AUX is the cache policy: 0, or 2 for non-temporal.
+template <int OFF, int AUX = 0>
 __device__ __forceinline__ void buffer_to_lds16(const uint8_t* base, uint32_t bytes, uint32_t voff,
                                                 uint32_t soff, uint8_t* lds) {
     const __amdgpu_buffer_rsrc_t r =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, static_cast<int>(bytes), kBufferFlags);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds + OFF), 16, voff,
-                                             soff, 0, 0);
+                                             soff, 0, AUX);
 }
 
 }  // namespace moe
