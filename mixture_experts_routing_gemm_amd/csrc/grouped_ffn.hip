@@ -610,7 +610,8 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
     constexpr bool kFp8 = is_fp8rows(MODE);
     constexpr bool kF8W = is_f8w(MODE);
     constexpr bool kDown = is_down(MODE);
-    // The bf16 up-projection takes its tiles round-robin within the XCD
+    // The up-projections (bf16 or fp8 rows, also the backward's recompute)
+    // and dh take their tiles round-robin within the XCD
     // (claim c goes to work-group c mod per_xcd) instead of from the XCD's
     // counter: the n-tiles that share a token panel then start together on
     // neighbouring work-groups and, with equal work, stay in step, so the
@@ -618,7 +619,7 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
     // L2 misses fell 12 % (the time about 0.5 %): with dynamic claims the
     // siblings drifted about a tile's tenth apart, more than the few steps
     // of traffic that L2 holds.
-    constexpr bool kStaticClaims = MODE == kModeUp;
+    constexpr bool kStaticClaims = MODE == kModeUp || MODE == kModeUpFp8 || MODE == kModeUpSave || MODE == kModeUpFp8Save || MODE == kModeDh;
     constexpr int KS = kF8W ? 2 * kBigBK : kBigBK;  // operand values per slice
     constexpr uint32_t EB = kF8W ? 1 : 2;          // bytes per operand value
     const int tid = threadIdx.x;
