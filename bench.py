@@ -348,6 +348,32 @@ def ffn_backward_leg(mm, torch, cfg, shape, buf, stream, x, w1, w3, w2, reps=5):
            "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / peak, 4),
            "mfma_frac_incl_recompute": round(16 * rows * d * h / (ms * 1e-3) / 1e12 / peak, 4)}
+    if mm.moe_ffn_saved_bytes(shape) > 0:
+        # the same backward from activations saved by moe_grouped_ffn_save
+        # (no recomputation); the saving forward is not timed here
+        saved = mm.alloc_saved(shape)
+        y_perm = torch.empty((R, d), dtype=torch.bfloat16, device="cuda")
+        y_sh = torch.empty((T, d), dtype=torch.bfloat16, device="cuda") if S else None
+        mm.moe_grouped_ffn_save(shape, x_perm, qp, offsets, x if S else None, w1, w3, w2, y_perm, y_sh,
+                                saved, mm.alloc_workspace(shape, mm.STAGE_FFN), stream)
+
+        def call_saved():
+            mm.moe_grouped_ffn_backward_saved(shape, x_perm, qp, offsets, x if S else None, w1, w3, w2,
+                                              saved, dy_perm, dy_sh, dx_perm, dx_sh, dw1, dw3, dw2, ws,
+                                              stream)
+        call_saved()
+        torch.cuda.synchronize()
+        for a_, b_ in ev:
+            a_.record(stream)
+            call_saved()
+            b_.record(stream)
+        torch.cuda.synchronize()
+        ms2 = float(np.median([a_.elapsed_time(b_) for a_, b_ in ev]))
+        res["saved_activations"] = {"us": round(ms2 * 1e3, 2),
+                                    "tflops": round(flops / (ms2 * 1e-3) / 1e12, 1),
+                                    "mfma_frac": round(flops / (ms2 * 1e-3) / 1e12 / peak, 4),
+                                    "saved_bytes": mm.moe_ffn_saved_bytes(shape)}
+        del saved, y_perm, y_sh
     del x_perm, qp, dy_perm, dy_sh, dx_perm, dx_sh, dw1, dw3, dw2, ws, ws_d
     torch.cuda.empty_cache()
     return res

@@ -332,6 +332,40 @@ int32_t moe_grouped_ffn_backward(const moe_shape *s, const void *x_perm, const f
                                  void *stream);
 
 /*
+ * Saving the expert activations for the backward instead of recomputing
+ * them (the same quantities as moe_grouped_ffn_backward's recomputation,
+ * [gsyq] 2.4; a training caller trades T*(k+S)*3*h*2 bytes of memory for
+ * the backward's recomputed up-projection).
+ *
+ * moe_ffn_saved_bytes: bytes of the buffer that holds them -- a, b and hid,
+ *  bf16, for the routed rows [T*k, h] and then the shared experts' token rows
+ *  [T, S*h], each section 256-byte aligned -- or 0 when the shape is not
+ *  supported: act must be MOE_BF16 and the shape on the persistent tiles
+ *  (d % 256 == 0, h % 128 == 0).
+ * moe_grouped_ffn_save: moe_grouped_ffn (same arguments, same results, bit
+ *  for bit) that also writes a, b and hid of every row into `saved`
+ *  (caller-owned, 256-byte aligned, saved_bytes >= moe_ffn_saved_bytes).
+ *  MOE_ERR_UNSUPPORTED for shapes moe_ffn_saved_bytes rejects;
+ *  MOE_ERR_INVALID_ARG for a missing, misaligned or short `saved`.
+ * moe_grouped_ffn_backward_saved: moe_grouped_ffn_backward (same arguments
+ *  and results) that reads a, b and hid from `saved`, as written by
+ *  moe_grouped_ffn_save on the same rows and weights, instead of recomputing
+ *  them; the results are the same bits. Same errors as the two above.
+ */
+size_t moe_ffn_saved_bytes(const moe_shape *s);
+int32_t moe_grouped_ffn_save(const moe_shape *s, const void *x_perm, const float *qparams,
+                             const int32_t *offsets, const void *x, const void *w1, const void *w3,
+                             const void *w2, void *y_perm, void *y_shared, void *saved,
+                             size_t saved_bytes, void *ws, size_t ws_bytes, void *stream);
+int32_t moe_grouped_ffn_backward_saved(const moe_shape *s, const void *x_perm,
+                                       const float *qparams, const int32_t *offsets,
+                                       const void *x, const void *w1, const void *w3,
+                                       const void *w2, const void *saved, size_t saved_bytes,
+                                       const void *dy_perm, const void *dy_shared, void *dx_perm,
+                                       void *dx_shared, float *dw1, float *dw3, float *dw2,
+                                       void *ws, size_t ws_bytes, void *stream);
+
+/*
  * The whole layer: moe_gate_topk -> moe_dispatch -> moe_grouped_ffn ->
  * moe_combine with intermediates in the workspace (MOE_STAGE_FORWARD bytes).
  * y [T,d] (act) is the layer output; topk_idx, topk_w, counts, offsets,

@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     moe_forward, moe_forward_fp8w, moe_forward_kernel_count, moe_fp8_weight_scale_floats,
     moe_quantize_weights, moe_forward_kernel_name, moe_forward_traced,
     moe_gate_topk, moe_get_device_error, moe_grouped_ffn, moe_grouped_ffn_backward, moe_shape,
+    moe_ffn_saved_bytes, alloc_saved, moe_grouped_ffn_save, moe_grouped_ffn_backward_saved,
     moe_workspace_bytes,
     moe_workspace_init, shape_of, status_string)
 from .buffers import ForwardBuffers  # noqa: F401

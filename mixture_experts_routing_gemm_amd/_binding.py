@@ -112,6 +112,13 @@ def _load():
     L.moe_grouped_ffn_backward.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                            vp, vp, sz, vp]
     L.moe_grouped_ffn_backward.restype = i32
+    L.moe_ffn_saved_bytes.argtypes = [sp]
+    L.moe_ffn_saved_bytes.restype = sz
+    L.moe_grouped_ffn_save.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp]
+    L.moe_grouped_ffn_save.restype = i32
+    L.moe_grouped_ffn_backward_saved.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp,
+                                                 vp, vp, vp, vp, sz, vp]
+    L.moe_grouped_ffn_backward_saved.restype = i32
     L.moe_gate_backward.restype = i32
     L.moe_forward.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_forward.restype = i32
@@ -140,7 +147,8 @@ EXPORTS = ["moe_workspace_bytes", "moe_workspace_init", "moe_status_string", "mo
            "moe_dispatch", "moe_dispatch_noalloc", "moe_grouped_ffn", "moe_combine", "moe_combine_backward",
            "moe_dispatch_backward", "moe_gate_backward", "moe_grouped_ffn_backward", "moe_forward", "moe_forward_traced",
            "moe_forward_kernel_count", "moe_forward_kernel_name", "moe_get_device_error",
-           "moe_fp8_weight_scale_floats", "moe_quantize_weights", "moe_forward_fp8w"]
+           "moe_fp8_weight_scale_floats", "moe_quantize_weights", "moe_forward_fp8w",
+           "moe_ffn_saved_bytes", "moe_grouped_ffn_save", "moe_grouped_ffn_backward_saved"]
 
 
 def status_string(status: int) -> str:
@@ -250,6 +258,38 @@ def moe_grouped_ffn_backward(shape, x_perm, qparams, offsets, x, w1, w3, w2, dy_
                                         _p(x), _p(w1), _p(w3), _p(w2), _p(dy_perm), _p(dy_shared),
                                         _p(dx_perm), _p(dx_shared), _p(dw1), _p(dw3), _p(dw2), wp,
                                         wn, _s(stream)), "moe_grouped_ffn_backward")
+
+
+def moe_ffn_saved_bytes(shape):
+    return int(lib.moe_ffn_saved_bytes(ctypes.byref(shape)))
+
+
+def alloc_saved(shape, device="cuda"):
+    """The caller buffer of activations saved for the backward (uint8)."""
+    n = moe_ffn_saved_bytes(shape)
+    if n == 0:
+        raise MoEError(-2, "moe_ffn_saved_bytes: shape not supported")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def moe_grouped_ffn_save(shape, x_perm, qparams, offsets, x, w1, w3, w2, y_perm, y_shared, saved,
+                         ws, stream=None):
+    wp, wn = _ws(ws)
+    sp_, sn = _ws(saved)
+    _check(lib.moe_grouped_ffn_save(ctypes.byref(shape), _p(x_perm), _p(qparams), _p(offsets), _p(x),
+                                    _p(w1), _p(w3), _p(w2), _p(y_perm), _p(y_shared), sp_, sn, wp, wn,
+                                    _s(stream)), "moe_grouped_ffn_save")
+
+
+def moe_grouped_ffn_backward_saved(shape, x_perm, qparams, offsets, x, w1, w3, w2, saved, dy_perm,
+                                   dy_shared, dx_perm, dx_shared, dw1, dw3, dw2, ws, stream=None):
+    wp, wn = _ws(ws)
+    sp_, sn = _ws(saved)
+    _check(lib.moe_grouped_ffn_backward_saved(ctypes.byref(shape), _p(x_perm), _p(qparams), _p(offsets),
+                                              _p(x), _p(w1), _p(w3), _p(w2), sp_, sn, _p(dy_perm),
+                                              _p(dy_shared), _p(dx_perm), _p(dx_shared), _p(dw1),
+                                              _p(dw3), _p(dw2), wp, wn, _s(stream)),
+           "moe_grouped_ffn_backward_saved")
 
 
 def moe_dispatch_backward(shape, dx_perm, dx_shared, dest_row, dx, stream=None):

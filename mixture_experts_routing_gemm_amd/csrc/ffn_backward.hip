@@ -510,7 +510,7 @@ hipError_t launch_ffn_bwd_gemms(const moe_shape& s, const void* x_perm, const fl
                                 const void* dy_perm, const void* dy_sh, void* dx_perm, void* dx_sh,
                                 int32_t* plan_f, int32_t* plan_dh, void* h_r, void* h_s, void* a_r,
                                 void* b_r, void* a_s, void* b_s, void* dd_r, void* dd_s,
-                                hipStream_t st, const Marks* mk);
+                                hipStream_t st, const Marks* mk, bool recompute);
 bool wgrad_supported(const moe_shape& s);
 size_t wgrad_ws_bytes(const moe_shape& s);
 hipError_t launch_ffn_wgrad(const moe_shape& s, const int32_t* offsets, const void* dd_r,
@@ -580,14 +580,46 @@ BwdLayout bwd_layout(const moe_shape& s) {
 
 size_t ffn_backward_ws_bytes(const moe_shape& s) { return bwd_layout(s).bytes; }
 
+// The activations a forward may save for the backward: a = W1 v, b = W3 v
+// and hid = silu(a) b, bf16, routed rows [T*k, hs] then the shared experts'
+// token rows [T, S*hs] (hs = h rounded up to 8), 256-byte aligned sections.
+SavedLayout saved_layout(const moe_shape& s) {
+    SavedLayout L;
+    const size_t hs = static_cast<size_t>(ffn_hidden_stride(s));
+    const size_t R = static_cast<size_t>(s.T) * s.k, TS = static_cast<size_t>(s.T) * s.S;
+    size_t off = 0;
+    auto take = [&](size_t n) {
+        const size_t at = off;
+        off = (off + n + 255) & ~static_cast<size_t>(255);
+        return at;
+    };
+    L.a_r = take(R * hs * 2);
+    L.b_r = take(R * hs * 2);
+    L.h_r = take(R * hs * 2);
+    L.a_s = take(TS * hs * 2);
+    L.b_s = take(TS * hs * 2);
+    L.h_s = take(TS * hs * 2);
+    L.bytes = off;
+    return L;
+}
+
 hipError_t launch_ffn_backward(const moe_shape& s, const void* x_perm, const float* qparams,
                                const int32_t* offsets, const void* x, const void* w1,
                                const void* w3, const void* w2, const void* dy_perm,
                                const void* dy_sh, void* dx_perm, void* dx_sh, float* dw1,
                                float* dw3, float* dw2, void* ws, hipStream_t st,
-                               const Marks* mk) {
+                               const Marks* mk, const void* saved) {
     const BwdLayout L = bwd_layout(s);
     uint8_t* w = static_cast<uint8_t*>(ws);
+    // a, b and hid: saved by the forward, or recomputed into the workspace
+    const SavedLayout SL = saved_layout(s);
+    uint8_t* sv = static_cast<uint8_t*>(const_cast<void*>(saved));
+    uint8_t* const p_a_r = sv != nullptr ? sv + SL.a_r : w + L.a_r;
+    uint8_t* const p_b_r = sv != nullptr ? sv + SL.b_r : w + L.b_r;
+    uint8_t* const p_h_r = sv != nullptr ? sv + SL.h_r : w + L.h_r;
+    uint8_t* const p_a_s = sv != nullptr ? sv + SL.a_s : w + L.a_s;
+    uint8_t* const p_b_s = sv != nullptr ? sv + SL.b_s : w + L.b_s;
+    uint8_t* const p_h_s = sv != nullptr ? sv + SL.h_s : w + L.h_s;
     BwdArgs a{};
     a.offsets = offsets;
     a.T = s.T;
@@ -605,12 +637,12 @@ hipError_t launch_ffn_backward(const moe_shape& s, const void* x_perm, const flo
     a.w2 = static_cast<const uint8_t*>(w2);
     a.dy_perm = static_cast<const uint8_t*>(dy_perm);
     a.dy_sh = static_cast<const uint8_t*>(dy_sh);
-    a.a_r = w + L.a_r;
-    a.b_r = w + L.b_r;
-    a.h_r = w + L.h_r;
-    a.a_s = w + L.a_s;
-    a.b_s = w + L.b_s;
-    a.h_s = w + L.h_s;
+    a.a_r = p_a_r;
+    a.b_r = p_b_r;
+    a.h_r = p_h_r;
+    a.a_s = p_a_s;
+    a.b_s = p_b_s;
+    a.h_s = p_h_s;
     a.da_r = w + L.da_r;
     a.db_r = w + L.db_r;
     a.da_s = w + L.da_s;
@@ -637,9 +669,9 @@ hipError_t launch_ffn_backward(const moe_shape& s, const void* x_perm, const flo
         if ((e = hipGetLastError()) != hipSuccess) return e;
         e = launch_ffn_bwd_gemms(s, x_perm, qparams, offsets, x, w1, w3, w2t, w13t, dy_perm, dy_sh,
                                  dx_perm, dx_sh, reinterpret_cast<int32_t*>(w + L.plan),
-                                 reinterpret_cast<int32_t*>(w + L.plan_dh), w + L.h_r, w + L.h_s,
-                                 w + L.a_r, w + L.b_r, w + L.a_s, w + L.b_s, w + L.da_r, w + L.da_s,
-                                 st, mk);
+                                 reinterpret_cast<int32_t*>(w + L.plan_dh), p_h_r, p_h_s,
+                                 p_a_r, p_b_r, p_a_s, p_b_s, w + L.da_r, w + L.da_s,
+                                 st, mk, sv == nullptr);
         if (e != hipSuccess) return e;
         // the weight gradients read [da | db] rows and the routed m-tile
         // prefix of 128-row tiles is not needed by them
@@ -653,10 +685,12 @@ hipError_t launch_ffn_backward(const moe_shape& s, const void* x_perm, const flo
         a.dd_gs = a.hs;
         e = launch_ffn_plan128(s, offsets, reinterpret_cast<int32_t*>(w + L.plan), st);
         if (e != hipSuccess) return e;
-        e = launch_ffn_recompute(s, x_perm, qparams, offsets, x, w1, w3,
-                                 reinterpret_cast<const int32_t*>(w + L.plan), w + L.h_r, w + L.h_s,
-                                 w + L.a_r, w + L.b_r, w + L.a_s, w + L.b_s, st);
-        if (e != hipSuccess) return e;
+        if (sv == nullptr) {
+            e = launch_ffn_recompute(s, x_perm, qparams, offsets, x, w1, w3,
+                                     reinterpret_cast<const int32_t*>(w + L.plan), w + L.h_r, w + L.h_s,
+                                     w + L.a_r, w + L.b_r, w + L.a_s, w + L.b_s, st);
+            if (e != hipSuccess) return e;
+        }
         mark(mk);
         const int64_t mtT = (s.T + kTB - 1) / kTB;
         const int64_t routed = static_cast<int64_t>(s.T) * s.k / kTB + s.E;  // routed m-tiles, at most
@@ -671,8 +705,8 @@ hipError_t launch_ffn_backward(const moe_shape& s, const void* x_perm, const flo
         mark(mk);
     }
     if (L.big && L.wg) {
-        e = launch_ffn_wgrad(s, offsets, w + L.da_r, w + L.da_s, x_perm, x, dy_perm, dy_sh, w + L.h_r,
-                             w + L.h_s, dw1, dw3, dw2, w + L.wgq, st);
+        e = launch_ffn_wgrad(s, offsets, w + L.da_r, w + L.da_s, x_perm, x, dy_perm, dy_sh, p_h_r,
+                             p_h_s, dw1, dw3, dw2, w + L.wgq, st);
         if (e != hipSuccess) return e;
         mark(mk);
         return hipSuccess;

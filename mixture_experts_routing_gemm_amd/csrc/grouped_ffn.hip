@@ -1454,6 +1454,8 @@ int plan_blocks(const PlanLayout& pl) {
         1, std::min<int64_t>(64, (std::max(pl.n_up, pl.n_down) + 255) / 256)));
 }
 
+}  // namespace
+
 // large tiles when both projections divide evenly into them (and K into
 // whole groups of four slices)
 bool use_big_tiles(const moe_shape& s) {
@@ -1464,7 +1466,6 @@ bool use_big_tiles(const moe_shape& s) {
     return s.act != MOE_F32 && fits32 && s.h % (kBigBN / 2) == 0 && s.d % kBigBN == 0 &&
            s.d % (4 * kBigBK) == 0 && s.h % (4 * kBigBK) == 0;
 }
-}  // namespace
 
 bool ffn_gathers_rows(const moe_shape& s) {
     return use_big_tiles(s) && s.act == MOE_BF16 && s.dispatch == MOE_BF16;
@@ -1490,9 +1491,14 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const floa
                               const int32_t* offsets, const void* x, const void* w1,
                               const void* w3, const void* w2, void* y_perm, void* y_shared,
                               int32_t* plan, void* h_routed, void* h_shared, bool plan_done,
-                              hipStream_t st, const Marks* mk, const int32_t* gather) {
+                              hipStream_t st, const Marks* mk, const int32_t* gather, void* pre_a_r,
+                              void* pre_b_r, void* pre_a_s, void* pre_b_s) {
     const bool f32 = s.act == MOE_F32;
     if (gather != nullptr && !ffn_gathers_rows(s)) return hipErrorInvalidValue;
+    // with pre_a_r: the up-projection also stores a = W1 v and b = W3 v
+    // (the persistent tiles only)
+    const bool save = pre_a_r != nullptr;
+    if (save && !use_big_tiles(s)) return hipErrorInvalidValue;
     const bool big = use_big_tiles(s);
     const int bm = f32 ? kF32BM : (big ? kBigBM : kBM);
     const PlanLayout pl = plan_layout(s);
@@ -1535,8 +1541,17 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const floa
     a.wb = static_cast<const uint8_t*>(w3);
     a.out_routed = static_cast<uint8_t*>(h_routed);
     a.out_shared = static_cast<uint8_t*>(h_shared);
+    a.pre_a_routed = static_cast<uint8_t*>(pre_a_r);
+    a.pre_b_routed = static_cast<uint8_t*>(pre_b_r);
+    a.pre_a_shared = static_cast<uint8_t*>(pre_a_s);
+    a.pre_b_shared = static_cast<uint8_t*>(pre_b_s);
     hipError_t err;
-    if (f32) {
+    if (save) {
+        a.ntn = 2 * s.h / kBigBN;
+        const int64_t mt = max_mtiles(s, bm, false);
+        err = s.dispatch == MOE_FP8_E4M3 ? launch_persistent<kModeUpFp8Save>(a, mt, st)
+                                         : launch_persistent<kModeUpSave>(a, mt, st);
+    } else if (f32) {
         a.ntn = (s.h + kF32BN - 1) / kF32BN;
         const int64_t mt = max_mtiles(s, kF32BM, false);
         ffn_gemm_f32_kernel<true><<<static_cast<unsigned>(mt * a.ntn), 256, 0, st>>>(a, 0);
@@ -1733,7 +1748,7 @@ hipError_t launch_ffn_bwd_gemms(const moe_shape& s, const void* x_perm, const fl
                                 const void* dy_perm, const void* dy_sh, void* dx_perm, void* dx_sh,
                                 int32_t* plan_f, int32_t* plan_dh, void* h_r, void* h_s, void* a_r,
                                 void* b_r, void* a_s, void* b_s, void* dd_r, void* dd_s,
-                                hipStream_t st, const Marks* mk) {
+                                hipStream_t st, const Marks* mk, bool recompute) {
     const PlanLayout pf = plan_layout(s);
     const PlanLayout pd = plan_layout(s, (s.h + kBigBN - 1) / kBigBN, s.d / kBigBN);
     int32_t* cf = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(plan_f) + pf.counters);
@@ -1777,10 +1792,13 @@ hipError_t launch_ffn_bwd_gemms(const moe_shape& s, const void* x_perm, const fl
     a.pre_a_shared = static_cast<uint8_t*>(a_s);
     a.pre_b_shared = static_cast<uint8_t*>(b_s);
     a.ntn = pf.ntn_up;
-    err = s.dispatch == MOE_FP8_E4M3 ? launch_persistent<kModeUpFp8Save>(a, max_mtiles(s, kBigBM, false), st)
-                                     : launch_persistent<kModeUpSave>(a, max_mtiles(s, kBigBM, false), st);
+    // (not when the forward saved a, b and H)
+    if (recompute) {
+        err = s.dispatch == MOE_FP8_E4M3 ? launch_persistent<kModeUpFp8Save>(a, max_mtiles(s, kBigBM, false), st)
+                                         : launch_persistent<kModeUpSave>(a, max_mtiles(s, kBigBM, false), st);
+        if (err != hipSuccess) return err;
+    }
     mark(mk);
-    if (err != hipSuccess) return err;
     // dh: [da | db] rows
     a.plan = plan_dh;
     a.tiles = td;

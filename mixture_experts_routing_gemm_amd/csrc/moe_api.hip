@@ -25,7 +25,10 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const floa
                               const int32_t* offsets, const void* x, const void* w1,
                               const void* w3, const void* w2, void* y_perm, void* y_shared,
                               int32_t* plan, void* h_routed, void* h_shared, bool plan_done,
-                              hipStream_t st, const Marks* mk, const int32_t* gather = nullptr);
+                              hipStream_t st, const Marks* mk, const int32_t* gather = nullptr,
+                              void* pre_a_r = nullptr, void* pre_b_r = nullptr, void* pre_a_s = nullptr,
+                              void* pre_b_s = nullptr);
+bool use_big_tiles(const moe_shape& s);
 // whether the whole-layer forward's up-projection reads its routed rows from
 // x through src_token (bf16 rows, persistent tiles) instead of from x_perm
 bool ffn_gathers_rows(const moe_shape& s);
@@ -61,7 +64,7 @@ hipError_t launch_ffn_backward(const moe_shape& s, const void* x_perm, const flo
                                const void* w3, const void* w2, const void* dy_perm,
                                const void* dy_sh, void* dx_perm, void* dx_sh, float* dw1,
                                float* dw3, float* dw2, void* ws, hipStream_t st,
-                               const Marks* mk);
+                               const Marks* mk, const void* saved = nullptr);
 
 __global__ void clear_header_kernel(uint32_t* hdr) { hdr[threadIdx.x] = 0u; }
 
@@ -515,6 +518,66 @@ int32_t moe_grouped_ffn_backward(const moe_shape* s, const void* x_perm, const f
     return hip_status(launch_ffn_backward(*s, x_perm, qparams, offsets, x, w1, w3, w2, dy_perm,
                                           dy_shared, dx_perm, dx_shared, dw1, dw3, dw2,
                                           at<void>(ws, L.fbwd), st, nullptr));
+}
+
+size_t moe_ffn_saved_bytes(const moe_shape* s) {
+    if (check_shape(s, true) != MOE_OK || s->act != MOE_BF16 || !use_big_tiles(*s)) return 0;
+    return saved_layout(*s).bytes;
+}
+
+int32_t moe_grouped_ffn_save(const moe_shape* s, const void* x_perm, const float* qparams,
+                             const int32_t* offsets, const void* x, const void* w1, const void* w3,
+                             const void* w2, void* y_perm, void* y_shared, void* saved,
+                             size_t saved_bytes, void* ws, size_t ws_bytes, void* stream) {
+    MOE_TRY(check_shape(s, true));
+    if (s->act != MOE_BF16 || !use_big_tiles(*s)) return MOE_ERR_UNSUPPORTED;
+    if (s->T == 0) return MOE_OK;
+    MOE_TRY(check_ptrs({x_perm, offsets, w1, w3, w2, y_perm, saved}));
+    if (s->S > 0) MOE_TRY(check_ptrs({x, y_shared}));
+    else if (y_shared != nullptr) return MOE_ERR_INVALID_ARG;
+    if (s->dispatch == MOE_FP8_E4M3) MOE_TRY(check_ptrs({qparams}));
+    MOE_TRY(check_opt({x, qparams}));
+    const SavedLayout SL = saved_layout(*s);
+    if ((reinterpret_cast<uintptr_t>(saved) & 255u) != 0 || saved_bytes < SL.bytes)
+        return MOE_ERR_INVALID_ARG;
+    MOE_TRY(check_ws(*s, MOE_STAGE_FFN, ws, ws_bytes));
+    const Layout L = layout(*s, MOE_STAGE_FFN);
+    uint8_t* sv = static_cast<uint8_t*>(saved);
+    return hip_status(launch_grouped_ffn(*s, x_perm, qparams, offsets, x, w1, w3, w2, y_perm,
+                                         y_shared, at<int32_t>(ws, L.plan), sv + SL.h_r,
+                                         s->S > 0 ? sv + SL.h_s : nullptr, false,
+                                         static_cast<hipStream_t>(stream), nullptr, nullptr,
+                                         sv + SL.a_r, sv + SL.b_r, s->S > 0 ? sv + SL.a_s : nullptr,
+                                         s->S > 0 ? sv + SL.b_s : nullptr));
+}
+
+int32_t moe_grouped_ffn_backward_saved(const moe_shape* s, const void* x_perm,
+                                       const float* qparams, const int32_t* offsets,
+                                       const void* x, const void* w1, const void* w3,
+                                       const void* w2, const void* saved, size_t saved_bytes,
+                                       const void* dy_perm, const void* dy_shared, void* dx_perm,
+                                       void* dx_shared, float* dw1, float* dw3, float* dw2,
+                                       void* ws, size_t ws_bytes, void* stream) {
+    MOE_TRY(check_shape(s, true));
+    if (s->act != MOE_BF16 || !use_big_tiles(*s)) return MOE_ERR_UNSUPPORTED;
+    if (s->T == 0)
+        return moe_grouped_ffn_backward(s, x_perm, qparams, offsets, x, w1, w3, w2, dy_perm,
+                                        dy_shared, dx_perm, dx_shared, dw1, dw3, dw2, ws, ws_bytes,
+                                        stream);
+    MOE_TRY(check_ptrs({saved}));
+    if ((reinterpret_cast<uintptr_t>(saved) & 255u) != 0 || saved_bytes < saved_layout(*s).bytes)
+        return MOE_ERR_INVALID_ARG;
+    MOE_TRY(check_ptrs({w1, w3, w2, dw1, dw3, dw2, x_perm, offsets, dy_perm, dx_perm}));
+    if (s->S > 0) MOE_TRY(check_ptrs({x, dy_shared, dx_shared}));
+    else if (dx_shared != nullptr || dy_shared != nullptr) return MOE_ERR_INVALID_ARG;
+    if (s->dispatch == MOE_FP8_E4M3) MOE_TRY(check_ptrs({qparams}));
+    MOE_TRY(check_opt({x, qparams}));
+    MOE_TRY(check_ws(*s, MOE_STAGE_FFN_BACKWARD, ws, ws_bytes));
+    const Layout L = layout(*s, MOE_STAGE_FFN_BACKWARD);
+    return hip_status(launch_ffn_backward(*s, x_perm, qparams, offsets, x, w1, w3, w2, dy_perm,
+                                          dy_shared, dx_perm, dx_shared, dw1, dw3, dw2,
+                                          at<void>(ws, L.fbwd), static_cast<hipStream_t>(stream),
+                                          nullptr, saved));
 }
 
 size_t moe_fp8_weight_scale_floats(const moe_shape* s) {

@@ -162,6 +162,13 @@ inline GateWgradGrid gate_wgrad_grid(int64_t T, int d, int E, int act_bytes) {
 // plane value and an x value is exact in float32, so only the order of the
 // float32 sums differs from a per-token sum. About two 256 x 256 tiles per
 // CU, chunks of at least 256 tokens.
+// byte offsets of a, b and hid (routed, then shared) in the buffer of
+// activations a forward saves for the backward (ffn_backward.hip)
+struct SavedLayout {
+    size_t a_r = 0, b_r = 0, h_r = 0, a_s = 0, b_s = 0, h_s = 0, bytes = 0;
+};
+SavedLayout saved_layout(const moe_shape& s);
+
 struct GateMfmaPlan {
     bool use;
     int F, C;       // plane features; token chunks

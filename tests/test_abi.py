@@ -174,3 +174,37 @@ def test_backward_entry_points_validate_on_the_host(mm):
     z = mm.make_shape(0, 256, 8, 2, 0, 128, "bf16")
     assert lib.moe_combine_backward(ctypes.byref(z), None, None, None, None, None, None, None) == 0
     assert lib.moe_dispatch_backward(ctypes.byref(z), None, None, None, None, None) == 0
+
+
+def test_saved_activation_entry_points_validate_on_the_host(mm):
+    """moe_ffn_saved_bytes: a, b and hid of the routed rows and of the shared
+    experts' token rows, each section 256-byte aligned, or 0 off the
+    persistent tiles; the save / saved-backward calls refuse such shapes
+    and a missing, misaligned or short buffer before anything is enqueued."""
+    lib = _raw(mm)
+    s = mm.make_shape(64, 256, 8, 2, 1, 128, "bf16")
+    # routed: 128 rows x 128 values x 2 bytes, three times; shared: 64 rows
+    assert mm.moe_ffn_saved_bytes(s) == 3 * 128 * 128 * 2 + 3 * 64 * 128 * 2
+    assert mm.moe_ffn_saved_bytes(mm.make_shape(64, 256, 8, 2, 0, 136, "bf16")) == 0  # h % 128
+    assert mm.moe_ffn_saved_bytes(mm.make_shape(64, 64, 8, 2, 0, 128, "f32")) == 0
+    n = mm.moe_ffn_saved_bytes(s)
+    p = ctypes.c_void_p(FAKE)
+    sp = ctypes.byref(s)
+    wsn = mm.moe_workspace_bytes(s, mm.STAGE_FFN)
+    # save: saved missing, misaligned (16 but not 256 bytes) or short
+    assert lib.moe_grouped_ffn_save(sp, p, None, p, p, p, p, p, p, p, None, n, p, wsn, None) == -1
+    assert lib.moe_grouped_ffn_save(sp, p, None, p, p, p, p, p, p, p, ctypes.c_void_p(FAKE + 16), n, p,
+                                    wsn, None) == -1
+    assert lib.moe_grouped_ffn_save(sp, p, None, p, p, p, p, p, p, p, p, n - 256, p, wsn, None) == -1
+    bad = mm.make_shape(64, 256, 8, 2, 1, 136, "bf16")
+    assert lib.moe_grouped_ffn_save(ctypes.byref(bad), p, None, p, p, p, p, p, p, p, p, n, p, wsn,
+                                    None) == -2
+    # saved backward: the same checks on `saved`, then the backward's own
+    bn = mm.moe_workspace_bytes(s, mm.STAGE_FFN_BACKWARD)
+    args = [p, None, p, p, p, p, p]
+    tail = [p, p, p, p, p, p, p, p, bn, None]
+    assert lib.moe_grouped_ffn_backward_saved(sp, *args, None, n, *tail) == -1
+    assert lib.moe_grouped_ffn_backward_saved(sp, *args, p, n - 256, *tail) == -1
+    assert lib.moe_grouped_ffn_backward_saved(ctypes.byref(bad), *args, p, n, *tail) == -2
+    assert lib.moe_grouped_ffn_backward_saved(sp, *args, p, n, p, p, p, p, p, p, p, p, bn - 256,
+                                              None) == -3

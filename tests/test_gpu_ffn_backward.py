@@ -139,3 +139,88 @@ def test_ffn_backward_zero_tokens_zeroes_the_weight_gradients():
     torch.cuda.synchronize()
     for t in dw:
         assert float(t.abs().max()) == 0.0
+
+
+def run_saved(cfg, seed=1):
+    """moe_grouped_ffn_save against moe_grouped_ffn, and the backward from
+    the saved activations against the one that recomputes them: the same
+    bits everywhere (the saved a, b and hid are what the recomputation
+    would produce, from the same kernel). Routing is synthetic (skewed for
+    128 experts); the oracle parity of these outputs is the other tests'."""
+    from moe_workloads import make_routing
+    mm = _mm()
+    T, d, E, k, S, h = cfg.T, cfg.d, cfg.E, cfg.k, cfg.S, cfg.h
+    say(f"[ffn saved] {cfg.name} T={T} d={d} E={E} k={k} S={S} h={h} dispatch={cfg.dispatch}")
+    shape = mm.shape_of(cfg)
+    assert mm.moe_ffn_saved_bytes(shape) > 0
+    idx = make_routing(T, E, k, seed=seed + 2, skew=3.0 if E >= 128 else 0.0)
+    counts = np.bincount(idx.ravel(), minlength=E)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(offsets[-1])
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    fp8 = cfg.dispatch == "fp8"
+    if fp8:
+        x_perm = torch.randint(0, 255, (R, d), dtype=torch.uint8, device="cuda", generator=g)
+        x_perm[(x_perm & 0x7f) == 0x7f] = 0  # no NaN codes
+        qp = torch.stack([torch.rand(R, device="cuda", generator=g) * 0.01 + 1e-3,
+                          torch.randn(R, device="cuda", generator=g) * 0.1], dim=1).contiguous()
+    else:
+        x_perm = (torch.randn((R, d), device="cuda", generator=g) * 0.5).to(torch.bfloat16)
+        qp = None
+    x = (torch.randn((T, d), device="cuda", generator=g) * 0.5).to(torch.bfloat16) if S else None
+    G = E + S
+    w1 = (torch.randn((G, h, d), device="cuda", generator=g) * 0.05).to(torch.bfloat16)
+    w3 = (torch.randn((G, h, d), device="cuda", generator=g) * 0.05).to(torch.bfloat16)
+    w2 = (torch.randn((G, d, h), device="cuda", generator=g) * 0.05).to(torch.bfloat16)
+    off = dev(offsets)
+    bf = torch.bfloat16
+
+    # forward: plain and saving
+    ws_f = mm.alloc_workspace(shape, mm.STAGE_FFN)
+    y0 = torch.empty((R, d), dtype=bf, device="cuda")
+    ys0 = torch.empty((T, d), dtype=bf, device="cuda") if S else None
+    mm.moe_grouped_ffn(shape, x_perm, qp, off, x, w1, w3, w2, y0, ys0, ws_f)
+    y1 = torch.empty_like(y0)
+    ys1 = torch.empty_like(ys0) if S else None
+    saved = mm.alloc_saved(shape)
+    mm.moe_grouped_ffn_save(shape, x_perm, qp, off, x, w1, w3, w2, y1, ys1, saved, ws_f)
+    torch.cuda.synchronize()
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16)), "y_perm differs"
+    if S:
+        assert torch.equal(ys0.view(torch.int16), ys1.view(torch.int16)), "y_shared differs"
+
+    # backward: recomputing and from the saved activations
+    dy = (torch.randn((R, d), device="cuda", generator=g) * 0.05).to(bf)
+    dys = (torch.randn((T, d), device="cuda", generator=g) * 0.05).to(bf) if S else None
+    ws_b = mm.alloc_workspace(shape, mm.STAGE_FFN_BACKWARD)
+
+    def outs():
+        return [torch.empty((R, d), dtype=bf, device="cuda"),
+                torch.empty((T, d), dtype=bf, device="cuda") if S else None,
+                torch.full((G, h, d), 7.0, device="cuda"), torch.full((G, h, d), 7.0, device="cuda"),
+                torch.full((G, d, h), 7.0, device="cuda")]
+    o0, o1 = outs(), outs()
+    mm.moe_grouped_ffn_backward(shape, x_perm, qp, off, x, w1, w3, w2, dy, dys, *o0, ws_b)
+    mm.moe_grouped_ffn_backward_saved(shape, x_perm, qp, off, x, w1, w3, w2, saved, dy, dys, *o1, ws_b)
+    torch.cuda.synchronize()
+    for name, a_, b_ in zip(("dx_perm", "dx_shared", "dw1", "dw3", "dw2"), o0, o1):
+        if a_ is None:
+            continue
+        bits = torch.int16 if a_.dtype == bf else torch.int32
+        ndiff = int((a_.view(bits) != b_.view(bits)).sum().item())
+        say(f"[ffn saved] {cfg.name} {name}: {ndiff} elements differ")
+        assert ndiff == 0, name
+
+
+@pytest.mark.parametrize("base,kw", [
+    ("deepseekmoe_bf16", dict(T=700, d=512, E=8, k=3, S=2, h=384)),
+    ("fp8_dispatch", dict(T=700, d=512, E=8, k=3, S=2, h=384)),
+    ("zipf_stress_bf16", dict(T=2048, d=256, E=128, k=4, h=128)),
+    ("zipf_stress_bf16", dict(T=1001, d=512, E=16, k=2, h=256)),
+], ids=["shared_experts", "fp8_rows", "skewed_E128", "ragged"])
+def test_ffn_saved_activations_small(base, kw):
+    run_saved(_cfg(base, **kw))
+
+
+def test_ffn_saved_activations_headline_shape():
+    run_saved(dataclasses.replace(CONFIGS["zipf_stress_bf16"], name="zipf_saved"))
