@@ -619,7 +619,15 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
     // L2 misses fell 12 % (the time about 0.5 %): with dynamic claims the
     // siblings drifted about a tile's tenth apart, more than the few steps
     // of traffic that L2 holds.
-    constexpr bool kStaticClaims = MODE == kModeUp || MODE == kModeUpFp8 || MODE == kModeUpSave || MODE == kModeUpFp8Save || MODE == kModeDh;
+    // The bf16 up-projection (pool mode) takes the same round-robin claims
+    // for all but the last tenth (in groups of four) of each XCD's list;
+    // those tiles form one pool that every work-group draws from when its
+    // own claims are done. The XCDs run at different speeds and a work-group
+    // gets 16 or 17 of its XCD's long tiles, so with round-robin claims only
+    // the work-groups sat idle 5 % of the kernel at its end; the pool cut the
+    // up-projection by 2.8 % on the 65536-token workload.
+    constexpr bool kPool = MODE == kModeUp;
+    constexpr bool kStaticClaims = MODE == kModeUpFp8 || MODE == kModeUpSave || MODE == kModeUpFp8Save || MODE == kModeDh;
     constexpr int KS = kF8W ? 2 * kBigBK : kBigBK;  // operand values per slice
     constexpr uint32_t EB = kF8W ? 1 : 2;          // bytes per operand value
     const int tid = threadIdx.x;
@@ -667,14 +675,66 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
     const int flo = tile_at(work * xcd / 8), fhi = tile_at(work * (xcd + 1) / 8);
     const int hlo = n_full + n_halft * xcd / 8, hhi = n_full + n_halft * (xcd + 1) / 8;
     const int nclaim = (fhi - flo) + (hhi - hlo);  // tiles of this XCD
-    auto tile_of = [&](int c) -> int { return c < fhi - flo ? flo + c : hlo + (c - (fhi - flo)); };
-    int C = blockIdx.x >> 3;  // claim index of the current tile
-    if (C >= nclaim) return;
+    auto tile_of_x = [&](int c) -> int { return c < fhi - flo ? flo + c : hlo + (c - (fhi - flo)); };
+    // Claim codes. Static and dynamic modes: c < nclaim is claim c of this
+    // XCD. Pool mode: [0, nstatic) this XCD's round-robin claims, then
+    // [nstatic, nstatic + npool) the pool of every XCD's last q claims
+    // (groups of four consecutive claims of one XCD, the XCDs in turn).
+    int nstatic = nclaim, npool = 0;
+    auto ranges = [&](int y, int& f0, int& f1, int& h0, int& h1) {
+        f0 = tile_at(work * y / 8);
+        f1 = tile_at(work * (y + 1) / 8);
+        h0 = n_full + n_halft * y / 8;
+        h1 = n_full + n_halft * (y + 1) / 8;
+    };
+    if constexpr (kPool) {
+        int nmin = nclaim;
+        for (int y = 0; y < 8; ++y) {
+            int f0, f1, h0, h1;
+            ranges(y, f0, f1, h0, h1);
+            nmin = min(nmin, (f1 - f0) + (h1 - h0));
+        }
+        const int q = (nmin / 10) & ~3;
+        nstatic = nclaim - q;
+        npool = 8 * q;
+    }
+    const int kNone = nstatic + npool;
+    auto tile_of = [&](int code) -> int {
+        if (!kPool || code < nstatic) return tile_of_x(code);
+        const int pidx = code - nstatic, q = npool / 8;
+        const int g = pidx >> 2, y = g & 7, j = ((g >> 3) << 2) | (pidx & 3);
+        int f0, f1, h0, h1;
+        ranges(y, f0, f1, h0, h1);
+        const int c = (f1 - f0) + (h1 - h0) - q + j;
+        return c < f1 - f0 ? f0 + c : h0 + (c - (f1 - f0));
+    };
+    // pool mode: this work-group's next claim (thread 0): its own claims
+    // C, C + per_xcd, ... below nstatic, then pool indices
+    int jc = 0;
+    auto claim_next = [&]() -> int {
+        const int c = static_cast<int>(blockIdx.x >> 3) + jc * per_xcd;
+        ++jc;
+        if (c < nstatic) return c;
+        const int pidx = atomicAdd(a.counters, 1);
+        return pidx < npool ? nstatic + pidx : kNone;
+    };
+    int C = blockIdx.x >> 3;  // claim code of the current tile
     int32_t* counter = a.counters + xcd;
     int Cn;
-    if constexpr (kStaticClaims) {
+    if constexpr (kPool) {
+        if (tid == 0) {
+            lds_next[0] = claim_next();
+            lds_next[1] = claim_next();
+        }
+        __syncthreads();
+        C = __builtin_amdgcn_readfirstlane(lds_next[0]);
+        Cn = __builtin_amdgcn_readfirstlane(lds_next[1]);
+        if (C >= kNone) return;
+    } else if constexpr (kStaticClaims) {
+        if (C >= nclaim) return;
         Cn = C + per_xcd;
     } else {
+        if (C >= nclaim) return;
         if (tid == 0) lds_next[0] = per_xcd + atomicAdd(counter, 1);
         __syncthreads();
         Cn = __builtin_amdgcn_readfirstlane(lds_next[0]);
@@ -686,7 +746,7 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
     // descriptors were written by another kernel, often on another XCD --
     // is not exposed by the wait at the top of the tile
     TileInfo pre = cur;
-    if (Cn < nclaim) pre = decode_tile<MODE>(a, tile_of(Cn), nsh);
+    if (Cn < kNone) pre = decode_tile<MODE>(a, tile_of(Cn), nsh);
     // Rows gathered from x: the tokens of this tile's rows and of the next
     // one's. Later tiles' tokens are loaded at the end of the epilogue two
     // tiles ahead, so the drain there covers them and no wait on them falls
@@ -694,7 +754,7 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
     const bool gather = can_gather<MODE>() && a.a_gather != nullptr;
     int tok[4] = {0, 0, 0, 0}, ptok[4] = {0, 0, 0, 0};
     if (gather && !cur.shared) gather_tokens<MODE>(a, cur, wave, lane, tok);
-    if (gather && Cn < nclaim && !pre.shared) gather_tokens<MODE>(a, pre, wave, lane, ptok);
+    if (gather && Cn < kNone && !pre.shared) gather_tokens<MODE>(a, pre, wave, lane, ptok);
     TileSrc src;
     tile_sources<MODE>(a, cur, wave, lane, op_ar, op_as, by_ar, by_as, gather, tok, src);
     if (gather) wait_vmcnt<0>();
@@ -703,7 +763,7 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
     // the claim on the tile after next; later ones are issued at the end of
     // each epilogue, whose drain of the stores also waits for the claim
     int claim = 0;
-    if (!kStaticClaims && Cn < nclaim && tid == 0) claim = atomicAdd(counter, 1);
+    if (!kStaticClaims && Cn < kNone && tid == 0) claim = kPool ? claim_next() : atomicAdd(counter, 1);
 
     // Requests of slice k of a tile into ring slot `slot`: kBigLoads
     // buffer-to-LDS instructions per wave, issued one at a time (i). Wave w
@@ -846,7 +906,7 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
 
     bf16x8 fa0[MB], fb0[NB], fa1[MB], fb1[NB];
     while (true) {
-        const bool has_next = Cn < nclaim;
+        const bool has_next = Cn < kNone;
         // the claim on the tile after the next one is already in `claim` and
         // goes out to the other waves before the last four slices. After the
         // last tile the "next" tile is this one again: its first slices are
@@ -992,7 +1052,7 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
             }
             // the last four slices; the claimed tile index goes out through
             // LDS with the first of these steps' barrier
-            if (!kStaticClaims && tid == 0) lds_next[0] = has_next ? per_xcd + claim : nclaim;
+            if (!kStaticClaims && tid == 0) lds_next[0] = has_next ? (kPool ? claim : per_xcd + claim) : kNone;
             step(ic<0>(), ic<1>(), ic<2>(), IDLE, k);
             step(ic<1>(), ic<2>(), ic<2>(), IDLE, k + 1);
             step(ic<2>(), ic<2>(), ic<2>(), IDLE, k + 2);
@@ -1002,8 +1062,8 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
             k_loop(std::true_type{});
         else
             k_loop(std::false_type{});
-        const int Cn2 = kStaticClaims ? (has_next ? Cn + per_xcd : nclaim) : __builtin_amdgcn_readfirstlane(lds_next[0]);
-        if (has_next && Cn2 < nclaim) pre = decode_tile<MODE>(a, tile_of(Cn2), nsh);
+        const int Cn2 = kStaticClaims ? (has_next ? Cn + per_xcd : kNone) : __builtin_amdgcn_readfirstlane(lds_next[0]);
+        if (has_next && Cn2 < kNone) pre = decode_tile<MODE>(a, tile_of(Cn2), nsh);
 
         // epilogue: acc[mb][nb][v] is token (m0 + wm*128 + mb*32 + lr) and
         // weight row (wn*64 + nb*32 + 8*(v/4) + 4*lg + v%4) of the tile. A
@@ -1240,9 +1300,9 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
             }
         }
         // the tokens of the tile after next (used at the top of the next tile)
-        if (gather && has_next && Cn2 < nclaim && !pre.shared) gather_tokens<MODE>(a, pre, wave, lane, ptok);
+        if (gather && has_next && Cn2 < kNone && !pre.shared) gather_tokens<MODE>(a, pre, wave, lane, ptok);
         // the next tile's claim on the one after it
-        if (!kStaticClaims && has_next && Cn2 < nclaim && tid == 0) claim = atomicAdd(counter, 1);
+        if (!kStaticClaims && has_next && Cn2 < kNone && tid == 0) claim = kPool ? claim_next() : atomicAdd(counter, 1);
         // the epilogue's stores also count in vmcnt: drain before the next
         // tile's counted waits (and, after the last tile, let the re-read
         // slices land before the work-group's LDS is released)
