@@ -619,15 +619,17 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
     // L2 misses fell 12 % (the time about 0.5 %): with dynamic claims the
     // siblings drifted about a tile's tenth apart, more than the few steps
     // of traffic that L2 holds.
-    // The bf16 up-projection (pool mode) takes the same round-robin claims
+    // The bf16 and fp8-row up-projections and the down-projection (pool
+    // mode) take the same round-robin claims
     // for all but the last tenth (in groups of four) of each XCD's list;
     // those tiles form one pool that every work-group draws from when its
     // own claims are done. The XCDs run at different speeds and a work-group
     // gets 16 or 17 of its XCD's long tiles, so with round-robin claims only
     // the work-groups sat idle 5 % of the kernel at its end; the pool cut the
-    // up-projection by 2.8 % on the 65536-token workload.
-    constexpr bool kPool = MODE == kModeUp;
-    constexpr bool kStaticClaims = MODE == kModeUpFp8 || MODE == kModeUpSave || MODE == kModeUpFp8Save || MODE == kModeDh;
+    // up-projection by 2.8 % and the down-projection by 3 % on the
+    // 65536-token workload, the fp8-row up-projection by 4 %.
+    constexpr bool kPool = MODE == kModeUp || MODE == kModeDown || MODE == kModeUpFp8;
+    constexpr bool kStaticClaims = MODE == kModeUpSave || MODE == kModeUpFp8Save || MODE == kModeDh;
     constexpr int KS = kF8W ? 2 * kBigBK : kBigBK;  // operand values per slice
     constexpr uint32_t EB = kF8W ? 1 : 2;          // bytes per operand value
     const int tid = threadIdx.x;
