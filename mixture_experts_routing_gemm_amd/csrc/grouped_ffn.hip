@@ -77,7 +77,7 @@ struct GemmArgs {
     const int32_t* offsets;   // [E+1]
     const int32_t* plan;      // [E+S+1]
     const int4* tiles;        // m-tile descriptors of this projection (persistent kernel)
-    int32_t* counters;        // 8 tile counters, one per XCD (persistent kernel)
+    int32_t* counters;        // tile counters of the persistent kernel ([0]: the pool's), zeroed by the plan
     const int32_t* tile_meta; // [routed half m-tiles, routed full m-tiles] (persistent kernel)
     const uint8_t* wa;        // up: W1 [G, h, d]; down: W2 [G, d, h]
     const uint8_t* wb;        // up: W3 [G, h, d]
@@ -610,26 +610,22 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
     constexpr bool kFp8 = is_fp8rows(MODE);
     constexpr bool kF8W = is_f8w(MODE);
     constexpr bool kDown = is_down(MODE);
-    // The up-projections (bf16 or fp8 rows, also the backward's recompute)
-    // and dh take their tiles round-robin within the XCD
-    // (claim c goes to work-group c mod per_xcd) instead of from the XCD's
-    // counter: the n-tiles that share a token panel then start together on
-    // neighbouring work-groups and, with equal work, stay in step, so the
-    // panel's slices are still in L2 when the siblings ask for them. Its
-    // L2 misses fell 12 % (the time about 0.5 %): with dynamic claims the
-    // siblings drifted about a tile's tenth apart, more than the few steps
-    // of traffic that L2 holds.
-    // The bf16 and fp8-row up-projections and the down-projection (pool
-    // mode) take the same round-robin claims
-    // for all but the last tenth (in groups of four) of each XCD's list;
-    // those tiles form one pool that every work-group draws from when its
-    // own claims are done. The XCDs run at different speeds and a work-group
-    // gets 16 or 17 of its XCD's long tiles, so with round-robin claims only
-    // the work-groups sat idle 5 % of the kernel at its end; the pool cut the
-    // up-projection by 2.8 % and the down-projection by 3 % on the
-    // 65536-token workload, the fp8-row up-projection by 4 %.
-    constexpr bool kPool = MODE == kModeUp || MODE == kModeDown || MODE == kModeUpFp8;
-    constexpr bool kStaticClaims = MODE == kModeUpSave || MODE == kModeUpFp8Save || MODE == kModeDh;
+    // Tile claims. A work-group takes its XCD's claims round-robin (claim c
+    // goes to work-group c mod per_xcd) for all but the last tenth (in
+    // groups of four) of the XCD's list; those tiles, of every XCD, form
+    // one pool that any work-group draws from, through one atomic counter,
+    // once its own claims are done (the fp8-weight modes have no pool).
+    //  - Round-robin: the n-tiles that share a token panel start together on
+    //    neighbouring work-groups and, with equal work, stay in step, so the
+    //    panel's slices are still in L2 when the siblings ask for them. With
+    //    claims from a per-XCD counter the siblings drifted about a tenth of
+    //    a tile apart, more than the few steps of traffic that L2 holds: the
+    //    up-projection's L2 misses were 12 % higher.
+    //  - Pool: the XCDs run at different speeds, and the up-projection's
+    //    long tiles split 16 or 17 per work-group; with round-robin claims
+    //    alone the work-groups sat idle 5 % of the kernel at its end. The
+    //    pool cut the up-projection by 2.8 % and the down-projection by 3 %
+    //    on the 65536-token workload, the fp8-row up-projection by 4 %.
     constexpr int KS = kF8W ? 2 * kBigBK : kBigBK;  // operand values per slice
     constexpr uint32_t EB = kF8W ? 1 : 2;          // bytes per operand value
     const int tid = threadIdx.x;
@@ -656,9 +652,7 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
     // (work-groups b with b % 8 == x) owns the full tiles whose work starts
     // in the x-th eighth of the full part, then the x-th eighth of the half
     // tiles, so the XCDs get equal work, each keeps its experts' weights in
-    // its own L2, and the short tiles come last. Within an XCD tiles are
-    // taken in claim order: the first round static, later ones from that
-    // XCD's counter.
+    // its own L2, and the short tiles come last. Claims: see above.
     const int routed = a.plan[a.E];
     const int n_half = a.tile_meta[0];
     const int mtT = static_cast<int>((a.T + kBigBM - 1) / kBigBM);
@@ -678,8 +672,7 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
     const int hlo = n_full + n_halft * xcd / 8, hhi = n_full + n_halft * (xcd + 1) / 8;
     const int nclaim = (fhi - flo) + (hhi - hlo);  // tiles of this XCD
     auto tile_of_x = [&](int c) -> int { return c < fhi - flo ? flo + c : hlo + (c - (fhi - flo)); };
-    // Claim codes. Static and dynamic modes: c < nclaim is claim c of this
-    // XCD. Pool mode: [0, nstatic) this XCD's round-robin claims, then
+    // Claim codes: [0, nstatic) this XCD's round-robin claims, then
     // [nstatic, nstatic + npool) the pool of every XCD's last q claims
     // (groups of four consecutive claims of one XCD, the XCDs in turn).
     int nstatic = nclaim, npool = 0;
@@ -689,20 +682,22 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
         h0 = n_full + n_halft * y / 8;
         h1 = n_full + n_halft * (y + 1) / 8;
     };
-    if constexpr (kPool) {
+    {
         int nmin = nclaim;
         for (int y = 0; y < 8; ++y) {
             int f0, f1, h0, h1;
             ranges(y, f0, f1, h0, h1);
             nmin = min(nmin, (f1 - f0) + (h1 - h0));
         }
-        const int q = (nmin / 10) & ~3;
+        // (none for the fp8-weight modes: at their register limit, the pool's
+        // bookkeeping spilled registers that every tile then reloaded)
+        const int q = is_f8w(MODE) ? 0 : (nmin / 10) & ~3;
         nstatic = nclaim - q;
         npool = 8 * q;
     }
     const int kNone = nstatic + npool;
     auto tile_of = [&](int code) -> int {
-        if (!kPool || code < nstatic) return tile_of_x(code);
+        if (code < nstatic) return tile_of_x(code);
         const int pidx = code - nstatic, q = npool / 8;
         const int g = pidx >> 2, y = g & 7, j = ((g >> 3) << 2) | (pidx & 3);
         int f0, f1, h0, h1;
@@ -710,37 +705,27 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
         const int c = (f1 - f0) + (h1 - h0) - q + j;
         return c < f1 - f0 ? f0 + c : h0 + (c - (f1 - f0));
     };
-    // pool mode: this work-group's next claim (thread 0): its own claims
-    // C, C + per_xcd, ... below nstatic, then pool indices
-    int jc = 0;
+    // this work-group's next claim (thread 0): its own claims C,
+    // C + per_xcd, ... below nstatic, then pool indices (the count of its
+    // claims is kept in LDS, not in a register the whole kernel long)
     auto claim_next = [&]() -> int {
+        const int jc = lds_next[2];
+        lds_next[2] = jc + 1;
         const int c = static_cast<int>(blockIdx.x >> 3) + jc * per_xcd;
-        ++jc;
         if (c < nstatic) return c;
         const int pidx = atomicAdd(a.counters, 1);
         return pidx < npool ? nstatic + pidx : kNone;
     };
-    int C = blockIdx.x >> 3;  // claim code of the current tile
-    int32_t* counter = a.counters + xcd;
-    int Cn;
-    if constexpr (kPool) {
-        if (tid == 0) {
-            lds_next[0] = claim_next();
-            lds_next[1] = claim_next();
-        }
-        __syncthreads();
-        C = __builtin_amdgcn_readfirstlane(lds_next[0]);
-        Cn = __builtin_amdgcn_readfirstlane(lds_next[1]);
-        if (C >= kNone) return;
-    } else if constexpr (kStaticClaims) {
-        if (C >= nclaim) return;
-        Cn = C + per_xcd;
-    } else {
-        if (C >= nclaim) return;
-        if (tid == 0) lds_next[0] = per_xcd + atomicAdd(counter, 1);
-        __syncthreads();
-        Cn = __builtin_amdgcn_readfirstlane(lds_next[0]);
+    int C, Cn;  // claim codes of the current and the next tile
+    if (tid == 0) {
+        lds_next[2] = 0;
+        lds_next[0] = claim_next();
+        lds_next[1] = claim_next();
     }
+    __syncthreads();
+    C = __builtin_amdgcn_readfirstlane(lds_next[0]);
+    Cn = __builtin_amdgcn_readfirstlane(lds_next[1]);
+    if (C >= kNone) return;
 
     TileInfo cur = decode_tile<MODE>(a, tile_of(C), nsh);
     // the next tile's descriptor: a scalar load, issued a tile ahead (for
@@ -765,7 +750,7 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
     // the claim on the tile after next; later ones are issued at the end of
     // each epilogue, whose drain of the stores also waits for the claim
     int claim = 0;
-    if (!kStaticClaims && Cn < kNone && tid == 0) claim = kPool ? claim_next() : atomicAdd(counter, 1);
+    if (Cn < kNone && tid == 0) claim = claim_next();
 
     // Requests of slice k of a tile into ring slot `slot`: kBigLoads
     // buffer-to-LDS instructions per wave, issued one at a time (i). Wave w
@@ -1054,7 +1039,7 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
             }
             // the last four slices; the claimed tile index goes out through
             // LDS with the first of these steps' barrier
-            if (!kStaticClaims && tid == 0) lds_next[0] = has_next ? (kPool ? claim : per_xcd + claim) : kNone;
+            if (tid == 0) lds_next[0] = has_next ? claim : kNone;
             step(ic<0>(), ic<1>(), ic<2>(), IDLE, k);
             step(ic<1>(), ic<2>(), ic<2>(), IDLE, k + 1);
             step(ic<2>(), ic<2>(), ic<2>(), IDLE, k + 2);
@@ -1064,7 +1049,7 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
             k_loop(std::true_type{});
         else
             k_loop(std::false_type{});
-        const int Cn2 = kStaticClaims ? (has_next ? Cn + per_xcd : kNone) : __builtin_amdgcn_readfirstlane(lds_next[0]);
+        const int Cn2 = __builtin_amdgcn_readfirstlane(lds_next[0]);
         if (has_next && Cn2 < kNone) pre = decode_tile<MODE>(a, tile_of(Cn2), nsh);
 
         // epilogue: acc[mb][nb][v] is token (m0 + wm*128 + mb*32 + lr) and
@@ -1304,7 +1289,7 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
         // the tokens of the tile after next (used at the top of the next tile)
         if (gather && has_next && Cn2 < kNone && !pre.shared) gather_tokens<MODE>(a, pre, wave, lane, ptok);
         // the next tile's claim on the one after it
-        if (!kStaticClaims && has_next && Cn2 < kNone && tid == 0) claim = kPool ? claim_next() : atomicAdd(counter, 1);
+        if (has_next && Cn2 < kNone && tid == 0) claim = claim_next();
         // the epilogue's stores also count in vmcnt: drain before the next
         // tile's counted waits (and, after the last tile, let the re-read
         // slices land before the work-group's LDS is released)
