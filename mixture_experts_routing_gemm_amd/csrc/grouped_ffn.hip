@@ -611,10 +611,11 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
     constexpr bool kF8W = is_f8w(MODE);
     constexpr bool kDown = is_down(MODE);
     // Tile claims. A work-group takes its XCD's claims round-robin (claim c
-    // goes to work-group c mod per_xcd) for all but the last tenth (in
-    // groups of four) of the XCD's list; those tiles, of every XCD, form
-    // one pool that any work-group draws from, through one atomic counter,
-    // once its own claims are done (the fp8-weight modes have no pool).
+    // goes to work-group c mod per_xcd) for all but the last tenth of the
+    // XCD's list; those tiles form the XCD's pool segment. A work-group whose
+    // own claims are done draws from its XCD's segment first (one atomic
+    // counter per segment), then from the other XCDs' in turn (the
+    // fp8-weight modes have no pool).
     //  - Round-robin: the n-tiles that share a token panel start together on
     //    neighbouring work-groups and, with equal work, stay in step, so the
     //    panel's slices are still in L2 when the siblings ask for them. With
@@ -626,6 +627,9 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
     //    alone the work-groups sat idle 5 % of the kernel at its end. The
     //    pool cut the up-projection by 2.8 % and the down-projection by 3 %
     //    on the 65536-token workload, the fp8-row up-projection by 4 %.
+    //    Drawing from any segment in one order cost 18 % more L2 misses in
+    //    the up-projection (4.25 against 5.0 GB on that workload) for the
+    //    same time: the stolen tiles' panels are in another XCD's L2.
     constexpr int KS = kF8W ? 2 * kBigBK : kBigBK;  // operand values per slice
     constexpr uint32_t EB = kF8W ? 1 : 2;          // bytes per operand value
     const int tid = threadIdx.x;
@@ -673,8 +677,7 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
     const int nclaim = (fhi - flo) + (hhi - hlo);  // tiles of this XCD
     auto tile_of_x = [&](int c) -> int { return c < fhi - flo ? flo + c : hlo + (c - (fhi - flo)); };
     // Claim codes: [0, nstatic) this XCD's round-robin claims, then
-    // [nstatic, nstatic + npool) the pool of every XCD's last q claims
-    // (groups of four consecutive claims of one XCD, the XCDs in turn).
+    // nstatic + y q + j for claim j of XCD y's segment (its last q claims).
     int nstatic = nclaim, npool = 0;
     auto ranges = [&](int y, int& f0, int& f1, int& h0, int& h1) {
         f0 = tile_at(work * y / 8);
@@ -699,7 +702,7 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
     auto tile_of = [&](int code) -> int {
         if (code < nstatic) return tile_of_x(code);
         const int pidx = code - nstatic, q = npool / 8;
-        const int g = pidx >> 2, y = g & 7, j = ((g >> 3) << 2) | (pidx & 3);
+        const int y = pidx / q, j = pidx - y * q;  // segment y: XCD y's last q claims
         int f0, f1, h0, h1;
         ranges(y, f0, f1, h0, h1);
         const int c = (f1 - f0) + (h1 - h0) - q + j;
@@ -713,12 +716,22 @@ __device__ __forceinline__ void persistent_gemm(const GemmArgs& a) {
         lds_next[2] = jc + 1;
         const int c = static_cast<int>(blockIdx.x >> 3) + jc * per_xcd;
         if (c < nstatic) return c;
-        const int pidx = atomicAdd(a.counters, 1);
-        return pidx < npool ? nstatic + pidx : kNone;
+        // the pool: this XCD's segment first (its panels are in this L2),
+        // then the other XCDs' in turn; lds_next[3] skips segments found empty
+        const int q = npool / 8;
+        if (q == 0) return kNone;
+        for (int t = lds_next[3]; t < 8; ++t) {
+            const int y = (xcd + t) & 7;
+            const int j = atomicAdd(a.counters + y, 1);
+            if (j < q) return nstatic + y * q + j;
+            lds_next[3] = t + 1;
+        }
+        return kNone;
     };
     int C, Cn;  // claim codes of the current and the next tile
     if (tid == 0) {
         lds_next[2] = 0;
+        lds_next[3] = 0;
         lds_next[0] = claim_next();
         lds_next[1] = claim_next();
     }
