@@ -422,9 +422,6 @@ __device__ __forceinline__ int token_dest(const int32_t* __restrict__ topk_idx,
     return dst;
 }
 
-// ROWS = false: the maps only, for a forward whose up-projection gathers
-// the rows from x itself
-template <bool ROWS>
 __global__ __launch_bounds__(256) void dispatch_permute_kernel(
     const uint8_t* __restrict__ x, const int32_t* __restrict__ topk_idx,
     const int32_t* __restrict__ rank, const int32_t* __restrict__ pre,
@@ -440,7 +437,6 @@ __global__ __launch_bounds__(256) void dispatch_permute_kernel(
     const int dst =
         token_dest(topk_idx, rank, pre, offsets, cap, reassign, t, E, k, lane, dest_row,
                    src_token);
-    if (!ROWS) return;
     int dj[kMaxK];
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) dj[j] = __shfl(dst, j, kWave);
@@ -465,6 +461,23 @@ __global__ __launch_bounds__(256) void dispatch_permute_kernel(
             }
         }
     }
+}
+
+// The maps only (dest_row, src_token), one thread per (token, slot): for a
+// whole-layer forward whose up-projection gathers the rows from x itself.
+// Its first fp.nblk work-groups write the FFN's tile plan, as the permute's do.
+__global__ __launch_bounds__(256) void dispatch_map_kernel(
+    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ rank,
+    const int32_t* __restrict__ pre, const int32_t* __restrict__ offsets, int cap, int reassign,
+    int64_t T, int E, int k, int32_t* __restrict__ dest_row, int32_t* __restrict__ src_token,
+    FfnPlanArgs fp) {
+    const int pb = permute_or_plan(fp, offsets, E, T);
+    if (pb < 0) return;
+    const int64_t i = static_cast<int64_t>(pb) * 256 + threadIdx.x;  // slot t * k + j
+    if (i >= T * k) return;
+    const int64_t t = i / k;
+    token_dest(topk_idx, rank, pre, offsets, cap, reassign, t, E, k, static_cast<int>(i - t * k),
+               dest_row, src_token);
 }
 
 // 16 bf16 values (two 16-byte chunks) -> 16 e4m3 codes (one 16-byte chunk)
@@ -744,11 +757,18 @@ hipError_t launch_dispatch(const moe_shape& s, const void* x, const int32_t* top
             s.quant == MOE_QUANT_TOKEN_ABSMAX ? 1 : 0, x_self, q_self);
     } else {
         const int row_bytes = s.d * (s.act == MOE_F32 ? 4 : 2);
-        // no x_perm: the maps only (the rows are gathered where they are used)
-        auto kern = x_perm == nullptr ? dispatch_permute_kernel<false> : dispatch_permute_kernel<true>;
-        kern<<<pblocks, 256, 0, st>>>(
-            static_cast<const uint8_t*>(x), topk_idx, rank, pre, offsets, s.capacity, reassign, s.T,
-            s.E, s.k, row_bytes, dest_row, src_token, static_cast<uint8_t*>(x_perm), fp);
+        if (x_perm == nullptr) {
+            // no x_perm: the maps only (the rows are gathered where they are used)
+            const unsigned mblocks = static_cast<unsigned>((s.T * s.k + 255) / 256) +
+                                     (fp.plan != nullptr ? static_cast<unsigned>(fp.nblk) : 0u);
+            dispatch_map_kernel<<<mblocks, 256, 0, st>>>(topk_idx, rank, pre, offsets, s.capacity,
+                                                         reassign, s.T, s.E, s.k, dest_row,
+                                                         src_token, fp);
+        } else {
+            dispatch_permute_kernel<<<pblocks, 256, 0, st>>>(
+                static_cast<const uint8_t*>(x), topk_idx, rank, pre, offsets, s.capacity, reassign,
+                s.T, s.E, s.k, row_bytes, dest_row, src_token, static_cast<uint8_t*>(x_perm), fp);
+        }
     }
     mark(mk);
     return hipGetLastError();
